@@ -1,0 +1,281 @@
+/*
+ * msa_oracle.c -- plain, slow, obviously-correct CPU oracle for MiniMax Sparse
+ * Attention (MSA).  TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg are its only callers.  The GPU library never
+ * links, loads or calls it, and it shares no source with the GPU library.
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "MSA 稀疏注意力三国杀：NSA / DSA / MoBA / MSA 四方案深度对比"
+ *        (ai-engineering-6yk.pages.dev), sections "第一步：粗筛", "第二步：精算",
+ *        "Kernel 创新：Outer Gather Q", "附录最有意思：head 涌现的三种模式".
+ *   [P3] "稀疏注意力速览（Sparse Attention，2019 ~ 2026）" (speedcell4.github.io),
+ *        entry "MiniMax Sparse Attention（MSA）".
+ *   [P5] "稀疏注意力架构革命：2026年长上下文大模型核心技术解析" (chenxutan.com),
+ *        section on standard self-attention (softmax(QK^T/sqrt(d_k))V).
+ *
+ * Every function works on ONE (sequence, KV-group) slice; the caller loops over
+ * slices.  All arithmetic is IEEE double.  Inputs arrive already decoded from
+ * their storage dtype (bf16/fp32 -> double is exact).
+ *
+ * Notation: N keys, block size B, nb = ceil(N/B) blocks; a query row r sits at
+ * absolute position pos[r] (0-based, pos < N) and owns block bt = pos/B.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - the index score is the raw dot product q_I . k_I (no scale, no activation);
+ *   - the block max-pool only covers keys j <= pos (causal), blocks b > bt are
+ *     not scored (written as NaN here, "not written" on the GPU);
+ *   - ties between equal block scores go to the lower block index;
+ *   - when fewer than k blocks are eligible, all bt+1 are selected and the rest
+ *     of the row is padded with -1; selections are emitted in ascending order;
+ *   - the main branch scales logits by softmax_scale (1/sqrt(d) by default).
+ *
+ * Parity status: every function here is pinned by tests against brute force,
+ * closed forms and special cases that reduce to textbook dense attention.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* [P1 第一步：粗筛 items 1-2; P3 MSA entry "先算 token 分数，再在块内 max-pool"]
+ * out[r*nb + b] = max over keys j in block b with j <= pos[r] of
+ *                 sum_c qI[r*dI + c] * kI[j*dI + c],          for b <= pos[r]/B;
+ * out[r*nb + b] = NaN for b > pos[r]/B (such blocks are not eligible). */
+void orc_index_scores(int64_t N, int B, int dI, int64_t nrows,
+                      const double *qI, const int64_t *pos, const double *kI,
+                      double *out)
+{
+    const int64_t nb = (N + B - 1) / B;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t p = pos[r];
+        const int64_t bt = p / B;
+        const double *q = qI + r * dI;
+        for (int64_t b = 0; b < nb; ++b) {
+            if (b > bt) { out[r * nb + b] = NAN; continue; }
+            double best = -INFINITY;
+            int64_t jend = (b + 1) * B - 1;
+            if (jend > p) jend = p;
+            for (int64_t j = b * B; j <= jend; ++j) {
+                const double *kk = kI + j * dI;
+                double s = 0.0;
+                for (int c = 0; c < dI; ++c) s += q[c] * kk[c];
+                if (s > best) best = s;
+            }
+            out[r * nb + b] = best;
+        }
+    }
+}
+
+/* [P1 第一步：粗筛 item 3 ("当前位置所在的块必选，其余按得分高低挑") and the closing
+ *  rule of the head-pattern appendix (only the own block is forced);
+ *  P3 MSA entry ("每个 GQA group 独立 Top-k 选块，并强制保留当前 token 所在 local block")]
+ * Row r: start from {own[r]}; repeatedly add the not-yet-chosen block b < own[r]
+ * with the largest score, ties to the smaller b, until min(k, own[r]+1) blocks
+ * are chosen.  Emit ascending, pad with -1.  scores is [nrows, nb]. */
+void orc_block_topk(int64_t nb, int k, int64_t nrows, const double *scores,
+                    const int64_t *own, int32_t *sel)
+{
+#pragma omp parallel
+    {
+        unsigned char *taken = (unsigned char *)calloc((size_t)nb, 1);
+        int64_t *chosen = (int64_t *)malloc(sizeof(int64_t) * (size_t)k);
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const double *s = scores + r * nb;
+            const int64_t bt = own[r];
+            int64_t want = bt + 1 < k ? bt + 1 : k;
+            memset(taken, 0, (size_t)nb);
+            int n = 0;
+            chosen[n++] = bt;
+            taken[bt] = 1;
+            while (n < want) {
+                int64_t best = -1;
+                for (int64_t b = 0; b < bt; ++b) {
+                    if (taken[b]) continue;
+                    if (best < 0 || s[b] > s[best]) best = b; /* strict: lower b keeps ties */
+                }
+                taken[best] = 1;
+                chosen[n++] = best;
+            }
+            /* ascending order: insertion sort of <= k ids */
+            for (int i = 1; i < n; ++i) {
+                int64_t v = chosen[i];
+                int j = i - 1;
+                while (j >= 0 && chosen[j] > v) { chosen[j + 1] = chosen[j]; --j; }
+                chosen[j + 1] = v;
+            }
+            for (int i = 0; i < k; ++i) sel[r * k + i] = i < n ? (int32_t)chosen[i] : -1;
+        }
+        free(taken);
+        free(chosen);
+    }
+}
+
+/* [P1 Kernel 创新：Outer Gather Q: "把所有选中了这块的 query 聚集到一起"]
+ * Inverse of one slice's selection: for every block b, the list of entries
+ * t*k + slot (ascending t) of query rows t whose selection holds b at `slot`.
+ * offsets has nb+1 entries (offsets[0] = 0); entries has room for T*k ints.
+ * Written as a two-pass counting sort so a full-size slice stays O(T*k). */
+void orc_invert(int64_t T, int k, int64_t nb, const int32_t *sel,
+                int64_t *offsets, int32_t *entries)
+{
+    int64_t *cursor = (int64_t *)calloc((size_t)nb, sizeof(int64_t));
+    for (int64_t b = 0; b <= nb; ++b) offsets[b] = 0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int i = 0; i < k; ++i) {
+            int32_t b = sel[t * k + i];
+            if (b >= 0) offsets[b + 1] += 1;
+        }
+    for (int64_t b = 0; b < nb; ++b) offsets[b + 1] += offsets[b];
+    for (int64_t b = 0; b < nb; ++b) cursor[b] = offsets[b];
+    for (int64_t t = 0; t < T; ++t)
+        for (int i = 0; i < k; ++i) {
+            int32_t b = sel[t * k + i];
+            if (b >= 0) entries[cursor[b]++] = (int32_t)(t * k + i);
+        }
+    free(cursor);
+}
+
+/* [P1 第二步：精算: full attention only over the chosen blocks; P3 MSA entry "Main
+ *  Branch 只在这些块上做精确 softmax attention"; P5 standard formula
+ *  softmax(QK^T/sqrt(d_k))V]
+ * For row r and each of the G query heads of this group:
+ *   J = union over valid sel[r][i] of [b*B, (b+1)*B) intersected with [0, pos[r]];
+ *   out[r,h,:] = sum_{j in J} softmax_j(scale * q[r,h,:].K[j,:]) V[j,:].
+ * q is [nrows, G, d]; K, V are [N, d]; sel is [nrows, k]; out is [nrows, G, d]. */
+void orc_attention(int64_t N, int B, int d, int G, int k, int64_t nrows,
+                   const double *q, const int64_t *pos, const int32_t *sel,
+                   const double *K, const double *V, double scale, double *out)
+{
+    (void)N;
+#pragma omp parallel
+    {
+        double *logit = (double *)malloc(sizeof(double) * (size_t)k * (size_t)B);
+        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)k * (size_t)B);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t p = pos[r];
+            int64_t nk = 0;
+            for (int i = 0; i < k; ++i) {
+                int32_t b = sel[r * k + i];
+                if (b < 0) continue;
+                for (int64_t j = (int64_t)b * B; j < ((int64_t)b + 1) * B && j <= p; ++j) key[nk++] = j;
+            }
+            for (int h = 0; h < G; ++h) {
+                const double *qq = q + (r * G + h) * d;
+                double m = -INFINITY;
+                for (int64_t a = 0; a < nk; ++a) {
+                    const double *kk = K + key[a] * d;
+                    double s = 0.0;
+                    for (int c = 0; c < d; ++c) s += qq[c] * kk[c];
+                    logit[a] = s * scale;
+                    if (logit[a] > m) m = logit[a];
+                }
+                double l = 0.0;
+                for (int64_t a = 0; a < nk; ++a) { logit[a] = exp(logit[a] - m); l += logit[a]; }
+                double *o = out + (r * G + h) * d;
+                for (int c = 0; c < d; ++c) o[c] = 0.0;
+                for (int64_t a = 0; a < nk; ++a) {
+                    const double w = logit[a] / l;
+                    const double *vv = V + key[a] * d;
+                    for (int c = 0; c < d; ++c) o[c] += w * vv[c];
+                }
+            }
+        }
+        free(logit);
+        free(key);
+    }
+}
+
+/* Partial form of the main branch, one result per selected block (the unit of
+ * work of the Outer-Gather-Q order in [P1 Kernel 创新：Outer Gather Q]):
+ *   lse[r,i,h] = log sum_{j in block sel[r][i], j <= pos} exp(scale q.K_j)
+ *   Op[r,i,h,:] = softmax over that block alone, applied to V.
+ * Slots with sel = -1 get lse = -inf and Op = 0.
+ * lse is [nrows, k, G]; Op is [nrows, k, G, d]. */
+void orc_attention_partials(int64_t N, int B, int d, int G, int k, int64_t nrows,
+                            const double *q, const int64_t *pos, const int32_t *sel,
+                            const double *K, const double *V, double scale,
+                            double *lse, double *Op)
+{
+    (void)N;
+#pragma omp parallel
+    {
+        double *logit = (double *)malloc(sizeof(double) * (size_t)B);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t p = pos[r];
+            for (int i = 0; i < k; ++i) {
+                const int32_t b = sel[r * k + i];
+                for (int h = 0; h < G; ++h) {
+                    double *o = Op + ((r * k + i) * G + h) * d;
+                    double *L = lse + (r * k + i) * G + h;
+                    for (int c = 0; c < d; ++c) o[c] = 0.0;
+                    if (b < 0) { *L = -INFINITY; continue; }
+                    const double *qq = q + (r * G + h) * d;
+                    int64_t j0 = (int64_t)b * B, nk = 0;
+                    double m = -INFINITY;
+                    for (int64_t j = j0; j < j0 + B && j <= p; ++j, ++nk) {
+                        const double *kk = K + j * d;
+                        double s = 0.0;
+                        for (int c = 0; c < d; ++c) s += qq[c] * kk[c];
+                        logit[nk] = s * scale;
+                        if (logit[nk] > m) m = logit[nk];
+                    }
+                    double l = 0.0;
+                    for (int64_t a = 0; a < nk; ++a) { logit[a] = exp(logit[a] - m); l += logit[a]; }
+                    for (int64_t a = 0; a < nk; ++a) {
+                        const double w = logit[a] / l;
+                        const double *vv = V + (j0 + a) * d;
+                        for (int c = 0; c < d; ++c) o[c] += w * vv[c];
+                    }
+                    *L = m + log(l);
+                }
+            }
+        }
+        free(logit);
+    }
+}
+
+/* Log-sum-exp merge of per-block partials (not on the pages; it is the identity
+ * softmax over a union of disjoint key sets = lse-weighted mix of the parts):
+ *   Lt = log sum_i exp(lse_i);  out = sum_i exp(lse_i - Lt) * Op_i.
+ * Slots with lse = -inf contribute nothing.  Shapes as in the partials. */
+void orc_lse_merge(int d, int G, int k, int64_t nrows, const double *lse,
+                   const double *Op, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        for (int h = 0; h < G; ++h) {
+            double m = -INFINITY;
+            for (int i = 0; i < k; ++i) {
+                double L = lse[(r * k + i) * G + h];
+                if (L > m) m = L;
+            }
+            double tot = 0.0;
+            for (int i = 0; i < k; ++i) {
+                double L = lse[(r * k + i) * G + h];
+                if (L != -INFINITY) tot += exp(L - m);
+            }
+            const double Lt = m + log(tot);
+            double *o = out + (r * G + h) * d;
+            for (int c = 0; c < d; ++c) o[c] = 0.0;
+            for (int i = 0; i < k; ++i) {
+                double L = lse[(r * k + i) * G + h];
+                if (L == -INFINITY) continue;
+                const double w = exp(L - Lt);
+                const double *src = Op + ((r * k + i) * G + h) * d;
+                for (int c = 0; c < d; ++c) o[c] += w * src[c];
+            }
+        }
+    }
+}
+
+/* Threads OpenMP will use for the parallel loops above (reported beside timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif

@@ -1,0 +1,268 @@
+"""Pins for the CPU oracle (CPU only).
+
+The pages print no worked MSA example, so the oracle is pinned by (a) a dense
+brute force that reaches every result by a different route, (b) closed forms,
+(c) special cases that reduce to textbook / library dense attention, and (d) the
+invariants the pages state (own block always selected, a fixed budget of k
+blocks).  Each test names the passage it pins."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import brute_force as bf
+
+RNG = np.random.default_rng(20260603)
+
+
+def _pos(N, T):
+    return np.arange(N - T, N, dtype=np.int64)
+
+
+# ------------------------------------------------------------------ index scores
+# "第一步：粗筛" items 1-2: score every token, block score = max inside the block.
+@pytest.mark.parametrize("N,T,B,dI", [(16, 16, 4, 3), (37, 20, 8, 5), (300, 300, 128, 32),
+                                      (129, 2, 128, 4), (1, 1, 4, 2)])
+def test_scores_match_dense_brute_force(N, T, B, dI):
+    qI = RNG.standard_normal((T, dI))
+    kI = RNG.standard_normal((N, dI))
+    pos = _pos(N, T)
+    got = oracle.slice_index_scores(qI, pos, kI, B)
+    ref = bf.scores(qI, kI, pos, B)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_allclose(got[ok], ref[ok], rtol=1e-12, atol=1e-12)
+
+
+def test_scores_closed_forms():
+    N, T, B, dI = 50, 50, 8, 6
+    pos = _pos(N, T)
+    nb = (N + B - 1) // B
+    # zero keys -> every eligible block score is exactly 0
+    s0 = oracle.slice_index_scores(RNG.standard_normal((T, dI)), pos, np.zeros((N, dI)), B)
+    elig = np.arange(nb)[None, :] <= (pos // B)[:, None]
+    assert np.all(s0[elig] == 0.0) and np.all(np.isnan(s0[~elig]))
+    # q = k = e0 -> every eligible block score is exactly 1
+    e0q = np.zeros((T, dI)); e0q[:, 0] = 1
+    e0k = np.zeros((N, dI)); e0k[:, 0] = 1
+    s1 = oracle.slice_index_scores(e0q, pos, e0k, B)
+    assert np.all(s1[elig] == 1.0)
+
+
+def test_scores_are_causal_inside_own_block():
+    # key j's value grows with j: the own-block maximum must stop at j = pos.
+    N, B = 24, 8
+    kI = np.arange(N, dtype=np.float64)[:, None]
+    qI = np.ones((N, 1))
+    s = oracle.slice_index_scores(qI, _pos(N, N), kI, B)
+    for t in range(N):
+        bt = t // B
+        assert s[t, bt] == t                      # max over keys bt*B..t is t itself
+        for b in range(bt):
+            assert s[t, b] == (b + 1) * B - 1     # full past blocks: their last key
+
+
+def test_scores_hand_worked_example():
+    # tiny example worked out by hand: B = 2, dI = 1, q = 1 for every row,
+    # keys 3,-1 | 0,5 | 2 (ragged last block)
+    kI = np.array([[3.0], [-1.0], [0.0], [5.0], [2.0]])
+    qI = np.ones((5, 1))
+    s = oracle.slice_index_scores(qI, _pos(5, 5), kI, 2)
+    expect = np.array([[3, np.nan, np.nan],
+                       [3, np.nan, np.nan],
+                       [3, 0, np.nan],
+                       [3, 5, np.nan],
+                       [3, 5, 2]], dtype=np.float64)
+    np.testing.assert_array_equal(s, expect)
+
+
+# ------------------------------------------------------------------ selection
+# "第一步：粗筛" item 3 and the head-pattern appendix: own block forced, the rest
+# by score; ties -> lower block id (fixed tie-break).
+@pytest.mark.parametrize("k", [1, 2, 4, 16, 64])
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_matches_sort_brute_force(k, ties):
+    T, nb = 200, 40
+    own = RNG.integers(0, nb, size=T)
+    sc = RNG.integers(0, 3, size=(T, nb)).astype(np.float64) if ties else RNG.standard_normal((T, nb))
+    got = oracle.slice_block_topk(sc, own, k)
+    ref = bf.topk(sc, own, k)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_topk_invariants():
+    T, nb, k = 500, 64, 16
+    own = RNG.integers(0, nb, size=T)
+    sc = RNG.standard_normal((T, nb))
+    sel = oracle.slice_block_topk(sc, own, k)
+    for t in range(T):
+        row = sel[t]
+        valid = row[row >= 0]
+        assert own[t] in valid                               # own block always present
+        assert len(valid) == min(k, own[t] + 1)              # fixed budget
+        assert np.all(valid <= own[t])                       # causal: no future block
+        assert np.all(np.diff(valid) > 0)                    # ascending, distinct
+        assert np.all(row[len(valid):] == -1)                # -1 padding at the end
+
+
+def test_topk_all_equal_pins_tie_break():
+    nb, k = 30, 5
+    own = np.array([29, 10, 3, 0])
+    sc = np.full((4, nb), 0.5)
+    sel = oracle.slice_block_topk(sc, own, k)
+    np.testing.assert_array_equal(sel[0], [0, 1, 2, 3, 29])
+    np.testing.assert_array_equal(sel[1], [0, 1, 2, 3, 10])
+    np.testing.assert_array_equal(sel[2], [0, 1, 2, 3, -1])
+    np.testing.assert_array_equal(sel[3], [0, -1, -1, -1, -1])
+
+
+def test_topk_signed_zero_is_a_tie():
+    sc = np.array([[1.0, -0.0, 0.0, 0.0, 0.0]])
+    sc[0, 0] = -1.0
+    sel = oracle.slice_block_topk(sc, np.array([4]), 2)
+    np.testing.assert_array_equal(sel[0], [1, 4])        # -0.0 == +0.0, lower id wins
+
+
+def test_topk_boosted_block_always_selected():
+    nb, k = 50, 4
+    own = np.arange(nb)
+    sc = RNG.standard_normal((nb, nb))
+    sc[:, 17] += 100.0
+    sel = oracle.slice_block_topk(sc, own, k)
+    for t in range(18, nb):
+        assert 17 in sel[t]
+
+
+def test_topk_k_at_least_nb_selects_every_causal_block():
+    nb = 12
+    own = np.arange(nb)
+    sel = oracle.slice_block_topk(RNG.standard_normal((nb, nb)), own, nb)
+    for t in range(nb):
+        np.testing.assert_array_equal(sel[t][: t + 1], np.arange(t + 1))
+
+
+# ------------------------------------------------------------------ inversion
+# "Kernel 创新：Outer Gather Q": gather, per KV block, every query that chose it.
+def test_invert_matches_brute_force_and_round_trips():
+    T, nb, k = 300, 20, 6
+    own = np.minimum(np.arange(T) // 15, nb - 1)
+    sel = oracle.slice_block_topk(RNG.standard_normal((T, nb)), own, k)
+    off, ent = oracle.slice_invert(sel, nb)
+    roff, rent = bf.invert(sel, nb)
+    np.testing.assert_array_equal(off, roff)
+    np.testing.assert_array_equal(ent, rent)
+    assert off[-1] == np.sum(sel >= 0)
+    for b in range(nb):
+        lst = ent[off[b]:off[b + 1]]
+        assert np.all(np.diff(lst // k) > 0)                 # ascending t, one slot per t
+        assert np.all(sel.reshape(-1)[lst] == b)              # every entry maps back to b
+
+
+# ------------------------------------------------------------------ attention
+# "第二步：精算": exact softmax attention restricted to the chosen blocks.
+def _rand_attn(N, T, G, d):
+    return (RNG.standard_normal((T, G, d)), RNG.standard_normal((N, d)),
+            RNG.standard_normal((N, d)))
+
+
+def test_attention_matches_dense_masked_brute_force():
+    N, T, G, d, B, k = 70, 33, 3, 8, 8, 3
+    q, K, V = _rand_attn(N, T, G, d)
+    pos = _pos(N, T)
+    own = pos // B
+    sel = oracle.slice_block_topk(RNG.standard_normal((T, (N + B - 1) // B)), own, k)
+    got = oracle.slice_attention(q, pos, sel, K, V, B, 0.37)
+    ref = bf.attention(q, K, V, pos, sel, B, 0.37)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_full_budget_is_dense_causal_sdpa():
+    # k >= nb: MSA reduces to dense causal attention (torch SDPA, fp64, explicit mask
+    # because queries are the LAST T positions).
+    N, T, G, d, B = 96, 40, 4, 16, 16
+    nb = N // B
+    q, K, V = _rand_attn(N, T, G, d)
+    pos = _pos(N, T)
+    sel = oracle.slice_block_topk(np.zeros((T, nb)), pos // B, nb)
+    got = oracle.slice_attention(q, pos, sel, K, V, B, 1 / np.sqrt(d))
+    qt = torch.from_numpy(q).permute(1, 0, 2)                 # [G, T, d]
+    Kt = torch.from_numpy(K)[None].expand(G, N, d)
+    Vt = torch.from_numpy(V)[None].expand(G, N, d)
+    mask = torch.from_numpy(np.arange(N)[None, :] <= pos[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mask)
+    np.testing.assert_allclose(got, ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_k1_is_block_local_causal():
+    N, T, G, d, B = 64, 64, 2, 4, 16
+    q, K, V = _rand_attn(N, T, G, d)
+    pos = _pos(N, T)
+    sel = oracle.slice_block_topk(RNG.standard_normal((T, N // B)), pos // B, 1)
+    got = oracle.slice_attention(q, pos, sel, K, V, B, 0.5)
+    for t in range(T):
+        lo = (pos[t] // B) * B
+        keys = np.arange(lo, pos[t] + 1)
+        for h in range(G):
+            lg = 0.5 * K[keys] @ q[t, h]
+            w = np.exp(lg - lg.max()); w /= w.sum()
+            np.testing.assert_allclose(got[t, h], w @ V[keys], rtol=1e-12, atol=1e-13)
+
+
+def test_partials_merge_equals_direct_attention():
+    # log-sum-exp merge over the per-block parts == softmax over the union
+    N, T, G, d, B, k = 200, 60, 2, 8, 16, 5
+    q, K, V = _rand_attn(N, T, G, d)
+    pos = _pos(N, T)
+    sel = oracle.slice_block_topk(RNG.standard_normal((T, (N + B - 1) // B)), pos // B, k)
+    lse, Op = oracle.slice_attention_partials(q, pos, sel, K, V, B, 0.3)
+    merged = oracle.slice_lse_merge(lse, Op)
+    direct = oracle.slice_attention(q, pos, sel, K, V, B, 0.3)
+    np.testing.assert_allclose(merged, direct, rtol=1e-11, atol=1e-13)
+    # single-slot lse is the textbook log-sum-exp of that block's logits
+    t, i, h = 59, 0, 1
+    b = sel[t, i]
+    keys = np.arange(b * B, min((b + 1) * B, pos[t] + 1))
+    lg = 0.3 * K[keys] @ q[t, h]
+    assert abs(lse[t, i, h] - (lg.max() + np.log(np.exp(lg - lg.max()).sum()))) < 1e-12
+    assert np.all(np.isneginf(lse[sel == -1]))
+
+
+def test_merge_of_random_partition_is_softmax_of_union():
+    # arbitrary partition of one key set into 4 parts, merged with the oracle's merge
+    n, d = 57, 6
+    lg = RNG.standard_normal(n) * 3
+    V = RNG.standard_normal((n, d))
+    part = RNG.integers(0, 4, size=n)
+    lse = np.full((1, 4, 1), -np.inf)
+    Op = np.zeros((1, 4, 1, d))
+    for i in range(4):
+        m = part == i
+        if m.any():
+            lse[0, i, 0] = np.log(np.exp(lg[m]).sum())
+            w = np.exp(lg[m] - lse[0, i, 0])
+            Op[0, i, 0] = w @ V[m]
+    out = oracle.slice_lse_merge(lse, Op)
+    w = np.exp(lg - lg.max()); w /= w.sum()
+    np.testing.assert_allclose(out[0, 0], w @ V, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ whole tensors
+def test_whole_tensor_walk_matches_slices():
+    S, Hkv, G, N, T, d, dI, B, k = 2, 2, 2, 40, 24, 4, 3, 8, 2
+    q = RNG.standard_normal((S, T, Hkv * G, d))
+    K = RNG.standard_normal((S, Hkv, N, d))
+    V = RNG.standard_normal((S, Hkv, N, d))
+    qI = RNG.standard_normal((S, Hkv, T, dI))
+    kI = RNG.standard_normal((S, Hkv, N, dI))
+    sc = oracle.index_scores(qI, kI, N, B)
+    sel = oracle.block_topk(sc, N, B, k)
+    out = oracle.attention(q, K, V, sel, B, 0.5)
+    pos = _pos(N, T)
+    for s in range(S):
+        for g in range(Hkv):
+            ref_sc = bf.scores(qI[s, g], kI[s, g], pos, B)
+            np.testing.assert_allclose(np.nan_to_num(sc[s, g]), np.nan_to_num(ref_sc), rtol=1e-12)
+            ref_sel = bf.topk(ref_sc, pos // B, k)
+            np.testing.assert_array_equal(sel[s, g], ref_sel)
+            ref = bf.attention(q[s][:, g * G:(g + 1) * G], K[s, g], V[s, g], pos, ref_sel, B, 0.5)
+            np.testing.assert_allclose(out[s][:, g * G:(g + 1) * G], ref, rtol=1e-11, atol=1e-13)
