@@ -1,0 +1,240 @@
+"""Python binding of libmsa.so -- MiniMax Sparse Attention (MSA) on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.  PyTorch
+is used for device memory and streams.  The names mirror the C ABI in
+include/msa.h (without the ``msa_`` prefix); tensors are passed as torch tensors
+(their ``data_ptr()``) or raw integer device addresses.
+
+If the library is missing the import still succeeds, but every call raises
+``MSAError``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_OK, MSA_ERR_INVALID_ARGUMENT, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_DEVICE = range(5)
+MSA_F32, MSA_BF16 = 0, 1
+MSA_CALL_INVERT, MSA_CALL_PREFILL, MSA_CALL_DECODE = 2, 3, 4
+
+EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_invert_selection", "msa_sparse_attn_prefill",
+            "msa_sparse_attn_decode", "msa_workspace_bytes", "msa_status_string",
+            "msa_last_error_message", "msa_profiler_enable", "msa_profiler_read")
+
+
+class MSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    """msa_problem (include/msa.h)."""
+    _fields_ = [("batch", ctypes.c_int32), ("num_q", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+    @property
+    def nb(self) -> int:
+        return (self.kv_len + self.block_size - 1) // self.block_size
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    def __repr__(self):
+        return "Problem(" + ", ".join("%s=%r" % (f, getattr(self, f)) for f, _ in self._fields_) + ")"
+
+
+def problem(batch, num_q, kv_len, num_heads, num_kv_heads, head_dim, index_dim, topk,
+            dtype=MSA_BF16, block_size=128, softmax_scale=0.0) -> Problem:
+    return Problem(batch, num_q, kv_len, num_heads, num_kv_heads, head_dim, index_dim, block_size,
+                   topk, dtype, softmax_scale)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmsa.so (raises MSAError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MSAError(MSA_ERR_DEVICE, "libmsa.so not built at %s (run __graft_entry__.build())" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        PP = ctypes.POINTER(Problem)
+        st = ctypes.c_int
+        L.msa_index_scores.argtypes = [PP, P, P, P, P]
+        L.msa_block_topk.argtypes = [PP, P, P, P]
+        L.msa_invert_selection.argtypes = [PP, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_sparse_attn_prefill.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_sparse_attn_decode.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
+        for f in ("msa_index_scores", "msa_block_topk", "msa_invert_selection",
+                  "msa_sparse_attn_prefill", "msa_sparse_attn_decode"):
+            getattr(L, f).restype = st
+        L.msa_workspace_bytes.argtypes = [PP, ctypes.c_int]
+        L.msa_workspace_bytes.restype = ctypes.c_size_t
+        L.msa_status_string.argtypes = [ctypes.c_int]
+        L.msa_status_string.restype = ctypes.c_char_p
+        L.msa_last_error_message.argtypes = []
+        L.msa_last_error_message.restype = ctypes.c_char_p
+        L.msa_profiler_enable.argtypes = [ctypes.c_int]
+        L.msa_profiler_enable.restype = st
+        L.msa_profiler_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
+        L.msa_profiler_read.restype = st
+        _lib = L
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return ctypes.c_void_p(x)
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    for t in tensors:
+        if hasattr(t, "is_cuda") and t.is_cuda:
+            import torch
+            return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def _check(status: int):
+    if status != MSA_OK:
+        L = lib()
+        raise MSAError(status, "%s: %s" % (L.msa_status_string(status).decode(),
+                                           L.msa_last_error_message().decode()))
+
+
+def status_string(status: int) -> str:
+    return lib().msa_status_string(status).decode()
+
+
+def last_error_message() -> str:
+    return lib().msa_last_error_message().decode()
+
+
+def workspace_bytes(prob: Problem, which_call: int) -> int:
+    return int(lib().msa_workspace_bytes(ctypes.byref(prob), which_call))
+
+
+def index_scores(prob: Problem, q_idx, k_idx, scores, stream=None) -> None:
+    _check(lib().msa_index_scores(ctypes.byref(prob), _ptr(q_idx), _ptr(k_idx), _ptr(scores),
+                                  _stream(stream, q_idx)))
+
+
+def block_topk(prob: Problem, scores, sel, stream=None) -> None:
+    _check(lib().msa_block_topk(ctypes.byref(prob), _ptr(scores), _ptr(sel), _stream(stream, scores)))
+
+
+def invert_selection(prob: Problem, sel, csr_offsets, csr_entries, workspace, workspace_bytes_: int,
+                     stream=None) -> None:
+    _check(lib().msa_invert_selection(ctypes.byref(prob), _ptr(sel), _ptr(csr_offsets), _ptr(csr_entries),
+                                      _ptr(workspace), workspace_bytes_, _stream(stream, sel)))
+
+
+def sparse_attn_prefill(prob: Problem, q, k, v, csr_offsets, csr_entries, sel, out, workspace,
+                        workspace_bytes_: int, stream=None) -> None:
+    _check(lib().msa_sparse_attn_prefill(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(csr_offsets),
+                                         _ptr(csr_entries), _ptr(sel), _ptr(out), _ptr(workspace),
+                                         workspace_bytes_, _stream(stream, q)))
+
+
+def sparse_attn_decode(prob: Problem, q, k_cache, v_cache, sel, out, workspace, workspace_bytes_: int,
+                       stream=None) -> None:
+    _check(lib().msa_sparse_attn_decode(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(sel), _ptr(out), _ptr(workspace), workspace_bytes_,
+                                        _stream(stream, q)))
+
+
+def profiler_enable(on: bool) -> None:
+    _check(lib().msa_profiler_enable(1 if on else 0))
+
+
+def profiler_read(kernel: str | None = None, reset: bool = True):
+    """(total device ms, launches) of `kernel` (None = all) since the last reset."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().msa_profiler_read(kernel.encode() if kernel else None, ctypes.byref(ms), ctypes.byref(n),
+                                   1 if reset else 0))
+    return ms.value, n.value
+
+
+# ------------------------------------------------------------------ allocating helpers
+@dataclass
+class PrefillBuffers:
+    scores: object
+    sel: object
+    csr_offsets: object
+    csr_entries: object
+    ws_invert: object
+    ws_prefill: object
+    out: object
+
+
+def alloc_prefill(prob: Problem, device="cuda") -> PrefillBuffers:
+    """Allocate (torch) every output and workspace of one prefill pass."""
+    import torch
+    S, T, Hkv, nb, k = prob.batch, prob.num_q, prob.num_kv_heads, prob.nb, prob.topk
+    odt = torch.bfloat16 if prob.dtype == MSA_BF16 else torch.float32
+    wi = max(workspace_bytes(prob, MSA_CALL_INVERT), 1)
+    wp = max(workspace_bytes(prob, MSA_CALL_PREFILL), 1)
+    return PrefillBuffers(
+        scores=torch.empty((S, Hkv, T, nb), dtype=torch.float32, device=device),
+        sel=torch.empty((S, Hkv, T, k), dtype=torch.int32, device=device),
+        csr_offsets=torch.empty((S, Hkv, nb + 1), dtype=torch.int32, device=device),
+        csr_entries=torch.empty((S * Hkv * T * k,), dtype=torch.int32, device=device),
+        ws_invert=torch.empty((wi,), dtype=torch.uint8, device=device),
+        ws_prefill=torch.empty((wp,), dtype=torch.uint8, device=device),
+        out=torch.empty((S, T, prob.num_heads, prob.head_dim), dtype=odt, device=device))
+
+
+def run_prefill(prob: Problem, q, k, v, q_idx, k_idx, bufs: PrefillBuffers, stream=None) -> None:
+    """The five-stage prefill pass: scores -> top-k -> inversion -> attention + merge."""
+    index_scores(prob, q_idx, k_idx, bufs.scores, stream)
+    block_topk(prob, bufs.scores, bufs.sel, stream)
+    invert_selection(prob, bufs.sel, bufs.csr_offsets, bufs.csr_entries, bufs.ws_invert,
+                     bufs.ws_invert.numel(), stream)
+    sparse_attn_prefill(prob, q, k, v, bufs.csr_offsets, bufs.csr_entries, bufs.sel, bufs.out,
+                        bufs.ws_prefill, bufs.ws_prefill.numel(), stream)
+
+
+@dataclass
+class DecodeBuffers:
+    scores: object
+    sel: object
+    ws_decode: object
+    out: object
+
+
+def alloc_decode(prob: Problem, device="cuda") -> DecodeBuffers:
+    import torch
+    S, T, Hkv, nb, k = prob.batch, prob.num_q, prob.num_kv_heads, prob.nb, prob.topk
+    odt = torch.bfloat16 if prob.dtype == MSA_BF16 else torch.float32
+    wd = max(workspace_bytes(prob, MSA_CALL_DECODE), 1)
+    return DecodeBuffers(
+        scores=torch.empty((S, Hkv, T, nb), dtype=torch.float32, device=device),
+        sel=torch.empty((S, Hkv, T, k), dtype=torch.int32, device=device),
+        ws_decode=torch.empty((wd,), dtype=torch.uint8, device=device),
+        out=torch.empty((S, T, prob.num_heads, prob.head_dim), dtype=odt, device=device))
+
+
+def run_decode(prob: Problem, q, k_cache, v_cache, q_idx, k_idx, bufs: DecodeBuffers, stream=None) -> None:
+    """One decode step: scores -> top-k -> query-centric split-K attention + merge."""
+    index_scores(prob, q_idx, k_idx, bufs.scores, stream)
+    block_topk(prob, bufs.scores, bufs.sel, stream)
+    sparse_attn_decode(prob, q, k_cache, v_cache, bufs.sel, bufs.out, bufs.ws_decode,
+                       bufs.ws_decode.numel(), stream)

@@ -1,0 +1,400 @@
+// attention.hip -- a4/a5/a6: the main branch.  Exact softmax attention restricted to
+// the selected blocks (page "MSA 稀疏注意力三国杀：NSA / DSA / MoBA / MSA 四方案深度对比",
+// section 第二步：精算; MSA entry of "稀疏注意力速览（Sparse Attention，2019 ~ 2026）":
+// "Main Branch 只在这些块上做精确 softmax attention"), organised in the
+// Outer-Gather-Q order of section Kernel 创新：Outer Gather Q for prefill (the KV block
+// is the outer loop, staged on chip once for every query row that chose it) and
+// query-centric split-K for decode (one workgroup per (query row, selected block)).
+//
+// Both produce per-(query row, slot, head) partials over ONE block:
+//   lse = m + log(l),  O = (sum_j exp(s_j - m) v_j) / l,   s_j = scale * q . k_j,
+// over the block's keys j <= p_t, and lse_merge combines the slots of a row:
+//   out = sum_i exp(lse_i - L) O_i,  L = log sum_i exp(lse_i).
+// Partial index of (s, t, g, slot): pidx = ((s*T + t)*Hkv + g)*k + slot;
+//   part_lse[pidx*G + h], part_o[(pidx*G + h)*d + c].
+//
+// This file holds the work-list builder, the VALU kernels (float32 problems, and
+// any problem the matrix-core kernel does not cover), the decode kernel and the
+// merge; the bf16 matrix-core prefill kernel is in attention_mfma.hip.
+#include "msa_internal.hpp"
+#include "scan.hpp"
+
+namespace msa {
+
+// matrix-core Outer-Gather-Q kernel (attention_mfma.hip)
+bool ogq_mfma_supported(const Dims& D);
+int ogq_mfma_rows_per_item(const Dims& D);
+hipError_t launch_ogq_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const int4* worklist, const int* n_items, int64_t grid,
+                           const int32_t* entries, float* part_lse, uint16_t* part_o, hipStream_t st);
+
+namespace {
+
+constexpr int kSimpleRows = 16;  // query rows per work item of the VALU kernel
+
+// ------------------------------------------------------------------ work list
+// Work item = (sgb = (s*Hkv + g)*nb + b, first csr position, row count <= R).
+__global__ void __launch_bounds__(256) wl_count(Dims D, const int32_t* __restrict__ off,
+                                                int* __restrict__ items, int R) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nsgb = (int64_t)D.S * D.Hkv * D.nb;
+  if (i >= nsgb) return;
+  const int64_t sg = i / D.nb;
+  const int b = (int)(i % D.nb);
+  const int64_t o = sg * (D.nb + 1) + b;
+  const int len = off[o + 1] - off[o];
+  items[i] = (len + R - 1) / R;
+}
+
+__global__ void __launch_bounds__(256) wl_emit(Dims D, const int32_t* __restrict__ off,
+                                               const int* __restrict__ items,
+                                               const int* __restrict__ itempos,
+                                               int4* __restrict__ wl, int R) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nsgb = (int64_t)D.S * D.Hkv * D.nb;
+  if (i >= nsgb) return;
+  const int64_t sg = i / D.nb;
+  const int b = (int)(i % D.nb);
+  const int64_t o = sg * (D.nb + 1) + b;
+  const int beg = off[o];
+  const int len = off[o + 1] - beg;
+  const int n = items[i];
+  const int p0 = itempos[i];
+  for (int j = 0; j < n; ++j) wl[p0 + j] = make_int4((int)i, beg + j * R, min(R, len - j * R), 0);
+}
+
+// ------------------------------------------------------------------ VALU block kernel
+// Stages K (as float, row stride DH+1: conflict-free lane-per-key reads) and V of one
+// block in LDS, then one wave per (row, head) pair computes the block-local softmax.
+template <typename T, int DH>
+struct BlockLds {
+  float K[128][DH + 1];
+  T V[128][DH];
+  float P[4][128];
+  float Q[4][DH];
+};
+
+template <typename T, int DH>
+__device__ void stage_block(const Dims& D, BlockLds<T, DH>& L, const T* k, const T* v, int64_t sg,
+                            int b) {
+  const int j0 = b * 128;
+  const int nvalid = min(128, D.N - j0);
+  const T* kb = k + (sg * D.N + j0) * DH;
+  const T* vb = v + (sg * D.N + j0) * DH;
+  for (int i = threadIdx.x; i < 128 * DH; i += 256) {
+    const int row = i / DH, c = i % DH;
+    const bool ok = row < nvalid;
+    L.K[row][c] = ok ? ldf(kb, i) : 0.0f;
+    L.V[row][c] = ok ? vb[i] : T(0);
+  }
+}
+
+// One (row t, slot, head h) against the staged block.
+template <typename T, typename PT, int DH>
+__device__ void attend_one(const Dims& D, BlockLds<T, DH>& L, const T* q, int s, int g, int b, int t,
+                           int slot, int h, float* part_lse, PT* part_o) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int p = D.pos0 + t;
+  const T* qv = q + (((int64_t)s * D.T + t) * D.H + g * D.G + h) * DH;
+  for (int c = lane; c < DH; c += 64) L.Q[wave][c] = ldf(qv, c);
+  __builtin_amdgcn_wave_barrier();
+  float lg[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = lane + 64 * u;
+    lg[u] = -INFINITY;
+    if (b * 128 + j <= p) {
+      float acc = 0.0f;
+      for (int c = 0; c < DH; ++c) acc = fmaf(L.Q[wave][c], L.K[j][c], acc);
+      lg[u] = acc * D.scale;
+    }
+  }
+  const float m = wave_max(fmaxf(lg[0], lg[1]));
+  const float p0 = lg[0] == -INFINITY ? 0.0f : exp2f((lg[0] - m) * kLog2e);
+  const float p1 = lg[1] == -INFINITY ? 0.0f : exp2f((lg[1] - m) * kLog2e);
+  const float l = wave_sum(p0 + p1);
+  L.P[wave][lane] = p0;
+  L.P[wave][lane + 64] = p1;
+  __builtin_amdgcn_wave_barrier();
+  const int64_t pidx = (((int64_t)s * D.T + t) * D.Hkv + g) * D.k + slot;
+  const float inv = 1.0f / l;
+  for (int c = lane; c < DH; c += 64) {
+    float acc = 0.0f;
+    for (int j = 0; j < 128; ++j) acc = fmaf(L.P[wave][j], ldf(&L.V[0][0], j * DH + c), acc);
+    stf(part_o, (pidx * D.G + h) * DH + c, acc * inv);
+  }
+  if (lane == 0) part_lse[pidx * D.G + h] = m + log2f(l) * kLn2;
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <typename T, typename PT, int DH>
+__global__ void __launch_bounds__(256) ogq_simple(Dims D, const T* __restrict__ q, const T* __restrict__ k,
+                                                  const T* __restrict__ v, const int4* __restrict__ wl,
+                                                  const int* __restrict__ n_items,
+                                                  const int32_t* __restrict__ entries,
+                                                  float* __restrict__ part_lse, PT* __restrict__ part_o) {
+  extern __shared__ unsigned char smem[];
+  BlockLds<T, DH>& L = *reinterpret_cast<BlockLds<T, DH>*>(smem);
+  if ((int)blockIdx.x >= *n_items) return;
+  const int4 w = wl[blockIdx.x];
+  const int64_t sg = w.x / D.nb;
+  const int b = w.x % D.nb;
+  const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
+  stage_block<T, DH>(D, L, k, v, sg, b);
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  for (int pr = wave; pr < w.z * D.G; pr += 4) {
+    const int e = entries[w.y + pr / D.G];
+    attend_one<T, PT, DH>(D, L, q, s, g, b, e / D.k, e % D.k, pr % D.G, part_lse, part_o);
+  }
+}
+
+// Decode: one workgroup per (row = (s, t, g), slot); unused slots get lse = -inf.
+template <typename T, int DH>
+__global__ void __launch_bounds__(256) decode_simple(Dims D, const T* __restrict__ q, const T* __restrict__ k,
+                                                     const T* __restrict__ v, const int32_t* __restrict__ sel,
+                                                     float* __restrict__ part_lse, float* __restrict__ part_o) {
+  extern __shared__ unsigned char smem[];
+  BlockLds<T, DH>& L = *reinterpret_cast<BlockLds<T, DH>*>(smem);
+  const int slot = blockIdx.y;
+  const int64_t row = blockIdx.x;  // ((s*T + t)*Hkv + g)
+  const int g = (int)(row % D.Hkv);
+  const int t = (int)((row / D.Hkv) % D.T);
+  const int s = (int)(row / ((int64_t)D.Hkv * D.T));
+  const int64_t sg = (int64_t)s * D.Hkv + g;
+  const int b = sel[(sg * D.T + t) * D.k + slot];
+  if (b < 0) {
+    const int64_t pidx = row * D.k + slot;
+    for (int h = threadIdx.x; h < D.G; h += 256) part_lse[pidx * D.G + h] = -INFINITY;
+    return;
+  }
+  stage_block<T, DH>(D, L, k, v, sg, b);
+  __syncthreads();
+  for (int h = threadIdx.x >> 6; h < D.G; h += 4)
+    attend_one<T, float, DH>(D, L, q, s, g, b, t, slot, h, part_lse, part_o);
+}
+
+// ------------------------------------------------------------------ merge
+__device__ __forceinline__ void load8f(const float* p, float* o) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 c = *reinterpret_cast<const float4*>(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = c.x; o[5] = c.y; o[6] = c.z; o[7] = c.w;
+}
+__device__ __forceinline__ void load8f(const uint16_t* p, float* o) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    o[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float* v) {
+  uint4 u;
+  u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+  u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+
+// One wave per row (s, t, g); each lane merges 8 consecutive outputs at a time.
+template <typename T, typename PT>
+__global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* __restrict__ sel,
+                                                        const float* __restrict__ part_lse,
+                                                        const PT* __restrict__ part_o, T* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
+  if (row >= rows) return;
+  const int g = (int)(row % D.Hkv);
+  const int t = (int)((row / D.Hkv) % D.T);
+  const int s = (int)(row / ((int64_t)D.Hkv * D.T));
+  const int32_t* sl = sel + (((int64_t)s * D.Hkv + g) * D.T + t) * D.k;
+  const int GD = D.G * D.d;
+  T* orow = out + (((int64_t)s * D.T + t) * D.H + g * D.G) * D.d;
+  for (int c8 = lane; c8 * 8 < GD; c8 += 64) {
+    const int h = c8 * 8 / D.d;
+    float m = -INFINITY;
+    for (int i = 0; i < D.k; ++i)
+      if (sl[i] >= 0) m = fmaxf(m, part_lse[(row * D.k + i) * D.G + h]);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float tot = 0.0f;
+    for (int i = 0; i < D.k; ++i) {
+      if (sl[i] < 0) continue;
+      const float w = exp2f((part_lse[(row * D.k + i) * D.G + h] - m) * kLog2e);
+      tot += w;
+      float o[8];
+      load8f(part_o + (row * D.k + i) * GD + c8 * 8, o);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = fmaf(w, o[u], acc[u]);
+    }
+    const float inv = 1.0f / tot;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] *= inv;
+    store8(orow + c8 * 8, acc);
+  }
+}
+
+template <typename T>
+size_t ogq_partial_elem() { return sizeof(T); }
+
+struct PrefillWs {
+  int* items;
+  int* itempos;
+  int* n_items;
+  void* scan_ws;
+  int4* wl;
+  float* part_lse;
+  void* part_o;
+  int64_t ub;
+};
+
+int rows_per_item(const Dims& D) {
+  return ogq_mfma_supported(D) ? ogq_mfma_rows_per_item(D) : kSimpleRows;
+}
+
+PrefillWs prefill_layout(const Dims& D, void* base, size_t* total) {
+  const int64_t nsgb = (int64_t)D.S * D.Hkv * D.nb;
+  const int64_t npart = (int64_t)D.S * D.T * D.Hkv * D.k;
+  const int R = rows_per_item(D);
+  PrefillWs w;
+  w.ub = nsgb + (npart + R - 1) / R;
+  unsigned char* p = static_cast<unsigned char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    void* r = p ? p + off : nullptr;
+    off += align_up(bytes, 256);
+    return r;
+  };
+  w.items = static_cast<int*>(take(nsgb * sizeof(int)));
+  w.itempos = static_cast<int*>(take(nsgb * sizeof(int)));
+  w.n_items = static_cast<int*>(take(sizeof(int)));
+  w.scan_ws = take(scan_workspace_bytes(nsgb));
+  w.wl = static_cast<int4*>(take(w.ub * sizeof(int4)));
+  w.part_lse = static_cast<float*>(take(npart * D.G * sizeof(float)));
+  const size_t pelem = D.dtype == MSA_BF16 ? 2 : 4;
+  w.part_o = take((size_t)npart * D.G * D.d * pelem);
+  *total = off;
+  return w;
+}
+
+template <typename T, typename PT, int DH>
+hipError_t launch_ogq_simple_t(const Dims& D, const void* q, const void* k, const void* v,
+                               const PrefillWs& w, const int32_t* entries, hipStream_t st) {
+  const size_t lds = sizeof(BlockLds<T, DH>);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ogq_simple<T, PT, DH>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  LaunchScope scope("ogq_simple", st);
+  hipLaunchKernelGGL((ogq_simple<T, PT, DH>), dim3((unsigned)w.ub), dim3(256), lds, st, D,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), w.wl,
+                     w.n_items, entries, w.part_lse, static_cast<PT*>(w.part_o));
+  return hipGetLastError();
+}
+
+template <typename T, int DH>
+hipError_t launch_decode_t(const Dims& D, const void* q, const void* k, const void* v, const int32_t* sel,
+                           float* part_lse, float* part_o, hipStream_t st) {
+  const size_t lds = sizeof(BlockLds<T, DH>);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_simple<T, DH>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
+  LaunchScope scope("decode_simple", st);
+  hipLaunchKernelGGL((decode_simple<T, DH>), dim3((unsigned)rows, (unsigned)D.k), dim3(256), lds, st, D,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sel,
+                     part_lse, part_o);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part_lse, const void* part_o,
+                            int part_o_is_bf16, void* out, hipStream_t st) {
+  const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  LaunchScope scope("lse_merge", st);
+  if (D.dtype == MSA_BF16) {
+    if (part_o_is_bf16)
+      hipLaunchKernelGGL((lse_merge_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, D, sel, part_lse,
+                         static_cast<const uint16_t*>(part_o), static_cast<uint16_t*>(out));
+    else
+      hipLaunchKernelGGL((lse_merge_kernel<uint16_t, float>), grid, dim3(256), 0, st, D, sel, part_lse,
+                         static_cast<const float*>(part_o), static_cast<uint16_t*>(out));
+  } else {
+    hipLaunchKernelGGL((lse_merge_kernel<float, float>), grid, dim3(256), 0, st, D, sel, part_lse,
+                       static_cast<const float*>(part_o), static_cast<float*>(out));
+  }
+  return hipGetLastError();
+}
+
+size_t prefill_workspace_bytes(const Dims& D) {
+  size_t total = 0;
+  (void)prefill_layout(D, nullptr, &total);
+  return total;
+}
+
+hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const void* v, const int32_t* off,
+                          const int32_t* entries, const int32_t* sel, void* out, void* ws, hipStream_t st) {
+  size_t total = 0;
+  const PrefillWs w = prefill_layout(D, ws, &total);
+  const int64_t nsgb = (int64_t)D.S * D.Hkv * D.nb;
+  const int R = rows_per_item(D);
+  const unsigned g256 = (unsigned)((nsgb + 255) / 256);
+  {
+    LaunchScope s("wl_count", st);
+    hipLaunchKernelGGL(wl_count, dim3(g256), dim3(256), 0, st, D, off, w.items, R);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_exclusive_scan(w.items, w.itempos, nsgb, w.n_items, w.scan_ws, st);
+  if (e != hipSuccess) return e;
+  {
+    LaunchScope s("wl_emit", st);
+    hipLaunchKernelGGL(wl_emit, dim3(g256), dim3(256), 0, st, D, off, w.items, w.itempos, w.wl, R);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ogq_mfma_supported(D)) {
+    e = launch_ogq_mfma(D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                        static_cast<const uint16_t*>(v), w.wl, w.n_items, w.ub, entries, w.part_lse,
+                        static_cast<uint16_t*>(w.part_o), st);
+  } else if (D.dtype == MSA_BF16) {
+    e = D.d == 64 ? launch_ogq_simple_t<uint16_t, uint16_t, 64>(D, q, k, v, w, entries, st)
+                  : launch_ogq_simple_t<uint16_t, uint16_t, 128>(D, q, k, v, w, entries, st);
+  } else {
+    e = D.d == 64 ? launch_ogq_simple_t<float, float, 64>(D, q, k, v, w, entries, st)
+                  : launch_ogq_simple_t<float, float, 128>(D, q, k, v, w, entries, st);
+  }
+  if (e != hipSuccess) return e;
+  return launch_lse_merge(D, sel, w.part_lse, w.part_o, D.dtype == MSA_BF16, out, st);
+}
+
+size_t decode_workspace_bytes(const Dims& D) {
+  const int64_t npart = (int64_t)D.S * D.T * D.Hkv * D.k * D.G;
+  return align_up((size_t)npart * sizeof(float), 256) + align_up((size_t)npart * D.d * sizeof(float), 256);
+}
+
+hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void* v, const int32_t* sel,
+                         void* out, void* ws, hipStream_t st) {
+  const int64_t npart = (int64_t)D.S * D.T * D.Hkv * D.k * D.G;
+  float* part_lse = static_cast<float*>(ws);
+  float* part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
+                                           align_up((size_t)npart * sizeof(float), 256));
+  hipError_t e;
+  if (D.dtype == MSA_BF16)
+    e = D.d == 64 ? launch_decode_t<uint16_t, 64>(D, q, k, v, sel, part_lse, part_o, st)
+                  : launch_decode_t<uint16_t, 128>(D, q, k, v, sel, part_lse, part_o, st);
+  else
+    e = D.d == 64 ? launch_decode_t<float, 64>(D, q, k, v, sel, part_lse, part_o, st)
+                  : launch_decode_t<float, 128>(D, q, k, v, sel, part_lse, part_o, st);
+  if (e != hipSuccess) return e;
+  return launch_lse_merge(D, sel, part_lse, part_o, 0, out, st);
+}
+
+}  // namespace msa

@@ -1,0 +1,169 @@
+// index_scores_mfma.hip -- a1 for bf16 prefill on gfx950 matrix cores.
+// Computes the index scores of page "MSA 稀疏注意力三国杀：NSA / DSA / MoBA / MSA
+// 四方案深度对比", section 第一步：粗筛 items 1-2 (token scores, max over each 128-token
+// block), causal inside the query's own block.
+//
+// Work unit (one workgroup, 4 waves): 256 consecutive query rows of one
+// (sequence, group) x a chunk of up to kChunk key blocks.  Each wave owns 64
+// queries as two 32-query MFMA B-operands held in registers for the whole unit.
+// Key blocks (128 keys x dI bf16) are staged through LDS, double buffered, with
+// a 16-byte row pad so the per-lane 16-byte reads are bank-conflict free.
+//
+// v_mfma_f32_32x32x16_bf16 with A = 32 keys, B = 32 queries: output column
+// n = lane % 32 is one query, so a lane's 16 accumulators are 16 keys of ONE
+// query and the block max is an in-register reduction plus one exchange with
+// lane ^ 32 (which holds the other 16 keys of each 32-key tile).  Output row i of
+// the 32x32 tile lives in lane half (i % 8) / 4, register 4 * (i / 8) + i % 4.
+// The contraction over dI may visit the index dimensions in any order as long
+// as A and B agree; here lane half h of k-step s covers dims [16 s + 8 h, +8).
+#include "msa_internal.hpp"
+
+namespace msa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kQW = 64;          // queries per wave
+constexpr int kQB = 4 * kQW;     // queries per workgroup
+constexpr int kChunk = 32;       // key blocks per workgroup
+constexpr int kBlk = 128;        // block size
+
+template <int DI>
+__global__ void __launch_bounds__(256) idx_scores_mfma(Dims D, const uint16_t* __restrict__ q_idx,
+                                                       const uint16_t* __restrict__ k_idx,
+                                                       float* __restrict__ scores) {
+  constexpr int KS = DI / 16;                 // MFMA k-steps
+  constexpr int ROWB = DI * 2 + 16;           // padded LDS bytes per key row
+  constexpr int CPR = DI / 8;                 // 16-byte chunks per key row
+  constexpr int PER_T = kBlk * CPR / 256;     // staging chunks per thread
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kBlk * ROWB];
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int n = lane & 31;
+  const int64_t sg = blockIdx.z;
+  const int t_first = blockIdx.x * kQB;
+  const int t_last = min(t_first + kQB - 1, D.T - 1);
+  const int bmax = (D.pos0 + t_last) / kBlk;
+  const int b0 = blockIdx.y * kChunk;
+  if (b0 > bmax) return;
+  const int b1 = min(b0 + kChunk - 1, bmax);
+
+  // B operands: this wave's 64 queries; pq = absolute position (INT_MAX if t >= T)
+  bf16x8 qf[2][KS];
+  int pq[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int t = t_first + wave * kQW + qt * 32 + n;
+    const int tc = t < D.T ? t : D.T - 1;
+    pq[qt] = t < D.T ? D.pos0 + t : 0x7FFFFFFF;
+    const uint16_t* qp = q_idx + (sg * D.T + tc) * DI + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qt][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+  }
+  // the wave's smallest own block: blocks >= it need the causal mask
+  const int t_w0 = min(t_first + wave * kQW, D.T - 1);
+  const int bmask = (D.pos0 + t_w0) / kBlk;
+
+  // my output row (lane half h writes query tile h) and its own block
+  const int t_out = t_first + wave * kQW + h * 32 + n;
+  const bool row_ok = t_out < D.T;
+  const int bt_out = row_ok ? (D.pos0 + t_out) / kBlk : -1;
+  float* out_row = scores + (sg * D.T + (row_ok ? t_out : 0)) * (int64_t)D.nb;
+  const bool vec_out = (D.nb & 3) == 0;
+
+  const uint16_t* kbase = k_idx + sg * (int64_t)D.N * DI;
+  uint4 stage[PER_T];
+  auto gload = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      const int row = c / CPR, col = c % CPR;
+      const int j = b * kBlk + row;
+      stage[u] = j < D.N ? *reinterpret_cast<const uint4*>(kbase + (int64_t)j * DI + col * 8)
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      const int row = c / CPR, col = c % CPR;
+      *reinterpret_cast<uint4*>(&lds[buf][row * ROWB + col * 16]) = stage[u];
+    }
+  };
+
+  gload(b0);
+  lstore(0);
+  __syncthreads();
+
+  float outv[4];
+  for (int b = b0; b <= b1; ++b) {
+    const int buf = (b - b0) & 1;
+    if (b < b1) gload(b + 1);
+    float rmax[2] = {-INFINITY, -INFINITY};
+    const bool masked = b >= bmask;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      bf16x8 af[KS];
+      const unsigned char* arow = &lds[buf][(kt * 32 + n) * ROWB + 16 * h];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(arow + ks * 32);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[qt][ks], acc, 0, 0, 0);
+        if (masked) {
+          const int jb = b * kBlk + kt * 32 + 4 * h;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[r] = -INFINITY;
+        }
+        float m = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+#pragma unroll
+        for (int r = 4; r < 16; r += 4) m = fmaxf(m, fmaxf(fmaxf(acc[r], acc[r + 1]), fmaxf(acc[r + 2], acc[r + 3])));
+        rmax[qt] = fmaxf(rmax[qt], m);
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) rmax[qt] = fmaxf(rmax[qt], __shfl_xor(rmax[qt], 32, 64));
+    const int slot = (b - b0) & 3;
+    outv[slot] = h == 0 ? rmax[0] : rmax[1];
+    if (slot == 3 || b == b1) {
+      const int bs = b - slot;
+      if (row_ok) {
+        if (vec_out && slot == 3 && b <= bt_out) {
+          *reinterpret_cast<float4*>(out_row + bs) = make_float4(outv[0], outv[1], outv[2], outv[3]);
+        } else {
+          for (int u = 0; u <= slot; ++u)
+            if (bs + u <= bt_out) out_row[bs + u] = outv[u];
+        }
+      }
+    }
+    if (b < b1) lstore(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_scores_mfma(const Dims& D, const uint16_t* q_idx, const uint16_t* k_idx,
+                                    float* scores, hipStream_t st) {
+  const int nq = (D.T + kQB - 1) / kQB;
+  const int bmax = (D.N - 1) / kBlk;
+  const int nchunk = bmax / kChunk + 1;
+  dim3 grid((unsigned)nq, (unsigned)nchunk, (unsigned)(D.S * D.Hkv));
+  LaunchScope scope("idx_scores_mfma", st);
+  switch (D.dI) {
+    case 32: hipLaunchKernelGGL(idx_scores_mfma<32>, grid, dim3(256), 0, st, D, q_idx, k_idx, scores); break;
+    case 64: hipLaunchKernelGGL(idx_scores_mfma<64>, grid, dim3(256), 0, st, D, q_idx, k_idx, scores); break;
+    default: hipLaunchKernelGGL(idx_scores_mfma<128>, grid, dim3(256), 0, st, D, q_idx, k_idx, scores); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

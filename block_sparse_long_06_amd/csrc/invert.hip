@@ -1,0 +1,165 @@
+// invert.hip -- a3: inversion of the per-query block selections into per-(sequence,
+// group, block) lists of query rows: the index behind the Outer-Gather-Q order of
+// page "MSA 稀疏注意力三国杀：NSA / DSA / MoBA / MSA 四方案深度对比", section
+// Kernel 创新：Outer Gather Q (KV block as the outer loop; gather every query that
+// chose the block).
+//
+// A stable counting sort, deterministic (no order depends on timing):
+//  1. count:   per chunk of kChunkT query rows of one (s, g), an LDS histogram over
+//              blocks, stored as cnt[(sg, b, chunk)] (chunk fastest);
+//  2. scan:    exclusive prefix sum over cnt in (sg, b, chunk) order = the global
+//              position of the first entry of each (sg, b, chunk);
+//  3. offsets: csr_offsets[sg, b] = position of (sg, b, chunk 0);
+//  4. scatter: one wave per chunk walks its rows 64 at a time (lane = row).  For
+//              each block, a 64-bit LDS mask of the lanes that chose it gives each
+//              lane its rank among the earlier lanes (popcount of the lower bits),
+//              and a per-block running count carries ranks across steps, so every
+//              list comes out in ascending row order.
+#include "msa_internal.hpp"
+#include "scan.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kChunkT = 1024;  // query rows per chunk
+
+__global__ void __launch_bounds__(256) invert_count(Dims D, const int32_t* __restrict__ sel,
+                                                    int* __restrict__ cnt, int nchunks) {
+  extern __shared__ int hist[];
+  const int c = blockIdx.x;
+  const int64_t sg = blockIdx.y;
+  for (int b = threadIdx.x; b < D.nb; b += 256) hist[b] = 0;
+  __syncthreads();
+  const int t0 = c * kChunkT;
+  const int t1 = min(t0 + kChunkT, D.T);
+  const int64_t e0 = (sg * D.T + t0) * D.k;
+  const int64_t e1 = (sg * D.T + t1) * D.k;
+  for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
+    const int b = sel[e];
+    if (b >= 0 && b < D.nb) atomicAdd(&hist[b], 1);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < D.nb; b += 256) cnt[(sg * D.nb + b) * nchunks + c] = hist[b];
+}
+
+__global__ void __launch_bounds__(256) invert_offsets(Dims D, const int* __restrict__ pos,
+                                                      const int* __restrict__ total,
+                                                      int32_t* __restrict__ offsets, int nchunks) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nsg = (int64_t)D.S * D.Hkv;
+  if (i >= nsg * (D.nb + 1)) return;
+  const int64_t sg = i / (D.nb + 1);
+  const int b = (int)(i % (D.nb + 1));
+  int v;
+  if (b < D.nb)
+    v = pos[(sg * D.nb + b) * nchunks];
+  else
+    v = sg + 1 < nsg ? pos[((sg + 1) * D.nb) * nchunks] : *total;
+  offsets[i] = v;
+}
+
+__global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __restrict__ sel,
+                                                     const int* __restrict__ pos,
+                                                     int32_t* __restrict__ entries, int nchunks) {
+  extern __shared__ unsigned char smem[];
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
+  uint16_t* run = reinterpret_cast<uint16_t*>(smem + sizeof(unsigned long long) * D.nb);
+  const int lane = threadIdx.x;
+  const int c = blockIdx.x;
+  const int64_t sg = blockIdx.y;
+  for (int b = lane; b < D.nb; b += 64) {
+    mask[b] = 0ull;
+    run[b] = 0;
+  }
+  __syncthreads();
+  const int t0 = c * kChunkT;
+  const int t1 = min(t0 + kChunkT, D.T);
+  const unsigned long long lower = (1ull << lane) - 1ull;
+  const int* pos_c = pos + (sg * D.nb) * nchunks + c;  // pos of (sg, b, c) = pos_c[b * nchunks]
+  for (int tb = t0; tb < t1; tb += 64) {
+    const int t = tb + lane;
+    const int32_t* srow = sel + (sg * D.T + t) * D.k;
+    // phase 1: mark the lanes that chose each block
+    for (int i = 0; i < D.k; ++i) {
+      const int b = t < t1 ? srow[i] : -1;
+      if (b >= 0 && b < D.nb) atomicOr(&mask[b], 1ull << lane);
+    }
+    __syncthreads();
+    // phase 2: rank among earlier lanes + running count -> global position
+    for (int i = 0; i < D.k; ++i) {
+      const int b = t < t1 ? srow[i] : -1;
+      if (b >= 0 && b < D.nb) {
+        const unsigned long long m = mask[b];
+        const int p = pos_c[(int64_t)b * nchunks] + run[b] + __popcll(m & lower);
+        entries[p] = t * D.k + i;
+      }
+    }
+    __syncthreads();
+    // phase 3: the lowest lane of each block advances its count and clears its mask
+    for (int i = 0; i < D.k; ++i) {
+      const int b = t < t1 ? srow[i] : -1;
+      if (b >= 0 && b < D.nb) {
+        const unsigned long long m = mask[b];
+        if ((m & lower) == 0ull) {
+          run[b] = (uint16_t)(run[b] + __popcll(m));
+          mask[b] = 0ull;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+static int invert_chunks(const Dims& D) { return (D.T + kChunkT - 1) / kChunkT; }
+
+size_t invert_workspace_bytes(const Dims& D) {
+  const int64_t m = (int64_t)D.S * D.Hkv * D.nb * invert_chunks(D);
+  return 2 * align_up((size_t)m * sizeof(int), 256) + align_up(sizeof(int), 256) +
+         scan_workspace_bytes(m);
+}
+
+hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, int32_t* entries,
+                         void* ws, hipStream_t st) {
+  const int nchunks = invert_chunks(D);
+  const int64_t nsg = (int64_t)D.S * D.Hkv;
+  const int64_t m = nsg * D.nb * nchunks;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  int* cnt = reinterpret_cast<int*>(w);
+  w += align_up((size_t)m * sizeof(int), 256);
+  int* pos = reinterpret_cast<int*>(w);
+  w += align_up((size_t)m * sizeof(int), 256);
+  int* total = reinterpret_cast<int*>(w);
+  w += align_up(sizeof(int), 256);
+  void* scan_ws = w;
+  {
+    LaunchScope s("invert_count", st);
+    hipLaunchKernelGGL(invert_count, dim3(nchunks, (unsigned)nsg), dim3(256), D.nb * sizeof(int), st, D,
+                       sel, cnt, nchunks);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_exclusive_scan(cnt, pos, m, total, scan_ws, st);
+  if (e != hipSuccess) return e;
+  {
+    const int64_t n = nsg * (D.nb + 1);
+    LaunchScope s("invert_offsets", st);
+    hipLaunchKernelGGL(invert_offsets, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, D, pos, total,
+                       offsets, nchunks);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    const size_t lds = (size_t)D.nb * (sizeof(unsigned long long) + sizeof(uint16_t));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(invert_scatter),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    LaunchScope s("invert_scatter", st);
+    hipLaunchKernelGGL(invert_scatter, dim3(nchunks, (unsigned)nsg), dim3(64), lds, st, D, sel, pos,
+                       entries, nchunks);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

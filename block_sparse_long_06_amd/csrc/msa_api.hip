@@ -1,0 +1,295 @@
+// msa_api.hip -- the C ABI of libmsa.so: host-side validation, workspace sizing,
+// error reporting, the opt-in kernel timer, and dispatch to the kernel launchers.
+// The operations themselves are documented in include/msa.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "msa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status fail(msa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+msa_status fail(msa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+msa_status ok() {
+  g_last_error.clear();
+  return MSA_OK;
+}
+
+msa_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MSA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool pow2_upto16(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// Validates the problem and fills D.  `need_index` / `need_main` select which
+// of the index-branch and main-branch fields must be supported.
+msa_status check_problem(const msa_problem* p, msa::Dims* D, bool need_index, bool need_main) {
+  if (p == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->batch < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", p->batch);
+  if (p->kv_len < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "kv_len must be >= 1 (got %d)", p->kv_len);
+  if (p->num_q < 1 || p->num_q > p->kv_len)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "num_q must be in [1, kv_len] (got %d, kv_len %d)",
+                p->num_q, p->kv_len);
+  if (p->num_kv_heads < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "num_kv_heads must be >= 1");
+  if (p->num_heads < 1 || p->num_heads % p->num_kv_heads != 0)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "num_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                p->num_heads, p->num_kv_heads);
+  if (p->block_size < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "block_size must be >= 1");
+  if (p->topk < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "topk must be >= 1 (got %d)", p->topk);
+  if (p->dtype != MSA_F32 && p->dtype != MSA_BF16)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "dtype must be MSA_F32 or MSA_BF16 (got %d)", p->dtype);
+  if (!(p->softmax_scale >= 0.0f) || isinf(p->softmax_scale))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (p->block_size != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "block_size must be 128 (got %d)", p->block_size);
+  if (p->topk > 64) return fail(MSA_ERR_UNSUPPORTED, "topk must be <= 64 (got %d)", p->topk);
+  const int64_t nb = ((int64_t)p->kv_len + p->block_size - 1) / p->block_size;
+  if (nb > 8192)
+    return fail(MSA_ERR_UNSUPPORTED, "kv_len %d gives %lld blocks; at most 8192 are supported",
+                p->kv_len, (long long)nb);
+  const int64_t rows = (int64_t)p->batch * p->num_kv_heads * p->num_q;
+  if (rows * p->topk >= (int64_t(1) << 31))
+    return fail(MSA_ERR_UNSUPPORTED, "batch * num_kv_heads * num_q * topk must be < 2^31");
+  if ((int64_t)p->batch * p->num_kv_heads > 65535)
+    return fail(MSA_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= 65535");
+  if (rows * nb >= (int64_t(1) << 40))
+    return fail(MSA_ERR_UNSUPPORTED, "block-score matrix too large");
+  if (need_index && p->index_dim != 32 && p->index_dim != 64 && p->index_dim != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "index_dim must be 32, 64 or 128 (got %d)", p->index_dim);
+  const int G = p->num_heads / p->num_kv_heads;
+  if (need_main) {
+    if (p->head_dim != 64 && p->head_dim != 128)
+      return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+    if (!pow2_upto16(G))
+      return fail(MSA_ERR_UNSUPPORTED, "num_heads / num_kv_heads must be 1, 2, 4, 8 or 16 (got %d)", G);
+  }
+  D->S = p->batch;
+  D->T = p->num_q;
+  D->N = p->kv_len;
+  D->H = p->num_heads;
+  D->Hkv = p->num_kv_heads;
+  D->G = G;
+  D->d = p->head_dim;
+  D->dI = p->index_dim;
+  D->B = p->block_size;
+  D->k = p->topk;
+  D->nb = (int)nb;
+  D->pos0 = p->kv_len - p->num_q;
+  D->dtype = p->dtype;
+  D->scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / sqrtf((float)p->head_dim);
+  return MSA_OK;
+}
+
+#define REQUIRE_PTR(x)                                                         \
+  do {                                                                         \
+    if ((x) == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, #x " is NULL"); \
+  } while (0)
+
+// ------------------------------------------------------------------ profiler state
+struct ProfRecord {
+  std::string name;
+  hipEvent_t start, stop;
+  bool used;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
+
+}  // namespace
+
+namespace msa {
+
+LaunchScope::LaunchScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (size_t i = 0; i < g_prof.size(); ++i)
+    if (!g_prof[i].used) { slot = (int)i; break; }
+  if (slot < 0) {
+    ProfRecord r;
+    if (hipEventCreate(&r.start) != hipSuccess) return;
+    if (hipEventCreate(&r.stop) != hipSuccess) { (void)hipEventDestroy(r.start); return; }
+    r.used = false;
+    g_prof.push_back(r);
+    slot = (int)g_prof.size() - 1;
+  }
+  g_prof[slot].used = true;
+  g_prof[slot].name = name;
+  (void)hipEventRecord(g_prof[slot].start, stream);
+}
+
+LaunchScope::~LaunchScope() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  (void)hipEventRecord(g_prof[slot].stop, stream);
+}
+
+}  // namespace msa
+
+extern "C" {
+
+const char* msa_status_string(msa_status s) {
+  switch (s) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARGUMENT: return "MSA_ERR_INVALID_ARGUMENT";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL";
+    case MSA_ERR_DEVICE: return "MSA_ERR_DEVICE";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char* msa_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t msa_workspace_bytes(const msa_problem* prob, int which) {
+  msa::Dims D;
+  switch (which) {
+    case MSA_CALL_INVERT:
+      if (check_problem(prob, &D, false, false) != MSA_OK) return 0;
+      return msa::invert_workspace_bytes(D);
+    case MSA_CALL_PREFILL:
+      if (check_problem(prob, &D, false, true) != MSA_OK) return 0;
+      return msa::prefill_workspace_bytes(D);
+    case MSA_CALL_DECODE:
+      if (check_problem(prob, &D, false, true) != MSA_OK) return 0;
+      return msa::decode_workspace_bytes(D);
+    default:
+      return 0;
+  }
+}
+
+msa_status msa_index_scores(const msa_problem* prob, const void* q_idx, const void* k_idx,
+                            float* scores, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, true, false);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(k_idx);
+  REQUIRE_PTR(scores);
+  return device_status(msa::launch_index_scores(D, q_idx, k_idx, scores, (hipStream_t)stream),
+                       "msa_index_scores launch");
+}
+
+msa_status msa_block_topk(const msa_problem* prob, const float* scores, int32_t* sel,
+                          void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, false);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(scores);
+  REQUIRE_PTR(sel);
+  return device_status(msa::launch_block_topk(D, scores, sel, (hipStream_t)stream),
+                       "msa_block_topk launch");
+}
+
+msa_status msa_invert_selection(const msa_problem* prob, const int32_t* sel,
+                                int32_t* csr_offsets, int32_t* csr_entries, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, false);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(csr_offsets);
+  REQUIRE_PTR(csr_entries);
+  const size_t need = msa::invert_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_invert_selection needs %zu workspace bytes, got %zu",
+                need, workspace_bytes);
+  if (need > 0) REQUIRE_PTR(workspace);
+  return device_status(
+      msa::launch_invert(D, sel, csr_offsets, csr_entries, workspace, (hipStream_t)stream),
+      "msa_invert_selection launch");
+}
+
+msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, const void* k,
+                                   const void* v, const int32_t* csr_offsets,
+                                   const int32_t* csr_entries, const int32_t* sel, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, true);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(csr_offsets);
+  REQUIRE_PTR(csr_entries);
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(out);
+  const size_t need = msa::prefill_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "msa_sparse_attn_prefill needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(msa::launch_prefill(D, q, k, v, csr_offsets, csr_entries, sel, out,
+                                           workspace, (hipStream_t)stream),
+                       "msa_sparse_attn_prefill launch");
+}
+
+msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* sel, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, true);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(out);
+  const size_t need = msa::decode_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "msa_sparse_attn_decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(
+      msa::launch_decode(D, q, k_cache, v_cache, sel, out, workspace, (hipStream_t)stream),
+      "msa_sparse_attn_decode launch");
+}
+
+msa_status msa_profiler_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return ok();
+}
+
+msa_status msa_profiler_read(const char* kernel, double* total_ms, int64_t* launches, int reset) {
+  if (total_ms == nullptr || launches == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "total_ms and launches must not be NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_prof) {
+    if (!r.used) continue;
+    if (kernel != nullptr && kernel[0] != '\0' && r.name != kernel) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return device_status(e, "profiler event wait");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return device_status(e, "profiler elapsed time");
+    tot += ms;
+    ++n;
+  }
+  if (reset)
+    for (auto& r : g_prof) r.used = false;
+  *total_ms = tot;
+  *launches = n;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// msa_internal.hpp -- shared declarations of libmsa's translation units.
+// Host launchers are declared here; device helpers are inline below.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/msa.h"
+
+namespace msa {
+
+// Problem sizes after validation (host and device copy by value).
+struct Dims {
+  int S, T, N, H, Hkv, G, d, dI, B, k, nb;
+  int pos0;      // N - T: absolute position of query row 0
+  int dtype;     // msa_dtype
+  float scale;   // main-branch logit scale (resolved, never 0)
+};
+
+// ----------------------------------------------------------------- profiler
+// Brackets a launch with hipEvents when the profiler is enabled.
+struct LaunchScope {
+  LaunchScope(const char* name, hipStream_t s);
+  ~LaunchScope();
+  int slot;
+  hipStream_t stream;
+};
+
+// ----------------------------------------------------------------- launchers
+// Each returns hipSuccess or the error of its first failing launch.
+hipError_t launch_index_scores(const Dims& D, const void* q_idx, const void* k_idx,
+                               float* scores, hipStream_t st);
+hipError_t launch_block_topk(const Dims& D, const float* scores, int32_t* sel, hipStream_t st);
+
+size_t invert_workspace_bytes(const Dims& D);
+hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, int32_t* entries,
+                         void* ws, hipStream_t st);
+
+size_t prefill_workspace_bytes(const Dims& D);
+hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const void* v,
+                          const int32_t* offsets, const int32_t* entries, const int32_t* sel,
+                          void* out, void* ws, hipStream_t st);
+
+size_t decode_workspace_bytes(const Dims& D);
+hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void* v,
+                         const int32_t* sel, void* out, void* ws, hipStream_t st);
+
+// Shared by the prefill and decode paths: merge per-slot partials into out.
+hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part_lse,
+                            const void* part_o, int part_o_is_bf16, void* out, hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ----------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {  // round to nearest even
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float ldf(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ldf(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ void stf(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void stf(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+// Wave64 reductions through cross-lane shuffles.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace msa

@@ -1,0 +1,179 @@
+// topk.hip -- a2: per-(sequence, group, query) block selection with the own block
+// forced.  Page "MSA 稀疏注意力三国杀：NSA / DSA / MoBA / MSA 四方案深度对比", section
+// 第一步：粗筛 item 3 (16 blocks, the current position's block always chosen, the
+// rest by score) and the head-pattern appendix (the own block is the only forced
+// rule); MSA entry of "稀疏注意力速览（Sparse Attention，2019 ~ 2026）".
+//
+// One wave64 per row.  The order key of a block is (score desc, id asc); scores
+// are mapped to order-preserving uint32 ("ord"), with -0 folded onto +0 so they
+// tie as IEEE values do.  Selecting the `need = k-1` best of n = b_t blocks:
+//   A. every lane keeps the max ord of its strided share of the row;
+//   B. tau1 = the need-th largest lane maximum (bitwise radix search with wave
+//      ballots).  At least `need` scores are >= tau1, so every selected block is
+//      >= tau1; those candidates are compacted into LDS in ascending id order;
+//   C. tau = the exact need-th largest ord among the candidates (same radix
+//      search); blocks with ord > tau are taken, and among ord == tau the lowest
+//      ids (radix search over ~id) fill the remaining places;
+//   D. the taken ids are compacted in ascending order and the own block appended.
+// If more than kCap candidates pass step B (heavy ties), steps C-D read the row
+// from memory instead of LDS: slower, same result.
+#include "msa_internal.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kCap = 512;
+
+__device__ __forceinline__ uint32_t ord_key(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u << 1) == 0u) u = 0u;  // -0 and +0 are the same value
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Candidate sources: element c (ascending c = ascending block id) -> (ord, id).
+struct LdsSrc {
+  const uint32_t* ord;
+  const int32_t* id;
+  int n;
+  __device__ uint32_t key(int c) const { return ord[c]; }
+  __device__ int32_t idx(int c) const { return id[c]; }
+};
+struct RowSrc {
+  const float* sc;
+  int n;
+  __device__ uint32_t key(int c) const { return ord_key(sc[c]); }
+  __device__ int32_t idx(int c) const { return c; }
+};
+
+// Largest x with #{elements e : f(e) >= x} >= want, where f(e) = key (mode 0) or
+// (key == tau ? ~id : 0) (mode 1).  Requires at least `want` elements.
+template <class Src>
+__device__ uint32_t radix_kth(const Src& src, int lane, int want, int mode, uint32_t tau) {
+  uint32_t prefix = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    int cnt = 0;
+    for (int base = 0; base < src.n; base += 64) {
+      const int c = base + lane;
+      bool f = false;
+      if (c < src.n) {
+        const uint32_t o = src.key(c);
+        const uint32_t v = mode == 0 ? o : (o == tau ? ~(uint32_t)src.idx(c) : 0u);
+        f = v >= cand;
+      }
+      cnt += __popcll(__ballot(f));
+    }
+    if (cnt >= want) prefix = cand;
+  }
+  return prefix;
+}
+
+template <class Src>
+__device__ void select_and_write(const Src& src, int lane, int need, int32_t* out) {
+  const uint32_t tau = radix_kth(src, lane, need, 0, 0u);
+  int c_gt = 0, c_eq = 0;
+  for (int base = 0; base < src.n; base += 64) {
+    const int c = base + lane;
+    const uint32_t o = c < src.n ? src.key(c) : 0u;
+    c_gt += __popcll(__ballot(c < src.n && o > tau));
+    c_eq += __popcll(__ballot(c < src.n && o == tau));
+  }
+  const int need_eq = need - c_gt;  // 1 <= need_eq <= c_eq
+  uint32_t iota = 0xFFFFFFFFu;      // ties with id <= iota are taken
+  if (need_eq < c_eq) iota = ~radix_kth(src, lane, need_eq, 1, tau);
+  int pos = 0;
+  for (int base = 0; base < src.n; base += 64) {
+    const int c = base + lane;
+    bool f = false;
+    int32_t id = 0;
+    if (c < src.n) {
+      const uint32_t o = src.key(c);
+      id = src.idx(c);
+      f = o > tau || (o == tau && (uint32_t)id <= iota);
+    }
+    const uint64_t m = __ballot(f);
+    const int at = pos + lanes_below(m);
+    if (f && at < need) out[at] = id;  // exactly `need` are flagged; the bound is insurance
+    pos += __popcll(m);
+  }
+}
+
+__global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const float* __restrict__ scores,
+                                                                  int32_t* __restrict__ sel) {
+  __shared__ uint32_t s_ord[kWaves][kCap];
+  __shared__ int32_t s_id[kWaves][kCap];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+  if (row >= rows) return;
+  const int t = (int)(row % D.T);
+  const int bt = (D.pos0 + t) / D.B;
+  const int k = D.k;
+  int32_t* out = sel + row * k;
+  const int n = bt;        // eligible blocks other than the own one: 0 .. bt-1
+  const int need = k - 1;  // how many of them are taken
+  if (need >= n) {         // budget covers every causal block
+    for (int i = lane; i < k; i += 64) out[i] = i <= bt ? i : -1;
+    return;
+  }
+  if (need == 0) {         // k == 1: the own block alone
+    if (lane == 0) out[0] = bt;
+    return;
+  }
+  const float* sc = scores + row * (int64_t)D.nb;
+  // A. lane maxima over a strided share of the row
+  uint32_t lmax = 0;
+  for (int i = lane; i < n; i += 64) {
+    const uint32_t o = ord_key(sc[i]);
+    lmax = o > lmax ? o : lmax;
+  }
+  // B. tau1 = need-th largest lane maximum; compact ord >= tau1 into LDS (ascending id)
+  uint32_t tau1 = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau1 | (1u << bit);
+    if (__popcll(__ballot(lmax >= cand)) >= need) tau1 = cand;
+  }
+  int C = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    uint32_t o = 0;
+    bool f = false;
+    if (i < n) {
+      o = ord_key(sc[i]);
+      f = o >= tau1;
+    }
+    const uint64_t m = __ballot(f);
+    const int p = C + lanes_below(m);
+    if (f && p < kCap) {
+      s_ord[wave][p] = o;
+      s_id[wave][p] = i;
+    }
+    C += __popcll(m);
+  }
+  if (C <= kCap) {
+    LdsSrc src{s_ord[wave], s_id[wave], C};
+    select_and_write(src, lane, need, out);
+  } else {
+    RowSrc src{sc, n};
+    select_and_write(src, lane, need, out);
+  }
+  if (lane == 0) out[need] = bt;  // the own block is the largest id of the row
+}
+
+}  // namespace
+
+hipError_t launch_block_topk(const Dims& D, const float* scores, int32_t* sel, hipStream_t st) {
+  const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
+  const int64_t grid = (rows + kWaves - 1) / kWaves;
+  LaunchScope scope("block_topk", st);
+  hipLaunchKernelGGL(block_topk_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, st, D, scores, sel);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,173 @@
+/*
+ * msa.h -- C ABI of libmsa.so: MiniMax Sparse Attention (MSA) prefill and decode
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Method, as described on the pages (cited by page title and section):
+ *   [P1] "MSA 稀疏注意力三国杀：NSA / DSA / MoBA / MSA 四方案深度对比",
+ *        sections 第一步：粗筛 (index branch, block max pooling, top-16 blocks with
+ *        the query's own block forced), 第二步：精算 (exact attention over the
+ *        16 x 128 = 2048 selected tokens), Kernel 创新：Outer Gather Q (KV block as
+ *        the outer loop: gather every query that chose a block, read it once).
+ *   [P3] "稀疏注意力速览（Sparse Attention，2019 ~ 2026）", entry "MiniMax Sparse
+ *        Attention（MSA）" (GQA groups, one index-query head and a shared index-key
+ *        head per group, in-block max-pool, per-group top-k, forced local block).
+ *
+ * Conventions for every call:
+ *   - All tensor arguments are DEVICE pointers to dense row-major arrays owned by
+ *     the caller; the library never allocates, frees or retains device memory
+ *     and never keeps a pointer after the call returns.
+ *   - The problem struct is a HOST pointer read during the call only.
+ *   - Each call validates its arguments on the host, then enqueues its kernels
+ *     asynchronously on `stream` (a hipStream_t; NULL = the default stream). It
+ *     never synchronises the device.
+ *   - On any status other than MSA_OK nothing was enqueued and no output was
+ *     touched; msa_last_error_message() describes the failure (thread-local).
+ *     Launch failures report MSA_ERR_DEVICE.  Asynchronous device faults surface
+ *     at the caller's next synchronisation.
+ *   - Calls are stateless and thread-safe (apart from the opt-in profiler).
+ *
+ * Shapes (S = batch, T = queries per sequence, N = kv length, H = query heads,
+ * Hkv = KV heads = GQA groups, G = H / Hkv, d = head dim, dI = index dim,
+ * B = block size, nb = ceil(N / B), k = top-k):
+ *   q       [S, T, H, d]     query head h belongs to group g = h / G
+ *   k, v    [S, Hkv, N, d]   keys / values (the full, uncompressed cache)
+ *   q_idx   [S, Hkv, T, dI]  one index-query head per group
+ *   k_idx   [S, Hkv, N, dI]  one index-key head per group
+ *   scores  [S, Hkv, T, nb]  float32 block scores
+ *   sel     [S, Hkv, T, k]   int32 selected block ids
+ *   out     [S, T, H, d]     attention output (same dtype as q)
+ * The T queries are the LAST T positions: query row t sits at p_t = N - T + t and
+ * owns block b_t = floor(p_t / B).  Element types follow problem.dtype (float32
+ * or bfloat16 bit patterns); scores and log-sum-exps are always float32.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, inconsistent or out-of-range sizes */
+  MSA_ERR_UNSUPPORTED = 2,        /* valid problem outside what the kernels implement */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MSA_ERR_DEVICE = 4              /* a HIP runtime call or kernel launch failed */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+typedef struct {
+  int32_t batch;         /* S >= 1 */
+  int32_t num_q;         /* T, 1 <= T <= N */
+  int32_t kv_len;        /* N, 1 <= N <= 8192 * block_size (need not be a multiple of it) */
+  int32_t num_heads;     /* H, a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* Hkv >= 1; G = H / Hkv must be 1, 2, 4, 8 or 16 */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t index_dim;     /* dI: 32, 64 or 128 */
+  int32_t block_size;    /* B: 128 */
+  int32_t topk;          /* k: 1..64 */
+  int32_t dtype;         /* msa_dtype of q, k, v, q_idx, k_idx, out */
+  float softmax_scale;   /* main-branch logit scale; 0 selects 1/sqrt(d) */
+} msa_problem;
+
+/* Which call a workspace size is asked for (msa_workspace_bytes). */
+enum { MSA_CALL_INVERT = 2, MSA_CALL_PREFILL = 3, MSA_CALL_DECODE = 4 };
+
+/*
+ * a1. Index branch scoring fused with the causal block max-pool
+ *     ([P1] 第一步：粗筛 items 1-2; [P3] MSA entry).
+ *   scores[s,g,t,b] = max_{j in [bB, min((b+1)B-1, p_t)]} sum_c q_idx[s,g,t,c] k_idx[s,g,j,c]
+ *   for b <= b_t, accumulated in float32 (bf16 products are exact in fp32).
+ *   Entries with b > b_t are NOT written (they are not eligible).
+ *   Raw dot product: no scale and no activation (both are monotone and would not
+ *   change the selection).
+ */
+msa_status msa_index_scores(const msa_problem* prob, const void* q_idx, const void* k_idx,
+                            float* scores, void* stream);
+
+/*
+ * a2. Per-group block top-k with the own block forced
+ *     ([P1] 第一步：粗筛 item 3 and the head-pattern appendix: the only forced rule
+ *     is that the query's own block is selected; [P3] MSA entry).
+ *   sel[s,g,t,:] = {b_t} plus the k-1 best blocks b < b_t ordered by
+ *   (score descending, block id ascending); fewer if b_t + 1 < k.
+ *   Written in ascending block order, padded with -1 to k entries.
+ *   Scores are compared as IEEE float32 values (+0 == -0); NaN scores are
+ *   outside the contract.  Reads only scores[s,g,t,0..b_t].
+ */
+msa_status msa_block_topk(const msa_problem* prob, const float* scores, int32_t* sel,
+                          void* stream);
+
+/*
+ * a3. Selection inversion into per-(sequence, group, block) query lists: the index
+ *     of the Outer-Gather-Q order ([P1] Kernel 创新：Outer Gather Q).
+ *   csr_offsets [S, Hkv, nb + 1] int32: global positions into csr_entries; the list
+ *     of (s, g, b) is csr_entries[csr_offsets[s,g,b] .. csr_offsets[s,g,b+1]).
+ *     csr_offsets[s,g,nb] == csr_offsets[s,g+1,0] (one flat array, (s, g, b) order).
+ *   csr_entries [S * Hkv * T * k] int32 (capacity): entry value t * k + slot for every
+ *     query row t whose sel[s,g,t,slot] == b, in ascending t.  Deterministic.
+ *   workspace: msa_workspace_bytes(prob, MSA_CALL_INVERT) bytes of device memory.
+ *   Requires S * Hkv * T * k < 2^31.  Entries of sel outside [0, nb) count as -1.
+ */
+msa_status msa_invert_selection(const msa_problem* prob, const int32_t* sel,
+                                int32_t* csr_offsets, int32_t* csr_entries, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * a4 + a5. Prefill main branch in Outer-Gather-Q order plus the log-sum-exp merge
+ *     ([P1] 第二步：精算 and Kernel 创新：Outer Gather Q; [P3] MSA entry "Main Branch
+ *     只在这些块上做精确 softmax attention").
+ *   For every (s, g, b) the K/V block is staged on chip once and every query row of
+ *   its csr list (all G heads of the group) is processed against it, giving a
+ *   per-(row, slot, head) partial (lse, O).  A second kernel merges the partials:
+ *     out[s,t,h,:] = sum_{j in J} softmax_j(scale * q[s,t,h,:] . k[s,g,j,:]) v[s,g,j,:]
+ *     J = union over valid slots of [bB, (b+1)B) intersected with [0, p_t].
+ *   sel, csr_offsets and csr_entries are the outputs of the two calls above.
+ *   workspace: msa_workspace_bytes(prob, MSA_CALL_PREFILL) bytes (partials + work list).
+ */
+msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, const void* k,
+                                   const void* v, const int32_t* csr_offsets,
+                                   const int32_t* csr_entries, const int32_t* sel, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * a6. Decode main branch: query-centric split-K over each query's selected blocks
+ *     ([P1] 第二步：精算 -- every generated token attends to a fixed 2048 tokens;
+ *     the whole uncompressed cache stays resident).  Same output definition as the
+ *     prefill call; any T is accepted, no inversion is needed.
+ *   k, v are the cache [S, Hkv, N, d]; q is [S, T, H, d] (T = 1 for plain decode).
+ *   workspace: msa_workspace_bytes(prob, MSA_CALL_DECODE) bytes.
+ */
+msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* sel, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace needed by a call (MSA_CALL_*); 0 for an invalid problem or call. */
+size_t msa_workspace_bytes(const msa_problem* prob, int which_call);
+
+/* Static description of a status code. */
+const char* msa_status_string(msa_status status);
+
+/* Thread-local detail of this thread's last failed call ("" if none). */
+const char* msa_last_error_message(void);
+
+/*
+ * Opt-in per-kernel timer (measurement aid).  While enabled, every launch of the
+ * library's kernels is bracketed by a pair of hipEvents recorded on the launch
+ * stream.  msa_profiler_read() waits for the recorded events, returns the summed
+ * device time (ms) and launch count of the kernel named `kernel` (NULL or "" =
+ * every kernel) since the last reset, and resets=1 clears the records.  Global
+ * state: not for concurrent use from several threads.
+ */
+msa_status msa_profiler_enable(int on);
+msa_status msa_profiler_read(const char* kernel, double* total_ms, int64_t* launches, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -1,0 +1,134 @@
+"""The five seeded synthetic MSA workloads (shapes of the pages' 1M-context setting).
+
+Each workload fixes the problem sizes and the recipe of every input tensor; the
+generator in this package produces them on device or host.  Nothing here computes
+any part of the attention method.
+
+  C0  tiny fp32 prefill      S 1, T = N = 2048,  H 4 / Hkv 1, d 64,  dI 32, k 4, iid N(0,1)
+  C1  bf16 prefill 32K       S 1, T = N = 32768, H 64 / Hkv 8, d 128, dI 64, k 16, iid N(0,1)
+  C2  bf16 prefill 128K      T = N = 131072, dims of C1, structured index inputs:
+                             boost channel (q_I[0] = 1, +3 sigma = +24 on k_I[0] of block 0
+                             and 8 needle blocks per group) and the recent band
+                             (8 rotary planes on dims 1..16, a^2 = 3: +24 at distance 0)
+  C3  bf16 decode            S 16 sequences x N = 1,048,576 cached keys, T = 1 (p = N - 1),
+                             H 64 / Hkv 8, d 128, dI 64, k 16; sink + 8 needles per
+                             (sequence, group) with the C2 boost channel, no band
+  C4  bf16 chunked prefill   S 1, T = 8192 queries at positions 1,040,384 .. 1,048,575,
+                             N = 1,048,576, dims of C1, iid N(0,1)
+
+Seeds are 0x4D534100 + workload index; tensor ids Q 1, K 2, V 3, q_I 4, k_I 5,
+needle draw 6, sampled rows 7.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import (BF16, F32, KIND_IID, KIND_KIDX, KIND_QIDX, TID_K, TID_KI, TID_Q, TID_QI, TID_ROWS, TID_V,
+               TensorSpec, band_table, h16, needle_blocks)
+
+SEED_BASE = 0x4D534100
+SIGMA_BOOST = 24.0   # 3 sigma with sigma = sqrt(dI) = 8
+BAND_A2 = 3.0        # band contribution a^2 * 8 planes = 24 = 3 sigma at distance 0
+
+
+@dataclass
+class Workload:
+    name: str
+    index: int
+    S: int
+    T: int
+    N: int
+    H: int
+    Hkv: int
+    d: int
+    dI: int
+    k: int
+    dtype: int
+    structure: str = "iid"           # "iid" | "band_sink_needles" | "sink_needles"
+    description: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.index
+
+    @property
+    def nb(self) -> int:
+        return (self.N + 127) // 128
+
+    @property
+    def G(self) -> int:
+        return self.H // self.Hkv
+
+    def problem(self):
+        import block_sparse_long_06_amd as msa
+        return msa.problem(self.S, self.T, self.N, self.H, self.Hkv, self.d, self.dI, self.k,
+                           dtype=self.dtype)
+
+    # ------------------------------------------------------------ tensor recipes
+    def boost_mask(self) -> np.ndarray | None:
+        if self.structure == "iid":
+            return None
+        mask = np.zeros((self.S, self.Hkv, self.nb), dtype=np.uint8)
+        mask[:, :, 0] = 1
+        nd = needle_blocks(self.seed, self.S, self.Hkv, self.nb, 8)
+        for s in range(self.S):
+            for g in range(self.Hkv):
+                mask[s, g, nd[s, g]] = 1
+        return mask
+
+    def band(self) -> np.ndarray | None:
+        return band_table(self.N, BAND_A2) if self.structure == "band_sink_needles" else None
+
+    def specs(self) -> dict:
+        dt = self.dtype
+        sd = self.seed
+        out = {
+            "q": TensorSpec((self.S, self.T, self.H, self.d), sd, TID_Q, dt),
+            "k": TensorSpec((self.S, self.Hkv, self.N, self.d), sd, TID_K, dt),
+            "v": TensorSpec((self.S, self.Hkv, self.N, self.d), sd, TID_V, dt),
+        }
+        if self.structure == "iid":
+            out["q_idx"] = TensorSpec((self.S, self.Hkv, self.T, self.dI), sd, TID_QI, dt)
+            out["k_idx"] = TensorSpec((self.S, self.Hkv, self.N, self.dI), sd, TID_KI, dt)
+        else:
+            band = self.band()
+            out["q_idx"] = TensorSpec((self.S, self.Hkv, self.T, self.dI), sd, TID_QI, dt, kind=KIND_QIDX,
+                                      pos_offset=self.N - self.T, band=band)
+            out["k_idx"] = TensorSpec((self.S, self.Hkv, self.N, self.dI), sd, TID_KI, dt, kind=KIND_KIDX,
+                                      boost=SIGMA_BOOST, block=128, boost_mask=self.boost_mask(), band=band)
+        return out
+
+    def sampled_rows(self, count: int, always=()) -> np.ndarray:
+        """Seeded sample of query rows (stream TID_ROWS), always including `always`."""
+        rows = set(int(r) for r in always if 0 <= r < self.T)
+        i = 0
+        while len(rows) < min(count, self.T):
+            v = int(h16(self.seed, TID_ROWS, 2 * i)) * 65536 + int(h16(self.seed, TID_ROWS, 2 * i + 1))
+            rows.add(v % self.T)
+            i += 1
+        return np.array(sorted(rows), dtype=np.int64)
+
+
+C0 = Workload("C0_tiny_fp32_prefill_2k", 0, S=1, T=2048, N=2048, H=4, Hkv=1, d=64, dI=32, k=4, dtype=F32,
+              description="tiny fp32 MSA prefill, seq 2048, 1 KV head, 4 query heads, d 64, dI 32, top-4")
+C1 = Workload("C1_bf16_prefill_32k", 1, S=1, T=32768, N=32768, H=64, Hkv=8, d=128, dI=64, k=16, dtype=BF16,
+              description="bf16 MSA prefill, seq 32768, 64/8 heads, d 128, dI 64, top-16")
+C2 = Workload("C2_bf16_prefill_128k_structured", 2, S=1, T=131072, N=131072, H=64, Hkv=8, d=128, dI=64, k=16,
+              dtype=BF16, structure="band_sink_needles",
+              description="bf16 MSA prefill, seq 131072, structured index keys (sink, band, needles)")
+C3 = Workload("C3_bf16_decode_16x1M", 3, S=16, T=1, N=1048576, H=64, Hkv=8, d=128, dI=64, k=16, dtype=BF16,
+              structure="sink_needles",
+              description="bf16 MSA decode, 16 sequences x 1,048,576-token KV cache, 1 new query each")
+C4 = Workload("C4_bf16_chunk_8k_at_1M", 4, S=1, T=8192, N=1048576, H=64, Hkv=8, d=128, dI=64, k=16,
+              dtype=BF16,
+              description="bf16 MSA chunked prefill, 8192 queries at the end of a 1,048,576-token KV")
+
+ALL = [C0, C1, C2, C3, C4]
+
+
+def small(name, S, T, N, H, Hkv, d, dI, k, dtype=BF16, structure="iid", index=100) -> Workload:
+    """A reduced workload with the same recipes (for parity tests that span ragged tiles)."""
+    return Workload(name, index, S=S, T=T, N=N, H=H, Hkv=Hkv, d=d, dI=dI, k=k, dtype=dtype, structure=structure)

@@ -1,0 +1,68 @@
+"""Helpers shared by the GPU parity tests: device inputs, host copies, comparisons.
+
+Inputs come from the seeded generator (synth); expected values come only from the
+CPU oracle.  Nothing here computes any step of the method."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import block_sparse_long_06_amd as msa
+import oracle
+import synth
+
+SCORE_RTOL = 1e-4                    # |d| <= 1e-4 * max(|ref|, 1)  (fp32 accumulation)
+ATOL = {synth.BF16: 2e-2, synth.F32: 1e-4}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU test run without a visible GPU")
+    msa.lib()
+
+
+def gen(wl, names=("q", "k", "v", "q_idx", "k_idx")):
+    specs = wl.specs()
+    return {n: synth.device_tensor(specs[n]) for n in names}
+
+
+def f64(t) -> np.ndarray:
+    return oracle.decode(t)
+
+
+def check_scores(gpu_rows, ref_rows, pos, B=128, what=""):
+    """gpu_rows/ref_rows [R, nb]: compare eligible entries (b <= own block)."""
+    R, nb = ref_rows.shape
+    elig = np.arange(nb)[None, :] <= (pos // B)[:, None]
+    g = gpu_rows[elig].astype(np.float64)
+    r = ref_rows[elig]
+    err = np.abs(g - r) / np.maximum(np.abs(r), 1.0)
+    worst = float(err.max()) if err.size else 0.0
+    say("  scores %s: %d entries, max scaled err %.3e" % (what, err.size, worst))
+    assert np.all(np.isfinite(g)), "non-finite GPU score"
+    assert worst <= SCORE_RTOL, "index scores off by %.3e (scaled)" % worst
+
+
+def check_out(gpu, ref, dtype, what=""):
+    g = gpu.astype(np.float64)
+    err = np.abs(g - ref)
+    rel_rms = float(np.sqrt(np.mean((g - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
+    say("  out %s: max abs err %.3e, rel rms %.3e" % (what, float(err.max()), rel_rms))
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    assert float(err.max()) <= ATOL[dtype], "attention output off by %.3e" % float(err.max())
+    return rel_rms
+
+
+def full_prefill(wl, inputs, bufs=None):
+    prob = wl.problem()
+    bufs = bufs or msa.alloc_prefill(prob)
+    msa.run_prefill(prob, inputs["q"], inputs["k"], inputs["v"], inputs["q_idx"], inputs["k_idx"], bufs)
+    torch.cuda.synchronize()
+    return prob, bufs

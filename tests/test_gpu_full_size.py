@@ -1,0 +1,163 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench times.
+
+The oracle cannot redo a 128K or 1M pass in seconds, so:
+  * index scores and attention outputs are checked on seeded samples of query rows
+    (always including tile edges), one row at a time in the oracle;
+  * the selection is checked bit-exact on EVERY row by running the oracle's top-k
+    on the GPU's block scores, and the inversion bit-exact on every list;
+  * properties that hold at any size are checked everywhere: own block present,
+    |sel| = min(k, b_t + 1), every output finite.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_06_amd as msa
+import oracle
+from synth import workloads as W
+from tests.gpu_util import check_out, check_scores, f64, gen, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_selection_everywhere(wl, sc_gpu, sel_gpu):
+    pos = oracle.positions(wl.N, wl.T)
+    own = pos // 128
+    for s in range(wl.S):
+        for g in range(wl.Hkv):
+            ref = oracle.slice_block_topk(sc_gpu[s, g], own, wl.k)
+            np.testing.assert_array_equal(sel_gpu[s, g], ref)
+    valid = sel_gpu >= 0
+    assert np.all(valid.sum(-1) == np.minimum(wl.k, own + 1)[None, None, :])
+    assert np.all(np.any(sel_gpu == own[None, None, :, None], axis=-1))
+    say("  selection bit-exact on all %d rows" % (wl.S * wl.Hkv * wl.T))
+
+
+def _check_inversion_everywhere(wl, sel_gpu, off_gpu, ent_gpu):
+    for s in range(wl.S):
+        for g in range(wl.Hkv):
+            r_off, r_ent = oracle.slice_invert(sel_gpu[s, g], wl.nb)
+            base = off_gpu[s, g, 0]
+            np.testing.assert_array_equal(off_gpu[s, g] - base, r_off)
+            np.testing.assert_array_equal(ent_gpu[base:base + r_off[-1]], r_ent)
+    say("  inversion bit-exact: %d entries" % int(off_gpu[-1, -1, -1]))
+
+
+def _structure_report(wl, sel_gpu):
+    """Fractions of selections that are own / sink / recent band / needle / other."""
+    pos = oracle.positions(wl.N, wl.T)
+    own = (pos // 128)[None, None, :, None]
+    mask = wl.boost_mask()
+    sel = sel_gpu
+    valid = sel >= 0
+    is_own = sel == own
+    is_sink = (sel == 0) & ~is_own
+    is_band = (own - sel <= 4) & (own - sel > 0) & ~is_sink
+    needle = np.zeros_like(valid)
+    if mask is not None:
+        for s in range(wl.S):
+            for g in range(wl.Hkv):
+                m = mask[s, g].astype(bool)
+                m[0] = False
+                needle[s, g] = m[np.maximum(sel[s, g], 0)] & valid[s, g]
+    needle &= ~is_own & ~is_sink & ~is_band
+    other = valid & ~is_own & ~is_sink & ~is_band & ~needle
+    tot = valid.sum()
+    say("  realised selections: own %.3f sink %.3f band %.3f needle %.3f other %.3f" % tuple(
+        float(x.sum()) / tot for x in (is_own, is_sink, is_band, needle, other)))
+
+
+def _sampled_rows_check(wl, inputs, sc_gpu, sel_gpu, out_gpu, rows, score_rows=None):
+    pos_all = oracle.positions(wl.N, wl.T)
+    G = wl.G
+    score_rows = rows if score_rows is None else score_rows
+    for s in range(wl.S):
+        for g in range(wl.Hkv):
+            kI = f64(inputs["k_idx"][s, g])
+            qI = f64(inputs["q_idx"][s, g][torch.from_numpy(score_rows).cuda()])
+            ref_sc = oracle.slice_index_scores(qI, pos_all[score_rows], kI, 128)
+            check_scores(sc_gpu[s, g][score_rows], ref_sc, pos_all[score_rows], what="s%d g%d" % (s, g))
+            del kI
+            K = f64(inputs["k"][s, g])
+            V = f64(inputs["v"][s, g])
+            q = f64(inputs["q"][s][torch.from_numpy(rows).cuda()][:, g * G:(g + 1) * G])
+            ref = oracle.slice_attention(q, pos_all[rows], sel_gpu[s, g][rows], K, V, 128, 1 / np.sqrt(wl.d))
+            check_out(out_gpu[s][rows][:, g * G:(g + 1) * G], ref, wl.dtype, what="s%d g%d" % (s, g))
+            del K, V
+
+
+def _prefill_full(wl, n_rows, n_score_rows):
+    require_gpu()
+    say("workload", wl.name)
+    inputs = gen(wl)
+    prob = wl.problem()
+    bufs = msa.alloc_prefill(prob)
+    msa.run_prefill(prob, inputs["q"], inputs["k"], inputs["v"], inputs["q_idx"], inputs["k_idx"], bufs)
+    torch.cuda.synchronize()
+    sc = bufs.scores.cpu().numpy()
+    sel = bufs.sel.cpu().numpy()
+    _check_selection_everywhere(wl, sc, sel)
+    _check_inversion_everywhere(wl, sel, bufs.csr_offsets.cpu().numpy(), bufs.csr_entries.cpu().numpy())
+    out = bufs.out
+    assert torch.isfinite(out.float()).all()
+    edges = [0, 1, 127, 128, 255, 256, wl.T // 2, wl.T - 129, wl.T - 128, wl.T - 1]
+    rows = wl.sampled_rows(n_rows, always=edges)
+    srows = wl.sampled_rows(n_score_rows, always=[0, 127, 128, wl.T - 1])
+    _sampled_rows_check(wl, inputs, sc, sel, f64(out), rows, srows)
+    if wl.structure != "iid":
+        _structure_report(wl, sel)
+    del inputs, bufs
+    torch.cuda.empty_cache()
+
+
+def test_c1_prefill_32k():
+    _prefill_full(W.C1, 128, 64)
+
+
+def test_c2_prefill_128k_structured():
+    _prefill_full(W.C2, 64, 16)
+
+
+def test_c4_chunk_8k_at_1m():
+    _prefill_full(W.C4, 64, 8)
+
+
+def test_c3_decode_16x1m():
+    require_gpu()
+    wl = W.C3
+    say("workload", wl.name)
+    inputs = gen(wl)
+    prob = wl.problem()
+    db = msa.alloc_decode(prob)
+    msa.run_decode(prob, inputs["q"], inputs["k"], inputs["v"], inputs["q_idx"], inputs["k_idx"], db)
+    torch.cuda.synchronize()
+    sc = db.scores.cpu().numpy()
+    sel = db.sel.cpu().numpy()
+    _check_selection_everywhere(wl, sc, sel)
+    _structure_report(wl, sel)
+    out = f64(db.out)
+    assert np.all(np.isfinite(out))
+    pos = np.array([wl.N - 1], dtype=np.int64)
+    G = wl.G
+    # index scores on 8 seeded (sequence, group) pairs; attention on all 128
+    pick = np.random.default_rng(wl.seed).choice(wl.S * wl.Hkv, size=8, replace=False)
+    pairs = [(int(r) // wl.Hkv, int(r) % wl.Hkv) for r in sorted(pick)]
+    for s, g in pairs:
+        ref_sc = oracle.slice_index_scores(f64(inputs["q_idx"][s, g]), pos, f64(inputs["k_idx"][s, g]), 128)
+        check_scores(sc[s, g], ref_sc, pos, what="s%d g%d" % (s, g))
+    Kh = np.full((wl.N, wl.d), np.nan)
+    Vh = np.full((wl.N, wl.d), np.nan)
+    for s in range(wl.S):
+        for g in range(wl.Hkv):
+            blocks = [int(b) for b in sel[s, g, 0] if b >= 0]
+            for b in blocks:
+                Kh[b * 128:(b + 1) * 128] = f64(inputs["k"][s, g, b * 128:(b + 1) * 128])
+                Vh[b * 128:(b + 1) * 128] = f64(inputs["v"][s, g, b * 128:(b + 1) * 128])
+            q = f64(inputs["q"][s][:, g * G:(g + 1) * G])
+            ref = oracle.slice_attention(q, pos, sel[s, g], Kh, Vh, 128, 1 / np.sqrt(wl.d))
+            check_out(out[s][:, g * G:(g + 1) * G], ref, wl.dtype, what="s%d g%d" % (s, g))
+            for b in blocks:  # re-poison: the oracle must never see another pair's blocks
+                Kh[b * 128:(b + 1) * 128] = np.nan
+                Vh[b * 128:(b + 1) * 128] = np.nan
+    del inputs, db
+    torch.cuda.empty_cache()

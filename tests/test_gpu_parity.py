@@ -1,0 +1,234 @@
+"""GPU parity: every C-ABI call against the CPU oracle on seeded inputs.
+
+Shapes here are small enough for the oracle to finish in seconds, yet span several
+tiles of every kernel and ragged tails (T and N not multiples of the tile sizes,
+T < N chunks, G in {1, 4, 8, 16}, d in {64, 128}, dI in {32, 64, 128}).
+
+Gates: index scores within 1e-4 (scaled); selection bit-exact when the oracle is
+fed the GPU's block scores; inversion bit-exact; attention within 2e-2 absolute
+(bf16) / 1e-4 (fp32) on the GPU's selection."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_06_amd as msa
+import oracle
+import synth
+from synth import workloads as W
+from tests.gpu_util import check_out, check_scores, f64, full_prefill, gen, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    W.C0,
+    W.small("bf16_g8_ragged_chunk", S=2, T=700, N=1000, H=16, Hkv=2, d=128, dI=64, k=4),
+    W.small("bf16_g4_d64_dI32", S=1, T=3000, N=3000, H=8, Hkv=2, d=64, dI=32, k=16),
+    W.small("bf16_g16_dI128_chunk", S=1, T=300, N=4500, H=16, Hkv=1, d=128, dI=128, k=8),
+    W.small("bf16_g1_k3", S=1, T=1500, N=1500, H=2, Hkv=2, d=64, dI=64, k=3),
+    W.small("bf16_short_T_full_budget", S=1, T=100, N=2000, H=16, Hkv=2, d=128, dI=64, k=16),
+    W.small("bf16_k1_block_local", S=1, T=600, N=900, H=8, Hkv=1, d=128, dI=64, k=1),
+    W.small("bf16_structured", S=1, T=4096, N=4096, H=16, Hkv=2, d=128, dI=64, k=16,
+            structure="band_sink_needles"),
+    W.small("fp32_g2_d128", S=2, T=500, N=777, H=4, Hkv=2, d=128, dI=64, k=5, dtype=synth.F32),
+    W.small("fp32_g8_d64", S=1, T=1200, N=1300, H=8, Hkv=1, d=64, dI=32, k=6, dtype=synth.F32),
+]
+
+
+def _verify_prefill(wl, inputs, bufs):
+    S, T, N, Hkv, G, nb, k = wl.S, wl.T, wl.N, wl.Hkv, wl.G, wl.nb, wl.k
+    pos = oracle.positions(N, T)
+    qI, kI = f64(inputs["q_idx"]), f64(inputs["k_idx"])
+    q, K, V = f64(inputs["q"]), f64(inputs["k"]), f64(inputs["v"])
+    sc = bufs.scores.cpu().numpy()
+    sel = bufs.sel.cpu().numpy()
+    off = bufs.csr_offsets.cpu().numpy()
+    ent = bufs.csr_entries.cpu().numpy()
+    out = f64(bufs.out)
+    scale = 1.0 / np.sqrt(wl.d)
+    differ = 0
+    for s in range(S):
+        for g in range(Hkv):
+            ref_sc = oracle.slice_index_scores(qI[s, g], pos, kI[s, g], 128)
+            check_scores(sc[s, g], ref_sc, pos, what="s%d g%d" % (s, g))
+            ref_sel = oracle.slice_block_topk(sc[s, g], pos // 128, k)
+            np.testing.assert_array_equal(sel[s, g], ref_sel)
+            differ += int(np.sum(np.any(oracle.slice_block_topk(ref_sc, pos // 128, k) != sel[s, g], axis=1)))
+            r_off, r_ent = oracle.slice_invert(sel[s, g], nb)
+            base = off[s, g, 0]
+            np.testing.assert_array_equal(off[s, g] - base, r_off)
+            np.testing.assert_array_equal(ent[base:base + r_off[-1]], r_ent)
+            ref = oracle.slice_attention(q[s][:, g * G:(g + 1) * G], pos, sel[s, g], K[s, g], V[s, g], 128, scale)
+            check_out(out[s][:, g * G:(g + 1) * G], ref, wl.dtype, what="s%d g%d" % (s, g))
+    say("  rows whose independent oracle selection differs: %d of %d" % (differ, S * Hkv * T))
+    assert off[-1, -1, -1] == np.sum(sel >= 0)
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[c.name for c in CASES])
+def test_prefill_pipeline_matches_oracle(wl):
+    require_gpu()
+    say("case", wl.name)
+    inputs = gen(wl)
+    _, bufs = full_prefill(wl, inputs)
+    _verify_prefill(wl, inputs, bufs)
+
+
+DEC_CASES = [
+    W.small("dec_bf16", S=3, T=1, N=5000, H=16, Hkv=2, d=128, dI=64, k=16, structure="sink_needles"),
+    W.small("dec_fp32", S=2, T=1, N=3333, H=8, Hkv=2, d=64, dI=32, k=4, dtype=synth.F32),
+    W.small("dec_bf16_multi_q", S=2, T=5, N=2000, H=8, Hkv=1, d=128, dI=64, k=8),
+]
+
+
+@pytest.mark.parametrize("wl", DEC_CASES, ids=[c.name for c in DEC_CASES])
+def test_decode_matches_oracle_and_prefill(wl):
+    require_gpu()
+    say("case", wl.name)
+    inputs = gen(wl)
+    prob = wl.problem()
+    db = msa.alloc_decode(prob)
+    msa.run_decode(prob, inputs["q"], inputs["k"], inputs["v"], inputs["q_idx"], inputs["k_idx"], db)
+    _, pb = full_prefill(wl, inputs)
+    torch.cuda.synchronize()
+    pos = oracle.positions(wl.N, wl.T)
+    qI, kI = f64(inputs["q_idx"]), f64(inputs["k_idx"])
+    q, K, V = f64(inputs["q"]), f64(inputs["k"]), f64(inputs["v"])
+    sc = db.scores.cpu().numpy()
+    sel = db.sel.cpu().numpy()
+    out = f64(db.out)
+    G = wl.G
+    for s in range(wl.S):
+        for g in range(wl.Hkv):
+            ref_sc = oracle.slice_index_scores(qI[s, g], pos, kI[s, g], 128)
+            check_scores(sc[s, g], ref_sc, pos, what="s%d g%d" % (s, g))
+            np.testing.assert_array_equal(sel[s, g], oracle.slice_block_topk(sc[s, g], pos // 128, wl.k))
+            ref = oracle.slice_attention(q[s][:, g * G:(g + 1) * G], pos, sel[s, g], K[s, g], V[s, g], 128,
+                                         1.0 / np.sqrt(wl.d))
+            check_out(out[s][:, g * G:(g + 1) * G], ref, wl.dtype, what="decode s%d g%d" % (s, g))
+    # the prefill path on the same problem agrees with the decode path
+    np.testing.assert_array_equal(pb.sel.cpu().numpy(), sel)
+    check_out(f64(pb.out), out, wl.dtype, what="prefill vs decode")
+
+
+def test_runs_are_bit_identical():
+    require_gpu()
+    wl = CASES[1]
+    inputs = gen(wl)
+    _, b1 = full_prefill(wl, inputs)
+    _, b2 = full_prefill(wl, inputs)
+    pos = oracle.positions(wl.N, wl.T)
+    elig = torch.from_numpy(np.arange(wl.nb)[None, :] <= (pos // 128)[:, None]).cuda()
+    assert torch.equal(b1.scores.masked_select(elig.expand_as(b1.scores)),
+                       b2.scores.masked_select(elig.expand_as(b2.scores)))
+    for name in ("sel", "csr_offsets", "out"):
+        assert torch.equal(getattr(b1, name), getattr(b2, name)), name
+    n = int(b1.csr_offsets[-1, -1, -1])
+    assert torch.equal(b1.csr_entries[:n], b2.csr_entries[:n])
+
+
+def test_nan_poison_unselected_blocks():
+    """Blocks no query selected are filled with NaN: outputs stay finite and identical."""
+    require_gpu()
+    wl = W.small("poison", S=1, T=32, N=8192, H=16, Hkv=2, d=128, dI=64, k=2)
+    inputs = gen(wl)
+    prob, bufs = full_prefill(wl, inputs)
+    ref_out = bufs.out.clone()
+    sel = bufs.sel.cpu().numpy()
+    K, V = inputs["k"], inputs["v"]
+    poisoned = 0
+    for s in range(wl.S):
+        for g in range(wl.Hkv):
+            used = set(int(b) for b in np.unique(sel[s, g]) if b >= 0)
+            for b in range(wl.nb):
+                if b not in used:
+                    K[s, g, b * 128:(b + 1) * 128] = float("nan")
+                    V[s, g, b * 128:(b + 1) * 128] = float("nan")
+                    poisoned += 1
+    say("  poisoned %d of %d blocks" % (poisoned, wl.S * wl.Hkv * wl.nb))
+    assert poisoned > 0
+    msa.sparse_attn_prefill(prob, inputs["q"], K, V, bufs.csr_offsets, bufs.csr_entries, bufs.sel, bufs.out,
+                            bufs.ws_prefill, bufs.ws_prefill.numel())
+    torch.cuda.synchronize()
+    assert torch.isfinite(bufs.out.float()).all()
+    assert torch.equal(bufs.out, ref_out)
+    # decode reads only its selected blocks as well
+    db = msa.alloc_decode(prob)
+    msa.run_decode(prob, inputs["q"], K, V, inputs["q_idx"], inputs["k_idx"], db)
+    torch.cuda.synchronize()
+    assert torch.isfinite(db.out.float()).all()
+
+
+# ------------------------------------------------------------------ adversarial top-k
+def _topk_case(scores_np, T, N, k):
+    prob = msa.problem(1, T, N, 8, 1, 128, 64, k)
+    sc = torch.from_numpy(scores_np.astype(np.float32)).cuda().reshape(1, 1, T, -1).contiguous()
+    sel = torch.full((1, 1, T, k), -7, dtype=torch.int32, device="cuda")
+    msa.block_topk(prob, sc, sel)
+    torch.cuda.synchronize()
+    pos = oracle.positions(N, T)
+    ref = oracle.slice_block_topk(scores_np.astype(np.float32).astype(np.float64), pos // 128, k)
+    np.testing.assert_array_equal(sel.cpu().numpy()[0, 0], ref)
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "signed_zero", "few_values", "neg_inf_and_huge",
+                                  "long_all_equal", "long_random", "long_ties_at_threshold"])
+@pytest.mark.parametrize("k", [1, 2, 16, 64])
+def test_topk_adversarial_rows(kind, k):
+    require_gpu()
+    rng = np.random.default_rng(zlib.crc32(kind.encode()) * 100 + k)
+    if kind.startswith("long"):
+        T, N = 130, 8192 * 128
+    else:
+        T, N = 300, 300 * 128
+    nb = (N + 127) // 128
+    if kind in ("all_equal", "long_all_equal"):
+        sc = np.full((T, nb), 0.75)
+    elif kind == "signed_zero":
+        sc = rng.choice([-0.0, 0.0, -1.0, 1.0], size=(T, nb))
+    elif kind == "few_values":
+        sc = rng.integers(0, 3, size=(T, nb)).astype(np.float64)
+    elif kind == "neg_inf_and_huge":
+        sc = rng.choice([-np.inf, np.inf, -3e38, 3e38, 1e-45, -1e-45], size=(T, nb))
+    elif kind == "long_random":
+        sc = rng.standard_normal((T, nb))
+    else:  # many ties exactly at the k-th value
+        sc = rng.standard_normal((T, nb)) - 10
+        sc[:, ::3] = 5.0
+    _topk_case(sc, T, N, k)
+
+
+def test_invert_skewed_selection():
+    """Every query picks block 0 and its own block (sink-like skew), k = 2."""
+    require_gpu()
+    T = N = 8192 * 4
+    k = 2
+    own = oracle.positions(N, T) // 128
+    sel_np = np.stack([np.zeros(T, dtype=np.int32), own.astype(np.int32)], axis=1)
+    sel_np[own == 0, 1] = -1
+    prob = msa.problem(1, T, N, 8, 1, 128, 64, k)
+    sel = torch.from_numpy(sel_np).cuda().reshape(1, 1, T, k).contiguous()
+    nb = prob.nb
+    off = torch.empty((1, 1, nb + 1), dtype=torch.int32, device="cuda")
+    ent = torch.empty((T * k,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((msa.workspace_bytes(prob, msa.MSA_CALL_INVERT),), dtype=torch.uint8, device="cuda")
+    msa.invert_selection(prob, sel, off, ent, ws, ws.numel())
+    torch.cuda.synchronize()
+    r_off, r_ent = oracle.slice_invert(sel_np, nb)
+    np.testing.assert_array_equal(off.cpu().numpy()[0, 0], r_off)
+    np.testing.assert_array_equal(ent.cpu().numpy()[: r_off[-1]], r_ent)
+
+
+def test_generator_device_matches_host():
+    require_gpu()
+    for wl in (W.small("gen", S=2, T=300, N=700, H=4, Hkv=2, d=64, dI=32, k=4, structure="band_sink_needles"),
+               W.small("gen32", S=1, T=100, N=260, H=2, Hkv=1, d=64, dI=32, k=4, dtype=synth.F32),
+               W.small("gen_sn", S=3, T=1, N=1000, H=4, Hkv=2, d=64, dI=64, k=4, structure="sink_needles")):
+        for name, spec in wl.specs().items():
+            dev = synth.device_tensor(spec)
+            host = synth.host_tensor(spec)
+            if spec.dtype == synth.BF16:
+                got = dev.cpu().view(torch.int16).numpy().view(np.uint16)
+            else:
+                got = dev.cpu().numpy()
+            assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(host).view(np.uint8)), (wl.name, name)
