@@ -1,0 +1,297 @@
+"""Benchmark of the MSA hot path on one MI355X.
+
+One step = one full MSA prefill pass over the 131,072-token workload (index scores
++ block max-pool, top-k, inversion, Outer-Gather-Q attention, LSE merge) followed by
+one decode step of 16 sequences over 1,048,576-token caches (index scores, top-k,
+split-K attention + merge).  Inputs are generated on the device before timing and
+stay resident in HBM.
+
+value  = prefill tokens/s = 131,072 / (device time of the prefill part of a step)
+decode = us per decode step (all 16 sequences advance one token), and / 16
+
+Per-kernel device times come from the library's own hipEvent timer (events recorded
+on the launch stream around every launch) over the timed region.  The roofline
+object prices the dominant kernel's ALGORITHMIC work (causal triangle, selected keys
+only, every tensor read or written once) against MI355X peaks (bf16 dense MFMA
+2.5 PFLOP/s, HBM 8 TB/s).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_BF16 = 2.5e15   # FLOP/s, dense
+PEAK_HBM = 8.0e12         # B/s
+METRIC = "MSA prefill tokens/s at 128K & decode µs/token at 1M; % MFMA/HBM peak"
+
+
+# ------------------------------------------------------------------ work model
+def positions(N, T):
+    return np.arange(N - T, N, dtype=np.int64)
+
+
+def prefill_model(S, T, N, H, Hkv, d, dI, k, B=128, esize=2, touched_blocks=None):
+    """Algorithmic flops / bytes per stage of one prefill pass (per launch)."""
+    G = H // Hkv
+    p = positions(N, T)
+    bt = p // B
+    nb = (N + B - 1) // B
+    slots = np.minimum(k, bt + 1)                        # valid selections per (t, g)
+    keys = (slots - 1) * B + (p - bt * B) + 1            # attended keys per (t, g)
+    n_slots = S * Hkv * int(slots.sum())
+    m = {}
+    m["idx_scores"] = dict(flops=2.0 * dI * S * Hkv * float((p + 1).sum()),
+                           bytes=esize * S * Hkv * (T + N) * dI + 4.0 * S * Hkv * float((bt + 1).sum()))
+    rows_reading = bt >= k                               # rows that must rank their past blocks
+    m["block_topk"] = dict(flops=0.0, bytes=4.0 * S * Hkv * float((bt * rows_reading).sum()) + 4.0 * S * Hkv * T * k)
+    m["invert"] = dict(flops=0.0, bytes=4.0 * S * Hkv * T * k + 4.0 * n_slots + 4.0 * S * Hkv * (nb + 1))
+    if touched_blocks is None:
+        touched_blocks = S * Hkv * nb
+    part = n_slots * G * (d * esize + 4.0)
+    m["ogq_attention"] = dict(flops=4.0 * d * G * S * Hkv * float(keys.sum()),
+                              bytes=esize * S * T * H * d + touched_blocks * 2.0 * B * d * esize + part + 4.0 * n_slots)
+    m["lse_merge"] = dict(flops=0.0, bytes=part + esize * S * T * H * d + 4.0 * S * Hkv * T * k)
+    return m
+
+
+def decode_model(S, N, H, Hkv, d, dI, k, B=128, esize=2):
+    G = H // Hkv
+    nb = (N + B - 1) // B
+    m = {}
+    m["idx_scores"] = dict(flops=2.0 * dI * S * Hkv * N, bytes=esize * S * Hkv * (N + 1) * dI + 4.0 * S * Hkv * nb)
+    m["block_topk"] = dict(flops=0.0, bytes=4.0 * S * Hkv * (nb - 1) + 4.0 * S * Hkv * k)
+    m["attention"] = dict(flops=4.0 * d * G * S * Hkv * k * B,
+                          bytes=S * Hkv * k * 2.0 * B * d * esize + 2.0 * esize * S * H * d + 4.0 * S * Hkv * k)
+    return m
+
+
+def attention_reduction_ratio(G, d, dI, N, budget=2048):
+    """Dense-attention flops / MSA flops (index branch + main branch) averaged over a
+    causal prefill of N tokens: 2*G*d*n / (2*G*d*budget + dI*n) at n = N/2."""
+    n = N / 2.0
+    return (2.0 * G * d * n) / (2.0 * G * d * budget + dI * n)
+
+
+def roofline(flops, nbytes, seconds):
+    """Bound by whichever of MFMA or HBM the algorithmic work needs longer on."""
+    t_mfma = flops / PEAK_MFMA_BF16
+    t_hbm = nbytes / PEAK_HBM
+    if t_mfma >= t_hbm:
+        a = flops / seconds / 1e12
+        return dict(bound="mfma", achieved=a, peak=PEAK_MFMA_BF16 / 1e12, unit="TFLOP/s", frac=a / (PEAK_MFMA_BF16 / 1e12))
+    a = nbytes / seconds / 1e9
+    return dict(bound="hbm", achieved=a, peak=PEAK_HBM / 1e9, unit="GB/s", frac=a / (PEAK_HBM / 1e9))
+
+
+# kernel name (library profiler) -> model stage
+PREFILL_KERNELS = {"idx_scores_mfma": "idx_scores", "block_topk": "block_topk", "ogq_mfma": "ogq_attention",
+                   "lse_merge": "lse_merge"}
+KERNEL_SOURCES = {"ogq_mfma": "attention_mfma.hip", "idx_scores_mfma": "index_scores_mfma.hip",
+                  "lse_merge": "attention.hip", "block_topk": "topk.hip"}
+
+
+def source_sha(kernel):
+    f = KERNEL_SOURCES.get(kernel)
+    if f is None:
+        return None
+    with open(os.path.join(ROOT, "block_sparse_long_06_amd", "csrc", f), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if
+    the summary is missing or was taken on a different version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_c2_prefill_128k.json" % kernel)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(wl, inputs, seconds_budget=12.0):
+    """The oracle, as is, on a bounded sample of query rows of the same workload:
+    index scores, top-k, inversion and attention for R rows x all groups.
+    Returns tokens/s (= rows / oracle seconds) and the thread count it used."""
+    import torch
+    import oracle
+    pos_all = positions(wl.N, wl.T)
+    G = wl.G
+    # host copies of one workload's inputs, decoded to float64 (not timed)
+    kI = [oracle.decode(inputs["k_idx"][0, g]) for g in range(wl.Hkv)]
+    K = [oracle.decode(inputs["k"][0, g]) for g in range(wl.Hkv)]
+    V = [oracle.decode(inputs["v"][0, g]) for g in range(wl.Hkv)]
+    rows_all = wl.sampled_rows(4096)
+    done_rows = 0
+    spent = 0.0
+    batch = 16
+    i = 0
+    while spent < seconds_budget and i < len(rows_all):
+        rows = rows_all[i:i + batch]
+        i += batch
+        idx = torch.from_numpy(rows).cuda()
+        qI = [oracle.decode(inputs["q_idx"][0, g][idx]) for g in range(wl.Hkv)]
+        q = oracle.decode(inputs["q"][0][idx])
+        t0 = time.perf_counter()
+        for g in range(wl.Hkv):
+            sc = oracle.slice_index_scores(qI[g], pos_all[rows], kI[g], 128)
+            sel = oracle.slice_block_topk(sc, pos_all[rows] // 128, wl.k)
+            oracle.slice_invert(sel, wl.nb)
+            oracle.slice_attention(q[:, g * G:(g + 1) * G], pos_all[rows], sel, K[g], V[g], 128, 1 / np.sqrt(wl.d))
+        spent += time.perf_counter() - t0
+        done_rows += len(rows)
+    return dict(value=done_rows / spent, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample="%d seeded query rows x %d groups of the 131072-token workload (full index scan, top-k, "
+                       "inversion, attention per row), %.1f s of CPU work" % (done_rows, wl.Hkv, spent))
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the MSA path shards by KV-head group and sequence with no "
+              "exchange inside MSA, and this build runs on a single MI355X only (--gpus %d refused)." % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_long_06_amd as msa
+    import synth
+    from synth import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    print("[bench] device: %s" % torch.cuda.get_device_name(0), file=sys.stderr, flush=True)
+    wp, wd = W.C2, W.C3
+    specs = wp.specs()
+    xp = {n: synth.device_tensor(specs[n]) for n in specs}
+    pprob = wp.problem()
+    pb = msa.alloc_prefill(pprob)
+    xd = db = dprob = None
+    if not args.no_decode:
+        ds = wd.specs()
+        xd = {n: synth.device_tensor(ds[n]) for n in ds}
+        dprob = wd.problem()
+        db = msa.alloc_decode(dprob)
+    torch.cuda.synchronize()
+    print("[bench] inputs resident: prefill %s, decode %s" % (wp.name, wd.name), file=sys.stderr, flush=True)
+
+    def prefill():
+        msa.run_prefill(pprob, xp["q"], xp["k"], xp["v"], xp["q_idx"], xp["k_idx"], pb)
+
+    def decode():
+        msa.run_decode(dprob, xd["q"], xd["k"], xd["v"], xd["q_idx"], xd["k_idx"], db)
+
+    for _ in range(args.warmup):
+        prefill()
+        if db is not None:
+            decode()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    msa.profiler_read(None, reset=True)
+    msa.profiler_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        prefill()
+        ev[i][1].record()
+        if db is not None:
+            decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    msa.profiler_enable(False)
+    kern = {}
+    for name in ("idx_scores_mfma", "block_topk", "invert_count", "invert_scatter", "invert_offsets",
+                 "scan_tile_sums", "scan_top", "scan_apply", "wl_count", "wl_emit", "ogq_mfma", "lse_merge",
+                 "idx_scores_rows", "block_topk_t1", "decode_simple", "decode_merge"):
+        ms, n = msa.profiler_read(name, reset=False)
+        if n:
+            kern[name] = dict(total_ms=ms, launches=n)
+    msa.profiler_read(None, reset=True)
+    prefill_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)) / args.steps
+    decode_ms = (sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)) / args.steps) if db else None
+    print("[bench] timed %d steps: prefill %.3f ms, decode %s ms" % (args.steps, prefill_ms,
+          "%.3f" % decode_ms if decode_ms else "-"), file=sys.stderr, flush=True)
+
+    # algorithmic work of the prefill pass, with the blocks actually touched
+    counts = pb.csr_offsets[..., 1:] - pb.csr_offsets[..., :-1]
+    touched = int((counts > 0).sum())
+    model = prefill_model(wp.S, wp.T, wp.N, wp.H, wp.Hkv, wp.d, wp.dI, wp.k, touched_blocks=touched)
+    stages = {}
+    for kname, stage in PREFILL_KERNELS.items():
+        if kname not in kern:
+            continue
+        per_launch_s = kern[kname]["total_ms"] / kern[kname]["launches"] / 1e3
+        rf = roofline(model[stage]["flops"], model[stage]["bytes"], per_launch_s)
+        stages[kname] = dict(ms=per_launch_s * 1e3, flops=model[stage]["flops"], bytes=model[stage]["bytes"], **rf)
+    inv_ms = sum(kern[n]["total_ms"] for n in ("invert_count", "invert_scatter", "invert_offsets") if n in kern)
+    stages["invert(all launches)"] = dict(ms=inv_ms / args.steps)
+    dominant = max((k for k in stages if k in PREFILL_KERNELS), key=lambda k: stages[k]["ms"])
+    dom = stages[dominant]
+    traffic = measured_traffic(dominant)
+    roof = dict(kernel=dominant, bound=dom["bound"], achieved=dom["achieved"], peak=dom["peak"], unit=dom["unit"],
+                frac=dom["frac"], traffic=traffic,
+                algorithmic_bytes=dom["bytes"], algorithmic_flops=dom["flops"], ms_per_launch=dom["ms"])
+
+    dec = None
+    if db is not None:
+        dm = decode_model(wd.S, wd.N, wd.H, wd.Hkv, wd.d, wd.dI, wd.k)
+        dstages = {}
+        if "idx_scores_rows" in kern:
+            s_ = kern["idx_scores_rows"]["total_ms"] / kern["idx_scores_rows"]["launches"] / 1e3
+            dstages["idx_scores_rows"] = dict(ms=s_ * 1e3, **roofline(dm["idx_scores"]["flops"], dm["idx_scores"]["bytes"], s_))
+        if "block_topk_t1" in kern:
+            s_ = kern["block_topk_t1"]["total_ms"] / kern["block_topk_t1"]["launches"] / 1e3
+            dstages["block_topk_t1"] = dict(ms=s_ * 1e3, **roofline(0.0, dm["block_topk"]["bytes"], s_))
+        if "decode_simple" in kern:
+            s_ = kern["decode_simple"]["total_ms"] / kern["decode_simple"]["launches"] / 1e3
+            dstages["decode_simple"] = dict(ms=s_ * 1e3, **roofline(dm["attention"]["flops"], dm["attention"]["bytes"], s_))
+        if "decode_merge" in kern:
+            dstages["decode_merge"] = dict(ms=kern["decode_merge"]["total_ms"] / kern["decode_merge"]["launches"])
+        dec = dict(workload=wd.description, us_per_step=decode_ms * 1e3, us_per_token_amortised=decode_ms * 1e3 / wd.S,
+                   sequences=wd.S, kv_len=wd.N, stages=dstages)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] oracle CPU baseline ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wp, xp)
+
+    value = wp.T / (prefill_ms / 1e3)
+    ms_per_step = (prefill_ms + (decode_ms or 0.0))
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wp.description, "batch": wp.S, "seq_len": wp.T, "num_heads": wp.H,
+                   "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
+        "prefill_ms": prefill_ms, "wall_s_timed": wall,
+        "decode": dec, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -315,10 +315,10 @@ hipError_t launch_decode_t(const Dims& D, const void* q, const void* k, const vo
 }  // namespace
 
 hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part_lse, const void* part_o,
-                            int part_o_is_bf16, void* out, hipStream_t st) {
+                            int part_o_is_bf16, void* out, hipStream_t st, const char* name) {
   const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
   const dim3 grid((unsigned)((rows + 3) / 4));
-  LaunchScope scope("lse_merge", st);
+  LaunchScope scope(name, st);
   if (D.dtype == MSA_BF16) {
     if (part_o_is_bf16)
       hipLaunchKernelGGL((lse_merge_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, D, sel, part_lse,
@@ -372,7 +372,7 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
                   : launch_ogq_simple_t<float, float, 128>(D, q, k, v, w, entries, st);
   }
   if (e != hipSuccess) return e;
-  return launch_lse_merge(D, sel, w.part_lse, w.part_o, D.dtype == MSA_BF16, out, st);
+  return launch_lse_merge(D, sel, w.part_lse, w.part_o, D.dtype == MSA_BF16, out, st, "lse_merge");
 }
 
 size_t decode_workspace_bytes(const Dims& D) {
@@ -394,7 +394,7 @@ hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void
     e = D.d == 64 ? launch_decode_t<float, 64>(D, q, k, v, sel, part_lse, part_o, st)
                   : launch_decode_t<float, 128>(D, q, k, v, sel, part_lse, part_o, st);
   if (e != hipSuccess) return e;
-  return launch_lse_merge(D, sel, part_lse, part_o, 0, out, st);
+  return launch_lse_merge(D, sel, part_lse, part_o, 0, out, st, "decode_merge");
 }
 
 }  // namespace msa

@@ -48,7 +48,8 @@ hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void
 
 // Shared by the prefill and decode paths: merge per-slot partials into out.
 hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part_lse,
-                            const void* part_o, int part_o_is_bf16, void* out, hipStream_t st);
+                            const void* part_o, int part_o_is_bf16, void* out, hipStream_t st,
+                            const char* name);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

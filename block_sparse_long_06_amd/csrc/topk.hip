@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
 hipError_t launch_block_topk(const Dims& D, const float* scores, int32_t* sel, hipStream_t st) {
   const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
   const int64_t grid = (rows + kWaves - 1) / kWaves;
-  LaunchScope scope("block_topk", st);
+  LaunchScope scope(D.T == 1 ? "block_topk_t1" : "block_topk", st);
   hipLaunchKernelGGL(block_topk_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, st, D, scores, sel);
   return hipGetLastError();
 }
