@@ -135,7 +135,7 @@ def cpu_baseline(wl, inputs, seconds_budget=12.0):
     kI = [oracle.decode(inputs["k_idx"][0, g]) for g in range(wl.Hkv)]
     K = [oracle.decode(inputs["k"][0, g]) for g in range(wl.Hkv)]
     V = [oracle.decode(inputs["v"][0, g]) for g in range(wl.Hkv)]
-    rows_all = wl.sampled_rows(4096)
+    rows_all = wl.sampled_rows(8192)
     done_rows = 0
     spent = 0.0
     batch = 16
@@ -226,7 +226,8 @@ def main():
     kern = {}
     for name in ("idx_scores_mfma", "block_topk", "invert_count", "invert_scatter", "invert_offsets",
                  "scan_tile_sums", "scan_top", "scan_apply", "wl_count", "wl_emit", "ogq_mfma", "lse_merge",
-                 "idx_scores_rows", "block_topk_t1", "decode_simple", "decode_merge"):
+                 "idx_scores_rows", "idx_scores_stream", "block_topk_t1", "decode_items", "decode_ogq_mfma",
+                 "decode_simple", "decode_merge"):
         ms, n = msa.profiler_read(name, reset=False)
         if n:
             kern[name] = dict(total_ms=ms, launches=n)
@@ -260,15 +261,17 @@ def main():
     if db is not None:
         dm = decode_model(wd.S, wd.N, wd.H, wd.Hkv, wd.d, wd.dI, wd.k)
         dstages = {}
-        if "idx_scores_rows" in kern:
-            s_ = kern["idx_scores_rows"]["total_ms"] / kern["idx_scores_rows"]["launches"] / 1e3
-            dstages["idx_scores_rows"] = dict(ms=s_ * 1e3, **roofline(dm["idx_scores"]["flops"], dm["idx_scores"]["bytes"], s_))
+        for kn in ("idx_scores_stream", "idx_scores_rows"):
+            if kn in kern:
+                s_ = kern[kn]["total_ms"] / kern[kn]["launches"] / 1e3
+                dstages[kn] = dict(ms=s_ * 1e3, **roofline(dm["idx_scores"]["flops"], dm["idx_scores"]["bytes"], s_))
         if "block_topk_t1" in kern:
             s_ = kern["block_topk_t1"]["total_ms"] / kern["block_topk_t1"]["launches"] / 1e3
             dstages["block_topk_t1"] = dict(ms=s_ * 1e3, **roofline(0.0, dm["block_topk"]["bytes"], s_))
-        if "decode_simple" in kern:
-            s_ = kern["decode_simple"]["total_ms"] / kern["decode_simple"]["launches"] / 1e3
-            dstages["decode_simple"] = dict(ms=s_ * 1e3, **roofline(dm["attention"]["flops"], dm["attention"]["bytes"], s_))
+        for kn in ("decode_ogq_mfma", "decode_simple"):
+            if kn in kern:
+                s_ = kern[kn]["total_ms"] / kern[kn]["launches"] / 1e3
+                dstages[kn] = dict(ms=s_ * 1e3, **roofline(dm["attention"]["flops"], dm["attention"]["bytes"], s_))
         if "decode_merge" in kern:
             dstages["decode_merge"] = dict(ms=kern["decode_merge"]["total_ms"] / kern["decode_merge"]["launches"])
         dec = dict(workload=wd.description, us_per_step=decode_ms * 1e3, us_per_token_amortised=decode_ms * 1e3 / wd.S,

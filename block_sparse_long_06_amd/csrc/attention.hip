@@ -27,6 +27,9 @@ int ogq_mfma_rows_per_item(const Dims& D);
 hipError_t launch_ogq_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const int4* worklist, const int* n_items, int64_t grid,
                            const int32_t* entries, float* part_lse, uint16_t* part_o, hipStream_t st);
+hipError_t launch_decode_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* sel, int4* wl, int32_t* ent, int* n_items, float* part_lse,
+                              uint16_t* part_o, hipStream_t st);
 
 namespace {
 
@@ -202,7 +205,9 @@ __device__ __forceinline__ void store8(uint16_t* p, const float* v) {
   *reinterpret_cast<uint4*>(p) = u;
 }
 
-// One wave per row (s, t, g); each lane merges 8 consecutive outputs at a time.
+// One wave per row (s, t, g); each lane merges 8 consecutive outputs at a time.  The
+// valid slots are found once per row (a 64-bit mask); partial loads are issued four
+// slots at a time so several 16-byte loads per lane are in flight.
 template <typename T, typename PT>
 __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* __restrict__ sel,
                                                         const float* __restrict__ part_lse,
@@ -215,27 +220,43 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* _
   const int t = (int)((row / D.Hkv) % D.T);
   const int s = (int)(row / ((int64_t)D.Hkv * D.T));
   const int32_t* sl = sel + (((int64_t)s * D.Hkv + g) * D.T + t) * D.k;
+  const uint64_t vmask = __ballot(lane < D.k && sl[lane < D.k ? lane : 0] >= 0);
   const int GD = D.G * D.d;
+  const float* lrow = part_lse + row * D.k * D.G;
+  const PT* orow_in = part_o + row * D.k * GD;
   T* orow = out + (((int64_t)s * D.T + t) * D.H + g * D.G) * D.d;
   for (int c8 = lane; c8 * 8 < GD; c8 += 64) {
     const int h = c8 * 8 / D.d;
     float m = -INFINITY;
     for (int i = 0; i < D.k; ++i)
-      if (sl[i] >= 0) m = fmaxf(m, part_lse[(row * D.k + i) * D.G + h]);
+      if ((vmask >> i) & 1ull) m = fmaxf(m, lrow[i * D.G + h]);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float tot = 0.0f;
-    for (int i = 0; i < D.k; ++i) {
-      if (sl[i] < 0) continue;
-      const float w = exp2f((part_lse[(row * D.k + i) * D.G + h] - m) * kLog2e);
-      tot += w;
-      float o[8];
-      load8f(part_o + (row * D.k + i) * GD + c8 * 8, o);
+    for (int i0 = 0; i0 < D.k; i0 += 4) {
+      float o[4][8];
+      float w[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] = fmaf(w, o[u], acc[u]);
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u;
+        const bool ok = i < D.k && ((vmask >> i) & 1ull);
+        w[u] = ok ? exp2f((lrow[i * D.G + h] - m) * kLog2e) : 0.0f;
+        if (ok) {
+          load8f(orow_in + (int64_t)i * GD + c8 * 8, o[u]);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) o[u][x] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        tot += w[u];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(w[u], o[u][x], acc[x]);
+      }
     }
     const float inv = 1.0f / tot;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] *= inv;
+    for (int x = 0; x < 8; ++x) acc[x] *= inv;
     store8(orow + c8 * 8, acc);
   }
 }
@@ -375,26 +396,66 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
   return launch_lse_merge(D, sel, w.part_lse, w.part_o, D.dtype == MSA_BF16, out, st, "lse_merge");
 }
 
+// Decode workspace: partial lse / O per (s, t, g, slot, head), plus (bf16 path) the
+// per-slot work items of the matrix-core kernel.
+struct DecodeWs {
+  float* part_lse;
+  void* part_o;
+  int4* wl;
+  int32_t* ent;
+  int* n_items;
+};
+
+static DecodeWs decode_layout(const Dims& D, void* base, size_t* total) {
+  const int64_t nslot = (int64_t)D.S * D.T * D.Hkv * D.k;
+  const int64_t npart = nslot * D.G;
+  const bool mfma = ogq_mfma_supported(D);
+  unsigned char* p = static_cast<unsigned char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    void* r = p ? p + off : nullptr;
+    off += align_up(bytes, 256);
+    return r;
+  };
+  DecodeWs w{};
+  w.part_lse = static_cast<float*>(take(npart * sizeof(float)));
+  w.part_o = take((size_t)npart * D.d * (mfma ? 2 : 4));
+  if (mfma) {
+    w.wl = static_cast<int4*>(take(nslot * sizeof(int4)));
+    w.ent = static_cast<int32_t*>(take(nslot * sizeof(int32_t)));
+    w.n_items = static_cast<int*>(take(sizeof(int)));
+  }
+  *total = off;
+  return w;
+}
+
 size_t decode_workspace_bytes(const Dims& D) {
-  const int64_t npart = (int64_t)D.S * D.T * D.Hkv * D.k * D.G;
-  return align_up((size_t)npart * sizeof(float), 256) + align_up((size_t)npart * D.d * sizeof(float), 256);
+  size_t total = 0;
+  (void)decode_layout(D, nullptr, &total);
+  return total;
 }
 
 hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void* v, const int32_t* sel,
                          void* out, void* ws, hipStream_t st) {
-  const int64_t npart = (int64_t)D.S * D.T * D.Hkv * D.k * D.G;
-  float* part_lse = static_cast<float*>(ws);
-  float* part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
-                                           align_up((size_t)npart * sizeof(float), 256));
+  size_t total = 0;
+  const DecodeWs w = decode_layout(D, ws, &total);
   hipError_t e;
+  if (ogq_mfma_supported(D)) {
+    e = launch_decode_mfma(D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), sel, w.wl, w.ent, w.n_items, w.part_lse,
+                           static_cast<uint16_t*>(w.part_o), st);
+    if (e != hipSuccess) return e;
+    return launch_lse_merge(D, sel, w.part_lse, w.part_o, 1, out, st, "decode_merge");
+  }
+  float* po = static_cast<float*>(w.part_o);
   if (D.dtype == MSA_BF16)
-    e = D.d == 64 ? launch_decode_t<uint16_t, 64>(D, q, k, v, sel, part_lse, part_o, st)
-                  : launch_decode_t<uint16_t, 128>(D, q, k, v, sel, part_lse, part_o, st);
+    e = D.d == 64 ? launch_decode_t<uint16_t, 64>(D, q, k, v, sel, w.part_lse, po, st)
+                  : launch_decode_t<uint16_t, 128>(D, q, k, v, sel, w.part_lse, po, st);
   else
-    e = D.d == 64 ? launch_decode_t<float, 64>(D, q, k, v, sel, part_lse, part_o, st)
-                  : launch_decode_t<float, 128>(D, q, k, v, sel, part_lse, part_o, st);
+    e = D.d == 64 ? launch_decode_t<float, 64>(D, q, k, v, sel, w.part_lse, po, st)
+                  : launch_decode_t<float, 128>(D, q, k, v, sel, w.part_lse, po, st);
   if (e != hipSuccess) return e;
-  return launch_lse_merge(D, sel, part_lse, part_o, 0, out, st, "decode_merge");
+  return launch_lse_merge(D, sel, w.part_lse, w.part_o, 0, out, st, "decode_merge");
 }
 
 }  // namespace msa

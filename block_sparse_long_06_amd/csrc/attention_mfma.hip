@@ -4,25 +4,29 @@
 // it is gathered and processed against one on-chip copy), computing the exact
 // block-restricted softmax of section 第二步：精算.
 //
-// Work item = one (sequence, group, KV block) and up to R = 128 / G query rows of its
-// inverted list (ascending rows).  M-rows = (query row, head) pairs, head fastest,
-// so one query row's G heads are G consecutive M-rows; each of the 4 waves owns 32.
+// Work item = one (sequence, group, KV block) and up to kItemRows query rows of its
+// inverted list (ascending rows).  One workgroup of 8 waves stages K and V once; the
+// rows are then cut into sub-chunks of 32 M-rows (M-row = (query row, head), head
+// fastest, so a sub-chunk is 32 / G query rows) and wave w walks sub-chunks w, w + 8,
+// ...  Waves are independent after the staging barrier: each owns an LDS buffer that
+// receives its gathered Q rows (coalesced 16-byte pieces; a query row's G heads are
+// contiguous) and is then reused to transpose its outputs into coalesced stores.
+// The next sub-chunk's Q rows are fetched into registers while the current one
+// computes; two waves per SIMD overlap one wave's softmax with the other's MFMAs.
 //
-//  * K (128 x d) is staged in LDS row-major with a 16-byte row pad; V is staged
-//    TRANSPOSED (d x 128, 8-byte row pad) so a lane can fetch 4 consecutive keys of
-//    one head dimension with one 8-byte read.
-//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys, B = 32 M-rows): the
-//    output column of lane n = lane % 32 is one M-row, so the row max and row sum
-//    are in-lane over 64 values plus one exchange with lane ^ 32.
+//  * LDS: K row-major (16-byte row pad), V TRANSPOSED (d x 128, 8-byte row pad, so a
+//    lane fetches 4 consecutive keys of one head dim with one 8-byte read).
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys, B = 32 M-rows): a lane's
+//    output column is one M-row, so row max and row sum are in-lane over 64 values
+//    plus one exchange with lane ^ 32.
 //  * P = exp2(s - m) stays in registers: accumulator registers 8p..8p+7 of key tile
-//    kt hold 8 keys of the lane's M-row, exactly the 8 k-elements a lane supplies
-//    to a B operand.  So O^T = V^T P^T is accumulated with k-step = (kt, p) whose
-//    key order is the accumulator's row order; the V^T A-operand reads the same
-//    keys from the transposed LDS copy (two runs of 4 consecutive keys).
+//    kt hold 8 keys of the lane's M-row, exactly the 8 k-elements a lane supplies to
+//    a B operand, so O^T = V^T P^T uses k-step (kt, p) with the accumulator's row
+//    order; the V^T A-operand reads the same keys (two runs of 4) from LDS.
 //  * 32x32 accumulator layout: output row i is held by lane half (i % 8) / 4 in
-//    register 4 * (i / 8) + i % 4.  The QK contraction visits head dims in the
-//    order lane half h, k-step s -> dims [64 h + 8 s, +8) (any order works as long
-//    as A and B agree), letting each lane read one contiguous 128-byte half row.
+//    register 4 * (i / 8) + i % 4.  The QK contraction visits head dims in the order
+//    lane half h, k-step s -> dims [d/2 * h + 8 s, +8) (any order works as long as A
+//    and B agree).
 //
 // Output: per (row, slot, head) partial O (bf16, normalised) and lse (fp32, natural
 // log), merged by lse_merge.
@@ -32,31 +36,48 @@ namespace msa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBlk = 128;
-constexpr int kKPad = 16;  // bytes of pad per K row
-constexpr int kVPad = 8;   // bytes of pad per V^T row
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kItemRows = 256;  // query rows per work item
 
 template <int DH>
-struct OgqLds {
-  static constexpr int KROW = DH * 2 + kKPad;
-  static constexpr int VROW = kBlk * 2 + kVPad;
-  unsigned char k[kBlk * KROW];
-  unsigned char vt[DH * VROW];
+struct __attribute__((aligned(16))) OgqLds {
+  static constexpr int KROW = DH * 2 + 16;   // K row, padded
+  static constexpr int VROW = kBlk * 2 + 8;  // V^T row, padded
+  static constexpr int QROW = DH * 2 + 16;   // per-wave Q / O row, padded
+  __attribute__((aligned(16))) unsigned char k[kBlk * KROW];
+  __attribute__((aligned(16))) unsigned char vt[DH * VROW];
+  __attribute__((aligned(16))) unsigned char buf[kWaves][32 * QROW];
+  int64_t qoff[kItemRows];   // element offset of the row's first head in q
+  int64_t pidx[kItemRows];   // partial index ((s*T + t)*Hkv + g)*k + slot
+  int pos[kItemRows];        // absolute position p_t
+  float lse[kWaves][32];
 };
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+// Completes this wave's earlier LDS accesses before its later ones and keeps the
+// compiler from moving LDS accesses across (lanes exchange data through LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
 template <int DH>
 __device__ __forceinline__ void stage_kv(OgqLds<DH>& L, const uint16_t* kb, const uint16_t* vb, int nvalid) {
-  // K: 16-byte chunks, row-major copy with a pad
   constexpr int CPR = DH / 8;
 #pragma unroll
-  for (int u = 0; u < kBlk * CPR / 256; ++u) {
-    const int c = threadIdx.x + 256 * u;
+  for (int u = 0; u < kBlk * CPR / kThreads; ++u) {
+    const int c = threadIdx.x + kThreads * u;
     const int row = c / CPR, col = c % CPR;
     const uint4 val = row < nvalid ? *reinterpret_cast<const uint4*>(kb + row * DH + col * 8)
                                    : make_uint4(0u, 0u, 0u, 0u);
@@ -64,9 +85,8 @@ __device__ __forceinline__ void stage_kv(OgqLds<DH>& L, const uint16_t* kb, cons
   }
   // V^T: thread = (4 consecutive keys, 8 consecutive dims); 4x8 transpose in registers
   const int kg = threadIdx.x & 31;
-#pragma unroll
-  for (int u = 0; u < DH / 64; ++u) {
-    const int dc = (threadIdx.x >> 5) + 8 * u;
+  const int dc = threadIdx.x >> 5;  // 0..15
+  if (dc < DH / 8) {
     uint32_t w[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -88,18 +108,50 @@ __device__ __forceinline__ void stage_kv(OgqLds<DH>& L, const uint16_t* kb, cons
   }
 }
 
+// One wave's gathered Q rows: piece p = lane + 64 u -> M-row p / (DH/8), column p % (DH/8).
+template <int DH>
+struct QRegs {
+  static constexpr int PIECES = 32 * DH / 8 / 64;
+  uint4 v[PIECES];
+};
+
 template <int DH, int G>
-__global__ void __launch_bounds__(256, 2) ogq_mfma(Dims D, const uint16_t* __restrict__ q,
-                                                   const uint16_t* __restrict__ k,
-                                                   const uint16_t* __restrict__ v,
-                                                   const int4* __restrict__ wl,
-                                                   const int* __restrict__ n_items,
-                                                   const int32_t* __restrict__ entries,
-                                                   float* __restrict__ part_lse,
-                                                   uint16_t* __restrict__ part_o) {
+__device__ __forceinline__ void load_q(QRegs<DH>& qr, const OgqLds<DH>& L, const uint16_t* q, int r0, int nrows,
+                                       int lane) {
+  constexpr int CPR = DH / 8;
+#pragma unroll
+  for (int u = 0; u < QRegs<DH>::PIECES; ++u) {
+    const int p = lane + 64 * u;
+    const int mr = p / CPR, col = p % CPR;
+    const int r = mr / G, hh = mr % G;
+    qr.v[u] = r < nrows ? *reinterpret_cast<const uint4*>(q + L.qoff[r0 + r] + hh * DH + col * 8)
+                        : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ void put_q(unsigned char* buf, const QRegs<DH>& qr, int lane) {
+  constexpr int CPR = DH / 8;
+#pragma unroll
+  for (int u = 0; u < QRegs<DH>::PIECES; ++u) {
+    const int p = lane + 64 * u;
+    *reinterpret_cast<uint4*>(buf + (p / CPR) * OgqLds<DH>::QROW + (p % CPR) * 16) = qr.v[u];
+  }
+}
+
+template <int DH, int G>
+__global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __restrict__ q,
+                                                     const uint16_t* __restrict__ k,
+                                                     const uint16_t* __restrict__ v,
+                                                     const int4* __restrict__ wl,
+                                                     const int* __restrict__ n_items,
+                                                     const int32_t* __restrict__ entries,
+                                                     float* __restrict__ part_lse,
+                                                     uint16_t* __restrict__ part_o) {
   constexpr int KS = DH / 16;  // k-steps of the QK contraction
   constexpr int DT = DH / 32;  // output dim tiles of PV
-  constexpr int RPW = 32 / G;  // query rows per wave
+  constexpr int RW = 32 / G;   // query rows per wave sub-chunk
+  constexpr int CPR = DH / 8;
   __shared__ OgqLds<DH> L;
 
   // XCD-aware item order: the 8 XCDs receive workgroups round-robin, so give each
@@ -111,144 +163,192 @@ __global__ void __launch_bounds__(256, 2) ogq_mfma(Dims D, const uint16_t* __res
   if (slot_in_xcd >= per_xcd || item >= n) return;
 
   const int4 w = wl[item];
+  if (w.z <= 0) return;  // empty item (decode slot with no block)
   const int64_t sg = w.x / D.nb;
   const int b = w.x % D.nb;
   const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
   const int j0 = b * kBlk;
   const int nvalid = min(kBlk, D.N - j0);
+  const int rows = w.z;
+
+  // per-row tables (one division per row, once per item)
+  for (int r = threadIdx.x; r < rows; r += kThreads) {
+    const int e = entries[w.y + r];
+    const int t = e / D.k;
+    const int slot = e - t * D.k;
+    L.qoff[r] = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G) * DH;
+    L.pidx[r] = (((int64_t)s * D.T + t) * D.Hkv + g) * D.k + slot;
+    L.pos[r] = D.pos0 + t;
+  }
   stage_kv<DH>(L, k + (sg * D.N + j0) * DH, v + (sg * D.N + j0) * DH, nvalid);
+  __syncthreads();
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int nl = lane & 31;
-  const int rr = wave * RPW + nl / G;  // local query row of this lane's M-row
-  const int hh = nl % G;               // head within the group
-  const bool row_ok = rr < w.z;
-  const int e = entries[w.y + (row_ok ? rr : 0)];
-  const int t = e / D.k;
-  const int slot = e % D.k;
-  const int p = D.pos0 + t;
-
-  // B operand of S^T: this lane's M-row, head dims [64h + 8ks, +8)
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp = q + (((int64_t)s * D.T + t) * D.H + g * G + hh) * DH + (DH / 2) * h;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 8 * ks);
-  }
-  __syncthreads();
-  const bool wave_live = wave * RPW < w.z;
-  if (!wave_live) return;  // no rows for this wave (no later barrier)
-
-  // S^T = K Q^T for the 4 key tiles
-  f32x16 sacc[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    sacc[kt] = f32x16{};
-    const unsigned char* arow = &L.k[(kt * 32 + nl) * OgqLds<DH>::KROW + DH * h];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
-      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kt], 0, 0, 0);
-    }
-  }
-  // scale into log2 units, causal mask inside the own block, row max
+  const int nsub = (rows + RW - 1) / RW;
+  int j = wave;
+  if (j >= nsub) return;
+  unsigned char* buf = L.buf[wave];
   const float sc = D.scale * kLog2e;
-  const bool need_mask = __ballot(row_ok && p < j0 + kBlk - 1) != 0ull;
-  float m = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = sacc[kt][r] * sc;
-      if (need_mask) {
-        const int j = j0 + kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (j > p) x = -INFINITY;
-      }
-      sacc[kt][r] = x;
-      m = fmaxf(m, x);
-    }
-  }
-  m = fmaxf(m, __shfl_xor(m, 32, 64));
-  // P = exp2(s - m); row sum in fp32; P packed to bf16 as PV B-operands
-  float l = 0.0f;
-  bf16x8 pf[4][2];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = exp2f(sacc[kt][8 * pp + 2 * i] - m);
-        const float c = exp2f(sacc[kt][8 * pp + 2 * i + 1] - m);
-        l += a + c;
-        pk[i] = pack_bf16x2(a, c);
-      }
-      pf[kt][pp] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    }
-  }
-  l += __shfl_xor(l, 32, 64);
 
-  // O^T = V^T P^T
-  f32x16 oacc[DT];
+  QRegs<DH> qn;
+  load_q<DH, G>(qn, L, q, j * RW, min(RW, rows - j * RW), lane);
+  put_q<DH>(buf, qn, lane);
+  wave_lds_sync();
+  if (j + kWaves < nsub) load_q<DH, G>(qn, L, q, (j + kWaves) * RW, min(RW, rows - (j + kWaves) * RW), lane);
+
+  while (true) {
+    const int r0 = j * RW;
+    const int nrows = min(RW, rows - r0);
+    const int rr = nl / G;  // this lane's query row within the sub-chunk
+    const bool row_ok = rr < nrows;
+    const int p = L.pos[r0 + (row_ok ? rr : 0)];
+
+    // S^T = K Q^T for the 4 key tiles
+    f32x16 sacc[4];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+    for (int kt = 0; kt < 4; ++kt) sacc[kt] = f32x16{};
+    {
+      const unsigned char* qrow = buf + nl * OgqLds<DH>::QROW + DH * h;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 bq = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const int kb0 = (kt * 32 + 16 * pp + 4 * h) * 2;  // byte offset of the first key run
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const unsigned char* vrow = &L.vt[(dt * 32 + nl) * OgqLds<DH>::VROW];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb0);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb0 + 16);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][pp], oacc[dt], 0, 0, 0);
+        for (int kt = 0; kt < 4; ++kt) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              &L.k[(kt * 32 + nl) * OgqLds<DH>::KROW + DH * h + 16 * ks]);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, sacc[kt], 0, 0, 0);
+        }
       }
     }
-  }
-
-  if (!row_ok) return;
-  const int64_t pidx = (((int64_t)s * D.T + t) * D.Hkv + g) * D.k + slot;
-  const float inv = 1.0f / l;
-  uint16_t* op = part_o + (pidx * G + hh) * DH + 4 * h;
+    // causal mask inside the own block; row max of the raw scores (scale > 0)
+    if (__ballot(row_ok && p < j0 + kBlk - 1) != 0ull) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      uint2 o;
-      o.x = pack_bf16x2(oacc[dt][4 * qd] * inv, oacc[dt][4 * qd + 1] * inv);
-      o.y = pack_bf16x2(oacc[dt][4 * qd + 2] * inv, oacc[dt][4 * qd + 3] * inv);
-      *reinterpret_cast<uint2*>(op + dt * 32 + 8 * qd) = o;
+        for (int r = 0; r < 16; ++r)
+          if (j0 + kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3) > p) sacc[kt][r] = -INFINITY;
     }
+    float m = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[kt][r]);
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const float msc = m * sc;
+    float l = 0.0f;
+    bf16x8 pf[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * pp + 2 * i], sc, -msc));
+          const float c = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * pp + 2 * i + 1], sc, -msc));
+          l += a + c;
+          pk[i] = cvt_bf16x2(a, c);
+        }
+        pf[kt][pp] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      }
+    }
+    l += __shfl_xor(l, 32, 64);
+
+    // O^T = V^T P^T
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int kb0 = (kt * 32 + 16 * pp + 4 * h) * 2;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const unsigned char* vrow = &L.vt[(dt * 32 + nl) * OgqLds<DH>::VROW];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb0);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb0 + 16);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][pp], oacc[dt], 0, 0, 0);
+        }
+      }
+    }
+    wave_lds_sync();  // this wave's Q rows are consumed: the buffer takes the outputs
+
+    const float inv = 1.0f / l;
+    unsigned char* orow = buf + nl * OgqLds<DH>::QROW + 8 * h;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        uint2 o;
+        o.x = cvt_bf16x2(oacc[dt][4 * qd] * inv, oacc[dt][4 * qd + 1] * inv);
+        o.y = cvt_bf16x2(oacc[dt][4 * qd + 2] * inv, oacc[dt][4 * qd + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + (dt * 32 + 8 * qd) * 2) = o;
+      }
+    }
+    if (h == 0) L.lse[wave][nl] = (msc + __builtin_amdgcn_logf(l)) * kLn2;
+    wave_lds_sync();
+
+    // coalesced partial stores: (row, slot) -> G heads x d contiguous
+#pragma unroll
+    for (int u = 0; u < QRegs<DH>::PIECES; ++u) {
+      const int pc = lane + 64 * u;
+      const int mr = pc / CPR, col = pc % CPR;
+      const int r = mr / G, hh = mr % G;
+      if (r < nrows)
+        *reinterpret_cast<uint4*>(part_o + (L.pidx[r0 + r] * G + hh) * DH + col * 8) =
+            *reinterpret_cast<const uint4*>(buf + mr * OgqLds<DH>::QROW + col * 16);
+    }
+    if (lane < 32 && lane / G < nrows) part_lse[L.pidx[r0 + lane / G] * G + lane % G] = L.lse[wave][lane];
+
+    j += kWaves;
+    if (j >= nsub) break;
+    wave_lds_sync();  // outputs read back: the buffer takes the next Q rows
+    put_q<DH>(buf, qn, lane);
+    wave_lds_sync();
+    if (j + kWaves < nsub) load_q<DH, G>(qn, L, q, (j + kWaves) * RW, min(RW, rows - (j + kWaves) * RW), lane);
   }
-  if (h == 0) part_lse[pidx * G + hh] = (m + log2f(l)) * kLn2;
 }
 
 template <int DH, int G>
-hipError_t launch_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int4* wl,
-                    const int* n_items, int64_t grid, const int32_t* entries, float* part_lse,
-                    uint16_t* part_o, hipStream_t st) {
-  LaunchScope scope("ogq_mfma", st);
-  hipLaunchKernelGGL((ogq_mfma<DH, G>), dim3((unsigned)grid), dim3(256), 0, st, D, q, k, v, wl, n_items,
+void launch_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int4* wl,
+              const int* n_items, int64_t grid, const int32_t* entries, float* part_lse, uint16_t* part_o,
+              hipStream_t st) {
+  hipLaunchKernelGGL((ogq_mfma<DH, G>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, wl, n_items,
                      entries, part_lse, part_o);
-  return hipGetLastError();
 }
 
-template <int DH>
-hipError_t launch_dh(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int4* wl,
-                     const int* n_items, int64_t grid, const int32_t* entries, float* part_lse,
-                     uint16_t* part_o, hipStream_t st) {
-  switch (D.G) {
-    case 1: return launch_t<DH, 1>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
-    case 2: return launch_t<DH, 2>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
-    case 4: return launch_t<DH, 4>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
-    case 8: return launch_t<DH, 8>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
-    default: return launch_t<DH, 16>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
-  }
+void launch_any(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int4* wl,
+                const int* n_items, int64_t grid, const int32_t* entries, float* part_lse, uint16_t* part_o,
+                hipStream_t st) {
+#define MSA_OGQ_CASE(DH_, G_) \
+  if (D.d == DH_ && D.G == G_) return launch_t<DH_, G_>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st)
+  MSA_OGQ_CASE(128, 8); MSA_OGQ_CASE(128, 1); MSA_OGQ_CASE(128, 2); MSA_OGQ_CASE(128, 4); MSA_OGQ_CASE(128, 16);
+  MSA_OGQ_CASE(64, 8); MSA_OGQ_CASE(64, 1); MSA_OGQ_CASE(64, 2); MSA_OGQ_CASE(64, 4); MSA_OGQ_CASE(64, 16);
+#undef MSA_OGQ_CASE
+}
+
+// Decode: one work item per (sequence, query row, group, slot) holding that single row,
+// so every selected block is processed once for its query (query-centric split-K).
+__global__ void __launch_bounds__(256) decode_items(Dims D, const int32_t* __restrict__ sel, int4* __restrict__ wl,
+                                                    int32_t* __restrict__ ent, int* __restrict__ n_items) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = (int64_t)D.S * D.T * D.Hkv * D.k;
+  if (i == 0) *n_items = (int)n;
+  if (i >= n) return;
+  const int slot = (int)(i % D.k);
+  const int g = (int)((i / D.k) % D.Hkv);
+  const int t = (int)((i / ((int64_t)D.k * D.Hkv)) % D.T);
+  const int s = (int)(i / ((int64_t)D.k * D.Hkv * D.T));
+  const int64_t sg = (int64_t)s * D.Hkv + g;
+  const int b = sel[(sg * D.T + t) * D.k + slot];
+  const bool ok = b >= 0 && b < D.nb;
+  wl[i] = make_int4(ok ? (int)(sg * D.nb + b) : 0, (int)i, ok ? 1 : 0, 0);
+  ent[i] = t * D.k + slot;
 }
 
 }  // namespace
@@ -258,14 +358,34 @@ bool ogq_mfma_supported(const Dims& D) {
          (D.G == 1 || D.G == 2 || D.G == 4 || D.G == 8 || D.G == 16);
 }
 
-int ogq_mfma_rows_per_item(const Dims& D) { return 128 / D.G; }
+int ogq_mfma_rows_per_item(const Dims& D) {
+  (void)D;
+  return kItemRows;
+}
 
 hipError_t launch_ogq_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const int4* wl, const int* n_items, int64_t ub, const int32_t* entries,
                            float* part_lse, uint16_t* part_o, hipStream_t st) {
   const int64_t grid = (ub + 7) / 8 * 8 + 8;  // >= 8 * ceil(n_items / 8) for any n_items <= ub
-  if (D.d == 64) return launch_dh<64>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
-  return launch_dh<128>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
+  LaunchScope scope("ogq_mfma", st);
+  launch_any(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* sel, int4* wl, int32_t* ent, int* n_items, float* part_lse,
+                              uint16_t* part_o, hipStream_t st) {
+  const int64_t n = (int64_t)D.S * D.T * D.Hkv * D.k;
+  {
+    LaunchScope scope("decode_items", st);
+    hipLaunchKernelGGL(decode_items, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, D, sel, wl, ent, n_items);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t grid = (n + 7) / 8 * 8 + 8;
+  LaunchScope scope("decode_ogq_mfma", st);
+  launch_any(D, q, k, v, wl, n_items, grid, ent, part_lse, part_o, st);
+  return hipGetLastError();
 }
 
 }  // namespace msa
