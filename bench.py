@@ -167,6 +167,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy 3 times (the known-size reference "
+                         "for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MSA path shards by KV-head group and sequence with no "
@@ -181,6 +184,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     print("[bench] device: %s" % torch.cuda.get_device_name(0), file=sys.stderr, flush=True)
+    if args.copy_probe:
+        src = torch.ones((1 << 29,), dtype=torch.bfloat16, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] copy probe: 3 x 1 GiB device copies", file=sys.stderr, flush=True)
     wp, wd = W.C2, W.C3
     specs = wp.specs()
     xp = {n: synth.device_tensor(specs[n]) for n in specs}

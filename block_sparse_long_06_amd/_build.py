@@ -19,6 +19,8 @@ ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-core accumulators in ordinary VGPRs: the epilogues read every element
+            "-mllvm", "-amdgpu-mfma-vgpr-form=true",
             "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
 
 

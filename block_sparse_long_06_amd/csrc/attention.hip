@@ -205,15 +205,22 @@ __device__ __forceinline__ void store8(uint16_t* p, const float* v) {
   *reinterpret_cast<uint4*>(p) = u;
 }
 
-// One wave per row (s, t, g); each lane merges 8 consecutive outputs at a time.  The
-// valid slots are found once per row (a 64-bit mask); partial loads are issued four
-// slots at a time so several 16-byte loads per lane are in flight.
+// One wave per row (s, t, g).  The row's slot lse values (k x G floats, contiguous)
+// are loaded with one coalesced access into LDS, turned there into normalised
+// weights w[i][h] = exp(lse_i - max) / sum, and lane l then accumulates the 8
+// consecutive outputs of chunks l, l + 64, ... with the partial loads of 8 slots
+// issued back to back.  Invalid slots (sel = -1) get weight 0 and are not loaded.
+constexpr int kMergeMaxKG = 64 * 16;  // k * G
+
 template <typename T, typename PT>
 __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* __restrict__ sel,
                                                         const float* __restrict__ part_lse,
                                                         const PT* __restrict__ part_o, T* __restrict__ out) {
+  __shared__ float wbuf[4][kMergeMaxKG];
+  __shared__ float hstat[4][2][16];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
   if (row >= rows) return;
   const int g = (int)(row % D.Hkv);
@@ -221,42 +228,56 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* _
   const int s = (int)(row / ((int64_t)D.Hkv * D.T));
   const int32_t* sl = sel + (((int64_t)s * D.Hkv + g) * D.T + t) * D.k;
   const uint64_t vmask = __ballot(lane < D.k && sl[lane < D.k ? lane : 0] >= 0);
-  const int GD = D.G * D.d;
-  const float* lrow = part_lse + row * D.k * D.G;
-  const PT* orow_in = part_o + row * D.k * GD;
-  T* orow = out + (((int64_t)s * D.T + t) * D.H + g * D.G) * D.d;
-  for (int c8 = lane; c8 * 8 < GD; c8 += 64) {
-    const int h = c8 * 8 / D.d;
+  const int G = D.G, KG = D.k * D.G, GD = D.G * D.d;
+  const float* lrow = part_lse + row * KG;
+  const PT* prow = part_o + row * (int64_t)D.k * GD;
+  T* orow = out + (((int64_t)s * D.T + t) * D.H + g * G) * D.d;
+  float* wb = wbuf[wave];
+  for (int x = lane; x < KG; x += 64) wb[x] = ((vmask >> (x / G)) & 1ull) ? lrow[x] : -INFINITY;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < G) {
     float m = -INFINITY;
-    for (int i = 0; i < D.k; ++i)
-      if ((vmask >> i) & 1ull) m = fmaxf(m, lrow[i * D.G + h]);
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < D.k; ++i) m = fmaxf(m, wb[i * G + lane]);
     float tot = 0.0f;
-    for (int i0 = 0; i0 < D.k; i0 += 4) {
-      float o[4][8];
-      float w[4];
+    for (int i = 0; i < D.k; ++i) tot += __builtin_amdgcn_exp2f((wb[i * G + lane] - m) * kLog2e);
+    hstat[wave][0][lane] = m;
+    hstat[wave][1][lane] = 1.0f / tot;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int x = lane; x < KG; x += 64) {
+    const int hh = x % G;
+    wb[x] = __builtin_amdgcn_exp2f((wb[x] - hstat[wave][0][hh]) * kLog2e) * hstat[wave][1][hh];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int c8 = lane; c8 * 8 < GD; c8 += 64) {
+    const int hh = c8 * 8 / D.d;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i0 = 0; i0 < D.k; i0 += 8) {
+      float o[8][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = i0 + u;
-        const bool ok = i < D.k && ((vmask >> i) & 1ull);
-        w[u] = ok ? exp2f((lrow[i * D.G + h] - m) * kLog2e) : 0.0f;
-        if (ok) {
-          load8f(orow_in + (int64_t)i * GD + c8 * 8, o[u]);
+        if (i < D.k && ((vmask >> i) & 1ull)) {
+          load8f(prow + (int64_t)i * GD + c8 * 8, o[u]);
         } else {
 #pragma unroll
           for (int x = 0; x < 8; ++x) o[u][x] = 0.0f;
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        tot += w[u];
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u;
+        const float w = i < D.k ? wb[i * G + hh] : 0.0f;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[x] = fmaf(w[u], o[u][x], acc[x]);
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(w, o[u][x], acc[x]);
       }
     }
-    const float inv = 1.0f / tot;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) acc[x] *= inv;
     store8(orow + c8 * 8, acc);
   }
 }

@@ -139,7 +139,8 @@ __device__ __forceinline__ void put_q(unsigned char* buf, const QRegs<DH>& qr, i
   }
 }
 
-template <int DH, int G>
+// DECODE only names a separate instantiation for the decode launches (same code).
+template <int DH, int G, bool DECODE>
 __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      const uint16_t* __restrict__ v,
@@ -314,19 +315,20 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
   }
 }
 
-template <int DH, int G>
+template <int DH, int G, bool DECODE>
 void launch_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int4* wl,
               const int* n_items, int64_t grid, const int32_t* entries, float* part_lse, uint16_t* part_o,
               hipStream_t st) {
-  hipLaunchKernelGGL((ogq_mfma<DH, G>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, wl, n_items,
+  hipLaunchKernelGGL((ogq_mfma<DH, G, DECODE>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, wl, n_items,
                      entries, part_lse, part_o);
 }
 
+template <bool DECODE>
 void launch_any(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int4* wl,
                 const int* n_items, int64_t grid, const int32_t* entries, float* part_lse, uint16_t* part_o,
                 hipStream_t st) {
 #define MSA_OGQ_CASE(DH_, G_) \
-  if (D.d == DH_ && D.G == G_) return launch_t<DH_, G_>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st)
+  if (D.d == DH_ && D.G == G_) return launch_t<DH_, G_, DECODE>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st)
   MSA_OGQ_CASE(128, 8); MSA_OGQ_CASE(128, 1); MSA_OGQ_CASE(128, 2); MSA_OGQ_CASE(128, 4); MSA_OGQ_CASE(128, 16);
   MSA_OGQ_CASE(64, 8); MSA_OGQ_CASE(64, 1); MSA_OGQ_CASE(64, 2); MSA_OGQ_CASE(64, 4); MSA_OGQ_CASE(64, 16);
 #undef MSA_OGQ_CASE
@@ -368,7 +370,7 @@ hipError_t launch_ogq_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, 
                            float* part_lse, uint16_t* part_o, hipStream_t st) {
   const int64_t grid = (ub + 7) / 8 * 8 + 8;  // >= 8 * ceil(n_items / 8) for any n_items <= ub
   LaunchScope scope("ogq_mfma", st);
-  launch_any(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
+  launch_any<false>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
   return hipGetLastError();
 }
 
@@ -384,7 +386,7 @@ hipError_t launch_decode_mfma(const Dims& D, const uint16_t* q, const uint16_t* 
   if (e != hipSuccess) return e;
   const int64_t grid = (n + 7) / 8 * 8 + 8;
   LaunchScope scope("decode_ogq_mfma", st);
-  launch_any(D, q, k, v, wl, n_items, grid, ent, part_lse, part_o, st);
+  launch_any<true>(D, q, k, v, wl, n_items, grid, ent, part_lse, part_o, st);
   return hipGetLastError();
 }
 

@@ -11,11 +11,15 @@
 //
 // v_mfma_f32_32x32x16_bf16 with A = 32 keys, B = 32 queries: output column
 // n = lane % 32 is one query, so a lane's 16 accumulators are 16 keys of ONE
-// query and the block max is an in-register reduction plus one exchange with
-// lane ^ 32 (which holds the other 16 keys of each 32-key tile).  Output row i of
+// query and the block max is an in-register max3 chain plus one exchange with
+// lane ^ 32 (which holds the other 16 keys of each 32-key tile).  All 32 MFMAs of
+// a block go to 8 independent accumulators before any is read.  Output row i of
 // the 32x32 tile lives in lane half (i % 8) / 4, register 4 * (i / 8) + i % 4.
 // The contraction over dI may visit the index dimensions in any order as long
 // as A and B agree; here lane half h of k-step s covers dims [16 s + 8 h, +8).
+//
+// Each row's block maxima of the chunk are collected in LDS and written at the end
+// as one contiguous run per row (whole cache lines instead of scattered pieces).
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -28,16 +32,25 @@ constexpr int kQW = 64;          // queries per wave
 constexpr int kQB = 4 * kQW;     // queries per workgroup
 constexpr int kChunk = 32;       // key blocks per workgroup
 constexpr int kBlk = 128;        // block size
+constexpr int kOutPad = kChunk + 1;
+
+__device__ __forceinline__ float max16(const f32x16& a) {
+  float m = __builtin_fmaxf(__builtin_fmaxf(a[0], a[1]), a[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, a[r]), a[r + 1]);
+  return __builtin_fmaxf(m, a[15]);
+}
 
 template <int DI>
-__global__ void __launch_bounds__(256) idx_scores_mfma(Dims D, const uint16_t* __restrict__ q_idx,
-                                                       const uint16_t* __restrict__ k_idx,
-                                                       float* __restrict__ scores) {
+__global__ void __launch_bounds__(256, 2) idx_scores_mfma(Dims D, const uint16_t* __restrict__ q_idx,
+                                                          const uint16_t* __restrict__ k_idx,
+                                                          float* __restrict__ scores) {
   constexpr int KS = DI / 16;                 // MFMA k-steps
   constexpr int ROWB = DI * 2 + 16;           // padded LDS bytes per key row
   constexpr int CPR = DI / 8;                 // 16-byte chunks per key row
   constexpr int PER_T = kBlk * CPR / 256;     // staging chunks per thread
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][kBlk * ROWB];
+  __shared__ float outb[4][kQW][kOutPad];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -67,13 +80,6 @@ __global__ void __launch_bounds__(256) idx_scores_mfma(Dims D, const uint16_t* _
   const int t_w0 = min(t_first + wave * kQW, D.T - 1);
   const int bmask = (D.pos0 + t_w0) / kBlk;
 
-  // my output row (lane half h writes query tile h) and its own block
-  const int t_out = t_first + wave * kQW + h * 32 + n;
-  const bool row_ok = t_out < D.T;
-  const int bt_out = row_ok ? (D.pos0 + t_out) / kBlk : -1;
-  float* out_row = scores + (sg * D.T + (row_ok ? t_out : 0)) * (int64_t)D.nb;
-  const bool vec_out = (D.nb & 3) == 0;
-
   const uint16_t* kbase = k_idx + sg * (int64_t)D.N * DI;
   uint4 stage[PER_T];
   auto gload = [&](int b) {
@@ -99,12 +105,10 @@ __global__ void __launch_bounds__(256) idx_scores_mfma(Dims D, const uint16_t* _
   lstore(0);
   __syncthreads();
 
-  float outv[4];
   for (int b = b0; b <= b1; ++b) {
     const int buf = (b - b0) & 1;
     if (b < b1) gload(b + 1);
-    float rmax[2] = {-INFINITY, -INFINITY};
-    const bool masked = b >= bmask;
+    f32x16 acc[2][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       bf16x8 af[KS];
@@ -113,39 +117,48 @@ __global__ void __launch_bounds__(256) idx_scores_mfma(Dims D, const uint16_t* _
       for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(arow + ks * 32);
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        f32x16 acc = {};
+        acc[qt][kt] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[qt][ks], acc, 0, 0, 0);
-        if (masked) {
+          acc[qt][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[qt][ks], acc[qt][kt], 0, 0, 0);
+      }
+    }
+    if (b >= bmask) {  // keys after the query's position do not count
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
           const int jb = b * kBlk + kt * 32 + 4 * h;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[r] = -INFINITY;
+            if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[qt][kt][r] = -INFINITY;
         }
-        float m = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-#pragma unroll
-        for (int r = 4; r < 16; r += 4) m = fmaxf(m, fmaxf(fmaxf(acc[r], acc[r + 1]), fmaxf(acc[r + 2], acc[r + 3])));
-        rmax[qt] = fmaxf(rmax[qt], m);
-      }
     }
+    float rmax[2];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) rmax[qt] = fmaxf(rmax[qt], __shfl_xor(rmax[qt], 32, 64));
-    const int slot = (b - b0) & 3;
-    outv[slot] = h == 0 ? rmax[0] : rmax[1];
-    if (slot == 3 || b == b1) {
-      const int bs = b - slot;
-      if (row_ok) {
-        if (vec_out && slot == 3 && b <= bt_out) {
-          *reinterpret_cast<float4*>(out_row + bs) = make_float4(outv[0], outv[1], outv[2], outv[3]);
-        } else {
-          for (int u = 0; u <= slot; ++u)
-            if (bs + u <= bt_out) out_row[bs + u] = outv[u];
-        }
-      }
+    for (int qt = 0; qt < 2; ++qt) {
+      const float m01 = __builtin_fmaxf(max16(acc[qt][0]), max16(acc[qt][1]));
+      const float m23 = __builtin_fmaxf(max16(acc[qt][2]), max16(acc[qt][3]));
+      rmax[qt] = __builtin_fmaxf(m01, m23);
+      rmax[qt] = __builtin_fmaxf(rmax[qt], __shfl_xor(rmax[qt], 32, 64));
     }
+    // lane half h records query tile h (both halves hold both maxima after the exchange)
+    outb[wave][h * 32 + n][b - b0] = h == 0 ? rmax[0] : rmax[1];
     if (b < b1) lstore(buf ^ 1);
     __syncthreads();
+  }
+
+  // one contiguous run per row: blocks b0 .. min(b1, own block)
+  const int t_out = t_first + wave * kQW + lane;
+  if (t_out < D.T) {
+    const int bt = (D.pos0 + t_out) / kBlk;
+    const int len = min(b1, bt) - b0 + 1;
+    float* out_row = scores + (sg * D.T + t_out) * (int64_t)D.nb + b0;
+    const float* src = outb[wave][lane];
+    int u = 0;
+    if ((D.nb & 3) == 0)
+      for (; u + 4 <= len; u += 4) *reinterpret_cast<float4*>(out_row + u) = make_float4(src[u], src[u + 1], src[u + 2], src[u + 3]);
+    for (; u < len; ++u) out_row[u] = src[u];
   }
 }
 

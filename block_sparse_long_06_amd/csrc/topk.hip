@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kCap = 512;
+constexpr int kRegPerLane = 16;  // rows of up to 1024 blocks are held in registers
 
 __device__ __forceinline__ uint32_t ord_key(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -127,6 +128,68 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
     return;
   }
   const float* sc = scores + row * (int64_t)D.nb;
+  if (n <= 64 * kRegPerLane) {
+    // Fast path: the row lives in registers (element i*64 + lane in slot i).
+    uint32_t o[kRegPerLane];
+    uint32_t lm = 0;
+#pragma unroll
+    for (int i = 0; i < kRegPerLane; ++i) {
+      const int c = i * 64 + lane;
+      o[i] = c < n ? ord_key(sc[c]) : 0u;
+      lm = o[i] > lm ? o[i] : lm;
+    }
+    uint32_t t1 = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = t1 | (1u << bit);
+      if (__popcll(__ballot(lm >= cand)) >= need) t1 = cand;
+    }
+    // candidates (ord >= t1) compacted in ascending id order
+    int C = 0;
+#pragma unroll
+    for (int i = 0; i < kRegPerLane; ++i) {
+      const bool f = i * 64 + lane < n && o[i] >= t1;
+      const uint64_t m = __ballot(f);
+      const int p = C + lanes_below(m);
+      if (f && p < kCap) {
+        s_ord[wave][p] = o[i];
+        s_id[wave][p] = i * 64 + lane;
+      }
+      C += __popcll(m);
+    }
+    if (C <= 64) {
+      // one candidate per lane: each radix step is one compare and one ballot
+      const bool have = lane < C;
+      const uint32_t co = have ? s_ord[wave][lane] : 0u;
+      const int32_t cid = have ? s_id[wave][lane] : 0;
+      uint32_t tau = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        if (__popcll(__ballot(have && co >= cand)) >= need) tau = cand;
+      }
+      const int c_gt = __popcll(__ballot(have && co > tau));
+      const uint64_t eqm = __ballot(have && co == tau);
+      const int need_eq = need - c_gt;
+      // ties at tau: the lowest ids win; candidates are in ascending id order, so the
+      // first need_eq set bits of eqm are taken
+      uint64_t take_eq = eqm;
+      for (int drop = __popcll(eqm) - need_eq; drop > 0; --drop) take_eq &= ~(1ull << (63 - __builtin_clzll(take_eq)));
+      const bool f = have && (co > tau || ((take_eq >> lane) & 1ull));
+      const uint64_t m = __ballot(f);
+      const int at = lanes_below(m);
+      if (f && at < need) out[at] = cid;
+      if (lane == 0) out[need] = bt;
+      return;
+    }
+    if (C <= kCap) {
+      LdsSrc src{s_ord[wave], s_id[wave], C};
+      select_and_write(src, lane, need, out);
+    } else {
+      RowSrc src{sc, n};
+      select_and_write(src, lane, need, out);
+    }
+    if (lane == 0) out[need] = bt;
+    return;
+  }
   // A. lane maxima over a strided share of the row
   uint32_t lmax = 0;
   for (int i = lane; i < n; i += 64) {
