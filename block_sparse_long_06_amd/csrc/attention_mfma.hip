@@ -29,7 +29,8 @@
 //    and B agree).
 //
 // Output: per (row, slot, head) partial O (bf16, normalised) and lse (fp32, natural
-// log), merged by lse_merge.
+// log), merged by lse_merge.  Partial O is written with non-temporal stores: it is
+// read back only by the merge, long after, and should not evict K/V or Q lines.
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -39,6 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlk = 128;
 constexpr int kWaves = 8;
@@ -301,8 +303,8 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
       const int mr = pc / CPR, col = pc % CPR;
       const int r = mr / G, hh = mr % G;
       if (r < nrows)
-        *reinterpret_cast<uint4*>(part_o + (L.pidx[r0 + r] * G + hh) * DH + col * 8) =
-            *reinterpret_cast<const uint4*>(buf + mr * OgqLds<DH>::QROW + col * 16);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(buf + mr * OgqLds<DH>::QROW + col * 16),
+                                    reinterpret_cast<u32x4*>(part_o + (L.pidx[r0 + r] * G + hh) * DH + col * 8));
     }
     if (lane < 32 && lane / G < nrows) part_lse[L.pidx[r0 + lane / G] * G + lane % G] = L.lse[wave][lane];
 

@@ -12,8 +12,11 @@
 // v_mfma_f32_32x32x16_bf16 with A = 32 keys, B = 32 queries: output column
 // n = lane % 32 is one query, so a lane's 16 accumulators are 16 keys of ONE
 // query and the block max is an in-register max3 chain plus one exchange with
-// lane ^ 32 (which holds the other 16 keys of each 32-key tile).  All 32 MFMAs of
-// a block go to 8 independent accumulators before any is read.  Output row i of
+// lane ^ 32 (which holds the other 16 keys of each 32-key tile).  The 32 MFMAs of
+// a block go to 8 independent accumulators, and key tile kt-1 is reduced only after
+// the MFMAs of tile kt are issued, so the max chain overlaps the matrix core.  The
+// causal mask is applied only in blocks that reach a query's position (a separate
+// instantiation of the block body).  Output row i of
 // the 32x32 tile lives in lane half (i % 8) / 4, register 4 * (i / 8) + i % 4.
 // The contraction over dI may visit the index dimensions in any order as long
 // as A and B agree; here lane half h of k-step s covers dims [16 s + 8 h, +8).
@@ -21,6 +24,7 @@
 // Each row's block maxima of the chunk are collected in LDS and written at the end
 // as one contiguous run per row (whole cache lines instead of scattered pieces).
 #include "msa_internal.hpp"
+#include <type_traits>
 
 namespace msa {
 namespace {
@@ -108,40 +112,51 @@ __global__ void __launch_bounds__(256, 2) idx_scores_mfma(Dims D, const uint16_t
   for (int b = b0; b <= b1; ++b) {
     const int buf = (b - b0) & 1;
     if (b < b1) gload(b + 1);
-    f32x16 acc[2][4];
+    float rmax[2] = {-INFINITY, -INFINITY};
+    auto body = [&](auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      f32x16 acc[2][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      bf16x8 af[KS];
-      const unsigned char* arow = &lds[buf][(kt * 32 + n) * ROWB + 16 * h];
+      for (int kt = 0; kt < 4; ++kt) {
+        bf16x8 af[KS];
+        const unsigned char* arow = &lds[buf][(kt * 32 + n) * ROWB + 16 * h];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(arow + ks * 32);
+        for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(arow + ks * 32);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          acc[qt][kt] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc[qt][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[qt][ks], acc[qt][kt], 0, 0, 0);
+        }
+        if (kt >= 1) {
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            if (MASKED) {
+              const int jb = b * kBlk + (kt - 1) * 32 + 4 * h;
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[qt][kt - 1][r] = -INFINITY;
+            }
+            rmax[qt] = __builtin_fmaxf(rmax[qt], max16(acc[qt][kt - 1]));
+          }
+        }
+      }
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        acc[qt][kt] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc[qt][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[qt][ks], acc[qt][kt], 0, 0, 0);
-      }
-    }
-    if (b >= bmask) {  // keys after the query's position do not count
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const int jb = b * kBlk + kt * 32 + 4 * h;
+        if (MASKED) {
+          const int jb = b * kBlk + 3 * 32 + 4 * h;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[qt][kt][r] = -INFINITY;
+            if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[qt][3][r] = -INFINITY;
         }
-    }
-    float rmax[2];
+        rmax[qt] = __builtin_fmaxf(rmax[qt], max16(acc[qt][3]));
+      }
+    };
+    if (b >= bmask) body(std::true_type{});
+    else body(std::false_type{});
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float m01 = __builtin_fmaxf(max16(acc[qt][0]), max16(acc[qt][1]));
-      const float m23 = __builtin_fmaxf(max16(acc[qt][2]), max16(acc[qt][3]));
-      rmax[qt] = __builtin_fmaxf(m01, m23);
-      rmax[qt] = __builtin_fmaxf(rmax[qt], __shfl_xor(rmax[qt], 32, 64));
-    }
+    for (int qt = 0; qt < 2; ++qt) rmax[qt] = __builtin_fmaxf(rmax[qt], __shfl_xor(rmax[qt], 32, 64));
     // lane half h records query tile h (both halves hold both maxima after the exchange)
     outb[wave][h * 32 + n][b - b0] = h == 0 ? rmax[0] : rmax[1];
     if (b < b1) lstore(buf ^ 1);
