@@ -155,8 +155,8 @@ def cpu_baseline(wl, inputs, seconds_budget=12.0):
         spent += time.perf_counter() - t0
         done_rows += len(rows)
     return dict(value=done_rows / spent, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                sample="%d seeded query rows x %d groups of the 131072-token workload (full index scan, top-k, "
-                       "inversion, attention per row), %.1f s of CPU work" % (done_rows, wl.Hkv, spent))
+                sample="%d seeded query rows x %d groups of the %s workload (full index scan, top-k, "
+                       "inversion, attention per row), %.1f s of CPU work" % (done_rows, wl.Hkv, wl.name, spent))
 
 
 # ------------------------------------------------------------------ main
@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--prefill", default="C2", choices=["C1", "C2", "C4"],
+                    help="prefill workload timed (default C2: the 131072-token headline configuration)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy 3 times (the known-size reference "
                          "for scaling hardware byte counters)")
@@ -192,7 +194,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         print("[bench] copy probe: 3 x 1 GiB device copies", file=sys.stderr, flush=True)
-    wp, wd = W.C2, W.C3
+    wp, wd = {"C1": W.C1, "C2": W.C2, "C4": W.C4}[args.prefill], W.C3
     specs = wp.specs()
     xp = {n: synth.device_tensor(specs[n]) for n in specs}
     pprob = wp.problem()
@@ -263,7 +265,7 @@ def main():
     stages["invert(all launches)"] = dict(ms=inv_ms / args.steps)
     dominant = max((k for k in stages if k in PREFILL_KERNELS), key=lambda k: stages[k]["ms"])
     dom = stages[dominant]
-    traffic = measured_traffic(dominant)
+    traffic = measured_traffic(dominant) if wp is W.C2 else None
     roof = dict(kernel=dominant, bound=dom["bound"], achieved=dom["achieved"], peak=dom["peak"], unit=dom["unit"],
                 frac=dom["frac"], traffic=traffic,
                 algorithmic_bytes=dom["bytes"], algorithmic_flops=dom["flops"], ms_per_launch=dom["ms"])

@@ -282,9 +282,6 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* _
   }
 }
 
-template <typename T>
-size_t ogq_partial_elem() { return sizeof(T); }
-
 struct PrefillWs {
   int* items;
   int* itempos;
@@ -406,10 +403,7 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
     e = launch_ogq_mfma(D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                         static_cast<const uint16_t*>(v), w.wl, w.n_items, w.ub, entries, w.part_lse,
                         static_cast<uint16_t*>(w.part_o), st);
-  } else if (D.dtype == MSA_BF16) {
-    e = D.d == 64 ? launch_ogq_simple_t<uint16_t, uint16_t, 64>(D, q, k, v, w, entries, st)
-                  : launch_ogq_simple_t<uint16_t, uint16_t, 128>(D, q, k, v, w, entries, st);
-  } else {
+  } else {  // float32 (every bf16 problem the ABI accepts takes the matrix-core kernel)
     e = D.d == 64 ? launch_ogq_simple_t<float, float, 64>(D, q, k, v, w, entries, st)
                   : launch_ogq_simple_t<float, float, 128>(D, q, k, v, w, entries, st);
   }
@@ -468,13 +462,9 @@ hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void
     if (e != hipSuccess) return e;
     return launch_lse_merge(D, sel, w.part_lse, w.part_o, 1, out, st, "decode_merge");
   }
-  float* po = static_cast<float*>(w.part_o);
-  if (D.dtype == MSA_BF16)
-    e = D.d == 64 ? launch_decode_t<uint16_t, 64>(D, q, k, v, sel, w.part_lse, po, st)
-                  : launch_decode_t<uint16_t, 128>(D, q, k, v, sel, w.part_lse, po, st);
-  else
-    e = D.d == 64 ? launch_decode_t<float, 64>(D, q, k, v, sel, w.part_lse, po, st)
-                  : launch_decode_t<float, 128>(D, q, k, v, sel, w.part_lse, po, st);
+  float* po = static_cast<float*>(w.part_o);  // float32 problems
+  e = D.d == 64 ? launch_decode_t<float, 64>(D, q, k, v, sel, w.part_lse, po, st)
+                : launch_decode_t<float, 128>(D, q, k, v, sel, w.part_lse, po, st);
   if (e != hipSuccess) return e;
   return launch_lse_merge(D, sel, w.part_lse, w.part_o, 0, out, st, "decode_merge");
 }

@@ -45,8 +45,9 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   return __builtin_fmaxf(m, a[15]);
 }
 
+// dI = 128 doubles the resident B operands, which leaves room for one wave per SIMD only.
 template <int DI>
-__global__ void __launch_bounds__(256, 2) idx_scores_mfma(Dims D, const uint16_t* __restrict__ q_idx,
+__global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D, const uint16_t* __restrict__ q_idx,
                                                           const uint16_t* __restrict__ k_idx,
                                                           float* __restrict__ scores) {
   constexpr int KS = DI / 16;                 // MFMA k-steps
