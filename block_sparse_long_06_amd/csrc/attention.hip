@@ -282,6 +282,81 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* _
   }
 }
 
+// The same merge for the common shape (bf16 partials, k <= 16, G * d = 512 * CPL): every
+// partial load of the lane (up to 16 slots x CPL 16-byte chunks) is issued first, and
+// the selection mask, lse values and weights are worked out while they are in flight.
+// Loads of invalid slots read unused workspace and are never accumulated.
+template <typename T, int CPL>
+__global__ void __launch_bounds__(256) lse_merge_bf16_k16(Dims D, const int32_t* __restrict__ sel,
+                                                          const float* __restrict__ part_lse,
+                                                          const uint16_t* __restrict__ part_o, T* __restrict__ out) {
+  __shared__ float wbuf[4][16 * 16];
+  __shared__ float hstat[4][2][16];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
+  if (row >= rows) return;
+  const int G = D.G, KG = D.k * D.G, GD = D.G * D.d;
+  const uint16_t* prow = part_o + row * (int64_t)D.k * GD;
+  uint4 raw[16][CPL];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      raw[i][c] = i < D.k ? *reinterpret_cast<const uint4*>(prow + (int64_t)i * GD + (lane + 64 * c) * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
+  const int g = (int)(row % D.Hkv);
+  const int t = (int)((row / D.Hkv) % D.T);
+  const int s = (int)(row / ((int64_t)D.Hkv * D.T));
+  const int32_t* sl = sel + (((int64_t)s * D.Hkv + g) * D.T + t) * D.k;
+  const uint64_t vmask = __ballot(lane < D.k && sl[lane < D.k ? lane : 0] >= 0);
+  const float* lrow = part_lse + row * KG;
+  float* wb = wbuf[wave];
+  for (int x = lane; x < KG; x += 64) wb[x] = ((vmask >> (x / G)) & 1ull) ? lrow[x] : -INFINITY;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < G) {
+    float m = -INFINITY;
+    for (int i = 0; i < D.k; ++i) m = fmaxf(m, wb[i * G + lane]);
+    float tot = 0.0f;
+    for (int i = 0; i < D.k; ++i) tot += __builtin_amdgcn_exp2f((wb[i * G + lane] - m) * kLog2e);
+    hstat[wave][0][lane] = m;
+    hstat[wave][1][lane] = 1.0f / tot;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int x = lane; x < KG; x += 64) {
+    const int hh = x % G;
+    wb[x] = __builtin_amdgcn_exp2f((wb[x] - hstat[wave][0][hh]) * kLog2e) * hstat[wave][1][hh];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  T* orow = out + (((int64_t)s * D.T + t) * D.H + g * G) * D.d;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int c8 = lane + 64 * c;
+    const int hh = c8 * 8 / D.d;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < D.k && ((vmask >> i) & 1ull)) {  // wave-uniform
+        const float w = wb[i * G + hh];
+        const uint32_t q4[4] = {raw[i][c].x, raw[i][c].y, raw[i][c].z, raw[i][c].w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          acc[2 * x] = fmaf(w, __builtin_bit_cast(float, q4[x] << 16), acc[2 * x]);
+          acc[2 * x + 1] = fmaf(w, __builtin_bit_cast(float, q4[x] & 0xFFFF0000u), acc[2 * x + 1]);
+        }
+      }
+    }
+    store8(orow + c8 * 8, acc);
+  }
+}
+
 struct PrefillWs {
   int* items;
   int* itempos;
@@ -358,7 +433,15 @@ hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part
   const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
   const dim3 grid((unsigned)((rows + 3) / 4));
   LaunchScope scope(name, st);
-  if (D.dtype == MSA_BF16) {
+  const int gd = D.G * D.d;
+  if (D.dtype == MSA_BF16 && part_o_is_bf16 && D.k <= 16 && (gd == 512 || gd == 1024)) {
+    if (gd == 1024)
+      hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 2>), grid, dim3(256), 0, st, D, sel, part_lse,
+                         static_cast<const uint16_t*>(part_o), static_cast<uint16_t*>(out));
+    else
+      hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 1>), grid, dim3(256), 0, st, D, sel, part_lse,
+                         static_cast<const uint16_t*>(part_o), static_cast<uint16_t*>(out));
+  } else if (D.dtype == MSA_BF16) {
     if (part_o_is_bf16)
       hipLaunchKernelGGL((lse_merge_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, D, sel, part_lse,
                          static_cast<const uint16_t*>(part_o), static_cast<uint16_t*>(out));
