@@ -3,26 +3,26 @@
 // 四方案深度对比", section 第一步：粗筛 items 1-2 (token scores, max over each 128-token
 // block), causal inside the query's own block.
 //
-// Work unit (one workgroup, 4 waves): 256 consecutive query rows of one
-// (sequence, group) x a chunk of up to kChunk key blocks.  Each wave owns 64
-// queries as two 32-query MFMA B-operands held in registers for the whole unit.
-// Key blocks (128 keys x dI bf16) are staged through LDS, double buffered, with
-// a 16-byte row pad so the per-lane 16-byte reads are bank-conflict free.
+// Work unit (one workgroup, 4 waves): 512 consecutive query rows of one
+// (sequence, group) x a chunk of up to kChunk key blocks.  Each wave owns 128
+// queries as four 32-query MFMA B-operands held in registers for the whole unit,
+// so each key fragment read from LDS feeds four MFMAs.  Key blocks (128 keys x dI
+// bf16) are staged through LDS, double buffered, with a 16-byte row pad so the
+// per-lane 16-byte reads are bank-conflict free.
 //
 // v_mfma_f32_32x32x16_bf16 with A = 32 keys, B = 32 queries: output column
 // n = lane % 32 is one query, so a lane's 16 accumulators are 16 keys of ONE
 // query and the block max is an in-register max3 chain plus one exchange with
-// lane ^ 32 (which holds the other 16 keys of each 32-key tile).  The 32 MFMAs of
-// a block go to 8 independent accumulators, and key tile kt-1 is reduced only after
-// the MFMAs of tile kt are issued, so the max chain overlaps the matrix core.  The
-// causal mask is applied only in blocks that reach a query's position (a separate
-// instantiation of the block body).  Output row i of
-// the 32x32 tile lives in lane half (i % 8) / 4, register 4 * (i / 8) + i % 4.
-// The contraction over dI may visit the index dimensions in any order as long
-// as A and B agree; here lane half h of k-step s covers dims [16 s + 8 h, +8).
+// lane ^ 32 (which holds the other 16 keys of each 32-key tile).  Key tile kt-1 is
+// reduced only after the MFMAs of tile kt are issued, so the max chain overlaps the
+// matrix core.  The causal mask is applied only in blocks that reach a query's
+// position (a separate instantiation of the block body).  Output row i of the
+// 32x32 tile lives in lane half (i % 8) / 4, register 4 * (i / 8) + i % 4.  The
+// contraction over dI may visit the index dimensions in any order as long as A and
+// B agree; here lane half h of k-step s covers dims [16 s + 8 h, +8).
 //
 // Each row's block maxima of the chunk are collected in LDS and written at the end
-// as one contiguous run per row (whole cache lines instead of scattered pieces).
+// as one contiguous run per row.
 #include "msa_internal.hpp"
 #include <type_traits>
 
@@ -32,9 +32,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kQW = 64;          // queries per wave
+constexpr int kQT = 4;
+constexpr int kQW = 32 * kQT;    // queries per wave
 constexpr int kQB = 4 * kQW;     // queries per workgroup
-constexpr int kChunk = 32;       // key blocks per workgroup
+constexpr int kChunk = 16;       // key blocks per workgroup
 constexpr int kBlk = 128;        // block size
 constexpr int kOutPad = kChunk + 1;
 
@@ -50,10 +51,10 @@ template <int DI>
 __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D, const uint16_t* __restrict__ q_idx,
                                                           const uint16_t* __restrict__ k_idx,
                                                           float* __restrict__ scores) {
-  constexpr int KS = DI / 16;                 // MFMA k-steps
-  constexpr int ROWB = DI * 2 + 16;           // padded LDS bytes per key row
-  constexpr int CPR = DI / 8;                 // 16-byte chunks per key row
-  constexpr int PER_T = kBlk * CPR / 256;     // staging chunks per thread
+  constexpr int KS = DI / 16;
+  constexpr int ROWB = DI * 2 + 16;
+  constexpr int CPR = DI / 8;
+  constexpr int PER_T = kBlk * CPR / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][kBlk * ROWB];
   __shared__ float outb[4][kQW][kOutPad];
 
@@ -69,11 +70,10 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
   if (b0 > bmax) return;
   const int b1 = min(b0 + kChunk - 1, bmax);
 
-  // B operands: this wave's 64 queries; pq = absolute position (INT_MAX if t >= T)
-  bf16x8 qf[2][KS];
-  int pq[2];
+  bf16x8 qf[kQT][KS];
+  int pq[kQT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) {
     const int t = t_first + wave * kQW + qt * 32 + n;
     const int tc = t < D.T ? t : D.T - 1;
     pq[qt] = t < D.T ? D.pos0 + t : 0x7FFFFFFF;
@@ -81,7 +81,6 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[qt][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
-  // the wave's smallest own block: blocks >= it need the causal mask
   const int t_w0 = min(t_first + wave * kQW, D.T - 1);
   const int bmask = (D.pos0 + t_w0) / kBlk;
 
@@ -113,10 +112,12 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
   for (int b = b0; b <= b1; ++b) {
     const int buf = (b - b0) & 1;
     if (b < b1) gload(b + 1);
-    float rmax[2] = {-INFINITY, -INFINITY};
+    float rmax[kQT];
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) rmax[qt] = -INFINITY;
     auto body = [&](auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      f32x16 acc[2][4];
+      f32x16 acc[2][kQT];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         bf16x8 af[KS];
@@ -124,57 +125,62 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(arow + ks * 32);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          acc[qt][kt] = f32x16{};
+        for (int qt = 0; qt < kQT; ++qt) {
+          acc[kt & 1][qt] = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            acc[qt][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[qt][ks], acc[qt][kt], 0, 0, 0);
+            acc[kt & 1][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[qt][ks], acc[kt & 1][qt], 0, 0, 0);
         }
         if (kt >= 1) {
+          const int pk = (kt - 1) & 1;
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
+          for (int qt = 0; qt < kQT; ++qt) {
             if (MASKED) {
               const int jb = b * kBlk + (kt - 1) * 32 + 4 * h;
 #pragma unroll
               for (int r = 0; r < 16; ++r)
-                if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[qt][kt - 1][r] = -INFINITY;
+                if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[pk][qt][r] = -INFINITY;
             }
-            rmax[qt] = __builtin_fmaxf(rmax[qt], max16(acc[qt][kt - 1]));
+            rmax[qt] = __builtin_fmaxf(rmax[qt], max16(acc[pk][qt]));
           }
         }
       }
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < kQT; ++qt) {
         if (MASKED) {
           const int jb = b * kBlk + 3 * 32 + 4 * h;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[qt][3][r] = -INFINITY;
+            if (jb + 8 * (r >> 2) + (r & 3) > pq[qt]) acc[1][qt][r] = -INFINITY;
         }
-        rmax[qt] = __builtin_fmaxf(rmax[qt], max16(acc[qt][3]));
+        rmax[qt] = __builtin_fmaxf(rmax[qt], max16(acc[1][qt]));
       }
     };
     if (b >= bmask) body(std::true_type{});
     else body(std::false_type{});
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) rmax[qt] = __builtin_fmaxf(rmax[qt], __shfl_xor(rmax[qt], 32, 64));
-    // lane half h records query tile h (both halves hold both maxima after the exchange)
-    outb[wave][h * 32 + n][b - b0] = h == 0 ? rmax[0] : rmax[1];
+    for (int qt = 0; qt < kQT; ++qt) rmax[qt] = __builtin_fmaxf(rmax[qt], __shfl_xor(rmax[qt], 32, 64));
+    // lane half h records query tiles 2h and 2h + 1
+    outb[wave][(2 * h) * 32 + n][b - b0] = h == 0 ? rmax[0] : rmax[2];
+    outb[wave][(2 * h + 1) * 32 + n][b - b0] = h == 0 ? rmax[1] : rmax[3];
     if (b < b1) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  // one contiguous run per row: blocks b0 .. min(b1, own block)
-  const int t_out = t_first + wave * kQW + lane;
-  if (t_out < D.T) {
-    const int bt = (D.pos0 + t_out) / kBlk;
-    const int len = min(b1, bt) - b0 + 1;
-    float* out_row = scores + (sg * D.T + t_out) * (int64_t)D.nb + b0;
-    const float* src = outb[wave][lane];
-    int u = 0;
-    if ((D.nb & 3) == 0)
-      for (; u + 4 <= len; u += 4) *reinterpret_cast<float4*>(out_row + u) = make_float4(src[u], src[u + 1], src[u + 2], src[u + 3]);
-    for (; u < len; ++u) out_row[u] = src[u];
+#pragma unroll
+  for (int rr = 0; rr < kQW / 64; ++rr) {
+    const int rl = lane + 64 * rr;
+    const int t_out = t_first + wave * kQW + rl;
+    if (t_out < D.T) {
+      const int bt = (D.pos0 + t_out) / kBlk;
+      const int len = min(b1, bt) - b0 + 1;
+      float* out_row = scores + (sg * D.T + t_out) * (int64_t)D.nb + b0;
+      const float* src = outb[wave][rl];
+      int u = 0;
+      if ((D.nb & 3) == 0)
+        for (; u + 4 <= len; u += 4) *reinterpret_cast<float4*>(out_row + u) = make_float4(src[u], src[u + 1], src[u + 2], src[u + 3]);
+      for (; u < len; ++u) out_row[u] = src[u];
+    }
   }
 }
 
