@@ -94,11 +94,71 @@ def roofline(flops, nbytes, seconds):
     return dict(bound="hbm", achieved=a, peak=PEAK_HBM / 1e9, unit="GB/s", frac=a / (PEAK_HBM / 1e9))
 
 
-# kernel name (library profiler) -> model stage
-PREFILL_KERNELS = {"idx_scores_mfma": "idx_scores", "block_topk": "block_topk", "ogq_mfma": "ogq_attention",
-                   "lse_merge": "lse_merge"}
-KERNEL_SOURCES = {"ogq_mfma": "attention_mfma.hip", "idx_scores_mfma": "index_scores_mfma.hip",
-                  "lse_merge": "attention.hip", "block_topk": "topk.hip"}
+def query_tile_split(wl, sel, min_rows=32, cap=32):
+    """Per-(row, slot) flag of the library's query-tile split, recomputed from sel for
+    reporting: block b is tile-shared for (s, g, 128-position query tile) when at least
+    max(min_rows, ceil(rows / 2)) of the tile's rows chose it and the tile has at least
+    min_rows rows; at most `cap` such blocks are kept, the highest ids first."""
+    import torch
+    S, Hkv, T, k = sel.shape
+    dev = sel.device
+    nb = wl.nb
+    pos = torch.arange(wl.N - wl.T, wl.N, device=dev, dtype=torch.int64)
+    qb = (pos // 128) - (wl.N - wl.T) // 128                                  # tile of each row
+    nqb = int(qb.max()) + 1
+    rows = torch.bincount(qb, minlength=nqb)                                  # rows per tile
+    thr = torch.clamp((rows + 1) // 2, min=min_rows)
+    s64 = sel.to(torch.int64)
+    valid = s64 >= 0
+    sg = torch.arange(S * Hkv, device=dev).view(S, Hkv, 1, 1)
+    key = (sg * nqb + qb.view(1, 1, T, 1)) * nb + s64.clamp(min=0)
+    cnt = torch.bincount(key[valid], minlength=S * Hkv * nqb * nb).view(S * Hkv, nqb, nb)
+    cand = (cnt >= thr.view(1, nqb, 1)) & (rows >= min_rows).view(1, nqb, 1)
+    from_top = torch.flip(torch.cumsum(torch.flip(cand.to(torch.int32), [2]), 2), [2])
+    keep = cand & (from_top <= cap)
+    return valid & keep.view(-1)[key.clamp(min=0)], keep
+
+
+def attention_split_model(wl, sel, hot, keep, esize=2):
+    """Algorithmic work of the two attention kernels and the merge for one selection.
+    Each kernel is priced for the (row, block) pairs it handles: scores and PV over the
+    attended keys; Q of every row it serves once, K/V of every block it touches once,
+    one partial (G x (d bf16 + lse)) per pair (Outer-Gather-Q) or per row (query tile)."""
+    import torch
+    S, Hkv, T, k = sel.shape
+    G, d, B = wl.G, wl.d, 128
+    pos = torch.arange(wl.N - wl.T, wl.N, device=sel.device, dtype=torch.int64).view(1, 1, T, 1)
+    bt = pos // B
+    s64 = sel.to(torch.int64)
+    valid = s64 >= 0
+    keys = torch.where(s64 == bt, pos - bt * B + 1, torch.full_like(s64, B)) * valid
+    cold = valid & ~hot
+    part = G * (d * esize + 4.0)
+    qrow = G * d * esize
+    kv = 2.0 * B * d * esize
+    rows_hot = int(hot.any(dim=3).sum())
+    rows_cold = int(cold.any(dim=3).sum())
+    n_cold = int(cold.sum())
+    sgb_cold = torch.zeros(S * Hkv * wl.nb, dtype=torch.bool, device=sel.device)
+    sgi = torch.arange(S * Hkv, device=sel.device).view(S, Hkv, 1, 1) * wl.nb
+    sgb_cold[(sgi + s64.clamp(min=0))[cold]] = True
+    m = {}
+    m["hot_mfma"] = dict(flops=4.0 * d * G * float((keys * hot).sum()),
+                         bytes=rows_hot * (qrow + part) + int(keep.any(dim=1).sum()) * kv)
+    m["ogq_mfma"] = dict(flops=4.0 * d * G * float((keys * cold).sum()),
+                         bytes=rows_cold * qrow + int(sgb_cold.sum()) * kv + n_cold * (part + 4.0))
+    m["lse_merge"] = dict(flops=0.0, bytes=(n_cold + rows_hot) * part + esize * S * T * wl.H * d
+                          + S * Hkv * T * (4.0 * k + 8.0))
+    m["pairs"] = dict(query_tile=int(hot.sum()), outer_gather_q=n_cold, rows_with_query_tile=rows_hot)
+    return m
+
+
+# kernel name (library profiler) -> model stage (the attention kernels and the merge
+# are priced by attention_split_model from the run's own selection)
+PREFILL_KERNELS = {"idx_scores_mfma": "idx_scores", "block_topk": "block_topk", "ogq_mfma": "ogq_mfma",
+                   "hot_mfma": "hot_mfma", "lse_merge": "lse_merge"}
+KERNEL_SOURCES = {"ogq_mfma": "attention_mfma.hip", "hot_mfma": "attention_mfma.hip",
+                  "idx_scores_mfma": "index_scores_mfma.hip", "lse_merge": "attention.hip", "block_topk": "topk.hip"}
 
 
 def source_sha(kernel):
@@ -157,6 +217,56 @@ def cpu_baseline(wl, inputs, seconds_budget=12.0):
     return dict(value=done_rows / spent, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
                 sample="%d seeded query rows x %d groups of the %s workload (full index scan, top-k, "
                        "inversion, attention per row), %.1f s of CPU work" % (done_rows, wl.Hkv, wl.name, spent))
+
+
+def selection_structure(wl, sel, csr_offsets):
+    """Realised structure of one prefill selection (reported, never timed).
+
+    Classes of each valid (query, group, slot), first match wins: own block; sink
+    (block 0); needle (a boosted block of the generator other than 0); band (1-4
+    blocks before the own one); other.  `tile_shared` is the fraction of valid slots
+    whose block is also chosen by at least half of the queries in the same 128-position
+    query block and group; `csr_rows` summarises the per-(group, block) row counts."""
+    import torch
+    S, Hkv, T, k = sel.shape
+    dev = sel.device
+    pos = torch.arange(wl.N - wl.T, wl.N, device=dev, dtype=torch.int64)
+    bt = (pos // 128).view(1, 1, T, 1)
+    s64 = sel.to(torch.int64)
+    valid = s64 >= 0
+    n_valid = int(valid.sum())
+    own = valid & (s64 == bt)
+    sink = valid & ~own & (s64 == 0)
+    bm = wl.boost_mask()
+    if bm is not None:
+        boost = torch.from_numpy(bm.astype(np.bool_)).to(dev)                       # [S, Hkv, nb]
+        sidx = torch.arange(S, device=dev).view(S, 1, 1, 1).expand_as(s64)
+        gidx = torch.arange(Hkv, device=dev).view(1, Hkv, 1, 1).expand_as(s64)
+        needle = valid & ~own & ~sink & boost[sidx, gidx, s64.clamp(min=0)]
+    else:
+        needle = torch.zeros_like(valid)
+    band = valid & ~own & ~sink & ~needle & (s64 >= bt - 4)
+    other = valid & ~own & ~sink & ~needle & ~band
+    frac = {n: float(m.sum()) / max(n_valid, 1)
+            for n, m in (("own", own), ("sink", sink), ("needle", needle), ("band", band), ("other", other))}
+    # blocks shared inside a 128-position query block
+    qb = bt - int((wl.N - wl.T) // 128)
+    nqb = int(qb.max()) + 1
+    nb = wl.nb
+    sg = (torch.arange(S, device=dev).view(S, 1, 1, 1) * Hkv + torch.arange(Hkv, device=dev).view(1, Hkv, 1, 1))
+    key = ((sg * nqb + qb) * nb + s64.clamp(min=0))
+    cnt = torch.bincount(key[valid], minlength=S * Hkv * nqb * nb)
+    rows_in_qb = torch.bincount(qb.view(-1), minlength=nqb).view(1, 1, nqb)           # queries per query block
+    at = cnt[key.clamp(min=0)]
+    tile_rows = rows_in_qb.view(-1)[qb.expand_as(s64)]
+    shared = valid & (2 * at >= tile_rows)
+    frac["tile_shared"] = float(shared.sum()) / max(n_valid, 1)
+    counts = (csr_offsets[..., 1:] - csr_offsets[..., :-1]).reshape(-1).to(torch.float64)
+    nz = counts[counts > 0]
+    csr = dict(blocks_touched=int(nz.numel()), max=int(nz.max()) if nz.numel() else 0,
+               p50=float(torch.quantile(nz, 0.5)) if nz.numel() else 0.0,
+               p99=float(torch.quantile(nz, 0.99)) if nz.numel() else 0.0)
+    return dict(fractions=frac, valid_slots=n_valid, csr_rows=csr)
 
 
 # ------------------------------------------------------------------ main
@@ -239,6 +349,7 @@ def main():
     kern = {}
     for name in ("idx_scores_mfma", "block_topk", "invert_count", "invert_scatter", "invert_offsets",
                  "scan_tile_sums", "scan_top", "scan_apply", "wl_count", "wl_emit", "ogq_mfma", "lse_merge",
+                 "hot_select", "cold_count", "cold_scatter", "cold_offsets", "hot_mfma",
                  "idx_scores_rows", "idx_scores_stream", "block_topk_t1", "decode_items", "decode_ogq_mfma",
                  "decode_simple", "decode_merge"):
         ms, n = msa.profiler_read(name, reset=False)
@@ -254,6 +365,13 @@ def main():
     counts = pb.csr_offsets[..., 1:] - pb.csr_offsets[..., :-1]
     touched = int((counts > 0).sum())
     model = prefill_model(wp.S, wp.T, wp.N, wp.H, wp.Hkv, wp.d, wp.dI, wp.k, touched_blocks=touched)
+    if os.environ.get("MSA_HOT_TILES", "1").startswith("0"):
+        hot_flag = torch.zeros_like(pb.sel, dtype=torch.bool)
+        keep = torch.zeros((1, 1, 1), dtype=torch.bool, device=pb.sel.device)
+    else:
+        hot_flag, keep = query_tile_split(wp, pb.sel)
+    split = attention_split_model(wp, pb.sel, hot_flag, keep)
+    model.update({kk: split[kk] for kk in ("hot_mfma", "ogq_mfma", "lse_merge")})
     stages = {}
     for kname, stage in PREFILL_KERNELS.items():
         if kname not in kern:
@@ -263,6 +381,16 @@ def main():
         stages[kname] = dict(ms=per_launch_s * 1e3, flops=model[stage]["flops"], bytes=model[stage]["bytes"], **rf)
     inv_ms = sum(kern[n]["total_ms"] for n in ("invert_count", "invert_scatter", "invert_offsets") if n in kern)
     stages["invert(all launches)"] = dict(ms=inv_ms / args.steps)
+    split_ms = sum(kern[n]["total_ms"] for n in ("hot_select", "cold_count", "cold_scatter", "cold_offsets")
+                   if n in kern)
+    stages["query_tile_split(all launches)"] = dict(ms=split_ms / args.steps)
+    # a4 as a whole (both attention kernels) against the full a4 work
+    a4_ms = sum(kern[n]["total_ms"] for n in ("ogq_mfma", "hot_mfma") if n in kern) / args.steps
+    if a4_ms > 0:
+        stages["a4_attention(ogq_mfma+hot_mfma)"] = dict(
+            ms=a4_ms, flops=model["ogq_attention"]["flops"], bytes=model["ogq_attention"]["bytes"],
+            **roofline(model["ogq_attention"]["flops"], model["ogq_attention"]["bytes"], a4_ms / 1e3))
+
     dominant = max((k for k in stages if k in PREFILL_KERNELS), key=lambda k: stages[k]["ms"])
     dom = stages[dominant]
     traffic = measured_traffic(dominant) if wp is W.C2 else None
@@ -305,6 +433,8 @@ def main():
                    "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
         "prefill_ms": prefill_ms, "wall_s_timed": wall,
         "decode": dec, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
+        "selection_structure": selection_structure(wp, pb.sel, pb.csr_offsets),
+        "attention_pairs": split["pairs"],
     }
     print(json.dumps(line))
 

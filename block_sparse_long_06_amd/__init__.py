@@ -15,7 +15,8 @@ import os
 from dataclasses import dataclass
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmsa.so")
+# MSA_LIBRARY may name another build of the same library (e.g. a debug build).
+LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARGUMENT, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_DEVICE = range(5)
 MSA_F32, MSA_BF16 = 0, 1

@@ -19,6 +19,8 @@
 #include "msa_internal.hpp"
 #include "scan.hpp"
 
+#include <stdlib.h>
+
 namespace msa {
 
 // matrix-core Outer-Gather-Q kernel (attention_mfma.hip)
@@ -30,6 +32,8 @@ hipError_t launch_ogq_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, 
 hipError_t launch_decode_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* sel, int4* wl, int32_t* ent, int* n_items, float* part_lse,
                               uint16_t* part_o, hipStream_t st);
+hipError_t launch_hot_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const HotSplit& h,
+                           float* part_lse, uint16_t* part_o, hipStream_t st);
 
 namespace {
 
@@ -215,7 +219,8 @@ constexpr int kMergeMaxKG = 64 * 16;  // k * G
 template <typename T, typename PT>
 __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* __restrict__ sel,
                                                         const float* __restrict__ part_lse,
-                                                        const PT* __restrict__ part_o, T* __restrict__ out) {
+                                                        const PT* __restrict__ part_o,
+                                                        const uint64_t* __restrict__ hotmask, T* __restrict__ out) {
   __shared__ float wbuf[4][kMergeMaxKG];
   __shared__ float hstat[4][2][16];
   const int lane = threadIdx.x & 63;
@@ -227,7 +232,11 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* _
   const int t = (int)((row / D.Hkv) % D.T);
   const int s = (int)(row / ((int64_t)D.Hkv * D.T));
   const int32_t* sl = sel + (((int64_t)s * D.Hkv + g) * D.T + t) * D.k;
-  const uint64_t vmask = __ballot(lane < D.k && sl[lane < D.k ? lane : 0] >= 0);
+  uint64_t vmask = __ballot(lane < D.k && sl[lane < D.k ? lane : 0] >= 0);
+  if (hotmask != nullptr) {
+    const uint64_t hm = hotmask[row];
+    vmask &= ~(hm & (hm - 1));  // hot slots other than the lowest
+  }
   const int G = D.G, KG = D.k * D.G, GD = D.G * D.d;
   const float* lrow = part_lse + row * KG;
   const PT* prow = part_o + row * (int64_t)D.k * GD;
@@ -282,14 +291,17 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* _
   }
 }
 
-// The same merge for the common shape (bf16 partials, k <= 16, G * d = 512 * CPL): every
-// partial load of the lane (up to 16 slots x CPL 16-byte chunks) is issued first, and
-// the selection mask, lse values and weights are worked out while they are in flight.
-// Loads of invalid slots read unused workspace and are never accumulated.
-template <typename T, int CPL>
+// The same merge for the common shape (bf16 partials, k <= 16, G * d = 512 * CPL).
+// Without a hot mask every partial load of the lane (up to 16 slots x CPL 16-byte
+// chunks) is issued first, and the selection mask, lse values and weights are worked
+// out while they are in flight (loads of invalid slots read unused workspace and are
+// never accumulated).  With a hot mask (HOT) the slot mask is formed first and only
+// the slots that are read are loaded: skipped hot slots hold no partial.
+template <typename T, int CPL, bool HOT>
 __global__ void __launch_bounds__(256) lse_merge_bf16_k16(Dims D, const int32_t* __restrict__ sel,
                                                           const float* __restrict__ part_lse,
-                                                          const uint16_t* __restrict__ part_o, T* __restrict__ out) {
+                                                          const uint16_t* __restrict__ part_o,
+                                                          const uint64_t* __restrict__ hotmask, T* __restrict__ out) {
   __shared__ float wbuf[4][16 * 16];
   __shared__ float hstat[4][2][16];
   const int lane = threadIdx.x & 63;
@@ -299,18 +311,31 @@ __global__ void __launch_bounds__(256) lse_merge_bf16_k16(Dims D, const int32_t*
   if (row >= rows) return;
   const int G = D.G, KG = D.k * D.G, GD = D.G * D.d;
   const uint16_t* prow = part_o + row * (int64_t)D.k * GD;
-  uint4 raw[16][CPL];
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-      raw[i][c] = i < D.k ? *reinterpret_cast<const uint4*>(prow + (int64_t)i * GD + (lane + 64 * c) * 8)
-                          : make_uint4(0u, 0u, 0u, 0u);
   const int g = (int)(row % D.Hkv);
   const int t = (int)((row / D.Hkv) % D.T);
   const int s = (int)(row / ((int64_t)D.Hkv * D.T));
   const int32_t* sl = sel + (((int64_t)s * D.Hkv + g) * D.T + t) * D.k;
-  const uint64_t vmask = __ballot(lane < D.k && sl[lane < D.k ? lane : 0] >= 0);
+  uint4 raw[16][CPL];
+  uint64_t vmask;
+  if (HOT) {
+    vmask = __ballot(lane < D.k && sl[lane < D.k ? lane : 0] >= 0);
+    const uint64_t hm = hotmask[row];
+    vmask &= ~(hm & (hm - 1));
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        raw[i][c] = (vmask >> i) & 1ull ? *reinterpret_cast<const uint4*>(prow + (int64_t)i * GD + (lane + 64 * c) * 8)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        raw[i][c] = i < D.k ? *reinterpret_cast<const uint4*>(prow + (int64_t)i * GD + (lane + 64 * c) * 8)
+                            : make_uint4(0u, 0u, 0u, 0u);
+    vmask = __ballot(lane < D.k && sl[lane < D.k ? lane : 0] >= 0);
+  }
   const float* lrow = part_lse + row * KG;
   float* wb = wbuf[wave];
   for (int x = lane; x < KG; x += 64) wb[x] = ((vmask >> (x / G)) & 1ull) ? lrow[x] : -INFINITY;
@@ -366,6 +391,8 @@ struct PrefillWs {
   float* part_lse;
   void* part_o;
   int64_t ub;
+  bool has_hot;
+  HotSplit hs;  // query-tile split (matrix-core problems)
 };
 
 int rows_per_item(const Dims& D) {
@@ -393,8 +420,22 @@ PrefillWs prefill_layout(const Dims& D, void* base, size_t* total) {
   w.part_lse = static_cast<float*>(take(npart * D.G * sizeof(float)));
   const size_t pelem = D.dtype == MSA_BF16 ? 2 : 4;
   w.part_o = take((size_t)npart * D.G * D.d * pelem);
+  w.has_hot = ogq_mfma_supported(D);
+  w.hs = HotSplit{};
+  if (w.has_hot) {
+    size_t hb = 0;
+    (void)hot_split_layout(D, nullptr, &hb);
+    void* hbase = take(hb);
+    w.hs = hot_split_layout(D, hbase, &hb);
+  }
   *total = off;
   return w;
+}
+
+// The query-tile pass is on unless the environment sets MSA_HOT_TILES=0.
+bool hot_tiles_enabled() {
+  const char* e = getenv("MSA_HOT_TILES");
+  return !(e != nullptr && e[0] == '0');
 }
 
 template <typename T, typename PT, int DH>
@@ -429,28 +470,37 @@ hipError_t launch_decode_t(const Dims& D, const void* q, const void* k, const vo
 }  // namespace
 
 hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part_lse, const void* part_o,
-                            int part_o_is_bf16, void* out, hipStream_t st, const char* name) {
+                            int part_o_is_bf16, const uint64_t* hotmask, void* out, hipStream_t st,
+                            const char* name) {
   const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
   const dim3 grid((unsigned)((rows + 3) / 4));
   LaunchScope scope(name, st);
   const int gd = D.G * D.d;
+  const uint16_t* pb = static_cast<const uint16_t*>(part_o);
+  uint16_t* ob = static_cast<uint16_t*>(out);
   if (D.dtype == MSA_BF16 && part_o_is_bf16 && D.k <= 16 && (gd == 512 || gd == 1024)) {
-    if (gd == 1024)
-      hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 2>), grid, dim3(256), 0, st, D, sel, part_lse,
-                         static_cast<const uint16_t*>(part_o), static_cast<uint16_t*>(out));
+    if (gd == 1024 && hotmask)
+      hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 2, true>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
+                         hotmask, ob);
+    else if (gd == 1024)
+      hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 2, false>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
+                         hotmask, ob);
+    else if (hotmask)
+      hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 1, true>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
+                         hotmask, ob);
     else
-      hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 1>), grid, dim3(256), 0, st, D, sel, part_lse,
-                         static_cast<const uint16_t*>(part_o), static_cast<uint16_t*>(out));
+      hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 1, false>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
+                         hotmask, ob);
   } else if (D.dtype == MSA_BF16) {
     if (part_o_is_bf16)
-      hipLaunchKernelGGL((lse_merge_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, D, sel, part_lse,
-                         static_cast<const uint16_t*>(part_o), static_cast<uint16_t*>(out));
+      hipLaunchKernelGGL((lse_merge_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
+                         hotmask, ob);
     else
       hipLaunchKernelGGL((lse_merge_kernel<uint16_t, float>), grid, dim3(256), 0, st, D, sel, part_lse,
-                         static_cast<const float*>(part_o), static_cast<uint16_t*>(out));
+                         static_cast<const float*>(part_o), hotmask, ob);
   } else {
     hipLaunchKernelGGL((lse_merge_kernel<float, float>), grid, dim3(256), 0, st, D, sel, part_lse,
-                       static_cast<const float*>(part_o), static_cast<float*>(out));
+                       static_cast<const float*>(part_o), hotmask, static_cast<float*>(out));
   }
   return hipGetLastError();
 }
@@ -468,11 +518,19 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
   const int64_t nsgb = (int64_t)D.S * D.Hkv * D.nb;
   const int R = rows_per_item(D);
   const unsigned g256 = (unsigned)((nsgb + 255) / 256);
+  hipError_t e;
+  const bool hot = w.has_hot && hot_tiles_enabled();
+  if (hot) {  // Outer-Gather-Q then takes only the cold part of the CSR
+    e = launch_hot_split(D, sel, off, entries, w.hs, st);
+    if (e != hipSuccess) return e;
+    off = w.hs.cold_off;
+    entries = w.hs.cold_ent;
+  }
   {
     LaunchScope s("wl_count", st);
     hipLaunchKernelGGL(wl_count, dim3(g256), dim3(256), 0, st, D, off, w.items, R);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_exclusive_scan(w.items, w.itempos, nsgb, w.n_items, w.scan_ws, st);
   if (e != hipSuccess) return e;
@@ -491,7 +549,13 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
                   : launch_ogq_simple_t<float, float, 128>(D, q, k, v, w, entries, st);
   }
   if (e != hipSuccess) return e;
-  return launch_lse_merge(D, sel, w.part_lse, w.part_o, D.dtype == MSA_BF16, out, st, "lse_merge");
+  if (hot) {
+    e = launch_hot_mfma(D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                        static_cast<const uint16_t*>(v), w.hs, w.part_lse, static_cast<uint16_t*>(w.part_o), st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_lse_merge(D, sel, w.part_lse, w.part_o, D.dtype == MSA_BF16, hot ? w.hs.hotmask : nullptr, out,
+                          st, "lse_merge");
 }
 
 // Decode workspace: partial lse / O per (s, t, g, slot, head), plus (bf16 path) the
@@ -543,13 +607,13 @@ hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void
                            static_cast<const uint16_t*>(v), sel, w.wl, w.ent, w.n_items, w.part_lse,
                            static_cast<uint16_t*>(w.part_o), st);
     if (e != hipSuccess) return e;
-    return launch_lse_merge(D, sel, w.part_lse, w.part_o, 1, out, st, "decode_merge");
+    return launch_lse_merge(D, sel, w.part_lse, w.part_o, 1, nullptr, out, st, "decode_merge");
   }
   float* po = static_cast<float*>(w.part_o);  // float32 problems
   e = D.d == 64 ? launch_decode_t<float, 64>(D, q, k, v, sel, w.part_lse, po, st)
                 : launch_decode_t<float, 128>(D, q, k, v, sel, w.part_lse, po, st);
   if (e != hipSuccess) return e;
-  return launch_lse_merge(D, sel, w.part_lse, w.part_o, 0, out, st, "decode_merge");
+  return launch_lse_merge(D, sel, w.part_lse, w.part_o, 0, nullptr, out, st, "decode_merge");
 }
 
 }  // namespace msa

@@ -33,6 +33,8 @@
 // read back only by the merge, long after, and should not evict K/V or Q lines.
 #include "msa_internal.hpp"
 
+#include <type_traits>
+
 namespace msa {
 namespace {
 
@@ -74,29 +76,64 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
+// K/V staging in two halves (global -> registers, registers -> LDS) so that a kernel
+// can fetch the next block while it computes on the current one.  Thread layout:
+// K: 16-byte pieces, row-major; V^T: thread = (4 consecutive keys, 8 consecutive dims),
+// transposed 4x8 in registers.
 template <int DH>
-__device__ __forceinline__ void stage_kv(OgqLds<DH>& L, const uint16_t* kb, const uint16_t* vb, int nvalid) {
+struct KVRegs {
+  static constexpr int KP = kBlk * DH / 8 / kThreads;  // K pieces per thread
+  uint4 k[KP];
+  uint4 v[4];
+};
+
+template <int DH>
+__device__ __forceinline__ void gload_k(uint4 (&rk)[KVRegs<DH>::KP], const uint16_t* kb, int nvalid) {
   constexpr int CPR = DH / 8;
 #pragma unroll
-  for (int u = 0; u < kBlk * CPR / kThreads; ++u) {
+  for (int u = 0; u < KVRegs<DH>::KP; ++u) {
     const int c = threadIdx.x + kThreads * u;
     const int row = c / CPR, col = c % CPR;
-    const uint4 val = row < nvalid ? *reinterpret_cast<const uint4*>(kb + row * DH + col * 8)
-                                   : make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(&L.k[row * OgqLds<DH>::KROW + col * 16]) = val;
+    rk[u] = row < nvalid ? *reinterpret_cast<const uint4*>(kb + row * DH + col * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
-  // V^T: thread = (4 consecutive keys, 8 consecutive dims); 4x8 transpose in registers
+}
+
+template <int DH>
+__device__ __forceinline__ void gload_v(uint4 (&rv)[4], const uint16_t* vb, int nvalid) {
   const int kg = threadIdx.x & 31;
   const int dc = threadIdx.x >> 5;  // 0..15
-  if (dc < DH / 8) {
-    uint32_t w[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 4 * kg + i;
-      const uint4 x = key < nvalid ? *reinterpret_cast<const uint4*>(vb + key * DH + dc * 8)
-                                   : make_uint4(0u, 0u, 0u, 0u);
-      w[i][0] = x.x; w[i][1] = x.y; w[i][2] = x.z; w[i][3] = x.w;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int key = 4 * kg + i;
+    rv[i] = dc < DH / 8 && key < nvalid ? *reinterpret_cast<const uint4*>(vb + key * DH + dc * 8)
+                                         : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ void gload_kv(KVRegs<DH>& r, const uint16_t* kb, const uint16_t* vb, int nvalid) {
+  gload_k<DH>(r.k, kb, nvalid);
+  gload_v<DH>(r.v, vb, nvalid);
+}
+
+template <int DH>
+__device__ __forceinline__ void lstore_k(unsigned char* lk, const uint4 (&rk)[KVRegs<DH>::KP]) {
+  constexpr int CPR = DH / 8;
+#pragma unroll
+  for (int u = 0; u < KVRegs<DH>::KP; ++u) {
+    const int c = threadIdx.x + kThreads * u;
+    const int row = c / CPR, col = c % CPR;
+    *reinterpret_cast<uint4*>(&lk[row * OgqLds<DH>::KROW + col * 16]) = rk[u];
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ void lstore_vt(unsigned char* lvt, const uint4 (&rv)[4]) {
+  const int kg = threadIdx.x & 31;
+  const int dc = threadIdx.x >> 5;
+  if (dc < DH / 8) {
+    const uint32_t w[4][4] = {{rv[0].x, rv[0].y, rv[0].z, rv[0].w}, {rv[1].x, rv[1].y, rv[1].z, rv[1].w},
+                              {rv[2].x, rv[2].y, rv[2].z, rv[2].w}, {rv[3].x, rv[3].y, rv[3].z, rv[3].w}};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int sh = (e & 1) * 16;
@@ -105,9 +142,22 @@ __device__ __forceinline__ void stage_kv(OgqLds<DH>& L, const uint16_t* kb, cons
       uint2 o;
       o.x = k0 | (k1 << 16);
       o.y = k2 | (k3 << 16);
-      *reinterpret_cast<uint2*>(&L.vt[(dc * 8 + e) * OgqLds<DH>::VROW + kg * 8]) = o;
+      *reinterpret_cast<uint2*>(&lvt[(dc * 8 + e) * OgqLds<DH>::VROW + kg * 8]) = o;
     }
   }
+}
+
+template <int DH>
+__device__ __forceinline__ void lstore_kv(unsigned char* lk, unsigned char* lvt, const KVRegs<DH>& r) {
+  lstore_k<DH>(lk, r.k);
+  lstore_vt<DH>(lvt, r.v);
+}
+
+template <int DH>
+__device__ __forceinline__ void stage_kv(OgqLds<DH>& L, const uint16_t* kb, const uint16_t* vb, int nvalid) {
+  KVRegs<DH> r;
+  gload_kv<DH>(r, kb, vb, nvalid);
+  lstore_kv<DH>(L.k, L.vt, r);
 }
 
 // One wave's gathered Q rows: piece p = lane + 64 u -> M-row p / (DH/8), column p % (DH/8).
@@ -317,6 +367,247 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
   }
 }
 
+// ------------------------------------------------------------------ query-tile pass
+// Hot blocks of a 128-position query tile (chosen by most of its rows; hot_tiles.hip)
+// are processed tile-wise: one workgroup = 8 waves x 32 M-rows of one (sequence,
+// group, tile) slice; each wave's Q B-operands stay in registers while the tile's hot
+// blocks stream through double-buffered LDS (the next block is fetched into registers
+// during the current block's MFMAs; one barrier per block).  Online softmax over the
+// blocks: m and l per M-row, the O^T accumulators rescaled by exp2((m_old - m_new) sc)
+// when the max grows.  A row that did not select a block masks all of that block's
+// scores; the causal mask applies inside the own block.  Each row with hot slots writes
+// ONE partial (over all its hot blocks) at its lowest hot slot; the merge skips the
+// row's other hot slots.
+template <int DH>
+struct __attribute__((aligned(16))) HotLds {
+  static constexpr int KROW = OgqLds<DH>::KROW, VROW = OgqLds<DH>::VROW, QROW = OgqLds<DH>::QROW;
+  // k[0..1] also serve, after the block loop, as the 8 per-wave output buffers
+  // (8 * 32 * QROW bytes == 2 * kBlk * KROW bytes).
+  __attribute__((aligned(16))) unsigned char k[2][kBlk * KROW];
+  __attribute__((aligned(16))) unsigned char vt[2][DH * VROW];
+  int64_t pidx[kWaves][32];
+  float lse[kWaves][32];
+};
+
+template <int DH, int G>
+__global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __restrict__ q,
+                                                     const uint16_t* __restrict__ k,
+                                                     const uint16_t* __restrict__ v,
+                                                     const int32_t* __restrict__ hot,
+                                                     const uint64_t* __restrict__ hotmask,
+                                                     const uint32_t* __restrict__ selbits,
+                                                     float* __restrict__ part_lse,
+                                                     uint16_t* __restrict__ part_o, int ntiles, int wpt) {
+  constexpr int KS = DH / 16;
+  constexpr int DT = DH / 32;
+  constexpr int RW = 32 / G;           // query rows per wave
+  constexpr int QWG = kWaves * RW;     // query rows per workgroup
+  constexpr int CPR = DH / 8;
+  constexpr int QROW = HotLds<DH>::QROW;
+  static_assert(kWaves * 32 * QROW <= 2 * kBlk * HotLds<DH>::KROW, "output buffers overlay k[0..1]");
+  __shared__ HotLds<DH> L;
+
+  // XCD-aware order: consecutive items (slices of one tile, then neighbouring tiles of
+  // one group, which share most hot blocks) go to one XCD.
+  const int nitems = D.S * D.Hkv * ntiles * wpt;  // < 2^31 (checked at launch)
+  const int per_xcd = (nitems + 7) / 8;
+  const int slot_in_xcd = blockIdx.x >> 3;
+  const int item = (blockIdx.x & 7) * per_xcd + slot_in_xcd;
+  if (slot_in_xcd >= per_xcd || item >= nitems) return;
+  const int part = item % wpt;
+  const int ti = (item / wpt) % ntiles;
+  const int64_t sg = item / (wpt * ntiles);
+  const int32_t* hl = hot + (sg * ntiles + ti) * kHotStride;
+  const int nh = hl[0];
+  if (nh <= 0) return;
+  const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
+  const int tau = D.pos0 / kHotTile + ti;
+  const int t_lo = max(tau * kHotTile, D.pos0) - D.pos0;
+  const int t_end = min(tau * kHotTile + kHotTile, D.N) - D.pos0;
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int nl = lane & 31;
+  const int tq0 = t_lo + part * QWG + wave * RW;  // the wave's first query row
+  const int t = tq0 + nl / G;                     // this lane's M-row = (t, head nl % G)
+  const bool row_ok = t < t_end;
+  const int64_t rowid = ((int64_t)s * D.T + (row_ok ? t : 0)) * D.Hkv + g;
+  const uint32_t sb = row_ok ? selbits[rowid] : 0u;
+  const int p = D.pos0 + (row_ok ? t : 0);
+
+  // Q B-operands: lane half h, k-step ks -> head dims [DH/2 h + 8 ks, +8)
+  bf16x8 bq[KS];
+  {
+    const uint16_t* qp = q + (((int64_t)s * D.T + (row_ok ? t : 0)) * D.H + (int64_t)g * G + nl % G) * DH + (DH / 2) * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bq[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 8 * ks) : bf16x8{};
+  }
+  if (h == 0 && nl % G == 0) {
+    int64_t pi = -1;
+    if (row_ok) {
+      const uint64_t hm = hotmask[rowid];
+      if (hm != 0ull) pi = rowid * D.k + __builtin_ctzll(hm);
+    }
+    L.pidx[wave][nl / G] = pi;
+  }
+
+  const int64_t kvbase = sg * D.N;
+  KVRegs<DH> nx;
+  {
+    const int b = hl[1];
+    gload_kv<DH>(nx, k + (kvbase + (int64_t)b * kBlk) * DH, v + (kvbase + (int64_t)b * kBlk) * DH,
+                 min(kBlk, D.N - b * kBlk));
+    lstore_kv<DH>(L.k[0], L.vt[0], nx);
+  }
+  __syncthreads();
+
+  const float sc = D.scale * kLog2e;
+  // Running reference max m (raw score units) of each M-row.  It is raised only when a
+  // row's max exceeds it by more than kLazy in exp2 units, so P <= 2^kLazy and the O
+  // accumulators are rescaled rarely (any reference gives the same normalised result).
+  // Finite start value: fully masked blocks leave everything unchanged.
+  constexpr float kLazy = 8.0f;
+  float m = -3.0e38f;
+  float l = 0.0f;
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+
+  for (int i = 0; i < nh; ++i) {
+    const int cur = i & 1;
+    // The next block (this one again after the last: a harmless reload into the idle
+    // buffer) is fetched in two halves: K during the first 64-key half of this block,
+    // V during the second; each half is stored into the other LDS buffer once fetched.
+    const int bn = hl[1 + min(i + 1, nh - 1)];
+    const int nvn = min(kBlk, D.N - bn * kBlk);
+    gload_k<DH>(nx.k, k + (kvbase + (int64_t)bn * kBlk) * DH, nvn);
+    const int j0 = hl[1 + i] * kBlk;
+    const bool chose = (sb >> i) & 1u;
+    const bool any = __ballot(chose) != 0ull;
+    // causal mask (keys j > p) only where a row that chose the block ends inside it; a row
+    // that did not choose the block gets P = 0 through an infinite exponent offset below
+    const bool need_mask = __ballot(chose && p < j0 + kBlk - 1) != 0ull;
+    auto half = [&](auto hf_tag) {
+      constexpr int HF = decltype(hf_tag)::value;
+      const unsigned char* lk = L.k[cur];
+      const unsigned char* lvt = L.vt[cur];
+      f32x16 sacc[2];
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int kt = 2 * HF + k2;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lk[(kt * 32 + nl) * HotLds<DH>::KROW + DH * h + 16 * ks]);
+          sacc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[ks], sacc[k2], 0, 0, 0);
+        }
+      }
+      if (need_mask) {
+        // key j0 + 64 HF + 32 k2 + 8 (r / 4) + 4 h + r % 4 > p, constant part on the left
+        const int bound = p - j0 - 64 * HF - 4 * h;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * k2 + 8 * (r >> 2) + (r & 3) > bound) sacc[k2][r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[k2][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (!chose) mx = -INFINITY;
+      if (__ballot(mx * sc > m * sc + kLazy) != 0ull) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m - mn) * sc);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
+      // exponent offset; +inf for a row that did not choose the block: fma(s, sc, -inf) is
+      // -inf for every finite or -inf score, so its P is exactly 0
+      const float msc = chose ? m * sc : INFINITY;
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const float a = __builtin_amdgcn_exp2f(fmaf(sacc[k2][8 * pp + 2 * x], sc, -msc));
+            const float c = __builtin_amdgcn_exp2f(fmaf(sacc[k2][8 * pp + 2 * x + 1], sc, -msc));
+            l += a + c;
+            pk[x] = cvt_bf16x2(a, c);
+          }
+          pf[k2][pp] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        }
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int kb0 = ((2 * HF + k2) * 32 + 16 * pp + 4 * h) * 2;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const unsigned char* vrow = &lvt[(dt * 32 + nl) * HotLds<DH>::VROW];
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb0);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb0 + 16);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[k2][pp], oacc[dt], 0, 0, 0);
+          }
+        }
+      }
+    };
+    if (any) half(std::integral_constant<int, 0>{});
+    lstore_k<DH>(L.k[cur ^ 1], nx.k);
+    gload_v<DH>(nx.v, v + (kvbase + (int64_t)bn * kBlk) * DH, nvn);
+    if (any) half(std::integral_constant<int, 1>{});
+    lstore_vt<DH>(L.vt[cur ^ 1], nx.v);
+    __syncthreads();
+  }
+  l += __shfl_xor(l, 32, 64);
+
+  // every wave is past the last barrier: k[0..1] take the transposed outputs
+  unsigned char* buf = &L.k[0][0] + wave * 32 * QROW;
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  unsigned char* orow = buf + nl * QROW + 8 * h;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      uint2 o;
+      o.x = cvt_bf16x2(oacc[dt][4 * qd] * inv, oacc[dt][4 * qd + 1] * inv);
+      o.y = cvt_bf16x2(oacc[dt][4 * qd + 2] * inv, oacc[dt][4 * qd + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + (dt * 32 + 8 * qd) * 2) = o;
+    }
+  }
+  if (h == 0) L.lse[wave][nl] = (m * sc + __builtin_amdgcn_logf(l)) * kLn2;
+  wave_lds_sync();
+#pragma unroll
+  for (int u = 0; u < QRegs<DH>::PIECES; ++u) {
+    const int pc = lane + 64 * u;
+    const int mr = pc / CPR, col = pc % CPR;
+    const int r = mr / G, hh = mr % G;
+    const int64_t pi = L.pidx[wave][r];
+    if (tq0 + r < t_end && pi >= 0)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(buf + mr * QROW + col * 16),
+                                  reinterpret_cast<u32x4*>(part_o + (pi * G + hh) * DH + col * 8));
+  }
+  if (lane < 32) {
+    const int r = lane / G;
+    const int64_t pi = L.pidx[wave][r];
+    if (tq0 + r < t_end && pi >= 0) part_lse[pi * G + lane % G] = L.lse[wave][lane];
+  }
+}
+
 template <int DH, int G, bool DECODE>
 void launch_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int4* wl,
               const int* n_items, int64_t grid, const int32_t* entries, float* part_lse, uint16_t* part_o,
@@ -355,7 +646,30 @@ __global__ void __launch_bounds__(256) decode_items(Dims D, const int32_t* __res
   ent[i] = t * D.k + slot;
 }
 
+template <int DH, int G>
+void launch_hot_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const HotSplit& h,
+                  float* part_lse, uint16_t* part_o, int wpt, int64_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((hot_mfma<DH, G>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, h.hot, h.hotmask,
+                     h.selbits, part_lse, part_o, h.ntiles, wpt);
+}
+
 }  // namespace
+
+hipError_t launch_hot_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const HotSplit& h,
+                           float* part_lse, uint16_t* part_o, hipStream_t st) {
+  const int qwg = kWaves * (32 / D.G);
+  const int wpt = (kHotTile + qwg - 1) / qwg;
+  const int64_t nitems = (int64_t)D.S * D.Hkv * h.ntiles * wpt;
+  if (nitems >= (1ll << 31) - 8) return hipErrorInvalidValue;
+  const int64_t grid = (nitems + 7) / 8 * 8;
+  LaunchScope scope("hot_mfma", st);
+#define MSA_HOT_CASE(DH_, G_) \
+  if (D.d == DH_ && D.G == G_) { launch_hot_t<DH_, G_>(D, q, k, v, h, part_lse, part_o, wpt, grid, st); return hipGetLastError(); }
+  MSA_HOT_CASE(128, 8); MSA_HOT_CASE(128, 1); MSA_HOT_CASE(128, 2); MSA_HOT_CASE(128, 4); MSA_HOT_CASE(128, 16);
+  MSA_HOT_CASE(64, 8); MSA_HOT_CASE(64, 1); MSA_HOT_CASE(64, 2); MSA_HOT_CASE(64, 4); MSA_HOT_CASE(64, 16);
+#undef MSA_HOT_CASE
+  return hipErrorInvalidValue;
+}
 
 bool ogq_mfma_supported(const Dims& D) {
   return D.dtype == MSA_BF16 && (D.d == 64 || D.d == 128) &&

@@ -1,0 +1,285 @@
+// hot_tiles.hip -- split of the prefill selection into query-tile ("hot") blocks and
+// Outer-Gather-Q ("cold") pairs.
+//
+// The pages' head-pattern appendix (page "MSA 稀疏注意力三国杀：NSA / DSA / MoBA / MSA
+// 四方案深度对比") shows that neighbouring queries choose largely the same blocks: the
+// diagonal (own and adjacent blocks), the sink and per-group stripes.  A block chosen by
+// most rows of one 128-position query tile is cheaper to process tile-wise -- the tile's
+// Q rows stay on chip while the block streams past once, and the row keeps ONE partial
+// for all such blocks -- than to gather every row's Q again and write one partial per
+// (row, block).  The remaining (row, block) pairs keep the Outer-Gather-Q order of
+// section Kernel 创新：Outer Gather Q.  Both halves compute exact block-restricted
+// softmax terms, so the merged result is the same exact attention.
+//
+// Query tile tau = absolute positions [128 tau, 128 tau + 127] intersected with the
+// query rows [N - T, N).  A block b is hot for (s, g, tau) when at least half of the
+// tile's rows, and at least kHotMinRows rows, selected it; at most kHotMax hot blocks
+// are kept, taken in descending id order so the tile's own block (chosen by every row)
+// always stays.  Outputs, per row (s, t, g):
+//   hotmask  uint64: bit slot set if sel[s,g,t,slot] is a hot block of the row's tile;
+//   selbits  uint32: bit i set if the row selected hot block i of its tile;
+// per (s, g, tau): hot list {count, ids...} (kHotStride ints).
+// The cold CSR keeps the entries of the caller's CSR whose slot bit is clear, in the
+// same order and the same format (flat (s, g, b) offsets, ascending rows).
+#include "msa_internal.hpp"
+#include "scan.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kHotMinRows = 32;
+constexpr int kChunk = 2048;   // CSR positions per workgroup of the compaction
+constexpr int kMaxNb = 8192;
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Rows [t_lo, t_end) of query tile `ti` (0-based from the tile holding row 0).
+__device__ __forceinline__ void tile_rows(const Dims& D, int ti, int& t_lo, int& t_end) {
+  const int tau = D.pos0 / kHotTile + ti;
+  t_lo = max(tau * kHotTile, D.pos0) - D.pos0;
+  t_end = min(tau * kHotTile + kHotTile, D.N) - D.pos0;
+}
+
+// One workgroup per (s, g, tile): block histogram of the tile's selections in LDS.
+__global__ void __launch_bounds__(256) hot_select(Dims D, const int32_t* __restrict__ sel,
+                                                  int32_t* __restrict__ hot, uint64_t* __restrict__ hotmask,
+                                                  uint32_t* __restrict__ selbits, int ntiles) {
+  __shared__ int hist[kMaxNb];
+  __shared__ int s_hot[kHotMax];
+  __shared__ int s_n;
+  const int ti = blockIdx.x;
+  const int64_t sg = blockIdx.y;
+  const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
+  int t_lo, t_end;
+  tile_rows(D, ti, t_lo, t_end);
+  const int rows = t_end - t_lo;
+  const int32_t* srow = sel + (sg * D.T + t_lo) * D.k;
+  const bool active = rows >= kHotMinRows;
+  if (active) {
+    for (int b = threadIdx.x; b < D.nb; b += 256) hist[b] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < rows * D.k; i += 256) {
+      const int b = srow[i];
+      if (b >= 0 && b < D.nb) atomicAdd(&hist[b], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int thr = max(kHotMinRows, (rows + 1) / 2);
+      int n = 0;
+      for (int base = D.nb - 1; base >= 0 && n < kHotMax; base -= 64) {
+        const int b = base - lane;
+        const bool f = b >= 0 && hist[b] >= thr;
+        const uint64_t m = __ballot(f);
+        const int at = n + lanes_below(m);
+        if (f && at < kHotMax) s_hot[at] = b;
+        n += __popcll(m);
+      }
+      if (lane == 0) s_n = min(n, kHotMax);
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < s_n) hist[s_hot[threadIdx.x]] = -1 - (int)threadIdx.x;  // hot index, negated
+    __syncthreads();
+  } else if (threadIdx.x == 0) {
+    s_n = 0;
+  }
+  if (!active) __syncthreads();
+  const int nh = s_n;
+  for (int r = threadIdx.x; r < rows; r += 256) {
+    uint64_t hm = 0;
+    uint32_t sb = 0;
+    if (nh > 0) {
+      for (int slot = 0; slot < D.k; ++slot) {
+        const int b = srow[r * D.k + slot];
+        if (b >= 0 && b < D.nb) {
+          const int x = hist[b];
+          if (x < 0) {
+            hm |= 1ull << slot;
+            sb |= 1u << (-1 - x);
+          }
+        }
+      }
+    }
+    const int64_t row = ((int64_t)s * D.T + t_lo + r) * D.Hkv + g;
+    hotmask[row] = hm;
+    selbits[row] = sb;
+  }
+  if ((int)threadIdx.x <= kHotMax) {
+    const int i = threadIdx.x;
+    hot[(sg * ntiles + ti) * kHotStride + i] = i == 0 ? nh : (i - 1 < nh ? s_hot[i - 1] : -1);
+  }
+}
+
+// ------------------------------------------------------------------ cold CSR
+// Positions [F0, total) of the flat entry array, F = csr_offsets flattened over
+// (s, g, b) with nb + 1 values per (s, g); F0 = F[0], total = F[last].
+
+// Largest sg in [lo, hi] whose list starts at or before position i.
+__device__ __forceinline__ int sg_of(const int32_t* off, int nb1, int lo, int hi, int i) {
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[(int64_t)mid * nb1] <= i) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ bool entry_cold(const Dims& D, const uint64_t* hotmask, int sg, int e) {
+  if ((unsigned)e >= (unsigned)(D.T * D.k)) return true;
+  const int t = e / D.k, slot = e - t * D.k;
+  const int s = sg / D.Hkv, g = sg - s * D.Hkv;
+  return ((hotmask[((int64_t)s * D.T + t) * D.Hkv + g] >> slot) & 1ull) == 0ull;
+}
+
+struct ChunkRange {
+  int lo, hi, sg_lo, sg_hi;
+};
+
+__device__ __forceinline__ bool chunk_range(const Dims& D, const int32_t* off, ChunkRange& c) {
+  const int nb1 = D.nb + 1, nsg = D.S * D.Hkv;
+  const int F0 = off[0];
+  const int total = off[(int64_t)nsg * nb1 - 1];
+  c.lo = F0 + (int)blockIdx.x * kChunk;
+  if (c.lo >= total) return false;
+  c.hi = min(c.lo + kChunk, total);
+  c.sg_lo = sg_of(off, nb1, 0, nsg - 1, c.lo);
+  c.sg_hi = sg_of(off, nb1, c.sg_lo, nsg - 1, c.hi - 1);
+  return true;
+}
+
+__global__ void __launch_bounds__(256) cold_count(Dims D, const int32_t* __restrict__ off,
+                                                  const int32_t* __restrict__ ent,
+                                                  const uint64_t* __restrict__ hotmask, int* __restrict__ cnt) {
+  __shared__ int wsum[4];
+  ChunkRange c;
+  int n = 0;
+  if (chunk_range(D, off, c)) {
+    for (int i = c.lo + threadIdx.x; i < c.hi; i += 256) {
+      const int sg = c.sg_lo == c.sg_hi ? c.sg_lo : sg_of(off, D.nb + 1, c.sg_lo, c.sg_hi, i);
+      n += entry_cold(D, hotmask, sg, ent[i]) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, 64);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+// rank[i - F0] = number of cold entries before position i; cold entries are copied
+// to cold_ent[rank].
+__global__ void __launch_bounds__(256) cold_scatter(Dims D, const int32_t* __restrict__ off,
+                                                    const int32_t* __restrict__ ent,
+                                                    const uint64_t* __restrict__ hotmask,
+                                                    const int* __restrict__ base, int32_t* __restrict__ cold_ent,
+                                                    int32_t* __restrict__ rank) {
+  __shared__ int wsum[4];
+  ChunkRange c;
+  if (!chunk_range(D, off, c)) return;
+  const int F0 = off[0];
+  const int wave = threadIdx.x >> 6;
+  int run = base[blockIdx.x];
+  for (int r0 = c.lo; r0 < c.hi; r0 += 256) {
+    const int i = r0 + threadIdx.x;
+    const bool in = i < c.hi;
+    const int e = in ? ent[i] : 0;
+    bool cold = false;
+    if (in) {
+      const int sg = c.sg_lo == c.sg_hi ? c.sg_lo : sg_of(off, D.nb + 1, c.sg_lo, c.sg_hi, i);
+      cold = entry_cold(D, hotmask, sg, e);
+    }
+    const uint64_t m = __ballot(cold);
+    if ((threadIdx.x & 63) == 0) wsum[wave] = __popcll(m);
+    __syncthreads();
+    int before = run;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int rk = before + lanes_below(m);
+    if (in) rank[i - F0] = rk;
+    if (cold) cold_ent[rk] = e;
+    run += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(256) cold_offsets(Dims D, const int32_t* __restrict__ off,
+                                                    const int32_t* __restrict__ rank,
+                                                    const int* __restrict__ n_cold, int32_t* __restrict__ cold_off) {
+  const int64_t nflat = (int64_t)D.S * D.Hkv * (D.nb + 1);
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= nflat) return;
+  const int F0 = off[0];
+  const int total = off[nflat - 1];
+  const int p = off[x];
+  cold_off[x] = p >= total ? *n_cold : rank[p - F0];
+}
+
+}  // namespace
+
+int hot_num_tiles(const Dims& D) { return (D.N - 1) / kHotTile - D.pos0 / kHotTile + 1; }
+
+HotSplit hot_split_layout(const Dims& D, void* base, size_t* total) {
+  const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
+  const int64_t npart = rows * D.k;
+  const int64_t nchunk = (npart + kChunk - 1) / kChunk;
+  const int64_t nflat = (int64_t)D.S * D.Hkv * (D.nb + 1);
+  unsigned char* p = static_cast<unsigned char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    void* r = p ? p + off : nullptr;
+    off += align_up(bytes, 256);
+    return r;
+  };
+  HotSplit h{};
+  h.ntiles = hot_num_tiles(D);
+  h.nchunk = nchunk;
+  h.hot = static_cast<int32_t*>(take((size_t)D.S * D.Hkv * h.ntiles * kHotStride * sizeof(int32_t)));
+  h.hotmask = static_cast<uint64_t*>(take(rows * sizeof(uint64_t)));
+  h.selbits = static_cast<uint32_t*>(take(rows * sizeof(uint32_t)));
+  h.cold_off = static_cast<int32_t*>(take(nflat * sizeof(int32_t)));
+  h.cold_ent = static_cast<int32_t*>(take(npart * sizeof(int32_t)));
+  h.rank = static_cast<int32_t*>(take(npart * sizeof(int32_t)));
+  h.chunk_cnt = static_cast<int*>(take(nchunk * sizeof(int)));
+  h.chunk_base = static_cast<int*>(take(nchunk * sizeof(int)));
+  h.n_cold = static_cast<int*>(take(sizeof(int)));
+  h.scan_ws = take(scan_workspace_bytes(nchunk));
+  *total = off;
+  return h;
+}
+
+hipError_t launch_hot_split(const Dims& D, const int32_t* sel, const int32_t* off, const int32_t* ent,
+                            const HotSplit& h, hipStream_t st) {
+  if (D.nb > kMaxNb) return hipErrorInvalidValue;
+  {
+    LaunchScope s("hot_select", st);
+    hipLaunchKernelGGL(hot_select, dim3((unsigned)h.ntiles, (unsigned)(D.S * D.Hkv)), dim3(256), 0, st, D, sel,
+                       h.hot, h.hotmask, h.selbits, h.ntiles);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    LaunchScope s("cold_count", st);
+    hipLaunchKernelGGL(cold_count, dim3((unsigned)h.nchunk), dim3(256), 0, st, D, off, ent, h.hotmask, h.chunk_cnt);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_exclusive_scan(h.chunk_cnt, h.chunk_base, h.nchunk, h.n_cold, h.scan_ws, st);
+  if (e != hipSuccess) return e;
+  {
+    LaunchScope s("cold_scatter", st);
+    hipLaunchKernelGGL(cold_scatter, dim3((unsigned)h.nchunk), dim3(256), 0, st, D, off, ent, h.hotmask,
+                       h.chunk_base, h.cold_ent, h.rank);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nflat = (int64_t)D.S * D.Hkv * (D.nb + 1);
+  {
+    LaunchScope s("cold_offsets", st);
+    hipLaunchKernelGGL(cold_offsets, dim3((unsigned)((nflat + 255) / 256)), dim3(256), 0, st, D, off, h.rank,
+                       h.n_cold, h.cold_off);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

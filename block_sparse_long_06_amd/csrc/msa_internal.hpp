@@ -46,10 +46,35 @@ size_t decode_workspace_bytes(const Dims& D);
 hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void* v,
                          const int32_t* sel, void* out, void* ws, hipStream_t st);
 
-// Shared by the prefill and decode paths: merge per-slot partials into out.
+// Shared by the prefill and decode paths: merge per-slot partials into out.  With
+// hotmask (per row (s, t, g)), only the lowest hot slot of a row is read: it holds
+// the row's partial over all of its hot blocks; the other hot slots are skipped.
 hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part_lse,
-                            const void* part_o, int part_o_is_bf16, void* out, hipStream_t st,
-                            const char* name);
+                            const void* part_o, int part_o_is_bf16, const uint64_t* hotmask, void* out,
+                            hipStream_t st, const char* name);
+
+// Query-tile / Outer-Gather-Q split of a prefill selection (hot_tiles.hip).
+constexpr int kHotTile = 128;            // query tile: one 128-position block
+constexpr int kHotMax = 32;              // hot blocks kept per (sequence, group, tile)
+constexpr int kHotStride = kHotMax + 1;  // {count, ids...} per (sequence, group, tile)
+struct HotSplit {
+  int ntiles;
+  int64_t nchunk;
+  int32_t* hot;         // [S*Hkv, ntiles, kHotStride]
+  uint64_t* hotmask;    // [S, T, Hkv]
+  uint32_t* selbits;    // [S, T, Hkv]
+  int32_t* cold_off;    // [S, Hkv, nb + 1]
+  int32_t* cold_ent;    // [S*T*Hkv*k] capacity
+  int32_t* rank;        // [S*T*Hkv*k]
+  int* chunk_cnt;
+  int* chunk_base;
+  int* n_cold;
+  void* scan_ws;
+};
+int hot_num_tiles(const Dims& D);
+HotSplit hot_split_layout(const Dims& D, void* base, size_t* total);
+hipError_t launch_hot_split(const Dims& D, const int32_t* sel, const int32_t* off, const int32_t* ent,
+                            const HotSplit& h, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

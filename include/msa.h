@@ -126,8 +126,17 @@ msa_status msa_invert_selection(const msa_problem* prob, const int32_t* sel,
  *   per-(row, slot, head) partial (lse, O).  A second kernel merges the partials:
  *     out[s,t,h,:] = sum_{j in J} softmax_j(scale * q[s,t,h,:] . k[s,g,j,:]) v[s,g,j,:]
  *     J = union over valid slots of [bB, (b+1)B) intersected with [0, p_t].
- *   sel, csr_offsets and csr_entries are the outputs of the two calls above.
- *   workspace: msa_workspace_bytes(prob, MSA_CALL_PREFILL) bytes (partials + work list).
+ *   sel, csr_offsets and csr_entries are the outputs of the two calls above (sel rows
+ *   hold distinct blocks b <= b_t).
+ *   bf16 problems: a block chosen by at least half (and at least 32) of the rows of one
+ *   128-position query tile is instead processed tile-wise -- the tile's Q rows stay on
+ *   chip while the block streams past, and each row keeps one partial over all such
+ *   blocks -- and only the remaining (row, block) entries of the CSR take the
+ *   Outer-Gather-Q kernel.  The result is the same exact attention.  Setting the
+ *   environment variable MSA_HOT_TILES=0 (read at each call) sends every entry through
+ *   the Outer-Gather-Q kernel.
+ *   workspace: msa_workspace_bytes(prob, MSA_CALL_PREFILL) bytes (partials, work list,
+ *   query-tile split).
  */
 msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, const void* k,
                                    const void* v, const int32_t* csr_offsets,

@@ -31,6 +31,11 @@ CASES = [
     W.small("bf16_k1_block_local", S=1, T=600, N=900, H=8, Hkv=1, d=128, dI=64, k=1),
     W.small("bf16_structured", S=1, T=4096, N=4096, H=16, Hkv=2, d=128, dI=64, k=16,
             structure="band_sink_needles"),
+    W.small("bf16_structured_ragged", S=2, T=1000, N=3000, H=16, Hkv=2, d=128, dI=64, k=16,
+            structure="band_sink_needles"),
+    # k >= nb for most rows: every causal block is chosen by every row of a tile, so the
+    # last tiles have more than 32 blocks that qualify as tile-shared (the cap applies)
+    W.small("bf16_k64_all_blocks_shared", S=1, T=5120, N=5120, H=8, Hkv=1, d=128, dI=64, k=64),
     W.small("fp32_g2_d128", S=2, T=500, N=777, H=4, Hkv=2, d=128, dI=64, k=5, dtype=synth.F32),
     W.small("fp32_g8_d64", S=1, T=1200, N=1300, H=8, Hkv=1, d=64, dI=32, k=6, dtype=synth.F32),
 ]
@@ -72,6 +77,26 @@ def test_prefill_pipeline_matches_oracle(wl):
     inputs = gen(wl)
     _, bufs = full_prefill(wl, inputs)
     _verify_prefill(wl, inputs, bufs)
+
+
+QT_OFF_CASES = [c for c in CASES if c.name in ("bf16_g8_ragged_chunk", "bf16_structured",
+                                                 "bf16_k64_all_blocks_shared", "bf16_g1_k3")]
+
+
+@pytest.mark.parametrize("wl", QT_OFF_CASES, ids=[c.name for c in QT_OFF_CASES])
+def test_prefill_without_query_tiles(wl, monkeypatch):
+    """MSA_HOT_TILES=0: every (row, block) pair takes the Outer-Gather-Q kernel.  The
+    output matches the oracle, and the default run (query-tile pass for tile-shared
+    blocks) within rounding."""
+    require_gpu()
+    say("case", wl.name, "(query tiles off)")
+    inputs = gen(wl)
+    _, on = full_prefill(wl, inputs)
+    monkeypatch.setenv("MSA_HOT_TILES", "0")
+    _, off = full_prefill(wl, inputs)
+    monkeypatch.delenv("MSA_HOT_TILES")
+    _verify_prefill(wl, inputs, off)
+    check_out(f64(on.out), f64(off.out), wl.dtype, what="query tiles on vs off")
 
 
 DEC_CASES = [
