@@ -104,10 +104,23 @@ __device__ void select_and_write(const Src& src, int lane, int need, int32_t* ou
   }
 }
 
+// Completes this wave's earlier LDS accesses before its later ones (lanes exchange data
+// through LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// VEC: rows start 16-byte aligned (nb % 4 == 0), so each lane fetches 4 consecutive
+// scores per load; the row is then re-distributed through LDS so that lane l holds
+// blocks l, l + 64, ... (the layout the ascending-id compaction below relies on).
+template <bool VEC>
 __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const float* __restrict__ scores,
                                                                   int32_t* __restrict__ sel) {
-  __shared__ uint32_t s_ord[kWaves][kCap];
-  __shared__ int32_t s_id[kWaves][kCap];
+  __shared__ __attribute__((aligned(16))) uint32_t s_buf[kWaves][2 * kCap];  // row staging / candidates
+  uint32_t* const s_ord_w = s_buf[threadIdx.x >> 6];
+  int32_t* const s_id_w = reinterpret_cast<int32_t*>(s_buf[threadIdx.x >> 6] + kCap);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
@@ -132,11 +145,33 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
     // Fast path: the row lives in registers (element i*64 + lane in slot i).
     uint32_t o[kRegPerLane];
     uint32_t lm = 0;
+    if (VEC) {
+      static_assert(2 * kCap >= 64 * kRegPerLane, "row staging fits the candidate buffer");
 #pragma unroll
-    for (int i = 0; i < kRegPerLane; ++i) {
-      const int c = i * 64 + lane;
-      o[i] = c < n ? ord_key(sc[c]) : 0u;
-      lm = o[i] > lm ? o[i] : lm;
+      for (int i = 0; i < kRegPerLane / 4; ++i) {
+        const int c = i * 256 + 4 * lane;
+        const float4 x = c < n ? *reinterpret_cast<const float4*>(sc + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        uint4 u;
+        u.x = c < n ? ord_key(x.x) : 0u;
+        u.y = c + 1 < n ? ord_key(x.y) : 0u;
+        u.z = c + 2 < n ? ord_key(x.z) : 0u;
+        u.w = c + 3 < n ? ord_key(x.w) : 0u;
+        *reinterpret_cast<uint4*>(&s_ord_w[c]) = u;
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < kRegPerLane; ++i) {
+        o[i] = s_ord_w[i * 64 + lane];
+        lm = o[i] > lm ? o[i] : lm;
+      }
+      wave_lds_sync();  // the staging area takes the candidates next
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRegPerLane; ++i) {
+        const int c = i * 64 + lane;
+        o[i] = c < n ? ord_key(sc[c]) : 0u;
+        lm = o[i] > lm ? o[i] : lm;
+      }
     }
     uint32_t t1 = 0;
     for (int bit = 31; bit >= 0; --bit) {
@@ -151,16 +186,16 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
       const uint64_t m = __ballot(f);
       const int p = C + lanes_below(m);
       if (f && p < kCap) {
-        s_ord[wave][p] = o[i];
-        s_id[wave][p] = i * 64 + lane;
+        s_ord_w[p] = o[i];
+        s_id_w[p] = i * 64 + lane;
       }
       C += __popcll(m);
     }
     if (C <= 64) {
       // one candidate per lane: each radix step is one compare and one ballot
       const bool have = lane < C;
-      const uint32_t co = have ? s_ord[wave][lane] : 0u;
-      const int32_t cid = have ? s_id[wave][lane] : 0;
+      const uint32_t co = have ? s_ord_w[lane] : 0u;
+      const int32_t cid = have ? s_id_w[lane] : 0;
       uint32_t tau = 0;
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = tau | (1u << bit);
@@ -181,7 +216,7 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
       return;
     }
     if (C <= kCap) {
-      LdsSrc src{s_ord[wave], s_id[wave], C};
+      LdsSrc src{s_ord_w, s_id_w, C};
       select_and_write(src, lane, need, out);
     } else {
       RowSrc src{sc, n};
@@ -190,11 +225,22 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
     if (lane == 0) out[need] = bt;
     return;
   }
-  // A. lane maxima over a strided share of the row
+  // A. lane maxima over a share of the row (any split works: only the maxima matter)
   uint32_t lmax = 0;
-  for (int i = lane; i < n; i += 64) {
-    const uint32_t o = ord_key(sc[i]);
-    lmax = o > lmax ? o : lmax;
+  if (VEC) {
+    for (int c = 4 * lane; c < n; c += 256) {
+      const float4 x = *reinterpret_cast<const float4*>(sc + c);
+      const uint32_t a = ord_key(x.x);
+      const uint32_t b = c + 1 < n ? ord_key(x.y) : 0u;
+      const uint32_t d = c + 2 < n ? ord_key(x.z) : 0u;
+      const uint32_t e = c + 3 < n ? ord_key(x.w) : 0u;
+      lmax = max(max(lmax, a), max(b, max(d, e)));
+    }
+  } else {
+    for (int i = lane; i < n; i += 64) {
+      const uint32_t o = ord_key(sc[i]);
+      lmax = o > lmax ? o : lmax;
+    }
   }
   // B. tau1 = need-th largest lane maximum; compact ord >= tau1 into LDS (ascending id)
   uint32_t tau1 = 0;
@@ -214,13 +260,13 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
     const uint64_t m = __ballot(f);
     const int p = C + lanes_below(m);
     if (f && p < kCap) {
-      s_ord[wave][p] = o;
-      s_id[wave][p] = i;
+      s_ord_w[p] = o;
+      s_id_w[p] = i;
     }
     C += __popcll(m);
   }
   if (C <= kCap) {
-    LdsSrc src{s_ord[wave], s_id[wave], C};
+    LdsSrc src{s_ord_w, s_id_w, C};
     select_and_write(src, lane, need, out);
   } else {
     RowSrc src{sc, n};
@@ -235,7 +281,11 @@ hipError_t launch_block_topk(const Dims& D, const float* scores, int32_t* sel, h
   const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
   const int64_t grid = (rows + kWaves - 1) / kWaves;
   LaunchScope scope(D.T == 1 ? "block_topk_t1" : "block_topk", st);
-  hipLaunchKernelGGL(block_topk_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, st, D, scores, sel);
+  const bool vec = D.nb % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15u) == 0;
+  if (vec)
+    hipLaunchKernelGGL(block_topk_kernel<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0, st, D, scores, sel);
+  else
+    hipLaunchKernelGGL(block_topk_kernel<false>, dim3((unsigned)grid), dim3(kWaves * 64), 0, st, D, scores, sel);
   return hipGetLastError();
 }
 

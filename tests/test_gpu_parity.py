@@ -197,7 +197,8 @@ def _topk_case(scores_np, T, N, k):
 
 
 @pytest.mark.parametrize("kind", ["all_equal", "signed_zero", "few_values", "neg_inf_and_huge",
-                                  "long_all_equal", "long_random", "long_ties_at_threshold"])
+                                  "long_all_equal", "long_random", "long_ties_at_threshold",
+                                  "few_values_odd_nb", "long_random_odd_nb", "ties_at_threshold_odd_nb"])
 @pytest.mark.parametrize("k", [1, 2, 16, 64])
 def test_topk_adversarial_rows(kind, k):
     require_gpu()
@@ -206,6 +207,9 @@ def test_topk_adversarial_rows(kind, k):
         T, N = 130, 8192 * 128
     else:
         T, N = 300, 300 * 128
+    if kind.endswith("_odd_nb"):  # nb % 4 != 0: rows are not 16-byte aligned (scalar loads)
+        N = N - 128 - 5
+        kind = kind[: -len("_odd_nb")]
     nb = (N + 127) // 128
     if kind in ("all_equal", "long_all_equal"):
         sc = np.full((T, nb), 0.75)
