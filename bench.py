@@ -94,11 +94,12 @@ def roofline(flops, nbytes, seconds):
     return dict(bound="hbm", achieved=a, peak=PEAK_HBM / 1e9, unit="GB/s", frac=a / (PEAK_HBM / 1e9))
 
 
-def query_tile_split(wl, sel, min_rows=32, cap=32):
+def query_tile_split(wl, sel, min_rows=32, cap=32, min_blocks=2):
     """Per-(row, slot) flag of the library's query-tile split, recomputed from sel for
     reporting: block b is tile-shared for (s, g, 128-position query tile) when at least
     max(min_rows, ceil(rows / 2)) of the tile's rows chose it and the tile has at least
-    min_rows rows; at most `cap` such blocks are kept, the highest ids first."""
+    min_rows rows; at most `cap` such blocks are kept, the highest ids first, and a tile
+    with fewer than `min_blocks` of them keeps none."""
     import torch
     S, Hkv, T, k = sel.shape
     dev = sel.device
@@ -116,6 +117,7 @@ def query_tile_split(wl, sel, min_rows=32, cap=32):
     cand = (cnt >= thr.view(1, nqb, 1)) & (rows >= min_rows).view(1, nqb, 1)
     from_top = torch.flip(torch.cumsum(torch.flip(cand.to(torch.int32), [2]), 2), [2])
     keep = cand & (from_top <= cap)
+    keep &= (cand.sum(dim=2, keepdim=True) >= min_blocks)
     return valid & keep.view(-1)[key.clamp(min=0)], keep
 
 

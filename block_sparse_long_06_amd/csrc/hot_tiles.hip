@@ -15,7 +15,8 @@
 // query rows [N - T, N).  A block b is hot for (s, g, tau) when at least half of the
 // tile's rows, and at least kHotMinRows rows, selected it; at most kHotMax hot blocks
 // are kept, taken in descending id order so the tile's own block (chosen by every row)
-// always stays.  Outputs, per row (s, t, g):
+// always stays.  A tile with fewer than kHotMinBlocks such blocks (typically its own
+// block alone) keeps all its pairs on the Outer-Gather-Q path.  Outputs, per row (s, t, g):
 //   hotmask  uint64: bit slot set if sel[s,g,t,slot] is a hot block of the row's tile;
 //   selbits  uint32: bit i set if the row selected hot block i of its tile;
 // per (s, g, tau): hot list {count, ids...} (kHotStride ints).
@@ -28,6 +29,7 @@ namespace msa {
 namespace {
 
 constexpr int kHotMinRows = 32;
+constexpr int kHotMinBlocks = 2;
 constexpr int kChunk = 2048;   // CSR positions per workgroup of the compaction
 constexpr int kMaxNb = 8192;
 
@@ -77,7 +79,9 @@ __global__ void __launch_bounds__(256) hot_select(Dims D, const int32_t* __restr
         if (f && at < kHotMax) s_hot[at] = b;
         n += __popcll(m);
       }
-      if (lane == 0) s_n = min(n, kHotMax);
+      // a tile whose only shared block is its own is left to Outer-Gather-Q: staging one
+      // block per workgroup slice costs more than it saves
+      if (lane == 0) s_n = n >= kHotMinBlocks ? min(n, kHotMax) : 0;
     }
     __syncthreads();
     if ((int)threadIdx.x < s_n) hist[s_hot[threadIdx.x]] = -1 - (int)threadIdx.x;  // hot index, negated

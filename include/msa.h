@@ -129,10 +129,10 @@ msa_status msa_invert_selection(const msa_problem* prob, const int32_t* sel,
  *   sel, csr_offsets and csr_entries are the outputs of the two calls above (sel rows
  *   hold distinct blocks b <= b_t).
  *   bf16 problems: a block chosen by at least half (and at least 32) of the rows of one
- *   128-position query tile is instead processed tile-wise -- the tile's Q rows stay on
- *   chip while the block streams past, and each row keeps one partial over all such
- *   blocks -- and only the remaining (row, block) entries of the CSR take the
- *   Outer-Gather-Q kernel.  The result is the same exact attention.  Setting the
+ *   128-position query tile that has at least two such blocks is instead processed
+ *   tile-wise -- the tile's Q rows stay on chip while the block streams past, and each
+ *   row keeps one partial over all such blocks -- and only the remaining (row, block)
+ *   entries of the CSR take the Outer-Gather-Q kernel.  The result is the same exact attention.  Setting the
  *   environment variable MSA_HOT_TILES=0 (read at each call) sends every entry through
  *   the Outer-Gather-Q kernel.
  *   workspace: msa_workspace_bytes(prob, MSA_CALL_PREFILL) bytes (partials, work list,
