@@ -368,243 +368,315 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
 }
 
 // ------------------------------------------------------------------ query-tile pass
-// Hot blocks of a 128-position query tile (chosen by most of its rows; hot_tiles.hip)
-// are processed tile-wise: one workgroup = 8 waves x 32 M-rows of one (sequence,
-// group, tile) slice; each wave's Q B-operands stay in registers while the tile's hot
-// blocks stream through double-buffered LDS (the next block is fetched into registers
-// during the current block's MFMAs; one barrier per block).  Online softmax over the
-// blocks: m and l per M-row, the O^T accumulators rescaled by exp2((m_old - m_new) sc)
-// when the max grows.  A row that did not select a block masks all of that block's
-// scores; the causal mask applies inside the own block.  Each row with hot slots writes
-// ONE partial (over all its hot blocks) at its lowest hot slot; the merge skips the
-// row's other hot slots.
+// Shared blocks of a 128-position query tile (chosen by most of its rows;
+// hot_tiles.hip) are processed tile-wise.  Work item = one 8-wave slice of a tile:
+// 8 waves x 32 M-rows (32 query rows at G = 8).  Each wave's Q B-operands stay in
+// registers while the tile's shared blocks stream through double-buffered LDS (the
+// next block's K is fetched during the first 64-key half of the current block, its V
+// during the second; one barrier per block).  Online softmax over the blocks with a
+// lazy reference max m: it is raised only when a row's max exceeds it by more than
+// kLazy in exp2 units, so P <= 2^kLazy and the O^T accumulators are rescaled rarely
+// (any reference gives the same normalised result).  A row that did not choose a
+// block gets P = 0 through an infinite exponent offset; the causal mask applies
+// inside the own block.  Each row with shared slots writes ONE partial (over all its
+// shared blocks) at its lowest shared slot; the merge skips its other shared slots.
+//
+// The kernel is persistent: one workgroup per CU walks a contiguous range of the
+// compacted item list of its XCD (neighbouring tiles of one group share most of their
+// blocks, so they stay in that XCD's L2).  The next item's first block is staged into
+// the idle buffer during the current item's last block, and its Q rows are fetched
+// while the current item writes its outputs, so only the first item pays the
+// start-up latency.
 template <int DH>
 struct __attribute__((aligned(16))) HotLds {
-  static constexpr int KROW = OgqLds<DH>::KROW, VROW = OgqLds<DH>::VROW, QROW = OgqLds<DH>::QROW;
-  // k[0..1] also serve, after the block loop, as the 8 per-wave output buffers
-  // (8 * 32 * QROW bytes == 2 * kBlk * KROW bytes).
-  __attribute__((aligned(16))) unsigned char k[2][kBlk * KROW];
-  __attribute__((aligned(16))) unsigned char vt[2][DH * VROW];
-  int64_t pidx[kWaves][32];
+  static constexpr int KROW = OgqLds<DH>::KROW, VROW = OgqLds<DH>::VROW;
+  static constexpr int QROW = DH * 2 + 8;             // output transpose row
+  static constexpr int KB = kBlk * KROW;              // K part of a buffer
+  static constexpr int BUF = KB + DH * VROW;          // K | V^T
+  // buf[b] holds one block; the buffer freed by an item's last block receives that
+  // item's transposed outputs (8 waves x 32 rows x QROW bytes)
+  __attribute__((aligned(16))) unsigned char buf[2][BUF];
+  int64_t pidx[2][kWaves][32];  // per item parity: partial index of the wave's rows, -1 if none
   float lse[kWaves][32];
 };
+
+// Per-item values of one lane.
+struct HotItem {
+  const int32_t* hl;  // {count, block ids...}
+  int nh;
+  int64_t sg;
+  int s, g;
+  int t_end;          // one past the tile's last row
+  int tq0;            // the wave's first query row
+  bool row_ok;
+  uint32_t sb;        // shared blocks chosen by the lane's row
+  int p;              // the row's position
+};
+
+template <int DH, int G>
+__device__ __forceinline__ void hot_item_load(HotItem& it, bf16x8 (&bq)[DH / 16], const Dims& D, const uint16_t* q,
+                                              const int32_t* hot, const int32_t* tiles, const uint64_t* hotmask,
+                                              const uint32_t* selbits, int item, int ntiles, int wpt,
+                                              int64_t (&pidx)[kWaves][32]) {
+  constexpr int KS = DH / 16;
+  constexpr int RW = 32 / G;
+  constexpr int QWG = kWaves * RW;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int nl = lane & 31;
+  const int part = item % wpt;
+  const int tl = tiles[item / wpt];
+  const int ti = tl % ntiles;
+  it.sg = tl / ntiles;
+  it.hl = hot + (int64_t)tl * kHotStride;
+  it.nh = it.hl[0];
+  it.s = (int)(it.sg / D.Hkv);
+  it.g = (int)(it.sg % D.Hkv);
+  const int tau = D.pos0 / kHotTile + ti;
+  const int t_lo = max(tau * kHotTile, D.pos0) - D.pos0;
+  it.t_end = min(tau * kHotTile + kHotTile, D.N) - D.pos0;
+  it.tq0 = t_lo + part * QWG + wave * RW;
+  const int t = it.tq0 + nl / G;  // this lane's M-row = (t, head nl % G)
+  it.row_ok = t < it.t_end;
+  const int tt = it.row_ok ? t : 0;
+  const int64_t rowid = ((int64_t)it.s * D.T + tt) * D.Hkv + it.g;
+  it.sb = it.row_ok ? selbits[rowid] : 0u;
+  it.p = D.pos0 + tt;
+  // Q B-operands: lane half h, k-step ks -> head dims [DH/2 h + 8 ks, +8)
+  const uint16_t* qp = q + (((int64_t)it.s * D.T + tt) * D.H + (int64_t)it.g * G + nl % G) * DH + (DH / 2) * h;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) bq[ks] = it.row_ok ? *reinterpret_cast<const bf16x8*>(qp + 8 * ks) : bf16x8{};
+  if (h == 0 && nl % G == 0) {
+    int64_t pi = -1;
+    if (it.row_ok) {
+      const uint64_t hm = hotmask[rowid];
+      if (hm != 0ull) pi = rowid * D.k + __builtin_ctzll(hm);
+    }
+    pidx[wave][nl / G] = pi;
+  }
+}
 
 template <int DH, int G>
 __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      const uint16_t* __restrict__ v,
                                                      const int32_t* __restrict__ hot,
+                                                     const int32_t* __restrict__ tiles,
+                                                     const int* __restrict__ ntile,
                                                      const uint64_t* __restrict__ hotmask,
                                                      const uint32_t* __restrict__ selbits,
                                                      float* __restrict__ part_lse,
                                                      uint16_t* __restrict__ part_o, int ntiles, int wpt) {
   constexpr int KS = DH / 16;
   constexpr int DT = DH / 32;
-  constexpr int RW = 32 / G;           // query rows per wave
-  constexpr int QWG = kWaves * RW;     // query rows per workgroup
   constexpr int CPR = DH / 8;
   constexpr int QROW = HotLds<DH>::QROW;
-  static_assert(kWaves * 32 * QROW <= 2 * kBlk * HotLds<DH>::KROW, "output buffers overlay k[0..1]");
+  static_assert(kWaves * 32 * QROW <= HotLds<DH>::BUF, "output transpose fits one buffer");
   __shared__ HotLds<DH> L;
 
-  // XCD-aware order: consecutive items (slices of one tile, then neighbouring tiles of
-  // one group, which share most hot blocks) go to one XCD.
-  const int nitems = D.S * D.Hkv * ntiles * wpt;  // < 2^31 (checked at launch)
+  // this workgroup's items: a round-robin share of its XCD's contiguous range
+  const int nitems = *ntile * wpt;
   const int per_xcd = (nitems + 7) / 8;
-  const int slot_in_xcd = blockIdx.x >> 3;
-  const int item = (blockIdx.x & 7) * per_xcd + slot_in_xcd;
-  if (slot_in_xcd >= per_xcd || item >= nitems) return;
-  const int part = item % wpt;
-  const int ti = (item / wpt) % ntiles;
-  const int64_t sg = item / (wpt * ntiles);
-  const int32_t* hl = hot + (sg * ntiles + ti) * kHotStride;
-  const int nh = hl[0];
-  if (nh <= 0) return;
-  const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
-  const int tau = D.pos0 / kHotTile + ti;
-  const int t_lo = max(tau * kHotTile, D.pos0) - D.pos0;
-  const int t_end = min(tau * kHotTile + kHotTile, D.N) - D.pos0;
+  const int xcd = blockIdx.x & 7;
+  const int nwx = ((int)gridDim.x - xcd + 7) / 8;  // workgroups on this XCD
+  const int end = min((xcd + 1) * per_xcd, nitems);
+  int item = xcd * per_xcd + (int)(blockIdx.x >> 3);
+  if (item >= end) return;
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int nl = lane & 31;
-  const int tq0 = t_lo + part * QWG + wave * RW;  // the wave's first query row
-  const int t = tq0 + nl / G;                     // this lane's M-row = (t, head nl % G)
-  const bool row_ok = t < t_end;
-  const int64_t rowid = ((int64_t)s * D.T + (row_ok ? t : 0)) * D.Hkv + g;
-  const uint32_t sb = row_ok ? selbits[rowid] : 0u;
-  const int p = D.pos0 + (row_ok ? t : 0);
+  const float sc = D.scale * kLog2e;
+  constexpr float kLazy = 8.0f;
 
-  // Q B-operands: lane half h, k-step ks -> head dims [DH/2 h + 8 ks, +8)
+  HotItem it;
   bf16x8 bq[KS];
-  {
-    const uint16_t* qp = q + (((int64_t)s * D.T + (row_ok ? t : 0)) * D.H + (int64_t)g * G + nl % G) * DH + (DH / 2) * h;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      bq[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 8 * ks) : bf16x8{};
-  }
-  if (h == 0 && nl % G == 0) {
-    int64_t pi = -1;
-    if (row_ok) {
-      const uint64_t hm = hotmask[rowid];
-      if (hm != 0ull) pi = rowid * D.k + __builtin_ctzll(hm);
-    }
-    L.pidx[wave][nl / G] = pi;
-  }
-
-  const int64_t kvbase = sg * D.N;
+  int par = 0;
+  hot_item_load<DH, G>(it, bq, D, q, hot, tiles, hotmask, selbits, item, ntiles, wpt, L.pidx[par]);
   KVRegs<DH> nx;
   {
-    const int b = hl[1];
-    gload_kv<DH>(nx, k + (kvbase + (int64_t)b * kBlk) * DH, v + (kvbase + (int64_t)b * kBlk) * DH,
-                 min(kBlk, D.N - b * kBlk));
-    lstore_kv<DH>(L.k[0], L.vt[0], nx);
+    const int b = it.hl[1];
+    const int64_t kv0 = (it.sg * D.N + (int64_t)b * kBlk) * DH;
+    gload_kv<DH>(nx, k + kv0, v + kv0, min(kBlk, D.N - b * kBlk));
+    lstore_k<DH>(L.buf[0], nx.k);
+    lstore_vt<DH>(L.buf[0] + HotLds<DH>::KB, nx.v);
   }
   __syncthreads();
+  int cur = 0;
 
-  const float sc = D.scale * kLog2e;
-  // Running reference max m (raw score units) of each M-row.  It is raised only when a
-  // row's max exceeds it by more than kLazy in exp2 units, so P <= 2^kLazy and the O
-  // accumulators are rescaled rarely (any reference gives the same normalised result).
-  // Finite start value: fully masked blocks leave everything unchanged.
-  constexpr float kLazy = 8.0f;
-  float m = -3.0e38f;
-  float l = 0.0f;
-  f32x16 oacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  while (true) {
+    const int next_item = item + nwx;
+    const bool has_next = next_item < end;
+    // the first block of the next item (its hot list is all that is needed now)
+    int nb_first = 0;
+    int64_t nsg = 0;
+    if (has_next) {
+      const int ntl = tiles[next_item / wpt];
+      nsg = ntl / ntiles;
+      nb_first = hot[(int64_t)ntl * kHotStride + 1];
+    }
 
-  for (int i = 0; i < nh; ++i) {
-    const int cur = i & 1;
-    // The next block (this one again after the last: a harmless reload into the idle
-    // buffer) is fetched in two halves: K during the first 64-key half of this block,
-    // V during the second; each half is stored into the other LDS buffer once fetched.
-    const int bn = hl[1 + min(i + 1, nh - 1)];
-    const int nvn = min(kBlk, D.N - bn * kBlk);
-    gload_k<DH>(nx.k, k + (kvbase + (int64_t)bn * kBlk) * DH, nvn);
-    const int j0 = hl[1 + i] * kBlk;
-    const bool chose = (sb >> i) & 1u;
-    const bool any = __ballot(chose) != 0ull;
-    // causal mask (keys j > p) only where a row that chose the block ends inside it; a row
-    // that did not choose the block gets P = 0 through an infinite exponent offset below
-    const bool need_mask = __ballot(chose && p < j0 + kBlk - 1) != 0ull;
-    auto half = [&](auto hf_tag) {
-      constexpr int HF = decltype(hf_tag)::value;
-      const unsigned char* lk = L.k[cur];
-      const unsigned char* lvt = L.vt[cur];
-      f32x16 sacc[2];
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
+    float m = -3.0e38f;  // running reference max of the raw scores (finite start)
+    float l = 0.0f;
+    f32x16 oacc[DT];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int kt = 2 * HF + k2;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lk[(kt * 32 + nl) * HotLds<DH>::KROW + DH * h + 16 * ks]);
-          sacc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[ks], sacc[k2], 0, 0, 0);
-        }
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+
+    for (int i = 0; i < it.nh; ++i) {
+      // next block: this item's next one, else the next item's first, else this one again
+      // (a harmless reload into the idle buffer)
+      int bn = it.hl[1 + min(i + 1, it.nh - 1)];
+      int64_t bsg = it.sg;
+      if (i + 1 == it.nh && has_next) {
+        bn = nb_first;
+        bsg = nsg;
       }
-      if (need_mask) {
-        // key j0 + 64 HF + 32 k2 + 8 (r / 4) + 4 h + r % 4 > p, constant part on the left
-        const int bound = p - j0 - 64 * HF - 4 * h;
+      const int nvn = min(kBlk, D.N - bn * kBlk);
+      const int64_t kvn = (bsg * D.N + (int64_t)bn * kBlk) * DH;
+      gload_k<DH>(nx.k, k + kvn, nvn);
+      const int j0 = it.hl[1 + i] * kBlk;
+      const bool chose = (it.sb >> i) & 1u;
+      const bool any = __ballot(chose) != 0ull;
+      // causal mask (keys j > p) only where a row that chose the block ends inside it; a row
+      // that did not choose the block gets P = 0 through an infinite exponent offset below
+      const bool need_mask = __ballot(chose && it.p < j0 + kBlk - 1) != 0ull;
+      const unsigned char* lk = L.buf[cur];
+      const unsigned char* lvt = L.buf[cur] + HotLds<DH>::KB;
+      auto half = [&](auto hf_tag) {
+        constexpr int HF = decltype(hf_tag)::value;
+        f32x16 sacc[2];
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int kt = 2 * HF + k2;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lk[(kt * 32 + nl) * HotLds<DH>::KROW + DH * h + 16 * ks]);
+            sacc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[ks], sacc[k2], 0, 0, 0);
+          }
+        }
+        if (need_mask) {
+          // key j0 + 64 HF + 32 k2 + 8 (r / 4) + 4 h + r % 4 > p, constant part on the left
+          const int bound = it.p - j0 - 64 * HF - 4 * h;
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * k2 + 8 * (r >> 2) + (r & 3) > bound) sacc[k2][r] = -INFINITY;
+        }
+        float mx = -INFINITY;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * k2 + 8 * (r >> 2) + (r & 3) > bound) sacc[k2][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[k2][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (!chose) mx = -INFINITY;
+        if (__ballot(mx * sc > m * sc + kLazy) != 0ull) {
+          const float mn = fmaxf(m, mx);
+          const float alpha = __builtin_amdgcn_exp2f((m - mn) * sc);
+          m = mn;
+          l *= alpha;
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+          for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[k2][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (!chose) mx = -INFINITY;
-      if (__ballot(mx * sc > m * sc + kLazy) != 0ull) {
-        const float mn = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m - mn) * sc);
-        m = mn;
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      }
-      // exponent offset; +inf for a row that did not choose the block: fma(s, sc, -inf) is
-      // -inf for every finite or -inf score, so its P is exactly 0
-      const float msc = chose ? m * sc : INFINITY;
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          uint32_t pk[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const float a = __builtin_amdgcn_exp2f(fmaf(sacc[k2][8 * pp + 2 * x], sc, -msc));
-            const float c = __builtin_amdgcn_exp2f(fmaf(sacc[k2][8 * pp + 2 * x + 1], sc, -msc));
-            l += a + c;
-            pk[x] = cvt_bf16x2(a, c);
-          }
-          pf[k2][pp] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
         }
-      }
+        // exponent offset; +inf for a row that did not choose the block: fma(s, sc, -inf) is
+        // -inf for every finite or -inf score, so its P is exactly 0
+        const float msc = chose ? m * sc : INFINITY;
+        bf16x8 pf[2][2];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const int kb0 = ((2 * HF + k2) * 32 + 16 * pp + 4 * h) * 2;
+          for (int pp = 0; pp < 2; ++pp) {
+            uint32_t pk[4];
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const unsigned char* vrow = &lvt[(dt * 32 + nl) * HotLds<DH>::VROW];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb0);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb0 + 16);
-            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[k2][pp], oacc[dt], 0, 0, 0);
+            for (int x = 0; x < 4; ++x) {
+              const float a = __builtin_amdgcn_exp2f(fmaf(sacc[k2][8 * pp + 2 * x], sc, -msc));
+              const float c = __builtin_amdgcn_exp2f(fmaf(sacc[k2][8 * pp + 2 * x + 1], sc, -msc));
+              l += a + c;
+              pk[x] = cvt_bf16x2(a, c);
+            }
+            pf[k2][pp] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
           }
         }
-      }
-    };
-    if (any) half(std::integral_constant<int, 0>{});
-    lstore_k<DH>(L.k[cur ^ 1], nx.k);
-    gload_v<DH>(nx.v, v + (kvbase + (int64_t)bn * kBlk) * DH, nvn);
-    if (any) half(std::integral_constant<int, 1>{});
-    lstore_vt<DH>(L.vt[cur ^ 1], nx.v);
-    __syncthreads();
-  }
-  l += __shfl_xor(l, 32, 64);
-
-  // every wave is past the last barrier: k[0..1] take the transposed outputs
-  unsigned char* buf = &L.k[0][0] + wave * 32 * QROW;
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  unsigned char* orow = buf + nl * QROW + 8 * h;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+        for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      uint2 o;
-      o.x = cvt_bf16x2(oacc[dt][4 * qd] * inv, oacc[dt][4 * qd + 1] * inv);
-      o.y = cvt_bf16x2(oacc[dt][4 * qd + 2] * inv, oacc[dt][4 * qd + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + (dt * 32 + 8 * qd) * 2) = o;
+          for (int pp = 0; pp < 2; ++pp) {
+            const int kb0 = ((2 * HF + k2) * 32 + 16 * pp + 4 * h) * 2;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              const unsigned char* vrow = &lvt[(dt * 32 + nl) * HotLds<DH>::VROW];
+              const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb0);
+              const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb0 + 16);
+              const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[k2][pp], oacc[dt], 0, 0, 0);
+            }
+          }
+        }
+      };
+      if (any) half(std::integral_constant<int, 0>{});
+      lstore_k<DH>(L.buf[cur ^ 1], nx.k);
+      gload_v<DH>(nx.v, v + kvn, nvn);
+      if (any) half(std::integral_constant<int, 1>{});
+      lstore_vt<DH>(L.buf[cur ^ 1] + HotLds<DH>::KB, nx.v);
+      __syncthreads();
+      cur ^= 1;
     }
-  }
-  if (h == 0) L.lse[wave][nl] = (m * sc + __builtin_amdgcn_logf(l)) * kLn2;
-  wave_lds_sync();
+    l += __shfl_xor(l, 32, 64);
+
+    // buf[cur] holds the next item's first block; buf[cur ^ 1] (this item's last block)
+    // takes the transposed outputs
+    const HotItem done = it;
+    const int dpar = par;
+    if (has_next) {
+      par ^= 1;
+      hot_item_load<DH, G>(it, bq, D, q, hot, tiles, hotmask, selbits, next_item, ntiles, wpt, L.pidx[par]);
+    }
+    unsigned char* buf = L.buf[cur ^ 1] + wave * 32 * QROW;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    unsigned char* orow = buf + nl * QROW + 8 * h;
 #pragma unroll
-  for (int u = 0; u < QRegs<DH>::PIECES; ++u) {
-    const int pc = lane + 64 * u;
-    const int mr = pc / CPR, col = pc % CPR;
-    const int r = mr / G, hh = mr % G;
-    const int64_t pi = L.pidx[wave][r];
-    if (tq0 + r < t_end && pi >= 0)
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(buf + mr * QROW + col * 16),
-                                  reinterpret_cast<u32x4*>(part_o + (pi * G + hh) * DH + col * 8));
-  }
-  if (lane < 32) {
-    const int r = lane / G;
-    const int64_t pi = L.pidx[wave][r];
-    if (tq0 + r < t_end && pi >= 0) part_lse[pi * G + lane % G] = L.lse[wave][lane];
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        uint2 o;
+        o.x = cvt_bf16x2(oacc[dt][4 * qd] * inv, oacc[dt][4 * qd + 1] * inv);
+        o.y = cvt_bf16x2(oacc[dt][4 * qd + 2] * inv, oacc[dt][4 * qd + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + (dt * 32 + 8 * qd) * 2) = o;
+      }
+    }
+    if (h == 0) L.lse[wave][nl] = (m * sc + __builtin_amdgcn_logf(l)) * kLn2;
+    wave_lds_sync();
+#pragma unroll
+    for (int u = 0; u < QRegs<DH>::PIECES; ++u) {
+      const int pc = lane + 64 * u;
+      const int mr = pc / CPR, col = pc % CPR;
+      const int r = mr / G, hh = mr % G;
+      const int64_t pi = L.pidx[dpar][wave][r];
+      if (done.tq0 + r < done.t_end && pi >= 0) {
+        // rows are QROW = 8 (mod 16) bytes apart: two 8-byte LDS reads
+        const unsigned char* src = buf + mr * QROW + col * 16;
+        const uint2 lo = *reinterpret_cast<const uint2*>(src);
+        const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+        const u32x4 val = {lo.x, lo.y, hi.x, hi.y};
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(part_o + (pi * G + hh) * DH + col * 8));
+      }
+    }
+    if (lane < 32) {
+      const int r = lane / G;
+      const int64_t pi = L.pidx[dpar][wave][r];
+      if (done.tq0 + r < done.t_end && pi >= 0) part_lse[pi * G + lane % G] = L.lse[wave][lane];
+    }
+    if (!has_next) break;
+    item = next_item;
+    // every wave has read its outputs back before the next item's first block stages its
+    // successor into this buffer
+    __syncthreads();
   }
 }
 
@@ -648,9 +720,9 @@ __global__ void __launch_bounds__(256) decode_items(Dims D, const int32_t* __res
 
 template <int DH, int G>
 void launch_hot_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const HotSplit& h,
-                  float* part_lse, uint16_t* part_o, int wpt, int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((hot_mfma<DH, G>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, h.hot, h.hotmask,
-                     h.selbits, part_lse, part_o, h.ntiles, wpt);
+                  float* part_lse, uint16_t* part_o, int wpt, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((hot_mfma<DH, G>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, h.hot, h.tiles,
+                     h.ntile, h.hotmask, h.selbits, part_lse, part_o, h.ntiles, wpt);
 }
 
 }  // namespace
@@ -659,9 +731,14 @@ hipError_t launch_hot_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, 
                            float* part_lse, uint16_t* part_o, hipStream_t st) {
   const int qwg = kWaves * (32 / D.G);
   const int wpt = (kHotTile + qwg - 1) / qwg;
-  const int64_t nitems = (int64_t)D.S * D.Hkv * h.ntiles * wpt;
-  if (nitems >= (1ll << 31) - 8) return hipErrorInvalidValue;
-  const int64_t grid = (nitems + 7) / 8 * 8;
+  if ((int64_t)D.S * D.Hkv * h.ntiles * wpt >= (1ll << 31)) return hipErrorInvalidValue;
+  // persistent: one workgroup per CU (the LDS footprint allows one)
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int grid = max(ncu, 8);
   LaunchScope scope("hot_mfma", st);
 #define MSA_HOT_CASE(DH_, G_) \
   if (D.d == DH_ && D.G == G_) { launch_hot_t<DH_, G_>(D, q, k, v, h, part_lse, part_o, wpt, grid, st); return hipGetLastError(); }

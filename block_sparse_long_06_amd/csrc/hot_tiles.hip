@@ -116,6 +116,27 @@ __global__ void __launch_bounds__(256) hot_select(Dims D, const int32_t* __restr
   }
 }
 
+// One workgroup lists, in (s, g, tile) order, the tiles that have shared blocks.
+__global__ void __launch_bounds__(1024) hot_compact(const int32_t* __restrict__ hot, int64_t ntot,
+                                                    int32_t* __restrict__ tiles, int* __restrict__ count) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int run = 0;
+  for (int64_t base = 0; base < ntot; base += 1024) {
+    const int64_t i = base + threadIdx.x;
+    const bool f = i < ntot && hot[i * kHotStride] > 0;
+    const uint64_t m = __ballot(f);
+    if (lane == 0) wsum[wave] = __popcll(m);
+    __syncthreads();
+    int before = run;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (f) tiles[before + lanes_below(m)] = (int32_t)i;
+    for (int w = 0; w < 16; ++w) run += wsum[w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *count = run;
+}
+
 // ------------------------------------------------------------------ cold CSR
 // Positions [F0, total) of the flat entry array, F = csr_offsets flattened over
 // (s, g, b) with nb + 1 values per (s, g); F0 = F[0], total = F[last].
@@ -239,6 +260,8 @@ HotSplit hot_split_layout(const Dims& D, void* base, size_t* total) {
   h.ntiles = hot_num_tiles(D);
   h.nchunk = nchunk;
   h.hot = static_cast<int32_t*>(take((size_t)D.S * D.Hkv * h.ntiles * kHotStride * sizeof(int32_t)));
+  h.tiles = static_cast<int32_t*>(take((size_t)D.S * D.Hkv * h.ntiles * sizeof(int32_t)));
+  h.ntile = static_cast<int*>(take(sizeof(int)));
   h.hotmask = static_cast<uint64_t*>(take(rows * sizeof(uint64_t)));
   h.selbits = static_cast<uint32_t*>(take(rows * sizeof(uint32_t)));
   h.cold_off = static_cast<int32_t*>(take(nflat * sizeof(int32_t)));
@@ -261,6 +284,13 @@ hipError_t launch_hot_split(const Dims& D, const int32_t* sel, const int32_t* of
                        h.hot, h.hotmask, h.selbits, h.ntiles);
   }
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    LaunchScope s("hot_compact", st);
+    hipLaunchKernelGGL(hot_compact, dim3(1), dim3(1024), 0, st, h.hot, (int64_t)D.S * D.Hkv * h.ntiles, h.tiles,
+                       h.ntile);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     LaunchScope s("cold_count", st);

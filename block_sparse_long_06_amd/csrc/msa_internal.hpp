@@ -61,6 +61,8 @@ struct HotSplit {
   int ntiles;
   int64_t nchunk;
   int32_t* hot;         // [S*Hkv, ntiles, kHotStride]
+  int32_t* tiles;       // (s*Hkv + g)*ntiles + tile of every tile with shared blocks, in order
+  int* ntile;           // their number
   uint64_t* hotmask;    // [S, T, Hkv]
   uint32_t* selbits;    // [S, T, Hkv]
   int32_t* cold_off;    // [S, Hkv, nb + 1]

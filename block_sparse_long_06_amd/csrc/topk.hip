@@ -32,6 +32,11 @@ __device__ __forceinline__ uint32_t ord_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of ord_key (ord_key(ord_inv(o)) == o for every o that ord_key produces).
+__device__ __forceinline__ float ord_inv(uint32_t o) {
+  return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
@@ -42,6 +47,13 @@ struct LdsSrc {
   const int32_t* id;
   int n;
   __device__ uint32_t key(int c) const { return ord[c]; }
+  __device__ int32_t idx(int c) const { return id[c]; }
+};
+struct LdsFloatSrc {
+  const float* val;
+  const int32_t* id;
+  int n;
+  __device__ uint32_t key(int c) const { return ord_key(val[c]); }
   __device__ int32_t idx(int c) const { return id[c]; }
 };
 struct RowSrc {
@@ -142,86 +154,94 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
   }
   const float* sc = scores + row * (int64_t)D.nb;
   if (n <= 64 * kRegPerLane) {
-    // Fast path: the row lives in registers (element i*64 + lane in slot i).
-    uint32_t o[kRegPerLane];
-    uint32_t lm = 0;
+    // Fast path: the row lives in registers (element i*64 + lane in slot i), compared
+    // as IEEE floats (the same order as ord_key, -0 == +0 included); only the lane
+    // maxima and the candidates are mapped to ord_key for the bitwise searches.
+    // Elements at n and beyond are -inf.
+    float* const s_f = reinterpret_cast<float*>(s_ord_w);  // row staging: the whole candidate buffer
+    const int ni = (n + 63) >> 6;                           // 64-element segments holding the row
+    float o[kRegPerLane];
     if (VEC) {
       static_assert(2 * kCap >= 64 * kRegPerLane, "row staging fits the candidate buffer");
 #pragma unroll
       for (int i = 0; i < kRegPerLane / 4; ++i) {
         const int c = i * 256 + 4 * lane;
-        const float4 x = c < n ? *reinterpret_cast<const float4*>(sc + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-        uint4 u;
-        u.x = c < n ? ord_key(x.x) : 0u;
-        u.y = c + 1 < n ? ord_key(x.y) : 0u;
-        u.z = c + 2 < n ? ord_key(x.z) : 0u;
-        u.w = c + 3 < n ? ord_key(x.w) : 0u;
-        *reinterpret_cast<uint4*>(&s_ord_w[c]) = u;
+        if (c < n) *reinterpret_cast<float4*>(&s_f[c]) = *reinterpret_cast<const float4*>(sc + c);
       }
       wave_lds_sync();
+      if (n + lane < ni * 64) s_f[n + lane] = -INFINITY;  // tail of the last segment
+      wave_lds_sync();
 #pragma unroll
-      for (int i = 0; i < kRegPerLane; ++i) {
-        o[i] = s_ord_w[i * 64 + lane];
-        lm = o[i] > lm ? o[i] : lm;
-      }
+      for (int i = 0; i < kRegPerLane; ++i) o[i] = i < ni ? s_f[i * 64 + lane] : -INFINITY;
       wave_lds_sync();  // the staging area takes the candidates next
     } else {
 #pragma unroll
       for (int i = 0; i < kRegPerLane; ++i) {
         const int c = i * 64 + lane;
-        o[i] = c < n ? ord_key(sc[c]) : 0u;
-        lm = o[i] > lm ? o[i] : lm;
+        o[i] = i < ni && c < n ? sc[c] : -INFINITY;
       }
     }
+    float lmf = o[0];
+#pragma unroll
+    for (int i = 1; i < kRegPerLane; ++i) lmf = fmaxf(lmf, o[i]);
+    const uint32_t lm = ord_key(lmf);
     uint32_t t1 = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = t1 | (1u << bit);
       if (__popcll(__ballot(lm >= cand)) >= need) t1 = cand;
     }
-    // candidates (ord >= t1) compacted in ascending id order
-    int C = 0;
+    const float t1f = ord_inv(t1);
+    if (t1f > -INFINITY) {  // otherwise -inf scores reach the threshold: generic path below
+      // candidates (value >= t1) compacted in ascending id order; -inf padding never passes
+      int C = 0;
 #pragma unroll
-    for (int i = 0; i < kRegPerLane; ++i) {
-      const bool f = i * 64 + lane < n && o[i] >= t1;
-      const uint64_t m = __ballot(f);
-      const int p = C + lanes_below(m);
-      if (f && p < kCap) {
-        s_ord_w[p] = o[i];
-        s_id_w[p] = i * 64 + lane;
+      for (int i = 0; i < kRegPerLane; ++i) {
+        if (i < ni) {
+          const bool f = o[i] >= t1f;
+          const uint64_t m = __ballot(f);
+          if (m != 0ull) {
+            const int p = C + lanes_below(m);
+            if (f && p < kCap) {
+              s_f[p] = o[i];
+              s_id_w[p] = i * 64 + lane;
+            }
+            C += __popcll(m);
+          }
+        }
       }
-      C += __popcll(m);
-    }
-    if (C <= 64) {
-      // one candidate per lane: each radix step is one compare and one ballot
-      const bool have = lane < C;
-      const uint32_t co = have ? s_ord_w[lane] : 0u;
-      const int32_t cid = have ? s_id_w[lane] : 0;
-      uint32_t tau = 0;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
-        if (__popcll(__ballot(have && co >= cand)) >= need) tau = cand;
+      if (C <= 64) {
+        // one candidate per lane: each radix step is one compare and one ballot
+        const bool have = lane < C;
+        const uint32_t co = have ? ord_key(s_f[lane]) : 0u;
+        const int32_t cid = have ? s_id_w[lane] : 0;
+        uint32_t tau = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = tau | (1u << bit);
+          if (__popcll(__ballot(have && co >= cand)) >= need) tau = cand;
+        }
+        const int c_gt = __popcll(__ballot(have && co > tau));
+        const uint64_t eqm = __ballot(have && co == tau);
+        const int need_eq = need - c_gt;
+        // ties at tau: the lowest ids win; candidates are in ascending id order, so the
+        // first need_eq set bits of eqm are taken
+        uint64_t take_eq = eqm;
+        for (int drop = __popcll(eqm) - need_eq; drop > 0; --drop) take_eq &= ~(1ull << (63 - __builtin_clzll(take_eq)));
+        const bool f = have && (co > tau || ((take_eq >> lane) & 1ull));
+        const uint64_t m = __ballot(f);
+        const int at = lanes_below(m);
+        if (f && at < need) out[at] = cid;
+        if (lane == 0) out[need] = bt;
+        return;
       }
-      const int c_gt = __popcll(__ballot(have && co > tau));
-      const uint64_t eqm = __ballot(have && co == tau);
-      const int need_eq = need - c_gt;
-      // ties at tau: the lowest ids win; candidates are in ascending id order, so the
-      // first need_eq set bits of eqm are taken
-      uint64_t take_eq = eqm;
-      for (int drop = __popcll(eqm) - need_eq; drop > 0; --drop) take_eq &= ~(1ull << (63 - __builtin_clzll(take_eq)));
-      const bool f = have && (co > tau || ((take_eq >> lane) & 1ull));
-      const uint64_t m = __ballot(f);
-      const int at = lanes_below(m);
-      if (f && at < need) out[at] = cid;
-      if (lane == 0) out[need] = bt;
-      return;
+      if (C <= kCap) {
+        LdsFloatSrc src{s_f, s_id_w, C};
+        select_and_write(src, lane, need, out);
+        if (lane == 0) out[need] = bt;
+        return;
+      }
     }
-    if (C <= kCap) {
-      LdsSrc src{s_ord_w, s_id_w, C};
-      select_and_write(src, lane, need, out);
-    } else {
-      RowSrc src{sc, n};
-      select_and_write(src, lane, need, out);
-    }
+    RowSrc src{sc, n};
+    select_and_write(src, lane, need, out);
     if (lane == 0) out[need] = bt;
     return;
   }
