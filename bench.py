@@ -281,6 +281,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--prefill", default="C2", choices=["C1", "C2", "C4"],
                     help="prefill workload timed (default C2: the 131072-token headline configuration)")
+    ap.add_argument("--no-fp8-decode", action="store_true",
+                    help="skip the extra decode timing with the index keys stored as FP8 E4M3 (serving variant)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy 3 times (the known-size reference "
                          "for scaling hardware byte counters)")
@@ -312,11 +314,16 @@ def main():
     pprob = wp.problem()
     pb = msa.alloc_prefill(pprob)
     xd = db = dprob = None
+    kidx8 = db8 = dprob8 = None
     if not args.no_decode:
         ds = wd.specs()
         xd = {n: synth.device_tensor(ds[n]) for n in ds}
         dprob = wd.problem()
         db = msa.alloc_decode(dprob)
+        if not args.no_fp8_decode:
+            kidx8 = synth.device_tensor(W.C3_FP8.specs()["k_idx"])   # the same values, stored as E4M3
+            dprob8 = W.C3_FP8.problem()
+            db8 = msa.alloc_decode(dprob8)
     torch.cuda.synchronize()
     print("[bench] inputs resident: prefill %s, decode %s" % (wp.name, wd.name), file=sys.stderr, flush=True)
 
@@ -420,6 +427,41 @@ def main():
         dec = dict(workload=wd.description, us_per_step=decode_ms * 1e3, us_per_token_amortised=decode_ms * 1e3 / wd.S,
                    sequences=wd.S, kv_len=wd.N, stages=dstages)
 
+    dec8 = None
+    if db8 is not None:
+        # serving variant, outside the timed step: the same decode with 1-byte index keys
+        def decode8():
+            msa.run_decode(dprob8, xd["q"], xd["k"], xd["v"], xd["q_idx"], kidx8, db8)
+        decode8()
+        torch.cuda.synchronize()
+        msa.profiler_read(None, reset=True)
+        msa.profiler_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            decode8()
+        e1.record()
+        torch.cuda.synchronize()
+        msa.profiler_enable(False)
+        ms8 = e0.elapsed_time(e1) / args.steps
+        k8 = {}
+        for kn in ("idx_scores_stream", "block_topk_t1", "decode_items", "decode_ogq_mfma", "decode_merge"):
+            tms, nl = msa.profiler_read(kn, reset=False)
+            if nl:
+                k8[kn] = dict(ms=tms / nl)
+        msa.profiler_read(None, reset=True)
+        kbytes8 = wd.S * wd.Hkv * wd.N * wd.dI * 1.0 + 4.0 * wd.S * wd.Hkv * wd.nb
+        if "idx_scores_stream" in k8:
+            s8 = k8["idx_scores_stream"]["ms"] / 1e3
+            k8["idx_scores_stream"].update(roofline(2.0 * wd.dI * wd.S * wd.Hkv * wd.N, kbytes8, s8))
+        # share of the bf16-key selections (valid slots) that the E4M3-key run also chose
+        a, b = db.sel, db8.sel
+        hit = ((a.unsqueeze(-1) == b.unsqueeze(-2)).any(-1) & (a >= 0)).sum().item()
+        overlap = hit / max(1, (a >= 0).sum().item())
+        dec8 = dict(workload=W.C3_FP8.description, us_per_step=ms8 * 1e3, us_per_token_amortised=ms8 * 1e3 / wd.S,
+                    stages=k8, selection_overlap_with_bf16_keys=overlap)
+        print("[bench] decode with E4M3 index keys: %.3f ms per step" % ms8, file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline ...", file=sys.stderr, flush=True)
@@ -434,7 +476,7 @@ def main():
         "config": {"workload": wp.description, "batch": wp.S, "seq_len": wp.T, "num_heads": wp.H,
                    "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
         "prefill_ms": prefill_ms, "wall_s_timed": wall,
-        "decode": dec, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
+        "decode": dec, "decode_e4m3_index_keys": dec8, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
         "selection_structure": selection_structure(wp, pb.sel, pb.csr_offsets),
         "attention_pairs": split["pairs"],
     }

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARGUMENT, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_DEVICE = range(5)
-MSA_F32, MSA_BF16 = 0, 1
+MSA_F32, MSA_BF16, MSA_FP8_E4M3 = 0, 1, 2
 MSA_CALL_INVERT, MSA_CALL_PREFILL, MSA_CALL_DECODE = 2, 3, 4
 
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_invert_selection", "msa_sparse_attn_prefill",
@@ -39,7 +39,7 @@ class Problem(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("index_key_dtype", ctypes.c_int32)]
 
     @property
     def nb(self) -> int:
@@ -54,9 +54,9 @@ class Problem(ctypes.Structure):
 
 
 def problem(batch, num_q, kv_len, num_heads, num_kv_heads, head_dim, index_dim, topk,
-            dtype=MSA_BF16, block_size=128, softmax_scale=0.0) -> Problem:
+            dtype=MSA_BF16, block_size=128, softmax_scale=0.0, index_key_dtype=0) -> Problem:
     return Problem(batch, num_q, kv_len, num_heads, num_kv_heads, head_dim, index_dim, block_size,
-                   topk, dtype, softmax_scale)
+                   topk, dtype, softmax_scale, index_key_dtype)
 
 
 _lib = None

@@ -7,16 +7,18 @@
 //
 //   scores[s,g,t,b] = max_{bB <= j <= min((b+1)B-1, p_t)} q_idx[s,g,t,:] . k_idx[s,g,j,:]
 //
-// Two kernels:
-//  * idx_scores_rows: one wave per (row, block), lane per key, fp32 FMAs.  Used
-//    for float32 inputs and for short query counts (the decode shape, where the
-//    stage is a stream over the index keys).
+// Kernels:
+//  * idx_scores_rows: one wave per (row, block), lane per key, fp32 FMAs (float32
+//    inputs and mid-sized query counts).
+//  * idx_scores_stream: the decode shape (a few queries), a stream over the keys.
 //  * idx_scores_mfma (index_scores_mfma.hip): bf16 prefill on matrix cores.
+// Index keys are bf16 / float32 like the queries, or OCP E4M3 bytes (bf16 problems),
+// decoded exactly with the hardware converter before the products.
 #include "msa_internal.hpp"
 
 namespace msa {
 
-hipError_t launch_index_scores_mfma(const Dims& D, const uint16_t* q_idx, const uint16_t* k_idx,
+hipError_t launch_index_scores_mfma(const Dims& D, const uint16_t* q_idx, const void* k_idx,
                                     float* scores, hipStream_t st);
 
 namespace {
@@ -34,6 +36,21 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* o) {
   o[6] = __builtin_bit_cast(float, u.w << 16);
   o[7] = __builtin_bit_cast(float, u.w & 0xFFFF0000u);
 }
+// 4 OCP E4M3 bytes of a word -> 4 floats (exact), one hardware conversion per byte.
+// (The single-byte form: the packed two-value builtin had its second result replaced
+// by its first by this compiler.)
+__device__ __forceinline__ void e4m3x4(uint32_t w, float* o) {
+  o[0] = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+  o[1] = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+  o[2] = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+  o[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+}
+// 8 OCP E4M3 bytes -> 8 floats (exact).
+__device__ __forceinline__ void load8(const uint8_t* p, float* o) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  e4m3x4(u.x, o);
+  e4m3x4(u.y, o + 4);
+}
 __device__ __forceinline__ void load8(const float* p, float* o) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -42,9 +59,9 @@ __device__ __forceinline__ void load8(const float* p, float* o) {
 }
 
 // grid: (rows = S*Hkv*T, ceil(nb / kWaves)); wave w of block (r, y) scores block y*kWaves + w.
-template <typename T>
+template <typename T, typename TK>
 __global__ void __launch_bounds__(kWaves * 64) idx_scores_rows(Dims D, const T* __restrict__ q_idx,
-                                                               const T* __restrict__ k_idx,
+                                                               const TK* __restrict__ k_idx,
                                                                float* __restrict__ scores) {
   const int lane = threadIdx.x & 63;
   const int64_t row = blockIdx.x;
@@ -55,10 +72,10 @@ __global__ void __launch_bounds__(kWaves * 64) idx_scores_rows(Dims D, const T* 
   const int bt = p / D.B;
   if (b > bt) return;
   const T* q = q_idx + row * D.dI;
-  const T* kbase = k_idx + sg * (int64_t)D.N * D.dI;
+  const TK* kbase = k_idx + sg * (int64_t)D.N * D.dI;
   float best = -INFINITY;
   for (int j = b * D.B + lane; j < (b + 1) * D.B && j <= p; j += 64) {
-    const T* kk = kbase + (int64_t)j * D.dI;
+    const TK* kk = kbase + (int64_t)j * D.dI;
     float acc = 0.0f;
     for (int c = 0; c < D.dI; c += 8) {
       float qv[8], kv[8];
@@ -76,19 +93,22 @@ __global__ void __launch_bounds__(kWaves * 64) idx_scores_rows(Dims D, const T* 
 // Decode shape (T <= kStreamT queries per (s, g)): a stream over the index keys.  One
 // workgroup scores kStreamBlocks consecutive blocks of one (s, g) for all its queries.
 // Thread = (key slot, 16-byte column of the key row): every load instruction of the
-// workgroup covers one contiguous 4 KB run of keys.  The DI/8 lanes sharing a key add
+// workgroup covers one contiguous 4 KB run of keys.  The lanes sharing a key add
 // their partial dots with xor shuffles; the block max is a wave reduction over key
 // slots plus an LDS step across the 4 waves.
 constexpr int kStreamT = 8;
 constexpr int kStreamBlocks = 8;
 
-template <int DI, int TQ>
+// TK = uint16_t (bf16 keys: 8 dims per 16-byte lane load) or uint8_t (E4M3 keys: 16
+// dims per 16-byte lane load, decoded with the hardware converter).
+template <int DI, int TQ, typename TK>
 __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t* __restrict__ q_idx,
-                                                         const uint16_t* __restrict__ k_idx,
+                                                         const TK* __restrict__ k_idx,
                                                          float* __restrict__ scores) {
-  constexpr int CPR = DI / 8;            // lanes per key row
-  constexpr int KPP = 256 / CPR;         // keys per pass of the workgroup
-  constexpr int PASSES = 128 / KPP;      // passes per block
+  constexpr int DPL = 16 / (int)sizeof(TK);  // dims per lane and key
+  constexpr int CPR = DI / DPL;              // lanes per key row
+  constexpr int KPP = 256 / CPR;             // keys per pass of the workgroup
+  constexpr int PASSES = 128 / KPP;          // passes per block
   __shared__ float red[4][TQ];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = threadIdx.x % CPR;
@@ -96,15 +116,16 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
   const int64_t sg = blockIdx.y;
   const int b0 = blockIdx.x * kStreamBlocks;
   const int T = D.T;
-  float qv[TQ][8];
+  float qv[TQ][DPL];
   int pq[TQ];
 #pragma unroll
   for (int tq = 0; tq < TQ; ++tq) {
     const int t = tq < T ? tq : T - 1;
     pq[tq] = tq < T ? D.pos0 + tq : -1;
-    load8(q_idx + (sg * T + t) * DI + col * 8, qv[tq]);
+#pragma unroll
+    for (int x = 0; x < DPL; x += 8) load8(q_idx + (sg * T + t) * DI + col * DPL + x, &qv[tq][x]);
   }
-  const uint16_t* kbase = k_idx + sg * (int64_t)D.N * DI + col * 8;
+  const TK* kbase = k_idx + sg * (int64_t)D.N * DI + col * DPL;
   const int bend = min(b0 + kStreamBlocks, D.nb);
   for (int b = b0; b < bend; ++b) {
     uint4 kr[PASSES];
@@ -120,17 +141,22 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
     for (int u = 0; u < PASSES; ++u) {
       const int j = b * 128 + u * KPP + kslot;
       const uint32_t w4[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
-      float kv[8];
+      float kv[DPL];
+      if constexpr (sizeof(TK) == 2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kv[2 * i] = __builtin_bit_cast(float, w4[i] << 16);
-        kv[2 * i + 1] = __builtin_bit_cast(float, w4[i] & 0xFFFF0000u);
+        for (int i = 0; i < 4; ++i) {
+          kv[2 * i] = __builtin_bit_cast(float, w4[i] << 16);
+          kv[2 * i + 1] = __builtin_bit_cast(float, w4[i] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e4m3x4(w4[i], &kv[4 * i]);
       }
 #pragma unroll
       for (int tq = 0; tq < TQ; ++tq) {
         float acc = 0.0f;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc = fmaf(qv[tq][x], kv[x], acc);
+        for (int x = 0; x < DPL; ++x) acc = fmaf(qv[tq][x], kv[x], acc);
 #pragma unroll
         for (int o = 1; o < CPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
         if (j <= pq[tq]) m[tq] = fmaxf(m[tq], acc);
@@ -153,13 +179,20 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
   }
 }
 
-template <int DI>
-void launch_stream_di(const Dims& D, const uint16_t* q, const uint16_t* k, float* sc, hipStream_t st) {
+template <int DI, typename TK>
+void launch_stream_di(const Dims& D, const uint16_t* q, const TK* k, float* sc, hipStream_t st) {
   dim3 grid((unsigned)((D.nb + kStreamBlocks - 1) / kStreamBlocks), (unsigned)(D.S * D.Hkv));
   if (D.T == 1)
-    hipLaunchKernelGGL((idx_scores_stream<DI, 1>), grid, dim3(256), 0, st, D, q, k, sc);
+    hipLaunchKernelGGL((idx_scores_stream<DI, 1, TK>), grid, dim3(256), 0, st, D, q, k, sc);
   else
-    hipLaunchKernelGGL((idx_scores_stream<DI, kStreamT>), grid, dim3(256), 0, st, D, q, k, sc);
+    hipLaunchKernelGGL((idx_scores_stream<DI, kStreamT, TK>), grid, dim3(256), 0, st, D, q, k, sc);
+}
+
+template <typename TK>
+void launch_stream(const Dims& D, const uint16_t* q, const TK* k, float* sc, hipStream_t st) {
+  if (D.dI == 32) launch_stream_di<32>(D, q, k, sc, st);
+  else if (D.dI == 64) launch_stream_di<64>(D, q, k, sc, st);
+  else launch_stream_di<128>(D, q, k, sc, st);
 }
 
 }  // namespace
@@ -167,25 +200,26 @@ void launch_stream_di(const Dims& D, const uint16_t* q, const uint16_t* k, float
 hipError_t launch_index_scores(const Dims& D, const void* q_idx, const void* k_idx, float* scores,
                                hipStream_t st) {
   const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
+  const bool f8 = D.kdtype == MSA_FP8_E4M3;
   if (D.dtype == MSA_BF16 && D.T >= 256)
-    return launch_index_scores_mfma(D, static_cast<const uint16_t*>(q_idx),
-                                    static_cast<const uint16_t*>(k_idx), scores, st);
+    return launch_index_scores_mfma(D, static_cast<const uint16_t*>(q_idx), k_idx, scores, st);
   if (D.dtype == MSA_BF16 && D.T <= kStreamT) {
     const uint16_t* q = static_cast<const uint16_t*>(q_idx);
-    const uint16_t* k = static_cast<const uint16_t*>(k_idx);
     LaunchScope scope("idx_scores_stream", st);
-    if (D.dI == 32) launch_stream_di<32>(D, q, k, scores, st);
-    else if (D.dI == 64) launch_stream_di<64>(D, q, k, scores, st);
-    else launch_stream_di<128>(D, q, k, scores, st);
+    if (f8) launch_stream(D, q, static_cast<const uint8_t*>(k_idx), scores, st);
+    else launch_stream(D, q, static_cast<const uint16_t*>(k_idx), scores, st);
     return hipGetLastError();
   }
   dim3 grid((unsigned)rows, (unsigned)((D.nb + kWaves - 1) / kWaves));
   LaunchScope scope("idx_scores_rows", st);
-  if (D.dtype == MSA_BF16)
-    hipLaunchKernelGGL(idx_scores_rows<uint16_t>, grid, dim3(kWaves * 64), 0, st, D,
+  if (D.dtype == MSA_BF16 && f8)
+    hipLaunchKernelGGL((idx_scores_rows<uint16_t, uint8_t>), grid, dim3(kWaves * 64), 0, st, D,
+                       static_cast<const uint16_t*>(q_idx), static_cast<const uint8_t*>(k_idx), scores);
+  else if (D.dtype == MSA_BF16)
+    hipLaunchKernelGGL((idx_scores_rows<uint16_t, uint16_t>), grid, dim3(kWaves * 64), 0, st, D,
                        static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), scores);
   else
-    hipLaunchKernelGGL(idx_scores_rows<float>, grid, dim3(kWaves * 64), 0, st, D,
+    hipLaunchKernelGGL((idx_scores_rows<float, float>), grid, dim3(kWaves * 64), 0, st, D,
                        static_cast<const float*>(q_idx), static_cast<const float*>(k_idx), scores);
   return hipGetLastError();
 }

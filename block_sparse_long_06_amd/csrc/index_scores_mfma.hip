@@ -46,10 +46,22 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   return __builtin_fmaxf(m, a[15]);
 }
 
+// Bytes B and B+1 of a word of OCP E4M3 codes -> two bf16 in one word.  Exact: E4M3
+// values have 3 mantissa bits and exponents inside the bf16 range, so each float's low
+// 16 bits are zero.  One hardware conversion per byte (the packed two-value builtin had
+// its second result replaced by its first by this compiler).
+template <int B>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const float f0 = __builtin_amdgcn_cvt_f32_fp8((int)w, B);
+  const float f1 = __builtin_amdgcn_cvt_f32_fp8((int)w, B + 1);
+  return (__builtin_bit_cast(uint32_t, f0) >> 16) | (__builtin_bit_cast(uint32_t, f1) & 0xFFFF0000u);
+}
+
 // dI = 128 doubles the resident B operands, which leaves room for one wave per SIMD only.
-template <int DI>
+// TK: uint16_t (bf16 keys) or uint8_t (E4M3 keys, widened to bf16 when staged).
+template <int DI, typename TK>
 __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D, const uint16_t* __restrict__ q_idx,
-                                                          const uint16_t* __restrict__ k_idx,
+                                                          const TK* __restrict__ k_idx,
                                                           float* __restrict__ scores) {
   constexpr int KS = DI / 16;
   constexpr int ROWB = DI * 2 + 16;
@@ -84,16 +96,17 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
   const int t_w0 = min(t_first + wave * kQW, D.T - 1);
   const int bmask = (D.pos0 + t_w0) / kBlk;
 
-  const uint16_t* kbase = k_idx + sg * (int64_t)D.N * DI;
-  uint4 stage[PER_T];
+  const TK* kbase = k_idx + sg * (int64_t)D.N * DI;
+  // one piece = 8 key dims: 16 bytes of bf16 or 8 bytes of E4M3
+  typedef typename std::conditional<sizeof(TK) == 2, uint4, uint2>::type Piece;
+  Piece stage[PER_T];
   auto gload = [&](int b) {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int c = threadIdx.x + 256 * u;
       const int row = c / CPR, col = c % CPR;
       const int j = b * kBlk + row;
-      stage[u] = j < D.N ? *reinterpret_cast<const uint4*>(kbase + (int64_t)j * DI + col * 8)
-                         : make_uint4(0u, 0u, 0u, 0u);
+      stage[u] = j < D.N ? *reinterpret_cast<const Piece*>(kbase + (int64_t)j * DI + col * 8) : Piece{};
     }
   };
   auto lstore = [&](int buf) {
@@ -101,7 +114,14 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
     for (int u = 0; u < PER_T; ++u) {
       const int c = threadIdx.x + 256 * u;
       const int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<uint4*>(&lds[buf][row * ROWB + col * 16]) = stage[u];
+      uint4 w;
+      if constexpr (sizeof(TK) == 2) {
+        w = stage[u];
+      } else {
+        w = make_uint4(e4m3x2_to_bf16x2<0>(stage[u].x), e4m3x2_to_bf16x2<2>(stage[u].x),
+                       e4m3x2_to_bf16x2<0>(stage[u].y), e4m3x2_to_bf16x2<2>(stage[u].y));
+      }
+      *reinterpret_cast<uint4*>(&lds[buf][row * ROWB + col * 16]) = w;
     }
   };
 
@@ -184,20 +204,26 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
   }
 }
 
+template <typename TK>
+void launch_mfma_t(const Dims& D, dim3 grid, const uint16_t* q_idx, const TK* k_idx, float* scores, hipStream_t st) {
+  switch (D.dI) {
+    case 32: hipLaunchKernelGGL((idx_scores_mfma<32, TK>), grid, dim3(256), 0, st, D, q_idx, k_idx, scores); break;
+    case 64: hipLaunchKernelGGL((idx_scores_mfma<64, TK>), grid, dim3(256), 0, st, D, q_idx, k_idx, scores); break;
+    default: hipLaunchKernelGGL((idx_scores_mfma<128, TK>), grid, dim3(256), 0, st, D, q_idx, k_idx, scores); break;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_index_scores_mfma(const Dims& D, const uint16_t* q_idx, const uint16_t* k_idx,
+hipError_t launch_index_scores_mfma(const Dims& D, const uint16_t* q_idx, const void* k_idx,
                                     float* scores, hipStream_t st) {
   const int nq = (D.T + kQB - 1) / kQB;
   const int bmax = (D.N - 1) / kBlk;
   const int nchunk = bmax / kChunk + 1;
   dim3 grid((unsigned)nq, (unsigned)nchunk, (unsigned)(D.S * D.Hkv));
   LaunchScope scope("idx_scores_mfma", st);
-  switch (D.dI) {
-    case 32: hipLaunchKernelGGL(idx_scores_mfma<32>, grid, dim3(256), 0, st, D, q_idx, k_idx, scores); break;
-    case 64: hipLaunchKernelGGL(idx_scores_mfma<64>, grid, dim3(256), 0, st, D, q_idx, k_idx, scores); break;
-    default: hipLaunchKernelGGL(idx_scores_mfma<128>, grid, dim3(256), 0, st, D, q_idx, k_idx, scores); break;
-  }
+  if (D.kdtype == MSA_FP8_E4M3) launch_mfma_t(D, grid, q_idx, static_cast<const uint8_t*>(k_idx), scores, st);
+  else launch_mfma_t(D, grid, q_idx, static_cast<const uint16_t*>(k_idx), scores, st);
   return hipGetLastError();
 }
 

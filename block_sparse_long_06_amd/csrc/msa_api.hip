@@ -56,6 +56,11 @@ msa_status check_problem(const msa_problem* p, msa::Dims* D, bool need_index, bo
   if (p->topk < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "topk must be >= 1 (got %d)", p->topk);
   if (p->dtype != MSA_F32 && p->dtype != MSA_BF16)
     return fail(MSA_ERR_INVALID_ARGUMENT, "dtype must be MSA_F32 or MSA_BF16 (got %d)", p->dtype);
+  if (p->index_key_dtype != 0 && p->index_key_dtype != p->dtype && p->index_key_dtype != MSA_FP8_E4M3)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "index_key_dtype must be 0, dtype or MSA_FP8_E4M3 (got %d)",
+                p->index_key_dtype);
+  if (p->index_key_dtype == MSA_FP8_E4M3 && p->dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "MSA_FP8_E4M3 index keys need dtype MSA_BF16");
   if (!(p->softmax_scale >= 0.0f) || isinf(p->softmax_scale))
     return fail(MSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
   if (p->block_size != 128)
@@ -94,6 +99,7 @@ msa_status check_problem(const msa_problem* p, msa::Dims* D, bool need_index, bo
   D->nb = (int)nb;
   D->pos0 = p->kv_len - p->num_q;
   D->dtype = p->dtype;
+  D->kdtype = p->index_key_dtype == MSA_FP8_E4M3 ? MSA_FP8_E4M3 : p->dtype;
   D->scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / sqrtf((float)p->head_dim);
   return MSA_OK;
 }

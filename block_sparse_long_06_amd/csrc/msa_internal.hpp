@@ -16,6 +16,7 @@ struct Dims {
   int pos0;      // N - T: absolute position of query row 0
   int dtype;     // msa_dtype
   float scale;   // main-branch logit scale (resolved, never 0)
+  int kdtype;    // msa_dtype of k_idx (resolved: dtype or MSA_FP8_E4M3)
 };
 
 // ----------------------------------------------------------------- profiler

@@ -58,7 +58,11 @@ typedef enum {
   MSA_ERR_DEVICE = 4              /* a HIP runtime call or kernel launch failed */
 } msa_status;
 
-typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+typedef enum {
+  MSA_F32 = 0,
+  MSA_BF16 = 1,
+  MSA_FP8_E4M3 = 2  /* OCP FP8 E4M3 (bias 7, max 448, NaN 0x7F/0xFF): index keys only */
+} msa_dtype;
 
 typedef struct {
   int32_t batch;         /* S >= 1 */
@@ -70,8 +74,12 @@ typedef struct {
   int32_t index_dim;     /* dI: 32, 64 or 128 */
   int32_t block_size;    /* B: 128 */
   int32_t topk;          /* k: 1..64 */
-  int32_t dtype;         /* msa_dtype of q, k, v, q_idx, k_idx, out */
+  int32_t dtype;         /* msa_dtype of q, k, v, q_idx, out (and k_idx, see below) */
   float softmax_scale;   /* main-branch logit scale; 0 selects 1/sqrt(d) */
+  int32_t index_key_dtype; /* element type of k_idx: 0 = dtype, or MSA_FP8_E4M3 (with
+                              dtype MSA_BF16): 1-byte index keys halve the bytes the
+                              decode-time index stream reads.  Any scale of the keys is
+                              the caller's to fold into q_idx (scores are bilinear). */
 } msa_problem;
 
 /* Which call a workspace size is asked for (msa_workspace_bytes). */
@@ -85,6 +93,9 @@ enum { MSA_CALL_INVERT = 2, MSA_CALL_PREFILL = 3, MSA_CALL_DECODE = 4 };
  *   Entries with b > b_t are NOT written (they are not eligible).
  *   Raw dot product: no scale and no activation (both are monotone and would not
  *   change the selection).
+ *   With index_key_dtype = MSA_FP8_E4M3, k_idx holds one E4M3 byte per element; each
+ *   key is decoded exactly (E4M3 values are bf16 values) and the products are formed
+ *   as for bf16 keys.
  */
 msa_status msa_index_scores(const msa_problem* prob, const void* q_idx, const void* k_idx,
                             float* scores, void* stream);

@@ -80,15 +80,37 @@ def _p(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+def e4m3_table() -> np.ndarray:
+    """The 256 values of the OCP FP8 E4M3 format as float64: sign bit, 4 exponent bits
+    (bias 7), 3 mantissa bits; exponent field 0 holds subnormals m * 2^-9; code
+    S.1111.111 is NaN (there is no infinity)."""
+    c = np.arange(256)
+    s = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    v = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = s * v
+    v[(e == 15) & (m == 7)] = np.nan
+    return v
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """uint8 E4M3 codes -> float64, exactly."""
+    return e4m3_table()[np.asarray(codes, dtype=np.uint8)]
+
+
 def decode(x) -> np.ndarray:
     """Stored input -> float64, exactly.  Accepts numpy float arrays, numpy uint16
-    arrays holding bf16 bit patterns, or (CPU) torch tensors of float32/bfloat16."""
+    arrays holding bf16 bit patterns, or (CPU) torch tensors of float32, bfloat16 or
+    float8_e4m3fn (decoded with e4m3_table)."""
     try:
         import torch  # noqa: F401  (torch is optional for pure-numpy callers)
         if isinstance(x, torch.Tensor):
             x = x.detach().cpu()
             if x.dtype == torch.bfloat16:
                 x = x.view(torch.int16).numpy().view(np.uint16)
+            elif x.dtype == torch.float8_e4m3fn:
+                return decode_e4m3(x.view(torch.uint8).numpy())
             else:
                 x = x.numpy()
     except ImportError:

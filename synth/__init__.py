@@ -16,7 +16,8 @@ arithmetic.  Every element is a pure function of (seed, tensor id, flat index):
 The device generator (``synth_dev.hip`` -> ``libmsa_synth.so``) implements the
 same hash and reads the same table, so host and device agree bit for bit.
 Structure (index keys with sink / needle / recent-band boosts) is added in
-float32 and rounded once to the storage dtype (bf16 round-to-nearest-even).
+float32 and rounded once to the storage dtype (bf16 round-to-nearest-even; for
+1-byte index keys OCP E4M3, round-to-nearest-even, saturating at 448).
 
 Structured index inputs (the emergent head patterns: a diagonal band of recent
 context, a leftmost sink column and per-group stripes at other distances):
@@ -46,7 +47,7 @@ M2 = np.uint64(0x94D049BB133111EB)
 
 TID_Q, TID_K, TID_V, TID_QI, TID_KI, TID_NEEDLE, TID_ROWS = 1, 2, 3, 4, 5, 6, 7
 KIND_IID, KIND_QIDX, KIND_KIDX = 0, 1, 2
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2   # FP8: OCP E4M3 (index keys only)
 
 
 def _mix64(z: np.ndarray) -> np.ndarray:
@@ -175,11 +176,40 @@ def values_at(spec: TensorSpec, flat: np.ndarray) -> np.ndarray:
     return v.astype(np.float32)
 
 
+def f32_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP FP8 E4M3 codes (uint8): round to nearest even, magnitudes beyond the
+    largest finite value (448) saturate to it.  Finite inputs only.  Storage encoding of
+    the generator (the device generator implements the same steps)."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    sign = ((u >> np.uint32(24)) & np.uint32(0x80)).astype(np.uint32)
+    a = np.abs(x)
+    au = a.view(np.uint32)
+    # normal range: 3 mantissa bits kept, round half to even on the 20 dropped bits
+    e = (au >> np.uint32(23)).astype(np.int64) - 127
+    mant = (au & np.uint32(0x7FFFFF)).astype(np.int64)
+    keep = mant >> 20
+    rem = mant & 0xFFFFF
+    up = (rem > 0x80000) | ((rem == 0x80000) & ((keep & 1) == 1))
+    keep = keep + up
+    e = np.where(keep == 8, e + 1, e)
+    keep = np.where(keep == 8, 0, keep)
+    normal = np.minimum(((e + 7) << 3) | keep, 0x7E)
+    # below the smallest normal (2^-6): multiples of 2^-9, rounded half to even
+    sub = np.rint(a.astype(np.float64) * 512.0).astype(np.int64)
+    code = np.where(a < np.float32(0.015625), sub, normal)
+    code = np.where(a >= np.float32(448.0), 0x7E, code)
+    return (code.astype(np.uint32) | sign).astype(np.uint8)
+
+
 def host_tensor(spec: TensorSpec) -> np.ndarray:
-    """The whole tensor on the host, in storage form (float32 array, or uint16 bf16 bits)."""
+    """The whole tensor on the host, in storage form (float32 array, uint16 bf16 bits,
+    or uint8 E4M3 codes)."""
     n = int(np.prod(spec.shape))
     v = values_at(spec, np.arange(n, dtype=np.int64)).reshape(spec.shape)
-    return v if spec.dtype == F32 else f32_to_bf16_bits(v)
+    if spec.dtype == F32:
+        return v
+    return f32_to_bf16_bits(v) if spec.dtype == BF16 else f32_to_e4m3(v)
 
 
 # ------------------------------------------------------------------ device side
@@ -212,14 +242,15 @@ def _load_dev():
 
 
 def device_tensor(spec: TensorSpec, device="cuda"):
-    """Generate the tensor directly in device memory (torch tensor of float32/bfloat16).
+    """Generate the tensor directly in device memory (torch tensor of float32, bfloat16 or
+    float8_e4m3fn).
 
     Bit-identical to host_tensor(spec).  Small side tables (the normal table, the
     band table, the boost mask) are copied up; the bulk never crosses PCIe."""
     import torch
     lib = _load_dev()
     S, A, L, D = spec.shape
-    tdt = torch.float32 if spec.dtype == F32 else torch.bfloat16
+    tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.float8_e4m3fn}[spec.dtype]
     out = torch.empty((S, A, L, D), dtype=tdt, device=device)
     table = torch.from_numpy(normal_table()).to(device)
     band = torch.from_numpy(np.ascontiguousarray(spec.band)).to(device) if spec.band is not None else None

@@ -23,9 +23,36 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
+// float32 -> OCP E4M3 code: round to nearest even, saturating at 448 (finite inputs).
+// The same steps as synth.f32_to_e4m3 on the host.
+__device__ __forceinline__ uint8_t f32_to_e4m3_rne(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    code = (uint32_t)(int)rintf(a * 512.0f);
+  } else {
+    const uint32_t au = __builtin_bit_cast(uint32_t, a);
+    int e = (int)(au >> 23) - 127;
+    const uint32_t mant = au & 0x7FFFFFu;
+    uint32_t keep = mant >> 20;
+    const uint32_t rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
+    if (keep == 8u) {
+      keep = 0u;
+      ++e;
+    }
+    code = min((uint32_t)(((e + 7) << 3) | (int)keep), 0x7Eu);
+  }
+  return (uint8_t)(code | sign);
+}
+
 struct FillArgs {
   void* dst;
-  int dtype;  // 0 f32, 1 bf16
+  int dtype;  // 0 f32, 1 bf16, 2 OCP E4M3
   int64_t S, A, L, D;
   uint64_t key;
   const float* table;
@@ -58,8 +85,10 @@ __global__ void __launch_bounds__(256) fill_kernel(FillArgs p, int64_t n) {
     }
     if (p.dtype == 0)
       static_cast<float*>(p.dst)[f] = v;
-    else
+    else if (p.dtype == 1)
       static_cast<uint16_t*>(p.dst)[f] = f32_to_bf16_rne(v);
+    else
+      static_cast<uint8_t*>(p.dst)[f] = f32_to_e4m3_rne(v);
   }
 }
 

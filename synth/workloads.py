@@ -15,6 +15,7 @@ any part of the attention method.
                              (sequence, group) with the C2 boost channel, no band
   C4  bf16 chunked prefill   S 1, T = 8192 queries at positions 1,040,384 .. 1,048,575,
                              N = 1,048,576, dims of C1, iid N(0,1)
+  (C3_FP8: C3 with its index keys stored as OCP FP8 E4M3, the serving variant.)
 
 Seeds are 0x4D534100 + workload index; tensor ids Q 1, K 2, V 3, q_I 4, k_I 5,
 needle draw 6, sampled rows 7.
@@ -25,7 +26,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import (BF16, F32, KIND_IID, KIND_KIDX, KIND_QIDX, TID_K, TID_KI, TID_Q, TID_QI, TID_ROWS, TID_V,
+from . import (BF16, F32, FP8, KIND_IID, KIND_KIDX, KIND_QIDX, TID_K, TID_KI, TID_Q, TID_QI, TID_ROWS, TID_V,
                TensorSpec, band_table, h16, needle_blocks)
 
 SEED_BASE = 0x4D534100
@@ -49,6 +50,7 @@ class Workload:
     structure: str = "iid"           # "iid" | "band_sink_needles" | "sink_needles"
     description: str = ""
     extra: dict = field(default_factory=dict)
+    kidx_dtype: int = None           # storage of the index keys (None: dtype; FP8 = E4M3)
 
     @property
     def seed(self) -> int:
@@ -62,10 +64,15 @@ class Workload:
     def G(self) -> int:
         return self.H // self.Hkv
 
+    @property
+    def kdtype(self) -> int:
+        return self.dtype if self.kidx_dtype is None else self.kidx_dtype
+
     def problem(self):
         import block_sparse_long_06_amd as msa
         return msa.problem(self.S, self.T, self.N, self.H, self.Hkv, self.d, self.dI, self.k,
-                           dtype=self.dtype)
+                           dtype=self.dtype,
+                           index_key_dtype=msa.MSA_FP8_E4M3 if self.kdtype == FP8 else 0)
 
     # ------------------------------------------------------------ tensor recipes
     def boost_mask(self) -> np.ndarray | None:
@@ -90,14 +97,15 @@ class Workload:
             "k": TensorSpec((self.S, self.Hkv, self.N, self.d), sd, TID_K, dt),
             "v": TensorSpec((self.S, self.Hkv, self.N, self.d), sd, TID_V, dt),
         }
+        kdt = self.kdtype
         if self.structure == "iid":
             out["q_idx"] = TensorSpec((self.S, self.Hkv, self.T, self.dI), sd, TID_QI, dt)
-            out["k_idx"] = TensorSpec((self.S, self.Hkv, self.N, self.dI), sd, TID_KI, dt)
+            out["k_idx"] = TensorSpec((self.S, self.Hkv, self.N, self.dI), sd, TID_KI, kdt)
         else:
             band = self.band()
             out["q_idx"] = TensorSpec((self.S, self.Hkv, self.T, self.dI), sd, TID_QI, dt, kind=KIND_QIDX,
                                       pos_offset=self.N - self.T, band=band)
-            out["k_idx"] = TensorSpec((self.S, self.Hkv, self.N, self.dI), sd, TID_KI, dt, kind=KIND_KIDX,
+            out["k_idx"] = TensorSpec((self.S, self.Hkv, self.N, self.dI), sd, TID_KI, kdt, kind=KIND_KIDX,
                                       boost=SIGMA_BOOST, block=128, boost_mask=self.boost_mask(), band=band)
         return out
 
@@ -128,7 +136,14 @@ C4 = Workload("C4_bf16_chunk_8k_at_1M", 4, S=1, T=8192, N=1048576, H=64, Hkv=8, 
 
 ALL = [C0, C1, C2, C3, C4]
 
+# C3 with 1-byte index keys (OCP E4M3, the same seeded values rounded once): the
+# serving variant of the decode index stream.  Not one of the five configurations.
+C3_FP8 = Workload("C3_bf16_decode_16x1M_e4m3_index_keys", 3, S=16, T=1, N=1048576, H=64, Hkv=8, d=128, dI=64,
+                  k=16, dtype=BF16, structure="sink_needles", kidx_dtype=FP8,
+                  description="bf16 MSA decode, 16 sequences x 1,048,576-token KV cache, index keys in FP8 E4M3")
 
-def small(name, S, T, N, H, Hkv, d, dI, k, dtype=BF16, structure="iid", index=100) -> Workload:
+
+def small(name, S, T, N, H, Hkv, d, dI, k, dtype=BF16, structure="iid", index=100, kidx_dtype=None) -> Workload:
     """A reduced workload with the same recipes (for parity tests that span ragged tiles)."""
-    return Workload(name, index, S=S, T=T, N=N, H=H, Hkv=Hkv, d=d, dI=dI, k=k, dtype=dtype, structure=structure)
+    return Workload(name, index, S=S, T=T, N=N, H=H, Hkv=Hkv, d=d, dI=dI, k=k, dtype=dtype, structure=structure,
+                    kidx_dtype=kidx_dtype)

@@ -53,6 +53,8 @@ def _good(**kw):
     (dict(topk=65), msa.MSA_ERR_UNSUPPORTED),
     (dict(kv_len=8192 * 128 + 1, num_q=1), msa.MSA_ERR_UNSUPPORTED),
     (dict(index_dim=48), msa.MSA_ERR_UNSUPPORTED),
+    (dict(index_key_dtype=5), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(index_key_dtype=msa.MSA_FP8_E4M3, dtype=msa.MSA_F32), msa.MSA_ERR_UNSUPPORTED),
     (dict(num_q=1 << 20, kv_len=1 << 20, num_kv_heads=128, num_heads=128), msa.MSA_ERR_UNSUPPORTED),
 ])
 def test_bad_problem_is_rejected_before_any_launch(kw, status):

@@ -79,6 +79,27 @@ def test_prefill_pipeline_matches_oracle(wl):
     _verify_prefill(wl, inputs, bufs)
 
 
+# 1-byte index keys (OCP E4M3; the serving variant): matrix-core indexer (T >= 256),
+# the row kernel (8 < T < 256) and, below, the decode stream.  The oracle decodes the
+# same E4M3 bytes exactly.
+FP8_CASES = [
+    W.small("bf16_e4m3_keys_structured", S=1, T=2048, N=3000, H=16, Hkv=2, d=128, dI=64, k=16,
+            structure="band_sink_needles", kidx_dtype=synth.FP8),
+    W.small("bf16_e4m3_keys_rows_dI128", S=2, T=100, N=1500, H=8, Hkv=2, d=64, dI=128, k=8, kidx_dtype=synth.FP8),
+    W.small("bf16_e4m3_keys_dI32", S=1, T=700, N=900, H=4, Hkv=1, d=64, dI=32, k=4, kidx_dtype=synth.FP8),
+]
+
+
+@pytest.mark.parametrize("wl", FP8_CASES, ids=[c.name for c in FP8_CASES])
+def test_prefill_with_e4m3_index_keys(wl):
+    require_gpu()
+    say("case", wl.name)
+    inputs = gen(wl)
+    assert inputs["k_idx"].dtype == torch.float8_e4m3fn
+    _, bufs = full_prefill(wl, inputs)
+    _verify_prefill(wl, inputs, bufs)
+
+
 QT_OFF_CASES = [c for c in CASES if c.name in ("bf16_g8_ragged_chunk", "bf16_structured",
                                                  "bf16_k64_all_blocks_shared", "bf16_g1_k3")]
 
@@ -103,6 +124,9 @@ DEC_CASES = [
     W.small("dec_bf16", S=3, T=1, N=5000, H=16, Hkv=2, d=128, dI=64, k=16, structure="sink_needles"),
     W.small("dec_fp32", S=2, T=1, N=3333, H=8, Hkv=2, d=64, dI=32, k=4, dtype=synth.F32),
     W.small("dec_bf16_multi_q", S=2, T=5, N=2000, H=8, Hkv=1, d=128, dI=64, k=8),
+    W.small("dec_e4m3_keys", S=3, T=1, N=5000, H=16, Hkv=2, d=128, dI=64, k=16, structure="sink_needles",
+            kidx_dtype=synth.FP8),
+    W.small("dec_e4m3_keys_multi_q_dI32", S=2, T=3, N=2100, H=8, Hkv=2, d=64, dI=32, k=8, kidx_dtype=synth.FP8),
 ]
 
 
@@ -252,12 +276,16 @@ def test_generator_device_matches_host():
     require_gpu()
     for wl in (W.small("gen", S=2, T=300, N=700, H=4, Hkv=2, d=64, dI=32, k=4, structure="band_sink_needles"),
                W.small("gen32", S=1, T=100, N=260, H=2, Hkv=1, d=64, dI=32, k=4, dtype=synth.F32),
-               W.small("gen_sn", S=3, T=1, N=1000, H=4, Hkv=2, d=64, dI=64, k=4, structure="sink_needles")):
+               W.small("gen_sn", S=3, T=1, N=1000, H=4, Hkv=2, d=64, dI=64, k=4, structure="sink_needles"),
+               W.small("gen_f8", S=2, T=200, N=900, H=4, Hkv=2, d=64, dI=64, k=4, structure="band_sink_needles",
+                       kidx_dtype=synth.FP8)):
         for name, spec in wl.specs().items():
             dev = synth.device_tensor(spec)
             host = synth.host_tensor(spec)
             if spec.dtype == synth.BF16:
                 got = dev.cpu().view(torch.int16).numpy().view(np.uint16)
+            elif spec.dtype == synth.FP8:
+                got = dev.cpu().view(torch.uint8).numpy()
             else:
                 got = dev.cpu().numpy()
             assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(host).view(np.uint8)), (wl.name, name)

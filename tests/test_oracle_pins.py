@@ -266,3 +266,34 @@ def test_whole_tensor_walk_matches_slices():
             np.testing.assert_array_equal(sel[s, g], ref_sel)
             ref = bf.attention(q[s][:, g * G:(g + 1) * G], K[s, g], V[s, g], pos, ref_sel, B, 0.5)
             np.testing.assert_allclose(out[s][:, g * G:(g + 1) * G], ref, rtol=1e-11, atol=1e-13)
+
+
+# ------------------------------------------------------------------ 1-byte index keys
+# Serving variant of the index keys: OCP FP8 E4M3 storage, decoded exactly.
+def test_e4m3_table_matches_the_format_definition():
+    t = oracle.e4m3_table()
+    # values fixed by the format: bias 7, 3 mantissa bits, subnormals m * 2^-9, no infinity
+    assert t[0x38] == 1.0 and t[0xB8] == -1.0
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0          # largest finite
+    assert t[0x08] == 2.0 ** -6                             # smallest normal
+    assert t[0x01] == 2.0 ** -9 and t[0x07] == 7 * 2.0 ** -9  # subnormals
+    assert t[0x00] == 0.0 and np.signbit(t[0x80])           # +0 and -0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert t[0x39] == 1.125 and t[0x40] == 2.0
+    finite = t[~np.isnan(t)]
+    assert len(finite) == 254
+    # monotone over the positive codes
+    assert np.all(np.diff(t[0x00:0x7F]) > 0)
+
+
+def test_e4m3_table_matches_torch_float8():
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    t = oracle.e4m3_table()
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(t))
+    np.testing.assert_array_equal(t[~nan], ref[~nan])
+
+
+def test_decode_handles_e4m3_tensors():
+    codes = torch.tensor([0x38, 0x7E, 0x81, 0x00], dtype=torch.uint8)
+    np.testing.assert_array_equal(oracle.decode(codes.view(torch.float8_e4m3fn)), [1.0, 448.0, -2.0 ** -9, 0.0])

@@ -30,6 +30,26 @@ def test_bf16_rounding_is_nearest_even():
     assert abs(float(back[4]) - 3.140625) < 1e-7
 
 
+def test_e4m3_encoding_is_nearest_even_and_saturating():
+    import torch
+    x = np.array([1.0, 1.0625, 1.1875, 1.125, -3.5, 448.0, 449.0, 1000.0, -1e6, 0.0, -0.0,
+                  2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -6, 0.015625 * 0.999], dtype=np.float32)
+    c = synth.f32_to_e4m3(x)
+    # 1.0625 lies halfway between 1.0 (mantissa 0) and 1.125 (1): even -> 1.0;
+    # 1.1875 halfway between 1.125 (1) and 1.25 (2): even -> 1.25
+    assert list(c[:5]) == [0x38, 0x38, 0x3A, 0x39, 0xC6]
+    assert list(c[5:9]) == [0x7E, 0x7E, 0x7E, 0xFE]          # saturation at +-448
+    assert c[9] == 0x00 and c[10] == 0x80                    # signed zeros
+    assert c[11] == 0x00 and c[12] == 0x02                   # subnormal ties to even
+    assert c[13] == 0x08 and c[14] == 0x08                   # rounds up into the smallest normal
+    # inside the finite range the encoding is torch's round-to-nearest-even conversion
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.standard_normal(100000) * 20, rng.standard_normal(100000) * 0.02]).astype(np.float32)
+    v = v[np.abs(v) < 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(synth.f32_to_e4m3(v), ref)
+
+
 def test_generation_is_deterministic_and_seed_dependent():
     a = synth.TensorSpec((1, 2, 50, 8), 7, synth.TID_Q)
     b = synth.TensorSpec((1, 2, 50, 8), 8, synth.TID_Q)
