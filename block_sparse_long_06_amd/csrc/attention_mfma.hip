@@ -14,15 +14,19 @@
 // The next sub-chunk's Q rows are fetched into registers while the current one
 // computes; two waves per SIMD overlap one wave's softmax with the other's MFMAs.
 //
-//  * LDS: K row-major (16-byte row pad), V TRANSPOSED (d x 128, 8-byte row pad, so a
-//    lane fetches 4 consecutive keys of one head dim with one 8-byte read).
+//  * LDS: K row-major (16-byte row pad), V TRANSPOSED (d x 128, 16-byte row pad).  In
+//    a V^T row the keys of every 16-key group are stored in the order in which one lane
+//    half feeds them to the PV contraction (see the P item below), so a lane fetches its
+//    8 keys of one head dim with one 16-byte read.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys, B = 32 M-rows): a lane's
 //    output column is one M-row, so row max and row sum are in-lane over 64 values
 //    plus one exchange with lane ^ 32.
 //  * P = exp2(s - m) stays in registers: accumulator registers 8p..8p+7 of key tile
 //    kt hold 8 keys of the lane's M-row, exactly the 8 k-elements a lane supplies to
 //    a B operand, so O^T = V^T P^T uses k-step (kt, p) with the accumulator's row
-//    order; the V^T A-operand reads the same keys (two runs of 4) from LDS.
+//    order.  Those 8 keys of lane half h are k0 + 4h + {0..3} and k0 + 8 + 4h + {0..3}
+//    (k0 = 16 p); V^T stores key k0 + 8a + 4h + x at column k0 + 8h + 4a + x, so they
+//    are one contiguous 16-byte run.
 //  * 32x32 accumulator layout: output row i is held by lane half (i % 8) / 4 in
 //    register 4 * (i / 8) + i % 4.  The QK contraction visits head dims in the order
 //    lane half h, k-step s -> dims [d/2 * h + 8 s, +8) (any order works as long as A
@@ -52,7 +56,7 @@ constexpr int kItemRows = 256;  // query rows per work item
 template <int DH>
 struct __attribute__((aligned(16))) OgqLds {
   static constexpr int KROW = DH * 2 + 16;   // K row, padded
-  static constexpr int VROW = kBlk * 2 + 8;  // V^T row, padded
+  static constexpr int VROW = kBlk * 2 + 16;  // V^T row, padded
   static constexpr int QROW = DH * 2 + 16;   // per-wave Q / O row, padded
   __attribute__((aligned(16))) unsigned char k[kBlk * KROW];
   __attribute__((aligned(16))) unsigned char vt[DH * VROW];
@@ -131,6 +135,8 @@ template <int DH>
 __device__ __forceinline__ void lstore_vt(unsigned char* lvt, const uint4 (&rv)[4]) {
   const int kg = threadIdx.x & 31;
   const int dc = threadIdx.x >> 5;
+  // keys 4 kg .. 4 kg + 3 = k0 + 8a + 4h + {0..3} go to columns k0 + 8h + 4a + {0..3}
+  const int kc = (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1);
   if (dc < DH / 8) {
     const uint32_t w[4][4] = {{rv[0].x, rv[0].y, rv[0].z, rv[0].w}, {rv[1].x, rv[1].y, rv[1].z, rv[1].w},
                               {rv[2].x, rv[2].y, rv[2].z, rv[2].w}, {rv[3].x, rv[3].y, rv[3].z, rv[3].w}};
@@ -142,7 +148,7 @@ __device__ __forceinline__ void lstore_vt(unsigned char* lvt, const uint4 (&rv)[
       uint2 o;
       o.x = k0 | (k1 << 16);
       o.y = k2 | (k3 << 16);
-      *reinterpret_cast<uint2*>(&lvt[(dc * 8 + e) * OgqLds<DH>::VROW + kg * 8]) = o;
+      *reinterpret_cast<uint2*>(&lvt[(dc * 8 + e) * OgqLds<DH>::VROW + kc * 8]) = o;
     }
   }
 }
@@ -318,13 +324,10 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        const int kb0 = (kt * 32 + 16 * pp + 4 * h) * 2;
+        const int kb0 = (kt * 32 + 16 * pp + 8 * h) * 2;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const unsigned char* vrow = &L.vt[(dt * 32 + nl) * OgqLds<DH>::VROW];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb0);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb0 + 16);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&L.vt[(dt * 32 + nl) * OgqLds<DH>::VROW + kb0]);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][pp], oacc[dt], 0, 0, 0);
         }
       }
@@ -607,13 +610,10 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
         for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
-            const int kb0 = ((2 * HF + k2) * 32 + 16 * pp + 4 * h) * 2;
+            const int kb0 = ((2 * HF + k2) * 32 + 16 * pp + 8 * h) * 2;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-              const unsigned char* vrow = &lvt[(dt * 32 + nl) * HotLds<DH>::VROW];
-              const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb0);
-              const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb0 + 16);
-              const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+              const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lvt[(dt * 32 + nl) * HotLds<DH>::VROW + kb0]);
               oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[k2][pp], oacc[dt], 0, 0, 0);
             }
           }
