@@ -272,6 +272,74 @@ def selection_structure(wl, sel, csr_offsets):
 
 
 # ------------------------------------------------------------------ main
+def paged_decode(args, msa, wd, xd):
+    """The decode workload over a ragged batch in a paged cache, outside the timed step:
+    sequence lengths drawn (seeded) from [N/2, N], every 128-position block in its own
+    page of a shuffled pool [pages, Hkv, 128, .] holding the same values as the dense
+    cache.  Reports the step time and the index stream's rate over the bytes it must read
+    (sum of lengths x Hkv x dI x 2)."""
+    import numpy as np
+    import torch
+    S, N, Hkv, B = wd.S, wd.N, wd.Hkv, 128
+    nb = N // B
+    rng = np.random.default_rng(wd.seed + 8)
+    lens = rng.integers(N // 2, N + 1, size=S)
+    need = (lens + B - 1) // B
+    num_pages = int(need.sum())
+    perm = rng.permutation(num_pages)
+    table = np.full((S, nb), -1, dtype=np.int32)
+    flat, pages, i = [], [], 0
+    for s in range(S):
+        table[s, :need[s]] = perm[i:i + need[s]]
+        flat.extend(range(s * nb, s * nb + int(need[s])))
+        pages.extend(perm[i:i + need[s]].tolist())
+        i += int(need[s])
+    flat = torch.tensor(flat, dtype=torch.int64, device="cuda")
+    pages = torch.tensor(pages, dtype=torch.int64, device="cuda")
+
+    def to_pool(dense):
+        w = dense.shape[-1]
+        src = dense.view(S, Hkv, nb, B, w).permute(0, 2, 1, 3, 4).reshape(S * nb, Hkv, B, w)
+        pool = torch.empty((num_pages, Hkv, B, w), dtype=dense.dtype, device="cuda")
+        pool[pages] = src[flat]
+        return pool
+
+    pools = {n: to_pool(xd[n]) for n in ("k", "v", "k_idx")}
+    kv_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    lay = msa.kv_layout(kv_lens, torch.from_numpy(table).cuda(), num_pages)
+    prob = wd.problem()
+    bufs = msa.alloc_decode(prob)
+
+    def step():
+        msa.run_decode_kv(prob, lay, xd["q"], pools["k"], pools["v"], xd["q_idx"], pools["k_idx"], bufs)
+    step()
+    torch.cuda.synchronize()
+    msa.profiler_read(None, reset=True)
+    msa.profiler_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    msa.profiler_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    st = {}
+    for kn in ("idx_scores_stream", "block_topk_t1", "decode_items", "decode_ogq_mfma", "decode_merge"):
+        tms, nl = msa.profiler_read(kn, reset=False)
+        if nl:
+            st[kn] = dict(ms=tms / nl)
+    msa.profiler_read(None, reset=True)
+    if "idx_scores_stream" in st:
+        kbytes = float(lens.sum()) * Hkv * wd.dI * 2.0 + 4.0 * float(need.sum()) * Hkv
+        sec = st["idx_scores_stream"]["ms"] / 1e3
+        st["idx_scores_stream"].update(roofline(2.0 * wd.dI * float(lens.sum()) * Hkv, kbytes, sec))
+    del pools
+    return dict(workload="%s, ragged lengths in [N/2, N] (mean %d), paged (%d shuffled 128-position pages)"
+                % (wd.description, int(lens.mean()), num_pages),
+                us_per_step=ms * 1e3, us_per_token_amortised=ms * 1e3 / S, stages=st)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +351,8 @@ def main():
                     help="prefill workload timed (default C2: the 131072-token headline configuration)")
     ap.add_argument("--no-fp8-decode", action="store_true",
                     help="skip the extra decode timing with the index keys stored as FP8 E4M3 (serving variant)")
+    ap.add_argument("--no-paged-decode", action="store_true",
+                    help="skip the extra decode timing over ragged lengths and a paged cache (serving variant)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy 3 times (the known-size reference "
                          "for scaling hardware byte counters)")
@@ -462,6 +532,12 @@ def main():
                     stages=k8, selection_overlap_with_bf16_keys=overlap)
         print("[bench] decode with E4M3 index keys: %.3f ms per step" % ms8, file=sys.stderr, flush=True)
 
+    decp = None
+    if db is not None and not args.no_paged_decode:
+        decp = paged_decode(args, msa, wd, xd)
+        print("[bench] decode over ragged lengths and a paged cache: %.3f ms per step" % (decp["us_per_step"] / 1e3),
+              file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline ...", file=sys.stderr, flush=True)
@@ -476,7 +552,7 @@ def main():
         "config": {"workload": wp.description, "batch": wp.S, "seq_len": wp.T, "num_heads": wp.H,
                    "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
         "prefill_ms": prefill_ms, "wall_s_timed": wall,
-        "decode": dec, "decode_e4m3_index_keys": dec8, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
+        "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
         "selection_structure": selection_structure(wp, pb.sel, pb.csr_offsets),
         "attention_pairs": split["pairs"],
     }

@@ -24,7 +24,8 @@ MSA_CALL_INVERT, MSA_CALL_PREFILL, MSA_CALL_DECODE = 2, 3, 4
 
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_invert_selection", "msa_sparse_attn_prefill",
             "msa_sparse_attn_decode", "msa_workspace_bytes", "msa_status_string",
-            "msa_last_error_message", "msa_profiler_enable", "msa_profiler_read")
+            "msa_last_error_message", "msa_profiler_enable", "msa_profiler_read", "msa_index_scores_kv",
+            "msa_block_topk_kv", "msa_sparse_attn_decode_kv")
 
 
 class MSAError(RuntimeError):
@@ -53,6 +54,24 @@ class Problem(ctypes.Structure):
         return "Problem(" + ", ".join("%s=%r" % (f, getattr(self, f)) for f, _ in self._fields_) + ")"
 
 
+class KVLayout(ctypes.Structure):
+    """msa_kv_layout: per-sequence lengths and an optional page table (device pointers)."""
+    _fields_ = [("kv_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("table_stride", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
+
+
+def kv_layout(kv_lens, block_table=None, num_pages: int = 0) -> KVLayout:
+    """Layout for the per-sequence calls: kv_lens int32 [S] on the device; block_table int32
+    [S, stride] on the device (or None for dense caches); num_pages = pages in each pool."""
+    lay = KVLayout()
+    lay.kv_lens = kv_lens.data_ptr()
+    lay.block_table = block_table.data_ptr() if block_table is not None else None
+    lay.table_stride = int(block_table.shape[1]) if block_table is not None else 0
+    lay.num_pages = int(num_pages)
+    lay._keep = (kv_lens, block_table)  # the tensors must outlive the calls
+    return lay
+
+
 def problem(batch, num_q, kv_len, num_heads, num_kv_heads, head_dim, index_dim, topk,
             dtype=MSA_BF16, block_size=128, softmax_scale=0.0, index_key_dtype=0) -> Problem:
     return Problem(batch, num_q, kv_len, num_heads, num_kv_heads, head_dim, index_dim, block_size,
@@ -77,8 +96,13 @@ def lib():
         L.msa_invert_selection.argtypes = [PP, P, P, P, P, ctypes.c_size_t, P]
         L.msa_sparse_attn_prefill.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_sparse_attn_decode.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
+        LP = ctypes.POINTER(KVLayout)
+        L.msa_index_scores_kv.argtypes = [PP, LP, P, P, P, P]
+        L.msa_block_topk_kv.argtypes = [PP, LP, P, P, P]
+        L.msa_sparse_attn_decode_kv.argtypes = [PP, LP, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in ("msa_index_scores", "msa_block_topk", "msa_invert_selection",
-                  "msa_sparse_attn_prefill", "msa_sparse_attn_decode"):
+                  "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_index_scores_kv",
+                  "msa_block_topk_kv", "msa_sparse_attn_decode_kv"):
             getattr(L, f).restype = st
         L.msa_workspace_bytes.argtypes = [PP, ctypes.c_int]
         L.msa_workspace_bytes.restype = ctypes.c_size_t
@@ -161,6 +185,27 @@ def sparse_attn_decode(prob: Problem, q, k_cache, v_cache, sel, out, workspace, 
                                         _stream(stream, q)))
 
 
+def _lay(layout):
+    return ctypes.byref(layout) if layout is not None else None
+
+
+def index_scores_kv(prob: Problem, layout: KVLayout, q_idx, k_idx, scores, stream=None) -> None:
+    _check(lib().msa_index_scores_kv(ctypes.byref(prob), _lay(layout), _ptr(q_idx), _ptr(k_idx), _ptr(scores),
+                                     _stream(stream, q_idx)))
+
+
+def block_topk_kv(prob: Problem, layout: KVLayout, scores, sel, stream=None) -> None:
+    _check(lib().msa_block_topk_kv(ctypes.byref(prob), _lay(layout), _ptr(scores), _ptr(sel),
+                                   _stream(stream, scores)))
+
+
+def sparse_attn_decode_kv(prob: Problem, layout: KVLayout, q, k_cache, v_cache, sel, out, workspace,
+                          workspace_bytes_: int, stream=None) -> None:
+    _check(lib().msa_sparse_attn_decode_kv(ctypes.byref(prob), _lay(layout), _ptr(q), _ptr(k_cache),
+                                           _ptr(v_cache), _ptr(sel), _ptr(out), _ptr(workspace),
+                                           workspace_bytes_, _stream(stream, q)))
+
+
 def profiler_enable(on: bool) -> None:
     _check(lib().msa_profiler_enable(1 if on else 0))
 
@@ -239,3 +284,12 @@ def run_decode(prob: Problem, q, k_cache, v_cache, q_idx, k_idx, bufs: DecodeBuf
     block_topk(prob, bufs.scores, bufs.sel, stream)
     sparse_attn_decode(prob, q, k_cache, v_cache, bufs.sel, bufs.out, bufs.ws_decode,
                        bufs.ws_decode.numel(), stream)
+
+
+def run_decode_kv(prob: Problem, layout: KVLayout, q, k_cache, v_cache, q_idx, k_idx, bufs: DecodeBuffers,
+                  stream=None) -> None:
+    """One decode step over ragged / paged caches (same stages as run_decode)."""
+    index_scores_kv(prob, layout, q_idx, k_idx, bufs.scores, stream)
+    block_topk_kv(prob, layout, bufs.scores, bufs.sel, stream)
+    sparse_attn_decode_kv(prob, layout, q, k_cache, v_cache, bufs.sel, bufs.out, bufs.ws_decode,
+                          bufs.ws_decode.numel(), stream)

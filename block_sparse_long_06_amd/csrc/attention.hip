@@ -85,9 +85,11 @@ template <typename T, int DH>
 __device__ void stage_block(const Dims& D, BlockLds<T, DH>& L, const T* k, const T* v, int64_t sg,
                             int b) {
   const int j0 = b * 128;
-  const int nvalid = min(128, D.N - j0);
-  const T* kb = k + (sg * D.N + j0) * DH;
-  const T* vb = v + (sg * D.N + j0) * DH;
+  const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
+  const int64_t kv0 = kv_row(D, s, g, j0, DH);  // a block is contiguous; an invalid page reads as 0
+  const int nvalid = kv0 < 0 ? 0 : min(128, seq_len(D, s) - j0);
+  const T* kb = k + (kv0 < 0 ? 0 : kv0);
+  const T* vb = v + (kv0 < 0 ? 0 : kv0);
   for (int i = threadIdx.x; i < 128 * DH; i += 256) {
     const int row = i / DH, c = i % DH;
     const bool ok = row < nvalid;
@@ -101,7 +103,7 @@ template <typename T, typename PT, int DH>
 __device__ void attend_one(const Dims& D, BlockLds<T, DH>& L, const T* q, int s, int g, int b, int t,
                            int slot, int h, float* part_lse, PT* part_o) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int p = D.pos0 + t;
+  const int p = seq_pos0(D, s) + t;
   const T* qv = q + (((int64_t)s * D.T + t) * D.H + g * D.G + h) * DH;
   for (int c = lane; c < DH; c += 64) L.Q[wave][c] = ldf(qv, c);
   __builtin_amdgcn_wave_barrier();

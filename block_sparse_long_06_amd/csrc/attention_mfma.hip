@@ -227,7 +227,9 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
   const int b = w.x % D.nb;
   const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
   const int j0 = b * kBlk;
-  const int nvalid = min(kBlk, D.N - j0);
+  const int pos0 = seq_pos0(D, s);
+  const int64_t kv0 = kv_row(D, s, g, j0, DH);  // a block is contiguous; an invalid page reads as 0
+  const int nvalid = kv0 < 0 ? 0 : min(kBlk, seq_len(D, s) - j0);
   const int rows = w.z;
 
   // per-row tables (one division per row, once per item)
@@ -237,9 +239,9 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
     const int slot = e - t * D.k;
     L.qoff[r] = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G) * DH;
     L.pidx[r] = (((int64_t)s * D.T + t) * D.Hkv + g) * D.k + slot;
-    L.pos[r] = D.pos0 + t;
+    L.pos[r] = pos0 + t;
   }
-  stage_kv<DH>(L, k + (sg * D.N + j0) * DH, v + (sg * D.N + j0) * DH, nvalid);
+  stage_kv<DH>(L, k + (kv0 < 0 ? 0 : kv0), v + (kv0 < 0 ? 0 : kv0), nvalid);
   __syncthreads();
 
   const int wave = threadIdx.x >> 6;

@@ -68,14 +68,15 @@ __global__ void __launch_bounds__(kWaves * 64) idx_scores_rows(Dims D, const T* 
   const int b = blockIdx.y * kWaves + (threadIdx.x >> 6);
   const int t = (int)(row % D.T);
   const int64_t sg = row / D.T;
-  const int p = D.pos0 + t;
+  const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
+  const int p = seq_pos0(D, s) + t;
   const int bt = p / D.B;
   if (b > bt) return;
   const T* q = q_idx + row * D.dI;
-  const TK* kbase = k_idx + sg * (int64_t)D.N * D.dI;
-  float best = -INFINITY;
-  for (int j = b * D.B + lane; j < (b + 1) * D.B && j <= p; j += 64) {
-    const TK* kk = kbase + (int64_t)j * D.dI;
+  const int64_t kb0 = kv_row(D, s, g, b * D.B, D.dI);  // a block's rows are contiguous
+  float best = kb0 < 0 ? 0.0f : -INFINITY;               // rows of an invalid page read as 0
+  for (int j = b * D.B + lane; kb0 >= 0 && j < (b + 1) * D.B && j <= p; j += 64) {
+    const TK* kk = k_idx + kb0 + (int64_t)(j - b * D.B) * D.dI;
     float acc = 0.0f;
     for (int c = 0; c < D.dI; c += 8) {
       float qv[8], kv[8];
@@ -114,25 +115,30 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
   const int col = threadIdx.x % CPR;
   const int kslot = threadIdx.x / CPR;
   const int64_t sg = blockIdx.y;
+  const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
   const int b0 = blockIdx.x * kStreamBlocks;
   const int T = D.T;
+  const int ns = seq_len(D, s);
   float qv[TQ][DPL];
   int pq[TQ];
 #pragma unroll
   for (int tq = 0; tq < TQ; ++tq) {
     const int t = tq < T ? tq : T - 1;
-    pq[tq] = tq < T ? D.pos0 + tq : -1;
+    pq[tq] = tq < T ? ns - T + tq : -1;
 #pragma unroll
     for (int x = 0; x < DPL; x += 8) load8(q_idx + (sg * T + t) * DI + col * DPL + x, &qv[tq][x]);
   }
-  const TK* kbase = k_idx + sg * (int64_t)D.N * DI + col * DPL;
-  const int bend = min(b0 + kStreamBlocks, D.nb);
+  const int bend = min(b0 + kStreamBlocks, (ns + 127) / 128);
   for (int b = b0; b < bend; ++b) {
+    // a block's rows are contiguous (dense cache or one page); an invalid page reads as 0
+    const int64_t kb0 = kv_row(D, s, g, b * 128, DI);
+    const TK* kbase = k_idx + (kb0 < 0 ? 0 : kb0) + col * DPL;
     uint4 kr[PASSES];
 #pragma unroll
     for (int u = 0; u < PASSES; ++u) {
-      const int j = b * 128 + u * KPP + kslot;
-      kr[u] = j < D.N ? *reinterpret_cast<const uint4*>(kbase + (int64_t)j * DI) : make_uint4(0u, 0u, 0u, 0u);
+      const int jj = u * KPP + kslot;
+      kr[u] = kb0 >= 0 && b * 128 + jj < ns ? *reinterpret_cast<const uint4*>(kbase + (int64_t)jj * DI)
+                                            : make_uint4(0u, 0u, 0u, 0u);
     }
     float m[TQ];
 #pragma unroll

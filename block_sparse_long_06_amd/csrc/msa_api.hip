@@ -100,7 +100,31 @@ msa_status check_problem(const msa_problem* p, msa::Dims* D, bool need_index, bo
   D->pos0 = p->kv_len - p->num_q;
   D->dtype = p->dtype;
   D->kdtype = p->index_key_dtype == MSA_FP8_E4M3 ? MSA_FP8_E4M3 : p->dtype;
+  D->kv_lens = nullptr;
+  D->block_table = nullptr;
+  D->bt_stride = 0;
+  D->num_pages = 0;
   D->scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / sqrtf((float)p->head_dim);
+  return MSA_OK;
+}
+
+// Validates a per-sequence cache layout on the host and records it in D.
+msa_status apply_layout(const msa_kv_layout* L, msa::Dims* D) {
+  if (L == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "layout is NULL");
+  if (L->kv_lens == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "layout->kv_lens is NULL");
+  if (D->T > 8) return fail(MSA_ERR_UNSUPPORTED, "the per-sequence calls take num_q <= 8 (got %d)", D->T);
+  if (L->block_table != nullptr) {
+    if (L->table_stride < D->nb)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "layout->table_stride %d < ceil(kv_len / block_size) = %d",
+                  L->table_stride, D->nb);
+    if (L->num_pages < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "layout->num_pages must be >= 1");
+    if ((int64_t)L->num_pages * D->Hkv * D->B * (D->d > D->dI ? D->d : D->dI) >= (int64_t(1) << 40))
+      return fail(MSA_ERR_UNSUPPORTED, "page pool too large");
+  }
+  D->kv_lens = L->kv_lens;
+  D->block_table = L->block_table;
+  D->bt_stride = L->block_table != nullptr ? L->table_stride : 0;
+  D->num_pages = L->block_table != nullptr ? L->num_pages : 0;
   return MSA_OK;
 }
 
@@ -266,6 +290,55 @@ msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, const 
   return device_status(
       msa::launch_decode(D, q, k_cache, v_cache, sel, out, workspace, (hipStream_t)stream),
       "msa_sparse_attn_decode launch");
+}
+
+msa_status msa_index_scores_kv(const msa_problem* prob, const msa_kv_layout* layout, const void* q_idx,
+                               const void* k_idx, float* scores, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, true, false);
+  if (st != MSA_OK) return st;
+  st = apply_layout(layout, &D);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(k_idx);
+  REQUIRE_PTR(scores);
+  return device_status(msa::launch_index_scores(D, q_idx, k_idx, scores, (hipStream_t)stream),
+                       "msa_index_scores_kv launch");
+}
+
+msa_status msa_block_topk_kv(const msa_problem* prob, const msa_kv_layout* layout, const float* scores,
+                             int32_t* sel, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, false);
+  if (st != MSA_OK) return st;
+  st = apply_layout(layout, &D);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(scores);
+  REQUIRE_PTR(sel);
+  return device_status(msa::launch_block_topk(D, scores, sel, (hipStream_t)stream), "msa_block_topk_kv launch");
+}
+
+msa_status msa_sparse_attn_decode_kv(const msa_problem* prob, const msa_kv_layout* layout, const void* q,
+                                     const void* k_cache, const void* v_cache, const int32_t* sel, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, true);
+  if (st != MSA_OK) return st;
+  st = apply_layout(layout, &D);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(out);
+  const size_t need = msa::decode_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "msa_sparse_attn_decode_kv needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(
+      msa::launch_decode(D, q, k_cache, v_cache, sel, out, workspace, (hipStream_t)stream),
+      "msa_sparse_attn_decode_kv launch");
 }
 
 msa_status msa_profiler_enable(int on) {

@@ -17,6 +17,12 @@ struct Dims {
   int dtype;     // msa_dtype
   float scale;   // main-branch logit scale (resolved, never 0)
   int kdtype;    // msa_dtype of k_idx (resolved: dtype or MSA_FP8_E4M3)
+  // Cache layout of the per-sequence calls (null: dense [S, Hkv, N, .] caches, every
+  // sequence N positions long).
+  const int32_t* kv_lens;      // [S] device: sequence s holds positions 0 .. kv_lens[s]-1
+  const int32_t* block_table;  // [S, bt_stride] device: page of logical block b, or null
+  int bt_stride;
+  int num_pages;               // pages of the pools [num_pages, Hkv, B, .]
 };
 
 // ----------------------------------------------------------------- profiler
@@ -105,6 +111,25 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// Length of sequence s: kv_lens[s] clamped to [T, N] (a device-side value outside the
+// contract can never address memory outside the caller's buffers), N without kv_lens.
+__device__ __forceinline__ int seq_len(const Dims& D, int s) {
+  if (D.kv_lens == nullptr) return D.N;
+  const int n = D.kv_lens[s];
+  return n < D.T ? D.T : (n > D.N ? D.N : n);
+}
+// Absolute position of query row 0 of sequence s (its queries are its last T positions).
+__device__ __forceinline__ int seq_pos0(const Dims& D, int s) { return seq_len(D, s) - D.T; }
+// Element offset of cache row j of (sequence s, group g) in a cache of row width w: dense
+// [S, Hkv, N, w], or the pool [num_pages, Hkv, B, w] through the block table (one page =
+// one 128-position block).  -1 for a page id outside [0, num_pages): such rows read as 0.
+__device__ __forceinline__ int64_t kv_row(const Dims& D, int s, int g, int j, int w) {
+  if (D.block_table == nullptr) return (((int64_t)s * D.Hkv + g) * D.N + j) * w;
+  const int page = D.block_table[(int64_t)s * D.bt_stride + (j >> 7)];
+  if ((unsigned)page >= (unsigned)D.num_pages) return -1;
+  return (((int64_t)page * D.Hkv + g) * 128 + (j & 127)) * w;
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
   const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
   if (row >= rows) return;
   const int t = (int)(row % D.T);
-  const int bt = (D.pos0 + t) / D.B;
+  const int bt = (seq_pos0(D, (int)(row / ((int64_t)D.Hkv * D.T))) + t) / D.B;
   const int k = D.k;
   int32_t* out = sel + row * k;
   const int n = bt;        // eligible blocks other than the own one: 0 .. bt-1

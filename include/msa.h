@@ -166,6 +166,52 @@ msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, const 
                                   const void* v_cache, const int32_t* sel, void* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Serving variants of the decode step: ragged per-sequence cache lengths and paged caches
+ * ([P1] 第二步：精算 -- the whole uncompressed cache stays resident, and each new token
+ * reads 16 of its 128-token blocks; one page here IS one such block).
+ *
+ *   kv_lens      DEVICE int32 [S]: sequence s holds positions 0 .. kv_lens[s]-1, and its
+ *                T queries are its last T positions (p = kv_lens[s] - T + t).  Required.
+ *                Contract: T <= kv_lens[s] <= prob->kv_len; a value outside is clamped to
+ *                that range on the device (never an out-of-bounds access).
+ *   block_table  DEVICE int32 [S, table_stride] or NULL.  NULL: the caches are dense
+ *                [S, Hkv, kv_len, w] (w = head_dim for k/v, index_dim for k_idx) and only
+ *                kv_lens applies.  Otherwise every cache argument is a page pool
+ *                [num_pages, Hkv, block_size, w] and logical block b of sequence s is page
+ *                block_table[s * table_stride + b] (entries for b < ceil(kv_lens[s] / B) are
+ *                read).  A page id outside [0, num_pages) reads as zeros (its scores and
+ *                attention contributions are then meaningless, but no memory outside the
+ *                pools is touched).
+ *   table_stride >= ceil(kv_len / block_size) when block_table != NULL.
+ *   num_pages    >= 1 when block_table != NULL.
+ * The problem's kv_len is the capacity (the largest allowed length); nb = ceil(kv_len / B)
+ * sizes the scores rows.  These calls take num_q <= 8 (decode and few-token speculative
+ * decode); other sizes return MSA_ERR_UNSUPPORTED.
+ */
+typedef struct {
+  const int32_t* kv_lens;
+  const int32_t* block_table;
+  int32_t table_stride;
+  int32_t num_pages;
+} msa_kv_layout;
+
+/* a1 of msa_index_scores for the layout: scores [S, Hkv, T, nb], entries b > b_t of each
+ * row not written, b_t = floor((kv_lens[s] - T + t) / B). */
+msa_status msa_index_scores_kv(const msa_problem* prob, const msa_kv_layout* layout, const void* q_idx,
+                               const void* k_idx, float* scores, void* stream);
+
+/* a2 of msa_block_topk with the own block b_t of each row taken from kv_lens (only
+ * layout->kv_lens is read). */
+msa_status msa_block_topk_kv(const msa_problem* prob, const msa_kv_layout* layout, const float* scores,
+                             int32_t* sel, void* stream);
+
+/* a6 of msa_sparse_attn_decode for the layout (workspace: msa_workspace_bytes(prob,
+ * MSA_CALL_DECODE) bytes). */
+msa_status msa_sparse_attn_decode_kv(const msa_problem* prob, const msa_kv_layout* layout, const void* q,
+                                     const void* k_cache, const void* v_cache, const int32_t* sel, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device workspace needed by a call (MSA_CALL_*); 0 for an invalid problem or call. */
 size_t msa_workspace_bytes(const msa_problem* prob, int which_call);
 

@@ -122,3 +122,47 @@ def test_profiler_read_without_records():
     msa.profiler_enable(False)
     ms, n = msa.profiler_read(None)
     assert ms == 0.0 and n == 0
+
+
+def _layout(kv_lens=1, block_table=None, stride=0, pages=0):
+    lay = msa.KVLayout()
+    lay.kv_lens = kv_lens
+    lay.block_table = block_table
+    lay.table_stride = stride
+    lay.num_pages = pages
+    return lay
+
+
+@pytest.mark.parametrize("lay,kw,status", [
+    (None, {}, msa.MSA_ERR_INVALID_ARGUMENT),                                    # no layout
+    ("nolens", {}, msa.MSA_ERR_INVALID_ARGUMENT),                                # kv_lens NULL
+    ("dense", dict(num_q=9), msa.MSA_ERR_UNSUPPORTED),                           # more than 8 queries
+    ("shortstride", {}, msa.MSA_ERR_INVALID_ARGUMENT),                           # table_stride < nb
+    ("nopages", {}, msa.MSA_ERR_INVALID_ARGUMENT),                               # num_pages < 1
+])
+def test_kv_layout_is_validated_on_the_host(lay, kw, status):
+    p = _good(**dict(dict(num_q=1, kv_len=1000), **kw))
+    layouts = {None: None, "nolens": _layout(kv_lens=None), "dense": _layout(),
+               "shortstride": _layout(block_table=1, stride=7, pages=10),   # nb = 8
+               "nopages": _layout(block_table=1, stride=8, pages=0)}
+    L = layouts[lay]
+    for call in (lambda: msa.index_scores_kv(p, L, 1, 1, 1, stream=0),
+                 lambda: msa.block_topk_kv(p, L, 1, 1, stream=0),
+                 lambda: msa.sparse_attn_decode_kv(p, L, 1, 1, 1, 1, 1, 1, 1 << 40, stream=0)):
+        with pytest.raises(msa.MSAError) as ei:
+            call()
+        assert ei.value.status == status
+        assert msa.last_error_message() != ""
+
+
+def test_kv_calls_reject_null_pointers_and_small_workspace():
+    p = _good(num_q=1, kv_len=1000)
+    L = _layout(block_table=1, stride=8, pages=3)
+    with pytest.raises(msa.MSAError) as ei:
+        msa.index_scores_kv(p, L, 1, None, 1, stream=0)
+    assert ei.value.status == msa.MSA_ERR_INVALID_ARGUMENT
+    need = msa.workspace_bytes(p, msa.MSA_CALL_DECODE)
+    with pytest.raises(msa.MSAError) as ei:
+        msa.sparse_attn_decode_kv(p, L, 1, 1, 1, 1, 1, 1, need - 1, stream=0)
+    assert ei.value.status == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+
