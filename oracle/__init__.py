@@ -63,9 +63,16 @@ def _load():
         lib.orc_attention_partials.argtypes = [i64, i32, i32, i32, i32, i64, P, P, P, P, P,
                                                ctypes.c_double, P, P]
         lib.orc_lse_merge.argtypes = [i32, i32, i32, i64, P, P, P]
+        lib.orc_attention_train.argtypes = [i64, i32, i32, i32, i32, i64, P, P, P, P, P, ctypes.c_double,
+                                            P, P, P]
+        lib.orc_attention_backward.argtypes = [i64, i32, i32, i32, i32, i64, P, P, P, P, P, ctypes.c_double,
+                                               P, P, P, P]
+        lib.orc_index_kl.argtypes = [i64, i32, i64, P, P, P, ctypes.c_double, P, P]
+        lib.orc_index_backward.argtypes = [i64, i32, i32, i32, i64, P, P, P, P, P, P, P]
         lib.orc_num_threads.restype = ctypes.c_int
         for f in ("orc_index_scores", "orc_block_topk", "orc_invert", "orc_attention",
-                  "orc_attention_partials", "orc_lse_merge"):
+                  "orc_attention_partials", "orc_lse_merge", "orc_attention_train", "orc_attention_backward",
+                  "orc_index_kl", "orc_index_backward"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -199,6 +206,66 @@ def slice_lse_merge(lse, Op) -> np.ndarray:
     out = np.empty((R, G, d), dtype=np.float64)
     _load().orc_lse_merge(d, G, k, R, _p(lse), _p(Op), _p(out))
     return out
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def slice_attention_train(q_rows, pos, sel_rows, K, V, B: int, scale: float):
+    """-> (out [R, G, d], lse [R, G] natural log, mass [R, k] teacher block masses)."""
+    q_rows, K, V = _f64(q_rows), _f64(K), _f64(V)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel_rows = np.ascontiguousarray(sel_rows, dtype=np.int32)
+    R, G, d = q_rows.shape
+    k = sel_rows.shape[1]
+    out = np.empty((R, G, d))
+    lse = np.empty((R, G))
+    mass = np.empty((R, k))
+    _load().orc_attention_train(K.shape[0], B, d, G, k, R, _p(q_rows), _p(pos), _p(sel_rows), _p(K), _p(V),
+                                float(scale), _p(out), _p(lse), _p(mass))
+    return out, lse, mass
+
+
+def slice_attention_backward(q_rows, pos, sel_rows, K, V, B: int, scale: float, dout):
+    """Gradients of sum(dout * out) -> (dq [R, G, d], dK [N, d], dV [N, d])."""
+    q_rows, K, V, dout = _f64(q_rows), _f64(K), _f64(V), _f64(dout)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel_rows = np.ascontiguousarray(sel_rows, dtype=np.int32)
+    R, G, d = q_rows.shape
+    k = sel_rows.shape[1]
+    dq = np.empty((R, G, d))
+    dK = np.empty(K.shape)
+    dV = np.empty(V.shape)
+    _load().orc_attention_backward(K.shape[0], B, d, G, k, R, _p(q_rows), _p(pos), _p(sel_rows), _p(K), _p(V),
+                                   float(scale), _p(dout), _p(dq), _p(dK), _p(dV))
+    return dq, dK, dV
+
+
+def slice_index_kl(scores, sel_rows, mass, sigma: float):
+    """scores [R, nb], sel [R, k], teacher mass [R, k] -> (loss [R], dscore [R, k])."""
+    scores, mass = _f64(scores), _f64(mass)
+    sel_rows = np.ascontiguousarray(sel_rows, dtype=np.int32)
+    R, nb = scores.shape
+    k = sel_rows.shape[1]
+    loss = np.empty((R,))
+    dscore = np.empty((R, k))
+    _load().orc_index_kl(nb, k, R, _p(scores), _p(sel_rows), _p(mass), float(sigma), _p(loss), _p(dscore))
+    return loss, dscore
+
+
+def slice_index_backward(qI_rows, pos, sel_rows, KI, B: int, dscore):
+    """-> (dqI [R, dI], dKI [N, dI]) through the causal block max-pool."""
+    qI_rows, KI, dscore = _f64(qI_rows), _f64(KI), _f64(dscore)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel_rows = np.ascontiguousarray(sel_rows, dtype=np.int32)
+    R, dI = qI_rows.shape
+    k = sel_rows.shape[1]
+    dqI = np.empty((R, dI))
+    dKI = np.empty(KI.shape)
+    _load().orc_index_backward(KI.shape[0], B, dI, k, R, _p(qI_rows), _p(pos), _p(sel_rows), _p(KI), _p(dscore),
+                               _p(dqI), _p(dKI))
+    return dqI, dKI
 
 
 # ------------------------------------------------------- whole-tensor conveniences

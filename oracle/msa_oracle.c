@@ -10,6 +10,7 @@
  *        "Kernel 创新：Outer Gather Q", "附录最有意思：head 涌现的三种模式".
  *   [P3] "稀疏注意力速览（Sparse Attention，2019 ~ 2026）" (speedcell4.github.io),
  *        entry "MiniMax Sparse Attention（MSA）".
+ *   [P1] also section "索引分支训练：KL 对齐" for the training functions.
  *   [P5] "稀疏注意力架构革命：2026年长上下文大模型核心技术解析" (chenxutan.com),
  *        section on standard self-attention (softmax(QK^T/sqrt(d_k))V).
  *
@@ -30,7 +31,8 @@
  *   - the main branch scales logits by softmax_scale (1/sqrt(d) by default).
  *
  * Parity status: every function here is pinned by tests against brute force,
- * closed forms and special cases that reduce to textbook dense attention.
+ * closed forms and special cases that reduce to textbook dense attention; the
+ * training functions against float64 autograd, closed forms and finite differences.
  */
 #include <math.h>
 #include <stdint.h>
@@ -267,6 +269,216 @@ void orc_lse_merge(int d, int G, int k, int64_t nrows, const double *lse,
                 const double w = exp(L - Lt);
                 const double *src = Op + ((r * k + i) * G + h) * d;
                 for (int c = 0; c < d; ++c) o[c] += w * src[c];
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ training
+ * [P1 索引分支训练：KL 对齐: the index branch learns from the main branch's attention
+ *  distribution through a KL divergence, and the training signal updates only the index
+ *  branch (the teacher is cut from the gradient); P3 MSA entry "KL loss 让 index 分布对齐
+ *  Main Branch 概率（teacher stop-gradient）"]
+ * Readings where the pages are silent (also in the design notes):
+ *   - teacher of row r = the main branch's attention mass on each selected block,
+ *     averaged over the G heads of the group (L1-normalised over the selection);
+ *   - student = softmax over the same selected blocks of sigma * block score;
+ *   - loss per row = KL(teacher || student); gradients are of the sum of row losses;
+ *   - the max-pool passes the gradient of a block score to its arg-max key, the lowest
+ *     position among equal maxima. */
+
+/* The main branch of orc_attention, also returning for each row and head the
+ * natural-log normaliser lse[r,h] = log sum_{j in J} exp(scale q.K_j), and for each
+ * selected slot the teacher mass[r,i] = (1/G) sum_h sum_{j in block sel[r][i], j <= pos}
+ * softmax_j (0 for a -1 slot).  lse is [nrows, G]; mass is [nrows, k]. */
+void orc_attention_train(int64_t N, int B, int d, int G, int k, int64_t nrows,
+                         const double *q, const int64_t *pos, const int32_t *sel,
+                         const double *K, const double *V, double scale, double *out,
+                         double *lse, double *mass)
+{
+    (void)N;
+#pragma omp parallel
+    {
+        double *logit = (double *)malloc(sizeof(double) * (size_t)k * (size_t)B);
+        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)k * (size_t)B);
+        int *slot = (int *)malloc(sizeof(int) * (size_t)k * (size_t)B);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t p = pos[r];
+            int64_t nk = 0;
+            for (int i = 0; i < k; ++i) {
+                mass[r * k + i] = 0.0;
+                int32_t b = sel[r * k + i];
+                if (b < 0) continue;
+                for (int64_t j = (int64_t)b * B; j < ((int64_t)b + 1) * B && j <= p; ++j) {
+                    key[nk] = j;
+                    slot[nk++] = i;
+                }
+            }
+            for (int h = 0; h < G; ++h) {
+                const double *qq = q + (r * G + h) * d;
+                double m = -INFINITY;
+                for (int64_t a = 0; a < nk; ++a) {
+                    const double *kk = K + key[a] * d;
+                    double s = 0.0;
+                    for (int c = 0; c < d; ++c) s += qq[c] * kk[c];
+                    logit[a] = s * scale;
+                    if (logit[a] > m) m = logit[a];
+                }
+                double l = 0.0;
+                for (int64_t a = 0; a < nk; ++a) { logit[a] = exp(logit[a] - m); l += logit[a]; }
+                lse[r * G + h] = m + log(l);
+                double *o = out + (r * G + h) * d;
+                for (int c = 0; c < d; ++c) o[c] = 0.0;
+                for (int64_t a = 0; a < nk; ++a) {
+                    const double w = logit[a] / l;
+                    const double *vv = V + key[a] * d;
+                    for (int c = 0; c < d; ++c) o[c] += w * vv[c];
+                    mass[r * k + slot[a]] += w / G;
+                }
+            }
+        }
+        free(logit);
+        free(key);
+        free(slot);
+    }
+}
+
+/* Gradients of the main branch: with out as in orc_attention and an upstream gradient
+ * dout [nrows, G, d], the gradients of sum_{r,h} dout[r,h,:] . out[r,h,:] with respect to
+ * q [nrows, G, d], K [N, d] and V [N, d] (chain rule through the softmax):
+ *   P_j = softmax_j(scale q.K_j) over J,   dP_j = dout . V_j,   D = sum_j P_j dP_j,
+ *   dS_j = P_j (dP_j - D),   dq += scale sum_j dS_j K_j,
+ *   dK_j += scale dS_j q,    dV_j += P_j dout.
+ * dq, dK, dV are overwritten.  Serial (the K/V gradients accumulate across rows). */
+void orc_attention_backward(int64_t N, int B, int d, int G, int k, int64_t nrows,
+                            const double *q, const int64_t *pos, const int32_t *sel,
+                            const double *K, const double *V, double scale, const double *dout,
+                            double *dq, double *dK, double *dV)
+{
+    memset(dq, 0, sizeof(double) * (size_t)nrows * (size_t)G * (size_t)d);
+    memset(dK, 0, sizeof(double) * (size_t)N * (size_t)d);
+    memset(dV, 0, sizeof(double) * (size_t)N * (size_t)d);
+    double *P = (double *)malloc(sizeof(double) * (size_t)k * (size_t)B);
+    double *dP = (double *)malloc(sizeof(double) * (size_t)k * (size_t)B);
+    int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)k * (size_t)B);
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t p = pos[r];
+        int64_t nk = 0;
+        for (int i = 0; i < k; ++i) {
+            int32_t b = sel[r * k + i];
+            if (b < 0) continue;
+            for (int64_t j = (int64_t)b * B; j < ((int64_t)b + 1) * B && j <= p; ++j) key[nk++] = j;
+        }
+        for (int h = 0; h < G; ++h) {
+            const double *qq = q + (r * G + h) * d;
+            const double *go = dout + (r * G + h) * d;
+            double m = -INFINITY;
+            for (int64_t a = 0; a < nk; ++a) {
+                const double *kk = K + key[a] * d;
+                double s = 0.0;
+                for (int c = 0; c < d; ++c) s += qq[c] * kk[c];
+                P[a] = s * scale;
+                if (P[a] > m) m = P[a];
+            }
+            double l = 0.0;
+            for (int64_t a = 0; a < nk; ++a) { P[a] = exp(P[a] - m); l += P[a]; }
+            double D = 0.0;
+            for (int64_t a = 0; a < nk; ++a) {
+                P[a] /= l;
+                const double *vv = V + key[a] * d;
+                double t = 0.0;
+                for (int c = 0; c < d; ++c) t += go[c] * vv[c];
+                dP[a] = t;
+                D += P[a] * t;
+            }
+            double *gq = dq + (r * G + h) * d;
+            for (int64_t a = 0; a < nk; ++a) {
+                const double dS = P[a] * (dP[a] - D);
+                const double *kk = K + key[a] * d;
+                double *gk = dK + key[a] * d;
+                double *gv = dV + key[a] * d;
+                for (int c = 0; c < d; ++c) {
+                    gq[c] += scale * dS * kk[c];
+                    gk[c] += scale * dS * qq[c];
+                    gv[c] += P[a] * go[c];
+                }
+            }
+        }
+    }
+    free(P);
+    free(dP);
+    free(key);
+}
+
+/* KL alignment of the index branch, one row at a time.  scores are the block scores
+ * [nrows, nb] of orc_index_scores, mass the teacher [nrows, k] of orc_attention_train.
+ * Over the valid slots i of row r (sel >= 0):
+ *   pT_i = mass_i / sum mass,   pS_i = softmax_i(sigma * scores[r, sel[r][i]]),
+ *   loss[r] = sum_i pT_i (log pT_i - log pS_i)   (a term with pT_i = 0 is 0),
+ *   dscore[r,i] = d loss[r] / d scores[r, sel[r][i]] = sigma (pS_i - pT_i)  (teacher fixed);
+ * dscore is 0 for -1 slots. */
+void orc_index_kl(int64_t nb, int k, int64_t nrows, const double *scores, const int32_t *sel,
+                  const double *mass, double sigma, double *loss, double *dscore)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        double m = -INFINITY, tm = 0.0;
+        for (int i = 0; i < k; ++i) {
+            const int32_t b = sel[r * k + i];
+            if (b < 0) continue;
+            const double z = sigma * scores[r * nb + b];
+            if (z > m) m = z;
+            tm += mass[r * k + i];
+        }
+        double l = 0.0;
+        for (int i = 0; i < k; ++i) {
+            const int32_t b = sel[r * k + i];
+            if (b >= 0) l += exp(sigma * scores[r * nb + b] - m);
+        }
+        const double logl = log(l);
+        double L = 0.0;
+        for (int i = 0; i < k; ++i) {
+            const int32_t b = sel[r * k + i];
+            dscore[r * k + i] = 0.0;
+            if (b < 0) continue;
+            const double logpS = sigma * scores[r * nb + b] - m - logl;
+            const double pT = mass[r * k + i] / tm;
+            if (pT > 0.0) L += pT * (log(pT) - logpS);
+            dscore[r * k + i] = sigma * (exp(logpS) - pT);
+        }
+        loss[r] = L;
+    }
+}
+
+/* Index-branch input gradients through the causal block max-pool.  For each row r and
+ * valid slot i (block b = sel[r][i]): j* = the lowest position j in [bB, min((b+1)B-1,
+ * pos[r])] with the largest q_I[r] . k_I[j]; then dqI[r] += dscore[r,i] k_I[j*] and
+ * dKI[j*] += dscore[r,i] q_I[r].  qI is [nrows, dI], KI [N, dI]; dqI, dKI overwritten.
+ * Serial (the key gradients accumulate across rows). */
+void orc_index_backward(int64_t N, int B, int dI, int k, int64_t nrows, const double *qI,
+                        const int64_t *pos, const int32_t *sel, const double *KI,
+                        const double *dscore, double *dqI, double *dKI)
+{
+    memset(dqI, 0, sizeof(double) * (size_t)nrows * (size_t)dI);
+    memset(dKI, 0, sizeof(double) * (size_t)N * (size_t)dI);
+    for (int64_t r = 0; r < nrows; ++r) {
+        const double *qq = qI + r * dI;
+        for (int i = 0; i < k; ++i) {
+            const int32_t b = sel[r * k + i];
+            if (b < 0) continue;
+            int64_t best_j = -1;
+            double best = -INFINITY;
+            for (int64_t j = (int64_t)b * B; j < ((int64_t)b + 1) * B && j <= pos[r]; ++j) {
+                double s = 0.0;
+                for (int c = 0; c < dI; ++c) s += qq[c] * KI[j * dI + c];
+                if (best_j < 0 || s > best) { best = s; best_j = j; }
+            }
+            if (best_j < 0) continue;
+            const double g = dscore[r * k + i];
+            for (int c = 0; c < dI; ++c) {
+                dqI[r * dI + c] += g * KI[best_j * dI + c];
+                dKI[best_j * dI + c] += g * qq[c];
             }
         }
     }

@@ -297,3 +297,164 @@ def test_e4m3_table_matches_torch_float8():
 def test_decode_handles_e4m3_tensors():
     codes = torch.tensor([0x38, 0x7E, 0x81, 0x00], dtype=torch.uint8)
     np.testing.assert_array_equal(oracle.decode(codes.view(torch.float8_e4m3fn)), [1.0, 448.0, -2.0 ** -9, 0.0])
+
+
+# ------------------------------------------------------------------ training
+# "索引分支训练：KL 对齐" (the index branch is taught by the main branch's attention
+# distribution through a KL divergence, teacher cut from the gradient) and the MSA entry's
+# "KL loss ... teacher stop-gradient".  The gradients are pinned against torch autograd
+# in float64 on the dense masked formulation (a different route: autograd of the
+# brute-force mask-and-softmax, not the oracle's hand-derived chain rule) and against
+# finite differences of the oracle's own forward.
+def _mask(pos, sel, N, B):
+    blk = np.arange(N) // B
+    m = np.zeros((len(pos), N), dtype=bool)
+    for t in range(len(pos)):
+        m[t] = np.isin(blk, sel[t][sel[t] >= 0]) & (np.arange(N) <= pos[t])
+    return torch.from_numpy(m)
+
+
+def _train_case(N=70, T=33, G=3, d=8, B=8, k=3):
+    q, K, V = _rand_attn(N, T, G, d)
+    pos = _pos(N, T)
+    sel = oracle.slice_block_topk(RNG.standard_normal((T, (N + B - 1) // B)), pos // B, k)
+    return q, K, V, pos, sel
+
+
+def test_attention_train_lse_and_teacher_mass_match_brute_force():
+    N, B, scale = 70, 8, 0.41
+    q, K, V, pos, sel = _train_case(N=N, B=B)
+    out, lse, mass = oracle.slice_attention_train(q, pos, sel, K, V, B, scale)
+    np.testing.assert_allclose(out, oracle.slice_attention(q, pos, sel, K, V, B, scale), rtol=1e-12, atol=1e-13)
+    logits = np.einsum("tgd,nd->tgn", q, K) * scale
+    logits = np.where(_mask(pos, sel, N, B).numpy()[:, None, :], logits, -np.inf)
+    m = logits.max(axis=2)
+    ref_lse = m + np.log(np.exp(logits - m[..., None]).sum(axis=2))
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+    P = np.exp(logits - ref_lse[..., None])               # dense probabilities [T, G, N]
+    blk = np.arange(N) // B
+    for t in range(len(pos)):
+        for i, b in enumerate(sel[t]):
+            want = 0.0 if b < 0 else P[t][:, blk == b].sum() / q.shape[1]
+            assert abs(mass[t, i] - want) < 1e-12
+    np.testing.assert_allclose(mass.sum(axis=1), 1.0, rtol=1e-12)
+
+
+def test_attention_backward_matches_fp64_autograd():
+    N, B, scale = 70, 8, 0.37
+    q, K, V, pos, sel = _train_case(N=N, B=B)
+    dout = RNG.standard_normal(q.shape)
+    dq, dK, dV = oracle.slice_attention_backward(q, pos, sel, K, V, B, scale, dout)
+    tq, tK, tV = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, K, V))
+    logits = torch.einsum("tgd,nd->tgn", tq, tK) * scale
+    logits = logits.masked_fill(~_mask(pos, sel, N, B)[:, None, :], float("-inf"))
+    out = torch.einsum("tgn,nd->tgd", torch.softmax(logits, dim=2), tV)
+    (out * torch.from_numpy(dout)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dK, tK.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dV, tV.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_backward_finite_differences():
+    N, T, G, d, B, k, scale = 24, 10, 2, 4, 8, 2, 0.5
+    q, K, V, pos, sel = _train_case(N=N, T=T, G=G, d=d, B=B, k=k)
+    dout = RNG.standard_normal(q.shape)
+    dq, dK, dV = oracle.slice_attention_backward(q, pos, sel, K, V, B, scale, dout)
+
+    def f(q_, K_, V_):
+        return float((oracle.slice_attention(q_, pos, sel, K_, V_, B, scale) * dout).sum())
+    eps = 1e-6
+    for arr, grad, which in ((q, dq, 0), (K, dK, 1), (V, dV, 2)):
+        for idx in [tuple(RNG.integers(0, s) for s in arr.shape) for _ in range(6)]:
+            a, b = arr.copy(), arr.copy()
+            a[idx] += eps
+            b[idx] -= eps
+            args_a = [q, K, V]
+            args_b = [q, K, V]
+            args_a[which], args_b[which] = a, b
+            fd = (f(*args_a) - f(*args_b)) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(fd)), (which, idx, fd, grad[idx])
+
+
+def test_index_kl_closed_forms():
+    R, nb, k, sigma = 6, 9, 4, 0.7
+    scores = RNG.standard_normal((R, nb))
+    sel = np.array([np.sort(RNG.choice(nb, k, replace=False)) for _ in range(R)], dtype=np.int32)
+    sel[0, 2:] = -1                                          # a row with two valid slots
+    # teacher = student: zero loss, zero gradient
+    z = sigma * np.take_along_axis(scores, np.maximum(sel, 0), axis=1)
+    z = np.where(sel >= 0, z, -np.inf)
+    pS = np.exp(z - z.max(axis=1, keepdims=True))
+    pS /= pS.sum(axis=1, keepdims=True)
+    loss, ds = oracle.slice_index_kl(scores, sel, pS * 3.0, sigma)   # any positive scale of the teacher
+    np.testing.assert_allclose(loss, 0.0, atol=1e-12)
+    np.testing.assert_allclose(ds, 0.0, atol=1e-12)
+    # one-hot teacher: the loss is the student's negative log-probability of that block
+    onehot = np.zeros((R, k))
+    onehot[:, 1] = 1.0
+    loss, ds = oracle.slice_index_kl(scores, sel, onehot, sigma)
+    np.testing.assert_allclose(loss, -np.log(pS[:, 1]), rtol=1e-12)
+    np.testing.assert_allclose(ds[:, 1], sigma * (pS[:, 1] - 1.0), rtol=1e-12)
+    # equal scores: uniform student, loss = log(#valid) - entropy(teacher)
+    pT = RNG.random((R, k))
+    pT = np.where(sel >= 0, pT, 0.0)
+    loss, ds = oracle.slice_index_kl(np.zeros((R, nb)), sel, pT, sigma)
+    nv = (sel >= 0).sum(axis=1)
+    q_ = pT / pT.sum(axis=1, keepdims=True)
+    ent = -np.where(q_ > 0, q_ * np.log(np.where(q_ > 0, q_, 1.0)), 0.0).sum(axis=1)
+    np.testing.assert_allclose(loss, np.log(nv) - ent, rtol=1e-12)
+    np.testing.assert_allclose(ds.sum(axis=1), 0.0, atol=1e-12)   # probabilities on both sides sum to 1
+    assert np.all(ds[sel < 0] == 0.0)
+
+
+def test_index_kl_gradient_finite_differences():
+    R, nb, k, sigma = 5, 8, 4, 1.3
+    scores = RNG.standard_normal((R, nb))
+    sel = np.array([np.sort(RNG.choice(nb, k, replace=False)) for _ in range(R)], dtype=np.int32)
+    mass = RNG.random((R, k))
+    loss, ds = oracle.slice_index_kl(scores, sel, mass, sigma)
+    assert np.all(loss >= -1e-15)
+    eps = 1e-6
+    for r in range(R):
+        for i in range(k):
+            a, b = scores.copy(), scores.copy()
+            a[r, sel[r, i]] += eps
+            b[r, sel[r, i]] -= eps
+            fd = (oracle.slice_index_kl(a, sel, mass, sigma)[0][r] - oracle.slice_index_kl(b, sel, mass, sigma)[0][r])
+            assert abs(fd / (2 * eps) - ds[r, i]) < 1e-7
+
+
+def test_index_backward_matches_fp64_autograd_through_the_max_pool():
+    N, T, B, dI, k = 70, 33, 8, 5, 3
+    qI, KI = RNG.standard_normal((T, dI)), RNG.standard_normal((N, dI))
+    pos = _pos(N, T)
+    sel = oracle.slice_block_topk(RNG.standard_normal((T, (N + B - 1) // B)), pos // B, k)
+    dscore = RNG.standard_normal((T, k)) * (sel >= 0)
+    dq, dK = oracle.slice_index_backward(qI, pos, sel, KI, B, dscore)
+    tq = torch.tensor(qI, requires_grad=True)
+    tK = torch.tensor(KI, requires_grad=True)
+    nb = (N + B - 1) // B
+    s = tq @ tK.T                                            # [T, N] token scores
+    causal = torch.from_numpy(np.arange(N)[None, :] <= pos[:, None])
+    s = s.masked_fill(~causal, float("-inf"))
+    s = torch.nn.functional.pad(s, (0, nb * B - N), value=float("-inf")).view(T, nb, B)
+    blockscore = s.amax(dim=2)                               # [T, nb] (no ties in random data)
+    chosen = torch.from_numpy(np.maximum(sel, 0)).long()
+    picked = torch.gather(blockscore, 1, chosen)
+    (picked * torch.from_numpy(dscore)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dK, tK.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_index_backward_tie_goes_to_the_lowest_position():
+    N, B, dI = 16, 8, 3
+    KI = np.zeros((N, dI))
+    KI[:, 0] = 1.0                                           # every key scores the same
+    qI = np.array([[2.0, 0.0, 0.0]])
+    pos = np.array([N - 1])
+    sel = np.array([[0, 1]], dtype=np.int32)
+    dq, dK = oracle.slice_index_backward(qI, pos, sel, KI, B, np.array([[1.0, 0.5]]))
+    assert np.count_nonzero(dK.any(axis=1)) == 2
+    np.testing.assert_allclose(dK[0], [2.0, 0.0, 0.0])
+    np.testing.assert_allclose(dK[8], [1.0, 0.0, 0.0])
+    np.testing.assert_allclose(dq[0], [1.5, 0.0, 0.0])
