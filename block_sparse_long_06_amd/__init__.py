@@ -20,12 +20,13 @@ LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARGUMENT, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_DEVICE = range(5)
 MSA_F32, MSA_BF16, MSA_FP8_E4M3 = 0, 1, 2
-MSA_CALL_INVERT, MSA_CALL_PREFILL, MSA_CALL_DECODE = 2, 3, 4
+MSA_CALL_INVERT, MSA_CALL_PREFILL, MSA_CALL_DECODE, MSA_CALL_BACKWARD, MSA_CALL_INDEX_BACKWARD = 2, 3, 4, 5, 6
 
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_invert_selection", "msa_sparse_attn_prefill",
             "msa_sparse_attn_decode", "msa_workspace_bytes", "msa_status_string",
             "msa_last_error_message", "msa_profiler_enable", "msa_profiler_read", "msa_index_scores_kv",
-            "msa_block_topk_kv", "msa_sparse_attn_decode_kv")
+            "msa_block_topk_kv", "msa_sparse_attn_decode_kv", "msa_sparse_attn_prefill_train",
+            "msa_sparse_attn_backward", "msa_index_kl", "msa_index_backward")
 
 
 class MSAError(RuntimeError):
@@ -100,9 +101,14 @@ def lib():
         L.msa_index_scores_kv.argtypes = [PP, LP, P, P, P, P]
         L.msa_block_topk_kv.argtypes = [PP, LP, P, P, P]
         L.msa_sparse_attn_decode_kv.argtypes = [PP, LP, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_sparse_attn_prefill_train.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_sparse_attn_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_index_kl.argtypes = [PP, P, P, P, ctypes.c_float, P, P, P]
+        L.msa_index_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in ("msa_index_scores", "msa_block_topk", "msa_invert_selection",
                   "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_index_scores_kv",
-                  "msa_block_topk_kv", "msa_sparse_attn_decode_kv"):
+                  "msa_block_topk_kv", "msa_sparse_attn_decode_kv", "msa_sparse_attn_prefill_train",
+                  "msa_sparse_attn_backward", "msa_index_kl", "msa_index_backward"):
             getattr(L, f).restype = st
         L.msa_workspace_bytes.argtypes = [PP, ctypes.c_int]
         L.msa_workspace_bytes.restype = ctypes.c_size_t
@@ -206,6 +212,32 @@ def sparse_attn_decode_kv(prob: Problem, layout: KVLayout, q, k_cache, v_cache, 
                                            workspace_bytes_, _stream(stream, q)))
 
 
+def sparse_attn_prefill_train(prob: Problem, q, k, v, csr_offsets, csr_entries, sel, out, lse, block_mass,
+                              workspace, workspace_bytes_: int, stream=None) -> None:
+    _check(lib().msa_sparse_attn_prefill_train(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(csr_offsets),
+                                               _ptr(csr_entries), _ptr(sel), _ptr(out), _ptr(lse), _ptr(block_mass),
+                                               _ptr(workspace), workspace_bytes_, _stream(stream, q)))
+
+
+def sparse_attn_backward(prob: Problem, q, k, v, out, dout, lse, csr_offsets, csr_entries, dq, dk, dv, workspace,
+                         workspace_bytes_: int, stream=None) -> None:
+    _check(lib().msa_sparse_attn_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                          _ptr(lse), _ptr(csr_offsets), _ptr(csr_entries), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), _ptr(workspace), workspace_bytes_, _stream(stream, q)))
+
+
+def index_kl(prob: Problem, scores, sel, block_mass, sigma: float, loss, dscores, stream=None) -> None:
+    _check(lib().msa_index_kl(ctypes.byref(prob), _ptr(scores), _ptr(sel), _ptr(block_mass), float(sigma),
+                              _ptr(loss), _ptr(dscores), _stream(stream, scores)))
+
+
+def index_backward(prob: Problem, q_idx, k_idx, csr_offsets, csr_entries, dscores, dq_idx, dk_idx, argmax,
+                   workspace, workspace_bytes_: int, stream=None) -> None:
+    _check(lib().msa_index_backward(ctypes.byref(prob), _ptr(q_idx), _ptr(k_idx), _ptr(csr_offsets),
+                                    _ptr(csr_entries), _ptr(dscores), _ptr(dq_idx), _ptr(dk_idx), _ptr(argmax),
+                                    _ptr(workspace), workspace_bytes_, _stream(stream, q_idx)))
+
+
 def profiler_enable(on: bool) -> None:
     _check(lib().msa_profiler_enable(1 if on else 0))
 
@@ -293,3 +325,57 @@ def run_decode_kv(prob: Problem, layout: KVLayout, q, k_cache, v_cache, q_idx, k
     block_topk_kv(prob, layout, bufs.scores, bufs.sel, stream)
     sparse_attn_decode_kv(prob, layout, q, k_cache, v_cache, bufs.sel, bufs.out, bufs.ws_decode,
                           bufs.ws_decode.numel(), stream)
+
+
+@dataclass
+class TrainBuffers:
+    """Outputs and workspaces of one training step (forward with lse and teacher, main-branch
+    backward, index KL and index backward)."""
+    fwd: PrefillBuffers
+    lse: object
+    mass: object
+    dq: object
+    dk: object
+    dv: object
+    ws_bwd: object
+    loss: object
+    dscores: object
+    dq_idx: object
+    dk_idx: object
+    argmax: object
+    ws_ibwd: object
+
+
+def alloc_train(prob: Problem, device="cuda") -> TrainBuffers:
+    import torch
+    S, T, N, H, Hkv, d, dI, k = (prob.batch, prob.num_q, prob.kv_len, prob.num_heads, prob.num_kv_heads,
+                                 prob.head_dim, prob.index_dim, prob.topk)
+    f32 = dict(dtype=torch.float32, device=device)
+    return TrainBuffers(
+        fwd=alloc_prefill(prob, device),
+        lse=torch.empty((S, T, H), **f32), mass=torch.empty((S, Hkv, T, k), **f32),
+        dq=torch.empty((S, T, H, d), **f32), dk=torch.empty((S, Hkv, N, d), **f32),
+        dv=torch.empty((S, Hkv, N, d), **f32),
+        ws_bwd=torch.empty((max(workspace_bytes(prob, MSA_CALL_BACKWARD), 1),), dtype=torch.uint8, device=device),
+        loss=torch.empty((S, Hkv, T), **f32), dscores=torch.empty((S, Hkv, T, k), **f32),
+        dq_idx=torch.empty((S, Hkv, T, dI), **f32), dk_idx=torch.empty((S, Hkv, N, dI), **f32),
+        argmax=torch.full((S, Hkv, T, k), -1, dtype=torch.int32, device=device),
+        ws_ibwd=torch.empty((max(workspace_bytes(prob, MSA_CALL_INDEX_BACKWARD), 1),), dtype=torch.uint8,
+                            device=device))
+
+
+def run_train_step(prob: Problem, q, k, v, q_idx, k_idx, dout, bufs: TrainBuffers, sigma: float = 0.0,
+                   stream=None) -> None:
+    """Forward (scores, top-k, inversion, attention with lse and teacher), then the main-branch
+    backward for the upstream gradient dout, the index KL and the index-branch backward."""
+    f = bufs.fwd
+    index_scores(prob, q_idx, k_idx, f.scores, stream)
+    block_topk(prob, f.scores, f.sel, stream)
+    invert_selection(prob, f.sel, f.csr_offsets, f.csr_entries, f.ws_invert, f.ws_invert.numel(), stream)
+    sparse_attn_prefill_train(prob, q, k, v, f.csr_offsets, f.csr_entries, f.sel, f.out, bufs.lse, bufs.mass,
+                              f.ws_prefill, f.ws_prefill.numel(), stream)
+    sparse_attn_backward(prob, q, k, v, f.out, dout, bufs.lse, f.csr_offsets, f.csr_entries, bufs.dq, bufs.dk,
+                         bufs.dv, bufs.ws_bwd, bufs.ws_bwd.numel(), stream)
+    index_kl(prob, f.scores, f.sel, bufs.mass, sigma, bufs.loss, bufs.dscores, stream)
+    index_backward(prob, q_idx, k_idx, f.csr_offsets, f.csr_entries, bufs.dscores, bufs.dq_idx, bufs.dk_idx,
+                   bufs.argmax, bufs.ws_ibwd, bufs.ws_ibwd.numel(), stream)

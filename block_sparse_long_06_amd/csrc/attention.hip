@@ -222,7 +222,8 @@ template <typename T, typename PT>
 __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* __restrict__ sel,
                                                         const float* __restrict__ part_lse,
                                                         const PT* __restrict__ part_o,
-                                                        const uint64_t* __restrict__ hotmask, T* __restrict__ out) {
+                                                        const uint64_t* __restrict__ hotmask, T* __restrict__ out,
+                                                        float* __restrict__ lse_out, float* __restrict__ mass_out) {
   __shared__ float wbuf[4][kMergeMaxKG];
   __shared__ float hstat[4][2][16];
   const int lane = threadIdx.x & 63;
@@ -266,6 +267,15 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* _
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // training outputs: the row's log-sum-exp per head, and per slot the share of the
+  // attention that falls on that block, averaged over the group's heads
+  if (lse_out != nullptr && lane < G)
+    lse_out[((int64_t)s * D.T + t) * D.H + g * G + lane] = hstat[wave][0][lane] - __logf(hstat[wave][1][lane]);
+  if (mass_out != nullptr && lane < D.k) {
+    float mw = 0.0f;
+    for (int hh = 0; hh < G; ++hh) mw += wb[lane * G + hh];
+    mass_out[(((int64_t)s * D.Hkv + g) * D.T + t) * D.k + lane] = mw / (float)G;
+  }
   for (int c8 = lane; c8 * 8 < GD; c8 += 64) {
     const int hh = c8 * 8 / D.d;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -473,14 +483,15 @@ hipError_t launch_decode_t(const Dims& D, const void* q, const void* k, const vo
 
 hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part_lse, const void* part_o,
                             int part_o_is_bf16, const uint64_t* hotmask, void* out, hipStream_t st,
-                            const char* name) {
+                            const char* name, float* lse_out, float* mass_out) {
   const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
   const dim3 grid((unsigned)((rows + 3) / 4));
   LaunchScope scope(name, st);
   const int gd = D.G * D.d;
   const uint16_t* pb = static_cast<const uint16_t*>(part_o);
   uint16_t* ob = static_cast<uint16_t*>(out);
-  if (D.dtype == MSA_BF16 && part_o_is_bf16 && D.k <= 16 && (gd == 512 || gd == 1024)) {
+  const bool train = lse_out != nullptr || mass_out != nullptr;
+  if (!train && D.dtype == MSA_BF16 && part_o_is_bf16 && D.k <= 16 && (gd == 512 || gd == 1024)) {
     if (gd == 1024 && hotmask)
       hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 2, true>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
                          hotmask, ob);
@@ -496,14 +507,51 @@ hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part
   } else if (D.dtype == MSA_BF16) {
     if (part_o_is_bf16)
       hipLaunchKernelGGL((lse_merge_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
-                         hotmask, ob);
+                         hotmask, ob, lse_out, mass_out);
     else
       hipLaunchKernelGGL((lse_merge_kernel<uint16_t, float>), grid, dim3(256), 0, st, D, sel, part_lse,
-                         static_cast<const float*>(part_o), hotmask, ob);
+                         static_cast<const float*>(part_o), hotmask, ob, lse_out, mass_out);
   } else {
     hipLaunchKernelGGL((lse_merge_kernel<float, float>), grid, dim3(256), 0, st, D, sel, part_lse,
-                       static_cast<const float*>(part_o), hotmask, static_cast<float*>(out));
+                       static_cast<const float*>(part_o), hotmask, static_cast<float*>(out), lse_out, mass_out);
   }
+  return hipGetLastError();
+}
+
+WorkList work_list_layout(const Dims& D, int R, void* base, size_t* total) {
+  const int64_t nsgb = (int64_t)D.S * D.Hkv * D.nb;
+  const int64_t npart = (int64_t)D.S * D.T * D.Hkv * D.k;
+  WorkList w;
+  w.ub = nsgb + (npart + R - 1) / R;
+  unsigned char* p = static_cast<unsigned char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    void* r = p ? p + off : nullptr;
+    off += align_up(bytes, 256);
+    return r;
+  };
+  w.items = static_cast<int*>(take(nsgb * sizeof(int)));
+  w.itempos = static_cast<int*>(take(nsgb * sizeof(int)));
+  w.n_items = static_cast<int*>(take(sizeof(int)));
+  w.scan_ws = take(scan_workspace_bytes(nsgb));
+  w.wl = static_cast<int4*>(take(w.ub * sizeof(int4)));
+  *total = off;
+  return w;
+}
+
+hipError_t launch_work_list(const Dims& D, const int32_t* off, int R, const WorkList& w, hipStream_t st) {
+  const int64_t nsgb = (int64_t)D.S * D.Hkv * D.nb;
+  const unsigned g256 = (unsigned)((nsgb + 255) / 256);
+  {
+    LaunchScope s("wl_count", st);
+    hipLaunchKernelGGL(wl_count, dim3(g256), dim3(256), 0, st, D, off, w.items, R);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_exclusive_scan(w.items, w.itempos, nsgb, w.n_items, w.scan_ws, st);
+  if (e != hipSuccess) return e;
+  LaunchScope s("wl_emit", st);
+  hipLaunchKernelGGL(wl_emit, dim3(g256), dim3(256), 0, st, D, off, w.items, w.itempos, w.wl, R);
   return hipGetLastError();
 }
 
@@ -514,14 +562,16 @@ size_t prefill_workspace_bytes(const Dims& D) {
 }
 
 hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const void* v, const int32_t* off,
-                          const int32_t* entries, const int32_t* sel, void* out, void* ws, hipStream_t st) {
+                          const int32_t* entries, const int32_t* sel, void* out, void* ws, hipStream_t st,
+                          float* lse_out, float* mass_out) {
   size_t total = 0;
   const PrefillWs w = prefill_layout(D, ws, &total);
   const int64_t nsgb = (int64_t)D.S * D.Hkv * D.nb;
   const int R = rows_per_item(D);
   const unsigned g256 = (unsigned)((nsgb + 255) / 256);
   hipError_t e;
-  const bool hot = w.has_hot && hot_tiles_enabled();
+  // the training outputs need one partial per (row, slot): no query-tile pass then
+  const bool hot = w.has_hot && hot_tiles_enabled() && lse_out == nullptr && mass_out == nullptr;
   if (hot) {  // Outer-Gather-Q then takes only the cold part of the CSR
     e = launch_hot_split(D, sel, off, entries, w.hs, st);
     if (e != hipSuccess) return e;
@@ -557,7 +607,7 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
     if (e != hipSuccess) return e;
   }
   return launch_lse_merge(D, sel, w.part_lse, w.part_o, D.dtype == MSA_BF16, hot ? w.hs.hotmask : nullptr, out,
-                          st, "lse_merge");
+                          st, "lse_merge", lse_out, mass_out);
 }
 
 // Decode workspace: partial lse / O per (s, t, g, slot, head), plus (bf16 path) the

@@ -1,0 +1,559 @@
+// backward.hip -- the training path of MSA on gfx950.
+//
+// Page "MSA 稀疏注意力三国杀：NSA / DSA / MoBA / MSA 四方案深度对比", section 索引分支训练：
+// KL 对齐 (the index branch is taught by the main branch's attention distribution through
+// a KL divergence; the training signal reaches only the index branch), and the MSA entry of
+// "稀疏注意力速览（Sparse Attention，2019 ~ 2026）" (KL loss, teacher stop-gradient).
+//
+//  * attn_bwd: gradients of the block-sparse main branch (dQ, dK, dV) in the Outer-Gather-Q
+//    order of section Kernel 创新：Outer Gather Q: one work item = (sequence, group, KV
+//    block) and up to kRows rows of its inverted list; the block's K, V and K^T are staged
+//    once and every gathered row is processed against them.  Each of the 4 waves owns 32
+//    keys.  Per sub-chunk of 32 M-rows (M-row = (row, head)):
+//        S = Q K^T and dP = dO V^T          (v_mfma_f32_32x32x16_bf16; lane = key,
+//                                              registers = M-rows)
+//        P = exp2(S scale log2e - lse log2e),  dS = P (dP - D)      (D = rowsum(dO o O))
+//        dV^T += dO^T P,  dK^T += Q^T dS    (the P / dS registers are the B operands: their
+//                                              M-row order is the accumulator's; dO^T and
+//                                              Q^T are stored in LDS in that order)
+//        dQ = dS K                          (dS through LDS, wave w takes head dims
+//                                              [32w, 32w+32); K^T in LDS is the B operand)
+//    dQ goes to the fp32 output with hardware float atomics (a row's k slots are
+//    different items); dK, dV are accumulated in registers over the item's rows and added
+//    once per item (a block's list can span several items).
+//  * index_kl: per row, KL(teacher || student) over the selected blocks and its gradient
+//    with respect to the block scores (teacher = the forward's block masses).
+//  * index_bwd: the gradient of the block scores through the causal max-pool: per (row,
+//    selected block) the arg-max key (lowest position among equal maxima, scores in fp32
+//    summed in index order) takes dscore * q_I, and the row takes dscore * k_I[j*].
+#include "msa_internal.hpp"
+
+namespace msa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBlk = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRows = 256;  // query rows per work item
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+// Column of M-row m in the transposed Q / dO buffers: the 8 M-rows one lane half feeds
+// to a k-step (16p + 4h + {0..3}, 16p + 8 + 4h + {0..3}) are stored contiguously.
+__device__ __forceinline__ int mrow_col(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// M-row held by accumulator register r of lane half h (32x32 output layout).
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+template <int DH>
+struct __attribute__((aligned(16))) BwdLds {
+  static constexpr int KROW = DH * 2 + 16;    // K / V row-major, bytes
+  static constexpr int KTROW = kBlk * 2 + 16; // K^T row (one head dim over the block's keys)
+  static constexpr int QROW = DH * 2 + 16;    // Q / dO row-major (32 M-rows)
+  static constexpr int TROW = 32 * 2 + 16;    // Q^T / dO^T row (one head dim over 32 M-rows)
+  static constexpr int SROW = kBlk * 2 + 16;  // dS row (one M-row over the block's keys)
+  __attribute__((aligned(16))) unsigned char kr[kBlk * KROW];
+  __attribute__((aligned(16))) unsigned char vr[kBlk * KROW];
+  __attribute__((aligned(16))) unsigned char kt[DH * KTROW];
+  __attribute__((aligned(16))) unsigned char qs[32 * QROW];
+  __attribute__((aligned(16))) unsigned char dos[32 * QROW];
+  __attribute__((aligned(16))) unsigned char qt[DH * TROW];
+  __attribute__((aligned(16))) unsigned char dot[DH * TROW];
+  __attribute__((aligned(16))) unsigned char ds[32 * SROW];
+  float lse2[32];      // lse * log2(e); +inf for an M-row past the item's rows
+  float drow[32];
+  int pos[32];
+  int64_t dqoff[32];   // element offset of the M-row's dQ row; -1 if none
+};
+
+// D[s, t, h] = sum_c dO[s, t, h, c] O[s, t, h, c] (fp32), 16 lanes per row.
+template <int DH>
+__global__ void __launch_bounds__(256) drow_kernel(int64_t rows, const uint16_t* __restrict__ out,
+                                                   const uint16_t* __restrict__ dout, float* __restrict__ drow) {
+  const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  float acc = 0.0f;
+  if (r < rows) {
+    for (int c = sub * 8; c < DH; c += 128) {
+      const uint4 a = *reinterpret_cast<const uint4*>(out + r * DH + c);
+      const uint4 b = *reinterpret_cast<const uint4*>(dout + r * DH + c);
+      const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(bf16_to_f32((uint16_t)(wa[i] & 0xFFFFu)), bf16_to_f32((uint16_t)(wb[i] & 0xFFFFu)), acc);
+        acc = fmaf(bf16_to_f32((uint16_t)(wa[i] >> 16)), bf16_to_f32((uint16_t)(wb[i] >> 16)), acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (r < rows && sub == 0) drow[r] = acc;
+}
+
+__global__ void __launch_bounds__(256) zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+
+template <int DH, int G>
+__global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* __restrict__ q,
+                                                        const uint16_t* __restrict__ k,
+                                                        const uint16_t* __restrict__ v,
+                                                        const uint16_t* __restrict__ dout,
+                                                        const float* __restrict__ lse,
+                                                        const float* __restrict__ drow,
+                                                        const int4* __restrict__ wl, const int* __restrict__ n_items,
+                                                        const int32_t* __restrict__ entries,
+                                                        float* __restrict__ dq, float* __restrict__ dk,
+                                                        float* __restrict__ dv) {
+  using L_ = BwdLds<DH>;
+  constexpr int KS = DH / 16;  // k-steps over the head dims
+  constexpr int DT = DH / 32;  // head-dim tiles
+  constexpr int CPR = DH / 8;  // 16-byte pieces per row
+  __shared__ L_ L;
+
+  // XCD-aware order: consecutive items (same KV block) in one XCD's L2
+  const int n = *n_items;
+  const int per_xcd = (n + 7) / 8;
+  const int slot_in_xcd = blockIdx.x >> 3;
+  const int item = (blockIdx.x & 7) * per_xcd + slot_in_xcd;
+  if (slot_in_xcd >= per_xcd || item >= n) return;
+  const int4 w = wl[item];
+  if (w.z <= 0) return;
+  const int64_t sg = w.x / D.nb;
+  const int b = w.x % D.nb;
+  const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
+  const int j0 = b * kBlk;
+  const int nvalid = min(kBlk, D.N - j0);
+  const int rows = w.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, nl = lane & 31;
+  const float sc = D.scale * kLog2e;
+
+  // ---- stage K, V (row-major) and K^T (head dim major, keys in order)
+  {
+    const uint16_t* kb = k + (sg * D.N + j0) * DH;
+    const uint16_t* vb = v + (sg * D.N + j0) * DH;
+    for (int c = threadIdx.x; c < kBlk * CPR; c += kThreads) {
+      const int row = c / CPR, col = c % CPR;
+      const bool ok = row < nvalid;
+      const uint4 kk = ok ? *reinterpret_cast<const uint4*>(kb + row * DH + col * 8) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 vv = ok ? *reinterpret_cast<const uint4*>(vb + row * DH + col * 8) : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&L.kr[row * L_::KROW + col * 16]) = kk;
+      *reinterpret_cast<uint4*>(&L.vr[row * L_::KROW + col * 16]) = vv;
+    }
+    // K^T: thread = (4 consecutive keys, 8 consecutive head dims), a 4 x 8 transpose
+    for (int c = threadIdx.x; c < (kBlk / 4) * CPR; c += kThreads) {
+      const int kg = c % (kBlk / 4), dc = c / (kBlk / 4);
+      uint32_t wv[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 4 * kg + i;
+        const uint4 x = key < nvalid ? *reinterpret_cast<const uint4*>(kb + key * DH + dc * 8)
+                                     : make_uint4(0u, 0u, 0u, 0u);
+        wv[i][0] = x.x; wv[i][1] = x.y; wv[i][2] = x.z; wv[i][3] = x.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        uint2 o;
+        o.x = ((wv[0][e >> 1] >> sh) & 0xFFFFu) | (((wv[1][e >> 1] >> sh) & 0xFFFFu) << 16);
+        o.y = ((wv[2][e >> 1] >> sh) & 0xFFFFu) | (((wv[3][e >> 1] >> sh) & 0xFFFFu) << 16);
+        *reinterpret_cast<uint2*>(&L.kt[(dc * 8 + e) * L_::KTROW + kg * 8]) = o;
+      }
+    }
+  }
+
+  f32x16 dkt[DT], dvt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dkt[dt] = f32x16{};
+    dvt[dt] = f32x16{};
+  }
+  const int mrows = rows * G;
+  const int first_pos = D.pos0 + entries[w.y] / D.k;  // rows ascend: the smallest position
+  const bool need_mask = first_pos < j0 + kBlk - 1;
+  const int key = j0 + 32 * wave + nl;                // this lane's key
+
+  for (int m0 = 0; m0 < mrows; m0 += 32) {
+    __syncthreads();  // previous sub-chunk's buffers are free (and the staging is complete)
+    // ---- gather Q and dO of 32 M-rows: row-major and transposed copies
+    for (int c = threadIdx.x; c < 32 * CPR; c += kThreads) {
+      const int m = c / CPR, col = c % CPR;
+      const int mr = m0 + m;
+      uint4 qq = make_uint4(0u, 0u, 0u, 0u), gg = make_uint4(0u, 0u, 0u, 0u);
+      if (mr < mrows) {
+        const int e = entries[w.y + mr / G];
+        const int t = e / D.k;
+        const int64_t off = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mr % G) * DH + col * 8;
+        qq = *reinterpret_cast<const uint4*>(q + off);
+        gg = *reinterpret_cast<const uint4*>(dout + off);
+      }
+      *reinterpret_cast<uint4*>(&L.qs[m * L_::QROW + col * 16]) = qq;
+      *reinterpret_cast<uint4*>(&L.dos[m * L_::QROW + col * 16]) = gg;
+      const uint32_t wq[4] = {qq.x, qq.y, qq.z, qq.w}, wg[4] = {gg.x, gg.y, gg.z, gg.w};
+      const int mc = mrow_col(m);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        *reinterpret_cast<uint16_t*>(&L.qt[(col * 8 + e) * L_::TROW + mc * 2]) = (uint16_t)(wq[e >> 1] >> sh);
+        *reinterpret_cast<uint16_t*>(&L.dot[(col * 8 + e) * L_::TROW + mc * 2]) = (uint16_t)(wg[e >> 1] >> sh);
+      }
+    }
+    if (threadIdx.x < 32) {
+      const int m = threadIdx.x, mr = m0 + m;
+      if (mr < mrows) {
+        const int t = entries[w.y + mr / G] / D.k;
+        const int64_t hr = ((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mr % G;
+        L.lse2[m] = lse[hr] * kLog2e;
+        L.drow[m] = drow[hr];
+        L.pos[m] = D.pos0 + t;
+        L.dqoff[m] = hr * DH;
+      } else {
+        L.lse2[m] = INFINITY;  // P = 0 for an M-row past the list
+        L.drow[m] = 0.0f;
+        L.pos[m] = -1;
+        L.dqoff[m] = -1;
+      }
+    }
+    __syncthreads();
+
+    // ---- S = Q K^T and dP = dO V^T for this wave's 32 keys
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&L.qs[nl * L_::QROW + (16 * ks + 8 * h) * 2]);
+      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&L.kr[(32 * wave + nl) * L_::KROW + (16 * ks + 8 * h) * 2]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
+      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&L.dos[nl * L_::QROW + (16 * ks + 8 * h) * 2]);
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&L.vr[(32 * wave + nl) * L_::KROW + (16 * ks + 8 * h) * 2]);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, bv, pacc, 0, 0, 0);
+    }
+    // ---- P, dS (registers r hold M-rows acc_row(r, h) of this lane's key)
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = acc_row(r, h);
+      float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], sc, -L.lse2[m]));
+      if (need_mask && key > L.pos[m]) p = 0.0f;
+      pv[r] = p;
+      dsv[r] = p * (pacc[r] - L.drow[m]);
+    }
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      uint32_t wp[4], wsd[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        wp[x] = cvt_bf16x2(pv[8 * pp + 2 * x], pv[8 * pp + 2 * x + 1]);
+        wsd[x] = cvt_bf16x2(dsv[8 * pp + 2 * x], dsv[8 * pp + 2 * x + 1]);
+      }
+      pb[pp] = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
+      sb[pp] = __builtin_bit_cast(bf16x8, make_uint4(wsd[0], wsd[1], wsd[2], wsd[3]));
+    }
+    // ---- dV^T += dO^T P, dK^T += Q^T dS (k-step pp = M-rows of register group pp)
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&L.dot[(32 * dt + nl) * L_::TROW + (16 * pp + 8 * h) * 2]);
+        dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pb[pp], dvt[dt], 0, 0, 0);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&L.qt[(32 * dt + nl) * L_::TROW + (16 * pp + 8 * h) * 2]);
+        dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[pp], dkt[dt], 0, 0, 0);
+      }
+    }
+    // ---- dS to LDS (M-row major) for dQ
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      *reinterpret_cast<uint16_t*>(&L.ds[acc_row(r, h) * L_::SROW + (32 * wave + nl) * 2]) =
+          (uint16_t)(cvt_bf16x2(dsv[r], 0.0f) & 0xFFFFu);
+    __syncthreads();
+    // ---- dQ = scale * dS K for head dims [32 wave, 32 wave + 32)
+    if (wave < DT) {
+      f32x16 qacc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < kBlk / 16; ++ks) {
+        const bf16x8 as = *reinterpret_cast<const bf16x8*>(&L.ds[nl * L_::SROW + (16 * ks + 8 * h) * 2]);
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&L.kt[(32 * wave + nl) * L_::KTROW + (16 * ks + 8 * h) * 2]);
+        qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bk, qacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t o = L.dqoff[acc_row(r, h)];
+        if (o >= 0) unsafeAtomicAdd(dq + o + 32 * wave + nl, qacc[r] * D.scale);
+      }
+    }
+  }
+
+  // ---- dK, dV of the block: through LDS (row-major fp32 over the K / V staging area) so
+  // that the atomic adds of a wave cover contiguous head dims
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(L.kr);  // kBlk x DH fp32 fits K + V staging
+  static_assert(sizeof(float) * kBlk * DH <= 2 * kBlk * BwdLds<DH>::KROW, "reduction buffer fits");
+  for (int which = 0; which < 2; ++which) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float val = which == 0 ? dkt[dt][r] * D.scale : dvt[dt][r];
+        red[(32 * wave + nl) * DH + 32 * dt + acc_row(r, h)] = val;
+      }
+    __syncthreads();
+    float* dst = (which == 0 ? dk : dv) + (sg * D.N + j0) * DH;
+    for (int i = threadIdx.x; i < nvalid * DH; i += kThreads) unsafeAtomicAdd(dst + i, red[i]);
+    __syncthreads();
+  }
+}
+
+// Per row: KL(teacher || student) over the selected blocks and d loss / d block score.
+__global__ void __launch_bounds__(256) index_kl_kernel(Dims D, const float* __restrict__ scores,
+                                                       const int32_t* __restrict__ sel,
+                                                       const float* __restrict__ mass, float sigma,
+                                                       float* __restrict__ loss, float* __restrict__ dscore) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (s, g, t)
+  if (row >= (int64_t)D.S * D.Hkv * D.T) return;
+  const int32_t* sl = sel + row * D.k;
+  const float* ms = mass + row * D.k;
+  const float* sc = scores + row * (int64_t)D.nb;
+  float mx = -INFINITY, tm = 0.0f;
+  for (int i = 0; i < D.k; ++i) {
+    const int b = sl[i];
+    if (b < 0 || b >= D.nb) continue;
+    mx = fmaxf(mx, sigma * sc[b]);
+    tm += ms[i];
+  }
+  float l = 0.0f;
+  for (int i = 0; i < D.k; ++i) {
+    const int b = sl[i];
+    if (b >= 0 && b < D.nb) l += expf(sigma * sc[b] - mx);
+  }
+  const float logl = logf(l);
+  float L = 0.0f;
+  for (int i = 0; i < D.k; ++i) {
+    const int b = sl[i];
+    float gsc = 0.0f;
+    if (b >= 0 && b < D.nb) {
+      const float logps = sigma * sc[b] - mx - logl;
+      const float pt = tm > 0.0f ? ms[i] / tm : 0.0f;
+      if (pt > 0.0f) L += pt * (logf(pt) - logps);
+      gsc = sigma * (expf(logps) - pt);
+    }
+    dscore[row * D.k + i] = gsc;
+  }
+  loss[row] = L;
+}
+
+// Index keys of one block in LDS as fp32 (row pad of one float: conflict-free lane-per-key
+// reads), plus the block's key-gradient accumulator.
+template <int DI>
+struct IdxBwdLds {
+  float kf[kBlk][DI + 1];
+  float dk[kBlk][DI + 1];
+  float qrow[kWaves][DI];
+};
+
+template <int DI>
+__global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __restrict__ q_idx,
+                                                      const uint16_t* __restrict__ k_idx,
+                                                      const int4* __restrict__ wl, const int* __restrict__ n_items,
+                                                      const int32_t* __restrict__ entries,
+                                                      const float* __restrict__ dscore, float* __restrict__ dq_idx,
+                                                      float* __restrict__ dk_idx, int32_t* __restrict__ argmax) {
+  __shared__ IdxBwdLds<DI> L;
+  const int n = *n_items;
+  const int per_xcd = (n + 7) / 8;
+  const int slot_in_xcd = blockIdx.x >> 3;
+  const int item = (blockIdx.x & 7) * per_xcd + slot_in_xcd;
+  if (slot_in_xcd >= per_xcd || item >= n) return;
+  const int4 w = wl[item];
+  if (w.z <= 0) return;
+  const int64_t sg = w.x / D.nb;
+  const int b = w.x % D.nb;
+  const int j0 = b * kBlk;
+  const int nvalid = min(kBlk, D.N - j0);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint16_t* kb = k_idx + (sg * D.N + j0) * DI;
+  for (int i = threadIdx.x; i < kBlk * DI; i += kThreads) {
+    const int key = i / DI, c = i % DI;
+    L.kf[key][c] = key < nvalid ? bf16_to_f32(kb[i]) : 0.0f;
+    L.dk[key][c] = 0.0f;
+  }
+  __syncthreads();
+  for (int r = wave; r < w.z; r += kWaves) {
+    const int e = entries[w.y + r];
+    const int t = e / D.k, slot = e - t * D.k;
+    const int p = D.pos0 + t;
+    const int64_t qr = sg * D.T + t;  // (s, g, t)
+    for (int c = lane; c < DI; c += 64) L.qrow[wave][c] = bf16_to_f32(q_idx[qr * DI + c]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // scores of keys lane and lane + 64, summed in index order
+    float s0 = 0.0f, s1 = 0.0f;
+    for (int c = 0; c < DI; ++c) {
+      const float qc = L.qrow[wave][c];
+      s0 = fmaf(qc, L.kf[lane][c], s0);
+      s1 = fmaf(qc, L.kf[lane + 64][c], s1);
+    }
+    const bool v0 = lane < nvalid && j0 + lane <= p;
+    const bool v1 = lane + 64 < nvalid && j0 + lane + 64 <= p;
+    if (!v0) s0 = -INFINITY;
+    if (!v1) s1 = -INFINITY;
+    const float best = wave_max(fmaxf(s0, s1));
+    // lowest position holding the maximum
+    const uint64_t m0 = __ballot(v0 && s0 == best), m1 = __ballot(v1 && s1 == best);
+    // (no key holds the maximum only for NaN scores: then the row takes no update)
+    const int js = m0 != 0ull ? __builtin_ctzll(m0) : (m1 != 0ull ? 64 + __builtin_ctzll(m1) : -1);
+    const float gsc = dscore[qr * D.k + slot];
+    if (lane == 0 && argmax != nullptr) argmax[qr * D.k + slot] = js >= 0 ? j0 + js : -1;
+    for (int c = lane; js >= 0 && c < DI; c += 64) {
+      unsafeAtomicAdd(dq_idx + qr * DI + c, gsc * L.kf[js][c]);
+      atomicAdd(&L.dk[js][c], gsc * L.qrow[wave][c]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  __syncthreads();
+  float* dst = dk_idx + (sg * D.N + j0) * DI;
+  for (int i = threadIdx.x; i < nvalid * DI; i += kThreads) {
+    const float x = L.dk[i / DI][i % DI];
+    if (x != 0.0f) unsafeAtomicAdd(dst + i, x);
+  }
+}
+
+struct BwdWs {
+  WorkList wlst;
+  float* drow;
+};
+
+BwdWs backward_layout(const Dims& D, void* base, size_t* total) {
+  BwdWs w;
+  size_t wlb = 0;
+  (void)work_list_layout(D, kRows, nullptr, &wlb);
+  unsigned char* p = static_cast<unsigned char*>(base);
+  w.wlst = work_list_layout(D, kRows, p, &wlb);
+  size_t off = align_up(wlb, 256);
+  w.drow = p ? reinterpret_cast<float*>(p + off) : nullptr;
+  off += align_up((size_t)D.S * D.T * D.H * sizeof(float), 256);
+  *total = off;
+  return w;
+}
+
+hipError_t zero(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+template <int DH, int G>
+void launch_bwd_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                  const float* lse, const float* drow, const WorkList& wl, const int32_t* entries, float* dq,
+                  float* dk, float* dv, hipStream_t st) {
+  const int64_t grid = (wl.ub + 7) / 8 * 8 + 8;
+  hipLaunchKernelGGL((attn_bwd<DH, G>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, dout, lse, drow,
+                     wl.wl, wl.n_items, entries, dq, dk, dv);
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(const Dims& D) {
+  size_t total = 0;
+  (void)backward_layout(D, nullptr, &total);
+  return total;
+}
+
+hipError_t launch_attn_backward(const Dims& D, const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, const int32_t* off, const int32_t* entries,
+                                float* dq, float* dk, float* dv, void* ws, hipStream_t st) {
+  size_t total = 0;
+  const BwdWs w = backward_layout(D, ws, &total);
+  hipError_t e;
+  {
+    LaunchScope scope("bwd_zero", st);
+    e = zero(dq, (int64_t)D.S * D.T * D.H * D.d, st);
+    if (e == hipSuccess) e = zero(dk, (int64_t)D.S * D.Hkv * D.N * D.d, st);
+    if (e == hipSuccess) e = zero(dv, (int64_t)D.S * D.Hkv * D.N * D.d, st);
+  }
+  if (e != hipSuccess) return e;
+  {
+    const int64_t rows = (int64_t)D.S * D.T * D.H;
+    LaunchScope scope("bwd_drow", st);
+    const dim3 grid((unsigned)((rows * 16 + 255) / 256));
+    if (D.d == 64)
+      hipLaunchKernelGGL(drow_kernel<64>, grid, dim3(256), 0, st, rows, static_cast<const uint16_t*>(out),
+                         static_cast<const uint16_t*>(dout), w.drow);
+    else
+      hipLaunchKernelGGL(drow_kernel<128>, grid, dim3(256), 0, st, rows, static_cast<const uint16_t*>(out),
+                         static_cast<const uint16_t*>(dout), w.drow);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  e = launch_work_list(D, off, kRows, w.wlst, st);
+  if (e != hipSuccess) return e;
+  LaunchScope scope("attn_bwd", st);
+  const uint16_t *qb = static_cast<const uint16_t*>(q), *kb = static_cast<const uint16_t*>(k),
+                 *vb = static_cast<const uint16_t*>(v), *gb = static_cast<const uint16_t*>(dout);
+#define MSA_BWD_CASE(DH_, G_)                                                                  \
+  if (D.d == DH_ && D.G == G_) {                                                               \
+    launch_bwd_t<DH_, G_>(D, qb, kb, vb, gb, lse, w.drow, w.wlst, entries, dq, dk, dv, st);  \
+    return hipGetLastError();                                                                  \
+  }
+  MSA_BWD_CASE(128, 8); MSA_BWD_CASE(128, 1); MSA_BWD_CASE(128, 2); MSA_BWD_CASE(128, 4); MSA_BWD_CASE(128, 16);
+  MSA_BWD_CASE(64, 8); MSA_BWD_CASE(64, 1); MSA_BWD_CASE(64, 2); MSA_BWD_CASE(64, 4); MSA_BWD_CASE(64, 16);
+#undef MSA_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_index_kl(const Dims& D, const float* scores, const int32_t* sel, const float* mass, float sigma,
+                           float* loss, float* dscore, hipStream_t st) {
+  const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
+  LaunchScope scope("index_kl", st);
+  hipLaunchKernelGGL(index_kl_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, D, scores, sel, mass,
+                     sigma, loss, dscore);
+  return hipGetLastError();
+}
+
+size_t index_backward_workspace_bytes(const Dims& D) {
+  size_t total = 0;
+  (void)work_list_layout(D, kRows, nullptr, &total);
+  return total;
+}
+
+hipError_t launch_index_backward(const Dims& D, const void* q_idx, const void* k_idx, const int32_t* off,
+                                 const int32_t* entries, const float* dscore, float* dq_idx, float* dk_idx,
+                                 int32_t* argmax, void* ws, hipStream_t st) {
+  size_t total = 0;
+  const WorkList wl = work_list_layout(D, kRows, ws, &total);
+  hipError_t e;
+  {
+    LaunchScope scope("index_bwd_zero", st);
+    e = zero(dq_idx, (int64_t)D.S * D.Hkv * D.T * D.dI, st);
+    if (e == hipSuccess) e = zero(dk_idx, (int64_t)D.S * D.Hkv * D.N * D.dI, st);
+  }
+  if (e != hipSuccess) return e;
+  e = launch_work_list(D, off, kRows, wl, st);
+  if (e != hipSuccess) return e;
+  const int64_t grid = (wl.ub + 7) / 8 * 8 + 8;
+  LaunchScope scope("index_bwd", st);
+  const uint16_t *qb = static_cast<const uint16_t*>(q_idx), *kb = static_cast<const uint16_t*>(k_idx);
+  if (D.dI == 32)
+    hipLaunchKernelGGL(index_bwd<32>, dim3((unsigned)grid), dim3(kThreads), 0, st, D, qb, kb, wl.wl, wl.n_items,
+                       entries, dscore, dq_idx, dk_idx, argmax);
+  else if (D.dI == 64)
+    hipLaunchKernelGGL(index_bwd<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, D, qb, kb, wl.wl, wl.n_items,
+                       entries, dscore, dq_idx, dk_idx, argmax);
+  else
+    hipLaunchKernelGGL(index_bwd<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, D, qb, kb, wl.wl, wl.n_items,
+                       entries, dscore, dq_idx, dk_idx, argmax);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -128,6 +128,14 @@ msa_status apply_layout(const msa_kv_layout* L, msa::Dims* D) {
   return MSA_OK;
 }
 
+// The training calls run the bf16 kernels only.
+msa_status check_train(const msa::Dims& D, bool index) {
+  if (D.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "the training calls need dtype MSA_BF16");
+  if (index && D.kdtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "the index-branch training calls need bf16 index keys");
+  return MSA_OK;
+}
+
 #define REQUIRE_PTR(x)                                                         \
   do {                                                                         \
     if ((x) == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, #x " is NULL"); \
@@ -200,6 +208,12 @@ size_t msa_workspace_bytes(const msa_problem* prob, int which) {
     case MSA_CALL_DECODE:
       if (check_problem(prob, &D, false, true) != MSA_OK) return 0;
       return msa::decode_workspace_bytes(D);
+    case MSA_CALL_BACKWARD:
+      if (check_problem(prob, &D, false, true) != MSA_OK || check_train(D, false) != MSA_OK) return 0;
+      return msa::backward_workspace_bytes(D);
+    case MSA_CALL_INDEX_BACKWARD:
+      if (check_problem(prob, &D, true, false) != MSA_OK || check_train(D, true) != MSA_OK) return 0;
+      return msa::index_backward_workspace_bytes(D);
     default:
       return 0;
   }
@@ -339,6 +353,107 @@ msa_status msa_sparse_attn_decode_kv(const msa_problem* prob, const msa_kv_layou
   return device_status(
       msa::launch_decode(D, q, k_cache, v_cache, sel, out, workspace, (hipStream_t)stream),
       "msa_sparse_attn_decode_kv launch");
+}
+
+msa_status msa_sparse_attn_prefill_train(const msa_problem* prob, const void* q, const void* k,
+                                         const void* v, const int32_t* csr_offsets,
+                                         const int32_t* csr_entries, const int32_t* sel, void* out,
+                                         float* lse, float* block_mass, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, true);
+  if (st != MSA_OK) return st;
+  if ((st = check_train(D, false)) != MSA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(csr_offsets);
+  REQUIRE_PTR(csr_entries);
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(block_mass);
+  const size_t need = msa::prefill_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "msa_sparse_attn_prefill_train needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(msa::launch_prefill(D, q, k, v, csr_offsets, csr_entries, sel, out, workspace,
+                                           (hipStream_t)stream, lse, block_mass),
+                       "msa_sparse_attn_prefill_train launch");
+}
+
+msa_status msa_sparse_attn_backward(const msa_problem* prob, const void* q, const void* k,
+                                    const void* v, const void* out, const void* dout,
+                                    const float* lse, const int32_t* csr_offsets,
+                                    const int32_t* csr_entries, float* dq, float* dk, float* dv,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, true);
+  if (st != MSA_OK) return st;
+  if ((st = check_train(D, false)) != MSA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(dout);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(csr_offsets);
+  REQUIRE_PTR(csr_entries);
+  REQUIRE_PTR(dq);
+  REQUIRE_PTR(dk);
+  REQUIRE_PTR(dv);
+  const size_t need = msa::backward_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_sparse_attn_backward needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(msa::launch_attn_backward(D, q, k, v, out, dout, lse, csr_offsets, csr_entries, dq, dk, dv,
+                                                 workspace, (hipStream_t)stream),
+                       "msa_sparse_attn_backward launch");
+}
+
+msa_status msa_index_kl(const msa_problem* prob, const float* scores, const int32_t* sel,
+                        const float* block_mass, float sigma, float* loss, float* dscores,
+                        void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, true, false);
+  if (st != MSA_OK) return st;
+  if ((st = check_train(D, true)) != MSA_OK) return st;
+  if (!(sigma >= 0.0f) || isinf(sigma)) return fail(MSA_ERR_INVALID_ARGUMENT, "sigma must be finite and >= 0");
+  REQUIRE_PTR(scores);
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(block_mass);
+  REQUIRE_PTR(loss);
+  REQUIRE_PTR(dscores);
+  const float sg = sigma > 0.0f ? sigma : 1.0f / sqrtf((float)D.dI);
+  return device_status(msa::launch_index_kl(D, scores, sel, block_mass, sg, loss, dscores, (hipStream_t)stream),
+                       "msa_index_kl launch");
+}
+
+msa_status msa_index_backward(const msa_problem* prob, const void* q_idx, const void* k_idx,
+                              const int32_t* csr_offsets, const int32_t* csr_entries,
+                              const float* dscores, float* dq_idx, float* dk_idx, int32_t* argmax,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, true, false);
+  if (st != MSA_OK) return st;
+  if ((st = check_train(D, true)) != MSA_OK) return st;
+  REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(k_idx);
+  REQUIRE_PTR(csr_offsets);
+  REQUIRE_PTR(csr_entries);
+  REQUIRE_PTR(dscores);
+  REQUIRE_PTR(dq_idx);
+  REQUIRE_PTR(dk_idx);
+  const size_t need = msa::index_backward_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_index_backward needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(msa::launch_index_backward(D, q_idx, k_idx, csr_offsets, csr_entries, dscores, dq_idx,
+                                                  dk_idx, argmax, workspace, (hipStream_t)stream),
+                       "msa_index_backward launch");
 }
 
 msa_status msa_profiler_enable(int on) {

@@ -45,11 +45,38 @@ hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, in
                          void* ws, hipStream_t st);
 
 size_t prefill_workspace_bytes(const Dims& D);
+// lse_out [S, T, H] and mass_out [S, Hkv, T, k] (both optional) are the training outputs.
 hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const void* v,
                           const int32_t* offsets, const int32_t* entries, const int32_t* sel,
-                          void* out, void* ws, hipStream_t st);
+                          void* out, void* ws, hipStream_t st, float* lse_out = nullptr,
+                          float* mass_out = nullptr);
 
 size_t decode_workspace_bytes(const Dims& D);
+
+// Work list over an inverted selection (attention.hip): one item per (s, g, b) and run of
+// at most R rows of its list, as int4 {(s*Hkv + g)*nb + b, first csr position, rows, 0}.
+struct WorkList {
+  int* items;
+  int* itempos;
+  int* n_items;
+  void* scan_ws;
+  int4* wl;
+  int64_t ub;  // upper bound on the number of items
+};
+WorkList work_list_layout(const Dims& D, int R, void* base, size_t* total);
+hipError_t launch_work_list(const Dims& D, const int32_t* off, int R, const WorkList& w, hipStream_t st);
+
+// Training path (backward.hip).
+size_t backward_workspace_bytes(const Dims& D);
+hipError_t launch_attn_backward(const Dims& D, const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, const int32_t* off, const int32_t* entries,
+                                float* dq, float* dk, float* dv, void* ws, hipStream_t st);
+hipError_t launch_index_kl(const Dims& D, const float* scores, const int32_t* sel, const float* mass, float sigma,
+                           float* loss, float* dscore, hipStream_t st);
+size_t index_backward_workspace_bytes(const Dims& D);
+hipError_t launch_index_backward(const Dims& D, const void* q_idx, const void* k_idx, const int32_t* off,
+                                 const int32_t* entries, const float* dscore, float* dq_idx, float* dk_idx,
+                                 int32_t* argmax, void* ws, hipStream_t st);
 hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void* v,
                          const int32_t* sel, void* out, void* ws, hipStream_t st);
 
@@ -58,7 +85,8 @@ hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void
 // the row's partial over all of its hot blocks; the other hot slots are skipped.
 hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part_lse,
                             const void* part_o, int part_o_is_bf16, const uint64_t* hotmask, void* out,
-                            hipStream_t st, const char* name);
+                            hipStream_t st, const char* name, float* lse_out = nullptr,
+                            float* mass_out = nullptr);
 
 // Query-tile / Outer-Gather-Q split of a prefill selection (hot_tiles.hip).
 constexpr int kHotTile = 128;            // query tile: one 128-position block

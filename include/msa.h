@@ -83,7 +83,8 @@ typedef struct {
 } msa_problem;
 
 /* Which call a workspace size is asked for (msa_workspace_bytes). */
-enum { MSA_CALL_INVERT = 2, MSA_CALL_PREFILL = 3, MSA_CALL_DECODE = 4 };
+enum { MSA_CALL_INVERT = 2, MSA_CALL_PREFILL = 3, MSA_CALL_DECODE = 4, MSA_CALL_BACKWARD = 5,
+       MSA_CALL_INDEX_BACKWARD = 6 };
 
 /*
  * a1. Index branch scoring fused with the causal block max-pool
@@ -211,6 +212,64 @@ msa_status msa_block_topk_kv(const msa_problem* prob, const msa_kv_layout* layou
 msa_status msa_sparse_attn_decode_kv(const msa_problem* prob, const msa_kv_layout* layout, const void* q,
                                      const void* k_cache, const void* v_cache, const int32_t* sel, void* out,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Training path ([P1] 索引分支训练：KL 对齐 -- the index branch learns from the main
+ * branch's attention distribution through a KL divergence and only it receives that
+ * signal; [P3] MSA entry: KL loss, teacher stop-gradient).  dtype MSA_BF16, index keys
+ * bf16 (index_key_dtype 0 or MSA_BF16); other problems return MSA_ERR_UNSUPPORTED.
+ * Gradients are float32 and are OVERWRITTEN (the calls zero them first).
+ *
+ * Readings of the pages used here:
+ *   teacher  mass[s,g,t,i] = the main branch's attention on block sel[s,g,t,i] for row t,
+ *            averaged over the G heads of group g (0 for a -1 slot; a row sums to 1);
+ *   student  softmax over the row's selected blocks of sigma * scores[s,g,t,b];
+ *   loss     KL(teacher / sum(teacher) || student) per row; gradients are those of the SUM
+ *            of row losses, the teacher held fixed;
+ *   max-pool the gradient of a block score reaches its arg-max key (lowest position among
+ *            equal maxima, scores accumulated in float32).
+ */
+
+/* a4 + a5 of msa_sparse_attn_prefill with the training outputs (every pair takes the
+ * Outer-Gather-Q kernel, whatever MSA_HOT_TILES says):
+ *   lse        float32 [S, T, H]: log sum_j exp(scale q.K_j) over the row's attended keys;
+ *   block_mass float32 [S, Hkv, T, k]: the teacher above.
+ * workspace: msa_workspace_bytes(prob, MSA_CALL_PREFILL) bytes. */
+msa_status msa_sparse_attn_prefill_train(const msa_problem* prob, const void* q, const void* k,
+                                         const void* v, const int32_t* csr_offsets,
+                                         const int32_t* csr_entries, const int32_t* sel, void* out,
+                                         float* lse, float* block_mass, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/* Gradients of sum(dout * out) for the main branch, out being the prefill output for the
+ * same q, k, v and selection (dout, out bf16 [S, T, H, d]; lse from the call above):
+ *   dq float32 [S, T, H, d], dk and dv float32 [S, Hkv, N, d].
+ * The KV block is the outer loop (csr lists from msa_invert_selection).  Accumulation
+ * uses float atomics: the result is exact up to the order of float32 additions.
+ * workspace: msa_workspace_bytes(prob, MSA_CALL_BACKWARD) bytes. */
+msa_status msa_sparse_attn_backward(const msa_problem* prob, const void* q, const void* k,
+                                    const void* v, const void* out, const void* dout,
+                                    const float* lse, const int32_t* csr_offsets,
+                                    const int32_t* csr_entries, float* dq, float* dk, float* dv,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The index-branch KL per row and its gradient with respect to the selected block scores:
+ *   scores float32 [S, Hkv, T, nb] (msa_index_scores), sel [S, Hkv, T, k],
+ *   block_mass [S, Hkv, T, k] (teacher), sigma > 0 (0 selects 1 / sqrt(index_dim));
+ *   loss float32 [S, Hkv, T]; dscores float32 [S, Hkv, T, k] (0 for -1 slots). */
+msa_status msa_index_kl(const msa_problem* prob, const float* scores, const int32_t* sel,
+                        const float* block_mass, float sigma, float* loss, float* dscores,
+                        void* stream);
+
+/* Index-branch input gradients through the causal block max-pool, in Outer-Gather-Q order:
+ *   dq_idx float32 [S, Hkv, T, dI], dk_idx float32 [S, Hkv, N, dI];
+ *   argmax int32 [S, Hkv, T, k] (optional, may be NULL): the arg-max position of each
+ *   selected block; entries of -1 slots are left untouched.
+ * workspace: msa_workspace_bytes(prob, MSA_CALL_INDEX_BACKWARD) bytes. */
+msa_status msa_index_backward(const msa_problem* prob, const void* q_idx, const void* k_idx,
+                              const int32_t* csr_offsets, const int32_t* csr_entries,
+                              const float* dscores, float* dq_idx, float* dk_idx, int32_t* argmax,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace needed by a call (MSA_CALL_*); 0 for an invalid problem or call. */
 size_t msa_workspace_bytes(const msa_problem* prob, int which_call);

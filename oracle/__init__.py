@@ -69,10 +69,12 @@ def _load():
                                                P, P, P, P]
         lib.orc_index_kl.argtypes = [i64, i32, i64, P, P, P, ctypes.c_double, P, P]
         lib.orc_index_backward.argtypes = [i64, i32, i32, i32, i64, P, P, P, P, P, P, P]
+        lib.orc_index_argmax.argtypes = [i64, i32, i32, i32, i64, P, P, P, P, P, P, P, P]
+        lib.orc_index_backward_at.argtypes = [i64, i32, i32, i64, P, P, P, P, P, P]
         lib.orc_num_threads.restype = ctypes.c_int
         for f in ("orc_index_scores", "orc_block_topk", "orc_invert", "orc_attention",
                   "orc_attention_partials", "orc_lse_merge", "orc_attention_train", "orc_attention_backward",
-                  "orc_index_kl", "orc_index_backward"):
+                  "orc_index_kl", "orc_index_backward", "orc_index_argmax", "orc_index_backward_at"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -265,6 +267,36 @@ def slice_index_backward(qI_rows, pos, sel_rows, KI, B: int, dscore):
     dKI = np.empty(KI.shape)
     _load().orc_index_backward(KI.shape[0], B, dI, k, R, _p(qI_rows), _p(pos), _p(sel_rows), _p(KI), _p(dscore),
                                _p(dqI), _p(dKI))
+    return dqI, dKI
+
+
+def slice_index_argmax(qI_rows, pos, sel_rows, KI, B: int, cand=None):
+    """-> (jbest [R, k] int64, best [R, k], cand_val [R, k]): the max-pool arg-max (lowest
+    position among equal scores), its score, and the score at the candidate positions."""
+    qI_rows, KI = _f64(qI_rows), _f64(KI)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel_rows = np.ascontiguousarray(sel_rows, dtype=np.int32)
+    R, dI = qI_rows.shape
+    k = sel_rows.shape[1]
+    jb = np.empty((R, k), dtype=np.int64)
+    best = np.empty((R, k))
+    cv = np.empty((R, k))
+    c = None if cand is None else np.ascontiguousarray(cand, dtype=np.int64)
+    _load().orc_index_argmax(KI.shape[0], B, dI, k, R, _p(qI_rows), _p(pos), _p(sel_rows), _p(KI),
+                             _p(c) if c is not None else None, _p(jb), _p(best), _p(cv))
+    return jb, best, cv
+
+
+def slice_index_backward_at(qI_rows, jstar, KI, dscore):
+    """The max-pool gradient scatter for given arg-max positions jstar [R, k] (-1 = none)."""
+    qI_rows, KI, dscore = _f64(qI_rows), _f64(KI), _f64(dscore)
+    jstar = np.ascontiguousarray(jstar, dtype=np.int64)
+    R, dI = qI_rows.shape
+    k = jstar.shape[1]
+    dqI = np.empty((R, dI))
+    dKI = np.empty(KI.shape)
+    _load().orc_index_backward_at(KI.shape[0], dI, k, R, _p(qI_rows), _p(jstar), _p(KI), _p(dscore), _p(dqI),
+                                  _p(dKI))
     return dqI, dKI
 
 

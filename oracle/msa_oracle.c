@@ -484,6 +484,55 @@ void orc_index_backward(int64_t N, int B, int dI, int k, int64_t nrows, const do
     }
 }
 
+/* The arg-max of the max-pool where several keys may be correct: for each row r and valid
+ * slot i, jbest[r,i] / best[r,i] = the lowest position holding the largest score in the
+ * block (double) and that score, and cand_val[r,i] = the score at position cand[r,i]
+ * (NaN if that position is outside the block's causal range).  -1 slots: jbest = -1. */
+void orc_index_argmax(int64_t N, int B, int dI, int k, int64_t nrows, const double *qI,
+                      const int64_t *pos, const int32_t *sel, const double *KI, const int64_t *cand,
+                      int64_t *jbest, double *best, double *cand_val)
+{
+    (void)N;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const double *qq = qI + r * dI;
+        for (int i = 0; i < k; ++i) {
+            const int64_t o = r * k + i;
+            const int32_t b = sel[o];
+            jbest[o] = -1;
+            best[o] = -INFINITY;
+            cand_val[o] = NAN;
+            if (b < 0) continue;
+            for (int64_t j = (int64_t)b * B; j < ((int64_t)b + 1) * B && j <= pos[r]; ++j) {
+                double s = 0.0;
+                for (int c = 0; c < dI; ++c) s += qq[c] * KI[j * dI + c];
+                if (jbest[o] < 0 || s > best[o]) { best[o] = s; jbest[o] = j; }
+                if (cand != NULL && j == cand[o]) cand_val[o] = s;
+            }
+        }
+    }
+}
+
+/* The scatter of orc_index_backward for given arg-max positions j[r,i] (-1 = none):
+ * dqI[r] += dscore[r,i] k_I[j], dKI[j] += dscore[r,i] q_I[r].  Serial. */
+void orc_index_backward_at(int64_t N, int dI, int k, int64_t nrows, const double *qI,
+                           const int64_t *jstar, const double *KI, const double *dscore,
+                           double *dqI, double *dKI)
+{
+    memset(dqI, 0, sizeof(double) * (size_t)nrows * (size_t)dI);
+    memset(dKI, 0, sizeof(double) * (size_t)N * (size_t)dI);
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int i = 0; i < k; ++i) {
+            const int64_t j = jstar[r * k + i];
+            if (j < 0) continue;
+            const double g = dscore[r * k + i];
+            for (int c = 0; c < dI; ++c) {
+                dqI[r * dI + c] += g * KI[j * dI + c];
+                dKI[j * dI + c] += g * qI[r * dI + c];
+            }
+        }
+}
+
 /* Threads OpenMP will use for the parallel loops above (reported beside timings). */
 #ifdef _OPENMP
 #include <omp.h>

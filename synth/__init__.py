@@ -45,7 +45,7 @@ GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 M1 = np.uint64(0xBF58476D1CE4E5B9)
 M2 = np.uint64(0x94D049BB133111EB)
 
-TID_Q, TID_K, TID_V, TID_QI, TID_KI, TID_NEEDLE, TID_ROWS = 1, 2, 3, 4, 5, 6, 7
+TID_Q, TID_K, TID_V, TID_QI, TID_KI, TID_NEEDLE, TID_ROWS, TID_DOUT = 1, 2, 3, 4, 5, 6, 7, 9
 KIND_IID, KIND_QIDX, KIND_KIDX = 0, 1, 2
 F32, BF16, FP8 = 0, 1, 2   # FP8: OCP E4M3 (index keys only)
 

@@ -18,7 +18,7 @@ any part of the attention method.
   (C3_FP8: C3 with its index keys stored as OCP FP8 E4M3, the serving variant.)
 
 Seeds are 0x4D534100 + workload index; tensor ids Q 1, K 2, V 3, q_I 4, k_I 5,
-needle draw 6, sampled rows 7.
+needle draw 6, sampled rows 7, upstream gradient dO of the training step 9.
 """
 from __future__ import annotations
 
@@ -26,8 +26,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import (BF16, F32, FP8, KIND_IID, KIND_KIDX, KIND_QIDX, TID_K, TID_KI, TID_Q, TID_QI, TID_ROWS, TID_V,
-               TensorSpec, band_table, h16, needle_blocks)
+from . import (BF16, F32, FP8, KIND_IID, KIND_KIDX, KIND_QIDX, TID_DOUT, TID_K, TID_KI, TID_Q, TID_QI, TID_ROWS,
+               TID_V, TensorSpec, band_table, h16, needle_blocks)
 
 SEED_BASE = 0x4D534100
 SIGMA_BOOST = 24.0   # 3 sigma with sigma = sqrt(dI) = 8
@@ -108,6 +108,10 @@ class Workload:
             out["k_idx"] = TensorSpec((self.S, self.Hkv, self.N, self.dI), sd, TID_KI, kdt, kind=KIND_KIDX,
                                       boost=SIGMA_BOOST, block=128, boost_mask=self.boost_mask(), band=band)
         return out
+
+    def dout_spec(self) -> TensorSpec:
+        """Upstream gradient of the attention output for a training step: [S, T, H, d], iid."""
+        return TensorSpec((self.S, self.T, self.H, self.d), self.seed, TID_DOUT, self.dtype)
 
     def sampled_rows(self, count: int, always=()) -> np.ndarray:
         """Seeded sample of query rows (stream TID_ROWS), always including `always`."""

@@ -1,0 +1,134 @@
+"""GPU parity of the training path: forward with lse and teacher mass, main-branch backward,
+index-branch KL and its max-pool backward, each against the CPU oracle on the GPU's
+selection (the selection itself is gated by the forward parity tests).
+
+Tolerances:
+  * lse and teacher mass: 1e-4 absolute (float32 sums of exactly formed bf16 products);
+  * dq, dk, dv: relative RMS error <= GRAD_REL_RMS and max abs error <= GRAD_MAX_REL * max|ref|
+    (P and dS enter the matrix cores as bf16, and D = rowsum(dO o O) uses the bf16 output:
+    each carries a relative rounding of 2^-9);
+  * KL loss and dscore: 1e-4 (float32 exp / log of float32 scores);
+  * index gradients: the GPU's arg-max must be a maximiser of the fp64 block scores up to
+    float32 summation error (several keys can be correct: the scores are summed in float32);
+    the gradients are then compared with the oracle's scatter at those positions, 1e-4
+    relative to the largest entry (float32 atomic sums)."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_06_amd as msa
+import oracle
+import synth
+from synth import workloads as W
+from tests.gpu_util import f64, gen, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+B = 128
+# about five units of the 2^-9 relative rounding that P and dS carry as bf16 MFMA operands
+# (observed: relative RMS <= 1.9e-3, max error <= 3.5e-3 of max |ref|)
+GRAD_REL_RMS = 1e-2
+GRAD_MAX_REL = 2e-2
+
+CASES = [
+    (W.small("train_bf16_g8", S=1, T=700, N=1000, H=16, Hkv=2, d=128, dI=64, k=4), 0.125),
+    (W.small("train_bf16_g4_d64_ragged", S=2, T=300, N=555, H=8, Hkv=2, d=64, dI=32, k=3), 0.0),
+    (W.small("train_bf16_structured", S=1, T=1024, N=1024, H=8, Hkv=1, d=128, dI=64, k=8,
+             structure="band_sink_needles"), 0.05),
+    (W.small("train_bf16_g16_dI128", S=1, T=300, N=900, H=16, Hkv=1, d=128, dI=128, k=4), 0.1),
+]
+
+
+def _grad_check(got, ref, what):
+    err = got - ref
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    rel_rms = float(np.sqrt(np.mean(err ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
+    mx = float(np.abs(err).max()) / scale
+    say("  %s: rel rms %.3e, max abs err / max |ref| %.3e" % (what, rel_rms, mx))
+    assert np.all(np.isfinite(got)), "non-finite gradient"
+    assert rel_rms <= GRAD_REL_RMS, "%s relative RMS error %.3e" % (what, rel_rms)
+    assert mx <= GRAD_MAX_REL, "%s max error %.3e of max |ref|" % (what, mx)
+
+
+@pytest.mark.parametrize("wl,sigma", CASES, ids=[c[0].name for c in CASES])
+def test_training_step_matches_the_oracle(wl, sigma):
+    require_gpu()
+    say("case", wl.name)
+    inputs = gen(wl)
+    dout = synth.device_tensor(wl.dout_spec())
+    prob = wl.problem()
+    tb = msa.alloc_train(prob)
+    msa.run_train_step(prob, inputs["q"], inputs["k"], inputs["v"], inputs["q_idx"], inputs["k_idx"], dout, tb,
+                       sigma=sigma)
+    torch.cuda.synchronize()
+    sig = sigma if sigma > 0 else 1.0 / np.sqrt(wl.dI)
+    scale = 1.0 / np.sqrt(wl.d)
+    G = wl.G
+    pos = oracle.positions(wl.N, wl.T)
+    q, K, V, gO = f64(inputs["q"]), f64(inputs["k"]), f64(inputs["v"]), f64(dout)
+    qI, kI = f64(inputs["q_idx"]), f64(inputs["k_idx"])
+    out = f64(tb.fwd.out)
+    sel = tb.fwd.sel.cpu().numpy()
+    sc = tb.fwd.scores.cpu().numpy()
+    lse, mass = tb.lse.cpu().numpy(), tb.mass.cpu().numpy()
+    dq, dk, dv = tb.dq.cpu().numpy(), tb.dk.cpu().numpy(), tb.dv.cpu().numpy()
+    loss, dsc = tb.loss.cpu().numpy(), tb.dscores.cpu().numpy()
+    dqi, dki, am = tb.dq_idx.cpu().numpy(), tb.dk_idx.cpu().numpy(), tb.argmax.cpu().numpy()
+    for s in range(wl.S):
+        for g in range(wl.Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            o_ref, lse_ref, mass_ref = oracle.slice_attention_train(q[s][:, hs], pos, sel[s, g], K[s, g], V[s, g], B,
+                                                                    scale)
+            e_out = float(np.abs(out[s][:, hs] - o_ref).max())
+            e_lse = float(np.abs(lse[s][:, hs] - lse_ref).max())
+            e_mass = float(np.abs(mass[s, g] - mass_ref).max())
+            say("  s%d g%d forward: out %.3e, lse %.3e, mass %.3e" % (s, g, e_out, e_lse, e_mass))
+            assert e_out <= 2e-2 and e_lse <= 1e-4 and e_mass <= 1e-4
+            # main-branch backward
+            dq_ref, dK_ref, dV_ref = oracle.slice_attention_backward(q[s][:, hs], pos, sel[s, g], K[s, g], V[s, g],
+                                                                     B, scale, gO[s][:, hs])
+            _grad_check(dq[s][:, hs], dq_ref, "s%d g%d dq" % (s, g))
+            _grad_check(dk[s, g], dK_ref, "s%d g%d dk" % (s, g))
+            _grad_check(dv[s, g], dV_ref, "s%d g%d dv" % (s, g))
+            # index KL on the GPU's scores and teacher
+            l_ref, d_ref = oracle.slice_index_kl(sc[s, g], sel[s, g], mass[s, g], sig)
+            e_l = float(np.abs(loss[s, g] - l_ref).max())
+            e_d = float(np.abs(dsc[s, g] - d_ref).max())
+            say("  s%d g%d KL: loss %.3e, dscore %.3e (mean loss %.4f)" % (s, g, e_l, e_d, float(l_ref.mean())))
+            assert e_l <= 1e-4 * max(1.0, float(np.abs(l_ref).max())) and e_d <= 1e-4 * max(sig, 1e-3) * 10
+            # index backward: the GPU's arg-max is a maximiser, then the scatter at it
+            ok = sel[s, g] >= 0
+            jb, best, cv = oracle.slice_index_argmax(qI[s, g], pos, sel[s, g], kI[s, g], B, cand=am[s, g])
+            assert np.all(am[s, g][~ok] == -1)
+            assert np.all(np.isfinite(cv[ok])), "arg-max outside its block's causal range"
+            tol = 1e-5 * np.maximum(1.0, np.abs(best[ok]))
+            assert np.all(best[ok] - cv[ok] <= tol), "GPU arg-max is not a maximiser"
+            say("  s%d g%d arg-max: %d of %d equal to the fp64 choice" % (s, g, int((am[s, g] == jb)[ok].sum()),
+                                                                         int(ok.sum())))
+            dqi_ref, dki_ref = oracle.slice_index_backward_at(qI[s, g], am[s, g], kI[s, g], dsc[s, g])
+            for got, ref, what in ((dqi[s, g], dqi_ref, "dq_idx"), (dki[s, g], dki_ref, "dk_idx")):
+                e = float(np.abs(got - ref).max()) / max(float(np.abs(ref).max()), 1e-30)
+                say("  s%d g%d %s: max err / max |ref| %.3e" % (s, g, what, e))
+                assert e <= 1e-4
+
+
+def test_teacher_masses_sum_to_one_and_unselected_blocks_get_no_gradient():
+    require_gpu()
+    wl = CASES[0][0]
+    inputs = gen(wl)
+    dout = synth.device_tensor(wl.dout_spec())
+    prob = wl.problem()
+    tb = msa.alloc_train(prob)
+    msa.run_train_step(prob, inputs["q"], inputs["k"], inputs["v"], inputs["q_idx"], inputs["k_idx"], dout, tb)
+    torch.cuda.synchronize()
+    m = tb.mass.cpu().numpy()
+    np.testing.assert_allclose(m.sum(axis=-1), 1.0, atol=1e-5)
+    sel = tb.fwd.sel.cpu().numpy()
+    dk, dv, dki = tb.dk.cpu().numpy(), tb.dv.cpu().numpy(), tb.dk_idx.cpu().numpy()
+    for s in range(wl.S):
+        for g in range(wl.Hkv):
+            chosen = np.zeros(wl.nb, dtype=bool)
+            chosen[sel[s, g][sel[s, g] >= 0]] = True
+            for b in np.nonzero(~chosen)[0]:
+                rows = slice(b * B, min((b + 1) * B, wl.N))
+                assert not dk[s, g, rows].any() and not dv[s, g, rows].any() and not dki[s, g, rows].any()

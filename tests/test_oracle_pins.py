@@ -458,3 +458,26 @@ def test_index_backward_tie_goes_to_the_lowest_position():
     np.testing.assert_allclose(dK[0], [2.0, 0.0, 0.0])
     np.testing.assert_allclose(dK[8], [1.0, 0.0, 0.0])
     np.testing.assert_allclose(dq[0], [1.5, 0.0, 0.0])
+
+
+def test_index_argmax_and_scatter_agree_with_the_fused_backward():
+    N, T, B, dI, k = 70, 33, 8, 5, 3
+    qI, KI = RNG.standard_normal((T, dI)), RNG.standard_normal((N, dI))
+    pos = _pos(N, T)
+    sel = oracle.slice_block_topk(RNG.standard_normal((T, (N + B - 1) // B)), pos // B, k)
+    dscore = RNG.standard_normal((T, k)) * (sel >= 0)
+    jb, best, cv = oracle.slice_index_argmax(qI, pos, sel, KI, B, cand=None)
+    # the block scores of the max-pool are the best values
+    sc = oracle.slice_index_scores(qI, pos, KI, B)
+    ok = sel >= 0
+    np.testing.assert_allclose(best[ok], np.take_along_axis(sc, np.maximum(sel, 0), axis=1)[ok], rtol=1e-12)
+    assert np.all(jb[~ok] == -1) and np.all(jb[ok] // B == sel[ok]) and np.all(jb[ok] <= pos[:, None].repeat(k, 1)[ok])
+    # the score at a candidate position is reported; outside the block it is NaN
+    _, _, cv = oracle.slice_index_argmax(qI, pos, sel, KI, B, cand=jb)
+    np.testing.assert_array_equal(cv[ok], best[ok])
+    _, _, cv2 = oracle.slice_index_argmax(qI, pos, sel, KI, B, cand=np.where(ok, jb + B, -1))
+    assert np.all(np.isnan(cv2))
+    a = oracle.slice_index_backward(qI, pos, sel, KI, B, dscore)
+    b = oracle.slice_index_backward_at(qI, jb, KI, dscore)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-14, atol=1e-14)
