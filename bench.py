@@ -340,6 +340,53 @@ def paged_decode(args, msa, wd, xd):
                 us_per_step=ms * 1e3, us_per_token_amortised=ms * 1e3 / S, stages=st)
 
 
+def train_step(args, msa, wl):
+    """One training step of wl, outside the timed prefill step: index scores, top-k,
+    inversion, the forward with lse and teacher mass (every pair in Outer-Gather-Q order),
+    the main-branch backward for a seeded upstream gradient, the index KL and the
+    index-branch backward.  Stage times come from the library timer.  The attention
+    backward is priced at 10 d flops per (row, head, attended key): five products (S, dP,
+    dV, dK, dQ) of 2 d each, against the bf16 matrix-core peak."""
+    import torch
+    import synth
+    specs = wl.specs()
+    x = {n: synth.device_tensor(specs[n]) for n in specs}
+    dout = synth.device_tensor(wl.dout_spec())
+    prob = wl.problem()
+    tb = msa.alloc_train(prob)
+
+    def step():
+        msa.run_train_step(prob, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], dout, tb)
+    step()
+    torch.cuda.synchronize()
+    msa.profiler_read(None, reset=True)
+    msa.profiler_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    msa.profiler_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    st = {}
+    for kn in ("idx_scores_mfma", "block_topk", "ogq_mfma", "lse_merge", "bwd_zero", "bwd_drow", "attn_bwd", "dq_merge",
+               "index_kl", "index_bwd_zero", "index_bwd"):
+        tms, nl = msa.profiler_read(kn, reset=False)
+        if nl:
+            st[kn] = dict(ms=tms / nl)
+    msa.profiler_read(None, reset=True)
+    m = prefill_model(wl.S, wl.T, wl.N, wl.H, wl.Hkv, wl.d, wl.dI, wl.k)
+    fwd_flops = m["ogq_attention"]["flops"]
+    if "attn_bwd" in st:
+        st["attn_bwd"].update(roofline(2.5 * fwd_flops, 0.0, st["attn_bwd"]["ms"] / 1e3), flops=2.5 * fwd_flops)
+    if "ogq_mfma" in st:
+        st["ogq_mfma"].update(roofline(fwd_flops, m["ogq_attention"]["bytes"], st["ogq_mfma"]["ms"] / 1e3))
+    del tb, x
+    return dict(workload=wl.description + ", training step (forward + backward + index KL)",
+                ms_per_step=ms, tokens_per_s=wl.T / (ms / 1e3), stages=st)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +400,8 @@ def main():
                     help="skip the extra decode timing with the index keys stored as FP8 E4M3 (serving variant)")
     ap.add_argument("--no-paged-decode", action="store_true",
                     help="skip the extra decode timing over ragged lengths and a paged cache (serving variant)")
+    ap.add_argument("--train", default="C1", choices=["C1", "C2", "none"],
+                    help="workload of the extra training-step timing (default C1, 32768 tokens)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy 3 times (the known-size reference "
                          "for scaling hardware byte counters)")
@@ -538,6 +587,11 @@ def main():
         print("[bench] decode over ragged lengths and a paged cache: %.3f ms per step" % (decp["us_per_step"] / 1e3),
               file=sys.stderr, flush=True)
 
+    trn = None
+    if args.train != "none":
+        trn = train_step(args, msa, {"C1": W.C1, "C2": W.C2}[args.train])
+        print("[bench] training step (%s): %.3f ms" % (args.train, trn["ms_per_step"]), file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline ...", file=sys.stderr, flush=True)
@@ -552,7 +606,7 @@ def main():
         "config": {"workload": wp.description, "batch": wp.S, "seq_len": wp.T, "num_heads": wp.H,
                    "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
         "prefill_ms": prefill_ms, "wall_s_timed": wall,
-        "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
+        "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "training_step": trn, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
         "selection_structure": selection_structure(wp, pb.sel, pb.csr_offsets),
         "attention_pairs": split["pairs"],
     }

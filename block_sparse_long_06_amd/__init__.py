@@ -102,7 +102,7 @@ def lib():
         L.msa_block_topk_kv.argtypes = [PP, LP, P, P, P]
         L.msa_sparse_attn_decode_kv.argtypes = [PP, LP, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_sparse_attn_prefill_train.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        L.msa_sparse_attn_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_sparse_attn_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_index_kl.argtypes = [PP, P, P, P, ctypes.c_float, P, P, P]
         L.msa_index_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in ("msa_index_scores", "msa_block_topk", "msa_invert_selection",
@@ -219,11 +219,12 @@ def sparse_attn_prefill_train(prob: Problem, q, k, v, csr_offsets, csr_entries, 
                                                _ptr(workspace), workspace_bytes_, _stream(stream, q)))
 
 
-def sparse_attn_backward(prob: Problem, q, k, v, out, dout, lse, csr_offsets, csr_entries, dq, dk, dv, workspace,
-                         workspace_bytes_: int, stream=None) -> None:
+def sparse_attn_backward(prob: Problem, q, k, v, out, dout, lse, sel, csr_offsets, csr_entries, dq, dk, dv,
+                         workspace, workspace_bytes_: int, stream=None) -> None:
     _check(lib().msa_sparse_attn_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
-                                          _ptr(lse), _ptr(csr_offsets), _ptr(csr_entries), _ptr(dq), _ptr(dk),
-                                          _ptr(dv), _ptr(workspace), workspace_bytes_, _stream(stream, q)))
+                                          _ptr(lse), _ptr(sel), _ptr(csr_offsets), _ptr(csr_entries), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes_,
+                                          _stream(stream, q)))
 
 
 def index_kl(prob: Problem, scores, sel, block_mass, sigma: float, loss, dscores, stream=None) -> None:
@@ -374,8 +375,8 @@ def run_train_step(prob: Problem, q, k, v, q_idx, k_idx, dout, bufs: TrainBuffer
     invert_selection(prob, f.sel, f.csr_offsets, f.csr_entries, f.ws_invert, f.ws_invert.numel(), stream)
     sparse_attn_prefill_train(prob, q, k, v, f.csr_offsets, f.csr_entries, f.sel, f.out, bufs.lse, bufs.mass,
                               f.ws_prefill, f.ws_prefill.numel(), stream)
-    sparse_attn_backward(prob, q, k, v, f.out, dout, bufs.lse, f.csr_offsets, f.csr_entries, bufs.dq, bufs.dk,
-                         bufs.dv, bufs.ws_bwd, bufs.ws_bwd.numel(), stream)
+    sparse_attn_backward(prob, q, k, v, f.out, dout, bufs.lse, f.sel, f.csr_offsets, f.csr_entries, bufs.dq,
+                         bufs.dk, bufs.dv, bufs.ws_bwd, bufs.ws_bwd.numel(), stream)
     index_kl(prob, f.scores, f.sel, bufs.mass, sigma, bufs.loss, bufs.dscores, stream)
     index_backward(prob, q_idx, k_idx, f.csr_offsets, f.csr_entries, bufs.dscores, bufs.dq_idx, bufs.dk_idx,
                    bufs.argmax, bufs.ws_ibwd, bufs.ws_ibwd.numel(), stream)

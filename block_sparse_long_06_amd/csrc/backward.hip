@@ -18,9 +18,10 @@
 //                                              Q^T are stored in LDS in that order)
 //        dQ = dS K                          (dS through LDS, wave w takes head dims
 //                                              [32w, 32w+32); K^T in LDS is the B operand)
-//    dQ goes to the fp32 output with hardware float atomics (a row's k slots are
-//    different items); dK, dV are accumulated in registers over the item's rows and added
-//    once per item (a block's list can span several items).
+//    dQ of each (row, slot, head) is stored as a bf16 partial (a row's k slots are
+//    different items) and a merge kernel sums a row's partials; dK, dV are accumulated in
+//    registers over the item's rows and added once per item with float atomics (a block's
+//    list can span several items).
 //  * index_kl: per row, KL(teacher || student) over the selected blocks and its gradient
 //    with respect to the block scores (teacher = the forward's block masses).
 //  * index_bwd: the gradient of the block scores through the causal max-pool: per (row,
@@ -39,7 +40,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kBlk = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRows = 256;  // query rows per work item
+constexpr int kRows = 1024;  // query rows per work item
 
 __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   const f32x2 x = {a, b};
@@ -68,10 +69,10 @@ struct __attribute__((aligned(16))) BwdLds {
   __attribute__((aligned(16))) unsigned char qt[DH * TROW];
   __attribute__((aligned(16))) unsigned char dot[DH * TROW];
   __attribute__((aligned(16))) unsigned char ds[32 * SROW];
-  float lse2[32];      // lse * log2(e); +inf for an M-row past the item's rows
-  float drow[32];
-  int pos[32];
-  int64_t dqoff[32];   // element offset of the M-row's dQ row; -1 if none
+  __attribute__((aligned(16))) float lse2[32];  // lse * log2(e); +inf for an M-row past the item's rows
+  __attribute__((aligned(16))) float drow[32];
+  __attribute__((aligned(16))) int pos[32];
+  int64_t dqoff[32];   // element offset of the M-row's dQ partial; -1 if none
 };
 
 // D[s, t, h] = sum_c dO[s, t, h, c] O[s, t, h, c] (fp32), 16 lanes per row.
@@ -111,7 +112,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
                                                         const float* __restrict__ drow,
                                                         const int4* __restrict__ wl, const int* __restrict__ n_items,
                                                         const int32_t* __restrict__ entries,
-                                                        float* __restrict__ dq, float* __restrict__ dk,
+                                                        uint16_t* __restrict__ part_dq, float* __restrict__ dk,
                                                         float* __restrict__ dv) {
   using L_ = BwdLds<DH>;
   constexpr int KS = DH / 16;  // k-steps over the head dims
@@ -181,23 +182,40 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
   const bool need_mask = first_pos < j0 + kBlk - 1;
   const int key = j0 + 32 * wave + nl;                // this lane's key
 
+  // Q and dO pieces of a sub-chunk: piece c -> M-row c % 32, 16-byte column c / 32 (lanes
+  // of a wave take consecutive M-rows, so the transposed 2-byte LDS writes of one
+  // instruction fall in distinct dwords).  The next sub-chunk's pieces are fetched into
+  // registers while the current one computes.
+  constexpr int NP = 32 * CPR / kThreads;
+  static_assert(NP >= 1 && 32 * CPR == NP * kThreads, "whole pieces per thread");
+  uint4 nq[NP], ng[NP];
+  auto fetch = [&](int m0n) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int c = threadIdx.x + kThreads * u;
+      const int mr = m0n + c % 32, col = c / 32;
+      nq[u] = make_uint4(0u, 0u, 0u, 0u);
+      ng[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (mr < mrows) {
+        const int t = entries[w.y + mr / G] / D.k;
+        const int64_t off = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mr % G) * DH + col * 8;
+        nq[u] = *reinterpret_cast<const uint4*>(q + off);
+        ng[u] = *reinterpret_cast<const uint4*>(dout + off);
+      }
+    }
+  };
+  fetch(0);
+
   for (int m0 = 0; m0 < mrows; m0 += 32) {
     __syncthreads();  // previous sub-chunk's buffers are free (and the staging is complete)
-    // ---- gather Q and dO of 32 M-rows: row-major and transposed copies
-    for (int c = threadIdx.x; c < 32 * CPR; c += kThreads) {
-      const int m = c / CPR, col = c % CPR;
-      const int mr = m0 + m;
-      uint4 qq = make_uint4(0u, 0u, 0u, 0u), gg = make_uint4(0u, 0u, 0u, 0u);
-      if (mr < mrows) {
-        const int e = entries[w.y + mr / G];
-        const int t = e / D.k;
-        const int64_t off = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mr % G) * DH + col * 8;
-        qq = *reinterpret_cast<const uint4*>(q + off);
-        gg = *reinterpret_cast<const uint4*>(dout + off);
-      }
-      *reinterpret_cast<uint4*>(&L.qs[m * L_::QROW + col * 16]) = qq;
-      *reinterpret_cast<uint4*>(&L.dos[m * L_::QROW + col * 16]) = gg;
-      const uint32_t wq[4] = {qq.x, qq.y, qq.z, qq.w}, wg[4] = {gg.x, gg.y, gg.z, gg.w};
+    // ---- this sub-chunk's Q and dO: row-major and transposed copies
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int c = threadIdx.x + kThreads * u;
+      const int m = c % 32, col = c / 32;
+      *reinterpret_cast<uint4*>(&L.qs[m * L_::QROW + col * 16]) = nq[u];
+      *reinterpret_cast<uint4*>(&L.dos[m * L_::QROW + col * 16]) = ng[u];
+      const uint32_t wq[4] = {nq[u].x, nq[u].y, nq[u].z, nq[u].w}, wg[4] = {ng[u].x, ng[u].y, ng[u].z, ng[u].w};
       const int mc = mrow_col(m);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -209,12 +227,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
     if (threadIdx.x < 32) {
       const int m = threadIdx.x, mr = m0 + m;
       if (mr < mrows) {
-        const int t = entries[w.y + mr / G] / D.k;
+        const int e = entries[w.y + mr / G];
+        const int t = e / D.k;
         const int64_t hr = ((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mr % G;
+        const int64_t pidx = (((int64_t)s * D.T + t) * D.Hkv + g) * D.k + (e - t * D.k);
         L.lse2[m] = lse[hr] * kLog2e;
         L.drow[m] = drow[hr];
         L.pos[m] = D.pos0 + t;
-        L.dqoff[m] = hr * DH;
+        L.dqoff[m] = (pidx * G + mr % G) * DH;
       } else {
         L.lse2[m] = INFINITY;  // P = 0 for an M-row past the list
         L.drow[m] = 0.0f;
@@ -222,6 +242,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
         L.dqoff[m] = -1;
       }
     }
+    if (m0 + 32 < mrows) fetch(m0 + 32);
     __syncthreads();
 
     // ---- S = Q K^T and dP = dO V^T for this wave's 32 keys
@@ -236,14 +257,26 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
       pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, bv, pacc, 0, 0, 0);
     }
     // ---- P, dS (registers r hold M-rows acc_row(r, h) of this lane's key)
+    // per-M-row values of registers 4a .. 4a+3: M-rows 8a + 4h + {0..3}, one 16-byte read each
     float pv[16], dsv[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = acc_row(r, h);
-      float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], sc, -L.lse2[m]));
-      if (need_mask && key > L.pos[m]) p = 0.0f;
-      pv[r] = p;
-      dsv[r] = p * (pacc[r] - L.drow[m]);
+    for (int a = 0; a < 4; ++a) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&L.lse2[8 * a + 4 * h]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&L.drow[8 * a + 4 * h]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      int pq[4] = {0, 0, 0, 0};
+      if (need_mask) {
+        const int4 p4 = *reinterpret_cast<const int4*>(&L.pos[8 * a + 4 * h]);
+        pq[0] = p4.x; pq[1] = p4.y; pq[2] = p4.z; pq[3] = p4.w;
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 4 * a + x;
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], sc, -lv[x]));
+        if (need_mask && key > pq[x]) p = 0.0f;
+        pv[r] = p;
+        dsv[r] = p * (pacc[r] - dv4[x]);
+      }
     }
     bf16x8 pb[2], sb[2];
 #pragma unroll
@@ -286,7 +319,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t o = L.dqoff[acc_row(r, h)];
-        if (o >= 0) unsafeAtomicAdd(dq + o + 32 * wave + nl, qacc[r] * D.scale);
+        if (o >= 0) part_dq[o + 32 * wave + nl] = f32_to_bf16(qacc[r] * D.scale);
       }
     }
   }
@@ -309,6 +342,35 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
     for (int i = threadIdx.x; i < nvalid * DH; i += kThreads) unsafeAtomicAdd(dst + i, red[i]);
     __syncthreads();
   }
+}
+
+// dq[s, t, h, :] = sum over the valid slots of row (s, t, g) of its bf16 partials; one
+// thread per 8 head dims.
+__global__ void __launch_bounds__(256) dq_merge(Dims D, const int32_t* __restrict__ sel,
+                                                const uint16_t* __restrict__ part_dq, float* __restrict__ dq) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int gd8 = D.G * D.d / 8;
+  const int64_t row = i / gd8;  // (s, t, g)
+  if (row >= (int64_t)D.S * D.T * D.Hkv) return;
+  const int c8 = (int)(i % gd8);
+  const int g = (int)(row % D.Hkv);
+  const int t = (int)((row / D.Hkv) % D.T);
+  const int s = (int)(row / ((int64_t)D.Hkv * D.T));
+  const int32_t* sl = sel + (((int64_t)s * D.Hkv + g) * D.T + t) * D.k;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int slot = 0; slot < D.k; ++slot) {
+    if (sl[slot] < 0) continue;
+    const uint4 u = *reinterpret_cast<const uint4*>(part_dq + (row * D.k + slot) * (int64_t)D.G * D.d + c8 * 8);
+    const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      acc[2 * x] += bf16_to_f32((uint16_t)(wv[x] & 0xFFFFu));
+      acc[2 * x + 1] += bf16_to_f32((uint16_t)(wv[x] >> 16));
+    }
+  }
+  float* o = dq + (((int64_t)s * D.T + t) * D.H + (int64_t)g * D.G) * D.d + c8 * 8;
+  *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 // Per row: KL(teacher || student) over the selected blocks and d loss / d block score.
@@ -431,6 +493,7 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
 struct BwdWs {
   WorkList wlst;
   float* drow;
+  uint16_t* part_dq;  // [S, T, Hkv, k, G, d] bf16
 };
 
 BwdWs backward_layout(const Dims& D, void* base, size_t* total) {
@@ -442,6 +505,8 @@ BwdWs backward_layout(const Dims& D, void* base, size_t* total) {
   size_t off = align_up(wlb, 256);
   w.drow = p ? reinterpret_cast<float*>(p + off) : nullptr;
   off += align_up((size_t)D.S * D.T * D.H * sizeof(float), 256);
+  w.part_dq = p ? reinterpret_cast<uint16_t*>(p + off) : nullptr;
+  off += align_up((size_t)D.S * D.T * D.Hkv * D.k * D.G * D.d * sizeof(uint16_t), 256);
   *total = off;
   return w;
 }
@@ -455,11 +520,11 @@ hipError_t zero(float* p, int64_t n, hipStream_t st) {
 
 template <int DH, int G>
 void launch_bwd_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                  const float* lse, const float* drow, const WorkList& wl, const int32_t* entries, float* dq,
-                  float* dk, float* dv, hipStream_t st) {
+                  const float* lse, const float* drow, const WorkList& wl, const int32_t* entries,
+                  uint16_t* part_dq, float* dk, float* dv, hipStream_t st) {
   const int64_t grid = (wl.ub + 7) / 8 * 8 + 8;
   hipLaunchKernelGGL((attn_bwd<DH, G>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, dout, lse, drow,
-                     wl.wl, wl.n_items, entries, dq, dk, dv);
+                     wl.wl, wl.n_items, entries, part_dq, dk, dv);
 }
 
 }  // namespace
@@ -471,15 +536,14 @@ size_t backward_workspace_bytes(const Dims& D) {
 }
 
 hipError_t launch_attn_backward(const Dims& D, const void* q, const void* k, const void* v, const void* out,
-                                const void* dout, const float* lse, const int32_t* off, const int32_t* entries,
-                                float* dq, float* dk, float* dv, void* ws, hipStream_t st) {
+                                const void* dout, const float* lse, const int32_t* sel, const int32_t* off,
+                                const int32_t* entries, float* dq, float* dk, float* dv, void* ws, hipStream_t st) {
   size_t total = 0;
   const BwdWs w = backward_layout(D, ws, &total);
   hipError_t e;
   {
     LaunchScope scope("bwd_zero", st);
-    e = zero(dq, (int64_t)D.S * D.T * D.H * D.d, st);
-    if (e == hipSuccess) e = zero(dk, (int64_t)D.S * D.Hkv * D.N * D.d, st);
+    e = zero(dk, (int64_t)D.S * D.Hkv * D.N * D.d, st);
     if (e == hipSuccess) e = zero(dv, (int64_t)D.S * D.Hkv * D.N * D.d, st);
   }
   if (e != hipSuccess) return e;
@@ -498,18 +562,27 @@ hipError_t launch_attn_backward(const Dims& D, const void* q, const void* k, con
   if (e != hipSuccess) return e;
   e = launch_work_list(D, off, kRows, w.wlst, st);
   if (e != hipSuccess) return e;
-  LaunchScope scope("attn_bwd", st);
   const uint16_t *qb = static_cast<const uint16_t*>(q), *kb = static_cast<const uint16_t*>(k),
                  *vb = static_cast<const uint16_t*>(v), *gb = static_cast<const uint16_t*>(dout);
-#define MSA_BWD_CASE(DH_, G_)                                                                  \
-  if (D.d == DH_ && D.G == G_) {                                                               \
-    launch_bwd_t<DH_, G_>(D, qb, kb, vb, gb, lse, w.drow, w.wlst, entries, dq, dk, dv, st);  \
-    return hipGetLastError();                                                                  \
+  bool launched = false;
+  {
+    LaunchScope scope("attn_bwd", st);
+#define MSA_BWD_CASE(DH_, G_)                                                                          \
+  if (!launched && D.d == DH_ && D.G == G_) {                                                          \
+    launch_bwd_t<DH_, G_>(D, qb, kb, vb, gb, lse, w.drow, w.wlst, entries, w.part_dq, dk, dv, st);   \
+    launched = true;                                                                                   \
   }
-  MSA_BWD_CASE(128, 8); MSA_BWD_CASE(128, 1); MSA_BWD_CASE(128, 2); MSA_BWD_CASE(128, 4); MSA_BWD_CASE(128, 16);
-  MSA_BWD_CASE(64, 8); MSA_BWD_CASE(64, 1); MSA_BWD_CASE(64, 2); MSA_BWD_CASE(64, 4); MSA_BWD_CASE(64, 16);
+    MSA_BWD_CASE(128, 8); MSA_BWD_CASE(128, 1); MSA_BWD_CASE(128, 2); MSA_BWD_CASE(128, 4); MSA_BWD_CASE(128, 16);
+    MSA_BWD_CASE(64, 8); MSA_BWD_CASE(64, 1); MSA_BWD_CASE(64, 2); MSA_BWD_CASE(64, 4); MSA_BWD_CASE(64, 16);
 #undef MSA_BWD_CASE
-  return hipErrorInvalidValue;
+  }
+  if (!launched) return hipErrorInvalidValue;
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nthreads = (int64_t)D.S * D.T * D.Hkv * (D.G * D.d / 8);
+  LaunchScope scope("dq_merge", st);
+  hipLaunchKernelGGL(dq_merge, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, D, sel, w.part_dq, dq);
+  return hipGetLastError();
 }
 
 hipError_t launch_index_kl(const Dims& D, const float* scores, const int32_t* sel, const float* mass, float sigma,

@@ -385,7 +385,7 @@ msa_status msa_sparse_attn_prefill_train(const msa_problem* prob, const void* q,
 
 msa_status msa_sparse_attn_backward(const msa_problem* prob, const void* q, const void* k,
                                     const void* v, const void* out, const void* dout,
-                                    const float* lse, const int32_t* csr_offsets,
+                                    const float* lse, const int32_t* sel, const int32_t* csr_offsets,
                                     const int32_t* csr_entries, float* dq, float* dk, float* dv,
                                     void* workspace, size_t workspace_bytes, void* stream) {
   msa::Dims D;
@@ -398,6 +398,7 @@ msa_status msa_sparse_attn_backward(const msa_problem* prob, const void* q, cons
   REQUIRE_PTR(out);
   REQUIRE_PTR(dout);
   REQUIRE_PTR(lse);
+  REQUIRE_PTR(sel);
   REQUIRE_PTR(csr_offsets);
   REQUIRE_PTR(csr_entries);
   REQUIRE_PTR(dq);
@@ -408,8 +409,8 @@ msa_status msa_sparse_attn_backward(const msa_problem* prob, const void* q, cons
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_sparse_attn_backward needs %zu workspace bytes, got %zu", need,
                 workspace_bytes);
   REQUIRE_PTR(workspace);
-  return device_status(msa::launch_attn_backward(D, q, k, v, out, dout, lse, csr_offsets, csr_entries, dq, dk, dv,
-                                                 workspace, (hipStream_t)stream),
+  return device_status(msa::launch_attn_backward(D, q, k, v, out, dout, lse, sel, csr_offsets, csr_entries, dq, dk,
+                                                 dv, workspace, (hipStream_t)stream),
                        "msa_sparse_attn_backward launch");
 }
 

@@ -69,8 +69,8 @@ hipError_t launch_work_list(const Dims& D, const int32_t* off, int R, const Work
 // Training path (backward.hip).
 size_t backward_workspace_bytes(const Dims& D);
 hipError_t launch_attn_backward(const Dims& D, const void* q, const void* k, const void* v, const void* out,
-                                const void* dout, const float* lse, const int32_t* off, const int32_t* entries,
-                                float* dq, float* dk, float* dv, void* ws, hipStream_t st);
+                                const void* dout, const float* lse, const int32_t* sel, const int32_t* off,
+                                const int32_t* entries, float* dq, float* dk, float* dv, void* ws, hipStream_t st);
 hipError_t launch_index_kl(const Dims& D, const float* scores, const int32_t* sel, const float* mass, float sigma,
                            float* loss, float* dscore, hipStream_t st);
 size_t index_backward_workspace_bytes(const Dims& D);

@@ -242,14 +242,16 @@ msa_status msa_sparse_attn_prefill_train(const msa_problem* prob, const void* q,
                                          size_t workspace_bytes, void* stream);
 
 /* Gradients of sum(dout * out) for the main branch, out being the prefill output for the
- * same q, k, v and selection (dout, out bf16 [S, T, H, d]; lse from the call above):
+ * same q, k, v and selection (dout, out bf16 [S, T, H, d]; lse from the call above; sel and
+ * the csr lists of the forward):
  *   dq float32 [S, T, H, d], dk and dv float32 [S, Hkv, N, d].
- * The KV block is the outer loop (csr lists from msa_invert_selection).  Accumulation
- * uses float atomics: the result is exact up to the order of float32 additions.
- * workspace: msa_workspace_bytes(prob, MSA_CALL_BACKWARD) bytes. */
+ * The KV block is the outer loop.  dq is summed from bf16 per-(row, slot) partials; dk and
+ * dv combine work items with float atomics (exact up to the order of float32 additions).
+ * workspace: msa_workspace_bytes(prob, MSA_CALL_BACKWARD) bytes (it holds the dq partials:
+ * S * T * Hkv * k * G * d bf16 values). */
 msa_status msa_sparse_attn_backward(const msa_problem* prob, const void* q, const void* k,
                                     const void* v, const void* out, const void* dout,
-                                    const float* lse, const int32_t* csr_offsets,
+                                    const float* lse, const int32_t* sel, const int32_t* csr_offsets,
                                     const int32_t* csr_entries, float* dq, float* dk, float* dv,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
