@@ -71,10 +71,12 @@ def _load():
         lib.orc_index_backward.argtypes = [i64, i32, i32, i32, i64, P, P, P, P, P, P, P]
         lib.orc_index_argmax.argtypes = [i64, i32, i32, i32, i64, P, P, P, P, P, P, P, P]
         lib.orc_index_backward_at.argtypes = [i64, i32, i32, i64, P, P, P, P, P, P]
+        lib.orc_token_topk.argtypes = [i64, i32, i64, P, P, P]
         lib.orc_num_threads.restype = ctypes.c_int
         for f in ("orc_index_scores", "orc_block_topk", "orc_invert", "orc_attention",
                   "orc_attention_partials", "orc_lse_merge", "orc_attention_train", "orc_attention_backward",
-                  "orc_index_kl", "orc_index_backward", "orc_index_argmax", "orc_index_backward_at"):
+                  "orc_index_kl", "orc_index_backward", "orc_index_argmax", "orc_index_backward_at",
+                  "orc_token_topk"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -298,6 +300,26 @@ def slice_index_backward_at(qI_rows, jstar, KI, dscore):
     _load().orc_index_backward_at(KI.shape[0], dI, k, R, _p(qI_rows), _p(jstar), _p(KI), _p(dscore), _p(dqI),
                                   _p(dKI))
     return dqI, dKI
+
+
+def slice_token_scores(qI_rows, pos, kI) -> np.ndarray:
+    """Token-level index scores [R, N] (the block scores with block size 1; NaN past pos)."""
+    return slice_index_scores(qI_rows, pos, kI, 1)
+
+
+def slice_token_topk(scores, pos, budget: int) -> np.ndarray:
+    """scores [R, N] -> [R, budget] ascending positions of the top tokens (-1 padded)."""
+    scores = np.ascontiguousarray(np.nan_to_num(np.asarray(scores, dtype=np.float64), nan=-np.inf))
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    R, N = scores.shape
+    out = np.empty((R, budget), dtype=np.int32)
+    _load().orc_token_topk(N, budget, R, _p(scores), _p(pos), _p(out))
+    return out
+
+
+def slice_token_attention(q_rows, pos, tok_rows, K, V, scale: float) -> np.ndarray:
+    """Attention over selected token positions (the block attention with block size 1)."""
+    return slice_attention(q_rows, pos, tok_rows, K, V, 1, scale)
 
 
 # ------------------------------------------------------- whole-tensor conveniences

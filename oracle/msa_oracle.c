@@ -533,6 +533,44 @@ void orc_index_backward_at(int64_t N, int dI, int k, int64_t nrows, const double
         }
 }
 
+/* ------------------------------------------------------------------ token level
+ * [P1 分歧一：颗粒度: DSA picks 2048 single tokens per query where MSA picks 16 blocks
+ *  of 128 -- the same budget; P3 DSA entry: the lightning indexer scores every earlier
+ *  token and the top-k single tokens are kept.]  Token scores are orc_index_scores with
+ *  block size 1, token attention is orc_attention with block size 1; the selection differs:
+ *  no token is forced (reading: the pages name no forced rule for token-level selection).
+ * For each row r: the `budget` positions j <= pos[r] with the largest scores, ordered by
+ * (score desc, position asc), emitted in ascending position order; when fewer than budget
+ * positions are eligible all are taken; -1 pads.  scores is [nrows, N] (entries j > pos
+ * are not read); out is [nrows, budget]. */
+void orc_token_topk(int64_t N, int budget, int64_t nrows, const double *scores,
+                    const int64_t *pos, int32_t *out)
+{
+#pragma omp parallel
+    {
+        unsigned char *taken = (unsigned char *)malloc((size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const double *sc = scores + r * N;
+            const int64_t n = pos[r] + 1;
+            memset(taken, 0, (size_t)N);
+            const int64_t want = n < budget ? n : budget;
+            for (int64_t c = 0; c < want; ++c) {      /* repeated arg-max, lower position on ties */
+                int64_t best = -1;
+                for (int64_t j = 0; j < n; ++j)
+                    if (!taken[j] && (best < 0 || sc[j] > sc[best])) best = j;
+                taken[best] = 1;
+            }
+            int32_t *o = out + r * budget;
+            int64_t w = 0;
+            for (int64_t j = 0; j < n; ++j)
+                if (taken[j]) o[w++] = (int32_t)j;
+            for (; w < budget; ++w) o[w] = -1;
+        }
+        free(taken);
+    }
+}
+
 /* Threads OpenMP will use for the parallel loops above (reported beside timings). */
 #ifdef _OPENMP
 #include <omp.h>

@@ -481,3 +481,46 @@ def test_index_argmax_and_scatter_agree_with_the_fused_backward():
     b = oracle.slice_index_backward_at(qI, jb, KI, dscore)
     np.testing.assert_allclose(a[0], b[0], rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(a[1], b[1], rtol=1e-14, atol=1e-14)
+
+
+# ------------------------------------------------------------------ token level
+# "分歧一：颗粒度" (DSA: 2048 single tokens per query, MSA: 16 blocks x 128, same budget) and
+# the DSA entry of "稀疏注意力速览" (top-k single tokens by the indexer's token scores).
+@pytest.mark.parametrize("budget,ties", [(5, False), (5, True), (64, False), (300, False)])
+def test_token_topk_matches_sort_brute_force(budget, ties):
+    N, T = 200, 40
+    pos = _pos(N, T)
+    sc = RNG.integers(0, 4, (T, N)).astype(float) if ties else RNG.standard_normal((T, N))
+    got = oracle.slice_token_topk(sc, pos, budget)
+    for t in range(T):
+        n = pos[t] + 1
+        order = np.lexsort((np.arange(n), -sc[t, :n]))     # score desc, position asc
+        want = np.sort(order[:min(budget, n)])
+        np.testing.assert_array_equal(got[t, :len(want)], want)
+        assert np.all(got[t, len(want):] == -1)
+
+
+def test_token_scores_are_the_block_scores_of_block_size_one():
+    N, T, dI = 60, 60, 7
+    qI, kI = RNG.standard_normal((T, dI)), RNG.standard_normal((N, dI))
+    pos = _pos(N, T)
+    got = oracle.slice_token_scores(qI, pos, kI)
+    ref = qI @ kI.T
+    causal = np.arange(N)[None, :] <= pos[:, None]
+    np.testing.assert_allclose(got[causal], ref[causal], rtol=1e-12, atol=1e-12)
+    assert np.all(np.isnan(got[~causal]))
+
+
+def test_token_attention_matches_dense_masked_brute_force():
+    N, T, G, d = 90, 30, 3, 8
+    q, K, V = _rand_attn(N, T, G, d)
+    pos = _pos(N, T)
+    sc = oracle.slice_token_scores(RNG.standard_normal((T, 5)), pos, RNG.standard_normal((N, 5)))
+    tok = oracle.slice_token_topk(sc, pos, 17)
+    got = oracle.slice_token_attention(q, pos, tok, K, V, 0.29)
+    ref = bf.attention(q, K, V, pos, tok, 1, 0.29)              # block size 1 = single tokens
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    # the budget covers every causal token: dense causal attention
+    full = oracle.slice_token_attention(q, pos, oracle.slice_token_topk(sc, pos, N), K, V, 0.29)
+    dense = bf.attention(q, K, V, pos, np.tile(np.arange(N, dtype=np.int32), (T, 1)), 1, 0.29)
+    np.testing.assert_allclose(full, dense, rtol=1e-12, atol=1e-13)
