@@ -340,6 +340,53 @@ def paged_decode(args, msa, wd, xd):
                 us_per_step=ms * 1e3, us_per_token_amortised=ms * 1e3 / S, stages=st)
 
 
+def token_decode(args, msa, wd, xd, block_sel):
+    """The decode workload with token-level selection at the block path's budget (16 x 128 =
+    2048 tokens, the pages' granularity comparison), outside the timed step: step time per
+    stage and the share of the token-level picks that fall inside the blocks the block-level
+    step chose."""
+    import torch
+    budget = wd.k * 128
+    prob = wd.problem()
+    tb = msa.alloc_token_decode(prob, budget)
+
+    def step():
+        msa.run_token_decode(prob, xd["q"], xd["k"], xd["v"], xd["q_idx"], xd["k_idx"], tb, budget)
+    step()
+    torch.cuda.synchronize()
+    msa.profiler_read(None, reset=True)
+    msa.profiler_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    msa.profiler_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    st = {}
+    for kn in ("token_scores", "token_topk", "token_attn", "token_merge"):
+        tms, nl = msa.profiler_read(kn, reset=False)
+        if nl:
+            st[kn] = dict(ms=tms / nl)
+    msa.profiler_read(None, reset=True)
+    if "token_scores" in st:
+        kbytes = wd.S * wd.Hkv * wd.N * wd.dI * 2.0 + 4.0 * wd.S * wd.Hkv * wd.N
+        sec = st["token_scores"]["ms"] / 1e3
+        st["token_scores"].update(roofline(2.0 * wd.dI * wd.S * wd.Hkv * wd.N, kbytes, sec))
+    if "token_topk" in st:
+        sec = st["token_topk"]["ms"] / 1e3
+        st["token_topk"].update(roofline(0.0, 5 * 4.0 * wd.S * wd.Hkv * wd.N, sec))   # 5 passes over the scores
+    tok = tb.sel_tok                                            # [S, Hkv, 1, budget]
+    blk = block_sel                                             # [S, Hkv, 1, k]
+    inside = ((tok.unsqueeze(-1) // 128) == blk.unsqueeze(-2)).any(-1) & (tok >= 0)
+    share = inside.sum().item() / max(1, (tok >= 0).sum().item())
+    del tb
+    return dict(workload="%s, token-level selection of %d tokens" % (wd.description, budget),
+                us_per_step=ms * 1e3, us_per_token_amortised=ms * 1e3 / wd.S, stages=st,
+                share_of_token_picks_inside_the_block_selection=share)
+
+
 def train_step(args, msa, wl):
     """One training step of wl, outside the timed prefill step: index scores, top-k,
     inversion, the forward with lse and teacher mass (every pair in Outer-Gather-Q order),
@@ -581,6 +628,12 @@ def main():
                     stages=k8, selection_overlap_with_bf16_keys=overlap)
         print("[bench] decode with E4M3 index keys: %.3f ms per step" % ms8, file=sys.stderr, flush=True)
 
+    dect = None
+    if db is not None:
+        dect = token_decode(args, msa, wd, xd, db.sel)
+        print("[bench] decode with token-level selection: %.3f ms per step" % (dect["us_per_step"] / 1e3),
+              file=sys.stderr, flush=True)
+
     decp = None
     if db is not None and not args.no_paged_decode:
         decp = paged_decode(args, msa, wd, xd)
@@ -606,7 +659,8 @@ def main():
         "config": {"workload": wp.description, "batch": wp.S, "seq_len": wp.T, "num_heads": wp.H,
                    "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
         "prefill_ms": prefill_ms, "wall_s_timed": wall,
-        "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "training_step": trn, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
+        "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "decode_token_level": dect,
+        "training_step": trn, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
         "selection_structure": selection_structure(wp, pb.sel, pb.csr_offsets),
         "attention_pairs": split["pairs"],
     }

@@ -26,7 +26,8 @@ EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_invert_selection", "msa_s
             "msa_sparse_attn_decode", "msa_workspace_bytes", "msa_status_string",
             "msa_last_error_message", "msa_profiler_enable", "msa_profiler_read", "msa_index_scores_kv",
             "msa_block_topk_kv", "msa_sparse_attn_decode_kv", "msa_sparse_attn_prefill_train",
-            "msa_sparse_attn_backward", "msa_index_kl", "msa_index_backward")
+            "msa_sparse_attn_backward", "msa_index_kl", "msa_index_backward", "msa_token_scores",
+            "msa_token_topk", "msa_token_attn_decode", "msa_token_workspace_bytes")
 
 
 class MSAError(RuntimeError):
@@ -105,6 +106,13 @@ def lib():
         L.msa_sparse_attn_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_index_kl.argtypes = [PP, P, P, P, ctypes.c_float, P, P, P]
         L.msa_index_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_token_scores.argtypes = [PP, P, P, P, P]
+        L.msa_token_topk.argtypes = [PP, ctypes.c_int32, P, P, P]
+        L.msa_token_attn_decode.argtypes = [PP, ctypes.c_int32, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_token_workspace_bytes.argtypes = [PP, ctypes.c_int32]
+        L.msa_token_workspace_bytes.restype = ctypes.c_size_t
+        for f in ("msa_token_scores", "msa_token_topk", "msa_token_attn_decode"):
+            getattr(L, f).restype = st
         for f in ("msa_index_scores", "msa_block_topk", "msa_invert_selection",
                   "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_index_scores_kv",
                   "msa_block_topk_kv", "msa_sparse_attn_decode_kv", "msa_sparse_attn_prefill_train",
@@ -237,6 +245,26 @@ def index_backward(prob: Problem, q_idx, k_idx, csr_offsets, csr_entries, dscore
     _check(lib().msa_index_backward(ctypes.byref(prob), _ptr(q_idx), _ptr(k_idx), _ptr(csr_offsets),
                                     _ptr(csr_entries), _ptr(dscores), _ptr(dq_idx), _ptr(dk_idx), _ptr(argmax),
                                     _ptr(workspace), workspace_bytes_, _stream(stream, q_idx)))
+
+
+def token_scores(prob: Problem, q_idx, k_idx, scores, stream=None) -> None:
+    _check(lib().msa_token_scores(ctypes.byref(prob), _ptr(q_idx), _ptr(k_idx), _ptr(scores), _stream(stream, q_idx)))
+
+
+def token_topk(prob: Problem, budget: int, scores, sel_tok, stream=None) -> None:
+    _check(lib().msa_token_topk(ctypes.byref(prob), int(budget), _ptr(scores), _ptr(sel_tok),
+                                _stream(stream, scores)))
+
+
+def token_workspace_bytes(prob: Problem, budget: int) -> int:
+    return int(lib().msa_token_workspace_bytes(ctypes.byref(prob), int(budget)))
+
+
+def token_attn_decode(prob: Problem, budget: int, q, k_cache, v_cache, sel_tok, out, workspace,
+                      workspace_bytes_: int, stream=None) -> None:
+    _check(lib().msa_token_attn_decode(ctypes.byref(prob), int(budget), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(sel_tok), _ptr(out), _ptr(workspace), workspace_bytes_,
+                                       _stream(stream, q)))
 
 
 def profiler_enable(on: bool) -> None:
@@ -380,3 +408,30 @@ def run_train_step(prob: Problem, q, k, v, q_idx, k_idx, dout, bufs: TrainBuffer
     index_kl(prob, f.scores, f.sel, bufs.mass, sigma, bufs.loss, bufs.dscores, stream)
     index_backward(prob, q_idx, k_idx, f.csr_offsets, f.csr_entries, bufs.dscores, bufs.dq_idx, bufs.dk_idx,
                    bufs.argmax, bufs.ws_ibwd, bufs.ws_ibwd.numel(), stream)
+
+
+@dataclass
+class TokenBuffers:
+    scores: object
+    sel_tok: object
+    ws: object
+    out: object
+
+
+def alloc_token_decode(prob: Problem, budget: int = 2048, device="cuda") -> TokenBuffers:
+    import torch
+    S, T, N, Hkv = prob.batch, prob.num_q, prob.kv_len, prob.num_kv_heads
+    odt = torch.bfloat16
+    return TokenBuffers(
+        scores=torch.empty((S, Hkv, T, N), dtype=torch.float32, device=device),
+        sel_tok=torch.empty((S, Hkv, T, budget), dtype=torch.int32, device=device),
+        ws=torch.empty((max(token_workspace_bytes(prob, budget), 1),), dtype=torch.uint8, device=device),
+        out=torch.empty((S, T, prob.num_heads, prob.head_dim), dtype=odt, device=device))
+
+
+def run_token_decode(prob: Problem, q, k_cache, v_cache, q_idx, k_idx, bufs: TokenBuffers, budget: int = 2048,
+                     stream=None) -> None:
+    """Token-level decode step: token scores -> top-budget tokens -> attention over them."""
+    token_scores(prob, q_idx, k_idx, bufs.scores, stream)
+    token_topk(prob, budget, bufs.scores, bufs.sel_tok, stream)
+    token_attn_decode(prob, budget, q, k_cache, v_cache, bufs.sel_tok, bufs.out, bufs.ws, bufs.ws.numel(), stream)

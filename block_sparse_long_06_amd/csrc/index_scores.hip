@@ -101,8 +101,10 @@ constexpr int kStreamT = 8;
 constexpr int kStreamBlocks = 8;
 
 // TK = uint16_t (bf16 keys: 8 dims per 16-byte lane load) or uint8_t (E4M3 keys: 16
-// dims per 16-byte lane load, decoded with the hardware converter).
-template <int DI, int TQ, typename TK>
+// dims per 16-byte lane load, decoded with the hardware converter).  TOKEN: write every
+// causal key's score to tok [S, Hkv, T, N] instead of the block maxima (token-level
+// selection).
+template <int DI, int TQ, typename TK, bool TOKEN = false>
 __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t* __restrict__ q_idx,
                                                          const TK* __restrict__ k_idx,
                                                          float* __restrict__ scores) {
@@ -165,9 +167,14 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
         for (int x = 0; x < DPL; ++x) acc = fmaf(qv[tq][x], kv[x], acc);
 #pragma unroll
         for (int o = 1; o < CPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
-        if (j <= pq[tq]) m[tq] = fmaxf(m[tq], acc);
+        if constexpr (TOKEN) {
+          if (col == 0 && tq < T && j <= pq[tq]) scores[(sg * T + tq) * (int64_t)D.N + j] = acc;
+        } else {
+          if (j <= pq[tq]) m[tq] = fmaxf(m[tq], acc);
+        }
       }
     }
+    if constexpr (TOKEN) continue;
 #pragma unroll
     for (int tq = 0; tq < TQ; ++tq) {
       float x = m[tq];
@@ -201,7 +208,33 @@ void launch_stream(const Dims& D, const uint16_t* q, const TK* k, float* sc, hip
   else launch_stream_di<128>(D, q, k, sc, st);
 }
 
+template <int DI, typename TK>
+void launch_token_di(const Dims& D, const uint16_t* q, const TK* k, float* tok, hipStream_t st) {
+  dim3 grid((unsigned)((D.nb + kStreamBlocks - 1) / kStreamBlocks), (unsigned)(D.S * D.Hkv));
+  if (D.T == 1)
+    hipLaunchKernelGGL((idx_scores_stream<DI, 1, TK, true>), grid, dim3(256), 0, st, D, q, k, tok);
+  else
+    hipLaunchKernelGGL((idx_scores_stream<DI, kStreamT, TK, true>), grid, dim3(256), 0, st, D, q, k, tok);
+}
+
+template <typename TK>
+void launch_token(const Dims& D, const uint16_t* q, const TK* k, float* tok, hipStream_t st) {
+  if (D.dI == 32) launch_token_di<32>(D, q, k, tok, st);
+  else if (D.dI == 64) launch_token_di<64>(D, q, k, tok, st);
+  else launch_token_di<128>(D, q, k, tok, st);
+}
+
 }  // namespace
+
+// Token-level scores for decode shapes (bf16 queries, T <= kStreamT): tok [S, Hkv, T, N].
+hipError_t launch_token_scores(const Dims& D, const void* q_idx, const void* k_idx, float* tok, hipStream_t st) {
+  if (D.dtype != MSA_BF16 || D.T > kStreamT) return hipErrorInvalidValue;
+  const uint16_t* q = static_cast<const uint16_t*>(q_idx);
+  LaunchScope scope("token_scores", st);
+  if (D.kdtype == MSA_FP8_E4M3) launch_token(D, q, static_cast<const uint8_t*>(k_idx), tok, st);
+  else launch_token(D, q, static_cast<const uint16_t*>(k_idx), tok, st);
+  return hipGetLastError();
+}
 
 hipError_t launch_index_scores(const Dims& D, const void* q_idx, const void* k_idx, float* scores,
                                hipStream_t st) {

@@ -128,6 +128,15 @@ msa_status apply_layout(const msa_kv_layout* L, msa::Dims* D) {
   return MSA_OK;
 }
 
+// The token-level calls: decode shapes, bf16 queries.
+msa_status check_token(const msa::Dims& D, int budget) {
+  if (D.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "the token-level calls need dtype MSA_BF16");
+  if (D.T > 8) return fail(MSA_ERR_UNSUPPORTED, "the token-level calls take num_q <= 8 (got %d)", D.T);
+  if (budget < 1 || budget > 8192) return fail(MSA_ERR_UNSUPPORTED, "budget must be in 1 .. 8192 (got %d)", budget);
+  if ((int64_t)D.S * D.Hkv * D.T > 0x7FFFFFFF) return fail(MSA_ERR_UNSUPPORTED, "too many rows");
+  return MSA_OK;
+}
+
 // The training calls run the bf16 kernels only.
 msa_status check_train(const msa::Dims& D, bool index) {
   if (D.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "the training calls need dtype MSA_BF16");
@@ -211,6 +220,9 @@ size_t msa_workspace_bytes(const msa_problem* prob, int which) {
     case MSA_CALL_BACKWARD:
       if (check_problem(prob, &D, false, true) != MSA_OK || check_train(D, false) != MSA_OK) return 0;
       return msa::backward_workspace_bytes(D);
+    case MSA_CALL_TOKEN_DECODE:
+      if (check_problem(prob, &D, false, true) != MSA_OK || check_token(D, 2048) != MSA_OK) return 0;
+      return msa::token_workspace_bytes(D, 2048);
     case MSA_CALL_INDEX_BACKWARD:
       if (check_problem(prob, &D, true, false) != MSA_OK || check_train(D, true) != MSA_OK) return 0;
       return msa::index_backward_workspace_bytes(D);
@@ -455,6 +467,59 @@ msa_status msa_index_backward(const msa_problem* prob, const void* q_idx, const 
   return device_status(msa::launch_index_backward(D, q_idx, k_idx, csr_offsets, csr_entries, dscores, dq_idx,
                                                   dk_idx, argmax, workspace, (hipStream_t)stream),
                        "msa_index_backward launch");
+}
+
+msa_status msa_token_scores(const msa_problem* prob, const void* q_idx, const void* k_idx, float* scores,
+                            void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, true, false);
+  if (st != MSA_OK) return st;
+  if ((st = check_token(D, 1)) != MSA_OK) return st;
+  REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(k_idx);
+  REQUIRE_PTR(scores);
+  return device_status(msa::launch_token_scores(D, q_idx, k_idx, scores, (hipStream_t)stream),
+                       "msa_token_scores launch");
+}
+
+msa_status msa_token_topk(const msa_problem* prob, int32_t budget, const float* scores, int32_t* sel_tok,
+                          void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, false);
+  if (st != MSA_OK) return st;
+  if ((st = check_token(D, budget)) != MSA_OK) return st;
+  REQUIRE_PTR(scores);
+  REQUIRE_PTR(sel_tok);
+  return device_status(msa::launch_token_topk(D, budget, scores, sel_tok, (hipStream_t)stream),
+                       "msa_token_topk launch");
+}
+
+size_t msa_token_workspace_bytes(const msa_problem* prob, int32_t budget) {
+  msa::Dims D;
+  if (check_problem(prob, &D, false, true) != MSA_OK || check_token(D, budget) != MSA_OK) return 0;
+  return msa::token_workspace_bytes(D, budget);
+}
+
+msa_status msa_token_attn_decode(const msa_problem* prob, int32_t budget, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* sel_tok, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, true);
+  if (st != MSA_OK) return st;
+  if ((st = check_token(D, budget)) != MSA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(sel_tok);
+  REQUIRE_PTR(out);
+  const size_t need = msa::token_workspace_bytes(D, budget);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_token_attn_decode needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(msa::launch_token_attn(D, budget, q, k_cache, v_cache, sel_tok, out, workspace,
+                                              (hipStream_t)stream),
+                       "msa_token_attn_decode launch");
 }
 
 msa_status msa_profiler_enable(int on) {

@@ -66,6 +66,13 @@ struct WorkList {
 WorkList work_list_layout(const Dims& D, int R, void* base, size_t* total);
 hipError_t launch_work_list(const Dims& D, const int32_t* off, int R, const WorkList& w, hipStream_t st);
 
+// Token-level selection (index_scores.hip, token.hip).
+hipError_t launch_token_scores(const Dims& D, const void* q_idx, const void* k_idx, float* tok, hipStream_t st);
+hipError_t launch_token_topk(const Dims& D, int budget, const float* tok, int32_t* sel_tok, hipStream_t st);
+size_t token_workspace_bytes(const Dims& D, int budget);
+hipError_t launch_token_attn(const Dims& D, int budget, const void* q, const void* k, const void* v,
+                             const int32_t* sel_tok, void* out, void* ws, hipStream_t st);
+
 // Training path (backward.hip).
 size_t backward_workspace_bytes(const Dims& D);
 hipError_t launch_attn_backward(const Dims& D, const void* q, const void* k, const void* v, const void* out,

@@ -84,7 +84,7 @@ typedef struct {
 
 /* Which call a workspace size is asked for (msa_workspace_bytes). */
 enum { MSA_CALL_INVERT = 2, MSA_CALL_PREFILL = 3, MSA_CALL_DECODE = 4, MSA_CALL_BACKWARD = 5,
-       MSA_CALL_INDEX_BACKWARD = 6 };
+       MSA_CALL_INDEX_BACKWARD = 6, MSA_CALL_TOKEN_DECODE = 7 };
 
 /*
  * a1. Index branch scoring fused with the causal block max-pool
@@ -272,6 +272,31 @@ msa_status msa_index_backward(const msa_problem* prob, const void* q_idx, const 
                               const int32_t* csr_offsets, const int32_t* csr_entries,
                               const float* dscores, float* dq_idx, float* dk_idx, int32_t* argmax,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Token-level selection on the same indexer, the granularity the pages compare MSA with
+ * ([P1] 分歧一：颗粒度: DSA keeps 2048 single tokens per query, MSA 16 blocks x 128 -- the
+ * same budget; [P3] DSA entry).  Decode shapes: num_q <= 8, dtype MSA_BF16 (index keys
+ * bf16 or E4M3); other problems return MSA_ERR_UNSUPPORTED.  budget: 1 .. 8192.
+ *
+ * msa_token_scores: scores [S, Hkv, T, N] float32, scores[s,g,t,j] = q_idx[s,g,t] . k_idx[s,g,j]
+ *   for j <= p_t; entries j > p_t are not written.
+ * msa_token_topk: sel_tok [S, Hkv, T, budget] int32: the budget positions j <= p_t with the
+ *   largest scores (ties to the lower position; no forced token), in ascending order, -1
+ *   padded when fewer are eligible.  Reads only scores[s,g,t,0..p_t].
+ * msa_token_attn_decode: out [S, T, H, d]: for each query head, the exact softmax attention
+ *   over the row's selected positions (the block-level definition with block size 1).
+ *   workspace: msa_workspace_bytes(prob, MSA_CALL_TOKEN_DECODE) bytes for budget = 2048;
+ *   use msa_token_workspace_bytes for another budget.
+ */
+msa_status msa_token_scores(const msa_problem* prob, const void* q_idx, const void* k_idx, float* scores,
+                            void* stream);
+msa_status msa_token_topk(const msa_problem* prob, int32_t budget, const float* scores, int32_t* sel_tok,
+                          void* stream);
+msa_status msa_token_attn_decode(const msa_problem* prob, int32_t budget, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* sel_tok, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+size_t msa_token_workspace_bytes(const msa_problem* prob, int32_t budget);
 
 /* Device workspace needed by a call (MSA_CALL_*); 0 for an invalid problem or call. */
 size_t msa_workspace_bytes(const msa_problem* prob, int which_call);
