@@ -340,6 +340,44 @@ def paged_decode(args, msa, wd, xd):
                 us_per_step=ms * 1e3, us_per_token_amortised=ms * 1e3 / S, stages=st)
 
 
+def fused_selection(args, msa, wp, xp, pb):
+    """Index scores + top-k fused (no [S, Hkv, T, nb] score matrix) on the prefill workload,
+    outside the timed step: time per call, its workspace against the score matrix of the
+    unfused pair, and whether its selection equals the timed step's."""
+    import torch
+    prob = wp.problem()
+    ws = torch.empty((max(msa.workspace_bytes(prob, msa.MSA_CALL_INDEX_TOPK), 1),), dtype=torch.uint8, device="cuda")
+    sel = torch.empty_like(pb.sel)
+
+    def call():
+        msa.index_topk(prob, xp["q_idx"], xp["k_idx"], sel, ws, ws.numel())
+    call()
+    torch.cuda.synchronize()
+    msa.profiler_read(None, reset=True)
+    msa.profiler_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    msa.profiler_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    st = {}
+    for kn in ("idx_topk_mfma", "topk_merge"):
+        tms, nl = msa.profiler_read(kn, reset=False)
+        if nl:
+            st[kn] = dict(ms=tms / nl)
+    msa.profiler_read(None, reset=True)
+    m = prefill_model(wp.S, wp.T, wp.N, wp.H, wp.Hkv, wp.d, wp.dI, wp.k)
+    if "idx_topk_mfma" in st:
+        st["idx_topk_mfma"].update(roofline(m["idx_scores"]["flops"], 0.0, st["idx_topk_mfma"]["ms"] / 1e3))
+    same = bool(torch.equal(sel, pb.sel))
+    return dict(workload=wp.description + ", index scores + top-k fused", ms_per_call=ms, stages=st,
+                workspace_bytes=int(ws.numel()), score_matrix_bytes=int(pb.scores.numel() * 4),
+                selection_equal_to_the_unfused_calls=same)
+
+
 def token_decode(args, msa, wd, xd, block_sel):
     """The decode workload with token-level selection at the block path's budget (16 x 128 =
     2048 tokens, the pages' granularity comparison), outside the timed step: step time per
@@ -628,6 +666,11 @@ def main():
                     stages=k8, selection_overlap_with_bf16_keys=overlap)
         print("[bench] decode with E4M3 index keys: %.3f ms per step" % ms8, file=sys.stderr, flush=True)
 
+    fsel = fused_selection(args, msa, wp, xp, pb) if wp.k <= 16 else None
+    if fsel is not None:
+        print("[bench] fused index scores + top-k: %.3f ms (equal selection: %s)"
+              % (fsel["ms_per_call"], fsel["selection_equal_to_the_unfused_calls"]), file=sys.stderr, flush=True)
+
     dect = None
     if db is not None:
         dect = token_decode(args, msa, wd, xd, db.sel)
@@ -659,6 +702,7 @@ def main():
         "config": {"workload": wp.description, "batch": wp.S, "seq_len": wp.T, "num_heads": wp.H,
                    "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
         "prefill_ms": prefill_ms, "wall_s_timed": wall,
+        "fused_selection": fsel,
         "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "decode_token_level": dect,
         "training_step": trn, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
         "selection_structure": selection_structure(wp, pb.sel, pb.csr_offsets),

@@ -20,14 +20,15 @@ LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARGUMENT, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_DEVICE = range(5)
 MSA_F32, MSA_BF16, MSA_FP8_E4M3 = 0, 1, 2
-MSA_CALL_INVERT, MSA_CALL_PREFILL, MSA_CALL_DECODE, MSA_CALL_BACKWARD, MSA_CALL_INDEX_BACKWARD = 2, 3, 4, 5, 6
+(MSA_CALL_INVERT, MSA_CALL_PREFILL, MSA_CALL_DECODE, MSA_CALL_BACKWARD, MSA_CALL_INDEX_BACKWARD,
+ MSA_CALL_TOKEN_DECODE, MSA_CALL_INDEX_TOPK) = 2, 3, 4, 5, 6, 7, 8
 
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_invert_selection", "msa_sparse_attn_prefill",
             "msa_sparse_attn_decode", "msa_workspace_bytes", "msa_status_string",
             "msa_last_error_message", "msa_profiler_enable", "msa_profiler_read", "msa_index_scores_kv",
             "msa_block_topk_kv", "msa_sparse_attn_decode_kv", "msa_sparse_attn_prefill_train",
             "msa_sparse_attn_backward", "msa_index_kl", "msa_index_backward", "msa_token_scores",
-            "msa_token_topk", "msa_token_attn_decode", "msa_token_workspace_bytes")
+            "msa_token_topk", "msa_token_attn_decode", "msa_token_workspace_bytes", "msa_index_topk")
 
 
 class MSAError(RuntimeError):
@@ -106,6 +107,8 @@ def lib():
         L.msa_sparse_attn_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_index_kl.argtypes = [PP, P, P, P, ctypes.c_float, P, P, P]
         L.msa_index_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_index_topk.argtypes = [PP, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_index_topk.restype = st
         L.msa_token_scores.argtypes = [PP, P, P, P, P]
         L.msa_token_topk.argtypes = [PP, ctypes.c_int32, P, P, P]
         L.msa_token_attn_decode.argtypes = [PP, ctypes.c_int32, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -173,6 +176,12 @@ def workspace_bytes(prob: Problem, which_call: int) -> int:
 def index_scores(prob: Problem, q_idx, k_idx, scores, stream=None) -> None:
     _check(lib().msa_index_scores(ctypes.byref(prob), _ptr(q_idx), _ptr(k_idx), _ptr(scores),
                                   _stream(stream, q_idx)))
+
+
+def index_topk(prob: Problem, q_idx, k_idx, sel, workspace, workspace_bytes_: int, stream=None) -> None:
+    """Fused scores + top-k: the selection without the [S, Hkv, T, nb] block scores."""
+    _check(lib().msa_index_topk(ctypes.byref(prob), _ptr(q_idx), _ptr(k_idx), _ptr(sel), _ptr(workspace),
+                                workspace_bytes_, _stream(stream, q_idx)))
 
 
 def block_topk(prob: Problem, scores, sel, stream=None) -> None:

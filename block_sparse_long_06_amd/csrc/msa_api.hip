@@ -128,6 +128,13 @@ msa_status apply_layout(const msa_kv_layout* L, msa::Dims* D) {
   return MSA_OK;
 }
 
+// The fused selection: bf16 queries, lists of 15 blocks.
+msa_status check_fused(const msa::Dims& D) {
+  if (D.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "msa_index_topk needs dtype MSA_BF16");
+  if (D.k > 16) return fail(MSA_ERR_UNSUPPORTED, "msa_index_topk supports topk <= 16 (got %d)", D.k);
+  return MSA_OK;
+}
+
 // The token-level calls: decode shapes, bf16 queries.
 msa_status check_token(const msa::Dims& D, int budget) {
   if (D.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "the token-level calls need dtype MSA_BF16");
@@ -220,6 +227,9 @@ size_t msa_workspace_bytes(const msa_problem* prob, int which) {
     case MSA_CALL_BACKWARD:
       if (check_problem(prob, &D, false, true) != MSA_OK || check_train(D, false) != MSA_OK) return 0;
       return msa::backward_workspace_bytes(D);
+    case MSA_CALL_INDEX_TOPK:
+      if (check_problem(prob, &D, true, false) != MSA_OK || check_fused(D) != MSA_OK) return 0;
+      return msa::index_topk_workspace_bytes(D);
     case MSA_CALL_TOKEN_DECODE:
       if (check_problem(prob, &D, false, true) != MSA_OK || check_token(D, 2048) != MSA_OK) return 0;
       return msa::token_workspace_bytes(D, 2048);
@@ -241,6 +251,24 @@ msa_status msa_index_scores(const msa_problem* prob, const void* q_idx, const vo
   REQUIRE_PTR(scores);
   return device_status(msa::launch_index_scores(D, q_idx, k_idx, scores, (hipStream_t)stream),
                        "msa_index_scores launch");
+}
+
+msa_status msa_index_topk(const msa_problem* prob, const void* q_idx, const void* k_idx, int32_t* sel,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, true, false);
+  if (st != MSA_OK) return st;
+  if ((st = check_fused(D)) != MSA_OK) return st;
+  REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(k_idx);
+  REQUIRE_PTR(sel);
+  const size_t need = msa::index_topk_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_index_topk needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(msa::launch_index_topk(D, q_idx, k_idx, sel, workspace, (hipStream_t)stream),
+                       "msa_index_topk launch");
 }
 
 msa_status msa_block_topk(const msa_problem* prob, const float* scores, int32_t* sel,

@@ -66,6 +66,11 @@ struct WorkList {
 WorkList work_list_layout(const Dims& D, int R, void* base, size_t* total);
 hipError_t launch_work_list(const Dims& D, const int32_t* off, int R, const WorkList& w, hipStream_t st);
 
+// a1 + a2 fused (fused_topk.hip): selection without materialising the block scores.
+size_t index_topk_workspace_bytes(const Dims& D);
+hipError_t launch_index_topk(const Dims& D, const void* q_idx, const void* k_idx, int32_t* sel, void* ws,
+                             hipStream_t st);
+
 // Token-level selection (index_scores.hip, token.hip).
 hipError_t launch_token_scores(const Dims& D, const void* q_idx, const void* k_idx, float* tok, hipStream_t st);
 hipError_t launch_token_topk(const Dims& D, int budget, const float* tok, int32_t* sel_tok, hipStream_t st);

@@ -84,7 +84,7 @@ typedef struct {
 
 /* Which call a workspace size is asked for (msa_workspace_bytes). */
 enum { MSA_CALL_INVERT = 2, MSA_CALL_PREFILL = 3, MSA_CALL_DECODE = 4, MSA_CALL_BACKWARD = 5,
-       MSA_CALL_INDEX_BACKWARD = 6, MSA_CALL_TOKEN_DECODE = 7 };
+       MSA_CALL_INDEX_BACKWARD = 6, MSA_CALL_TOKEN_DECODE = 7, MSA_CALL_INDEX_TOPK = 8 };
 
 /*
  * a1. Index branch scoring fused with the causal block max-pool
@@ -113,6 +113,22 @@ msa_status msa_index_scores(const msa_problem* prob, const void* q_idx, const vo
  */
 msa_status msa_block_topk(const msa_problem* prob, const float* scores, int32_t* sel,
                           void* stream);
+
+/*
+ * a1 + a2 fused: the selection of msa_block_topk computed straight from the index keys,
+ *     without the [S, Hkv, T, nb] block scores ([P1] 第一步：粗筛).  Each row's block
+ *     maxima are formed as in msa_index_scores and merged, 16 blocks at a time, into a
+ *     running list of the row's 15 best past blocks (per span of 1024 blocks); a second
+ *     kernel merges the spans' lists and appends the own block.  The result is bit-identical
+ *     to msa_index_scores followed by msa_block_topk.  dtype MSA_BF16 (index keys bf16 or
+ *     E4M3), topk <= 16; other problems return MSA_ERR_UNSUPPORTED.  With num_q < 256 the
+ *     call runs those two kernels itself into the workspace (scores of fewer than 256 rows).
+ *   workspace: msa_workspace_bytes(prob, MSA_CALL_INDEX_TOPK) bytes
+ *     (S * Hkv * T * ceil(nb / 1024) * 15 candidates of 8 bytes; S * Hkv * T * nb floats
+ *     when num_q < 256).
+ */
+msa_status msa_index_topk(const msa_problem* prob, const void* q_idx, const void* k_idx, int32_t* sel,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * a3. Selection inversion into per-(sequence, group, block) query lists: the index
