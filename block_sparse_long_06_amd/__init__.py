@@ -28,7 +28,8 @@ EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_invert_selection", "msa_s
             "msa_last_error_message", "msa_profiler_enable", "msa_profiler_read", "msa_index_scores_kv",
             "msa_block_topk_kv", "msa_sparse_attn_decode_kv", "msa_sparse_attn_prefill_train",
             "msa_sparse_attn_backward", "msa_index_kl", "msa_index_backward", "msa_token_scores",
-            "msa_token_topk", "msa_token_attn_decode", "msa_token_workspace_bytes", "msa_index_topk")
+            "msa_token_topk", "msa_token_attn_decode", "msa_token_workspace_bytes", "msa_index_topk",
+            "msa_sparse_attn_prefill_kv")
 
 
 class MSAError(RuntimeError):
@@ -107,6 +108,9 @@ def lib():
         L.msa_sparse_attn_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_index_kl.argtypes = [PP, P, P, P, ctypes.c_float, P, P, P]
         L.msa_index_backward.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_sparse_attn_prefill_kv.argtypes = [PP, ctypes.POINTER(KVLayout), P, P, P, P, P, P, P, P,
+                                                 ctypes.c_size_t, P]
+        L.msa_sparse_attn_prefill_kv.restype = st
         L.msa_index_topk.argtypes = [PP, P, P, P, P, ctypes.c_size_t, P]
         L.msa_index_topk.restype = st
         L.msa_token_scores.argtypes = [PP, P, P, P, P]
@@ -220,6 +224,13 @@ def index_scores_kv(prob: Problem, layout: KVLayout, q_idx, k_idx, scores, strea
 def block_topk_kv(prob: Problem, layout: KVLayout, scores, sel, stream=None) -> None:
     _check(lib().msa_block_topk_kv(ctypes.byref(prob), _lay(layout), _ptr(scores), _ptr(sel),
                                    _stream(stream, scores)))
+
+
+def sparse_attn_prefill_kv(prob: Problem, layout: KVLayout, q, k, v, csr_offsets, csr_entries, sel, out, workspace,
+                           workspace_bytes_: int, stream=None) -> None:
+    _check(lib().msa_sparse_attn_prefill_kv(ctypes.byref(prob), _lay(layout), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(csr_offsets), _ptr(csr_entries), _ptr(sel), _ptr(out),
+                                            _ptr(workspace), workspace_bytes_, _stream(stream, q)))
 
 
 def sparse_attn_decode_kv(prob: Problem, layout: KVLayout, q, k_cache, v_cache, sel, out, workspace,
@@ -444,3 +455,13 @@ def run_token_decode(prob: Problem, q, k_cache, v_cache, q_idx, k_idx, bufs: Tok
     token_scores(prob, q_idx, k_idx, bufs.scores, stream)
     token_topk(prob, budget, bufs.scores, bufs.sel_tok, stream)
     token_attn_decode(prob, budget, q, k_cache, v_cache, bufs.sel_tok, bufs.out, bufs.ws, bufs.ws.numel(), stream)
+
+
+def run_prefill_kv(prob: Problem, layout: KVLayout, q, k, v, q_idx, k_idx, bufs: PrefillBuffers, stream=None) -> None:
+    """Batched chunked prefill over ragged / paged caches (same stages as run_prefill)."""
+    index_scores_kv(prob, layout, q_idx, k_idx, bufs.scores, stream)
+    block_topk_kv(prob, layout, bufs.scores, bufs.sel, stream)
+    invert_selection(prob, bufs.sel, bufs.csr_offsets, bufs.csr_entries, bufs.ws_invert, bufs.ws_invert.numel(),
+                     stream)
+    sparse_attn_prefill_kv(prob, layout, q, k, v, bufs.csr_offsets, bufs.csr_entries, bufs.sel, bufs.out,
+                           bufs.ws_prefill, bufs.ws_prefill.numel(), stream)

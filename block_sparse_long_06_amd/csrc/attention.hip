@@ -571,7 +571,9 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
   const unsigned g256 = (unsigned)((nsgb + 255) / 256);
   hipError_t e;
   // the training outputs need one partial per (row, slot): no query-tile pass then
-  const bool hot = w.has_hot && hot_tiles_enabled() && lse_out == nullptr && mass_out == nullptr;
+  // (nor with per-sequence lengths: the tile pass maps tiles through one position offset)
+  const bool hot = w.has_hot && hot_tiles_enabled() && lse_out == nullptr && mass_out == nullptr &&
+                   D.kv_lens == nullptr;
   if (hot) {  // Outer-Gather-Q then takes only the cold part of the CSR
     e = launch_hot_split(D, sel, off, entries, w.hs, st);
     if (e != hipSuccess) return e;

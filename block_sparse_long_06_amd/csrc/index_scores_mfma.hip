@@ -75,9 +75,12 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
   const int h = lane >> 5;
   const int n = lane & 31;
   const int64_t sg = blockIdx.z;
+  const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
+  const int ns = seq_len(D, s);      // N, or this sequence's length (per-sequence calls)
+  const int pos0 = ns - D.T;
   const int t_first = blockIdx.x * kQB;
   const int t_last = min(t_first + kQB - 1, D.T - 1);
-  const int bmax = (D.pos0 + t_last) / kBlk;
+  const int bmax = (pos0 + t_last) / kBlk;
   const int b0 = blockIdx.y * kChunk;
   if (b0 > bmax) return;
   const int b1 = min(b0 + kChunk - 1, bmax);
@@ -88,25 +91,27 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
   for (int qt = 0; qt < kQT; ++qt) {
     const int t = t_first + wave * kQW + qt * 32 + n;
     const int tc = t < D.T ? t : D.T - 1;
-    pq[qt] = t < D.T ? D.pos0 + t : 0x7FFFFFFF;
+    pq[qt] = t < D.T ? pos0 + t : 0x7FFFFFFF;
     const uint16_t* qp = q_idx + (sg * D.T + tc) * DI + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[qt][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
   const int t_w0 = min(t_first + wave * kQW, D.T - 1);
-  const int bmask = (D.pos0 + t_w0) / kBlk;
+  const int bmask = (pos0 + t_w0) / kBlk;
 
-  const TK* kbase = k_idx + sg * (int64_t)D.N * DI;
   // one piece = 8 key dims: 16 bytes of bf16 or 8 bytes of E4M3
   typedef typename std::conditional<sizeof(TK) == 2, uint4, uint2>::type Piece;
   Piece stage[PER_T];
   auto gload = [&](int b) {
+    // a block's keys are contiguous (dense cache or one page); an invalid page reads as 0
+    const int64_t kb0 = kv_row(D, s, g, b * kBlk, DI);
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int c = threadIdx.x + 256 * u;
       const int row = c / CPR, col = c % CPR;
       const int j = b * kBlk + row;
-      stage[u] = j < D.N ? *reinterpret_cast<const Piece*>(kbase + (int64_t)j * DI + col * 8) : Piece{};
+      stage[u] = kb0 >= 0 && j < ns ? *reinterpret_cast<const Piece*>(k_idx + kb0 + (int64_t)row * DI + col * 8)
+                                    : Piece{};
     }
   };
   auto lstore = [&](int buf) {
@@ -192,7 +197,7 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_scores_mfma(Dims D
     const int rl = lane + 64 * rr;
     const int t_out = t_first + wave * kQW + rl;
     if (t_out < D.T) {
-      const int bt = (D.pos0 + t_out) / kBlk;
+      const int bt = (pos0 + t_out) / kBlk;
       const int len = min(b1, bt) - b0 + 1;
       float* out_row = scores + (sg * D.T + t_out) * (int64_t)D.nb + b0;
       const float* src = outb[wave][rl];

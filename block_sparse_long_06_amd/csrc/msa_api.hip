@@ -112,7 +112,6 @@ msa_status check_problem(const msa_problem* p, msa::Dims* D, bool need_index, bo
 msa_status apply_layout(const msa_kv_layout* L, msa::Dims* D) {
   if (L == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "layout is NULL");
   if (L->kv_lens == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "layout->kv_lens is NULL");
-  if (D->T > 8) return fail(MSA_ERR_UNSUPPORTED, "the per-sequence calls take num_q <= 8 (got %d)", D->T);
   if (L->block_table != nullptr) {
     if (L->table_stride < D->nb)
       return fail(MSA_ERR_INVALID_ARGUMENT, "layout->table_stride %d < ceil(kv_len / block_size) = %d",
@@ -548,6 +547,32 @@ msa_status msa_token_attn_decode(const msa_problem* prob, int32_t budget, const 
   return device_status(msa::launch_token_attn(D, budget, q, k_cache, v_cache, sel_tok, out, workspace,
                                               (hipStream_t)stream),
                        "msa_token_attn_decode launch");
+}
+
+msa_status msa_sparse_attn_prefill_kv(const msa_problem* prob, const msa_kv_layout* layout, const void* q,
+                                      const void* k, const void* v, const int32_t* csr_offsets,
+                                      const int32_t* csr_entries, const int32_t* sel, void* out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, true);
+  if (st != MSA_OK) return st;
+  st = apply_layout(layout, &D);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(csr_offsets);
+  REQUIRE_PTR(csr_entries);
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(out);
+  const size_t need = msa::prefill_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "msa_sparse_attn_prefill_kv needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(msa::launch_prefill(D, q, k, v, csr_offsets, csr_entries, sel, out, workspace,
+                                           (hipStream_t)stream),
+                       "msa_sparse_attn_prefill_kv launch");
 }
 
 msa_status msa_profiler_enable(int on) {

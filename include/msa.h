@@ -203,8 +203,9 @@ msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, const 
  *   table_stride >= ceil(kv_len / block_size) when block_table != NULL.
  *   num_pages    >= 1 when block_table != NULL.
  * The problem's kv_len is the capacity (the largest allowed length); nb = ceil(kv_len / B)
- * sizes the scores rows.  These calls take num_q <= 8 (decode and few-token speculative
- * decode); other sizes return MSA_ERR_UNSUPPORTED.
+ * sizes the scores rows.  Any num_q: decode, speculative decode and batched chunked prefill
+ * (every sequence appends num_q queries at its end).  The prefill call runs every pair in
+ * the Outer-Gather-Q order (no query-tile pass); msa_invert_selection needs no layout.
  */
 typedef struct {
   const int32_t* kv_lens;
@@ -222,6 +223,13 @@ msa_status msa_index_scores_kv(const msa_problem* prob, const msa_kv_layout* lay
  * layout->kv_lens is read). */
 msa_status msa_block_topk_kv(const msa_problem* prob, const msa_kv_layout* layout, const float* scores,
                              int32_t* sel, void* stream);
+
+/* a4 + a5 of msa_sparse_attn_prefill for the layout (workspace: msa_workspace_bytes(prob,
+ * MSA_CALL_PREFILL) bytes). */
+msa_status msa_sparse_attn_prefill_kv(const msa_problem* prob, const msa_kv_layout* layout, const void* q,
+                                      const void* k, const void* v, const int32_t* csr_offsets,
+                                      const int32_t* csr_entries, const int32_t* sel, void* out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* a6 of msa_sparse_attn_decode for the layout (workspace: msa_workspace_bytes(prob,
  * MSA_CALL_DECODE) bytes). */

@@ -136,19 +136,20 @@ def _layout(kv_lens=1, block_table=None, stride=0, pages=0):
 @pytest.mark.parametrize("lay,kw,status", [
     (None, {}, msa.MSA_ERR_INVALID_ARGUMENT),                                    # no layout
     ("nolens", {}, msa.MSA_ERR_INVALID_ARGUMENT),                                # kv_lens NULL
-    ("dense", dict(num_q=9), msa.MSA_ERR_UNSUPPORTED),                           # more than 8 queries
+    ("hugepool", {}, msa.MSA_ERR_UNSUPPORTED),                                    # pool beyond 2^40 elements
     ("shortstride", {}, msa.MSA_ERR_INVALID_ARGUMENT),                           # table_stride < nb
     ("nopages", {}, msa.MSA_ERR_INVALID_ARGUMENT),                               # num_pages < 1
 ])
 def test_kv_layout_is_validated_on_the_host(lay, kw, status):
     p = _good(**dict(dict(num_q=1, kv_len=1000), **kw))
-    layouts = {None: None, "nolens": _layout(kv_lens=None), "dense": _layout(),
+    layouts = {None: None, "nolens": _layout(kv_lens=None), "hugepool": _layout(block_table=1, stride=8, pages=1 << 30),
                "shortstride": _layout(block_table=1, stride=7, pages=10),   # nb = 8
                "nopages": _layout(block_table=1, stride=8, pages=0)}
     L = layouts[lay]
     for call in (lambda: msa.index_scores_kv(p, L, 1, 1, 1, stream=0),
                  lambda: msa.block_topk_kv(p, L, 1, 1, stream=0),
-                 lambda: msa.sparse_attn_decode_kv(p, L, 1, 1, 1, 1, 1, 1, 1 << 40, stream=0)):
+                 lambda: msa.sparse_attn_decode_kv(p, L, 1, 1, 1, 1, 1, 1, 1 << 40, stream=0),
+                 lambda: msa.sparse_attn_prefill_kv(p, L, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 40, stream=0)):
         with pytest.raises(msa.MSAError) as ei:
             call()
         assert ei.value.status == status

@@ -154,3 +154,36 @@ def test_out_of_contract_device_values_stay_in_bounds():
     db = _run(prob, lay, inputs, pools)
     ref_inputs = dict(inputs, **zeroed)
     _verify(wl, ref_inputs, lens, db, "clamped / zero pages")
+
+
+PREFILL_CASES = [
+    (W.small("kvp_bf16", S=3, T=300, N=4000, H=16, Hkv=2, d=128, dI=64, k=16, structure="band_sink_needles"),
+     [4000, 300, 2345]),
+    (W.small("kvp_fp32", S=2, T=260, N=1500, H=8, Hkv=2, d=64, dI=32, k=4, dtype=synth.F32), [1500, 777]),
+    (W.small("kvp_e4m3_g1", S=2, T=512, N=3000, H=2, Hkv=2, d=128, dI=64, k=8, kidx_dtype=synth.FP8), [3000, 1029]),
+]
+
+
+def _run_prefill(prob, lay, inputs, caches):
+    pb = msa.alloc_prefill(prob)
+    msa.run_prefill_kv(prob, lay, inputs["q"], caches["k"], caches["v"], inputs["q_idx"], caches["k_idx"], pb)
+    torch.cuda.synchronize()
+    return pb
+
+
+@pytest.mark.parametrize("wl,lens", PREFILL_CASES, ids=[c[0].name for c in PREFILL_CASES])
+def test_ragged_and_paged_prefill_match_the_oracle(wl, lens):
+    require_gpu()
+    say("case", wl.name, "lens", lens)
+    inputs = gen(wl)
+    prob = wl.problem()
+    kv_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    dense = {n: _ragged_dense(inputs[n], lens) for n in ("k", "v", "k_idx")}
+    pb_dense = _run_prefill(prob, msa.kv_layout(kv_lens), inputs, dense)
+    _verify(wl, inputs, lens, pb_dense, "ragged dense prefill")
+    table, num_pages = _page_table(lens, wl.nb, seed=wl.seed + 1)
+    pools = {n: _to_pool(inputs[n], lens, table, num_pages) for n in ("k", "v", "k_idx")}
+    pb_paged = _run_prefill(prob, msa.kv_layout(kv_lens, torch.from_numpy(table).cuda(), num_pages), inputs, pools)
+    _verify(wl, inputs, lens, pb_paged, "paged prefill")
+    np.testing.assert_array_equal(pb_paged.sel.cpu().numpy(), pb_dense.sel.cpu().numpy())
+    assert torch.equal(pb_paged.out.view(torch.uint8), pb_dense.out.view(torch.uint8))
