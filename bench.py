@@ -456,7 +456,7 @@ def train_step(args, msa, wl):
     ms = e0.elapsed_time(e1) / args.steps
     st = {}
     for kn in ("idx_scores_mfma", "block_topk", "ogq_mfma", "lse_merge", "bwd_zero", "bwd_drow", "attn_bwd", "dq_merge",
-               "index_kl", "index_bwd_zero", "index_bwd"):
+               "index_kl", "index_bwd_zero", "index_bwd", "index_dq_gather"):
         tms, nl = msa.profiler_read(kn, reset=False)
         if nl:
             st[kn] = dict(ms=tms / nl)

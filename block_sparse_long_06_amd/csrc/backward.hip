@@ -24,9 +24,10 @@
 //    list can span several items).
 //  * index_kl: per row, KL(teacher || student) over the selected blocks and its gradient
 //    with respect to the block scores (teacher = the forward's block masses).
-//  * index_bwd: the gradient of the block scores through the causal max-pool: per (row,
-//    selected block) the arg-max key (lowest position among equal maxima, scores in fp32
-//    summed in index order) takes dscore * q_I, and the row takes dscore * k_I[j*].
+//  * index_bwd + index_dq_gather: the gradient of the block scores through the causal
+//    max-pool: per (row, selected block) the arg-max key (lowest position among equal
+//    maxima; scores as the matrix cores sum them in float32) takes dscore * q_I, and the
+//    row takes dscore * k_I[j*] summed over its slots.
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -204,7 +205,31 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
       }
     }
   };
+  // per-M-row values of the next sub-chunk (threads 0..31), fetched with its Q and dO
+  float n_lse2 = INFINITY, n_drow = 0.0f;
+  int n_pos = -1;
+  int64_t n_dqoff = -1;
+  auto fetch_meta = [&](int m0n) {
+    if (threadIdx.x < 32) {
+      const int mr = m0n + (int)threadIdx.x;
+      n_lse2 = INFINITY;  // P = 0 for an M-row past the list
+      n_drow = 0.0f;
+      n_pos = -1;
+      n_dqoff = -1;
+      if (mr < mrows) {
+        const int e = entries[w.y + mr / G];
+        const int t = e / D.k;
+        const int64_t hr = ((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mr % G;
+        const int64_t pidx = (((int64_t)s * D.T + t) * D.Hkv + g) * D.k + (e - t * D.k);
+        n_lse2 = lse[hr] * kLog2e;
+        n_drow = drow[hr];
+        n_pos = D.pos0 + t;
+        n_dqoff = (pidx * G + mr % G) * DH;
+      }
+    }
+  };
   fetch(0);
+  fetch_meta(0);
 
   for (int m0 = 0; m0 < mrows; m0 += 32) {
     __syncthreads();  // previous sub-chunk's buffers are free (and the staging is complete)
@@ -225,24 +250,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
       }
     }
     if (threadIdx.x < 32) {
-      const int m = threadIdx.x, mr = m0 + m;
-      if (mr < mrows) {
-        const int e = entries[w.y + mr / G];
-        const int t = e / D.k;
-        const int64_t hr = ((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mr % G;
-        const int64_t pidx = (((int64_t)s * D.T + t) * D.Hkv + g) * D.k + (e - t * D.k);
-        L.lse2[m] = lse[hr] * kLog2e;
-        L.drow[m] = drow[hr];
-        L.pos[m] = D.pos0 + t;
-        L.dqoff[m] = (pidx * G + mr % G) * DH;
-      } else {
-        L.lse2[m] = INFINITY;  // P = 0 for an M-row past the list
-        L.drow[m] = 0.0f;
-        L.pos[m] = -1;
-        L.dqoff[m] = -1;
-      }
+      const int m = threadIdx.x;
+      L.lse2[m] = n_lse2;
+      L.drow[m] = n_drow;
+      L.pos[m] = n_pos;
+      L.dqoff[m] = n_dqoff;
     }
-    if (m0 + 32 < mrows) fetch(m0 + 32);
+    if (m0 + 32 < mrows) {
+      fetch(m0 + 32);
+      fetch_meta(m0 + 32);
+    }
     __syncthreads();
 
     // ---- S = Q K^T and dP = dO V^T for this wave's 32 keys
@@ -411,23 +428,39 @@ __global__ void __launch_bounds__(256) index_kl_kernel(Dims D, const float* __re
   loss[row] = L;
 }
 
-// Index keys of one block in LDS as fp32 (row pad of one float: conflict-free lane-per-key
-// reads), plus the block's key-gradient accumulator.
+// One KV block's index keys in LDS (bf16 row-major, 16-byte row pad: the per-lane 16-byte
+// operand reads of a wave are bank-conflict free), plus the block's key-gradient
+// accumulator (fp32, one float of row pad).
 template <int DI>
 struct IdxBwdLds {
-  float kf[kBlk][DI + 1];
+  static constexpr int ROW = DI * 2 + 16;
+  __attribute__((aligned(16))) unsigned char k[kBlk * ROW];
   float dk[kBlk][DI + 1];
-  float qrow[kWaves][DI];
 };
 
+// Arg-max of the causal block max-pool per (row, selected block) on the matrix cores, and
+// the key side of its gradient.  Work item = (sequence, group, KV block) and up to kRows
+// rows of its inverted list; each wave takes 32 rows at a time:
+//   S^T = K_I q_I^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys from LDS, B = the 32 rows'
+//   index queries straight from memory, k-step ks / lane half h = index dims
+//   [16 ks + 8 h, +8)), so a lane's accumulators are 64 keys of ONE row; the row's
+//   maximum over its causal keys and the lowest key holding it are in-register scans plus
+//   one exchange with lane ^ 32.  Scores are the matrix cores' float32 sums of the exact
+//   bf16 products.
+// The arg-max goes to am (and to argmax when given); dk_idx[j*] += dscore * q_I[row] is
+// accumulated in LDS per item and added to memory once per item with float atomics.  The
+// query side dq_idx is gathered per row afterwards (index_dq_gather).
 template <int DI>
 __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __restrict__ q_idx,
                                                       const uint16_t* __restrict__ k_idx,
                                                       const int4* __restrict__ wl, const int* __restrict__ n_items,
                                                       const int32_t* __restrict__ entries,
-                                                      const float* __restrict__ dscore, float* __restrict__ dq_idx,
-                                                      float* __restrict__ dk_idx, int32_t* __restrict__ argmax) {
-  __shared__ IdxBwdLds<DI> L;
+                                                      const float* __restrict__ dscore, float* __restrict__ dk_idx,
+                                                      int32_t* __restrict__ am, int32_t* __restrict__ argmax) {
+  using L_ = IdxBwdLds<DI>;
+  constexpr int KS = DI / 16;
+  constexpr int CPR = DI / 8;
+  __shared__ L_ L;
   const int n = *n_items;
   const int per_xcd = (n + 7) / 8;
   const int slot_in_xcd = blockIdx.x >> 3;
@@ -439,48 +472,71 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
   const int b = w.x % D.nb;
   const int j0 = b * kBlk;
   const int nvalid = min(kBlk, D.N - j0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, nl = lane & 31;
   const uint16_t* kb = k_idx + (sg * D.N + j0) * DI;
-  for (int i = threadIdx.x; i < kBlk * DI; i += kThreads) {
-    const int key = i / DI, c = i % DI;
-    L.kf[key][c] = key < nvalid ? bf16_to_f32(kb[i]) : 0.0f;
-    L.dk[key][c] = 0.0f;
+  for (int c = threadIdx.x; c < kBlk * CPR; c += kThreads) {
+    const int key = c / CPR, col = c % CPR;
+    *reinterpret_cast<uint4*>(&L.k[key * L_::ROW + col * 16]) =
+        key < nvalid ? *reinterpret_cast<const uint4*>(kb + key * DI + col * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
+  for (int i = threadIdx.x; i < kBlk * (DI + 1); i += kThreads) (&L.dk[0][0])[i] = 0.0f;
   __syncthreads();
-  for (int r = wave; r < w.z; r += kWaves) {
-    const int e = entries[w.y + r];
-    const int t = e / D.k, slot = e - t * D.k;
-    const int p = D.pos0 + t;
+  for (int r0 = wave * 32; r0 < w.z; r0 += kWaves * 32) {
+    const int r = r0 + nl;  // this lane's row of the item (both lane halves)
+    const bool ok = r < w.z;
+    int t = 0, slot = 0;
+    if (ok) {
+      const int e = entries[w.y + r];
+      t = e / D.k;
+      slot = e - t * D.k;
+    }
     const int64_t qr = sg * D.T + t;  // (s, g, t)
-    for (int c = lane; c < DI; c += 64) L.qrow[wave][c] = bf16_to_f32(q_idx[qr * DI + c]);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // scores of keys lane and lane + 64, summed in index order
-    float s0 = 0.0f, s1 = 0.0f;
-    for (int c = 0; c < DI; ++c) {
-      const float qc = L.qrow[wave][c];
-      s0 = fmaf(qc, L.kf[lane][c], s0);
-      s1 = fmaf(qc, L.kf[lane + 64][c], s1);
+    bf16x8 bq[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bq[ks] = ok ? *reinterpret_cast<const bf16x8*>(q_idx + qr * DI + 16 * ks + 8 * h) : bf16x8{};
+    f32x16 acc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      acc[kt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&L.k[(kt * 32 + nl) * L_::ROW + (16 * ks + 8 * h) * 2]);
+        acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[ks], acc[kt], 0, 0, 0);
+      }
     }
-    const bool v0 = lane < nvalid && j0 + lane <= p;
-    const bool v1 = lane + 64 < nvalid && j0 + lane + 64 <= p;
-    if (!v0) s0 = -INFINITY;
-    if (!v1) s1 = -INFINITY;
-    const float best = wave_max(fmaxf(s0, s1));
-    // lowest position holding the maximum
-    const uint64_t m0 = __ballot(v0 && s0 == best), m1 = __ballot(v1 && s1 == best);
-    // (no key holds the maximum only for NaN scores: then the row takes no update)
-    const int js = m0 != 0ull ? __builtin_ctzll(m0) : (m1 != 0ull ? 64 + __builtin_ctzll(m1) : -1);
-    const float gsc = dscore[qr * D.k + slot];
-    if (lane == 0 && argmax != nullptr) argmax[qr * D.k + slot] = js >= 0 ? j0 + js : -1;
-    for (int c = lane; js >= 0 && c < DI; c += 64) {
-      unsafeAtomicAdd(dq_idx + qr * DI + c, gsc * L.kf[js][c]);
-      atomicAdd(&L.dk[js][c], gsc * L.qrow[wave][c]);
+    // keys kk <= lim are inside the block and causal for the row (kk = 0 always is: the
+    // block is one the row selected)
+    const int lim = min(nvalid - 1, D.pos0 + t - j0);
+    float best = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (kt * 32 + acc_row(q, h) <= lim) best = fmaxf(best, acc[kt][q]);
+    best = fmaxf(best, __shfl_xor(best, 32, 64));
+    // lowest key holding the maximum (none when every causal score is NaN: no update)
+    int idx = 0x7FFFFFFF;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int kk = kt * 32 + acc_row(q, h);
+        if (kk <= lim && acc[kt][q] == best) idx = min(idx, kk);
+      }
+    idx = min(idx, __shfl_xor(idx, 32, 64));
+    const int js = idx == 0x7FFFFFFF ? -1 : idx;
+    if (ok && h == 0) {
+      am[qr * D.k + slot] = js >= 0 ? j0 + js : -1;
+      if (argmax != nullptr) argmax[qr * D.k + slot] = js >= 0 ? j0 + js : -1;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (ok && js >= 0) {
+      const float gsc = dscore[qr * D.k + slot];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) atomicAdd(&L.dk[js][16 * ks + 8 * h + i], gsc * (float)bq[ks][i]);
+    }
   }
   __syncthreads();
   float* dst = dk_idx + (sg * D.N + j0) * DI;
@@ -488,6 +544,38 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
     const float x = L.dk[i / DI][i % DI];
     if (x != 0.0f) unsafeAtomicAdd(dst + i, x);
   }
+}
+
+// dq_idx[s, g, t] = sum over the row's slots with an arg-max j of dscore * k_I[s, g, j], in
+// slot order; 16 threads per row, DI / 16 index dims each.
+template <int DI>
+__global__ void __launch_bounds__(256) index_dq_gather(Dims D, const uint16_t* __restrict__ k_idx,
+                                                       const int32_t* __restrict__ am,
+                                                       const float* __restrict__ dscore,
+                                                       float* __restrict__ dq_idx) {
+  constexpr int PER = DI / 16;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid >> 4;  // (s, g, t)
+  if (row >= (int64_t)D.S * D.Hkv * D.T) return;
+  const int c0 = (int)(gid & 15) * PER;
+  const int64_t sg = row / D.T;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
+  for (int slot = 0; slot < D.k; ++slot) {
+    const int j = am[row * D.k + slot];
+    if (j < 0) continue;
+    const float gsc = dscore[row * D.k + slot];
+    const uint16_t* kp = k_idx + (sg * D.N + j) * DI + c0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = fmaf(gsc, bf16_to_f32(kp[i]), acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) dq_idx[row * DI + c0 + i] = acc[i];
+}
+
+__global__ void __launch_bounds__(256) fill_neg1(int32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = -1;
 }
 
 struct BwdWs {
@@ -594,9 +682,24 @@ hipError_t launch_index_kl(const Dims& D, const float* scores, const int32_t* se
   return hipGetLastError();
 }
 
+namespace {
+// index-backward workspace: the work list, then the arg-max of every (row, slot)
+WorkList index_bwd_layout(const Dims& D, void* base, int32_t** am, size_t* total) {
+  size_t wlb = 0;
+  (void)work_list_layout(D, kRows, nullptr, &wlb);
+  unsigned char* p = static_cast<unsigned char*>(base);
+  const WorkList wl = work_list_layout(D, kRows, p, &wlb);
+  const size_t off = align_up(wlb, 256);
+  *am = p ? reinterpret_cast<int32_t*>(p + off) : nullptr;
+  *total = off + align_up((size_t)D.S * D.Hkv * D.T * D.k * sizeof(int32_t), 256);
+  return wl;
+}
+}  // namespace
+
 size_t index_backward_workspace_bytes(const Dims& D) {
   size_t total = 0;
-  (void)work_list_layout(D, kRows, nullptr, &total);
+  int32_t* am = nullptr;
+  (void)index_bwd_layout(D, nullptr, &am, &total);
   return total;
 }
 
@@ -604,28 +707,47 @@ hipError_t launch_index_backward(const Dims& D, const void* q_idx, const void* k
                                  const int32_t* entries, const float* dscore, float* dq_idx, float* dk_idx,
                                  int32_t* argmax, void* ws, hipStream_t st) {
   size_t total = 0;
-  const WorkList wl = work_list_layout(D, kRows, ws, &total);
+  int32_t* am = nullptr;
+  const WorkList wl = index_bwd_layout(D, ws, &am, &total);
+  const int64_t nam = (int64_t)D.S * D.Hkv * D.T * D.k;
   hipError_t e;
   {
     LaunchScope scope("index_bwd_zero", st);
-    e = zero(dq_idx, (int64_t)D.S * D.Hkv * D.T * D.dI, st);
-    if (e == hipSuccess) e = zero(dk_idx, (int64_t)D.S * D.Hkv * D.N * D.dI, st);
+    e = zero(dk_idx, (int64_t)D.S * D.Hkv * D.N * D.dI, st);
+    if (e == hipSuccess && nam > 0) {
+      const int64_t blocks = (nam + 255) / 256 < 65536 ? (nam + 255) / 256 : 65536;
+      hipLaunchKernelGGL(fill_neg1, dim3((unsigned)blocks), dim3(256), 0, st, am, nam);
+      e = hipGetLastError();
+    }
   }
   if (e != hipSuccess) return e;
   e = launch_work_list(D, off, kRows, wl, st);
   if (e != hipSuccess) return e;
   const int64_t grid = (wl.ub + 7) / 8 * 8 + 8;
-  LaunchScope scope("index_bwd", st);
   const uint16_t *qb = static_cast<const uint16_t*>(q_idx), *kb = static_cast<const uint16_t*>(k_idx);
+  {
+    LaunchScope scope("index_bwd", st);
+    if (D.dI == 32)
+      hipLaunchKernelGGL(index_bwd<32>, dim3((unsigned)grid), dim3(kThreads), 0, st, D, qb, kb, wl.wl, wl.n_items,
+                         entries, dscore, dk_idx, am, argmax);
+    else if (D.dI == 64)
+      hipLaunchKernelGGL(index_bwd<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, D, qb, kb, wl.wl, wl.n_items,
+                         entries, dscore, dk_idx, am, argmax);
+    else
+      hipLaunchKernelGGL(index_bwd<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, D, qb, kb, wl.wl, wl.n_items,
+                         entries, dscore, dk_idx, am, argmax);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
+  LaunchScope scope("index_dq_gather", st);
+  const dim3 g2((unsigned)((rows * 16 + 255) / 256));
   if (D.dI == 32)
-    hipLaunchKernelGGL(index_bwd<32>, dim3((unsigned)grid), dim3(kThreads), 0, st, D, qb, kb, wl.wl, wl.n_items,
-                       entries, dscore, dq_idx, dk_idx, argmax);
+    hipLaunchKernelGGL(index_dq_gather<32>, g2, dim3(256), 0, st, D, kb, am, dscore, dq_idx);
   else if (D.dI == 64)
-    hipLaunchKernelGGL(index_bwd<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, D, qb, kb, wl.wl, wl.n_items,
-                       entries, dscore, dq_idx, dk_idx, argmax);
+    hipLaunchKernelGGL(index_dq_gather<64>, g2, dim3(256), 0, st, D, kb, am, dscore, dq_idx);
   else
-    hipLaunchKernelGGL(index_bwd<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, D, qb, kb, wl.wl, wl.n_items,
-                       entries, dscore, dq_idx, dk_idx, argmax);
+    hipLaunchKernelGGL(index_dq_gather<128>, g2, dim3(256), 0, st, D, kb, am, dscore, dq_idx);
   return hipGetLastError();
 }
 
