@@ -48,9 +48,27 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
-// Column of M-row m in the transposed Q / dO buffers: the 8 M-rows one lane half feeds
-// to a k-step (16p + 4h + {0..3}, 16p + 8 + 4h + {0..3}) are stored contiguously.
-__device__ __forceinline__ int mrow_col(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// An MFMA operand read TRANSPOSED out of a row-major bf16 tile in LDS: lane (n = lane % 32,
+// half h = lane / 32) gets column col0 + n of rows r0 + {0..3} (elements 0..3) and
+// r1 + {0..3} (elements 4..7); r0 and r1 may depend on h.  ds_read_b64_tr_b16 works in
+// groups of 16 lanes: destination lane i receives, as element j, the (i % 4)-th 16-bit
+// value of the 8 bytes addressed by source lane 4 j + i / 4, so source lane s = 4 j + q
+// addresses row r + j at columns col0 + 16 * (lane / 16 % 2) + 4 q .. + 3.
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int row_bytes, int r0, int r1, int col0,
+                                             int lane) {
+  const int sl = lane & 15, j = sl >> 2, q = sl & 3;
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * q;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const lds_u8* t = (const lds_u8*)tile;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r0 + j) * row_bytes + col * 2));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r1 + j) * row_bytes + col * 2));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
+}
 
 // M-row held by accumulator register r of lane half h (32x32 output layout).
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -58,22 +76,20 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 template <int DH>
 struct __attribute__((aligned(16))) BwdLds {
   static constexpr int KROW = DH * 2 + 16;    // K / V row-major, bytes
-  static constexpr int KTROW = kBlk * 2 + 16; // K^T row (one head dim over the block's keys)
   static constexpr int QROW = DH * 2 + 16;    // Q / dO row-major (32 M-rows)
-  static constexpr int TROW = 32 * 2 + 16;    // Q^T / dO^T row (one head dim over 32 M-rows)
   static constexpr int SROW = kBlk * 2 + 16;  // dS row (one M-row over the block's keys)
   __attribute__((aligned(16))) unsigned char kr[kBlk * KROW];
   __attribute__((aligned(16))) unsigned char vr[kBlk * KROW];
-  __attribute__((aligned(16))) unsigned char kt[DH * KTROW];
   __attribute__((aligned(16))) unsigned char qs[32 * QROW];
   __attribute__((aligned(16))) unsigned char dos[32 * QROW];
-  __attribute__((aligned(16))) unsigned char qt[DH * TROW];
-  __attribute__((aligned(16))) unsigned char dot[DH * TROW];
   __attribute__((aligned(16))) unsigned char ds[32 * SROW];
   __attribute__((aligned(16))) float lse2[32];  // lse * log2(e); +inf for an M-row past the item's rows
   __attribute__((aligned(16))) float drow[32];
   __attribute__((aligned(16))) int pos[32];
-  int64_t dqoff[32];   // element offset of the M-row's dQ partial; -1 if none
+  __attribute__((aligned(16))) unsigned char dqt[32 * QROW];  // a sub-chunk's dQ (bf16), stored next iteration
+  int64_t dqoff[2][32];  // by sub-chunk parity: element offset of the M-row's dQ partial (scratch row if none)
+  int rowt[kRows];     // the item's rows: query row t and slot, decoded once per item, so
+  int rslot[kRows];    // that no per-sub-chunk load waits on another global load
 };
 
 // D[s, t, h] = sum_c dO[s, t, h, c] O[s, t, h, c] (fp32), 16 lanes per row.
@@ -138,7 +154,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, nl = lane & 31;
   const float sc = D.scale * kLog2e;
 
-  // ---- stage K, V (row-major) and K^T (head dim major, keys in order)
+  // ---- stage K, V (row-major)
   {
     const uint16_t* kb = k + (sg * D.N + j0) * DH;
     const uint16_t* vb = v + (sg * D.N + j0) * DH;
@@ -150,26 +166,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
       *reinterpret_cast<uint4*>(&L.kr[row * L_::KROW + col * 16]) = kk;
       *reinterpret_cast<uint4*>(&L.vr[row * L_::KROW + col * 16]) = vv;
     }
-    // K^T: thread = (4 consecutive keys, 8 consecutive head dims), a 4 x 8 transpose
-    for (int c = threadIdx.x; c < (kBlk / 4) * CPR; c += kThreads) {
-      const int kg = c % (kBlk / 4), dc = c / (kBlk / 4);
-      uint32_t wv[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 4 * kg + i;
-        const uint4 x = key < nvalid ? *reinterpret_cast<const uint4*>(kb + key * DH + dc * 8)
-                                     : make_uint4(0u, 0u, 0u, 0u);
-        wv[i][0] = x.x; wv[i][1] = x.y; wv[i][2] = x.z; wv[i][3] = x.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        uint2 o;
-        o.x = ((wv[0][e >> 1] >> sh) & 0xFFFFu) | (((wv[1][e >> 1] >> sh) & 0xFFFFu) << 16);
-        o.y = ((wv[2][e >> 1] >> sh) & 0xFFFFu) | (((wv[3][e >> 1] >> sh) & 0xFFFFu) << 16);
-        *reinterpret_cast<uint2*>(&L.kt[(dc * 8 + e) * L_::KTROW + kg * 8]) = o;
-      }
-    }
   }
 
   f32x16 dkt[DT], dvt[DT];
@@ -178,8 +174,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
     dkt[dt] = f32x16{};
     dvt[dt] = f32x16{};
   }
+  for (int r = threadIdx.x; r < rows; r += kThreads) {
+    const int e = entries[w.y + r];
+    const int t = e / D.k;
+    L.rowt[r] = t;
+    L.rslot[r] = e - t * D.k;
+  }
+  __syncthreads();
   const int mrows = rows * G;
-  const int first_pos = D.pos0 + entries[w.y] / D.k;  // rows ascend: the smallest position
+  const int first_pos = D.pos0 + L.rowt[0];  // rows ascend: the smallest position
+  // M-rows past the list store their dQ here: one scratch row after the partials
+  const int64_t dq_trash = (int64_t)D.S * D.T * D.Hkv * D.k * G * DH;
   const bool need_mask = first_pos < j0 + kBlk - 1;
   const int key = j0 + 32 * wave + nl;                // this lane's key
 
@@ -190,76 +195,80 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
   constexpr int NP = 32 * CPR / kThreads;
   static_assert(NP >= 1 && 32 * CPR == NP * kThreads, "whole pieces per thread");
   uint4 nq[NP], ng[NP];
+  // Every load is unconditional (a row past the list reads row 0 and is zeroed after the
+  // load), and so are the dQ stores below: with no memory operation under a branch the
+  // compiler counts them exactly, and the loop head waits only for the previous
+  // iteration's loads, not for its dQ stores.
+  // (the zeroing of rows past the list happens where the data is stored to LDS, so that
+  // no instruction right after the loads waits for them)
   auto fetch = [&](int m0n) {
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int c = threadIdx.x + kThreads * u;
       const int mr = m0n + c % 32, col = c / 32;
-      nq[u] = make_uint4(0u, 0u, 0u, 0u);
-      ng[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (mr < mrows) {
-        const int t = entries[w.y + mr / G] / D.k;
-        const int64_t off = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mr % G) * DH + col * 8;
-        nq[u] = *reinterpret_cast<const uint4*>(q + off);
-        ng[u] = *reinterpret_cast<const uint4*>(dout + off);
-      }
+      const int mc = mr < mrows ? mr : 0;
+      const int t = L.rowt[mc / G];
+      const int64_t off = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mc % G) * DH + col * 8;
+      nq[u] = *reinterpret_cast<const uint4*>(q + off);
+      ng[u] = *reinterpret_cast<const uint4*>(dout + off);
     }
   };
-  // per-M-row values of the next sub-chunk (threads 0..31), fetched with its Q and dO
-  float n_lse2 = INFINITY, n_drow = 0.0f;
-  int n_pos = -1;
-  int64_t n_dqoff = -1;
-  auto fetch_meta = [&](int m0n) {
-    if (threadIdx.x < 32) {
-      const int mr = m0n + (int)threadIdx.x;
-      n_lse2 = INFINITY;  // P = 0 for an M-row past the list
-      n_drow = 0.0f;
-      n_pos = -1;
-      n_dqoff = -1;
-      if (mr < mrows) {
-        const int e = entries[w.y + mr / G];
-        const int t = e / D.k;
-        const int64_t hr = ((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mr % G;
-        const int64_t pidx = (((int64_t)s * D.T + t) * D.Hkv + g) * D.k + (e - t * D.k);
-        n_lse2 = lse[hr] * kLog2e;
-        n_drow = drow[hr];
-        n_pos = D.pos0 + t;
-        n_dqoff = (pidx * G + mr % G) * DH;
-      }
-    }
+  // per-M-row values of the next sub-chunk (threads 0..31), fetched with its Q and dO;
+  // lse is scaled only when it is stored (the load's result is not needed before)
+  float n_lse = 0.0f, n_drow = 0.0f;
+  int n_t = 0, n_slot = 0;
+  auto fetch_meta = [&](int m0n) {  // every thread (no branch); threads 0..31 store them
+    const int mr = m0n + (int)(threadIdx.x & 31);
+    const int mc = mr < mrows ? mr : 0;
+    n_t = L.rowt[mc / G];
+    n_slot = L.rslot[mc / G];
+    const int64_t hr = ((int64_t)s * D.T + n_t) * D.H + (int64_t)g * G + mc % G;
+    n_lse = lse[hr];
+    n_drow = drow[hr];
   };
   fetch(0);
   fetch_meta(0);
 
+  // dQ of a sub-chunk goes to an LDS tile and is stored at the start of the next
+  // iteration, before that iteration's prefetch: the loads waited for at a loop head are
+  // then never queued behind stores issued just before (this chip's counter does not
+  // order a store ahead of a later load); the first iteration stores to the scratch row
+  if (threadIdx.x < 32) L.dqoff[1][threadIdx.x] = dq_trash;
+  constexpr int OP = 32 * CPR / kThreads;  // 16-byte dQ pieces per thread
+  auto store_dq = [&](int par) {
+#pragma unroll
+    for (int u = 0; u < OP; ++u) {
+      const int c = threadIdx.x + kThreads * u;
+      const int m = c / CPR, col = c % CPR;  // a row's pieces in consecutive lanes
+      const uint4 x = *reinterpret_cast<const uint4*>(&L.dqt[m * L_::QROW + col * 16]);
+      *reinterpret_cast<uint4*>(part_dq + L.dqoff[par][m] + col * 8) = x;
+    }
+  };
+
   for (int m0 = 0; m0 < mrows; m0 += 32) {
+    const int par = (m0 >> 5) & 1;
     __syncthreads();  // previous sub-chunk's buffers are free (and the staging is complete)
-    // ---- this sub-chunk's Q and dO: row-major and transposed copies
+    store_dq(par ^ 1);  // the previous sub-chunk's dQ
+    // ---- this sub-chunk's Q and dO (rows past the list as zeros)
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int c = threadIdx.x + kThreads * u;
       const int m = c % 32, col = c / 32;
-      *reinterpret_cast<uint4*>(&L.qs[m * L_::QROW + col * 16]) = nq[u];
-      *reinterpret_cast<uint4*>(&L.dos[m * L_::QROW + col * 16]) = ng[u];
-      const uint32_t wq[4] = {nq[u].x, nq[u].y, nq[u].z, nq[u].w}, wg[4] = {ng[u].x, ng[u].y, ng[u].z, ng[u].w};
-      const int mc = mrow_col(m);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        *reinterpret_cast<uint16_t*>(&L.qt[(col * 8 + e) * L_::TROW + mc * 2]) = (uint16_t)(wq[e >> 1] >> sh);
-        *reinterpret_cast<uint16_t*>(&L.dot[(col * 8 + e) * L_::TROW + mc * 2]) = (uint16_t)(wg[e >> 1] >> sh);
-      }
+      const bool ok = m0 + m < mrows;
+      *reinterpret_cast<uint4*>(&L.qs[m * L_::QROW + col * 16]) = ok ? nq[u] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&L.dos[m * L_::QROW + col * 16]) = ok ? ng[u] : make_uint4(0u, 0u, 0u, 0u);
     }
     if (threadIdx.x < 32) {
-      const int m = threadIdx.x;
-      L.lse2[m] = n_lse2;
-      L.drow[m] = n_drow;
-      L.pos[m] = n_pos;
-      L.dqoff[m] = n_dqoff;
+      const int m = threadIdx.x, mr = m0 + m;
+      const bool ok = mr < mrows;
+      const int64_t pidx = (((int64_t)s * D.T + n_t) * D.Hkv + g) * D.k + n_slot;
+      L.lse2[m] = ok ? n_lse * kLog2e : INFINITY;  // P = 0 for an M-row past the list
+      L.drow[m] = ok ? n_drow : 0.0f;
+      L.pos[m] = ok ? D.pos0 + n_t : -1;
+      L.dqoff[par][m] = ok ? (pidx * G + mr % G) * DH : dq_trash;
     }
-    if (m0 + 32 < mrows) {
-      fetch(m0 + 32);
-      fetch_meta(m0 + 32);
-    }
+    fetch(m0 + 32);  // past the last sub-chunk: row-0 loads, never used
+    fetch_meta(m0 + 32);
     __syncthreads();
 
     // ---- S = Q K^T and dP = dO V^T for this wave's 32 keys
@@ -312,9 +321,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
     for (int pp = 0; pp < 2; ++pp) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&L.dot[(32 * dt + nl) * L_::TROW + (16 * pp + 8 * h) * 2]);
+        // rows (M-rows) 16 pp + 4 h + {0..3} and 16 pp + 8 + 4 h + {0..3}: register group pp
+        const bf16x8 ag = tr_operand(L.dos, L_::QROW, 16 * pp + 4 * h, 16 * pp + 8 + 4 * h, 32 * dt, lane);
         dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pb[pp], dvt[dt], 0, 0, 0);
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&L.qt[(32 * dt + nl) * L_::TROW + (16 * pp + 8 * h) * 2]);
+        const bf16x8 aq = tr_operand(L.qs, L_::QROW, 16 * pp + 4 * h, 16 * pp + 8 + 4 * h, 32 * dt, lane);
         dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[pp], dkt[dt], 0, 0, 0);
       }
     }
@@ -330,16 +340,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
 #pragma unroll
       for (int ks = 0; ks < kBlk / 16; ++ks) {
         const bf16x8 as = *reinterpret_cast<const bf16x8*>(&L.ds[nl * L_::SROW + (16 * ks + 8 * h) * 2]);
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&L.kt[(32 * wave + nl) * L_::KTROW + (16 * ks + 8 * h) * 2]);
+        // keys 16 ks + 8 h + {0..7}, the order of the dS row read above
+        const bf16x8 bk = tr_operand(L.kr, L_::KROW, 16 * ks + 8 * h, 16 * ks + 8 * h + 4, 32 * wave, lane);
         qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bk, qacc, 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t o = L.dqoff[acc_row(r, h)];
-        if (o >= 0) part_dq[o + 32 * wave + nl] = f32_to_bf16(qacc[r] * D.scale);
-      }
+      for (int r = 0; r < 16; ++r)
+        *reinterpret_cast<uint16_t*>(&L.dqt[acc_row(r, h) * L_::QROW + (32 * wave + nl) * 2]) =
+            f32_to_bf16(qacc[r] * D.scale);
     }
   }
+  __syncthreads();
+  store_dq(((mrows - 1) >> 5) & 1);  // the last sub-chunk's dQ
 
   // ---- dK, dV of the block: through LDS (row-major fp32 over the K / V staging area) so
   // that the atomic adds of a wave cover contiguous head dims
@@ -594,7 +606,8 @@ BwdWs backward_layout(const Dims& D, void* base, size_t* total) {
   w.drow = p ? reinterpret_cast<float*>(p + off) : nullptr;
   off += align_up((size_t)D.S * D.T * D.H * sizeof(float), 256);
   w.part_dq = p ? reinterpret_cast<uint16_t*>(p + off) : nullptr;
-  off += align_up((size_t)D.S * D.T * D.Hkv * D.k * D.G * D.d * sizeof(uint16_t), 256);
+  // + one scratch row (d values) that M-rows past an item's list write to
+  off += align_up(((size_t)D.S * D.T * D.Hkv * D.k * D.G + 1) * D.d * sizeof(uint16_t), 256);
   *total = off;
   return w;
 }
