@@ -413,8 +413,10 @@ def token_decode(args, msa, wd, xd, block_sel):
         sec = st["token_scores"]["ms"] / 1e3
         st["token_scores"].update(roofline(2.0 * wd.dI * wd.S * wd.Hkv * wd.N, kbytes, sec))
     if "token_topk" in st:
+        # algorithmic: every eligible score read once, the chosen positions written once
         sec = st["token_topk"]["ms"] / 1e3
-        st["token_topk"].update(roofline(0.0, 5 * 4.0 * wd.S * wd.Hkv * wd.N, sec))   # 5 passes over the scores
+        rows = wd.S * wd.Hkv * wd.T
+        st["token_topk"].update(roofline(0.0, 4.0 * rows * wd.N + 4.0 * rows * budget, sec))
     tok = tb.sel_tok                                            # [S, Hkv, 1, budget]
     blk = block_sel                                             # [S, Hkv, 1, k]
     inside = ((tok.unsqueeze(-1) // 128) == blk.unsqueeze(-2)).any(-1) & (tok >= 0)

@@ -114,7 +114,7 @@ def lib():
         L.msa_index_topk.argtypes = [PP, P, P, P, P, ctypes.c_size_t, P]
         L.msa_index_topk.restype = st
         L.msa_token_scores.argtypes = [PP, P, P, P, P]
-        L.msa_token_topk.argtypes = [PP, ctypes.c_int32, P, P, P]
+        L.msa_token_topk.argtypes = [PP, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
         L.msa_token_attn_decode.argtypes = [PP, ctypes.c_int32, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_token_workspace_bytes.argtypes = [PP, ctypes.c_int32]
         L.msa_token_workspace_bytes.restype = ctypes.c_size_t
@@ -271,9 +271,10 @@ def token_scores(prob: Problem, q_idx, k_idx, scores, stream=None) -> None:
     _check(lib().msa_token_scores(ctypes.byref(prob), _ptr(q_idx), _ptr(k_idx), _ptr(scores), _stream(stream, q_idx)))
 
 
-def token_topk(prob: Problem, budget: int, scores, sel_tok, stream=None) -> None:
-    _check(lib().msa_token_topk(ctypes.byref(prob), int(budget), _ptr(scores), _ptr(sel_tok),
-                                _stream(stream, scores)))
+def token_topk(prob: Problem, budget: int, scores, sel_tok, workspace, workspace_bytes_: int,
+               stream=None) -> None:
+    _check(lib().msa_token_topk(ctypes.byref(prob), int(budget), _ptr(scores), _ptr(sel_tok), _ptr(workspace),
+                                workspace_bytes_, _stream(stream, scores)))
 
 
 def token_workspace_bytes(prob: Problem, budget: int) -> int:
@@ -453,7 +454,7 @@ def run_token_decode(prob: Problem, q, k_cache, v_cache, q_idx, k_idx, bufs: Tok
                      stream=None) -> None:
     """Token-level decode step: token scores -> top-budget tokens -> attention over them."""
     token_scores(prob, q_idx, k_idx, bufs.scores, stream)
-    token_topk(prob, budget, bufs.scores, bufs.sel_tok, stream)
+    token_topk(prob, budget, bufs.scores, bufs.sel_tok, bufs.ws, bufs.ws.numel(), stream)
     token_attn_decode(prob, budget, q, k_cache, v_cache, bufs.sel_tok, bufs.out, bufs.ws, bufs.ws.numel(), stream)
 
 

@@ -510,14 +510,19 @@ msa_status msa_token_scores(const msa_problem* prob, const void* q_idx, const vo
 }
 
 msa_status msa_token_topk(const msa_problem* prob, int32_t budget, const float* scores, int32_t* sel_tok,
-                          void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream) {
   msa::Dims D;
   msa_status st = check_problem(prob, &D, false, false);
   if (st != MSA_OK) return st;
   if ((st = check_token(D, budget)) != MSA_OK) return st;
   REQUIRE_PTR(scores);
   REQUIRE_PTR(sel_tok);
-  return device_status(msa::launch_token_topk(D, budget, scores, sel_tok, (hipStream_t)stream),
+  const size_t need = msa::token_topk_workspace_bytes(D);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_token_topk needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  REQUIRE_PTR(workspace);
+  return device_status(msa::launch_token_topk(D, budget, scores, sel_tok, workspace, (hipStream_t)stream),
                        "msa_token_topk launch");
 }
 

@@ -73,7 +73,9 @@ hipError_t launch_index_topk(const Dims& D, const void* q_idx, const void* k_idx
 
 // Token-level selection (index_scores.hip, token.hip).
 hipError_t launch_token_scores(const Dims& D, const void* q_idx, const void* k_idx, float* tok, hipStream_t st);
-hipError_t launch_token_topk(const Dims& D, int budget, const float* tok, int32_t* sel_tok, hipStream_t st);
+hipError_t launch_token_topk(const Dims& D, int budget, const float* tok, int32_t* sel_tok, void* ws,
+                             hipStream_t st);
+size_t token_topk_workspace_bytes(const Dims& D);
 size_t token_workspace_bytes(const Dims& D, int budget);
 hipError_t launch_token_attn(const Dims& D, int budget, const void* q, const void* k, const void* v,
                              const int32_t* sel_tok, void* out, void* ws, hipStream_t st);

@@ -307,7 +307,10 @@ msa_status msa_index_backward(const msa_problem* prob, const void* q_idx, const 
  *   for j <= p_t; entries j > p_t are not written.
  * msa_token_topk: sel_tok [S, Hkv, T, budget] int32: the budget positions j <= p_t with the
  *   largest scores (ties to the lower position; no forced token), in ascending order, -1
- *   padded when fewer are eligible.  Reads only scores[s,g,t,0..p_t].
+ *   padded when fewer are eligible.  Reads only scores[s,g,t,0..p_t].  workspace: at least
+ *   msa_token_workspace_bytes(prob, budget) bytes (per-row histograms and candidate lists;
+ *   MSA_ERR_WORKSPACE_TOO_SMALL otherwise); the same buffer may then serve
+ *   msa_token_attn_decode on the same stream.
  * msa_token_attn_decode: out [S, T, H, d]: for each query head, the exact softmax attention
  *   over the row's selected positions (the block-level definition with block size 1).
  *   workspace: msa_workspace_bytes(prob, MSA_CALL_TOKEN_DECODE) bytes for budget = 2048;
@@ -316,7 +319,7 @@ msa_status msa_index_backward(const msa_problem* prob, const void* q_idx, const 
 msa_status msa_token_scores(const msa_problem* prob, const void* q_idx, const void* k_idx, float* scores,
                             void* stream);
 msa_status msa_token_topk(const msa_problem* prob, int32_t budget, const float* scores, int32_t* sel_tok,
-                          void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream);
 msa_status msa_token_attn_decode(const msa_problem* prob, int32_t budget, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* sel_tok, void* out, void* workspace,
                                  size_t workspace_bytes, void* stream);

@@ -102,6 +102,20 @@ def test_workspace_too_small_is_rejected():
     assert ei.value.status == msa.MSA_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_token_topk_needs_its_workspace():
+    # per row: a histogram, a chunk table and up to 16384 candidates (key + position)
+    p = _good(num_q=2, kv_len=300000)
+    need = msa.token_workspace_bytes(p, 2048)
+    rows = p.batch * p.num_kv_heads * p.num_q
+    assert need >= rows * 2 * 16384 * 4
+    with pytest.raises(msa.MSAError) as ei:
+        msa.token_topk(p, 2048, 1, 1, 1, need - 1, stream=0)
+    assert ei.value.status == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(msa.MSAError) as ei:
+        msa.token_topk(p, 2048, 1, 1, None, need, stream=0)
+    assert ei.value.status == msa.MSA_ERR_INVALID_ARGUMENT
+
+
 def test_workspace_sizes_scale_with_partials():
     # prefill workspace holds T*Hkv*k*G partials of (d bf16 + 1 fp32)
     p = _good(num_q=1000, kv_len=1000)

@@ -55,8 +55,8 @@ def test_token_decode_matches_the_oracle(wl, budget):
 @pytest.mark.parametrize("kind", ["few_values", "all_equal", "signed_zero", "one_huge"])
 def test_token_topk_adversarial_rows(kind):
     require_gpu()
-    S, T, N, budget = 1, 2, 70000, 2048
-    wl = W.small("tok_adv", S=S, T=T, N=N, H=8, Hkv=1, d=128, dI=64, k=16)
+    T, N, budget = 2, 70000, 2048
+    wl = W.small("tok_adv", S=1, T=T, N=N, H=8, Hkv=1, d=128, dI=64, k=16)
     prob = wl.problem()
     pos = oracle.positions(N, T)
     rng = np.random.default_rng(5)
@@ -70,9 +70,46 @@ def test_token_topk_adversarial_rows(kind):
     else:
         rows = rng.standard_normal((T, N)).astype(np.float32)
         rows[:, 12345] = 3e38
-    sc = torch.from_numpy(rows).reshape(S, 1, T, N).cuda()
-    sel = torch.empty((S, 1, T, budget), dtype=torch.int32, device="cuda")
-    msa.token_topk(prob, budget, sc, sel)
+    _check_topk(prob, rows, pos, budget)
+
+
+def _check_topk(prob, rows, pos, budget):
+    """msa_token_topk on rows [T, N] of one (sequence, group) against the oracle's top-k."""
+    T, N = rows.shape
+    sc = torch.from_numpy(rows).reshape(1, 1, T, N).cuda()
+    sel = torch.empty((1, 1, T, budget), dtype=torch.int32, device="cuda")
+    nws = msa.token_workspace_bytes(prob, budget)
+    ws = torch.empty((nws,), dtype=torch.uint8, device="cuda")
+    msa.token_topk(prob, budget, sc, sel, ws, nws)
     torch.cuda.synchronize()
     ref = oracle.slice_token_topk(np.where(np.arange(N)[None, :] <= pos[:, None], rows, np.nan), pos, budget)
     np.testing.assert_array_equal(sel.cpu().numpy()[0, 0], ref)
+
+
+@pytest.mark.parametrize("N,budget", [(300000, 2048), (200001, 700), (1048576, 8192)])
+def test_token_topk_long_rows(N, budget):
+    """Rows of many 16384-position chunks (the chunked path): Gaussian scores plus a band
+    of large values and a few equal maxima."""
+    require_gpu()
+    say("long rows", N, "budget", budget)
+    T = 2
+    wl = W.small("tok_long", S=1, T=T, N=N, H=8, Hkv=1, d=128, dI=64, k=16)
+    pos = oracle.positions(N, T)
+    rng = np.random.default_rng(N)
+    rows = (3.0 * rng.standard_normal((T, N))).astype(np.float32)
+    rows[:, 1000:1400] += 6.0
+    rows[:, 77777 % N] = rows[:, 5 % N] = 50.0
+    _check_topk(wl.problem(), rows, pos, budget)
+
+
+def test_token_topk_overflow_and_normal_rows_in_one_call():
+    """One row whose candidates exceed the chunked path's capacity (all equal: the one-
+    workgroup path takes it) next to an ordinary row."""
+    require_gpu()
+    T, N, budget = 2, 100000, 2048
+    wl = W.small("tok_mixed", S=1, T=T, N=N, H=8, Hkv=1, d=128, dI=64, k=16)
+    pos = oracle.positions(N, T)
+    rows = np.empty((T, N), np.float32)
+    rows[0] = 0.25
+    rows[1] = np.random.default_rng(3).standard_normal(N).astype(np.float32)
+    _check_topk(wl.problem(), rows, pos, budget)
