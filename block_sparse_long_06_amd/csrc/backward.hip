@@ -48,27 +48,7 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// An MFMA operand read TRANSPOSED out of a row-major bf16 tile in LDS: lane (n = lane % 32,
-// half h = lane / 32) gets column col0 + n of rows r0 + {0..3} (elements 0..3) and
-// r1 + {0..3} (elements 4..7); r0 and r1 may depend on h.  ds_read_b64_tr_b16 works in
-// groups of 16 lanes: destination lane i receives, as element j, the (i % 4)-th 16-bit
-// value of the 8 bytes addressed by source lane 4 j + i / 4, so source lane s = 4 j + q
-// addresses row r + j at columns col0 + 16 * (lane / 16 % 2) + 4 q .. + 3.
-__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int row_bytes, int r0, int r1, int col0,
-                                             int lane) {
-  const int sl = lane & 15, j = sl >> 2, q = sl & 3;
-  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * q;
-  typedef __attribute__((address_space(3))) unsigned char lds_u8;
-  const lds_u8* t = (const lds_u8*)tile;
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r0 + j) * row_bytes + col * 2));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r1 + j) * row_bytes + col * 2));
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, ab);
-}
+// (transposed operand reads: tr_operand, msa_internal.hpp)
 
 // M-row held by accumulator register r of lane half h (32x32 output layout).
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }

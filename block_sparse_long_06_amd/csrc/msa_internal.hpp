@@ -177,4 +177,28 @@ __device__ __forceinline__ int64_t kv_row(const Dims& D, int s, int g, int j, in
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// An MFMA operand (8 bf16) read TRANSPOSED out of a row-major bf16 tile in LDS with
+// gfx950's ds_read_b64_tr_b16: lane (n = lane % 32, half h = lane / 32) gets column
+// col0 + n of rows r0 + {0..3} (elements 0..3) and r1 + {0..3} (elements 4..7); r0 and r1
+// may depend on h.  The instruction works in groups of 16 lanes: destination lane i
+// receives, as element j, the (i % 4)-th 16-bit value of the 8 bytes addressed by source
+// lane 4 j + i / 4 (established with an in-bounds probe), so source lane s = 4 j + q
+// addresses row r + j at columns col0 + 16 * (lane / 16 % 2) + 4 q .. + 3.  Addresses are
+// 8-byte aligned when row_bytes and col0 are multiples of 8 bytes / 4 elements.
+typedef __bf16 tr_bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ tr_bf16x8 tr_operand(const unsigned char* tile, int row_bytes, int r0, int r1, int col0,
+                                                int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const int sl = lane & 15, j = sl >> 2, q = sl & 3;
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * q;
+  const lds_u8* t = (const lds_u8*)tile;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r0 + j) * row_bytes + col * 2));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r1 + j) * row_bytes + col * 2));
+  const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(tr_bf16x8, ab);
+}
+
 }  // namespace msa
