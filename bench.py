@@ -10,7 +10,8 @@ value  = prefill tokens/s = 131,072 / (device time of the prefill part of a step
 decode = us per decode step (all 16 sequences advance one token), and / 16
 
 Per-kernel device times come from the library's own hipEvent timer (events recorded
-on the launch stream around every launch) over the timed region.  The roofline
+on the launch stream around every launch) over the timed region: the mean per launch,
+and p50 / p95 over the launches (by default 20 timed steps after 3 warm-ups).  The roofline
 object prices the dominant kernel's ALGORITHMIC work (causal triangle, selected keys
 only, every tensor read or written once) against MI355X peaks (bf16 dense MFMA
 2.5 PFLOP/s, HBM 8 TB/s).
@@ -81,6 +82,15 @@ def attention_reduction_ratio(G, d, dI, N, budget=2048):
     causal prefill of N tokens: 2*G*d*n / (2*G*d*budget + dI*n) at n = N/2."""
     n = N / 2.0
     return (2.0 * G * d * n) / (2.0 * G * d * budget + dI * n)
+
+
+def percentiles(samples):
+    """p50 / p95 (ms) of per-launch or per-step times."""
+    import numpy as np
+    if not samples:
+        return {}
+    a = np.asarray(samples, dtype=np.float64)
+    return dict(p50_ms=float(np.percentile(a, 50)), p95_ms=float(np.percentile(a, 95)))
 
 
 def roofline(flops, nbytes, seconds):
@@ -477,8 +487,8 @@ def train_step(args, msa, wl):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--prefill", default="C2", choices=["C1", "C2", "C4"],
@@ -569,10 +579,12 @@ def main():
                  "decode_simple", "decode_merge"):
         ms, n = msa.profiler_read(name, reset=False)
         if n:
-            kern[name] = dict(total_ms=ms, launches=n)
+            kern[name] = dict(total_ms=ms, launches=n, samples=msa.profiler_samples(name))
     msa.profiler_read(None, reset=True)
-    prefill_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)) / args.steps
-    decode_ms = (sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)) / args.steps) if db else None
+    prefill_steps = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    decode_steps = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)] if db else None
+    prefill_ms = sum(prefill_steps) / args.steps
+    decode_ms = (sum(decode_steps) / args.steps) if db else None
     print("[bench] timed %d steps: prefill %.3f ms, decode %s ms" % (args.steps, prefill_ms,
           "%.3f" % decode_ms if decode_ms else "-"), file=sys.stderr, flush=True)
 
@@ -593,7 +605,8 @@ def main():
             continue
         per_launch_s = kern[kname]["total_ms"] / kern[kname]["launches"] / 1e3
         rf = roofline(model[stage]["flops"], model[stage]["bytes"], per_launch_s)
-        stages[kname] = dict(ms=per_launch_s * 1e3, flops=model[stage]["flops"], bytes=model[stage]["bytes"], **rf)
+        stages[kname] = dict(ms=per_launch_s * 1e3, **percentiles(kern[kname]["samples"]),
+                             flops=model[stage]["flops"], bytes=model[stage]["bytes"], **rf)
     inv_ms = sum(kern[n]["total_ms"] for n in ("invert_count", "invert_scatter", "invert_offsets") if n in kern)
     stages["invert(all launches)"] = dict(ms=inv_ms / args.steps)
     split_ms = sum(kern[n]["total_ms"] for n in ("hot_select", "cold_count", "cold_scatter", "cold_offsets")
@@ -620,7 +633,8 @@ def main():
         for kn in ("idx_scores_stream", "idx_scores_rows"):
             if kn in kern:
                 s_ = kern[kn]["total_ms"] / kern[kn]["launches"] / 1e3
-                dstages[kn] = dict(ms=s_ * 1e3, **roofline(dm["idx_scores"]["flops"], dm["idx_scores"]["bytes"], s_))
+                dstages[kn] = dict(ms=s_ * 1e3, **percentiles(kern[kn]["samples"]),
+                                   **roofline(dm["idx_scores"]["flops"], dm["idx_scores"]["bytes"], s_))
         if "block_topk_t1" in kern:
             s_ = kern["block_topk_t1"]["total_ms"] / kern["block_topk_t1"]["launches"] / 1e3
             dstages["block_topk_t1"] = dict(ms=s_ * 1e3, **roofline(0.0, dm["block_topk"]["bytes"], s_))
@@ -631,6 +645,8 @@ def main():
         if "decode_merge" in kern:
             dstages["decode_merge"] = dict(ms=kern["decode_merge"]["total_ms"] / kern["decode_merge"]["launches"])
         dec = dict(workload=wd.description, us_per_step=decode_ms * 1e3, us_per_token_amortised=decode_ms * 1e3 / wd.S,
+                   us_per_step_p50=1e3 * percentiles(decode_steps)["p50_ms"],
+                   us_per_step_p95=1e3 * percentiles(decode_steps)["p95_ms"],
                    sequences=wd.S, kv_len=wd.N, stages=dstages)
 
     dec8 = None
@@ -703,7 +719,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wp.description, "batch": wp.S, "seq_len": wp.T, "num_heads": wp.H,
                    "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
-        "prefill_ms": prefill_ms, "wall_s_timed": wall,
+        "prefill_ms": prefill_ms, "prefill_ms_p50": percentiles(prefill_steps)["p50_ms"],
+        "prefill_ms_p95": percentiles(prefill_steps)["p95_ms"], "wall_s_timed": wall,
         "fused_selection": fsel,
         "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "decode_token_level": dect,
         "training_step": trn, "stages": stages, "roofline": roof, "cpu_baseline": cpu,

@@ -25,7 +25,8 @@ MSA_F32, MSA_BF16, MSA_FP8_E4M3 = 0, 1, 2
 
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_invert_selection", "msa_sparse_attn_prefill",
             "msa_sparse_attn_decode", "msa_workspace_bytes", "msa_status_string",
-            "msa_last_error_message", "msa_profiler_enable", "msa_profiler_read", "msa_index_scores_kv",
+            "msa_last_error_message", "msa_profiler_enable", "msa_profiler_read", "msa_profiler_samples",
+            "msa_index_scores_kv",
             "msa_block_topk_kv", "msa_sparse_attn_decode_kv", "msa_sparse_attn_prefill_train",
             "msa_sparse_attn_backward", "msa_index_kl", "msa_index_backward", "msa_token_scores",
             "msa_token_topk", "msa_token_attn_decode", "msa_token_workspace_bytes", "msa_index_topk",
@@ -136,6 +137,9 @@ def lib():
         L.msa_profiler_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
         L.msa_profiler_read.restype = st
+        L.msa_profiler_samples.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int64,
+                                           ctypes.POINTER(ctypes.c_int64)]
+        L.msa_profiler_samples.restype = st
         _lib = L
     return _lib
 
@@ -299,6 +303,16 @@ def profiler_read(kernel: str | None = None, reset: bool = True):
     _check(lib().msa_profiler_read(kernel.encode() if kernel else None, ctypes.byref(ms), ctypes.byref(n),
                                    1 if reset else 0))
     return ms.value, n.value
+
+
+def profiler_samples(kernel: str | None = None) -> list:
+    """The individual launch durations (ms) of `kernel` (None = all) since the last reset."""
+    n = ctypes.c_int64()
+    name = kernel.encode() if kernel else None
+    _check(lib().msa_profiler_samples(name, None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_float * max(n.value, 1))()
+    _check(lib().msa_profiler_samples(name, buf, n.value, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]
 
 
 # ------------------------------------------------------------------ allocating helpers

@@ -610,4 +610,24 @@ msa_status msa_profiler_read(const char* kernel, double* total_ms, int64_t* laun
   return ok();
 }
 
+msa_status msa_profiler_samples(const char* kernel, float* ms_out, int64_t capacity, int64_t* count) {
+  if (count == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "count must not be NULL");
+  if (capacity > 0 && ms_out == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "ms_out must not be NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int64_t n = 0;
+  for (auto& r : g_prof) {
+    if (!r.used) continue;
+    if (kernel != nullptr && kernel[0] != '\0' && r.name != kernel) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return device_status(e, "profiler event wait");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return device_status(e, "profiler elapsed time");
+    if (n < capacity) ms_out[n] = ms;
+    ++n;
+  }
+  *count = n;
+  return ok();
+}
+
 }  // extern "C"

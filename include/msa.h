@@ -344,6 +344,11 @@ const char* msa_last_error_message(void);
  */
 msa_status msa_profiler_enable(int on);
 msa_status msa_profiler_read(const char* kernel, double* total_ms, int64_t* launches, int reset);
+/* The individual launch durations (ms) of `kernel` (NULL or "" = every kernel) recorded
+ * since the last reset, in no particular order (for percentiles): the first
+ * min(capacity, count) are written to ms_out (caller-owned host memory, may be NULL when
+ * capacity is 0) and *count receives the number recorded.  Does not reset. */
+msa_status msa_profiler_samples(const char* kernel, float* ms_out, int64_t capacity, int64_t* count);
 
 #ifdef __cplusplus
 }
