@@ -5,7 +5,7 @@
 // chose the block).
 //
 // A stable counting sort, deterministic (no order depends on timing):
-//  1. count:   per chunk of kChunkT query rows of one (s, g), an LDS histogram over
+//  1. count:   per chunk of `ct` query rows of one (s, g), an LDS histogram over
 //              blocks, stored as cnt[(sg, b, chunk)] (chunk fastest);
 //  2. scan:    exclusive prefix sum over cnt in (sg, b, chunk) order = the global
 //              position of the first entry of each (sg, b, chunk);
@@ -21,17 +21,25 @@
 namespace msa {
 namespace {
 
-constexpr int kChunkT = 1024;  // query rows per chunk
+// Query rows per chunk: 256 .. 1024, the largest power of two that still gives about
+// 2048 chunks (one wave each in the scatter: the ranking is latency-bound, so it wants
+// many waves; larger chunks mean fewer counts to scan and fewer masks to clear).
+int chunk_rows(const Dims& D) {
+  const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
+  int c = 256;
+  while (c < 1024 && rows / (2 * c) >= 2048) c *= 2;
+  return c;
+}
 
 __global__ void __launch_bounds__(256) invert_count(Dims D, const int32_t* __restrict__ sel,
-                                                    int* __restrict__ cnt, int nchunks) {
+                                                    int* __restrict__ cnt, int nchunks, int ct) {
   extern __shared__ int hist[];
   const int c = blockIdx.x;
   const int64_t sg = blockIdx.y;
   for (int b = threadIdx.x; b < D.nb; b += 256) hist[b] = 0;
   __syncthreads();
-  const int t0 = c * kChunkT;
-  const int t1 = min(t0 + kChunkT, D.T);
+  const int t0 = c * ct;
+  const int t1 = min(t0 + ct, D.T);
   const int64_t e0 = (sg * D.T + t0) * D.k;
   const int64_t e1 = (sg * D.T + t1) * D.k;
   for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
@@ -60,7 +68,7 @@ __global__ void __launch_bounds__(256) invert_offsets(Dims D, const int* __restr
 
 __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __restrict__ sel,
                                                      const int* __restrict__ pos,
-                                                     int32_t* __restrict__ entries, int nchunks) {
+                                                     int32_t* __restrict__ entries, int nchunks, int ct) {
   extern __shared__ unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
   uint16_t* run = reinterpret_cast<uint16_t*>(smem + sizeof(unsigned long long) * D.nb);
@@ -72,8 +80,8 @@ __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __re
     run[b] = 0;
   }
   __syncthreads();
-  const int t0 = c * kChunkT;
-  const int t1 = min(t0 + kChunkT, D.T);
+  const int t0 = c * ct;
+  const int t1 = min(t0 + ct, D.T);
   const unsigned long long lower = (1ull << lane) - 1ull;
   const int* pos_c = pos + (sg * D.nb) * nchunks + c;  // pos of (sg, b, c) = pos_c[b * nchunks]
   for (int tb = t0; tb < t1; tb += 64) {
@@ -112,7 +120,7 @@ __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __re
 
 }  // namespace
 
-static int invert_chunks(const Dims& D) { return (D.T + kChunkT - 1) / kChunkT; }
+static int invert_chunks(const Dims& D) { return (D.T + chunk_rows(D) - 1) / chunk_rows(D); }
 
 size_t invert_workspace_bytes(const Dims& D) {
   const int64_t m = (int64_t)D.S * D.Hkv * D.nb * invert_chunks(D);
@@ -136,7 +144,7 @@ hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, in
   {
     LaunchScope s("invert_count", st);
     hipLaunchKernelGGL(invert_count, dim3(nchunks, (unsigned)nsg), dim3(256), D.nb * sizeof(int), st, D,
-                       sel, cnt, nchunks);
+                       sel, cnt, nchunks, chunk_rows(D));
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -157,7 +165,7 @@ hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, in
     if (e != hipSuccess) return e;
     LaunchScope s("invert_scatter", st);
     hipLaunchKernelGGL(invert_scatter, dim3(nchunks, (unsigned)nsg), dim3(64), lds, st, D, sel, pos,
-                       entries, nchunks);
+                       entries, nchunks, chunk_rows(D));
   }
   return hipGetLastError();
 }
