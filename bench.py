@@ -195,6 +195,46 @@ def measured_traffic(kernel):
 
 
 # ------------------------------------------------------------------ CPU baseline
+def achievable_peaks():
+    """What this machine reaches with vendor-library kernels, for context beside the vendor
+    peaks (the rooflines stay against the vendor peaks): a square bf16 GEMM (hipBLASLt via
+    torch.matmul of contiguous operands), a device-to-device copy (bytes read + written)
+    and a plain sum (bytes read), each the best of 5 timed repetitions."""
+    import torch
+    out = {}
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev0.record()
+            fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            ts.append(ev0.elapsed_time(ev1) / 1e3)
+        return min(ts)
+
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    t = best(lambda: torch.matmul(a, b, out=c))
+    out["bf16_gemm_8192_tflops"] = 2.0 * n ** 3 / t / 1e12
+    del a, b, c
+    x = torch.ones((1 << 31,), dtype=torch.bfloat16, device="cuda")   # 4 GiB
+    y = torch.empty_like(x)
+    t = best(lambda: y.copy_(x))
+    out["hbm_copy_GBps"] = 2.0 * x.numel() * 2 / t / 1e9
+    t = best(lambda: x.sum())
+    out["hbm_read_sum_GBps"] = x.numel() * 2 / t / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    out["vendor_peaks"] = dict(bf16_dense_tflops=PEAK_MFMA_BF16 / 1e12, hbm_GBps=PEAK_HBM / 1e9)
+    return out
+
+
 def cpu_baseline(wl, inputs, seconds_budget=12.0):
     """The oracle, as is, on a bounded sample of query rows of the same workload:
     index scores, top-k, inversion and attention for R rows x all groups.
@@ -706,6 +746,10 @@ def main():
         trn = train_step(args, msa, {"C1": W.C1, "C2": W.C2}[args.train])
         print("[bench] training step (%s): %.3f ms" % (args.train, trn["ms_per_step"]), file=sys.stderr, flush=True)
 
+    peaks = achievable_peaks()
+    print("[bench] achievable: bf16 GEMM %.0f TFLOP/s, copy %.0f GB/s, read %.0f GB/s" % (
+        peaks["bf16_gemm_8192_tflops"], peaks["hbm_copy_GBps"], peaks["hbm_read_sum_GBps"]), file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline ...", file=sys.stderr, flush=True)
@@ -723,7 +767,7 @@ def main():
         "prefill_ms_p95": percentiles(prefill_steps)["p95_ms"], "wall_s_timed": wall,
         "fused_selection": fsel,
         "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "decode_token_level": dect,
-        "training_step": trn, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
+        "training_step": trn, "stages": stages, "roofline": roof, "achievable_peaks": peaks, "cpu_baseline": cpu,
         "selection_structure": selection_structure(wp, pb.sel, pb.csr_offsets),
         "attention_pairs": split["pairs"],
     }
