@@ -136,6 +136,8 @@ def test_profiler_read_without_records():
     msa.profiler_enable(False)
     ms, n = msa.profiler_read(None)
     assert ms == 0.0 and n == 0
+    assert msa.profiler_samples(None) == []
+    assert msa.profiler_samples("idx_scores_mfma") == []
 
 
 def _layout(kv_lens=1, block_table=None, stride=0, pages=0):

@@ -289,3 +289,25 @@ def test_generator_device_matches_host():
             else:
                 got = dev.cpu().numpy()
             assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(host).view(np.uint8)), (wl.name, name)
+
+
+def test_profiler_samples_add_up_to_the_totals():
+    """The per-launch durations of the library timer sum to its totals, one per launch."""
+    require_gpu()
+    wl = W.small("prof", S=1, T=600, N=600, H=8, Hkv=2, d=64, dI=32, k=4)
+    inputs = gen(wl)
+    prob = wl.problem()
+    pb = msa.alloc_prefill(prob)
+    msa.profiler_read(None, reset=True)
+    msa.profiler_enable(True)
+    for _ in range(3):
+        msa.run_prefill(prob, inputs["q"], inputs["k"], inputs["v"], inputs["q_idx"], inputs["k_idx"], pb)
+    torch.cuda.synchronize()
+    msa.profiler_enable(False)
+    for name in ("idx_scores_mfma", "block_topk", "lse_merge", None):
+        ms, n = msa.profiler_read(name, reset=False)
+        xs = msa.profiler_samples(name)
+        assert len(xs) == n and n >= 3 and all(x >= 0.0 for x in xs)
+        assert abs(sum(xs) - ms) <= 1e-6 * max(1.0, ms) + 1e-3
+    msa.profiler_read(None, reset=True)
+    assert msa.profiler_samples(None) == []
