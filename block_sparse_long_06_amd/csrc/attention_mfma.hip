@@ -14,9 +14,10 @@
 // The next sub-chunk's Q rows are fetched into registers while the current one
 // computes; two waves per SIMD overlap one wave's softmax with the other's MFMAs.
 //
-//  * LDS: K and V row-major (16-byte row pad).  The PV contraction's A operand (V^T: a
-//    lane's head dim over 8 keys) is read transposed with ds_read_b64_tr_b16 (tr_operand),
-//    rows = the 8 keys of the P item below.
+//  * LDS: K row-major (16-byte row pad), V TRANSPOSED (d x 128, 16-byte row pad).  In
+//    a V^T row the keys of every 16-key group are stored in the order in which one lane
+//    half feeds them to the PV contraction (see the P item below), so a lane fetches its
+//    8 keys of one head dim with one 16-byte read.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys, B = 32 M-rows): a lane's
 //    output column is one M-row, so row max and row sum are in-lane over 64 values
 //    plus one exchange with lane ^ 32.
@@ -24,7 +25,8 @@
 //    kt hold 8 keys of the lane's M-row, exactly the 8 k-elements a lane supplies to
 //    a B operand, so O^T = V^T P^T uses k-step (kt, p) with the accumulator's row
 //    order.  Those 8 keys of lane half h are k0 + 4h + {0..3} and k0 + 8 + 4h + {0..3}
-//    (k0 = 32 kt + 16 p): two transposed 8-byte reads of V rows.
+//    (k0 = 16 p); V^T stores key k0 + 8a + 4h + x at column k0 + 8h + 4a + x, so they
+//    are one contiguous 16-byte run.
 //  * 32x32 accumulator layout: output row i is held by lane half (i % 8) / 4 in
 //    register 4 * (i / 8) + i % 4.  The QK contraction visits head dims in the order
 //    lane half h, k-step s -> dims [d/2 * h + 8 s, +8) (any order works as long as A
@@ -53,10 +55,11 @@ constexpr int kItemRows = 256;  // query rows per work item
 
 template <int DH>
 struct __attribute__((aligned(16))) OgqLds {
-  static constexpr int KROW = DH * 2 + 16;   // K / V row, padded
+  static constexpr int KROW = DH * 2 + 16;   // K row, padded
+  static constexpr int VROW = kBlk * 2 + 16;  // V^T row, padded
   static constexpr int QROW = DH * 2 + 16;   // per-wave Q / O row, padded
   __attribute__((aligned(16))) unsigned char k[kBlk * KROW];
-  __attribute__((aligned(16))) unsigned char vr[kBlk * KROW];
+  __attribute__((aligned(16))) unsigned char vt[DH * VROW];
   __attribute__((aligned(16))) unsigned char buf[kWaves][32 * QROW];
   int64_t qoff[kItemRows];   // element offset of the row's first head in q
   int64_t pidx[kItemRows];   // partial index ((s*T + t)*Hkv + g)*k + slot
@@ -78,17 +81,18 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
 }
 
 // K/V staging in two halves (global -> registers, registers -> LDS) so that a kernel
-// can fetch the next block while it computes on the current one.  Thread layout: 16-byte
-// pieces, row-major, for both.
+// can fetch the next block while it computes on the current one.  Thread layout:
+// K: 16-byte pieces, row-major; V^T: thread = (4 consecutive keys, 8 consecutive dims),
+// transposed 4x8 in registers.
 template <int DH>
 struct KVRegs {
-  static constexpr int KP = kBlk * DH / 8 / kThreads;  // pieces per thread
+  static constexpr int KP = kBlk * DH / 8 / kThreads;  // K pieces per thread
   uint4 k[KP];
-  uint4 v[KP];
+  uint4 v[4];
 };
 
 template <int DH>
-__device__ __forceinline__ void gload_rows(uint4 (&rk)[KVRegs<DH>::KP], const uint16_t* kb, int nvalid) {
+__device__ __forceinline__ void gload_k(uint4 (&rk)[KVRegs<DH>::KP], const uint16_t* kb, int nvalid) {
   constexpr int CPR = DH / 8;
 #pragma unroll
   for (int u = 0; u < KVRegs<DH>::KP; ++u) {
@@ -99,13 +103,15 @@ __device__ __forceinline__ void gload_rows(uint4 (&rk)[KVRegs<DH>::KP], const ui
 }
 
 template <int DH>
-__device__ __forceinline__ void gload_k(uint4 (&rk)[KVRegs<DH>::KP], const uint16_t* kb, int nvalid) {
-  gload_rows<DH>(rk, kb, nvalid);
-}
-
-template <int DH>
-__device__ __forceinline__ void gload_v(uint4 (&rv)[KVRegs<DH>::KP], const uint16_t* vb, int nvalid) {
-  gload_rows<DH>(rv, vb, nvalid);
+__device__ __forceinline__ void gload_v(uint4 (&rv)[4], const uint16_t* vb, int nvalid) {
+  const int kg = threadIdx.x & 31;
+  const int dc = threadIdx.x >> 5;  // 0..15
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = 4 * kg + i;
+    rv[i] = dc < DH / 8 && key < nvalid ? *reinterpret_cast<const uint4*>(vb + key * DH + dc * 8)
+                                         : make_uint4(0u, 0u, 0u, 0u);
+  }
 }
 
 template <int DH>
@@ -115,7 +121,7 @@ __device__ __forceinline__ void gload_kv(KVRegs<DH>& r, const uint16_t* kb, cons
 }
 
 template <int DH>
-__device__ __forceinline__ void lstore_rows(unsigned char* lk, const uint4 (&rk)[KVRegs<DH>::KP]) {
+__device__ __forceinline__ void lstore_k(unsigned char* lk, const uint4 (&rk)[KVRegs<DH>::KP]) {
   constexpr int CPR = DH / 8;
 #pragma unroll
   for (int u = 0; u < KVRegs<DH>::KP; ++u) {
@@ -126,26 +132,38 @@ __device__ __forceinline__ void lstore_rows(unsigned char* lk, const uint4 (&rk)
 }
 
 template <int DH>
-__device__ __forceinline__ void lstore_k(unsigned char* lk, const uint4 (&rk)[KVRegs<DH>::KP]) {
-  lstore_rows<DH>(lk, rk);
+__device__ __forceinline__ void lstore_vt(unsigned char* lvt, const uint4 (&rv)[4]) {
+  const int kg = threadIdx.x & 31;
+  const int dc = threadIdx.x >> 5;
+  // keys 4 kg .. 4 kg + 3 = k0 + 8a + 4h + {0..3} go to columns k0 + 8h + 4a + {0..3}
+  const int kc = (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1);
+  if (dc < DH / 8) {
+    const uint32_t w[4][4] = {{rv[0].x, rv[0].y, rv[0].z, rv[0].w}, {rv[1].x, rv[1].y, rv[1].z, rv[1].w},
+                              {rv[2].x, rv[2].y, rv[2].z, rv[2].w}, {rv[3].x, rv[3].y, rv[3].z, rv[3].w}};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16;
+      const uint32_t k0 = (w[0][e >> 1] >> sh) & 0xFFFFu, k1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
+      const uint32_t k2 = (w[2][e >> 1] >> sh) & 0xFFFFu, k3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
+      uint2 o;
+      o.x = k0 | (k1 << 16);
+      o.y = k2 | (k3 << 16);
+      *reinterpret_cast<uint2*>(&lvt[(dc * 8 + e) * OgqLds<DH>::VROW + kc * 8]) = o;
+    }
+  }
 }
 
 template <int DH>
-__device__ __forceinline__ void lstore_v(unsigned char* lv, const uint4 (&rv)[KVRegs<DH>::KP]) {
-  lstore_rows<DH>(lv, rv);
-}
-
-template <int DH>
-__device__ __forceinline__ void lstore_kv(unsigned char* lk, unsigned char* lv, const KVRegs<DH>& r) {
+__device__ __forceinline__ void lstore_kv(unsigned char* lk, unsigned char* lvt, const KVRegs<DH>& r) {
   lstore_k<DH>(lk, r.k);
-  lstore_v<DH>(lv, r.v);
+  lstore_vt<DH>(lvt, r.v);
 }
 
 template <int DH>
 __device__ __forceinline__ void stage_kv(OgqLds<DH>& L, const uint16_t* kb, const uint16_t* vb, int nvalid) {
   KVRegs<DH> r;
   gload_kv<DH>(r, kb, vb, nvalid);
-  lstore_kv<DH>(L.k, L.vr, r);
+  lstore_kv<DH>(L.k, L.vt, r);
 }
 
 // One wave's gathered Q rows: piece p = lane + 64 u -> M-row p / (DH/8), column p % (DH/8).
@@ -308,10 +326,10 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        const int k0 = kt * 32 + 16 * pp + 4 * h;
+        const int kb0 = (kt * 32 + 16 * pp + 8 * h) * 2;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 a = tr_operand(L.vr, OgqLds<DH>::KROW, k0, k0 + 8, 32 * dt, lane);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&L.vt[(dt * 32 + nl) * OgqLds<DH>::VROW + kb0]);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][pp], oacc[dt], 0, 0, 0);
         }
       }
@@ -376,10 +394,10 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
 // start-up latency.
 template <int DH>
 struct __attribute__((aligned(16))) HotLds {
-  static constexpr int KROW = OgqLds<DH>::KROW;
+  static constexpr int KROW = OgqLds<DH>::KROW, VROW = OgqLds<DH>::VROW;
   static constexpr int QROW = DH * 2 + 8;             // output transpose row
   static constexpr int KB = kBlk * KROW;              // K part of a buffer
-  static constexpr int BUF = 2 * KB;                  // K | V (row-major)
+  static constexpr int BUF = KB + DH * VROW;          // K | V^T
   // buf[b] holds one block; the buffer freed by an item's last block receives that
   // item's transposed outputs (8 waves x 32 rows x QROW bytes)
   __attribute__((aligned(16))) unsigned char buf[2][BUF];
@@ -488,7 +506,7 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
     const int64_t kv0 = (it.sg * D.N + (int64_t)b * kBlk) * DH;
     gload_kv<DH>(nx, k + kv0, v + kv0, min(kBlk, D.N - b * kBlk));
     lstore_k<DH>(L.buf[0], nx.k);
-    lstore_v<DH>(L.buf[0] + HotLds<DH>::KB, nx.v);
+    lstore_vt<DH>(L.buf[0] + HotLds<DH>::KB, nx.v);
   }
   __syncthreads();
   int cur = 0;
@@ -530,7 +548,7 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
       // that did not choose the block gets P = 0 through an infinite exponent offset below
       const bool need_mask = __ballot(chose && it.p < j0 + kBlk - 1) != 0ull;
       const unsigned char* lk = L.buf[cur];
-      const unsigned char* lvr = L.buf[cur] + HotLds<DH>::KB;
+      const unsigned char* lvt = L.buf[cur] + HotLds<DH>::KB;
       auto half = [&](auto hf_tag) {
         constexpr int HF = decltype(hf_tag)::value;
         f32x16 sacc[2];
@@ -594,10 +612,10 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
         for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
-            const int k0 = (2 * HF + k2) * 32 + 16 * pp + 4 * h;
+            const int kb0 = ((2 * HF + k2) * 32 + 16 * pp + 8 * h) * 2;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-              const bf16x8 a = tr_operand(lvr, HotLds<DH>::KROW, k0, k0 + 8, 32 * dt, lane);
+              const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lvt[(dt * 32 + nl) * HotLds<DH>::VROW + kb0]);
               oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[k2][pp], oacc[dt], 0, 0, 0);
             }
           }
@@ -607,7 +625,7 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
       lstore_k<DH>(L.buf[cur ^ 1], nx.k);
       gload_v<DH>(nx.v, v + kvn, nvn);
       if (any) half(std::integral_constant<int, 1>{});
-      lstore_v<DH>(L.buf[cur ^ 1] + HotLds<DH>::KB, nx.v);
+      lstore_vt<DH>(L.buf[cur ^ 1] + HotLds<DH>::KB, nx.v);
       __syncthreads();
       cur ^= 1;
     }
