@@ -131,17 +131,31 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
     for (int x = 0; x < DPL; x += 8) load8(q_idx + (sg * T + t) * DI + col * DPL + x, &qv[tq][x]);
   }
   const int bend = min(b0 + kStreamBlocks, (ns + 127) / 128);
-  for (int b = b0; b < bend; ++b) {
-    // a block's rows are contiguous (dense cache or one page); an invalid page reads as 0
+  // a block's rows are contiguous (dense cache or one page); an invalid page reads as 0.
+  // Loads run one block ahead in registers (kn) so the next block's HBM reads overlap
+  // this block's dot products and reductions; block maxima are written at the end.
+  auto gload = [&](int b, uint4 (&kr)[PASSES]) {
     const int64_t kb0 = kv_row(D, s, g, b * 128, DI);
     const TK* kbase = k_idx + (kb0 < 0 ? 0 : kb0) + col * DPL;
-    uint4 kr[PASSES];
 #pragma unroll
     for (int u = 0; u < PASSES; ++u) {
       const int jj = u * KPP + kslot;
       kr[u] = kb0 >= 0 && b * 128 + jj < ns ? *reinterpret_cast<const uint4*>(kbase + (int64_t)jj * DI)
                                             : make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+  uint4 kr[PASSES], kn[PASSES];
+  if (b0 < bend) gload(b0, kn);
+  float bm[kStreamBlocks];
+#pragma unroll
+  for (int i = 0; i < kStreamBlocks; ++i) bm[i] = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kStreamBlocks; ++i) {
+    const int b = b0 + i;
+    if (b >= bend) break;
+#pragma unroll
+    for (int u = 0; u < PASSES; ++u) kr[u] = kn[u];
+    if (b + 1 < bend) gload(b + 1, kn);
     float m[TQ];
 #pragma unroll
     for (int tq = 0; tq < TQ; ++tq) m[tq] = -INFINITY;
@@ -152,13 +166,13 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
       float kv[DPL];
       if constexpr (sizeof(TK) == 2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kv[2 * i] = __builtin_bit_cast(float, w4[i] << 16);
-          kv[2 * i + 1] = __builtin_bit_cast(float, w4[i] & 0xFFFF0000u);
+        for (int i2 = 0; i2 < 4; ++i2) {
+          kv[2 * i2] = __builtin_bit_cast(float, w4[i2] << 16);
+          kv[2 * i2 + 1] = __builtin_bit_cast(float, w4[i2] & 0xFFFF0000u);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e4m3x4(w4[i], &kv[4 * i]);
+        for (int i2 = 0; i2 < 4; ++i2) e4m3x4(w4[i2], &kv[4 * i2]);
       }
 #pragma unroll
       for (int tq = 0; tq < TQ; ++tq) {
@@ -183,12 +197,21 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
       if (lane == 0) red[wave][tq] = x;
     }
     __syncthreads();
-    if (threadIdx.x < TQ && threadIdx.x < T) {
+    if (threadIdx.x < TQ) {
       const int tq = threadIdx.x;
-      const float x = fmaxf(fmaxf(red[0][tq], red[1][tq]), fmaxf(red[2][tq], red[3][tq]));
-      if (b <= pq[tq] / 128) scores[(sg * T + tq) * (int64_t)D.nb + b] = x;
+      bm[i] = fmaxf(fmaxf(red[0][tq], red[1][tq]), fmaxf(red[2][tq], red[3][tq]));
     }
     __syncthreads();
+  }
+  if constexpr (!TOKEN) {
+    if (threadIdx.x < TQ && threadIdx.x < T) {
+      const int tq = threadIdx.x;
+#pragma unroll
+      for (int i = 0; i < kStreamBlocks; ++i) {
+        const int b = b0 + i;
+        if (b < bend && b <= pq[tq] / 128) scores[(sg * T + tq) * (int64_t)D.nb + b] = bm[i];
+      }
+    }
   }
 }
 
