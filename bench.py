@@ -375,7 +375,7 @@ def paged_decode(args, msa, wd, xd):
     msa.profiler_enable(False)
     ms = e0.elapsed_time(e1) / args.steps
     st = {}
-    for kn in ("idx_scores_stream", "block_topk_t1", "decode_items", "decode_ogq_mfma", "decode_merge"):
+    for kn in ("idx_scores_stream", "block_topk_t1", "decode_attn", "decode_merge"):
         tms, nl = msa.profiler_read(kn, reset=False)
         if nl:
             st[kn] = dict(ms=tms / nl)
@@ -615,7 +615,7 @@ def main():
     for name in ("idx_scores_mfma", "block_topk", "invert_count", "invert_scatter", "invert_offsets",
                  "scan_tile_sums", "scan_top", "scan_apply", "wl_count", "wl_emit", "ogq_mfma", "lse_merge",
                  "hot_select", "cold_count", "cold_scatter", "cold_offsets", "hot_mfma",
-                 "idx_scores_rows", "idx_scores_stream", "block_topk_t1", "decode_items", "decode_ogq_mfma",
+                 "idx_scores_rows", "idx_scores_stream", "block_topk_t1", "decode_attn",
                  "decode_simple", "decode_merge"):
         ms, n = msa.profiler_read(name, reset=False)
         if n:
@@ -678,7 +678,7 @@ def main():
         if "block_topk_t1" in kern:
             s_ = kern["block_topk_t1"]["total_ms"] / kern["block_topk_t1"]["launches"] / 1e3
             dstages["block_topk_t1"] = dict(ms=s_ * 1e3, **roofline(0.0, dm["block_topk"]["bytes"], s_))
-        for kn in ("decode_ogq_mfma", "decode_simple"):
+        for kn in ("decode_attn", "decode_simple"):
             if kn in kern:
                 s_ = kern[kn]["total_ms"] / kern[kn]["launches"] / 1e3
                 dstages[kn] = dict(ms=s_ * 1e3, **roofline(dm["attention"]["flops"], dm["attention"]["bytes"], s_))
@@ -707,7 +707,7 @@ def main():
         msa.profiler_enable(False)
         ms8 = e0.elapsed_time(e1) / args.steps
         k8 = {}
-        for kn in ("idx_scores_stream", "block_topk_t1", "decode_items", "decode_ogq_mfma", "decode_merge"):
+        for kn in ("idx_scores_stream", "block_topk_t1", "decode_attn", "decode_merge"):
             tms, nl = msa.profiler_read(kn, reset=False)
             if nl:
                 k8[kn] = dict(ms=tms / nl)

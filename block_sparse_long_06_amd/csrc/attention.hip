@@ -29,11 +29,12 @@ int ogq_mfma_rows_per_item(const Dims& D);
 hipError_t launch_ogq_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const int4* worklist, const int* n_items, int64_t grid,
                            const int32_t* entries, float* part_lse, uint16_t* part_o, hipStream_t st);
-hipError_t launch_decode_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                              const int32_t* sel, int4* wl, int32_t* ent, int* n_items, float* part_lse,
-                              uint16_t* part_o, hipStream_t st);
 hipError_t launch_hot_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const HotSplit& h,
                            float* part_lse, uint16_t* part_o, hipStream_t st);
+// decode attention, one workgroup per (row, group, slot) (decode_attn.hip)
+bool decode_attn_supported(const Dims& D);
+hipError_t launch_decode_attn(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* sel, float* part_lse, uint16_t* part_o, hipStream_t st);
 
 namespace {
 
@@ -617,15 +618,12 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
 struct DecodeWs {
   float* part_lse;
   void* part_o;
-  int4* wl;
-  int32_t* ent;
-  int* n_items;
 };
 
 static DecodeWs decode_layout(const Dims& D, void* base, size_t* total) {
   const int64_t nslot = (int64_t)D.S * D.T * D.Hkv * D.k;
   const int64_t npart = nslot * D.G;
-  const bool mfma = ogq_mfma_supported(D);
+  const bool mfma = decode_attn_supported(D);  // bf16 partials
   unsigned char* p = static_cast<unsigned char*>(base);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -636,11 +634,6 @@ static DecodeWs decode_layout(const Dims& D, void* base, size_t* total) {
   DecodeWs w{};
   w.part_lse = static_cast<float*>(take(npart * sizeof(float)));
   w.part_o = take((size_t)npart * D.d * (mfma ? 2 : 4));
-  if (mfma) {
-    w.wl = static_cast<int4*>(take(nslot * sizeof(int4)));
-    w.ent = static_cast<int32_t*>(take(nslot * sizeof(int32_t)));
-    w.n_items = static_cast<int*>(take(sizeof(int)));
-  }
   *total = off;
   return w;
 }
@@ -656,10 +649,9 @@ hipError_t launch_decode(const Dims& D, const void* q, const void* k, const void
   size_t total = 0;
   const DecodeWs w = decode_layout(D, ws, &total);
   hipError_t e;
-  if (ogq_mfma_supported(D)) {
-    e = launch_decode_mfma(D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                           static_cast<const uint16_t*>(v), sel, w.wl, w.ent, w.n_items, w.part_lse,
-                           static_cast<uint16_t*>(w.part_o), st);
+  if (decode_attn_supported(D)) {
+    e = launch_decode_attn(D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), sel, w.part_lse, static_cast<uint16_t*>(w.part_o), st);
     if (e != hipSuccess) return e;
     return launch_lse_merge(D, sel, w.part_lse, w.part_o, 1, nullptr, out, st, "decode_merge");
   }

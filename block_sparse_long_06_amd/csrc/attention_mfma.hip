@@ -197,8 +197,7 @@ __device__ __forceinline__ void put_q(unsigned char* buf, const QRegs<DH>& qr, i
   }
 }
 
-// DECODE only names a separate instantiation for the decode launches (same code).
-template <int DH, int G, bool DECODE>
+template <int DH, int G>
 __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      const uint16_t* __restrict__ v,
@@ -222,7 +221,7 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
   if (slot_in_xcd >= per_xcd || item >= n) return;
 
   const int4 w = wl[item];
-  if (w.z <= 0) return;  // empty item (decode slot with no block)
+  if (w.z <= 0) return;  // empty item
   const int64_t sg = w.x / D.nb;
   const int b = w.x % D.nb;
   const int s = (int)(sg / D.Hkv), g = (int)(sg % D.Hkv);
@@ -682,42 +681,22 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
   }
 }
 
-template <int DH, int G, bool DECODE>
+template <int DH, int G>
 void launch_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int4* wl,
               const int* n_items, int64_t grid, const int32_t* entries, float* part_lse, uint16_t* part_o,
               hipStream_t st) {
-  hipLaunchKernelGGL((ogq_mfma<DH, G, DECODE>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, wl, n_items,
+  hipLaunchKernelGGL((ogq_mfma<DH, G>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, wl, n_items,
                      entries, part_lse, part_o);
 }
 
-template <bool DECODE>
 void launch_any(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int4* wl,
                 const int* n_items, int64_t grid, const int32_t* entries, float* part_lse, uint16_t* part_o,
                 hipStream_t st) {
 #define MSA_OGQ_CASE(DH_, G_) \
-  if (D.d == DH_ && D.G == G_) return launch_t<DH_, G_, DECODE>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st)
+  if (D.d == DH_ && D.G == G_) return launch_t<DH_, G_>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st)
   MSA_OGQ_CASE(128, 8); MSA_OGQ_CASE(128, 1); MSA_OGQ_CASE(128, 2); MSA_OGQ_CASE(128, 4); MSA_OGQ_CASE(128, 16);
   MSA_OGQ_CASE(64, 8); MSA_OGQ_CASE(64, 1); MSA_OGQ_CASE(64, 2); MSA_OGQ_CASE(64, 4); MSA_OGQ_CASE(64, 16);
 #undef MSA_OGQ_CASE
-}
-
-// Decode: one work item per (sequence, query row, group, slot) holding that single row,
-// so every selected block is processed once for its query (query-centric split-K).
-__global__ void __launch_bounds__(256) decode_items(Dims D, const int32_t* __restrict__ sel, int4* __restrict__ wl,
-                                                    int32_t* __restrict__ ent, int* __restrict__ n_items) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t n = (int64_t)D.S * D.T * D.Hkv * D.k;
-  if (i == 0) *n_items = (int)n;
-  if (i >= n) return;
-  const int slot = (int)(i % D.k);
-  const int g = (int)((i / D.k) % D.Hkv);
-  const int t = (int)((i / ((int64_t)D.k * D.Hkv)) % D.T);
-  const int s = (int)(i / ((int64_t)D.k * D.Hkv * D.T));
-  const int64_t sg = (int64_t)s * D.Hkv + g;
-  const int b = sel[(sg * D.T + t) * D.k + slot];
-  const bool ok = b >= 0 && b < D.nb;
-  wl[i] = make_int4(ok ? (int)(sg * D.nb + b) : 0, (int)i, ok ? 1 : 0, 0);
-  ent[i] = t * D.k + slot;
 }
 
 template <int DH, int G>
@@ -765,23 +744,7 @@ hipError_t launch_ogq_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, 
                            float* part_lse, uint16_t* part_o, hipStream_t st) {
   const int64_t grid = (ub + 7) / 8 * 8 + 8;  // >= 8 * ceil(n_items / 8) for any n_items <= ub
   LaunchScope scope("ogq_mfma", st);
-  launch_any<false>(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_mfma(const Dims& D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                              const int32_t* sel, int4* wl, int32_t* ent, int* n_items, float* part_lse,
-                              uint16_t* part_o, hipStream_t st) {
-  const int64_t n = (int64_t)D.S * D.T * D.Hkv * D.k;
-  {
-    LaunchScope scope("decode_items", st);
-    hipLaunchKernelGGL(decode_items, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, D, sel, wl, ent, n_items);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t grid = (n + 7) / 8 * 8 + 8;
-  LaunchScope scope("decode_ogq_mfma", st);
-  launch_any<true>(D, q, k, v, wl, n_items, grid, ent, part_lse, part_o, st);
+  launch_any(D, q, k, v, wl, n_items, grid, entries, part_lse, part_o, st);
   return hipGetLastError();
 }
 
