@@ -8,8 +8,8 @@
 // At decode the items hold one row each, so the matrix-core prefill kernel (built for
 // hundreds of rows per staged block) would stage 64 KB of K/V per row through LDS with
 // eight waves and compute with one.  This kernel is sized for that shape instead: one
-// 256-thread workgroup per item, ~41 KB of LDS, so several items run per CU and their
-// block reads overlap.
+// 256-thread workgroup per item, ~39 KB of LDS, so four items run per CU and their block
+// reads overlap.
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims read straight from
 //    global memory into registers (wave w owns keys 32 w .. 32 w + 31), B = the G query
 //    heads (columns >= G are zero).  Output lane l holds keys 4 (l / 16) + {0..3} of a
@@ -20,7 +20,7 @@
 //    contiguous 16-byte runs; PV uses the key order in which S^T left P in the registers:
 //    elements 0..3 = keys 4 g + {0..3} of the chunk's first 16-key tile, 4..7 = the same
 //    of its second.
-//  * V goes to LDS with 16-byte direct global -> LDS loads, rows padded to DH * 2 + 32
+//  * V goes to LDS with 16-byte direct global -> LDS loads, rows padded to DH * 2 + 16
 //    bytes; the V^T operand of O^T = V^T P^T is read with ds_read_b64_tr_b16, two reads
 //    per operand (rows 4 g and 16 + 4 g of the chunk).  The waves split the output dims
 //    (DH / 4 each) and read the four chunks' P operands from LDS.
@@ -69,10 +69,12 @@ __global__ void __launch_bounds__(256) decode_attn(Dims D, const uint16_t* __res
                                                    const uint16_t* __restrict__ v,
                                                    const int32_t* __restrict__ sel, float* __restrict__ part_lse,
                                                    uint16_t* __restrict__ part_o) {
-  constexpr int VROW = DH * 2 + 32;            // padded V row: transposing reads conflict-free
+  // padded V row: a transposing read (16 rows x 32 bytes per 16-lane group) then hits
+  // each bank twice, the minimum for its 512 bytes
+  constexpr int VROW = DH * 2 + 16;
   constexpr int VB = kB * VROW;                // bytes of the V tile
-  constexpr int PERW = VB / 4096;              // 1 KB direct-load instructions per wave
-  static_assert(PERW * 4096 == VB, "whole direct-load instructions per wave");
+  constexpr int NINST = VB / 1024;             // 1 KB direct-load instructions (wave w: w, w + 4, ...)
+  static_assert(NINST * 1024 == VB, "whole direct-load instructions");
   constexpr int KS = DH / 32;                  // k-steps of the QK contraction
   constexpr int DTW = DH / 64;                 // 16-dim output tiles per wave
   __shared__ __attribute__((aligned(16))) unsigned char vt[VB];
@@ -106,8 +108,8 @@ __global__ void __launch_bounds__(256) decode_attn(Dims D, const uint16_t* __res
   if (kv0 >= 0) {
     typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
-    for (int u = 0; u < PERW; ++u) {
-      const int off = (wave * PERW + u) * 1024;
+    for (int u = wave; u < NINST; u += 4) {
+      const int off = u * 1024;
       const int x = off + 16 * lane;
       const int r = x / VROW, o = x % VROW;
       const int c = o < DH * 2 ? o / 16 : 0;
@@ -115,9 +117,7 @@ __global__ void __launch_bounds__(256) decode_attn(Dims D, const uint16_t* __res
       __builtin_amdgcn_global_load_lds(v + kv0 + (int64_t)rr * DH + c * 8, (lds_void*)(vt + off), 16, 0, 0);
     }
   } else {
-#pragma unroll
-    for (int u = 0; u < VB / 16 / 256; ++u)
-      reinterpret_cast<u32x4*>(vt)[threadIdx.x + 256 * u] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < VB / 16; i += 256) reinterpret_cast<u32x4*>(vt)[i] = u32x4{0u, 0u, 0u, 0u};
   }
 
   // K (A operands, straight to registers) and Q (B operands)
