@@ -127,6 +127,10 @@ DEC_CASES = [
     W.small("dec_e4m3_keys", S=3, T=1, N=5000, H=16, Hkv=2, d=128, dI=64, k=16, structure="sink_needles",
             kidx_dtype=synth.FP8),
     W.small("dec_e4m3_keys_multi_q_dI32", S=2, T=3, N=2100, H=8, Hkv=2, d=64, dI=32, k=8, kidx_dtype=synth.FP8),
+    # every head-group size the bf16 decode kernel takes (its B operand holds up to 16 heads)
+    W.small("dec_bf16_g16", S=2, T=1, N=3000, H=16, Hkv=1, d=128, dI=64, k=16),
+    W.small("dec_bf16_g1_d64_multi_q", S=3, T=2, N=2500, H=2, Hkv=2, d=64, dI=64, k=8),
+    W.small("dec_bf16_g2", S=2, T=1, N=1800, H=4, Hkv=2, d=128, dI=32, k=4),
 ]
 
 
