@@ -51,7 +51,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBlk = 128;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kItemRows = 256;  // query rows per work item
+constexpr int kItemRows = 512;  // query rows per work item
 
 template <int DH>
 struct __attribute__((aligned(16))) OgqLds {
