@@ -66,46 +66,61 @@ __global__ void __launch_bounds__(256) invert_offsets(Dims D, const int* __restr
   offsets[i] = v;
 }
 
+// KR > 0: the row's k <= KR selections are read once into registers; KR == 0: any k,
+// re-read from memory in each phase.  The chunk's per-block start positions are gathered
+// into LDS first, so ranking an entry needs no memory access.
+template <int KR>
 __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __restrict__ sel,
                                                      const int* __restrict__ pos,
                                                      int32_t* __restrict__ entries, int nchunks, int ct) {
   extern __shared__ unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
-  uint16_t* run = reinterpret_cast<uint16_t*>(smem + sizeof(unsigned long long) * D.nb);
+  int* base = reinterpret_cast<int*>(smem + sizeof(unsigned long long) * D.nb);
+  uint16_t* run = reinterpret_cast<uint16_t*>(smem + (sizeof(unsigned long long) + sizeof(int)) * D.nb);
   const int lane = threadIdx.x;
   const int c = blockIdx.x;
   const int64_t sg = blockIdx.y;
+  const int* pos_c = pos + (sg * D.nb) * nchunks + c;  // pos of (sg, b, c) = pos_c[b * nchunks]
   for (int b = lane; b < D.nb; b += 64) {
     mask[b] = 0ull;
     run[b] = 0;
+    base[b] = pos_c[(int64_t)b * nchunks];
   }
   __syncthreads();
   const int t0 = c * ct;
   const int t1 = min(t0 + ct, D.T);
   const unsigned long long lower = (1ull << lane) - 1ull;
-  const int* pos_c = pos + (sg * D.nb) * nchunks + c;  // pos of (sg, b, c) = pos_c[b * nchunks]
+  const int k = KR > 0 ? KR : D.k;
   for (int tb = t0; tb < t1; tb += 64) {
     const int t = tb + lane;
     const int32_t* srow = sel + (sg * D.T + t) * D.k;
+    int bl[KR > 0 ? KR : 1];
+    if constexpr (KR > 0) {
+#pragma unroll
+      for (int i = 0; i < KR; ++i) bl[i] = t < t1 && i < D.k ? srow[i] : -1;
+    }
+    auto blk = [&](int i) { return KR > 0 ? bl[i] : (t < t1 ? srow[i] : -1); };
     // phase 1: mark the lanes that chose each block
-    for (int i = 0; i < D.k; ++i) {
-      const int b = t < t1 ? srow[i] : -1;
+#pragma unroll
+    for (int i = 0; i < k; ++i) {
+      const int b = blk(i);
       if (b >= 0 && b < D.nb) atomicOr(&mask[b], 1ull << lane);
     }
     __syncthreads();
     // phase 2: rank among earlier lanes + running count -> global position
-    for (int i = 0; i < D.k; ++i) {
-      const int b = t < t1 ? srow[i] : -1;
+#pragma unroll
+    for (int i = 0; i < k; ++i) {
+      const int b = blk(i);
       if (b >= 0 && b < D.nb) {
         const unsigned long long m = mask[b];
-        const int p = pos_c[(int64_t)b * nchunks] + run[b] + __popcll(m & lower);
-        entries[p] = t * D.k + i;
+        entries[base[b] + run[b] + __popcll(m & lower)] = t * D.k + i;
       }
     }
     __syncthreads();
     // phase 3: the lowest lane of each block advances its count and clears its mask
-    for (int i = 0; i < D.k; ++i) {
-      const int b = t < t1 ? srow[i] : -1;
+#pragma unroll
+    for (int i = 0; i < k; ++i) {
+      const int b = blk(i);
       if (b >= 0 && b < D.nb) {
         const unsigned long long m = mask[b];
         if ((m & lower) == 0ull) {
@@ -159,13 +174,18 @@ hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, in
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    const size_t lds = (size_t)D.nb * (sizeof(unsigned long long) + sizeof(uint16_t));
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(invert_scatter),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const size_t lds = (size_t)D.nb * (sizeof(unsigned long long) + sizeof(int) + sizeof(uint16_t));
+    const void* kern = D.k <= 16 ? reinterpret_cast<const void*>(invert_scatter<16>)
+                                 : reinterpret_cast<const void*>(invert_scatter<0>);
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     LaunchScope s("invert_scatter", st);
-    hipLaunchKernelGGL(invert_scatter, dim3(nchunks, (unsigned)nsg), dim3(64), lds, st, D, sel, pos,
-                       entries, nchunks, chunk_rows(D));
+    if (D.k <= 16)
+      hipLaunchKernelGGL(invert_scatter<16>, dim3(nchunks, (unsigned)nsg), dim3(64), lds, st, D, sel, pos,
+                         entries, nchunks, chunk_rows(D));
+    else
+      hipLaunchKernelGGL(invert_scatter<0>, dim3(nchunks, (unsigned)nsg), dim3(64), lds, st, D, sel, pos,
+                         entries, nchunks, chunk_rows(D));
   }
   return hipGetLastError();
 }
