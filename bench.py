@@ -614,7 +614,7 @@ def main():
     kern = {}
     for name in ("idx_scores_mfma", "block_topk", "invert_count", "invert_scatter", "invert_offsets",
                  "scan_tile_sums", "scan_top", "scan_apply", "wl_count", "wl_emit", "ogq_mfma", "lse_merge",
-                 "hot_select", "cold_count", "cold_scatter", "cold_offsets", "hot_mfma",
+                 "hot_select", "hot_compact", "cold_count", "cold_scatter", "cold_offsets", "hot_mfma",
                  "idx_scores_rows", "idx_scores_stream", "block_topk_t1", "decode_attn",
                  "decode_simple", "decode_merge"):
         ms, n = msa.profiler_read(name, reset=False)
@@ -649,7 +649,7 @@ def main():
                              flops=model[stage]["flops"], bytes=model[stage]["bytes"], **rf)
     inv_ms = sum(kern[n]["total_ms"] for n in ("invert_count", "invert_scatter", "invert_offsets") if n in kern)
     stages["invert(all launches)"] = dict(ms=inv_ms / args.steps)
-    split_ms = sum(kern[n]["total_ms"] for n in ("hot_select", "cold_count", "cold_scatter", "cold_offsets")
+    split_ms = sum(kern[n]["total_ms"] for n in ("hot_select", "hot_compact", "cold_count", "cold_scatter", "cold_offsets")
                    if n in kern)
     stages["query_tile_split(all launches)"] = dict(ms=split_ms / args.steps)
     # a4 as a whole (both attention kernels) against the full a4 work

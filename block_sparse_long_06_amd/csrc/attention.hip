@@ -576,7 +576,7 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
   const bool hot = w.has_hot && hot_tiles_enabled() && lse_out == nullptr && mass_out == nullptr &&
                    D.kv_lens == nullptr;
   if (hot) {  // Outer-Gather-Q then takes only the cold part of the CSR
-    e = launch_hot_split(D, sel, off, entries, w.hs, st);
+    e = launch_hot_split(D, sel, w.hs, st);
     if (e != hipSuccess) return e;
     off = w.hs.cold_off;
     entries = w.hs.cold_ent;

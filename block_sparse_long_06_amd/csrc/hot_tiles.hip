@@ -20,17 +20,16 @@
 //   hotmask  uint64: bit slot set if sel[s,g,t,slot] is a hot block of the row's tile;
 //   selbits  uint32: bit i set if the row selected hot block i of its tile;
 // per (s, g, tau): hot list {count, ids...} (kHotStride ints).
-// The cold CSR keeps the entries of the caller's CSR whose slot bit is clear, in the
-// same order and the same format (flat (s, g, b) offsets, ascending rows).
+// The cold CSR -- the selection inversion of the entries whose slot bit is clear, in the
+// same format and order as the full inversion (flat (s, g, b) offsets, ascending rows) --
+// is built by the inversion kernels themselves, with hotmask as their skip mask.
 #include "msa_internal.hpp"
-#include "scan.hpp"
 
 namespace msa {
 namespace {
 
 constexpr int kHotMinRows = 32;
 constexpr int kHotMinBlocks = 2;
-constexpr int kChunk = 2048;   // CSR positions per workgroup of the compaction
 constexpr int kMaxNb = 8192;
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
@@ -137,109 +136,6 @@ __global__ void __launch_bounds__(1024) hot_compact(const int32_t* __restrict__ 
   if (threadIdx.x == 0) *count = run;
 }
 
-// ------------------------------------------------------------------ cold CSR
-// Positions [F0, total) of the flat entry array, F = csr_offsets flattened over
-// (s, g, b) with nb + 1 values per (s, g); F0 = F[0], total = F[last].
-
-// Largest sg in [lo, hi] whose list starts at or before position i.
-__device__ __forceinline__ int sg_of(const int32_t* off, int nb1, int lo, int hi, int i) {
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[(int64_t)mid * nb1] <= i) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
-__device__ __forceinline__ bool entry_cold(const Dims& D, const uint64_t* hotmask, int sg, int e) {
-  if ((unsigned)e >= (unsigned)(D.T * D.k)) return true;
-  const int t = e / D.k, slot = e - t * D.k;
-  const int s = sg / D.Hkv, g = sg - s * D.Hkv;
-  return ((hotmask[((int64_t)s * D.T + t) * D.Hkv + g] >> slot) & 1ull) == 0ull;
-}
-
-struct ChunkRange {
-  int lo, hi, sg_lo, sg_hi;
-};
-
-__device__ __forceinline__ bool chunk_range(const Dims& D, const int32_t* off, ChunkRange& c) {
-  const int nb1 = D.nb + 1, nsg = D.S * D.Hkv;
-  const int F0 = off[0];
-  const int total = off[(int64_t)nsg * nb1 - 1];
-  c.lo = F0 + (int)blockIdx.x * kChunk;
-  if (c.lo >= total) return false;
-  c.hi = min(c.lo + kChunk, total);
-  c.sg_lo = sg_of(off, nb1, 0, nsg - 1, c.lo);
-  c.sg_hi = sg_of(off, nb1, c.sg_lo, nsg - 1, c.hi - 1);
-  return true;
-}
-
-__global__ void __launch_bounds__(256) cold_count(Dims D, const int32_t* __restrict__ off,
-                                                  const int32_t* __restrict__ ent,
-                                                  const uint64_t* __restrict__ hotmask, int* __restrict__ cnt) {
-  __shared__ int wsum[4];
-  ChunkRange c;
-  int n = 0;
-  if (chunk_range(D, off, c)) {
-    for (int i = c.lo + threadIdx.x; i < c.hi; i += 256) {
-      const int sg = c.sg_lo == c.sg_hi ? c.sg_lo : sg_of(off, D.nb + 1, c.sg_lo, c.sg_hi, i);
-      n += entry_cold(D, hotmask, sg, ent[i]) ? 1 : 0;
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, 64);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = n;
-  __syncthreads();
-  if (threadIdx.x == 0) cnt[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-}
-
-// rank[i - F0] = number of cold entries before position i; cold entries are copied
-// to cold_ent[rank].
-__global__ void __launch_bounds__(256) cold_scatter(Dims D, const int32_t* __restrict__ off,
-                                                    const int32_t* __restrict__ ent,
-                                                    const uint64_t* __restrict__ hotmask,
-                                                    const int* __restrict__ base, int32_t* __restrict__ cold_ent,
-                                                    int32_t* __restrict__ rank) {
-  __shared__ int wsum[4];
-  ChunkRange c;
-  if (!chunk_range(D, off, c)) return;
-  const int F0 = off[0];
-  const int wave = threadIdx.x >> 6;
-  int run = base[blockIdx.x];
-  for (int r0 = c.lo; r0 < c.hi; r0 += 256) {
-    const int i = r0 + threadIdx.x;
-    const bool in = i < c.hi;
-    const int e = in ? ent[i] : 0;
-    bool cold = false;
-    if (in) {
-      const int sg = c.sg_lo == c.sg_hi ? c.sg_lo : sg_of(off, D.nb + 1, c.sg_lo, c.sg_hi, i);
-      cold = entry_cold(D, hotmask, sg, e);
-    }
-    const uint64_t m = __ballot(cold);
-    if ((threadIdx.x & 63) == 0) wsum[wave] = __popcll(m);
-    __syncthreads();
-    int before = run;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const int rk = before + lanes_below(m);
-    if (in) rank[i - F0] = rk;
-    if (cold) cold_ent[rk] = e;
-    run += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-  }
-}
-
-__global__ void __launch_bounds__(256) cold_offsets(Dims D, const int32_t* __restrict__ off,
-                                                    const int32_t* __restrict__ rank,
-                                                    const int* __restrict__ n_cold, int32_t* __restrict__ cold_off) {
-  const int64_t nflat = (int64_t)D.S * D.Hkv * (D.nb + 1);
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= nflat) return;
-  const int F0 = off[0];
-  const int total = off[nflat - 1];
-  const int p = off[x];
-  cold_off[x] = p >= total ? *n_cold : rank[p - F0];
-}
-
 }  // namespace
 
 int hot_num_tiles(const Dims& D) { return (D.N - 1) / kHotTile - D.pos0 / kHotTile + 1; }
@@ -247,7 +143,6 @@ int hot_num_tiles(const Dims& D) { return (D.N - 1) / kHotTile - D.pos0 / kHotTi
 HotSplit hot_split_layout(const Dims& D, void* base, size_t* total) {
   const int64_t rows = (int64_t)D.S * D.T * D.Hkv;
   const int64_t npart = rows * D.k;
-  const int64_t nchunk = (npart + kChunk - 1) / kChunk;
   const int64_t nflat = (int64_t)D.S * D.Hkv * (D.nb + 1);
   unsigned char* p = static_cast<unsigned char*>(base);
   size_t off = 0;
@@ -258,7 +153,6 @@ HotSplit hot_split_layout(const Dims& D, void* base, size_t* total) {
   };
   HotSplit h{};
   h.ntiles = hot_num_tiles(D);
-  h.nchunk = nchunk;
   h.hot = static_cast<int32_t*>(take((size_t)D.S * D.Hkv * h.ntiles * kHotStride * sizeof(int32_t)));
   h.tiles = static_cast<int32_t*>(take((size_t)D.S * D.Hkv * h.ntiles * sizeof(int32_t)));
   h.ntile = static_cast<int*>(take(sizeof(int)));
@@ -266,17 +160,12 @@ HotSplit hot_split_layout(const Dims& D, void* base, size_t* total) {
   h.selbits = static_cast<uint32_t*>(take(rows * sizeof(uint32_t)));
   h.cold_off = static_cast<int32_t*>(take(nflat * sizeof(int32_t)));
   h.cold_ent = static_cast<int32_t*>(take(npart * sizeof(int32_t)));
-  h.rank = static_cast<int32_t*>(take(npart * sizeof(int32_t)));
-  h.chunk_cnt = static_cast<int*>(take(nchunk * sizeof(int)));
-  h.chunk_base = static_cast<int*>(take(nchunk * sizeof(int)));
-  h.n_cold = static_cast<int*>(take(sizeof(int)));
-  h.scan_ws = take(scan_workspace_bytes(nchunk));
+  h.inv_ws = take(invert_workspace_bytes(D));
   *total = off;
   return h;
 }
 
-hipError_t launch_hot_split(const Dims& D, const int32_t* sel, const int32_t* off, const int32_t* ent,
-                            const HotSplit& h, hipStream_t st) {
+hipError_t launch_hot_split(const Dims& D, const int32_t* sel, const HotSplit& h, hipStream_t st) {
   if (D.nb > kMaxNb) return hipErrorInvalidValue;
   {
     LaunchScope s("hot_select", st);
@@ -292,28 +181,8 @@ hipError_t launch_hot_split(const Dims& D, const int32_t* sel, const int32_t* of
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  {
-    LaunchScope s("cold_count", st);
-    hipLaunchKernelGGL(cold_count, dim3((unsigned)h.nchunk), dim3(256), 0, st, D, off, ent, h.hotmask, h.chunk_cnt);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = launch_exclusive_scan(h.chunk_cnt, h.chunk_base, h.nchunk, h.n_cold, h.scan_ws, st);
-  if (e != hipSuccess) return e;
-  {
-    LaunchScope s("cold_scatter", st);
-    hipLaunchKernelGGL(cold_scatter, dim3((unsigned)h.nchunk), dim3(256), 0, st, D, off, ent, h.hotmask,
-                       h.chunk_base, h.cold_ent, h.rank);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t nflat = (int64_t)D.S * D.Hkv * (D.nb + 1);
-  {
-    LaunchScope s("cold_offsets", st);
-    hipLaunchKernelGGL(cold_offsets, dim3((unsigned)((nflat + 255) / 256)), dim3(256), 0, st, D, off, h.rank,
-                       h.n_cold, h.cold_off);
-  }
-  return hipGetLastError();
+  // the cold lists: the inversion of the selections with the tile-shared slots left out
+  return launch_invert(D, sel, h.cold_off, h.cold_ent, h.inv_ws, st, h.hotmask);
 }
 
 }  // namespace msa

@@ -31,7 +31,16 @@ int chunk_rows(const Dims& D) {
   return c;
 }
 
+// An entry whose slot bit is set in its row's mask (hotmask [S, T, Hkv], nullable) is left
+// out: the same inversion then builds the list of the remaining entries only.
+__device__ __forceinline__ uint64_t row_skip(const Dims& D, const uint64_t* hotmask, int64_t sg, int t) {
+  if (hotmask == nullptr) return 0ull;
+  const int64_t s = sg / D.Hkv, g = sg % D.Hkv;
+  return hotmask[(s * D.T + t) * D.Hkv + g];
+}
+
 __global__ void __launch_bounds__(256) invert_count(Dims D, const int32_t* __restrict__ sel,
+                                                    const uint64_t* __restrict__ hotmask,
                                                     int* __restrict__ cnt, int nchunks, int ct) {
   extern __shared__ int hist[];
   const int c = blockIdx.x;
@@ -44,7 +53,10 @@ __global__ void __launch_bounds__(256) invert_count(Dims D, const int32_t* __res
   const int64_t e1 = (sg * D.T + t1) * D.k;
   for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
     const int b = sel[e];
-    if (b >= 0 && b < D.nb) atomicAdd(&hist[b], 1);
+    const int64_t r = e / D.k;  // sg * T + t
+    const int slot = (int)(e - r * D.k);
+    const bool skip = (row_skip(D, hotmask, sg, (int)(r - sg * D.T)) >> slot) & 1ull;
+    if (b >= 0 && b < D.nb && !skip) atomicAdd(&hist[b], 1);
   }
   __syncthreads();
   for (int b = threadIdx.x; b < D.nb; b += 256) cnt[(sg * D.nb + b) * nchunks + c] = hist[b];
@@ -71,6 +83,7 @@ __global__ void __launch_bounds__(256) invert_offsets(Dims D, const int* __restr
 // into LDS first, so ranking an entry needs no memory access.
 template <int KR>
 __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __restrict__ sel,
+                                                     const uint64_t* __restrict__ hotmask,
                                                      const int* __restrict__ pos,
                                                      int32_t* __restrict__ entries, int nchunks, int ct) {
   extern __shared__ unsigned char smem[];
@@ -94,12 +107,13 @@ __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __re
   for (int tb = t0; tb < t1; tb += 64) {
     const int t = tb + lane;
     const int32_t* srow = sel + (sg * D.T + t) * D.k;
+    const uint64_t skip = t < t1 ? row_skip(D, hotmask, sg, t) : 0ull;
     int bl[KR > 0 ? KR : 1];
     if constexpr (KR > 0) {
 #pragma unroll
-      for (int i = 0; i < KR; ++i) bl[i] = t < t1 && i < D.k ? srow[i] : -1;
+      for (int i = 0; i < KR; ++i) bl[i] = t < t1 && i < D.k && !((skip >> i) & 1ull) ? srow[i] : -1;
     }
-    auto blk = [&](int i) { return KR > 0 ? bl[i] : (t < t1 ? srow[i] : -1); };
+    auto blk = [&](int i) { return KR > 0 ? bl[i] : (t < t1 && !((skip >> i) & 1ull) ? srow[i] : -1); };
     // phase 1: mark the lanes that chose each block
 #pragma unroll
     for (int i = 0; i < k; ++i) {
@@ -143,8 +157,9 @@ size_t invert_workspace_bytes(const Dims& D) {
          scan_workspace_bytes(m);
 }
 
+// With a skip mask the kernels are timed under the cold_* names (the tile split's lists).
 hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, int32_t* entries,
-                         void* ws, hipStream_t st) {
+                         void* ws, hipStream_t st, const uint64_t* hotmask) {
   const int nchunks = invert_chunks(D);
   const int64_t nsg = (int64_t)D.S * D.Hkv;
   const int64_t m = nsg * D.nb * nchunks;
@@ -157,9 +172,9 @@ hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, in
   w += align_up(sizeof(int), 256);
   void* scan_ws = w;
   {
-    LaunchScope s("invert_count", st);
+    LaunchScope s(hotmask ? "cold_count" : "invert_count", st);
     hipLaunchKernelGGL(invert_count, dim3(nchunks, (unsigned)nsg), dim3(256), D.nb * sizeof(int), st, D,
-                       sel, cnt, nchunks, chunk_rows(D));
+                       sel, hotmask, cnt, nchunks, chunk_rows(D));
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -167,7 +182,7 @@ hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, in
   if (e != hipSuccess) return e;
   {
     const int64_t n = nsg * (D.nb + 1);
-    LaunchScope s("invert_offsets", st);
+    LaunchScope s(hotmask ? "cold_offsets" : "invert_offsets", st);
     hipLaunchKernelGGL(invert_offsets, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, D, pos, total,
                        offsets, nchunks);
   }
@@ -179,13 +194,13 @@ hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, in
                                  : reinterpret_cast<const void*>(invert_scatter<0>);
     e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    LaunchScope s("invert_scatter", st);
+    LaunchScope s(hotmask ? "cold_scatter" : "invert_scatter", st);
     if (D.k <= 16)
-      hipLaunchKernelGGL(invert_scatter<16>, dim3(nchunks, (unsigned)nsg), dim3(64), lds, st, D, sel, pos,
-                         entries, nchunks, chunk_rows(D));
+      hipLaunchKernelGGL(invert_scatter<16>, dim3(nchunks, (unsigned)nsg), dim3(64), lds, st, D, sel, hotmask,
+                         pos, entries, nchunks, chunk_rows(D));
     else
-      hipLaunchKernelGGL(invert_scatter<0>, dim3(nchunks, (unsigned)nsg), dim3(64), lds, st, D, sel, pos,
-                         entries, nchunks, chunk_rows(D));
+      hipLaunchKernelGGL(invert_scatter<0>, dim3(nchunks, (unsigned)nsg), dim3(64), lds, st, D, sel, hotmask,
+                         pos, entries, nchunks, chunk_rows(D));
   }
   return hipGetLastError();
 }

@@ -42,7 +42,8 @@ hipError_t launch_block_topk(const Dims& D, const float* scores, int32_t* sel, h
 
 size_t invert_workspace_bytes(const Dims& D);
 hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, int32_t* entries,
-                         void* ws, hipStream_t st);
+                         void* ws, hipStream_t st,
+                         const uint64_t* hotmask = nullptr);
 
 size_t prefill_workspace_bytes(const Dims& D);
 // lse_out [S, T, H] and mass_out [S, Hkv, T, k] (both optional) are the training outputs.
@@ -108,7 +109,6 @@ constexpr int kHotMax = 32;              // hot blocks kept per (sequence, group
 constexpr int kHotStride = kHotMax + 1;  // {count, ids...} per (sequence, group, tile)
 struct HotSplit {
   int ntiles;
-  int64_t nchunk;
   int32_t* hot;         // [S*Hkv, ntiles, kHotStride]
   int32_t* tiles;       // (s*Hkv + g)*ntiles + tile of every tile with shared blocks, in order
   int* ntile;           // their number
@@ -116,16 +116,11 @@ struct HotSplit {
   uint32_t* selbits;    // [S, T, Hkv]
   int32_t* cold_off;    // [S, Hkv, nb + 1]
   int32_t* cold_ent;    // [S*T*Hkv*k] capacity
-  int32_t* rank;        // [S*T*Hkv*k]
-  int* chunk_cnt;
-  int* chunk_base;
-  int* n_cold;
-  void* scan_ws;
+  void* inv_ws;         // workspace of the inversion that builds the cold lists
 };
 int hot_num_tiles(const Dims& D);
 HotSplit hot_split_layout(const Dims& D, void* base, size_t* total);
-hipError_t launch_hot_split(const Dims& D, const int32_t* sel, const int32_t* off, const int32_t* ent,
-                            const HotSplit& h, hipStream_t st);
+hipError_t launch_hot_split(const Dims& D, const int32_t* sel, const HotSplit& h, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
