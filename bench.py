@@ -545,7 +545,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MSA path shards by KV-head group and sequence with no "
-              "exchange inside MSA, and this build runs on a single MI355X only (--gpus %d refused)." % args.gpus,
+              "exchange inside MSA; this library runs on one MI355X (--gpus %d is not supported)." % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
