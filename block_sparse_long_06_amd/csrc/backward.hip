@@ -41,7 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kBlk = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRows = 1024;  // query rows per work item
+constexpr int kRows = 512;  // query rows per work item
 
 __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   const f32x2 x = {a, b};
