@@ -21,6 +21,8 @@
 
 #include <stdlib.h>
 
+#include <mutex>
+
 namespace msa {
 
 // matrix-core Outer-Gather-Q kernel (attention_mfma.hip)
@@ -451,6 +453,45 @@ bool hot_tiles_enabled() {
   return !(e != nullptr && e[0] == '0');
 }
 
+bool tile_overlap_enabled() {
+  const char* e = getenv("MSA_TILE_OVERLAP");
+  return !(e != nullptr && e[0] == '0');
+}
+
+// A second stream per device (default priority) for the query-tile kernel, with the two
+// events that fork it from and join it to the caller's stream.  The tile kernel keeps one
+// persistent workgroup per CU with a static share of tiles; launched first on its own
+// stream, the Outer-Gather-Q workgroups queued behind it on the caller's stream take each
+// CU as its tile workgroup retires, so neither kernel waits for the other's slowest CU.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;  // held from the fork record to the join wait: the events are shared
+SideStream g_side[kMaxDevices];
+
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& x = g_side[dev];
+  if (x.s == nullptr) {
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    x.s = s;
+    x.fork = f;
+    x.join = j;
+  }
+  *out = &x;
+  return hipSuccess;
+}
+
 template <typename T, typename PT, int DH>
 hipError_t launch_ogq_simple_t(const Dims& D, const void* q, const void* k, const void* v,
                                const PrefillWs& w, const int32_t* entries, hipStream_t st) {
@@ -575,11 +616,35 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
   // (nor with per-sequence lengths: the tile pass maps tiles through one position offset)
   const bool hot = w.has_hot && hot_tiles_enabled() && lse_out == nullptr && mass_out == nullptr &&
                    D.kv_lens == nullptr;
+  const bool overlap = hot && tile_overlap_enabled();
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  // on an early error return the caller's stream still waits for the tile kernel
+  struct Join {
+    hipStream_t st;
+    SideStream* side;
+    ~Join() {
+      if (side != nullptr) (void)hipStreamWaitEvent(st, side->join, 0);
+    }
+  } join{st, nullptr};
   if (hot) {  // Outer-Gather-Q then takes only the cold part of the CSR
     e = launch_hot_split(D, sel, w.hs, st);
     if (e != hipSuccess) return e;
     off = w.hs.cold_off;
     entries = w.hs.cold_ent;
+  }
+  if (overlap) {  // the tile kernel first, on the side stream, once the split is done
+    side_lock.lock();
+    e = side_stream(&side);
+    if (e == hipSuccess) e = hipEventRecord(side->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e == hipSuccess)
+      e = launch_hot_mfma(D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), w.hs, w.part_lse, static_cast<uint16_t*>(w.part_o),
+                          side->s);
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
+    if (e != hipSuccess) return e;
+    join.side = side;
   }
   {
     LaunchScope s("wl_count", st);
@@ -603,12 +668,15 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
     e = D.d == 64 ? launch_ogq_simple_t<float, float, 64>(D, q, k, v, w, entries, st)
                   : launch_ogq_simple_t<float, float, 128>(D, q, k, v, w, entries, st);
   }
-  if (e != hipSuccess) return e;
-  if (hot) {
+  if (overlap) {  // the merge reads both kernels' partials
+    join.side = nullptr;
+    e = hipStreamWaitEvent(st, side->join, 0);
+    side_lock.unlock();
+  } else if (hot) {
     e = launch_hot_mfma(D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                         static_cast<const uint16_t*>(v), w.hs, w.part_lse, static_cast<uint16_t*>(w.part_o), st);
-    if (e != hipSuccess) return e;
   }
+  if (e != hipSuccess) return e;
   return launch_lse_merge(D, sel, w.part_lse, w.part_o, D.dtype == MSA_BF16, hot ? w.hs.hotmask : nullptr, out,
                           st, "lse_merge", lse_out, mass_out);
 }

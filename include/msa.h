@@ -162,7 +162,11 @@ msa_status msa_invert_selection(const msa_problem* prob, const int32_t* sel,
  *   row keeps one partial over all such blocks -- and only the remaining (row, block)
  *   entries of the CSR take the Outer-Gather-Q kernel.  The result is the same exact attention.  Setting the
  *   environment variable MSA_HOT_TILES=0 (read at each call) sends every entry through
- *   the Outer-Gather-Q kernel.
+ *   the Outer-Gather-Q kernel.  The tile-wise kernel runs on a second stream the library
+ *   creates once per device (default priority), forked from `stream` by an event after
+ *   the split and joined back into it by an event before the merge, so all work is still
+ *   ordered on `stream` when the call returns; MSA_TILE_OVERLAP=0 keeps it on `stream`.
+ *   Calls on several host threads take turns between that fork and join.
  *   workspace: msa_workspace_bytes(prob, MSA_CALL_PREFILL) bytes (partials, work list,
  *   query-tile split).
  */

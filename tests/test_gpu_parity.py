@@ -120,6 +120,23 @@ def test_prefill_without_query_tiles(wl, monkeypatch):
     check_out(f64(on.out), f64(off.out), wl.dtype, what="query tiles on vs off")
 
 
+
+@pytest.mark.parametrize("wl", QT_OFF_CASES[:2], ids=[c.name for c in QT_OFF_CASES[:2]])
+def test_tile_kernel_on_its_own_stream_changes_no_bit(wl, monkeypatch):
+    """The query-tile kernel runs on a second stream beside Outer-Gather-Q by default
+    (MSA_TILE_OVERLAP=0 puts it back on the caller's stream after it).  The two write
+    disjoint partials, so the outputs are bit-identical, and both match the oracle."""
+    require_gpu()
+    say("case", wl.name, "(tile kernel overlap on / off)")
+    inputs = gen(wl)
+    _, on = full_prefill(wl, inputs)
+    monkeypatch.setenv("MSA_TILE_OVERLAP", "0")
+    _, off = full_prefill(wl, inputs)
+    monkeypatch.delenv("MSA_TILE_OVERLAP")
+    _verify_prefill(wl, inputs, on)
+    assert torch.equal(on.out.view(torch.uint8), off.out.view(torch.uint8))
+
+
 DEC_CASES = [
     W.small("dec_bf16", S=3, T=1, N=5000, H=16, Hkv=2, d=128, dI=64, k=16, structure="sink_needles"),
     W.small("dec_fp32", S=2, T=1, N=3333, H=8, Hkv=2, d=64, dI=32, k=4, dtype=synth.F32),
