@@ -633,7 +633,7 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
     off = w.hs.cold_off;
     entries = w.hs.cold_ent;
   }
-  if (overlap) {  // the tile kernel first, on the side stream, once the split is done
+  if (overlap) {  // the tile kernel first, on the side stream, once its tile lists are done
     side_lock.lock();
     e = side_stream(&side);
     if (e == hipSuccess) e = hipEventRecord(side->fork, st);
@@ -645,6 +645,10 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
     if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
     if (e != hipSuccess) return e;
     join.side = side;
+  }
+  if (hot) {  // the cold lists: the inversion of the selections without the tile-shared slots
+    e = launch_invert(D, sel, w.hs.cold_off, w.hs.cold_ent, w.hs.inv_ws, st, w.hs.hotmask);
+    if (e != hipSuccess) return e;
   }
   {
     LaunchScope s("wl_count", st);

@@ -22,7 +22,8 @@
 // per (s, g, tau): hot list {count, ids...} (kHotStride ints).
 // The cold CSR -- the selection inversion of the entries whose slot bit is clear, in the
 // same format and order as the full inversion (flat (s, g, b) offsets, ascending rows) --
-// is built by the inversion kernels themselves, with hotmask as their skip mask.
+// is built afterwards by the inversion kernels themselves, with hotmask as their skip mask
+// (the tile kernel needs only the outputs above, so it can start before that).
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -179,10 +180,7 @@ hipError_t launch_hot_split(const Dims& D, const int32_t* sel, const HotSplit& h
     hipLaunchKernelGGL(hot_compact, dim3(1), dim3(1024), 0, st, h.hot, (int64_t)D.S * D.Hkv * h.ntiles, h.tiles,
                        h.ntile);
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // the cold lists: the inversion of the selections with the tile-shared slots left out
-  return launch_invert(D, sel, h.cold_off, h.cold_ent, h.inv_ws, st, h.hotmask);
+  return hipGetLastError();
 }
 
 }  // namespace msa
