@@ -263,7 +263,7 @@ def cpu_baseline(wl, inputs, seconds_budget=12.0):
             sc = oracle.slice_index_scores(qI[g], pos_all[rows], kI[g], 128)
             sel = oracle.slice_block_topk(sc, pos_all[rows] // 128, wl.k)
             oracle.slice_invert(sel, wl.nb)
-            oracle.slice_attention(q[:, g * G:(g + 1) * G], pos_all[rows], sel, K[g], V[g], 128, 1 / np.sqrt(wl.d))
+            oracle.slice_attention(q[:, g * G:(g + 1) * G], pos_all[rows], sel, K[g], V[g], 128, wl.scale)
         spent += time.perf_counter() - t0
         done_rows += len(rows)
     return dict(value=done_rows / spent, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",

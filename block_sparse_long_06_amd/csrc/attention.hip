@@ -1,7 +1,7 @@
 // attention.hip -- a4/a5/a6: the main branch.  Exact softmax attention restricted to
 // the selected blocks (page "MSA 稀疏注意力三国杀：NSA / DSA / MoBA / MSA 四方案深度对比",
 // section 第二步：精算; MSA entry of "稀疏注意力速览（Sparse Attention，2019 ~ 2026）":
-// "Main Branch 只在这些块上做精确 softmax attention"), organised in the
+// the main branch attends exactly, with softmax, to the chosen blocks only), organised in the
 // Outer-Gather-Q order of section Kernel 创新：Outer Gather Q for prefill (the KV block
 // is the outer loop, staged on chip once for every query row that chose it) and
 // query-centric split-K for decode (one workgroup per (query row, selected block)).
@@ -672,6 +672,9 @@ hipError_t launch_prefill(const Dims& D, const void* q, const void* k, const voi
     e = D.d == 64 ? launch_ogq_simple_t<float, float, 64>(D, q, k, v, w, entries, st)
                   : launch_ogq_simple_t<float, float, 128>(D, q, k, v, w, entries, st);
   }
+  // a failed Outer-Gather-Q launch is reported as it is (the Join still makes the
+  // caller's stream wait for the tile kernel, with the side-stream lock held)
+  if (e != hipSuccess) return e;
   if (overlap) {  // the merge reads both kernels' partials
     join.side = nullptr;
     e = hipStreamWaitEvent(st, side->join, 0);

@@ -522,7 +522,9 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
       nb_first = hot[(int64_t)ntl * kHotStride + 1];
     }
 
-    float m = -3.0e38f;  // running reference max of the raw scores (finite start)
+    // running reference max in exp2 units (raw score times sc); a finite start keeps
+    // (ms - mn) finite, and no product with sc can overflow it whatever the scale
+    float ms = -3.0e38f;
     float l = 0.0f;
     f32x16 oacc[DT];
 #pragma unroll
@@ -578,10 +580,11 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[k2][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         if (!chose) mx = -INFINITY;
-        if (__ballot(mx * sc > m * sc + kLazy) != 0ull) {
-          const float mn = fmaxf(m, mx);
-          const float alpha = __builtin_amdgcn_exp2f((m - mn) * sc);
-          m = mn;
+        const float mxs = mx * sc;  // -inf for a row that did not choose the block
+        if (__ballot(mxs > ms + kLazy) != 0ull) {
+          const float mn = fmaxf(ms, mxs);
+          const float alpha = __builtin_amdgcn_exp2f(ms - mn);
+          ms = mn;
           l *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
@@ -590,7 +593,7 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
         }
         // exponent offset; +inf for a row that did not choose the block: fma(s, sc, -inf) is
         // -inf for every finite or -inf score, so its P is exactly 0
-        const float msc = chose ? m * sc : INFINITY;
+        const float msc = chose ? ms : INFINITY;
         bf16x8 pf[2][2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
@@ -651,7 +654,7 @@ __global__ void __launch_bounds__(kThreads) hot_mfma(Dims D, const uint16_t* __r
         *reinterpret_cast<uint2*>(orow + (dt * 32 + 8 * qd) * 2) = o;
       }
     }
-    if (h == 0) L.lse[wave][nl] = (m * sc + __builtin_amdgcn_logf(l)) * kLn2;
+    if (h == 0) L.lse[wave][nl] = (ms + __builtin_amdgcn_logf(l)) * kLn2;
     wave_lds_sync();
 #pragma unroll
     for (int u = 0; u < QRegs<DH>::PIECES; ++u) {

@@ -39,6 +39,50 @@ __device__ __forceinline__ uint64_t row_skip(const Dims& D, const uint64_t* hotm
   return hotmask[(s * D.T + t) * D.Hkv + g];
 }
 
+// Rows hold distinct block ids (msa_block_topk's rows do).  A repeated id is outside
+// that contract; its later slots are dropped here, by the count and the scatter alike,
+// so that every list position the count reserves is written.
+template <int KR>
+__device__ __forceinline__ void row_blocks(const Dims& D, const int32_t* srow, uint64_t skip, bool ok,
+                                           int (&bl)[KR]) {
+  if (KR % 4 == 0 && (D.k & 3) == 0 && (reinterpret_cast<uintptr_t>(srow) & 15) == 0) {
+    // 16-byte loads: the row starts 16-byte aligned and holds whole groups of four
+#pragma unroll
+    for (int i = 0; i < KR / 4; ++i) {
+      const int4 v = ok && 4 * i < D.k ? reinterpret_cast<const int4*>(srow)[i] : make_int4(-1, -1, -1, -1);
+      bl[4 * i] = v.x;
+      bl[4 * i + 1] = v.y;
+      bl[4 * i + 2] = v.z;
+      bl[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KR; ++i) bl[i] = ok && i < D.k ? srow[i] : -1;
+  }
+#pragma unroll
+  for (int i = 1; i < KR; ++i) {
+    bool rep = false;
+#pragma unroll
+    for (int j = 0; j < i; ++j) rep |= bl[j] == bl[i];
+    if (rep) bl[i] = -1;
+  }
+#pragma unroll
+  for (int i = 0; i < KR; ++i)
+    if ((skip >> i) & 1ull) bl[i] = -1;
+}
+
+// Slot i of a row held in memory (any k): its block, or -1 if skipped, out of range or
+// a repeat of an earlier slot.
+__device__ __forceinline__ int row_block_at(const Dims& D, const int32_t* srow, uint64_t skip, int i) {
+  const int b = srow[i];
+  if (b < 0 || b >= D.nb) return -1;
+  for (int j = 0; j < i; ++j)
+    if (srow[j] == b) return -1;
+  return ((skip >> i) & 1ull) ? -1 : b;
+}
+
+// One thread per query row of the chunk.
+template <int KR>
 __global__ void __launch_bounds__(256) invert_count(Dims D, const int32_t* __restrict__ sel,
                                                     const uint64_t* __restrict__ hotmask,
                                                     int* __restrict__ cnt, int nchunks, int ct) {
@@ -49,14 +93,21 @@ __global__ void __launch_bounds__(256) invert_count(Dims D, const int32_t* __res
   __syncthreads();
   const int t0 = c * ct;
   const int t1 = min(t0 + ct, D.T);
-  const int64_t e0 = (sg * D.T + t0) * D.k;
-  const int64_t e1 = (sg * D.T + t1) * D.k;
-  for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
-    const int b = sel[e];
-    const int64_t r = e / D.k;  // sg * T + t
-    const int slot = (int)(e - r * D.k);
-    const bool skip = (row_skip(D, hotmask, sg, (int)(r - sg * D.T)) >> slot) & 1ull;
-    if (b >= 0 && b < D.nb && !skip) atomicAdd(&hist[b], 1);
+  for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
+    const int32_t* srow = sel + (sg * D.T + t) * D.k;
+    const uint64_t skip = row_skip(D, hotmask, sg, t);
+    if constexpr (KR > 0) {
+      int bl[KR];
+      row_blocks<KR>(D, srow, skip, true, bl);
+#pragma unroll
+      for (int i = 0; i < KR; ++i)
+        if (bl[i] >= 0 && bl[i] < D.nb) atomicAdd(&hist[bl[i]], 1);
+    } else {
+      for (int i = 0; i < D.k; ++i) {
+        const int b = row_block_at(D, srow, skip, i);
+        if (b >= 0) atomicAdd(&hist[b], 1);
+      }
+    }
   }
   __syncthreads();
   for (int b = threadIdx.x; b < D.nb; b += 256) cnt[(sg * D.nb + b) * nchunks + c] = hist[b];
@@ -103,38 +154,36 @@ __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __re
   const int t0 = c * ct;
   const int t1 = min(t0 + ct, D.T);
   const unsigned long long lower = (1ull << lane) - 1ull;
-  const int k = KR > 0 ? KR : D.k;
   for (int tb = t0; tb < t1; tb += 64) {
     const int t = tb + lane;
     const int32_t* srow = sel + (sg * D.T + t) * D.k;
     const uint64_t skip = t < t1 ? row_skip(D, hotmask, sg, t) : 0ull;
     int bl[KR > 0 ? KR : 1];
-    if constexpr (KR > 0) {
+    if constexpr (KR > 0) row_blocks<KR>(D, srow, skip, t < t1, bl);
+    // f(slot, block) over the row's slots (block -1 where nothing is listed)
+    auto for_slots = [&](auto f) {
+      if constexpr (KR > 0) {
 #pragma unroll
-      for (int i = 0; i < KR; ++i) bl[i] = t < t1 && i < D.k && !((skip >> i) & 1ull) ? srow[i] : -1;
-    }
-    auto blk = [&](int i) { return KR > 0 ? bl[i] : (t < t1 && !((skip >> i) & 1ull) ? srow[i] : -1); };
+        for (int i = 0; i < KR; ++i) f(i, bl[i]);
+      } else {
+        for (int i = 0; i < D.k; ++i) f(i, t < t1 ? row_block_at(D, srow, skip, i) : -1);
+      }
+    };
     // phase 1: mark the lanes that chose each block
-#pragma unroll
-    for (int i = 0; i < k; ++i) {
-      const int b = blk(i);
+    for_slots([&](int, int b) {
       if (b >= 0 && b < D.nb) atomicOr(&mask[b], 1ull << lane);
-    }
+    });
     __syncthreads();
     // phase 2: rank among earlier lanes + running count -> global position
-#pragma unroll
-    for (int i = 0; i < k; ++i) {
-      const int b = blk(i);
+    for_slots([&](int i, int b) {
       if (b >= 0 && b < D.nb) {
         const unsigned long long m = mask[b];
         entries[base[b] + run[b] + __popcll(m & lower)] = t * D.k + i;
       }
-    }
+    });
     __syncthreads();
     // phase 3: the lowest lane of each block advances its count and clears its mask
-#pragma unroll
-    for (int i = 0; i < k; ++i) {
-      const int b = blk(i);
+    for_slots([&](int, int b) {
       if (b >= 0 && b < D.nb) {
         const unsigned long long m = mask[b];
         if ((m & lower) == 0ull) {
@@ -142,7 +191,7 @@ __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __re
           mask[b] = 0ull;
         }
       }
-    }
+    });
     __syncthreads();
   }
 }
@@ -173,8 +222,12 @@ hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, in
   void* scan_ws = w;
   {
     LaunchScope s(hotmask ? "cold_count" : "invert_count", st);
-    hipLaunchKernelGGL(invert_count, dim3(nchunks, (unsigned)nsg), dim3(256), D.nb * sizeof(int), st, D,
-                       sel, hotmask, cnt, nchunks, chunk_rows(D));
+    if (D.k <= 16)
+      hipLaunchKernelGGL(invert_count<16>, dim3(nchunks, (unsigned)nsg), dim3(256), D.nb * sizeof(int), st, D,
+                         sel, hotmask, cnt, nchunks, chunk_rows(D));
+    else
+      hipLaunchKernelGGL(invert_count<0>, dim3(nchunks, (unsigned)nsg), dim3(256), D.nb * sizeof(int), st, D,
+                         sel, hotmask, cnt, nchunks, chunk_rows(D));
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

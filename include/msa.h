@@ -24,7 +24,12 @@
  *     touched; msa_last_error_message() describes the failure (thread-local).
  *     Launch failures report MSA_ERR_DEVICE.  Asynchronous device faults surface
  *     at the caller's next synchronisation.
- *   - Calls are stateless and thread-safe (apart from the opt-in profiler).
+ *   - Calls keep no state between them, with two exceptions.  The bf16 prefill
+ *     call creates, on its first use per device, one extra stream (default priority)
+ *     and two events that it keeps until the process ends; a process-wide lock
+ *     serialises its use of them, so prefill calls from several host threads take
+ *     turns for that part of the call (see msa_sparse_attn_prefill).  The opt-in
+ *     profiler below is global state.  Calls are otherwise thread-safe.
  *
  * Shapes (S = batch, T = queries per sequence, N = kv length, H = query heads,
  * Hkv = KV heads = GQA groups, G = H / Hkv, d = head dim, dI = index dim,
@@ -140,6 +145,11 @@ msa_status msa_index_topk(const msa_problem* prob, const void* q_idx, const void
  *     query row t whose sel[s,g,t,slot] == b, in ascending t.  Deterministic.
  *   workspace: msa_workspace_bytes(prob, MSA_CALL_INVERT) bytes of device memory.
  *   Requires S * Hkv * T * k < 2^31.  Entries of sel outside [0, nb) count as -1.
+ *   Each row of sel must hold distinct block ids (msa_block_topk's rows do).  A row
+ *   that repeats an id is outside the contract: the id is listed once, for its first
+ *   slot, and the later slots are treated as -1 (so every position up to
+ *   csr_offsets[S-1, Hkv-1, nb] is written); msa_sparse_attn_prefill's output for such
+ *   a row is then unspecified.
  */
 msa_status msa_invert_selection(const msa_problem* prob, const int32_t* sel,
                                 int32_t* csr_offsets, int32_t* csr_entries, void* workspace,
@@ -147,8 +157,8 @@ msa_status msa_invert_selection(const msa_problem* prob, const int32_t* sel,
 
 /*
  * a4 + a5. Prefill main branch in Outer-Gather-Q order plus the log-sum-exp merge
- *     ([P1] 第二步：精算 and Kernel 创新：Outer Gather Q; [P3] MSA entry "Main Branch
- *     只在这些块上做精确 softmax attention").
+ *     ([P1] 第二步：精算 and Kernel 创新：Outer Gather Q; [P3] MSA entry: the main branch
+ *     attends exactly, with softmax, to those blocks only).
  *   For every (s, g, b) the K/V block is staged on chip once and every query row of
  *   its csr list (all G heads of the group) is processed against it, giving a
  *   per-(row, slot, head) partial (lse, O).  A second kernel merges the partials:

@@ -39,7 +39,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* [P1 第一步：粗筛 items 1-2; P3 MSA entry "先算 token 分数，再在块内 max-pool"]
+/* [P1 第一步：粗筛 items 1-2; P3 MSA entry: token scores first, then a max-pool inside each block]
  * out[r*nb + b] = max over keys j in block b with j <= pos[r] of
  *                 sum_c qI[r*dI + c] * kI[j*dI + c],          for b <= pos[r]/B;
  * out[r*nb + b] = NaN for b > pos[r]/B (such blocks are not eligible). */
@@ -69,9 +69,10 @@ void orc_index_scores(int64_t N, int B, int dI, int64_t nrows,
     }
 }
 
-/* [P1 第一步：粗筛 item 3 ("当前位置所在的块必选，其余按得分高低挑") and the closing
+/* [P1 第一步：粗筛 item 3 (the block of the current position is always taken, the others by score) and the closing
  *  rule of the head-pattern appendix (only the own block is forced);
- *  P3 MSA entry ("每个 GQA group 独立 Top-k 选块，并强制保留当前 token 所在 local block")]
+ *  P3 MSA entry (each GQA group runs its own top-k over blocks and always keeps the local block of the
+ *  current token)]
  * Row r: start from {own[r]}; repeatedly add the not-yet-chosen block b < own[r]
  * with the largest score, ties to the smaller b, until min(k, own[r]+1) blocks
  * are chosen.  Emit ascending, pad with -1.  scores is [nrows, nb]. */
@@ -114,7 +115,7 @@ void orc_block_topk(int64_t nb, int k, int64_t nrows, const double *scores,
     }
 }
 
-/* [P1 Kernel 创新：Outer Gather Q: "把所有选中了这块的 query 聚集到一起"]
+/* [P1 Kernel 创新：Outer Gather Q: for each block, collect every query that chose it]
  * Inverse of one slice's selection: for every block b, the list of entries
  * t*k + slot (ascending t) of query rows t whose selection holds b at `slot`.
  * offsets has nb+1 entries (offsets[0] = 0); entries has room for T*k ints.
@@ -139,8 +140,8 @@ void orc_invert(int64_t T, int k, int64_t nb, const int32_t *sel,
     free(cursor);
 }
 
-/* [P1 第二步：精算: full attention only over the chosen blocks; P3 MSA entry "Main
- *  Branch 只在这些块上做精确 softmax attention"; P5 standard formula
+/* [P1 第二步：精算: full attention only over the chosen blocks; P3 MSA entry: the main
+ *  branch computes exact softmax attention on those blocks only; P5 standard formula
  *  softmax(QK^T/sqrt(d_k))V]
  * For row r and each of the G query heads of this group:
  *   J = union over valid sel[r][i] of [b*B, (b+1)*B) intersected with [0, pos[r]];
@@ -277,8 +278,8 @@ void orc_lse_merge(int d, int G, int k, int64_t nrows, const double *lse,
 /* ------------------------------------------------------------------ training
  * [P1 索引分支训练：KL 对齐: the index branch learns from the main branch's attention
  *  distribution through a KL divergence, and the training signal updates only the index
- *  branch (the teacher is cut from the gradient); P3 MSA entry "KL loss 让 index 分布对齐
- *  Main Branch 概率（teacher stop-gradient）"]
+ *  branch (the teacher is cut from the gradient); P3 MSA entry: a KL loss
+ *  pulls the index distribution toward the main branch probabilities, teacher stop-gradient]
  * Readings where the pages are silent (also in the design notes):
  *   - teacher of row r = the main branch's attention mass on each selected block,
  *     averaged over the G heads of the group (L1-normalised over the selection);

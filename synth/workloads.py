@@ -51,6 +51,7 @@ class Workload:
     description: str = ""
     extra: dict = field(default_factory=dict)
     kidx_dtype: int = None           # storage of the index keys (None: dtype; FP8 = E4M3)
+    softmax_scale: float = 0.0       # main-branch logit scale of the problem (0: 1 / sqrt(d))
 
     @property
     def seed(self) -> int:
@@ -65,13 +66,18 @@ class Workload:
         return self.H // self.Hkv
 
     @property
+    def scale(self) -> float:
+        """The logit scale the problem resolves to (the library's rule: 0 means 1 / sqrt(d))."""
+        return float(np.float32(self.softmax_scale)) if self.softmax_scale > 0 else 1.0 / np.sqrt(self.d)
+
+    @property
     def kdtype(self) -> int:
         return self.dtype if self.kidx_dtype is None else self.kidx_dtype
 
     def problem(self):
         import block_sparse_long_06_amd as msa
         return msa.problem(self.S, self.T, self.N, self.H, self.Hkv, self.d, self.dI, self.k,
-                           dtype=self.dtype,
+                           dtype=self.dtype, softmax_scale=self.softmax_scale,
                            index_key_dtype=msa.MSA_FP8_E4M3 if self.kdtype == FP8 else 0)
 
     # ------------------------------------------------------------ tensor recipes
@@ -147,7 +153,8 @@ C3_FP8 = Workload("C3_bf16_decode_16x1M_e4m3_index_keys", 3, S=16, T=1, N=104857
                   description="bf16 MSA decode, 16 sequences x 1,048,576-token KV cache, index keys in FP8 E4M3")
 
 
-def small(name, S, T, N, H, Hkv, d, dI, k, dtype=BF16, structure="iid", index=100, kidx_dtype=None) -> Workload:
+def small(name, S, T, N, H, Hkv, d, dI, k, dtype=BF16, structure="iid", index=100, kidx_dtype=None,
+          softmax_scale=0.0) -> Workload:
     """A reduced workload with the same recipes (for parity tests that span ragged tiles)."""
     return Workload(name, index, S=S, T=T, N=N, H=H, Hkv=Hkv, d=d, dI=dI, k=k, dtype=dtype, structure=structure,
-                    kidx_dtype=kidx_dtype)
+                    kidx_dtype=kidx_dtype, softmax_scale=softmax_scale)

@@ -71,3 +71,34 @@ def full_prefill(wl, inputs, bufs=None):
     msa.run_prefill(prob, inputs["q"], inputs["k"], inputs["v"], inputs["q_idx"], inputs["k_idx"], bufs)
     torch.cuda.synchronize()
     return prob, bufs
+
+
+def verify_prefill(wl, inputs, bufs):
+    """Every stage of one prefill pass against the oracle: scores, selection on the GPU's
+    scores (bit-exact), inversion (bit-exact) and attention on the GPU's selection."""
+    S, T, N, Hkv, G, nb, k = wl.S, wl.T, wl.N, wl.Hkv, wl.G, wl.nb, wl.k
+    pos = oracle.positions(N, T)
+    qI, kI = f64(inputs["q_idx"]), f64(inputs["k_idx"])
+    q, K, V = f64(inputs["q"]), f64(inputs["k"]), f64(inputs["v"])
+    sc = bufs.scores.cpu().numpy()
+    sel = bufs.sel.cpu().numpy()
+    off = bufs.csr_offsets.cpu().numpy()
+    ent = bufs.csr_entries.cpu().numpy()
+    out = f64(bufs.out)
+    scale = wl.scale
+    differ = 0
+    for s in range(S):
+        for g in range(Hkv):
+            ref_sc = oracle.slice_index_scores(qI[s, g], pos, kI[s, g], 128)
+            check_scores(sc[s, g], ref_sc, pos, what="s%d g%d" % (s, g))
+            ref_sel = oracle.slice_block_topk(sc[s, g], pos // 128, k)
+            np.testing.assert_array_equal(sel[s, g], ref_sel)
+            differ += int(np.sum(np.any(oracle.slice_block_topk(ref_sc, pos // 128, k) != sel[s, g], axis=1)))
+            r_off, r_ent = oracle.slice_invert(sel[s, g], nb)
+            base = off[s, g, 0]
+            np.testing.assert_array_equal(off[s, g] - base, r_off)
+            np.testing.assert_array_equal(ent[base:base + r_off[-1]], r_ent)
+            ref = oracle.slice_attention(q[s][:, g * G:(g + 1) * G], pos, sel[s, g], K[s, g], V[s, g], 128, scale)
+            check_out(out[s][:, g * G:(g + 1) * G], ref, wl.dtype, what="s%d g%d" % (s, g))
+    say("  rows whose independent oracle selection differs: %d of %d" % (differ, S * Hkv * T))
+    assert off[-1, -1, -1] == np.sum(sel >= 0)

@@ -81,7 +81,7 @@ def _sampled_rows_check(wl, inputs, sc_gpu, sel_gpu, out_gpu, rows, score_rows=N
             K = f64(inputs["k"][s, g])
             V = f64(inputs["v"][s, g])
             q = f64(inputs["q"][s][torch.from_numpy(rows).cuda()][:, g * G:(g + 1) * G])
-            ref = oracle.slice_attention(q, pos_all[rows], sel_gpu[s, g][rows], K, V, 128, 1 / np.sqrt(wl.d))
+            ref = oracle.slice_attention(q, pos_all[rows], sel_gpu[s, g][rows], K, V, 128, wl.scale)
             check_out(out_gpu[s][rows][:, g * G:(g + 1) * G], ref, wl.dtype, what="s%d g%d" % (s, g))
             del K, V
 
@@ -154,7 +154,7 @@ def test_c3_decode_16x1m():
                 Kh[b * 128:(b + 1) * 128] = f64(inputs["k"][s, g, b * 128:(b + 1) * 128])
                 Vh[b * 128:(b + 1) * 128] = f64(inputs["v"][s, g, b * 128:(b + 1) * 128])
             q = f64(inputs["q"][s][:, g * G:(g + 1) * G])
-            ref = oracle.slice_attention(q, pos, sel[s, g], Kh, Vh, 128, 1 / np.sqrt(wl.d))
+            ref = oracle.slice_attention(q, pos, sel[s, g], Kh, Vh, 128, wl.scale)
             check_out(out[s][:, g * G:(g + 1) * G], ref, wl.dtype, what="s%d g%d" % (s, g))
             for b in blocks:  # re-poison: the oracle must never see another pair's blocks
                 Kh[b * 128:(b + 1) * 128] = np.nan

@@ -93,7 +93,7 @@ def _verify(wl, inputs, lens, db, what):
             check_scores(sc[s, g][:, :nbs], ref_sc, pos, what="%s s%d g%d len %d" % (what, s, g, n))
             np.testing.assert_array_equal(sel[s, g], oracle.slice_block_topk(sc[s, g][:, :nbs], pos // B, wl.k))
             ref = oracle.slice_attention(q[s][:, g * G:(g + 1) * G], pos, sel[s, g], K[s, g, :n], V[s, g, :n], B,
-                                         1.0 / np.sqrt(wl.d))
+                                         wl.scale)
             check_out(out[s][:, g * G:(g + 1) * G], ref, wl.dtype, what="%s s%d g%d" % (what, s, g))
 
 

@@ -17,7 +17,7 @@ import block_sparse_long_06_amd as msa
 import oracle
 import synth
 from synth import workloads as W
-from tests.gpu_util import check_out, check_scores, f64, full_prefill, gen, require_gpu, say
+from tests.gpu_util import check_out, check_scores, f64, full_prefill, gen, require_gpu, say, verify_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -41,42 +41,13 @@ CASES = [
 ]
 
 
-def _verify_prefill(wl, inputs, bufs):
-    S, T, N, Hkv, G, nb, k = wl.S, wl.T, wl.N, wl.Hkv, wl.G, wl.nb, wl.k
-    pos = oracle.positions(N, T)
-    qI, kI = f64(inputs["q_idx"]), f64(inputs["k_idx"])
-    q, K, V = f64(inputs["q"]), f64(inputs["k"]), f64(inputs["v"])
-    sc = bufs.scores.cpu().numpy()
-    sel = bufs.sel.cpu().numpy()
-    off = bufs.csr_offsets.cpu().numpy()
-    ent = bufs.csr_entries.cpu().numpy()
-    out = f64(bufs.out)
-    scale = 1.0 / np.sqrt(wl.d)
-    differ = 0
-    for s in range(S):
-        for g in range(Hkv):
-            ref_sc = oracle.slice_index_scores(qI[s, g], pos, kI[s, g], 128)
-            check_scores(sc[s, g], ref_sc, pos, what="s%d g%d" % (s, g))
-            ref_sel = oracle.slice_block_topk(sc[s, g], pos // 128, k)
-            np.testing.assert_array_equal(sel[s, g], ref_sel)
-            differ += int(np.sum(np.any(oracle.slice_block_topk(ref_sc, pos // 128, k) != sel[s, g], axis=1)))
-            r_off, r_ent = oracle.slice_invert(sel[s, g], nb)
-            base = off[s, g, 0]
-            np.testing.assert_array_equal(off[s, g] - base, r_off)
-            np.testing.assert_array_equal(ent[base:base + r_off[-1]], r_ent)
-            ref = oracle.slice_attention(q[s][:, g * G:(g + 1) * G], pos, sel[s, g], K[s, g], V[s, g], 128, scale)
-            check_out(out[s][:, g * G:(g + 1) * G], ref, wl.dtype, what="s%d g%d" % (s, g))
-    say("  rows whose independent oracle selection differs: %d of %d" % (differ, S * Hkv * T))
-    assert off[-1, -1, -1] == np.sum(sel >= 0)
-
-
 @pytest.mark.parametrize("wl", CASES, ids=[c.name for c in CASES])
 def test_prefill_pipeline_matches_oracle(wl):
     require_gpu()
     say("case", wl.name)
     inputs = gen(wl)
     _, bufs = full_prefill(wl, inputs)
-    _verify_prefill(wl, inputs, bufs)
+    verify_prefill(wl, inputs, bufs)
 
 
 # 1-byte index keys (OCP E4M3; the serving variant): matrix-core indexer (T >= 256),
@@ -97,7 +68,7 @@ def test_prefill_with_e4m3_index_keys(wl):
     inputs = gen(wl)
     assert inputs["k_idx"].dtype == torch.float8_e4m3fn
     _, bufs = full_prefill(wl, inputs)
-    _verify_prefill(wl, inputs, bufs)
+    verify_prefill(wl, inputs, bufs)
 
 
 QT_OFF_CASES = [c for c in CASES if c.name in ("bf16_g8_ragged_chunk", "bf16_structured",
@@ -116,7 +87,7 @@ def test_prefill_without_query_tiles(wl, monkeypatch):
     monkeypatch.setenv("MSA_HOT_TILES", "0")
     _, off = full_prefill(wl, inputs)
     monkeypatch.delenv("MSA_HOT_TILES")
-    _verify_prefill(wl, inputs, off)
+    verify_prefill(wl, inputs, off)
     check_out(f64(on.out), f64(off.out), wl.dtype, what="query tiles on vs off")
 
 
@@ -133,7 +104,7 @@ def test_tile_kernel_on_its_own_stream_changes_no_bit(wl, monkeypatch):
     monkeypatch.setenv("MSA_TILE_OVERLAP", "0")
     _, off = full_prefill(wl, inputs)
     monkeypatch.delenv("MSA_TILE_OVERLAP")
-    _verify_prefill(wl, inputs, on)
+    verify_prefill(wl, inputs, on)
     assert torch.equal(on.out.view(torch.uint8), off.out.view(torch.uint8))
 
 
@@ -174,7 +145,7 @@ def test_decode_matches_oracle_and_prefill(wl):
             check_scores(sc[s, g], ref_sc, pos, what="s%d g%d" % (s, g))
             np.testing.assert_array_equal(sel[s, g], oracle.slice_block_topk(sc[s, g], pos // 128, wl.k))
             ref = oracle.slice_attention(q[s][:, g * G:(g + 1) * G], pos, sel[s, g], K[s, g], V[s, g], 128,
-                                         1.0 / np.sqrt(wl.d))
+                                         wl.scale)
             check_out(out[s][:, g * G:(g + 1) * G], ref, wl.dtype, what="decode s%d g%d" % (s, g))
     # the prefill path on the same problem agrees with the decode path
     np.testing.assert_array_equal(pb.sel.cpu().numpy(), sel)
@@ -198,12 +169,19 @@ def test_runs_are_bit_identical():
 
 
 def test_nan_poison_unselected_blocks():
-    """Blocks no query selected are filled with NaN: outputs stay finite and identical."""
+    """Blocks no query selected are filled with NaN: the prefill and decode outputs stay finite
+    and bit-identical to those of the unpoisoned run."""
     require_gpu()
     wl = W.small("poison", S=1, T=32, N=8192, H=16, Hkv=2, d=128, dI=64, k=2)
     inputs = gen(wl)
     prob, bufs = full_prefill(wl, inputs)
     ref_out = bufs.out.clone()
+    # decode of the same rows before the poisoning (its selection is the prefill's)
+    db = msa.alloc_decode(prob)
+    msa.run_decode(prob, inputs["q"], inputs["k"], inputs["v"], inputs["q_idx"], inputs["k_idx"], db)
+    torch.cuda.synchronize()
+    assert torch.equal(db.sel, bufs.sel)
+    ref_dec = db.out.clone()
     sel = bufs.sel.cpu().numpy()
     K, V = inputs["k"], inputs["v"]
     poisoned = 0
@@ -222,11 +200,12 @@ def test_nan_poison_unselected_blocks():
     torch.cuda.synchronize()
     assert torch.isfinite(bufs.out.float()).all()
     assert torch.equal(bufs.out, ref_out)
-    # decode reads only its selected blocks as well
-    db = msa.alloc_decode(prob)
+    # decode reads only its selected blocks as well: finite and bit-identical
+    db.out.fill_(0)
     msa.run_decode(prob, inputs["q"], K, V, inputs["q_idx"], inputs["k_idx"], db)
     torch.cuda.synchronize()
     assert torch.isfinite(db.out.float()).all()
+    assert torch.equal(db.out, ref_dec)
 
 
 # ------------------------------------------------------------------ adversarial top-k
@@ -291,6 +270,48 @@ def test_invert_skewed_selection():
     r_off, r_ent = oracle.slice_invert(sel_np, nb)
     np.testing.assert_array_equal(off.cpu().numpy()[0, 0], r_off)
     np.testing.assert_array_equal(ent.cpu().numpy()[: r_off[-1]], r_ent)
+
+
+def dedup_rows(sel):
+    """sel with every repeat of a block id after its first slot in the row set to -1 (the
+    inversion's documented handling of rows outside the distinct-ids contract)."""
+    out = sel.copy()
+    for r in range(out.shape[0]):
+        seen = set()
+        for i in range(out.shape[1]):
+            b = int(out[r, i])
+            if b in seen:
+                out[r, i] = -1
+            elif b >= 0:
+                seen.add(b)
+    return out
+
+
+@pytest.mark.parametrize("k", [4, 16, 24])
+def test_invert_rows_with_repeated_ids(k):
+    """Rows that repeat a block id (outside the contract: msa_block_topk never does) list it
+    once, at its first slot; every list position is written (no stale entry for a prefill
+    to read as a row index)."""
+    require_gpu()
+    T, N = 1500, 1500 * 3
+    nb = (N + 127) // 128
+    rng = np.random.default_rng(1234 + k)
+    sel_np = rng.integers(-1, nb, size=(T, k)).astype(np.int32)
+    sel_np[:, 1] = sel_np[:, 0]                      # a repeat in every row
+    sel_np[::7, -1] = sel_np[::7, 0]                  # and one at the far end
+    sel_np[::5] = rng.integers(0, 3, size=(len(sel_np[::5]), k))  # heavy repeats
+    prob = msa.problem(1, T, N, 8, 1, 128, 64, k)
+    sel = torch.from_numpy(sel_np).cuda().reshape(1, 1, T, k).contiguous()
+    off = torch.empty((1, 1, nb + 1), dtype=torch.int32, device="cuda")
+    ent = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty((msa.workspace_bytes(prob, msa.MSA_CALL_INVERT),), dtype=torch.uint8, device="cuda")
+    msa.invert_selection(prob, sel, off, ent, ws, ws.numel())
+    torch.cuda.synchronize()
+    r_off, r_ent = oracle.slice_invert(dedup_rows(sel_np), nb)
+    got = ent.cpu().numpy()
+    np.testing.assert_array_equal(off.cpu().numpy()[0, 0], r_off)
+    np.testing.assert_array_equal(got[: r_off[-1]], r_ent)
+    assert np.all(got[: r_off[-1]] >= 0)
 
 
 def test_generator_device_matches_host():

@@ -48,7 +48,7 @@ def test_token_decode_matches_the_oracle(wl, budget):
             gpu_rows = np.where(causal, sc[s, g], np.nan)
             np.testing.assert_array_equal(sel[s, g], oracle.slice_token_topk(gpu_rows, pos, budget))
             ref_o = oracle.slice_token_attention(q[s][:, g * G:(g + 1) * G], pos, sel[s, g], K[s, g], V[s, g],
-                                                 1.0 / np.sqrt(wl.d))
+                                                 wl.scale)
             check_out(out[s][:, g * G:(g + 1) * G], ref_o, wl.dtype, what="token s%d g%d" % (s, g))
 
 

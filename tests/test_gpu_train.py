@@ -36,6 +36,19 @@ CASES = [
     (W.small("train_bf16_structured", S=1, T=1024, N=1024, H=8, Hkv=1, d=128, dI=64, k=8,
              structure="band_sink_needles"), 0.05),
     (W.small("train_bf16_g16_dI128", S=1, T=300, N=900, H=16, Hkv=1, d=128, dI=128, k=4), 0.1),
+    # the remaining (d, G) instantiations of the attention backward the ABI accepts
+    (W.small("train_bf16_d128_g1", S=1, T=520, N=700, H=2, Hkv=2, d=128, dI=64, k=4), 0.0),
+    (W.small("train_bf16_d128_g2", S=1, T=520, N=700, H=4, Hkv=2, d=128, dI=64, k=4), 0.0),
+    (W.small("train_bf16_d128_g4", S=1, T=520, N=700, H=8, Hkv=2, d=128, dI=64, k=4), 0.0),
+    (W.small("train_bf16_d64_g1", S=1, T=520, N=700, H=2, Hkv=2, d=64, dI=64, k=4), 0.0),
+    (W.small("train_bf16_d64_g2", S=1, T=520, N=700, H=4, Hkv=2, d=64, dI=64, k=4), 0.0),
+    (W.small("train_bf16_d64_g8", S=1, T=520, N=700, H=16, Hkv=2, d=64, dI=64, k=4), 0.0),
+    (W.small("train_bf16_d64_g16", S=1, T=520, N=700, H=16, Hkv=1, d=64, dI=64, k=4), 0.0),
+    # a logit scale far from 1/sqrt(d) (forward, lse and backward all take it)
+    (W.small("train_bf16_scale1_d128_g8", S=1, T=400, N=640, H=16, Hkv=2, d=128, dI=64, k=4,
+             softmax_scale=1.0), 0.0),
+    (W.small("train_bf16_scale1_d64_g2", S=1, T=400, N=640, H=4, Hkv=2, d=64, dI=32, k=4,
+             softmax_scale=1.0), 0.0),
 ]
 
 
@@ -62,7 +75,7 @@ def test_training_step_matches_the_oracle(wl, sigma):
                        sigma=sigma)
     torch.cuda.synchronize()
     sig = sigma if sigma > 0 else 1.0 / np.sqrt(wl.dI)
-    scale = 1.0 / np.sqrt(wl.d)
+    scale = wl.scale
     G = wl.G
     pos = oracle.positions(wl.N, wl.T)
     q, K, V, gO = f64(inputs["q"]), f64(inputs["k"]), f64(inputs["v"]), f64(dout)
