@@ -85,12 +85,13 @@ def attention_reduction_ratio(G, d, dI, N, budget=2048):
 
 
 def percentiles(samples):
-    """p50 / p95 (ms) of per-launch or per-step times."""
+    """p50 / p95 / p99 (ms) of per-launch or per-step times."""
     import numpy as np
     if not samples:
         return {}
     a = np.asarray(samples, dtype=np.float64)
-    return dict(p50_ms=float(np.percentile(a, 50)), p95_ms=float(np.percentile(a, 95)))
+    return dict(p50_ms=float(np.percentile(a, 50)), p95_ms=float(np.percentile(a, 95)),
+                p99_ms=float(np.percentile(a, 99)))
 
 
 def roofline(flops, nbytes, seconds):
@@ -237,8 +238,10 @@ def achievable_peaks():
 
 def cpu_baseline(wl, inputs, seconds_budget=12.0):
     """The oracle, as is, on a bounded sample of query rows of the same workload:
-    index scores, top-k, inversion and attention for R rows x all groups.
-    Returns tokens/s (= rows / oracle seconds) and the thread count it used."""
+    index scores, top-k, inversion and attention for R rows x all groups, each stage
+    timed on its own.  Returns tokens/s (= rows / oracle seconds), the thread count it
+    used, and per stage the seconds spent, the time per row and the time the whole
+    workload (T rows) would take at that rate."""
     import torch
     import oracle
     pos_all = positions(wl.N, wl.T)
@@ -249,26 +252,75 @@ def cpu_baseline(wl, inputs, seconds_budget=12.0):
     V = [oracle.decode(inputs["v"][0, g]) for g in range(wl.Hkv)]
     rows_all = wl.sampled_rows(8192)
     done_rows = 0
-    spent = 0.0
+    spent = dict(index_scores=0.0, block_topk=0.0, invert=0.0, attention=0.0)
     batch = 16
     i = 0
-    while spent < seconds_budget and i < len(rows_all):
+    while sum(spent.values()) < seconds_budget and i < len(rows_all):
         rows = rows_all[i:i + batch]
         i += batch
         idx = torch.from_numpy(rows).cuda()
         qI = [oracle.decode(inputs["q_idx"][0, g][idx]) for g in range(wl.Hkv)]
         q = oracle.decode(inputs["q"][0][idx])
-        t0 = time.perf_counter()
         for g in range(wl.Hkv):
+            t0 = time.perf_counter()
             sc = oracle.slice_index_scores(qI[g], pos_all[rows], kI[g], 128)
+            t1 = time.perf_counter()
             sel = oracle.slice_block_topk(sc, pos_all[rows] // 128, wl.k)
+            t2 = time.perf_counter()
             oracle.slice_invert(sel, wl.nb)
+            t3 = time.perf_counter()
             oracle.slice_attention(q[:, g * G:(g + 1) * G], pos_all[rows], sel, K[g], V[g], 128, wl.scale)
-        spent += time.perf_counter() - t0
+            t4 = time.perf_counter()
+            spent["index_scores"] += t1 - t0
+            spent["block_topk"] += t2 - t1
+            spent["invert"] += t3 - t2
+            spent["attention"] += t4 - t3
         done_rows += len(rows)
-    return dict(value=done_rows / spent, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+    total = sum(spent.values())
+    stages = {n: dict(s=v, ms_per_row=1e3 * v / done_rows, full_workload_s_extrapolated=v / done_rows * wl.T)
+              for n, v in spent.items()}
+    return dict(value=done_rows / total, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
                 sample="%d seeded query rows x %d groups of the %s workload (full index scan, top-k, "
-                       "inversion, attention per row), %.1f s of CPU work" % (done_rows, wl.Hkv, wl.name, spent))
+                       "inversion, attention per row), %.1f s of CPU work" % (done_rows, wl.Hkv, wl.name, total),
+                stages=stages)
+
+
+def cpu_decode_baseline(wd, inputs, pairs=3):
+    """The oracle, as is, on `pairs` seeded (sequence, group) rows of the decode step:
+    index scores over the whole cache, top-k and attention over the selected blocks.  One
+    decode row is one oracle row (its loops run over rows), so this runs on one thread.
+    Reported per stage, and as the decode step's time at that rate (16 x 8 rows)."""
+    import oracle
+    rng = np.random.default_rng(wd.seed + 7)
+    picks = sorted(set((int(rng.integers(wd.S)), int(rng.integers(wd.Hkv))) for _ in range(4 * pairs)))[:pairs]
+    pos = positions(wd.N, wd.T)
+    G = wd.G
+    spent = dict(index_scores=0.0, block_topk=0.0, attention=0.0)
+    for s_, g in picks:
+        kI = oracle.decode(inputs["k_idx"][s_, g])
+        K, V = oracle.decode(inputs["k"][s_, g]), oracle.decode(inputs["v"][s_, g])
+        qI = oracle.decode(inputs["q_idx"][s_, g])
+        q = oracle.decode(inputs["q"][s_])[:, g * G:(g + 1) * G]
+        t0 = time.perf_counter()
+        sc = oracle.slice_index_scores(qI, pos, kI, 128)
+        t1 = time.perf_counter()
+        sel = oracle.slice_block_topk(sc, pos // 128, wd.k)
+        t2 = time.perf_counter()
+        oracle.slice_attention(q, pos, sel, K, V, 128, wd.scale)
+        t3 = time.perf_counter()
+        spent["index_scores"] += t1 - t0
+        spent["block_topk"] += t2 - t1
+        spent["attention"] += t3 - t2
+        del kI, K, V
+    n = len(picks)
+    rows_per_step = wd.S * wd.Hkv * wd.T
+    per_row = sum(spent.values()) / n
+    return dict(value=per_row * rows_per_step * 1e6, unit="us per decode step (extrapolated)", cores=1,
+                kind="oracle",
+                sample="%d seeded (sequence, group) rows of the %s workload (index scan of %d keys, top-k, "
+                       "attention), %.1f s of CPU work; the step has %d such rows"
+                       % (n, wd.name, wd.N, sum(spent.values()), rows_per_step),
+                stages={k: dict(s=v, ms_per_row=1e3 * v / n) for k, v in spent.items()})
 
 
 def selection_structure(wl, sel, csr_offsets):
@@ -524,6 +576,95 @@ def train_step(args, msa, wl):
                 ms_per_step=ms, tokens_per_s=wl.T / (ms / 1e3), stages=st)
 
 
+PREFILL_TIMER_NAMES = ("idx_scores_mfma", "idx_scores_rows", "block_topk", "invert_count", "invert_scatter",
+                       "invert_offsets", "scan_tile_sums", "scan_top", "scan_apply", "wl_count", "wl_emit", "ogq_mfma",
+                       "ogq_simple", "lse_merge", "hot_select", "hot_compact", "cold_count", "cold_scatter",
+                       "cold_offsets", "hot_mfma")
+
+
+def read_timer(msa, names):
+    """Per-kernel totals, launch counts and per-launch samples of the library timer."""
+    kern = {}
+    for name in names:
+        ms, n = msa.profiler_read(name, reset=False)
+        if n:
+            kern[name] = dict(total_ms=ms, launches=n, samples=msa.profiler_samples(name))
+    return kern
+
+
+def prefill_stage_report(wp, pb, kern, steps):
+    """Per-stage device times and rooflines of the prefill passes recorded in `kern`
+    (steps passes of wp whose last selection is in pb), priced by the algorithmic model."""
+    import torch
+    # algorithmic work of the prefill pass, with the blocks actually touched
+    counts = pb.csr_offsets[..., 1:] - pb.csr_offsets[..., :-1]
+    touched = int((counts > 0).sum())
+    model = prefill_model(wp.S, wp.T, wp.N, wp.H, wp.Hkv, wp.d, wp.dI, wp.k, touched_blocks=touched)
+    if os.environ.get("MSA_HOT_TILES", "1").startswith("0"):
+        hot_flag = torch.zeros_like(pb.sel, dtype=torch.bool)
+        keep = torch.zeros((1, 1, 1), dtype=torch.bool, device=pb.sel.device)
+    else:
+        hot_flag, keep = query_tile_split(wp, pb.sel)
+    split = attention_split_model(wp, pb.sel, hot_flag, keep)
+    model.update({kk: split[kk] for kk in ("hot_mfma", "ogq_mfma", "lse_merge")})
+    stages = {}
+    for kname, stage in PREFILL_KERNELS.items():
+        if kname not in kern:
+            continue
+        per_launch_s = kern[kname]["total_ms"] / kern[kname]["launches"] / 1e3
+        rf = roofline(model[stage]["flops"], model[stage]["bytes"], per_launch_s)
+        stages[kname] = dict(ms=per_launch_s * 1e3, **percentiles(kern[kname]["samples"]),
+                             flops=model[stage]["flops"], bytes=model[stage]["bytes"], **rf)
+    inv_ms = sum(kern[n]["total_ms"] for n in ("invert_count", "invert_scatter", "invert_offsets") if n in kern)
+    stages["invert(all launches)"] = dict(ms=inv_ms / steps, **roofline(0.0, model["invert"]["bytes"], inv_ms / steps / 1e3))
+    split_ms = sum(kern[n]["total_ms"] for n in ("hot_select", "hot_compact", "cold_count", "cold_scatter", "cold_offsets")
+                   if n in kern)
+    stages["query_tile_split(all launches)"] = dict(ms=split_ms / steps)
+    # a4 as a whole (both attention kernels) against the full a4 work
+    a4_ms = sum(kern[n]["total_ms"] for n in ("ogq_mfma", "hot_mfma") if n in kern) / steps
+    if a4_ms > 0:
+        stages["a4_attention(ogq_mfma+hot_mfma)"] = dict(
+            ms=a4_ms, flops=model["ogq_attention"]["flops"], bytes=model["ogq_attention"]["bytes"],
+            **roofline(model["ogq_attention"]["flops"], model["ogq_attention"]["bytes"], a4_ms / 1e3))
+    return stages, split
+
+
+def other_prefill(args, msa, wl):
+    """One more prefill workload, timed on its own after the headline steps: tokens/s and
+    the per-stage rooflines, with the same timer and model as the headline workload."""
+    import torch
+    import synth
+    specs = wl.specs()
+    x = {n: synth.device_tensor(specs[n]) for n in specs}
+    prob = wl.problem()
+    pb = msa.alloc_prefill(prob)
+
+    def run():
+        msa.run_prefill(prob, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], pb)
+    for _ in range(max(args.warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    msa.profiler_read(None, reset=True)
+    msa.profiler_enable(True)
+    for i in range(args.steps):
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    msa.profiler_enable(False)
+    kern = read_timer(msa, PREFILL_TIMER_NAMES)
+    msa.profiler_read(None, reset=True)
+    steps_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    ms = sum(steps_ms) / len(steps_ms)
+    stages, split = prefill_stage_report(wl, pb, kern, args.steps)
+    del x, pb
+    torch.cuda.empty_cache()
+    return dict(workload=wl.description, tokens=wl.T, tokens_per_s=wl.T / (ms / 1e3), prefill_ms=ms,
+                **{"prefill_" + k: v for k, v in percentiles(steps_ms).items()}, stages=stages,
+                attention_pairs=split["pairs"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -539,6 +680,9 @@ def main():
                     help="skip the extra decode timing over ragged lengths and a paged cache (serving variant)")
     ap.add_argument("--train", default="C1", choices=["C1", "C2", "none"],
                     help="workload of the extra training-step timing (default C1, 32768 tokens)")
+    ap.add_argument("--other-prefill", default="C1,C4",
+                    help="further prefill workloads timed after the headline steps (comma list of C1, C2, C4, "
+                         "or 'none')")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy 3 times (the known-size reference "
                          "for scaling hardware byte counters)")
@@ -611,15 +755,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     msa.profiler_enable(False)
-    kern = {}
-    for name in ("idx_scores_mfma", "block_topk", "invert_count", "invert_scatter", "invert_offsets",
-                 "scan_tile_sums", "scan_top", "scan_apply", "wl_count", "wl_emit", "ogq_mfma", "lse_merge",
-                 "hot_select", "hot_compact", "cold_count", "cold_scatter", "cold_offsets", "hot_mfma",
-                 "idx_scores_rows", "idx_scores_stream", "block_topk_t1", "decode_attn",
-                 "decode_simple", "decode_merge"):
-        ms, n = msa.profiler_read(name, reset=False)
-        if n:
-            kern[name] = dict(total_ms=ms, launches=n, samples=msa.profiler_samples(name))
+    kern = read_timer(msa, PREFILL_TIMER_NAMES + ("idx_scores_stream", "block_topk_t1", "decode_attn",
+                                                  "decode_simple", "decode_merge"))
     msa.profiler_read(None, reset=True)
     prefill_steps = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     decode_steps = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)] if db else None
@@ -628,37 +765,7 @@ def main():
     print("[bench] timed %d steps: prefill %.3f ms, decode %s ms" % (args.steps, prefill_ms,
           "%.3f" % decode_ms if decode_ms else "-"), file=sys.stderr, flush=True)
 
-    # algorithmic work of the prefill pass, with the blocks actually touched
-    counts = pb.csr_offsets[..., 1:] - pb.csr_offsets[..., :-1]
-    touched = int((counts > 0).sum())
-    model = prefill_model(wp.S, wp.T, wp.N, wp.H, wp.Hkv, wp.d, wp.dI, wp.k, touched_blocks=touched)
-    if os.environ.get("MSA_HOT_TILES", "1").startswith("0"):
-        hot_flag = torch.zeros_like(pb.sel, dtype=torch.bool)
-        keep = torch.zeros((1, 1, 1), dtype=torch.bool, device=pb.sel.device)
-    else:
-        hot_flag, keep = query_tile_split(wp, pb.sel)
-    split = attention_split_model(wp, pb.sel, hot_flag, keep)
-    model.update({kk: split[kk] for kk in ("hot_mfma", "ogq_mfma", "lse_merge")})
-    stages = {}
-    for kname, stage in PREFILL_KERNELS.items():
-        if kname not in kern:
-            continue
-        per_launch_s = kern[kname]["total_ms"] / kern[kname]["launches"] / 1e3
-        rf = roofline(model[stage]["flops"], model[stage]["bytes"], per_launch_s)
-        stages[kname] = dict(ms=per_launch_s * 1e3, **percentiles(kern[kname]["samples"]),
-                             flops=model[stage]["flops"], bytes=model[stage]["bytes"], **rf)
-    inv_ms = sum(kern[n]["total_ms"] for n in ("invert_count", "invert_scatter", "invert_offsets") if n in kern)
-    stages["invert(all launches)"] = dict(ms=inv_ms / args.steps)
-    split_ms = sum(kern[n]["total_ms"] for n in ("hot_select", "hot_compact", "cold_count", "cold_scatter", "cold_offsets")
-                   if n in kern)
-    stages["query_tile_split(all launches)"] = dict(ms=split_ms / args.steps)
-    # a4 as a whole (both attention kernels) against the full a4 work
-    a4_ms = sum(kern[n]["total_ms"] for n in ("ogq_mfma", "hot_mfma") if n in kern) / args.steps
-    if a4_ms > 0:
-        stages["a4_attention(ogq_mfma+hot_mfma)"] = dict(
-            ms=a4_ms, flops=model["ogq_attention"]["flops"], bytes=model["ogq_attention"]["bytes"],
-            **roofline(model["ogq_attention"]["flops"], model["ogq_attention"]["bytes"], a4_ms / 1e3))
-
+    stages, split = prefill_stage_report(wp, pb, kern, args.steps)
     dominant = max((k for k in stages if k in PREFILL_KERNELS), key=lambda k: stages[k]["ms"])
     dom = stages[dominant]
     traffic = measured_traffic(dominant) if wp is W.C2 else None
@@ -687,6 +794,7 @@ def main():
         dec = dict(workload=wd.description, us_per_step=decode_ms * 1e3, us_per_token_amortised=decode_ms * 1e3 / wd.S,
                    us_per_step_p50=1e3 * percentiles(decode_steps)["p50_ms"],
                    us_per_step_p95=1e3 * percentiles(decode_steps)["p95_ms"],
+                   us_per_step_p99=1e3 * percentiles(decode_steps)["p99_ms"],
                    sequences=wd.S, kv_len=wd.N, stages=dstages)
 
     dec8 = None
@@ -746,6 +854,13 @@ def main():
         trn = train_step(args, msa, {"C1": W.C1, "C2": W.C2}[args.train])
         print("[bench] training step (%s): %.3f ms" % (args.train, trn["ms_per_step"]), file=sys.stderr, flush=True)
 
+    others = {}
+    if args.other_prefill != "none":
+        for name in [x for x in args.other_prefill.split(",") if x and x != args.prefill]:
+            others[name] = other_prefill(args, msa, {"C1": W.C1, "C2": W.C2, "C4": W.C4}[name])
+            print("[bench] prefill %s: %.3f ms (%.0f tokens/s)" % (name, others[name]["prefill_ms"],
+                  others[name]["tokens_per_s"]), file=sys.stderr, flush=True)
+
     peaks = achievable_peaks()
     print("[bench] achievable: bf16 GEMM %.0f TFLOP/s, copy %.0f GB/s, read %.0f GB/s" % (
         peaks["bf16_gemm_8192_tflops"], peaks["hbm_copy_GBps"], peaks["hbm_read_sum_GBps"]), file=sys.stderr, flush=True)
@@ -754,6 +869,9 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline ...", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wp, xp)
+        if xd is not None:
+            print("[bench] oracle CPU baseline of the decode step ...", file=sys.stderr, flush=True)
+            cpu["decode"] = cpu_decode_baseline(wd, xd)
 
     value = wp.T / (prefill_ms / 1e3)
     ms_per_step = (prefill_ms + (decode_ms or 0.0))
@@ -764,7 +882,8 @@ def main():
         "config": {"workload": wp.description, "batch": wp.S, "seq_len": wp.T, "num_heads": wp.H,
                    "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
         "prefill_ms": prefill_ms, "prefill_ms_p50": percentiles(prefill_steps)["p50_ms"],
-        "prefill_ms_p95": percentiles(prefill_steps)["p95_ms"], "wall_s_timed": wall,
+        "prefill_ms_p95": percentiles(prefill_steps)["p95_ms"], "prefill_ms_p99": percentiles(prefill_steps)["p99_ms"],
+        "wall_s_timed": wall, "other_prefill": others,
         "fused_selection": fsel,
         "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "decode_token_level": dect,
         "training_step": trn, "stages": stages, "roofline": roof, "achievable_peaks": peaks, "cpu_baseline": cpu,

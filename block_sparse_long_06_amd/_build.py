@@ -39,28 +39,39 @@ def flags_for(src: str) -> list:
     return f
 
 
+# The host-sanitizer variant (libmsa_san.so): AddressSanitizer and UndefinedBehaviorSanitizer
+# on the HOST code only (argument validation, workspace layouts, launch set-up); the device
+# code is built as usual.  It loads only into a process that preloads clang's ASan runtime
+# (tests/test_sanitizers.py runs the CPU suite that way).
+SAN_HOST_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split() + [
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+LIB_SAN = os.path.join(HERE, "libmsa_san.so")
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every csrc/*.hip to an object (in parallel) and link libmsa.so."""
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
+    """Compile every csrc/*.hip to an object (in parallel) and link libmsa.so (with
+    sanitize=True: the host-sanitizer variant libmsa_san.so)."""
+    objdir = os.path.join(HERE, "_build", "san") if sanitize else os.path.join(HERE, "_build")
+    lib = LIB_SAN if sanitize else LIB
     os.makedirs(objdir, exist_ok=True)
     procs = []
     objs = []
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = ["hipcc", *flags_for(src), "-c", src, "-o", obj]
+        cmd = ["hipcc", *flags_for(src), *(SAN_HOST_FLAGS if sanitize else []), "-c", src, "-o", obj]
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         if len(procs) >= jobs:
             _drain(procs, verbose)
     _drain(procs, verbose)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     subprocess.run(["hipcc", "-shared", "--offload-arch=" + ARCH, *objs, "-o", tmp], check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def _drain(procs, verbose):

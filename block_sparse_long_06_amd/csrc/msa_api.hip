@@ -199,7 +199,11 @@ LaunchScope::~LaunchScope() {
 extern "C" {
 
 const char* msa_status_string(msa_status s) {
-  switch (s) {
+  // a C caller may pass any int: read the bits as one, not as the C++ enum (whose range
+  // stops at 7), so an unknown value is not undefined behaviour here
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case MSA_OK: return "MSA_OK";
     case MSA_ERR_INVALID_ARGUMENT: return "MSA_ERR_INVALID_ARGUMENT";
     case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";

@@ -31,20 +31,37 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "msa_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+_DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+# MSA_ORACLE_LIBRARY may name another build of the same source (the sanitizer build)
+_LIB = os.environ.get("MSA_ORACLE_LIBRARY") or _DEFAULT_LIB
+SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+CLANG = "/opt/rocm/llvm/bin/clang"
 
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile msa_oracle.c with gcc (IEEE semantics: no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+    if force or not os.path.exists(_DEFAULT_LIB):
+        tmp = _DEFAULT_LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
                "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, _DEFAULT_LIB)
+    return _DEFAULT_LIB
+
+
+def build_sanitized(force: bool = True) -> str:
+    """The same source under AddressSanitizer + UndefinedBehaviorSanitizer (clang, whose
+    ASan runtime the GPU library's host-sanitizer build shares; serial: no OpenMP)."""
+    if force or not os.path.exists(SAN_LIB):
+        tmp = SAN_LIB + ".tmp%d" % os.getpid()
+        cmd = [CLANG, "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fsanitize=address,undefined",
+               "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-shared", "-fPIC", _SRC, "-o", tmp,
+               "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, SAN_LIB)
+    return SAN_LIB
 
 
 def _load():

@@ -14,6 +14,10 @@ import oracle
 import synth
 
 SCORE_RTOL = 1e-4                    # |d| <= 1e-4 * max(|ref|, 1)  (fp32 accumulation)
+# |d| <= ATOL * max(|ref|, 1) per element: the absolute gate for outputs up to unit size
+# (every default-scale workload: |o| ~ 0.03-0.05).  Above it the bf16 roundings scale with
+# the value (P, the partial O and the output each carry 2^-9 relative), e.g. at a logit
+# scale of 1.0, where softmax is peaked and |o| reaches ~4.
 ATOL = {synth.BF16: 2e-2, synth.F32: 1e-4}
 # bf16 outputs are also held to a relative RMS error of 1% (observed ~0.3%: bf16 inputs,
 # P and output rounding).  2e-2 absolute alone cannot see one block too many or too few
@@ -57,10 +61,12 @@ def check_scores(gpu_rows, ref_rows, pos, B=128, what=""):
 def check_out(gpu, ref, dtype, what=""):
     g = gpu.astype(np.float64)
     err = np.abs(g - ref)
+    scaled = err / np.maximum(np.abs(ref), 1.0)
     rel_rms = float(np.sqrt(np.mean((g - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
-    say("  out %s: max abs err %.3e, rel rms %.3e" % (what, float(err.max()), rel_rms))
+    say("  out %s: max abs err %.3e (scaled %.3e), rel rms %.3e" % (what, float(err.max()), float(scaled.max()),
+                                                                   rel_rms))
     assert np.all(np.isfinite(g)), "non-finite GPU output"
-    assert float(err.max()) <= ATOL[dtype], "attention output off by %.3e" % float(err.max())
+    assert float(scaled.max()) <= ATOL[dtype], "attention output off by %.3e (scaled)" % float(scaled.max())
     assert rel_rms <= REL_RMS_MAX[dtype], "attention output relative RMS error %.3e" % rel_rms
     return rel_rms
 
