@@ -30,7 +30,7 @@ EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_invert_selection", "msa_s
             "msa_block_topk_kv", "msa_sparse_attn_decode_kv", "msa_sparse_attn_prefill_train",
             "msa_sparse_attn_backward", "msa_index_kl", "msa_index_backward", "msa_token_scores",
             "msa_token_topk", "msa_token_attn_decode", "msa_token_workspace_bytes", "msa_index_topk",
-            "msa_sparse_attn_prefill_kv")
+            "msa_sparse_attn_prefill_kv", "msa_sparse_attn_decode_noalloc")
 
 
 class MSAError(RuntimeError):
@@ -101,6 +101,8 @@ def lib():
         L.msa_invert_selection.argtypes = [PP, P, P, P, P, ctypes.c_size_t, P]
         L.msa_sparse_attn_prefill.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_sparse_attn_decode.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_sparse_attn_decode_noalloc.argtypes = [PP, P, P, P, P, P, P]
+        L.msa_sparse_attn_decode_noalloc.restype = st
         LP = ctypes.POINTER(KVLayout)
         L.msa_index_scores_kv.argtypes = [PP, LP, P, P, P, P]
         L.msa_block_topk_kv.argtypes = [PP, LP, P, P, P]
@@ -214,6 +216,16 @@ def sparse_attn_decode(prob: Problem, q, k_cache, v_cache, sel, out, workspace, 
     _check(lib().msa_sparse_attn_decode(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                         _ptr(sel), _ptr(out), _ptr(workspace), workspace_bytes_,
                                         _stream(stream, q)))
+
+
+DECODE_SCRATCH_BYTES = 32 << 20  # MSA_DECODE_SCRATCH_BYTES
+
+
+def sparse_attn_decode_noalloc(prob: Problem, q, k_cache, v_cache, sel, out, stream=None) -> None:
+    """msa_sparse_attn_decode with the library's static scratch instead of a workspace (no
+    allocation; calls that overlap on one device race)."""
+    _check(lib().msa_sparse_attn_decode_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                _ptr(sel), _ptr(out), _stream(stream, q)))
 
 
 def _lay(layout):

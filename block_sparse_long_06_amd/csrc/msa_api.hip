@@ -166,6 +166,34 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRecord> g_prof;
 
+// ------------------------------------------------------------------ allocation-free decode
+// The decode partials of msa_sparse_attn_decode_noalloc live in this file-scope device array
+// (one copy per device, held until the process ends).  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the address hipGetSymbolAddress
+// returns for the current device, resolved once per device and kept here.
+static __device__ __align__(256) unsigned char scratch[MSA_DECODE_SCRATCH_BYTES];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+msa_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MSA_ERR_DEVICE, "device %d outside the %d devices the scratch table holds", dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MSA_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
 }  // namespace
 
 namespace msa {
@@ -347,6 +375,28 @@ msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, const 
   return device_status(
       msa::launch_decode(D, q, k_cache, v_cache, sel, out, workspace, (hipStream_t)stream),
       "msa_sparse_attn_decode launch");
+}
+
+msa_status msa_sparse_attn_decode_noalloc(const msa_problem* prob, const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* sel, void* out, void* stream) {
+  msa::Dims D;
+  msa_status st = check_problem(prob, &D, false, true);
+  if (st != MSA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(out);
+  const size_t need = msa::decode_workspace_bytes(D);
+  if (need > (size_t)MSA_DECODE_SCRATCH_BYTES)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "msa_sparse_attn_decode_noalloc: the problem needs %zu bytes of partials, above the %zu-byte "
+                "static scratch (use msa_sparse_attn_decode with a workspace)",
+                need, (size_t)MSA_DECODE_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws)) != MSA_OK) return st;
+  return device_status(msa::launch_decode(D, q, k_cache, v_cache, sel, out, ws, (hipStream_t)stream),
+                       "msa_sparse_attn_decode_noalloc launch");
 }
 
 msa_status msa_index_scores_kv(const msa_problem* prob, const msa_kv_layout* layout, const void* q_idx,

@@ -198,6 +198,27 @@ msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, const 
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * msa_sparse_attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, kernels and output as msa_sparse_attn_decode; the decode
+ * partials go to a static device array of MSA_DECODE_SCRATCH_BYTES owned by the library
+ * (one per device, held until the process ends).  The call allocates and frees nothing.
+ *   - A problem whose msa_workspace_bytes(prob, MSA_CALL_DECODE) exceeds
+ *     MSA_DECODE_SCRATCH_BYTES returns MSA_ERR_WORKSPACE_TOO_SMALL (at bf16 and d = 128 a
+ *     partial takes 260 bytes, so 32 MiB holds S * T * Hkv * k * G of about 129,000: 16
+ *     sequences x 7 queries of the 64-head, top-16 shape).
+ *   - Every call on one device uses that device's one array: calls that may overlap on a
+ *     device (several streams, or several host threads) race and must be serialised by
+ *     the caller.  Nothing in the array needs to start at zero; it keeps the last call's
+ *     partials.
+ *   - The first call on a device looks up the array's device address (no allocation);
+ *     make one call outside any graph capture first if the capture must not see it.
+ */
+#define MSA_DECODE_SCRATCH_BYTES (32u << 20)
+msa_status msa_sparse_attn_decode_noalloc(const msa_problem* prob, const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* sel, void* out, void* stream);
+
+/*
  * Serving variants of the decode step: ragged per-sequence cache lengths and paged caches
  * ([P1] 第二步：精算 -- the whole uncompressed cache stays resident, and each new token
  * reads 16 of its 128-token blocks; one page here IS one such block).

@@ -183,3 +183,21 @@ def test_kv_calls_reject_null_pointers_and_small_workspace():
         msa.sparse_attn_decode_kv(p, L, 1, 1, 1, 1, 1, 1, need - 1, stream=0)
     assert ei.value.status == msa.MSA_ERR_WORKSPACE_TOO_SMALL
 
+
+def test_no_alloc_decode_is_validated_on_the_host():
+    """Argument checks and the scratch-size limit come before any device call."""
+    prob = msa.problem(16, 8, 1 << 20, 64, 8, 128, 64, 16)
+    need = msa.workspace_bytes(prob, msa.MSA_CALL_DECODE)
+    assert need > msa.DECODE_SCRATCH_BYTES
+    L = msa.lib()
+    p = ctypes.c_void_p(16)
+    st = L.msa_sparse_attn_decode_noalloc(ctypes.byref(prob), p, p, p, p, p, None)
+    assert st == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    assert "static scratch" in msa.last_error_message()
+    small = msa.problem(16, 1, 1 << 20, 64, 8, 128, 64, 16)
+    assert msa.workspace_bytes(small, msa.MSA_CALL_DECODE) <= msa.DECODE_SCRATCH_BYTES
+    st = L.msa_sparse_attn_decode_noalloc(ctypes.byref(small), p, None, p, p, p, None)
+    assert st == msa.MSA_ERR_INVALID_ARGUMENT
+    st = L.msa_sparse_attn_decode_noalloc(ctypes.byref(_good(head_dim=96)), p, p, p, p, p, None)
+    assert st == msa.MSA_ERR_UNSUPPORTED
+
