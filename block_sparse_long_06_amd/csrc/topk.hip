@@ -383,6 +383,180 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
   if (lane == 0) out[need] = bt;  // the own block is the largest id of the row
 }
 
+// Long rows and few of them (decode: one row per (sequence, group), ~8K past blocks): one
+// 1024-thread workgroup per row reads the whole row in one pass, 8 consecutive scores per
+// thread (ids 8 tid .. 8 tid + 7), as order keys (0 = not eligible).
+//   1. each wave's threshold tau_w <= the need-th largest of its 512 keys (lane maxima,
+//      lane_kth); tau = the largest tau_w is still <= the row's need-th largest key, so
+//      every selected block has key >= tau;
+//   2. the keys >= tau are compacted into LDS in ascending id order (a scan of the
+//      per-thread counts inside each wave, then the wave totals);
+//   3. wave 0 holds the candidates in registers (candidate c in slot c / 64 of lane c % 64,
+//      so slot-major order is id order), finds the need-th largest key by a radix search
+//      over them, takes every larger key and, among keys equal to it, the lowest ids.
+//      More than kLongCap candidates (ties at the threshold) fall back to the row in memory.
+constexpr int kLongThreads = 1024;
+constexpr int kLongWaves = kLongThreads / 64;
+constexpr int kLongPer = 8;
+constexpr int kLongCap = 1024;
+constexpr int kLongSlots = kLongCap / 64;
+constexpr int64_t kLongRows = 16384;  // up to 16K rows (workgroups of 16 waves)
+
+template <bool VEC>
+__global__ void __launch_bounds__(kLongThreads) block_topk_long(Dims D, const float* __restrict__ scores,
+                                                               int32_t* __restrict__ sel) {
+  __shared__ uint32_t s_ord[kLongCap];
+  __shared__ int32_t s_id[kLongCap];
+  __shared__ uint32_t s_tau[kLongWaves];
+  __shared__ int s_cnt[kLongWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t r32 = blockIdx.x;
+  const int t = (int)(r32 % (uint32_t)D.T);
+  const int bt = (seq_pos0(D, (int)(r32 / ((uint32_t)D.Hkv * (uint32_t)D.T))) + t) / D.B;
+  const int k = D.k;
+  int32_t* out = sel + (int64_t)r32 * k;
+  const int n = bt;
+  const int need = k - 1;
+  if (need >= n) {  // uniform over the workgroup
+    for (int i = tid; i < k; i += kLongThreads) out[i] = i <= bt ? i : -1;
+    return;
+  }
+  if (need == 0) {
+    if (tid == 0) out[0] = bt;
+    return;
+  }
+  const float* sc = scores + (int64_t)r32 * D.nb;
+  const int base = kLongPer * tid;
+  uint32_t key[kLongPer];
+  if (VEC) {
+    // base is a multiple of 4 and rows are a multiple of 4 long: base < n keeps base + 3
+    // inside the row, base + 4 < n keeps base + 7 inside it
+    const float4 a = *reinterpret_cast<const float4*>(sc + (base < n ? base : 0));
+    const float4 b = *reinterpret_cast<const float4*>(sc + (base + 4 < n ? base + 4 : 0));
+    const float v[kLongPer] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int u = 0; u < kLongPer; ++u) key[u] = base + u < n ? ord_key(v[u]) : 0u;
+  } else {
+    float v[kLongPer];
+#pragma unroll
+    for (int u = 0; u < kLongPer; ++u) v[u] = sc[base + u < n ? base + u : 0];
+#pragma unroll
+    for (int u = 0; u < kLongPer; ++u) key[u] = base + u < n ? ord_key(v[u]) : 0u;
+  }
+  uint32_t lm = key[0];
+#pragma unroll
+  for (int u = 1; u < kLongPer; ++u) lm = max(lm, key[u]);
+  // 1. wave threshold (0 when fewer than `need` lanes of the wave hold eligible blocks)
+  const bool live = base < n;
+  const int nlive = __popcll(__ballot(live));
+  const uint32_t tau_w = nlive >= need ? lane_kth(lm, live, need) : 0u;
+  if (lane == 0) s_tau[wave] = tau_w;
+  __syncthreads();
+  uint32_t tau = 0u;
+#pragma unroll
+  for (int w = 0; w < kLongWaves; ++w) tau = max(tau, s_tau[w]);
+  // 2. candidates (eligible keys are > 0), ascending id order
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < kLongPer; ++u) c += (key[u] != 0u && key[u] >= tau) ? 1 : 0;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += x;
+  }
+  if (lane == 63) s_cnt[wave] = incl;
+  __syncthreads();
+  int wbase = 0, C = 0;
+#pragma unroll
+  for (int w = 0; w < kLongWaves; ++w) {
+    const int x = s_cnt[w];
+    wbase += w < wave ? x : 0;
+    C += x;
+  }
+  int p = wbase + incl - c;
+#pragma unroll
+  for (int u = 0; u < kLongPer; ++u) {
+    if (key[u] != 0u && key[u] >= tau) {
+      if (p < kLongCap) {
+        s_ord[p] = key[u];
+        s_id[p] = base + u;
+      }
+      ++p;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  if (C > kLongCap) {  // heavy ties at the threshold: the row from memory
+    RowSrc src{sc, n};
+    select_and_write(src, lane, need, out);
+  } else if (C <= 64) {
+    const bool have = lane < C;
+    pick_from_lanes(have ? s_ord[lane] : 0u, have ? s_id[lane] : 0, have, lane, need, out);
+  } else {
+    // 3. at least `need` candidates (every selected block is one), in registers
+    const int nu = (C + 63) >> 6;
+    uint32_t ck[kLongSlots];
+    int32_t ci[kLongSlots];
+#pragma unroll
+    for (int u = 0; u < kLongSlots; ++u) {
+      const int cc = lane + 64 * u;
+      ck[u] = cc < C ? s_ord[cc] : 0u;  // 0 never reaches a candidate prefix below
+      ci[u] = cc < C ? s_id[cc] : 0;
+    }
+    // prefix: the need-th largest candidate key, or a prefix of it that exactly `need`
+    // candidates reach (the search then stops: it separates them from the rest).  The
+    // search runs below the high bits every candidate shares.
+    uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+#pragma unroll
+    for (int u = 0; u < kLongSlots; ++u)
+      if (u < nu && lane + 64 * u < C) {
+        hi = max(hi, ck[u]);
+        lo = min(lo, ck[u]);
+      }
+    uint32_t whi, wlo;
+    wave_umax_umin(hi, lo, whi, wlo);
+    uint32_t prefix = whi;
+    if (whi != wlo) {
+      const int top = 31 - __builtin_clz(whi ^ wlo);
+      prefix = whi & ~((2u << top) - 1u);  // <= every candidate
+      for (int bit = top; bit >= 0; --bit) {
+        const uint32_t cand = prefix | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < kLongSlots; ++u)
+          if (u < nu) cnt += __popcll(__ballot(ck[u] >= cand));
+        if (cnt >= need) {
+          prefix = cand;
+          if (cnt == need) break;
+        }
+      }
+    }
+    int c_gt = 0;
+#pragma unroll
+    for (int u = 0; u < kLongSlots; ++u)
+      if (u < nu) c_gt += __popcll(__ballot(ck[u] > prefix));
+    const int need_eq = need - c_gt;  // >= 0 (0 when the search stopped between keys)
+    int pos = 0, eq_seen = 0;
+#pragma unroll
+    for (int u = 0; u < kLongSlots; ++u) {
+      if (u < nu) {
+        const bool eq = ck[u] == prefix;
+        const uint64_t meq = __ballot(eq);
+        const bool f = ck[u] > prefix || (eq && eq_seen + lanes_below(meq) < need_eq);
+        const uint64_t m = __ballot(f);
+        const int at = pos + lanes_below(m);
+        if (f && at < need) out[at] = ci[u];
+        pos += __popcll(m);
+        eq_seen += __popcll(meq);
+      }
+    }
+  }
+  if (lane == 0) out[need] = bt;  // the own block is the largest id of the row
+}
+
 }  // namespace
 
 hipError_t launch_block_topk(const Dims& D, const float* scores, int32_t* sel, hipStream_t st) {
@@ -391,6 +565,14 @@ hipError_t launch_block_topk(const Dims& D, const float* scores, int32_t* sel, h
   if (rows > (int64_t)UINT32_MAX || (int64_t)D.Hkv * D.T > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
   LaunchScope scope(D.T == 1 ? "block_topk_t1" : "block_topk", st);
   const bool vec = D.nb % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15u) == 0;
+  // long rows and too few of them to fill the chip one wave each: a workgroup per row
+  if (D.nb > 64 * kRegPerLane && rows <= kLongRows) {
+    if (vec)
+      hipLaunchKernelGGL(block_topk_long<true>, dim3((unsigned)rows), dim3(kLongThreads), 0, st, D, scores, sel);
+    else
+      hipLaunchKernelGGL(block_topk_long<false>, dim3((unsigned)rows), dim3(kLongThreads), 0, st, D, scores, sel);
+    return hipGetLastError();
+  }
   if (vec)
     hipLaunchKernelGGL(block_topk_kernel<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0, st, D, scores, sel);
   else
