@@ -1,7 +1,9 @@
 """GPU parity of the fused selection (index scores + top-k without the block-score matrix):
 its output must be bit-identical to msa_index_scores followed by msa_block_topk (whose
 selection the forward parity tests gate against the oracle), on shapes that span several
-16-block chunks, several 1024-block spans, ragged tails, E4M3 keys and k in {1, 4, 16}."""
+16-block chunks, several 1024-block spans, ragged tails, E4M3 keys and k in {1, 4, 16}.  Every
+row is also checked against the oracle: its top-k of the GPU's scores (bit-exact) and its
+index scores (1e-4 scaled)."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +12,7 @@ import block_sparse_long_06_amd as msa
 import oracle
 import synth
 from synth import workloads as W
-from tests.gpu_util import gen, require_gpu, say
+from tests.gpu_util import check_scores, f64, gen, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -42,14 +44,16 @@ def test_fused_selection_equals_the_two_calls(wl):
     a, b = sel.cpu().numpy(), sel_ref.cpu().numpy()
     say("  rows %d, equal rows %d" % (a.shape[0] * a.shape[1] * a.shape[2], int((a == b).all(-1).sum())))
     np.testing.assert_array_equal(a, b)
-    # and the selection is the oracle's top-k of the (unfused) GPU scores on a sample of rows
+    # and on every row the selection is the oracle's top-k of the (unfused) GPU scores, and
+    # those scores are the oracle's within the indexer tolerance
     pos = oracle.positions(wl.N, wl.T)
-    rows = np.unique(np.linspace(0, wl.T - 1, 64).astype(int))
     sc = scores.cpu().numpy()
+    qI, kI = f64(x["q_idx"]), f64(x["k_idx"])
     for s in range(wl.S):
         for g in range(wl.Hkv):
-            np.testing.assert_array_equal(a[s, g][rows], oracle.slice_block_topk(sc[s, g][rows], pos[rows] // 128,
-                                                                                wl.k))
+            np.testing.assert_array_equal(a[s, g], oracle.slice_block_topk(sc[s, g], pos // 128, wl.k))
+            check_scores(sc[s, g], oracle.slice_index_scores(qI[s, g], pos, kI[s, g], 128), pos,
+                         what="s%d g%d" % (s, g))
     # the candidate workspace is far smaller than the block-score matrix it replaces
     if wl.T >= 256:
         assert ws.numel() < scores.numel() * 4 or wl.nb < 64
