@@ -311,12 +311,14 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* _
 // chunks) is issued first, and the selection mask, lse values and weights are worked
 // out while they are in flight (loads of invalid slots read unused workspace and are
 // never accumulated).  With a hot mask (HOT) the slot mask is formed first and only
-// the slots that are read are loaded: skipped hot slots hold no partial.
+// the slots that are read are loaded: skipped hot slots hold no partial.  lse_out and
+// mass_out (optional, training) as in lse_merge_kernel.
 template <typename T, int CPL, bool HOT>
 __global__ void __launch_bounds__(256) lse_merge_bf16_k16(Dims D, const int32_t* __restrict__ sel,
                                                           const float* __restrict__ part_lse,
                                                           const uint16_t* __restrict__ part_o,
-                                                          const uint64_t* __restrict__ hotmask, T* __restrict__ out) {
+                                                          const uint64_t* __restrict__ hotmask, T* __restrict__ out,
+                                                          float* __restrict__ lse_out, float* __restrict__ mass_out) {
   __shared__ float wbuf[4][16 * 16];
   __shared__ float hstat[4][2][16];
   const int lane = threadIdx.x & 63;
@@ -375,6 +377,15 @@ __global__ void __launch_bounds__(256) lse_merge_bf16_k16(Dims D, const int32_t*
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // training outputs: the row's log-sum-exp per head, and per slot the share of the
+  // attention that falls on that block, averaged over the group's heads
+  if (lse_out != nullptr && lane < G)
+    lse_out[((int64_t)s * D.T + t) * D.H + g * G + lane] = hstat[wave][0][lane] - __logf(hstat[wave][1][lane]);
+  if (mass_out != nullptr && lane < D.k) {
+    float mw = 0.0f;
+    for (int hh = 0; hh < G; ++hh) mw += wb[lane * G + hh];
+    mass_out[(((int64_t)s * D.Hkv + g) * D.T + t) * D.k + lane] = mw / (float)G;
+  }
   T* orow = out + (((int64_t)s * D.T + t) * D.H + g * G) * D.d;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
@@ -533,19 +544,19 @@ hipError_t launch_lse_merge(const Dims& D, const int32_t* sel, const float* part
   const uint16_t* pb = static_cast<const uint16_t*>(part_o);
   uint16_t* ob = static_cast<uint16_t*>(out);
   const bool train = lse_out != nullptr || mass_out != nullptr;
-  if (!train && D.dtype == MSA_BF16 && part_o_is_bf16 && D.k <= 16 && (gd == 512 || gd == 1024)) {
+  if (D.dtype == MSA_BF16 && part_o_is_bf16 && D.k <= 16 && (gd == 512 || gd == 1024) && !(train && hotmask)) {
     if (gd == 1024 && hotmask)
       hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 2, true>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
-                         hotmask, ob);
+                         hotmask, ob, lse_out, mass_out);
     else if (gd == 1024)
       hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 2, false>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
-                         hotmask, ob);
+                         hotmask, ob, lse_out, mass_out);
     else if (hotmask)
       hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 1, true>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
-                         hotmask, ob);
+                         hotmask, ob, lse_out, mass_out);
     else
       hipLaunchKernelGGL((lse_merge_bf16_k16<uint16_t, 1, false>), grid, dim3(256), 0, st, D, sel, part_lse, pb,
-                         hotmask, ob);
+                         hotmask, ob, lse_out, mass_out);
   } else if (D.dtype == MSA_BF16) {
     if (part_o_is_bf16)
       hipLaunchKernelGGL((lse_merge_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, D, sel, part_lse, pb,

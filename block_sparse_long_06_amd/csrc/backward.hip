@@ -383,6 +383,9 @@ __global__ void __launch_bounds__(256) dq_merge(Dims D, const int32_t* __restric
 }
 
 // Per row: KL(teacher || student) over the selected blocks and d loss / d block score.
+// The row's selections, their block scores (a gather) and masses are all loaded before the
+// first is used (KR >= k slots held in registers; KR = 0: any k, from memory).
+template <int KR>
 __global__ void __launch_bounds__(256) index_kl_kernel(Dims D, const float* __restrict__ scores,
                                                        const int32_t* __restrict__ sel,
                                                        const float* __restrict__ mass, float sigma,
@@ -392,26 +395,58 @@ __global__ void __launch_bounds__(256) index_kl_kernel(Dims D, const float* __re
   const int32_t* sl = sel + row * D.k;
   const float* ms = mass + row * D.k;
   const float* sc = scores + row * (int64_t)D.nb;
+  constexpr int NR = KR > 0 ? KR : 1;
+  bool ok[NR];
+  float sv[NR], mv[NR];
+  if constexpr (KR > 0) {
+    int b[KR];
+#pragma unroll
+    for (int i = 0; i < KR; ++i) b[i] = i < D.k ? sl[i] : -1;
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+      ok[i] = b[i] >= 0 && b[i] < D.nb;
+      sv[i] = sc[ok[i] ? b[i] : 0];
+      mv[i] = i < D.k ? ms[i] : 0.0f;
+    }
+  }
+  auto slot = [&](int i, float& s_i, float& m_i) -> bool {  // block score and mass of slot i
+    if constexpr (KR > 0) {
+      s_i = sv[i];
+      m_i = mv[i];
+      return ok[i];
+    } else {
+      const int b = sl[i];
+      const bool v = b >= 0 && b < D.nb;
+      s_i = v ? sc[b] : 0.0f;
+      m_i = ms[i];
+      return v;
+    }
+  };
+  const int k = KR > 0 ? KR : D.k;
   float mx = -INFINITY, tm = 0.0f;
-  for (int i = 0; i < D.k; ++i) {
-    const int b = sl[i];
-    if (b < 0 || b >= D.nb) continue;
-    mx = fmaxf(mx, sigma * sc[b]);
-    tm += ms[i];
+#pragma unroll
+  for (int i = 0; i < k; ++i) {
+    float s_i, m_i;
+    if (!slot(i, s_i, m_i)) continue;
+    mx = fmaxf(mx, sigma * s_i);
+    tm += m_i;
   }
   float l = 0.0f;
-  for (int i = 0; i < D.k; ++i) {
-    const int b = sl[i];
-    if (b >= 0 && b < D.nb) l += expf(sigma * sc[b] - mx);
+#pragma unroll
+  for (int i = 0; i < k; ++i) {
+    float s_i, m_i;
+    if (slot(i, s_i, m_i)) l += expf(sigma * s_i - mx);
   }
   const float logl = logf(l);
   float L = 0.0f;
-  for (int i = 0; i < D.k; ++i) {
-    const int b = sl[i];
+#pragma unroll
+  for (int i = 0; i < k; ++i) {
+    if (i >= D.k) break;
+    float s_i, m_i;
     float gsc = 0.0f;
-    if (b >= 0 && b < D.nb) {
-      const float logps = sigma * sc[b] - mx - logl;
-      const float pt = tm > 0.0f ? ms[i] / tm : 0.0f;
+    if (slot(i, s_i, m_i)) {
+      const float logps = sigma * s_i - mx - logl;
+      const float pt = tm > 0.0f ? m_i / tm : 0.0f;
       if (pt > 0.0f) L += pt * (logf(pt) - logps);
       gsc = sigma * (expf(logps) - pt);
     }
@@ -670,8 +705,11 @@ hipError_t launch_index_kl(const Dims& D, const float* scores, const int32_t* se
                            float* loss, float* dscore, hipStream_t st) {
   const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
   LaunchScope scope("index_kl", st);
-  hipLaunchKernelGGL(index_kl_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, D, scores, sel, mass,
-                     sigma, loss, dscore);
+  const dim3 grid((unsigned)((rows + 255) / 256));
+  if (D.k <= 16)
+    hipLaunchKernelGGL(index_kl_kernel<16>, grid, dim3(256), 0, st, D, scores, sel, mass, sigma, loss, dscore);
+  else
+    hipLaunchKernelGGL(index_kl_kernel<0>, grid, dim3(256), 0, st, D, scores, sel, mass, sigma, loss, dscore);
   return hipGetLastError();
 }
 
