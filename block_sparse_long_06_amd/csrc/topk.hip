@@ -54,8 +54,12 @@ constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kHalfRowMirror = 0x141;
 constexpr int kRowMirror = 0x140;
 
+// DPP row broadcasts: the last lane of one row of 16 to the next row(s).
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+
 // Wave-uniform maximum and minimum of a per-lane value: a butterfly inside each row
-// of 16 lanes, then the four row results.
+// of 16 lanes, then the row results carried to lane 63 by two row broadcasts.
 __device__ __forceinline__ void wave_umax_umin(uint32_t a, uint32_t b, uint32_t& mx, uint32_t& mn) {
   a = max(a, dpp<kQuadSwap1>(a));
   b = min(b, dpp<kQuadSwap1>(b));
@@ -65,46 +69,52 @@ __device__ __forceinline__ void wave_umax_umin(uint32_t a, uint32_t b, uint32_t&
   b = min(b, dpp<kHalfRowMirror>(b));
   a = max(a, dpp<kRowMirror>(a));
   b = min(b, dpp<kRowMirror>(b));
-  const uint32_t a0 = __builtin_amdgcn_readlane(a, 0), a1 = __builtin_amdgcn_readlane(a, 16);
-  const uint32_t a2 = __builtin_amdgcn_readlane(a, 32), a3 = __builtin_amdgcn_readlane(a, 48);
-  const uint32_t b0 = __builtin_amdgcn_readlane(b, 0), b1 = __builtin_amdgcn_readlane(b, 16);
-  const uint32_t b2 = __builtin_amdgcn_readlane(b, 32), b3 = __builtin_amdgcn_readlane(b, 48);
-  mx = max(max(a0, a1), max(a2, a3));
-  mn = min(min(b0, b1), min(b2, b3));
+  // rows 1 and 3 take the row below; then rows 2 and 3 take row 1 (rows 0 and 2 of the
+  // first step, rows 0 and 1 of the second keep their value)
+  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp((int)a, (int)a, kRowBcast15, 0xA, 0xF, false));
+  b = min(b, (uint32_t)__builtin_amdgcn_update_dpp((int)b, (int)b, kRowBcast15, 0xA, 0xF, false));
+  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp((int)a, (int)a, kRowBcast31, 0xC, 0xF, false));
+  b = min(b, (uint32_t)__builtin_amdgcn_update_dpp((int)b, (int)b, kRowBcast31, 0xC, 0xF, false));
+  mx = __builtin_amdgcn_readlane(a, 63);
+  mn = __builtin_amdgcn_readlane(b, 63);
 }
 
-// One key per lane (`live` lanes only; at least `want` of them).  Returns x with
-// #{live keys >= x} >= want and x <= the want-th largest live key: either that key
-// itself, or a prefix of it that exactly `want` live keys reach (the search stops
-// there: the prefix then separates the `want` largest from the rest).  The search
-// runs over the bits below those that every live key shares.
-__device__ __forceinline__ uint32_t lane_kth(uint32_t key, bool live, int want) {
-  uint32_t hi, lo;
-  wave_umax_umin(live ? key : 0u, live ? key : 0xFFFFFFFFu, hi, lo);
+// One key per lane (`live` lanes only; at least `want` of them), every live key in
+// [lo, hi].  Returns x with #{live keys >= x} >= want and x <= the want-th largest live
+// key: either that key itself, or a prefix of it that exactly `want` live keys reach
+// (the search stops there: the prefix then separates the `want` largest from the
+// rest).  The search runs over the bits below those that hi and lo share (every live
+// key shares them too); its state is wave-uniform and stays on the scalar unit.
+__device__ __forceinline__ uint32_t lane_kth_in(uint32_t key, bool live, int want, uint32_t hi, uint32_t lo) {
   const uint32_t diff = hi ^ lo;
   if (diff == 0u) return hi;
-  const int top = 31 - __builtin_clz(diff);
-  uint32_t prefix = hi & ~((2u << top) - 1u);  // <= lo: every live key reaches it
-  const uint32_t k = live ? key : 0u;          // 0 never reaches a candidate (cand > 0)
-  for (int bit = top; bit >= 0; --bit) {
-    const uint32_t cand = prefix | (1u << bit);
-    const int c = __popcll(__ballot(k >= cand));
-    if (c >= want) {
-      prefix = cand;
-      if (c == want) break;
-    }
-  }
+  const uint32_t top = 0x80000000u >> __builtin_clz(diff);
+  uint32_t prefix = hi & ~(top + top - 1u);  // <= lo: every live key reaches it
+  uint32_t k = live ? key : 0u;  // 0 never reaches a candidate (cand > 0)
+  // one register holding the masked key: the compares below read it as is
+  __asm__ volatile("" : "+v"(k));
+  // two bits per pass (the exit is tested once per pass: a pass that starts with exactly
+  // `want` keys at the prefix keeps it so; past bit 0 the second step re-tests the prefix)
+  uint32_t b = top;
+  do {
+    uint32_t cand = prefix | b;
+    const int c1 = __popcll(__ballot(k >= cand));
+    prefix = c1 >= want ? cand : prefix;
+    cand = prefix | (b >> 1);
+    const int c2 = __popcll(__ballot(k >= cand));
+    prefix = c2 >= want ? cand : prefix;
+    b = (c1 == want || c2 == want) ? 0u : b >> 2;
+  } while (b != 0u);
   return prefix;
 }
 
+__device__ __forceinline__ uint32_t lane_kth(uint32_t key, bool live, int want) {
+  uint32_t hi, lo;
+  wave_umax_umin(live ? key : 0u, live ? key : 0xFFFFFFFFu, hi, lo);
+  return lane_kth_in(key, live, want, hi, lo);
+}
+
 // Candidate sources: element c (ascending c = ascending block id) -> (ord, id).
-struct LdsSrc {
-  const uint32_t* ord;
-  const int32_t* id;
-  int n;
-  __device__ uint32_t key(int c) const { return ord[c]; }
-  __device__ int32_t idx(int c) const { return id[c]; }
-};
 struct LdsFloatSrc {
   const float* val;
   const int32_t* id;
@@ -172,13 +182,14 @@ __device__ __forceinline__ void select_and_write(const Src& src, int lane, int n
   }
 }
 
-// Candidates held one per lane (lanes below C, in ascending id order, C >= need):
-// writes the `need` best by (ord desc, id asc) to out[0 .. need-1] in ascending id order.
-__device__ __forceinline__ void pick_from_lanes(uint32_t co, int32_t cid, bool have, int lane, int need,
-                                                int32_t* out) {
+// Candidates held one per lane (lanes below C, in ascending id order, C >= need), every
+// candidate key in [lo, hi]: writes the `need` best by (ord desc, id asc) to
+// out[0 .. need-1] in ascending id order.
+__device__ __forceinline__ void pick_from_lanes_in(uint32_t co, int32_t cid, bool have, int lane, int need,
+                                                   int32_t* out, uint32_t hi, uint32_t lo) {
   // when the search stops early exactly `need` candidates are >= tau and every one
   // equal to tau is taken below
-  const uint32_t tau = lane_kth(co, have, need);
+  const uint32_t tau = lane_kth_in(co, have, need, hi, lo);
   const int c_gt = __popcll(__ballot(have && co > tau));
   const uint64_t eqm = __ballot(have && co == tau);
   const int need_eq = need - c_gt;
@@ -192,6 +203,13 @@ __device__ __forceinline__ void pick_from_lanes(uint32_t co, int32_t cid, bool h
   if (f && at < need) out[at] = cid;
 }
 
+__device__ __forceinline__ void pick_from_lanes(uint32_t co, int32_t cid, bool have, int lane, int need,
+                                                int32_t* out) {
+  uint32_t hi, lo;
+  wave_umax_umin(have ? co : 0u, have ? co : 0xFFFFFFFFu, hi, lo);
+  pick_from_lanes_in(co, cid, have, lane, need, out, hi, lo);
+}
+
 // Completes this wave's earlier LDS accesses before its later ones (lanes exchange data
 // through LDS).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -200,6 +218,43 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Writes the selection of a row from its candidates in LDS (values s_f[0 .. C-1] with ids
+// s_id[...], ascending id order; C >= need; the buffer holds only the first kCap of them,
+// so beyond kCap the row is read again from memory).  Every candidate key lies in
+// [t1, hi].
+__device__ __forceinline__ void select_candidates(const float* s_f, const int32_t* s_id, int C, const float* sc,
+                                                  int n, int lane, int need, uint32_t hi, uint32_t t1,
+                                                  int32_t* out) {
+  if (C <= 64) {
+    const bool have = lane < C;
+    pick_from_lanes_in(have ? ord_key(s_f[lane]) : 0u, have ? s_id[lane] : 0, have, lane, need, out, hi, t1);
+  } else if (C <= kCap) {
+    LdsFloatSrc src{s_f, s_id, C};
+    select_and_write(src, lane, need, out);
+  } else {
+    RowSrc src{sc, n};
+    select_and_write(src, lane, need, out);
+  }
+}
+
+// Appends the scores of one 64-wide segment (element id0 + lane) that pass `f` to the
+// candidate buffer in ascending id order.  Positions wrap at kCap: past kCap candidates
+// the buffer is not read.
+__device__ __forceinline__ void append_candidates(bool f, float v, int id, int lane, float* s_f, int32_t* s_id,
+                                                  int& C) {
+  const uint64_t m = __ballot(f);
+  if (m != 0ull) {
+    const int p = (C + lanes_below(m)) & (kCap - 1);
+    if (f) {
+      s_f[p] = v;
+      s_id[p] = id;
+    }
+    C += __popcll(m);
+  }
+}
+
+// Grid: (ceil(T / kWaves), S * H_kv) when T >= kWaves (the workgroup's rows share the
+// sequence and group: no integer division per row), else (ceil(rows / kWaves)).
 // VEC: rows start 16-byte aligned (nb % 4 == 0), so each lane fetches 4 consecutive
 // scores per load; the row is then re-distributed through LDS so that lane l holds
 // blocks l, l + 64, ... (the layout the ascending-id compaction below relies on).
@@ -207,18 +262,26 @@ template <bool VEC>
 __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const float* __restrict__ scores,
                                                                   int32_t* __restrict__ sel) {
   __shared__ __attribute__((aligned(16))) uint32_t s_buf[kWaves][2 * kCap];  // row staging / candidates
-  uint32_t* const s_ord_w = s_buf[threadIdx.x >> 6];
+  float* const s_f = reinterpret_cast<float*>(s_buf[threadIdx.x >> 6]);
   int32_t* const s_id_w = reinterpret_cast<int32_t*>(s_buf[threadIdx.x >> 6] + kCap);
   // the wave index is uniform: the row's index arithmetic runs on the scalar unit
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
-  if (row >= rows) return;
-  // rows < 2^32 (checked at launch): 32-bit division
-  const uint32_t r32 = (uint32_t)row;
-  const int t = (int)(r32 % (uint32_t)D.T);
-  const int bt = (seq_pos0(D, (int)(r32 / ((uint32_t)D.Hkv * (uint32_t)D.T))) + t) / D.B;
+  int t, sg;
+  if (D.T >= kWaves) {
+    t = (int)blockIdx.x * kWaves + wave;
+    sg = (int)blockIdx.y;
+    if (t >= D.T) return;
+  } else {
+    // rows < 2^32 (checked at launch): 32-bit division
+    const int64_t r = (int64_t)blockIdx.x * kWaves + wave;
+    if (r >= (int64_t)D.S * D.Hkv * D.T) return;
+    t = (int)((uint32_t)r % (uint32_t)D.T);
+    sg = (int)((uint32_t)r / (uint32_t)D.T);
+  }
+  const int64_t row = (int64_t)sg * D.T + t;
+  const int p0 = D.kv_lens != nullptr ? seq_pos0(D, sg / D.Hkv) : D.pos0;
+  const int bt = (p0 + t) >> 7;  // blocks of 128 positions
   const int k = D.k;
   int32_t* out = sel + row * k;
   const int n = bt;        // eligible blocks other than the own one: 0 .. bt-1
@@ -237,14 +300,11 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
     // as IEEE floats (the same order as ord_key, -0 == +0 included); only the lane
     // maxima and the candidates are mapped to ord_key for the bitwise searches.
     // Elements at n and beyond are -inf.
-    float* const s_f = reinterpret_cast<float*>(s_ord_w);  // row staging: the whole candidate buffer
-    const int ni = (n + 63) >> 6;                           // 64-element segments holding the row
     float o[kRegPerLane];
     if (VEC) {
       static_assert(2 * kCap >= 64 * kRegPerLane, "row staging fits the candidate buffer");
       // every load is issued before the first store, none under a branch: out-of-row
-      // lanes re-read the row's first four scores (in bounds) and store them past the
-      // row's end, where the -inf tail below or nothing reads them
+      // lanes re-read the row's first four scores (in bounds) and store -inf instead
       float4 x[kRegPerLane / 4];
 #pragma unroll
       for (int i = 0; i < kRegPerLane / 4; ++i) {
@@ -252,12 +312,16 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
         x[i] = *reinterpret_cast<const float4*>(sc + (c < n ? c : 0));
       }
 #pragma unroll
-      for (int i = 0; i < kRegPerLane / 4; ++i) *reinterpret_cast<float4*>(&s_f[i * 256 + 4 * lane]) = x[i];
+      for (int i = 0; i < kRegPerLane / 4; ++i) {
+        const int c = i * 256 + 4 * lane;
+        if (!(c < n)) x[i] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        *reinterpret_cast<float4*>(&s_f[c]) = x[i];
+      }
       wave_lds_sync();
-      if (n + lane < ni * 64) s_f[n + lane] = -INFINITY;  // tail of the last segment
+      if (lane < ((4 - (n & 3)) & 3)) s_f[n + lane] = -INFINITY;  // the row's last, partial float4
       wave_lds_sync();
 #pragma unroll
-      for (int i = 0; i < kRegPerLane; ++i) o[i] = i < ni ? s_f[i * 64 + lane] : -INFINITY;
+      for (int i = 0; i < kRegPerLane; ++i) o[i] = s_f[i * 64 + lane];
       wave_lds_sync();  // the staging area takes the candidates next
     } else {
 #pragma unroll
@@ -267,119 +331,97 @@ __global__ void __launch_bounds__(kWaves * 64) block_topk_kernel(Dims D, const f
       }
 #pragma unroll
       for (int i = 0; i < kRegPerLane; ++i)
-        if (!(i < ni && i * 64 + lane < n)) o[i] = -INFINITY;
+        if (!(i * 64 + lane < n)) o[i] = -INFINITY;
     }
     float lmf = o[0];
 #pragma unroll
     for (int i = 1; i < kRegPerLane; ++i) lmf = fmaxf(lmf, o[i]);
     // lanes past the row's end hold no element; the others number min(n, 64) > need
-    const uint32_t t1 = lane_kth(ord_key(lmf), lane < n, need);
+    const bool live = lane < n;
+    const uint32_t lk = ord_key(lmf);
+    uint32_t hi, lo;
+    wave_umax_umin(live ? lk : 0u, live ? lk : 0xFFFFFFFFu, hi, lo);
+    const uint32_t t1 = lane_kth_in(lk, live, need, hi, lo);
     const float t1f = ord_inv(t1);
-    if (t1f > -INFINITY) {  // otherwise -inf scores reach the threshold: generic path below
+    if (t1f > -INFINITY) {  // otherwise -inf (or NaN) scores reach the threshold: the row from memory
       // candidates (value >= t1) compacted in ascending id order; -inf padding never passes
       int C = 0;
 #pragma unroll
-      for (int i = 0; i < kRegPerLane; ++i) {
-        if (i < ni) {
-          const bool f = o[i] >= t1f;
-          const uint64_t m = __ballot(f);
-          if (m != 0ull) {
-            const int p = C + lanes_below(m);
-            if (f && p < kCap) {
-              s_f[p] = o[i];
-              s_id_w[p] = i * 64 + lane;
-            }
-            C += __popcll(m);
-          }
-        }
-      }
-      if (C <= 64) {
-        const bool have = lane < C;
-        pick_from_lanes(have ? ord_key(s_f[lane]) : 0u, have ? s_id_w[lane] : 0, have, lane, need, out);
-        if (lane == 0) out[need] = bt;
-        return;
-      }
-      if (C <= kCap) {
-        LdsFloatSrc src{s_f, s_id_w, C};
-        select_and_write(src, lane, need, out);
-        if (lane == 0) out[need] = bt;
-        return;
-      }
+      for (int i = 0; i < kRegPerLane; ++i) append_candidates(o[i] >= t1f, o[i], i * 64 + lane, lane, s_f, s_id_w, C);
+      select_candidates(s_f, s_id_w, C, sc, n, lane, need, hi, t1, out);
+    } else {
+      RowSrc src{sc, n};
+      select_and_write(src, lane, need, out);
     }
+    if (lane == 0) out[need] = bt;
+    return;
+  }
+  // A. lane maxima over a share of the row (any split works: only the maxima matter),
+  // in the float domain; whole chunks with four loads in flight per lane, then the rest
+  float lmf = -INFINITY;
+  if (VEC) {
+    constexpr int kU = 4;
+    int c0 = 0;
+    for (; c0 + kU * 256 <= n; c0 += kU * 256) {
+      float4 x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) x[u] = *reinterpret_cast<const float4*>(sc + c0 + u * 256 + 4 * lane);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) lmf = fmaxf(lmf, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
+    }
+    for (; c0 < n; c0 += 256) {
+      const int c = c0 + 4 * lane;  // c < n keeps c + 3 < nb (rows are a multiple of 4 long)
+      const float4 x = *reinterpret_cast<const float4*>(sc + (c < n ? c : 0));
+      if (c < n) lmf = fmaxf(lmf, x.x);
+      if (c + 1 < n) lmf = fmaxf(lmf, x.y);
+      if (c + 2 < n) lmf = fmaxf(lmf, x.z);
+      if (c + 3 < n) lmf = fmaxf(lmf, x.w);
+    }
+  } else {
+    constexpr int kU = 4;
+    int i0 = 0;
+    for (; i0 + kU * 64 <= n; i0 += kU * 64) {
+      float x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) x[u] = sc[i0 + u * 64 + lane];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) lmf = fmaxf(lmf, x[u]);
+    }
+    for (; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const float x = sc[i < n ? i : 0];
+      if (i < n) lmf = fmaxf(lmf, x);
+    }
+  }
+  // B. t1 <= the need-th largest lane maximum (every lane holds elements: n > 1024);
+  // scores >= t1 compacted into LDS in ascending id order, eight loads in flight per lane
+  const uint32_t lk = ord_key(lmf);
+  uint32_t hi, lo;
+  wave_umax_umin(lk, lk, hi, lo);
+  const uint32_t t1 = lane_kth_in(lk, true, need, hi, lo);
+  const float t1f = ord_inv(t1);
+  if (!(t1f > -INFINITY)) {  // -inf (or NaN) scores reach the threshold: the row from memory
     RowSrc src{sc, n};
     select_and_write(src, lane, need, out);
     if (lane == 0) out[need] = bt;
     return;
   }
-  // A. lane maxima over a share of the row (any split works: only the maxima matter);
-  // four loads in flight per lane
-  constexpr int kU = 4;
-  uint32_t lmax = 0;
-  if (VEC) {
-    for (int c0 = 4 * lane; c0 < n; c0 += kU * 256) {
-      float4 x[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int c = c0 + u * 256;  // c < n keeps c + 3 < nb (rows are a multiple of 4 long)
-        x[u] = *reinterpret_cast<const float4*>(sc + (c < n ? c : 0));
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int c = c0 + u * 256;
-        const uint32_t a = c < n ? ord_key(x[u].x) : 0u;
-        const uint32_t b = c + 1 < n ? ord_key(x[u].y) : 0u;
-        const uint32_t d = c + 2 < n ? ord_key(x[u].z) : 0u;
-        const uint32_t e = c + 3 < n ? ord_key(x[u].w) : 0u;
-        lmax = max(max(lmax, a), max(b, max(d, e)));
-      }
-    }
-  } else {
-    for (int i0 = lane; i0 < n; i0 += kU * 64) {
-      uint32_t o[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) o[u] = ord_key(sc[i0 + u * 64 < n ? i0 + u * 64 : 0]);
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-        if (i0 + u * 64 >= n) o[u] = 0u;
-#pragma unroll
-      for (int u = 0; u < kU; ++u) lmax = max(lmax, o[u]);
-    }
-  }
-  // B. tau1 <= the need-th largest lane maximum (every lane holds elements: n > 1024);
-  // compact ord >= tau1 into LDS (ascending id), eight loads in flight per lane
-  const uint32_t tau1 = lane_kth(lmax, true, need);
   constexpr int kV = 8;
   int C = 0;
-  for (int b0 = 0; b0 < n; b0 += kV * 64) {
-    uint32_t o[kV];
+  int b0 = 0;
+  for (; b0 + kV * 64 <= n; b0 += kV * 64) {
+    float o[kV];
 #pragma unroll
-    for (int u = 0; u < kV; ++u) {
-      const int i = b0 + u * 64 + lane;
-      o[u] = ord_key(sc[i < n ? i : 0]);  // out-of-row lanes are masked below
-    }
+    for (int u = 0; u < kV; ++u) o[u] = sc[b0 + u * 64 + lane];
 #pragma unroll
-    for (int u = 0; u < kV; ++u) {
-      const int i = b0 + u * 64 + lane;
-      const bool f = i < n && o[u] >= tau1;
-      const uint64_t m = __ballot(f);
-      const int p = C + lanes_below(m);
-      if (f && p < kCap) {
-        s_ord_w[p] = o[u];
-        s_id_w[p] = i;
-      }
-      C += __popcll(m);
-    }
+    for (int u = 0; u < kV; ++u) append_candidates(o[u] >= t1f, o[u], b0 + u * 64 + lane, lane, s_f, s_id_w, C);
   }
-  if (C <= 64) {
-    const bool have = lane < C;
-    pick_from_lanes(have ? s_ord_w[lane] : 0u, have ? s_id_w[lane] : 0, have, lane, need, out);
-  } else if (C <= kCap) {
-    LdsSrc src{s_ord_w, s_id_w, C};
-    select_and_write(src, lane, need, out);
-  } else {
-    RowSrc src{sc, n};
-    select_and_write(src, lane, need, out);
+  for (; b0 < n; b0 += 64) {
+    const int i = b0 + lane;
+    const float v = sc[i < n ? i : 0];
+    append_candidates(i < n && v >= t1f, v, i, lane, s_f, s_id_w, C);
   }
+  select_candidates(s_f, s_id_w, C, sc, n, lane, need, hi, t1, out);
   if (lane == 0) out[need] = bt;  // the own block is the largest id of the row
 }
 
@@ -573,10 +615,13 @@ hipError_t launch_block_topk(const Dims& D, const float* scores, int32_t* sel, h
       hipLaunchKernelGGL(block_topk_long<false>, dim3((unsigned)rows), dim3(kLongThreads), 0, st, D, scores, sel);
     return hipGetLastError();
   }
+  // S * H_kv <= 65535 (checked with the problem)
+  const dim3 g2 = D.T >= kWaves ? dim3((unsigned)((D.T + kWaves - 1) / kWaves), (unsigned)(D.S * D.Hkv))
+                                : dim3((unsigned)grid);
   if (vec)
-    hipLaunchKernelGGL(block_topk_kernel<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0, st, D, scores, sel);
+    hipLaunchKernelGGL(block_topk_kernel<true>, g2, dim3(kWaves * 64), 0, st, D, scores, sel);
   else
-    hipLaunchKernelGGL(block_topk_kernel<false>, dim3((unsigned)grid), dim3(kWaves * 64), 0, st, D, scores, sel);
+    hipLaunchKernelGGL(block_topk_kernel<false>, g2, dim3(kWaves * 64), 0, st, D, scores, sel);
   return hipGetLastError();
 }
 

@@ -222,13 +222,22 @@ def _topk_case(scores_np, T, N, k):
 
 @pytest.mark.parametrize("kind", ["all_equal", "signed_zero", "few_values", "neg_inf_and_huge",
                                   "long_all_equal", "long_random", "long_ties_at_threshold",
-                                  "few_values_odd_nb", "long_random_odd_nb", "ties_at_threshold_odd_nb"])
+                                  "few_values_odd_nb", "long_random_odd_nb", "ties_at_threshold_odd_nb",
+                                  "mid_random", "mid_all_equal", "mid_ties_at_threshold", "mid_neg_inf_and_huge",
+                                  "mid_random_odd_nb"])
 @pytest.mark.parametrize("k", [1, 2, 16, 64])
 def test_topk_adversarial_rows(kind, k):
+    """Rows of up to 300 blocks (held in registers), 130 rows of 8192 blocks (a workgroup
+    per row) and 16,500 rows of up to 1100 blocks (more rows than the workgroup-per-row
+    kernel takes: rows past 1024 blocks stream the row twice, the rest stay in registers,
+    in one launch)."""
     require_gpu()
     rng = np.random.default_rng(zlib.crc32(kind.encode()) * 100 + k)
     if kind.startswith("long"):
         T, N = 130, 8192 * 128
+    elif kind.startswith("mid"):
+        T, N = 16500, 1100 * 128
+        kind = kind[len("mid_"):]
     else:
         T, N = 300, 300 * 128
     if kind.endswith("_odd_nb"):  # nb % 4 != 0: rows are not 16-byte aligned (scalar loads)
@@ -243,7 +252,7 @@ def test_topk_adversarial_rows(kind, k):
         sc = rng.integers(0, 3, size=(T, nb)).astype(np.float64)
     elif kind == "neg_inf_and_huge":
         sc = rng.choice([-np.inf, np.inf, -3e38, 3e38, 1e-45, -1e-45], size=(T, nb))
-    elif kind == "long_random":
+    elif kind in ("random", "long_random"):
         sc = rng.standard_normal((T, nb))
     else:  # many ties exactly at the k-th value
         sc = rng.standard_normal((T, nb)) - 10
