@@ -79,6 +79,61 @@ __device__ __forceinline__ void wave_umax_umin(uint32_t a, uint32_t b, uint32_t&
   mn = __builtin_amdgcn_readlane(b, 63);
 }
 
+constexpr int kQuadMirror = 0x1B;  // quad_perm [3,2,1,0]
+
+// Compare-exchange between the lane pairs of a DPP pattern: lanes with keep_max take the
+// larger key, their partners the smaller.
+template <int CTRL>
+__device__ __forceinline__ uint32_t cmpx(uint32_t x, bool keep_max) {
+  const uint32_t p = dpp<CTRL>(x);
+  return keep_max ? max(x, p) : min(x, p);
+}
+
+// Rotations within rows of 16 lanes: with row_ror:n lane i reads lane (i - n) mod 16.
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+constexpr int kRowRor12 = 0x12C;
+
+// Compare-exchange with the lane at distance 4 inside the row (lane i ^ 4).
+__device__ __forceinline__ uint32_t cmpx4(uint32_t x, bool keep_max, bool bit2) {
+  const uint32_t up = dpp<kRowRor12>(x);  // lane i + 4 (mod 16)
+  const uint32_t dn = dpp<kRowRor4>(x);   // lane i - 4 (mod 16)
+  const uint32_t p = bit2 ? dn : up;
+  return keep_max ? max(x, p) : min(x, p);
+}
+
+// The key of lane i ^ 16 (the neighbouring row, same position).  permlane16_swap trades
+// the odd rows of its first operand for the even rows of its second; with both operands
+// x, one result holds x and the other the neighbouring row's key, whichever is which.
+__device__ __forceinline__ uint32_t row_partner(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (uint32_t)r[0] ^ (uint32_t)r[1] ^ x;
+}
+
+// The need-th largest (1 <= need <= 16) of the keys in lanes 0..31.  Each row of 16
+// lanes is sorted in descending lane order (bitonic merges in the flip form: quads, then
+// halves, then the row); the 16 largest of rows 0 and 1 are the pairwise maxima of row 0
+// against row 1 reversed, a bitonic sequence that four half-cleaner steps sort.
+__device__ __forceinline__ uint32_t kth_of_32(uint32_t x, int lane, int need) {
+  const bool b0 = (lane & 1) == 0, b1 = (lane & 2) == 0, b2 = (lane & 4) == 0, b3 = (lane & 8) == 0;
+  x = cmpx<kQuadSwap1>(x, b0);
+  x = cmpx<kQuadMirror>(x, b1);
+  x = cmpx<kQuadSwap1>(x, b0);
+  x = cmpx<kHalfRowMirror>(x, b2);
+  x = cmpx<kQuadSwap2>(x, b1);
+  x = cmpx<kQuadSwap1>(x, b0);
+  x = cmpx<kRowMirror>(x, b3);
+  x = cmpx4(x, b2, !b2);
+  x = cmpx<kQuadSwap2>(x, b1);
+  x = cmpx<kQuadSwap1>(x, b0);
+  x = max(x, row_partner(dpp<kRowMirror>(x)));  // row 0: lane i against lane 31 - i
+  x = cmpx<kRowRor8>(x, b3);                     // lane i ^ 8
+  x = cmpx4(x, b2, !b2);
+  x = cmpx<kQuadSwap2>(x, b1);
+  x = cmpx<kQuadSwap1>(x, b0);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, need - 1);
+}
+
 // One key per lane (`live` lanes only; at least `want` of them), every live key in
 // [lo, hi].  Returns x with #{live keys >= x} >= want and x <= the want-th largest live
 // key: either that key itself, or a prefix of it that exactly `want` live keys reach
@@ -186,10 +241,11 @@ __device__ __forceinline__ void select_and_write(const Src& src, int lane, int n
 // candidate key in [lo, hi]: writes the `need` best by (ord desc, id asc) to
 // out[0 .. need-1] in ascending id order.
 __device__ __forceinline__ void pick_from_lanes_in(uint32_t co, int32_t cid, bool have, int lane, int need,
-                                                   int32_t* out, uint32_t hi, uint32_t lo) {
-  // when the search stops early exactly `need` candidates are >= tau and every one
-  // equal to tau is taken below
-  const uint32_t tau = lane_kth_in(co, have, need, hi, lo);
+                                                   int32_t* out, uint32_t hi, uint32_t lo, bool small) {
+  // small (at most 32 candidates, need <= 16): tau is the need-th largest key, from a
+  // sorting network; otherwise a bitwise search, which may stop at a prefix that exactly
+  // `need` candidates reach (every candidate equal to tau is then taken below)
+  const uint32_t tau = small ? kth_of_32(have ? co : 0u, lane, need) : lane_kth_in(co, have, need, hi, lo);
   const int c_gt = __popcll(__ballot(have && co > tau));
   const uint64_t eqm = __ballot(have && co == tau);
   const int need_eq = need - c_gt;
@@ -203,11 +259,13 @@ __device__ __forceinline__ void pick_from_lanes_in(uint32_t co, int32_t cid, boo
   if (f && at < need) out[at] = cid;
 }
 
-__device__ __forceinline__ void pick_from_lanes(uint32_t co, int32_t cid, bool have, int lane, int need,
+// The same for C candidates with no known key bounds.
+__device__ __forceinline__ void pick_from_lanes(uint32_t co, int32_t cid, bool have, int lane, int need, int C,
                                                 int32_t* out) {
-  uint32_t hi, lo;
-  wave_umax_umin(have ? co : 0u, have ? co : 0xFFFFFFFFu, hi, lo);
-  pick_from_lanes_in(co, cid, have, lane, need, out, hi, lo);
+  uint32_t hi = 0u, lo = 0u;
+  const bool small = C <= 32 && need <= 16;
+  if (!small) wave_umax_umin(have ? co : 0u, have ? co : 0xFFFFFFFFu, hi, lo);
+  pick_from_lanes_in(co, cid, have, lane, need, out, hi, lo, small);
 }
 
 // Completes this wave's earlier LDS accesses before its later ones (lanes exchange data
@@ -227,7 +285,8 @@ __device__ __forceinline__ void select_candidates(const float* s_f, const int32_
                                                   int32_t* out) {
   if (C <= 64) {
     const bool have = lane < C;
-    pick_from_lanes_in(have ? ord_key(s_f[lane]) : 0u, have ? s_id[lane] : 0, have, lane, need, out, hi, t1);
+    pick_from_lanes_in(have ? ord_key(s_f[lane]) : 0u, have ? s_id[lane] : 0, have, lane, need, out, hi, t1,
+                       C <= 32 && need <= 16);
   } else if (C <= kCap) {
     LdsFloatSrc src{s_f, s_id, C};
     select_and_write(src, lane, need, out);
@@ -536,7 +595,7 @@ __global__ void __launch_bounds__(kLongThreads) block_topk_long(Dims D, const fl
     select_and_write(src, lane, need, out);
   } else if (C <= 64) {
     const bool have = lane < C;
-    pick_from_lanes(have ? s_ord[lane] : 0u, have ? s_id[lane] : 0, have, lane, need, out);
+    pick_from_lanes(have ? s_ord[lane] : 0u, have ? s_id[lane] : 0, have, lane, need, C, out);
   } else {
     // 3. at least `need` candidates (every selected block is one), in registers
     const int nu = (C + 63) >> 6;
