@@ -100,6 +100,34 @@ __global__ void __launch_bounds__(256) zero_kernel(float* __restrict__ p, int64_
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
 }
 
+// dQ = scale * dS K for head dims [32 w, 32 w + 32) of one sub-chunk (dS M-row major in
+// LDS, K row-major), written to the bf16 dQ tile; two accumulators (even and odd key
+// steps) so that consecutive matrix instructions do not wait on each other.
+template <int DH>
+__device__ __forceinline__ void dq_tile(const unsigned char* ds, const unsigned char* kr, unsigned char* dqt, int w,
+                                        int lane, float scale) {
+  constexpr int SROW = kBlk * 2 + 16, KROW = DH * 2 + 16, QROW = DH * 2 + 16;
+  const int h = lane >> 5, nl = lane & 31;
+  f32x16 qa = f32x16{}, qb = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < kBlk / 16; ++ks) {
+    const bf16x8 as = *reinterpret_cast<const bf16x8*>(&ds[nl * SROW + (16 * ks + 8 * h) * 2]);
+    // keys 16 ks + 8 h + {0..7}, the order of the dS row read above
+    const bf16x8 bk = tr_operand(kr, KROW, 16 * ks + 8 * h, 16 * ks + 8 * h + 4, 32 * w, lane);
+    if (ks % 2 == 0)
+      qa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bk, qa, 0, 0, 0);
+    else
+      qb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bk, qb, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const uint32_t wq = cvt_bf16x2((qa[r] + qb[r]) * scale, (qa[r + 1] + qb[r + 1]) * scale);
+    unsigned char* d0 = &dqt[acc_row(r, h) * QROW + (32 * w + nl) * 2];
+    *reinterpret_cast<uint16_t*>(d0) = (uint16_t)(wq & 0xFFFFu);
+    *reinterpret_cast<uint16_t*>(d0 + QROW) = (uint16_t)(wq >> 16);
+  }
+}
+
 template <int DH, int G>
 __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
@@ -174,14 +202,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
   // registers while the current one computes.
   constexpr int NP = 32 * CPR / kThreads;
   static_assert(NP >= 1 && 32 * CPR == NP * kThreads, "whole pieces per thread");
-  uint4 nq[NP], ng[NP];
-  // Every load is unconditional (a row past the list reads row 0 and is zeroed after the
-  // load), and so are the dQ stores below: with no memory operation under a branch the
-  // compiler counts them exactly, and the loop head waits only for the previous
-  // iteration's loads, not for its dQ stores.
-  // (the zeroing of rows past the list happens where the data is stored to LDS, so that
-  // no instruction right after the loads waits for them)
-  auto fetch = [&](int m0n) {
+  // Two sub-chunks ahead are in flight (two register sets, the loop unrolled by two): one
+  // sub-chunk's gathered Q and dO (16 KB per item at d = 128) per round trip was too little
+  // to cover the gathers' latency.  Every load is unconditional (a row past the list reads
+  // row 0 and is zeroed where it is stored to LDS), and so are the dQ stores below: with
+  // no memory operation under a branch the compiler counts them exactly.
+  struct Pre {
+    uint4 q[NP], g[NP];
+    float lse, drow;  // per-M-row values (threads 0..31 store them); lse is scaled when stored
+    int t, slot;
+  };
+  auto fetch = [&](Pre& pr, int m0n) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int c = threadIdx.x + kThreads * u;
@@ -189,25 +220,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
       const int mc = mr < mrows ? mr : 0;
       const int t = L.rowt[mc / G];
       const int64_t off = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mc % G) * DH + col * 8;
-      nq[u] = *reinterpret_cast<const uint4*>(q + off);
-      ng[u] = *reinterpret_cast<const uint4*>(dout + off);
+      pr.q[u] = *reinterpret_cast<const uint4*>(q + off);
+      pr.g[u] = *reinterpret_cast<const uint4*>(dout + off);
     }
-  };
-  // per-M-row values of the next sub-chunk (threads 0..31), fetched with its Q and dO;
-  // lse is scaled only when it is stored (the load's result is not needed before)
-  float n_lse = 0.0f, n_drow = 0.0f;
-  int n_t = 0, n_slot = 0;
-  auto fetch_meta = [&](int m0n) {  // every thread (no branch); threads 0..31 store them
-    const int mr = m0n + (int)(threadIdx.x & 31);
+    const int mr = m0n + (int)(threadIdx.x & 31);  // every thread (no branch)
     const int mc = mr < mrows ? mr : 0;
-    n_t = L.rowt[mc / G];
-    n_slot = L.rslot[mc / G];
-    const int64_t hr = ((int64_t)s * D.T + n_t) * D.H + (int64_t)g * G + mc % G;
-    n_lse = lse[hr];
-    n_drow = drow[hr];
+    pr.t = L.rowt[mc / G];
+    pr.slot = L.rslot[mc / G];
+    const int64_t hr = ((int64_t)s * D.T + pr.t) * D.H + (int64_t)g * G + mc % G;
+    pr.lse = lse[hr];
+    pr.drow = drow[hr];
   };
-  fetch(0);
-  fetch_meta(0);
+  Pre pa, pb;
+  fetch(pa, 0);
+  fetch(pb, 32);  // past the last sub-chunk: row-0 loads, never used
 
   // dQ of a sub-chunk goes to an LDS tile and is stored at the start of the next
   // iteration, before that iteration's prefetch: the loads waited for at a loop head are
@@ -225,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
     }
   };
 
-  for (int m0 = 0; m0 < mrows; m0 += 32) {
+  auto step = [&](Pre& pr, int m0) __attribute__((always_inline)) {
     const int par = (m0 >> 5) & 1;
     __syncthreads();  // previous sub-chunk's buffers are free (and the staging is complete)
     store_dq(par ^ 1);  // the previous sub-chunk's dQ
@@ -235,20 +261,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
       const int c = threadIdx.x + kThreads * u;
       const int m = c % 32, col = c / 32;
       const bool ok = m0 + m < mrows;
-      *reinterpret_cast<uint4*>(&L.qs[m * L_::QROW + col * 16]) = ok ? nq[u] : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(&L.dos[m * L_::QROW + col * 16]) = ok ? ng[u] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&L.qs[m * L_::QROW + col * 16]) = ok ? pr.q[u] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&L.dos[m * L_::QROW + col * 16]) = ok ? pr.g[u] : make_uint4(0u, 0u, 0u, 0u);
     }
     if (threadIdx.x < 32) {
       const int m = threadIdx.x, mr = m0 + m;
       const bool ok = mr < mrows;
-      const int64_t pidx = (((int64_t)s * D.T + n_t) * D.Hkv + g) * D.k + n_slot;
-      L.lse2[m] = ok ? n_lse * kLog2e : INFINITY;  // P = 0 for an M-row past the list
-      L.drow[m] = ok ? n_drow : 0.0f;
-      L.pos[m] = ok ? D.pos0 + n_t : -1;
+      const int64_t pidx = (((int64_t)s * D.T + pr.t) * D.Hkv + g) * D.k + pr.slot;
+      L.lse2[m] = ok ? pr.lse * kLog2e : INFINITY;  // P = 0 for an M-row past the list
+      L.drow[m] = ok ? pr.drow : 0.0f;
+      L.pos[m] = ok ? D.pos0 + pr.t : -1;
       L.dqoff[par][m] = ok ? (pidx * G + mr % G) * DH : dq_trash;
     }
-    fetch(m0 + 32);  // past the last sub-chunk: row-0 loads, never used
-    fetch_meta(m0 + 32);
+    fetch(pr, m0 + 64);  // past the last sub-chunk: row-0 loads, never used
     __syncthreads();
 
     // ---- S = Q K^T and dP = dO V^T for this wave's 32 keys
@@ -308,30 +333,34 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
         dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[pp], dkt[dt], 0, 0, 0);
       }
     }
-    // ---- dS to LDS (M-row major) for dQ
+    // ---- dS to LDS (M-row major) for dQ: each packed pair holds M-rows acc_row(r, h) and
+    // acc_row(r, h) + 1 (r even)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      *reinterpret_cast<uint16_t*>(&L.ds[acc_row(r, h) * L_::SROW + (32 * wave + nl) * 2]) =
-          (uint16_t)(cvt_bf16x2(dsv[r], 0.0f) & 0xFFFFu);
+    for (int pp = 0; pp < 2; ++pp) {
+      const uint4 wv = __builtin_bit_cast(uint4, sb[pp]);
+      const uint32_t wsd[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        unsigned char* d0 = &L.ds[acc_row(8 * pp + 2 * x, h) * L_::SROW + (32 * wave + nl) * 2];
+        *reinterpret_cast<uint16_t*>(d0) = (uint16_t)(wsd[x] & 0xFFFFu);
+        *reinterpret_cast<uint16_t*>(d0 + L_::SROW) = (uint16_t)(wsd[x] >> 16);
+      }
+    }
     __syncthreads();
     // ---- dQ = scale * dS K for head dims [32 wave, 32 wave + 32)
     if (wave < DT) {
-      f32x16 qacc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < kBlk / 16; ++ks) {
-        const bf16x8 as = *reinterpret_cast<const bf16x8*>(&L.ds[nl * L_::SROW + (16 * ks + 8 * h) * 2]);
-        // keys 16 ks + 8 h + {0..7}, the order of the dS row read above
-        const bf16x8 bk = tr_operand(L.kr, L_::KROW, 16 * ks + 8 * h, 16 * ks + 8 * h + 4, 32 * wave, lane);
-        qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bk, qacc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        *reinterpret_cast<uint16_t*>(&L.dqt[acc_row(r, h) * L_::QROW + (32 * wave + nl) * 2]) =
-            f32_to_bf16(qacc[r] * D.scale);
+      dq_tile<DH>(L.ds, L.kr, L.dqt, wave, lane, D.scale);
     }
+  };
+  // Sub-chunks in pairs, the second one unconditional (past the list it is all empty
+  // M-rows: P = 0, nothing accumulates, its dQ goes to the scratch row), so that the loop
+  // body is straight-line and each loop head waits for one set of loads only.
+  for (int m0 = 0; m0 < mrows; m0 += 64) {
+    step(pa, m0);
+    step(pb, m0 + 32);
   }
   __syncthreads();
-  store_dq(((mrows - 1) >> 5) & 1);  // the last sub-chunk's dQ
+  store_dq(1);  // the last (odd) sub-chunk's dQ
 
   // ---- dK, dV of the block: through LDS (row-major fp32 over the K / V staging area) so
   // that the atomic adds of a wave cover contiguous head dims
