@@ -101,23 +101,22 @@ __global__ void __launch_bounds__(256) zero_kernel(float* __restrict__ p, int64_
 }
 
 // dQ = scale * dS K for head dims [32 w, 32 w + 32) of one sub-chunk (dS M-row major in
-// LDS, K row-major), written to the bf16 dQ tile; two accumulators (even and odd key
-// steps) so that consecutive matrix instructions do not wait on each other.
+// LDS, the K^T operands in registers), written to the bf16 dQ tile; two accumulators (even
+// and odd key steps) so that consecutive matrix instructions do not wait on each other.
 template <int DH>
-__device__ __forceinline__ void dq_tile(const unsigned char* ds, const unsigned char* kr, unsigned char* dqt, int w,
-                                        int lane, float scale) {
-  constexpr int SROW = kBlk * 2 + 16, KROW = DH * 2 + 16, QROW = DH * 2 + 16;
+__device__ __forceinline__ void dq_tile(const unsigned char* ds, const bf16x8 (&ktop)[kBlk / 16], unsigned char* dqt,
+                                        int w, int lane, float scale) {
+  constexpr int SROW = kBlk * 2 + 16, QROW = DH * 2 + 16;
   const int h = lane >> 5, nl = lane & 31;
   f32x16 qa = f32x16{}, qb = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < kBlk / 16; ++ks) {
+    // keys 16 ks + 8 h + {0..7}: the order of K^T operand ks
     const bf16x8 as = *reinterpret_cast<const bf16x8*>(&ds[nl * SROW + (16 * ks + 8 * h) * 2]);
-    // keys 16 ks + 8 h + {0..7}, the order of the dS row read above
-    const bf16x8 bk = tr_operand(kr, KROW, 16 * ks + 8 * h, 16 * ks + 8 * h + 4, 32 * w, lane);
     if (ks % 2 == 0)
-      qa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bk, qa, 0, 0, 0);
+      qa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, ktop[ks], qa, 0, 0, 0);
     else
-      qb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bk, qb, 0, 0, 0);
+      qb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, ktop[ks], qb, 0, 0, 0);
   }
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
@@ -195,6 +194,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
   const int64_t dq_trash = (int64_t)D.S * D.T * D.Hkv * D.k * G * DH;
   const bool need_mask = first_pos < j0 + kBlk - 1;
   const int key = j0 + 32 * wave + nl;                // this lane's key
+  // The block's operands that do not change over the item stay in registers (read from
+  // LDS once): K and V rows of this wave's 32 keys (B operands of S and dP, k-step ks =
+  // head dims 16 ks + 8 h + {0..7}) and, for dQ, K^T for head dims [32 wave, +32) (k-step
+  // ks = keys 16 ks + 8 h + {0..7}).  Every sub-chunk then reads only its Q, dO and dS.
+  bf16x8 kop[KS], vop[KS], ktop[kBlk / 16];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kop[ks] = *reinterpret_cast<const bf16x8*>(&L.kr[(32 * wave + nl) * L_::KROW + (16 * ks + 8 * h) * 2]);
+    vop[ks] = *reinterpret_cast<const bf16x8*>(&L.vr[(32 * wave + nl) * L_::KROW + (16 * ks + 8 * h) * 2]);
+  }
+#pragma unroll
+  for (int ks = 0; ks < kBlk / 16; ++ks)
+    ktop[ks] = wave < DT ? tr_operand(L.kr, L_::KROW, 16 * ks + 8 * h, 16 * ks + 8 * h + 4, 32 * wave, lane)
+                         : bf16x8{};
 
   // Q and dO pieces of a sub-chunk: piece c -> M-row c % 32, 16-byte column c / 32 (lanes
   // of a wave take consecutive M-rows, so the transposed 2-byte LDS writes of one
@@ -281,11 +294,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&L.qs[nl * L_::QROW + (16 * ks + 8 * h) * 2]);
-      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&L.kr[(32 * wave + nl) * L_::KROW + (16 * ks + 8 * h) * 2]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kop[ks], sacc, 0, 0, 0);
       const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&L.dos[nl * L_::QROW + (16 * ks + 8 * h) * 2]);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&L.vr[(32 * wave + nl) * L_::KROW + (16 * ks + 8 * h) * 2]);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, bv, pacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vop[ks], pacc, 0, 0, 0);
     }
     // ---- P, dS (registers r hold M-rows acc_row(r, h) of this lane's key)
     // per-M-row values of registers 4a .. 4a+3: M-rows 8a + 4h + {0..3}, one 16-byte read each
@@ -349,7 +360,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
     __syncthreads();
     // ---- dQ = scale * dS K for head dims [32 wave, 32 wave + 32)
     if (wave < DT) {
-      dq_tile<DH>(L.ds, L.kr, L.dqt, wave, lane, D.scale);
+      dq_tile<DH>(L.ds, ktop, L.dqt, wave, lane, D.scale);
     }
   };
   // Sub-chunks in pairs, the second one unconditional (past the list it is all empty
