@@ -56,7 +56,10 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 template <int DH>
 struct __attribute__((aligned(16))) BwdLds {
   static constexpr int KROW = DH * 2 + 16;    // K / V row-major, bytes
-  static constexpr int QROW = DH * 2 + 16;    // Q / dO row-major (32 M-rows)
+  // Q / dO row-major (32 M-rows): a row pitch of 20 banks (mod 64) keeps the 16-byte row
+  // reads conflict-free and spreads the transposed 8-byte reads (4 rows x 32 bytes per 16
+  // lanes) over at most two lanes per bank
+  static constexpr int QROW = DH * 2 + ((80 - DH * 2) % 256 + 256) % 256;
   static constexpr int SROW = kBlk * 2 + 16;  // dS row (one M-row over the block's keys)
   __attribute__((aligned(16))) unsigned char kr[kBlk * KROW];
   __attribute__((aligned(16))) unsigned char vr[kBlk * KROW];
@@ -106,7 +109,7 @@ __global__ void __launch_bounds__(256) zero_kernel(float* __restrict__ p, int64_
 template <int DH>
 __device__ __forceinline__ void dq_tile(const unsigned char* ds, const bf16x8 (&ktop)[kBlk / 16], unsigned char* dqt,
                                         int w, int lane, float scale) {
-  constexpr int SROW = kBlk * 2 + 16, QROW = DH * 2 + 16;
+  constexpr int SROW = BwdLds<DH>::SROW, QROW = BwdLds<DH>::QROW;
   const int h = lane >> 5, nl = lane & 31;
   f32x16 qa = f32x16{}, qb = f32x16{};
 #pragma unroll
