@@ -506,6 +506,7 @@ struct IdxBwdLds {
   static constexpr int ROW = DI * 2 + 16;
   __attribute__((aligned(16))) unsigned char k[kBlk * ROW];
   float dk[kBlk][DI + 1];
+  int rts[kRows];  // the item's rows, decoded once: query row t * 64 + slot (k <= 64)
 };
 
 // Arg-max of the causal block max-pool per (row, selected block) on the matrix cores, and
@@ -550,21 +551,36 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
         key < nvalid ? *reinterpret_cast<const uint4*>(kb + key * DI + col * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
   for (int i = threadIdx.x; i < kBlk * (DI + 1); i += kThreads) (&L.dk[0][0])[i] = 0.0f;
+  for (int r = threadIdx.x; r < w.z; r += kThreads) {
+    const int e = entries[w.y + r];
+    const int t = e / D.k;
+    L.rts[r] = t * 64 + (e - t * D.k);
+  }
   __syncthreads();
-  for (int r0 = wave * 32; r0 < w.z; r0 += kWaves * 32) {
-    const int r = r0 + nl;  // this lane's row of the item (both lane halves)
-    const bool ok = r < w.z;
-    int t = 0, slot = 0;
-    if (ok) {
-      const int e = entries[w.y + r];
-      t = e / D.k;
-      slot = e - t * D.k;
-    }
-    const int64_t qr = sg * D.T + t;  // (s, g, t)
-    bf16x8 bq[KS];
+  // A lane's row of one 32-row step (both lane halves): its index query, dscore and place,
+  // fetched one step ahead into one of two register sets (the loop is unrolled by two).
+  // Loads are unconditional: a lane past the item's rows reads the item's first row and
+  // writes nothing.
+  struct RowIn {
+    bf16x8 q[KS];
+    float gsc;
+    int t, slot;
+    bool ok;
+  };
+  auto fetch = [&](RowIn& x, int r0) __attribute__((always_inline)) {
+    const int r = r0 + nl;
+    x.ok = r < w.z;
+    const int rs = L.rts[x.ok ? r : 0];
+    x.t = rs >> 6;
+    x.slot = rs & 63;
+    const int64_t qr = sg * D.T + x.t;  // (s, g, t)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      bq[ks] = ok ? *reinterpret_cast<const bf16x8*>(q_idx + qr * DI + 16 * ks + 8 * h) : bf16x8{};
+    for (int ks = 0; ks < KS; ++ks) x.q[ks] = *reinterpret_cast<const bf16x8*>(q_idx + qr * DI + 16 * ks + 8 * h);
+    x.gsc = dscore[qr * D.k + x.slot];
+  };
+  constexpr int kStride = kWaves * 32;
+  auto body = [&](RowIn& x, int r0) __attribute__((always_inline)) {
+    const int64_t qr = sg * D.T + x.t;
     f32x16 acc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -572,12 +588,12 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&L.k[(kt * 32 + nl) * L_::ROW + (16 * ks + 8 * h) * 2]);
-        acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[ks], acc[kt], 0, 0, 0);
+        acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, x.q[ks], acc[kt], 0, 0, 0);
       }
     }
     // keys kk <= lim are inside the block and causal for the row (kk = 0 always is: the
     // block is one the row selected)
-    const int lim = min(nvalid - 1, D.pos0 + t - j0);
+    const int lim = min(nvalid - 1, D.pos0 + x.t - j0);
     float best = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -596,17 +612,25 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
       }
     idx = min(idx, __shfl_xor(idx, 32, 64));
     const int js = idx == 0x7FFFFFFF ? -1 : idx;
-    if (ok && h == 0) {
-      am[qr * D.k + slot] = js >= 0 ? j0 + js : -1;
-      if (argmax != nullptr) argmax[qr * D.k + slot] = js >= 0 ? j0 + js : -1;
+    if (x.ok && h == 0) {
+      am[qr * D.k + x.slot] = js >= 0 ? j0 + js : -1;
+      if (argmax != nullptr) argmax[qr * D.k + x.slot] = js >= 0 ? j0 + js : -1;
     }
-    if (ok && js >= 0) {
-      const float gsc = dscore[qr * D.k + slot];
+    if (x.ok && js >= 0) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) atomicAdd(&L.dk[js][16 * ks + 8 * h + i], gsc * (float)bq[ks][i]);
+        for (int i = 0; i < 8; ++i) atomicAdd(&L.dk[js][16 * ks + 8 * h + i], x.gsc * (float)x.q[ks][i]);
     }
+    fetch(x, r0 + 2 * kStride);
+  };
+  RowIn xa, xb;
+  fetch(xa, wave * 32);
+  fetch(xb, wave * 32 + kStride);
+  // steps in pairs, the second possibly past the item's rows (it then writes nothing)
+  for (int r0 = wave * 32; r0 < w.z; r0 += 2 * kStride) {
+    body(xa, r0);
+    body(xb, r0 + kStride);
   }
   __syncthreads();
   float* dst = dk_idx + (sg * D.N + j0) * DI;
