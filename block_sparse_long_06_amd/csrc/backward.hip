@@ -499,28 +499,37 @@ __global__ void __launch_bounds__(256) index_kl_kernel(Dims D, const float* __re
 }
 
 // One KV block's index keys in LDS (bf16 row-major, 16-byte row pad: the per-lane 16-byte
-// operand reads of a wave are bank-conflict free), plus the block's key-gradient
-// accumulator (fp32, one float of row pad).
+// operand reads of a wave are bank-conflict free), the item's rows, and for a round of RP
+// rows their index queries (row-major, the B operands of the key-gradient product) with
+// each row's arg-max key and split dscore (its A operands).
 template <int DI>
 struct IdxBwdLds {
   static constexpr int ROW = DI * 2 + 16;
+  static constexpr int RP = DI == 128 ? 128 : 256;  // rows per round
+  static constexpr int QP = DI * 2 + 16;             // query-row pitch
   __attribute__((aligned(16))) unsigned char k[kBlk * ROW];
-  float dk[kBlk][DI + 1];
-  int rts[kRows];  // the item's rows, decoded once: query row t * 64 + slot (k <= 64)
+  __attribute__((aligned(16))) unsigned char qr[RP * QP];
+  int rts[kRows];           // the item's rows, decoded once: query row t * 64 + slot (k <= 64)
+  int sjs[RP];              // a round's arg-max keys (-1: none)
+  uint32_t sw[RP];          // its dscores as two bf16 terms (hi | lo << 16)
 };
 
 // Arg-max of the causal block max-pool per (row, selected block) on the matrix cores, and
 // the key side of its gradient.  Work item = (sequence, group, KV block) and up to kRows
-// rows of its inverted list; each wave takes 32 rows at a time:
-//   S^T = K_I q_I^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys from LDS, B = the 32 rows'
-//   index queries straight from memory, k-step ks / lane half h = index dims
-//   [16 ks + 8 h, +8)), so a lane's accumulators are 64 keys of ONE row; the row's
-//   maximum over its causal keys and the lowest key holding it are in-register scans plus
-//   one exchange with lane ^ 32.  Scores are the matrix cores' float32 sums of the exact
-//   bf16 products.
-// The arg-max goes to am (and to argmax when given); dk_idx[j*] += dscore * q_I[row] is
-// accumulated in LDS per item and added to memory once per item with float atomics.  The
-// query side dq_idx is gathered per row afterwards (index_dq_gather).
+// rows of its inverted list, taken in rounds of RP rows:
+//  1. each wave takes 32 rows at a time: S^T = K_I q_I^T with v_mfma_f32_32x32x16_bf16 (A =
+//     32 keys from LDS, B = the 32 rows' index queries from memory, k-step ks / lane half h
+//     = index dims [16 ks + 8 h, +8)), so a lane's accumulators are 64 keys of ONE row; the
+//     row's maximum over its causal keys and the lowest key holding it are in-register
+//     scans plus one exchange with lane ^ 32 (scores are the matrix cores' float32 sums of
+//     the exact bf16 products).  The arg-max goes to am (and to argmax when given); the
+//     row's query, arg-max key and dscore go to LDS;
+//  2. wave w owns keys [32 w, 32 w + 32): dK += A B over the round's rows, with A[key][row] =
+//     the row's dscore if its arg-max is that key, else 0 (one-hot, dscore split into two
+//     bf16 terms so that the sum keeps float32 precision) and B = the rows' queries.
+// Each wave's dK tile goes to memory once per item with float atomics (float atomics into
+// LDS, one per (row, index dim), were an order of magnitude slower).  The query side dq_idx
+// is gathered per row afterwards (index_dq_gather).
 template <int DI>
 __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __restrict__ q_idx,
                                                       const uint16_t* __restrict__ k_idx,
@@ -531,6 +540,9 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
   using L_ = IdxBwdLds<DI>;
   constexpr int KS = DI / 16;
   constexpr int CPR = DI / 8;
+  constexpr int NT = DI / 32;  // index-dim tiles of the key gradient
+  constexpr int RP = L_::RP;
+  static_assert(kWaves * 32 == kBlk, "one 32-key tile per wave");
   __shared__ L_ L;
   const int n = *n_items;
   const int per_xcd = (n + 7) / 8;
@@ -550,7 +562,6 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
     *reinterpret_cast<uint4*>(&L.k[key * L_::ROW + col * 16]) =
         key < nvalid ? *reinterpret_cast<const uint4*>(kb + key * DI + col * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
-  for (int i = threadIdx.x; i < kBlk * (DI + 1); i += kThreads) (&L.dk[0][0])[i] = 0.0f;
   for (int r = threadIdx.x; r < w.z; r += kThreads) {
     const int e = entries[w.y + r];
     const int t = e / D.k;
@@ -560,27 +571,28 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
   // A lane's row of one 32-row step (both lane halves): its index query, dscore and place,
   // fetched one step ahead into one of two register sets (the loop is unrolled by two).
   // Loads are unconditional: a lane past the item's rows reads the item's first row and
-  // writes nothing.
+  // writes nothing to memory.
   struct RowIn {
     bf16x8 q[KS];
     float gsc;
     int t, slot;
     bool ok;
   };
-  auto fetch = [&](RowIn& x, int r0) __attribute__((always_inline)) {
+  auto fetch = [&](RowIn& x, int r0) __attribute__((always_inline)) {  // rows r0 + nl
     const int r = r0 + nl;
     x.ok = r < w.z;
     const int rs = L.rts[x.ok ? r : 0];
     x.t = rs >> 6;
     x.slot = rs & 63;
-    const int64_t qr = sg * D.T + x.t;  // (s, g, t)
+    const int64_t qi = sg * D.T + x.t;  // (s, g, t)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) x.q[ks] = *reinterpret_cast<const bf16x8*>(q_idx + qr * DI + 16 * ks + 8 * h);
-    x.gsc = dscore[qr * D.k + x.slot];
+    for (int ks = 0; ks < KS; ++ks) x.q[ks] = *reinterpret_cast<const bf16x8*>(q_idx + qi * DI + 16 * ks + 8 * h);
+    x.gsc = dscore[qi * D.k + x.slot];
   };
   constexpr int kStride = kWaves * 32;
-  auto body = [&](RowIn& x, int r0) __attribute__((always_inline)) {
-    const int64_t qr = sg * D.T + x.t;
+  // phase 1 of one 32-row step of round `base` (rows base + r0 + nl)
+  auto argmax_step = [&](RowIn& x, int base, int r0) __attribute__((always_inline)) {
+    const int64_t qi = sg * D.T + x.t;
     f32x16 acc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -613,31 +625,78 @@ __global__ void __launch_bounds__(kThreads) index_bwd(Dims D, const uint16_t* __
     idx = min(idx, __shfl_xor(idx, 32, 64));
     const int js = idx == 0x7FFFFFFF ? -1 : idx;
     if (x.ok && h == 0) {
-      am[qr * D.k + x.slot] = js >= 0 ? j0 + js : -1;
-      if (argmax != nullptr) argmax[qr * D.k + x.slot] = js >= 0 ? j0 + js : -1;
+      am[qi * D.k + x.slot] = js >= 0 ? j0 + js : -1;
+      if (argmax != nullptr) argmax[qi * D.k + x.slot] = js >= 0 ? j0 + js : -1;
     }
-    if (x.ok && js >= 0) {
+    // the row's query and its A-operand entry for phase 2 (rows past the item: key -1)
+    const int rl = r0 + nl;  // row within the round (< RP: r0 is a multiple of 32 below RP)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) atomicAdd(&L.dk[js][16 * ks + 8 * h + i], x.gsc * (float)x.q[ks][i]);
+    for (int ks = 0; ks < KS; ++ks)
+      *reinterpret_cast<bf16x8*>(&L.qr[rl * L_::QP + (16 * ks + 8 * h) * 2]) = x.q[ks];
+    if (h == 0) {
+      const uint32_t hi = cvt_bf16x2(x.gsc, 0.0f) & 0xFFFFu;
+      const uint32_t lo = cvt_bf16x2(x.gsc - bf16_to_f32((uint16_t)hi), 0.0f) & 0xFFFFu;
+      L.sjs[rl] = x.ok && js >= 0 ? js : -1;
+      L.sw[rl] = hi | (lo << 16);
     }
-    fetch(x, r0 + 2 * kStride);
+    fetch(x, base + r0 + 2 * kStride);
   };
-  RowIn xa, xb;
-  fetch(xa, wave * 32);
-  fetch(xb, wave * 32 + kStride);
-  // steps in pairs, the second possibly past the item's rows (it then writes nothing)
-  for (int r0 = wave * 32; r0 < w.z; r0 += 2 * kStride) {
-    body(xa, r0);
-    body(xb, r0 + kStride);
+  f32x16 dka[NT];  // this wave's dK: keys [32 wave, +32), index-dim tile nt
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) dka[nt] = f32x16{};
+  const int key = 32 * wave + nl;  // this lane's key (A-operand row) in phase 2
+  for (int base = 0; base < w.z; base += RP) {
+    const int rows = min(RP, w.z - base);
+    RowIn xa, xb;
+    fetch(xa, base + wave * 32);
+    fetch(xb, base + wave * 32 + kStride);
+    // steps in pairs, the second possibly past the round's rows (it then writes no memory;
+    // its LDS entries lie past the round's rows and are not read)
+    for (int r0 = wave * 32; r0 < rows; r0 += 2 * kStride) {
+      argmax_step(xa, base, r0);
+      if (r0 + kStride < RP) argmax_step(xb, base, r0 + kStride);
+    }
+    __syncthreads();
+    // phase 2: 16 rows per k-step, rows 16 s + 8 h + {0..7} of this lane half
+    for (int s0 = 0; s0 < rows; s0 += 16) {
+      const int rb = s0 + 8 * h;
+      const int4 j0v = *reinterpret_cast<const int4*>(&L.sjs[rb]);
+      const int4 j1v = *reinterpret_cast<const int4*>(&L.sjs[rb + 4]);
+      const uint4 w0v = *reinterpret_cast<const uint4*>(&L.sw[rb]);
+      const uint4 w1v = *reinterpret_cast<const uint4*>(&L.sw[rb + 4]);
+      const int jr[8] = {j0v.x, j0v.y, j0v.z, j0v.w, j1v.x, j1v.y, j1v.z, j1v.w};
+      const uint32_t wr[8] = {w0v.x, w0v.y, w0v.z, w0v.w, w1v.x, w1v.y, w1v.z, w1v.w};
+      uint32_t ah[4], al[4];
+#pragma unroll
+      for (int pq = 0; pq < 4; ++pq) {
+        // a row past the round's rows holds a stale entry: never matched (s0 + 16 <= RP,
+        // and rows >= `rows` are masked here)
+        const bool v0 = rb + 2 * pq < rows, v1 = rb + 2 * pq + 1 < rows;
+        const uint32_t w0 = v0 && jr[2 * pq] == key ? wr[2 * pq] : 0u;
+        const uint32_t w1 = v1 && jr[2 * pq + 1] == key ? wr[2 * pq + 1] : 0u;
+        ah[pq] = (w0 & 0xFFFFu) | (w1 << 16);
+        al[pq] = (w0 >> 16) | (w1 & 0xFFFF0000u);
+      }
+      const bf16x8 a_hi = __builtin_bit_cast(bf16x8, make_uint4(ah[0], ah[1], ah[2], ah[3]));
+      const bf16x8 a_lo = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 bq = tr_operand(L.qr, L_::QP, rb, rb + 4, 32 * nt, lane);
+        dka[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, bq, dka[nt], 0, 0, 0);
+        dka[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo, bq, dka[nt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the round's LDS rows are consumed
   }
-  __syncthreads();
+  // this wave's dK tile (rows = keys 32 wave + acc_row(r, h), columns = index dims 32 nt + nl)
   float* dst = dk_idx + (sg * D.N + j0) * DI;
-  for (int i = threadIdx.x; i < nvalid * DI; i += kThreads) {
-    const float x = L.dk[i / DI][i % DI];
-    if (x != 0.0f) unsafeAtomicAdd(dst + i, x);
-  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = dka[nt][r];
+      if (x != 0.0f) unsafeAtomicAdd(dst + (32 * wave + acc_row(r, h)) * DI + 32 * nt + nl, x);
+    }
 }
 
 // dq_idx[s, g, t] = sum over the row's slots with an arg-max j of dscore * k_I[s, g, j], in
