@@ -1,7 +1,9 @@
 """Benchmark of the MSA hot path on one MI355X.
 
 One step = one full MSA prefill pass over the 131,072-token workload (index scores
-+ block max-pool, top-k, inversion, Outer-Gather-Q attention, LSE merge) followed by
++ block max-pool and top-k -- by default fused in one kernel that never writes the block
+scores, bit-identical to the two separate calls, which are timed beside it; --selection
+two-call times them in the step --, inversion, Outer-Gather-Q attention, LSE merge) followed by
 one decode step of 16 sequences over 1,048,576-token caches (index scores, top-k,
 split-K attention + merge).  Inputs are generated on the device before timing and
 stay resident in HBM.
@@ -54,6 +56,13 @@ def prefill_model(S, T, N, H, Hkv, d, dI, k, B=128, esize=2, touched_blocks=None
     m = {}
     m["idx_scores"] = dict(flops=2.0 * dI * S * Hkv * float((p + 1).sum()),
                            bytes=esize * S * Hkv * (T + N) * dI + 4.0 * S * Hkv * float((bt + 1).sum()))
+    # fused selection: the same index products; its per-(row, span) candidate lists of 15
+    # (score, id) are written once and read once by the merge
+    nspan = (nb + 1023) // 1024
+    cand = 8.0 * 15 * S * Hkv * T * nspan
+    m["idx_topk"] = dict(flops=m["idx_scores"]["flops"],
+                         bytes=esize * S * Hkv * (T + N) * dI + cand + 4.0 * S * Hkv * T * k)
+    m["topk_merge"] = dict(flops=0.0, bytes=cand + 4.0 * S * Hkv * T * k)
     rows_reading = bt >= k                               # rows that must rank their past blocks
     m["block_topk"] = dict(flops=0.0, bytes=4.0 * S * Hkv * float((bt * rows_reading).sum()) + 4.0 * S * Hkv * T * k)
     m["invert"] = dict(flops=0.0, bytes=4.0 * S * Hkv * T * k + 4.0 * n_slots + 4.0 * S * Hkv * (nb + 1))
@@ -168,10 +177,12 @@ def attention_split_model(wl, sel, hot, keep, esize=2):
 
 # kernel name (library profiler) -> model stage (the attention kernels and the merge
 # are priced by attention_split_model from the run's own selection)
-PREFILL_KERNELS = {"idx_scores_mfma": "idx_scores", "block_topk": "block_topk", "ogq_mfma": "ogq_mfma",
-                   "hot_mfma": "hot_mfma", "lse_merge": "lse_merge"}
+PREFILL_KERNELS = {"idx_scores_mfma": "idx_scores", "block_topk": "block_topk", "idx_topk_mfma": "idx_topk",
+                   "topk_merge": "topk_merge", "ogq_mfma": "ogq_mfma", "hot_mfma": "hot_mfma",
+                   "lse_merge": "lse_merge"}
 KERNEL_SOURCES = {"ogq_mfma": "attention_mfma.hip", "hot_mfma": "attention_mfma.hip",
-                  "idx_scores_mfma": "index_scores_mfma.hip", "lse_merge": "attention.hip", "block_topk": "topk.hip"}
+                  "idx_scores_mfma": "index_scores_mfma.hip", "lse_merge": "attention.hip", "block_topk": "topk.hip",
+                  "idx_topk_mfma": "fused_topk.hip", "topk_merge": "fused_topk.hip"}
 
 
 def source_sha(kernel):
@@ -442,17 +453,24 @@ def paged_decode(args, msa, wd, xd):
                 us_per_step=ms * 1e3, us_per_token_amortised=ms * 1e3 / S, stages=st)
 
 
-def fused_selection(args, msa, wp, xp, pb):
-    """Index scores + top-k fused (no [S, Hkv, T, nb] score matrix) on the prefill workload,
-    outside the timed step: time per call, its workspace against the score matrix of the
-    unfused pair, and whether its selection equals the timed step's."""
+def other_selection(args, msa, wp, xp, pb, fused):
+    """The selection path the timed step does not use, on the prefill workload and outside
+    the timed step: the fused index scores + top-k (fused=True; no [S, Hkv, T, nb] score
+    matrix) or the two calls msa_index_scores + msa_block_topk.  Time per pass, per kernel,
+    the workspace of the fused call against the score matrix, and whether its selection
+    equals the timed step's."""
     import torch
     prob = wp.problem()
-    ws = torch.empty((max(msa.workspace_bytes(prob, msa.MSA_CALL_INDEX_TOPK), 1),), dtype=torch.uint8, device="cuda")
     sel = torch.empty_like(pb.sel)
+    ws = torch.empty((max(msa.workspace_bytes(prob, msa.MSA_CALL_INDEX_TOPK), 1),), dtype=torch.uint8, device="cuda")
+    scores = None if fused else torch.empty((wp.S, wp.Hkv, wp.T, wp.nb), dtype=torch.float32, device="cuda")
 
     def call():
-        msa.index_topk(prob, xp["q_idx"], xp["k_idx"], sel, ws, ws.numel())
+        if fused:
+            msa.index_topk(prob, xp["q_idx"], xp["k_idx"], sel, ws, ws.numel())
+        else:
+            msa.index_scores(prob, xp["q_idx"], xp["k_idx"], scores)
+            msa.block_topk(prob, scores, sel)
     call()
     torch.cuda.synchronize()
     msa.profiler_read(None, reset=True)
@@ -465,19 +483,20 @@ def fused_selection(args, msa, wp, xp, pb):
     torch.cuda.synchronize()
     msa.profiler_enable(False)
     ms = e0.elapsed_time(e1) / args.steps
+    m = prefill_model(wp.S, wp.T, wp.N, wp.H, wp.Hkv, wp.d, wp.dI, wp.k)
     st = {}
-    for kn in ("idx_topk_mfma", "topk_merge"):
+    for kn in (("idx_topk_mfma", "topk_merge") if fused else ("idx_scores_mfma", "block_topk")):
         tms, nl = msa.profiler_read(kn, reset=False)
         if nl:
-            st[kn] = dict(ms=tms / nl)
+            stage = m[PREFILL_KERNELS[kn]]
+            st[kn] = dict(ms=tms / nl, **roofline(stage["flops"], stage["bytes"], tms / nl / 1e3))
     msa.profiler_read(None, reset=True)
-    m = prefill_model(wp.S, wp.T, wp.N, wp.H, wp.Hkv, wp.d, wp.dI, wp.k)
-    if "idx_topk_mfma" in st:
-        st["idx_topk_mfma"].update(roofline(m["idx_scores"]["flops"], 0.0, st["idx_topk_mfma"]["ms"] / 1e3))
     same = bool(torch.equal(sel, pb.sel))
-    return dict(workload=wp.description + ", index scores + top-k fused", ms_per_call=ms, stages=st,
-                workspace_bytes=int(ws.numel()), score_matrix_bytes=int(pb.scores.numel() * 4),
-                selection_equal_to_the_unfused_calls=same)
+    return dict(workload=wp.description + (", index scores + top-k fused" if fused else
+                                           ", index scores and top-k as two calls"),
+                fused=fused, ms_per_pass=ms, stages=st, fused_workspace_bytes=int(ws.numel()),
+                score_matrix_bytes=int(wp.S * wp.Hkv * wp.T * wp.nb * 4),
+                selection_equal_to_the_timed_step=same)
 
 
 def token_decode(args, msa, wd, xd, block_sel):
@@ -579,7 +598,7 @@ def train_step(args, msa, wl):
 PREFILL_TIMER_NAMES = ("idx_scores_mfma", "idx_scores_rows", "block_topk", "invert_count", "invert_scatter",
                        "invert_offsets", "scan_tile_sums", "scan_top", "scan_apply", "wl_count", "wl_emit", "ogq_mfma",
                        "ogq_simple", "lse_merge", "hot_select", "hot_compact", "cold_count", "cold_scatter",
-                       "cold_offsets", "hot_mfma")
+                       "cold_offsets", "hot_mfma", "idx_topk_mfma", "topk_merge")
 
 
 def read_timer(msa, names):
@@ -629,15 +648,17 @@ def prefill_stage_report(wp, pb, kern, steps):
     return stages, split
 
 
-def other_prefill(args, msa, wl):
+def other_prefill(args, msa, wl, fused):
     """One more prefill workload, timed on its own after the headline steps: tokens/s and
-    the per-stage rooflines, with the same timer and model as the headline workload."""
+    the per-stage rooflines, with the same timer and model as the headline workload.  With
+    fused, the pass selects blocks with the fused index scores + top-k (no block-score
+    matrix) in place of the two separate calls."""
     import torch
     import synth
     specs = wl.specs()
     x = {n: synth.device_tensor(specs[n]) for n in specs}
     prob = wl.problem()
-    pb = msa.alloc_prefill(prob)
+    pb = msa.alloc_prefill(prob, fused_selection=fused)
 
     def run():
         msa.run_prefill(prob, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], pb)
@@ -660,7 +681,8 @@ def other_prefill(args, msa, wl):
     stages, split = prefill_stage_report(wl, pb, kern, args.steps)
     del x, pb
     torch.cuda.empty_cache()
-    return dict(workload=wl.description, tokens=wl.T, tokens_per_s=wl.T / (ms / 1e3), prefill_ms=ms,
+    desc = wl.description + (", fused index scores + top-k" if fused else ", index scores and top-k as two calls")
+    return dict(workload=desc, tokens=wl.T, tokens_per_s=wl.T / (ms / 1e3), prefill_ms=ms,
                 **{"prefill_" + k: v for k, v in percentiles(steps_ms).items()}, stages=stages,
                 attention_pairs=split["pairs"])
 
@@ -681,8 +703,14 @@ def main():
     ap.add_argument("--train", default="C1", choices=["C1", "C2", "none"],
                     help="workload of the extra training-step timing (default C1, 32768 tokens)")
     ap.add_argument("--other-prefill", default="C1,C4",
-                    help="further prefill workloads timed after the headline steps (comma list of C1, C2, C4, "
-                         "or 'none')")
+                    help="further prefill workloads timed after the headline steps with the same --selection "
+                         "(comma list of C1, C2, C4, each optionally suffixed '+fused' or '+two-call' to override "
+                         "the selection path, or 'none')")
+    ap.add_argument("--selection", default="fused", choices=["fused", "two-call"],
+                    help="block selection of the timed prefill pass: the fused index scores + top-k kernel "
+                         "(default; no block-score matrix) or msa_index_scores + msa_block_topk; the other one is "
+                         "timed beside it, outside the step (falls back to two-call where the fused call does not "
+                         "apply: top-k > 16)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy 3 times (the known-size reference "
                          "for scaling hardware byte counters)")
@@ -712,7 +740,8 @@ def main():
     specs = wp.specs()
     xp = {n: synth.device_tensor(specs[n]) for n in specs}
     pprob = wp.problem()
-    pb = msa.alloc_prefill(pprob)
+    use_fused = args.selection == "fused" and wp.k <= 16
+    pb = msa.alloc_prefill(pprob, fused_selection=use_fused)
     xd = db = dprob = None
     kidx8 = db8 = dprob8 = None
     if not args.no_decode:
@@ -832,10 +861,11 @@ def main():
                     stages=k8, selection_overlap_with_bf16_keys=overlap)
         print("[bench] decode with E4M3 index keys: %.3f ms per step" % ms8, file=sys.stderr, flush=True)
 
-    fsel = fused_selection(args, msa, wp, xp, pb) if wp.k <= 16 else None
-    if fsel is not None:
-        print("[bench] fused index scores + top-k: %.3f ms (equal selection: %s)"
-              % (fsel["ms_per_call"], fsel["selection_equal_to_the_unfused_calls"]), file=sys.stderr, flush=True)
+    osel = other_selection(args, msa, wp, xp, pb, fused=not use_fused) if wp.k <= 16 else None
+    if osel is not None:
+        print("[bench] selection %s, outside the step: %.3f ms (equal selection: %s)"
+              % ("fused" if osel["fused"] else "as two calls", osel["ms_per_pass"],
+                 osel["selection_equal_to_the_timed_step"]), file=sys.stderr, flush=True)
 
     dect = None
     if db is not None:
@@ -857,7 +887,10 @@ def main():
     others = {}
     if args.other_prefill != "none":
         for name in [x for x in args.other_prefill.split(",") if x and x != args.prefill]:
-            others[name] = other_prefill(args, msa, {"C1": W.C1, "C2": W.C2, "C4": W.C4}[name])
+            base, _, how = name.partition("+")
+            wl = {"C1": W.C1, "C2": W.C2, "C4": W.C4}[base]
+            fused = (how == "fused" or (how == "" and args.selection == "fused")) and wl.k <= 16
+            others[name] = other_prefill(args, msa, wl, fused)
             print("[bench] prefill %s: %.3f ms (%.0f tokens/s)" % (name, others[name]["prefill_ms"],
                   others[name]["tokens_per_s"]), file=sys.stderr, flush=True)
 
@@ -884,7 +917,7 @@ def main():
         "prefill_ms": prefill_ms, "prefill_ms_p50": percentiles(prefill_steps)["p50_ms"],
         "prefill_ms_p95": percentiles(prefill_steps)["p95_ms"], "prefill_ms_p99": percentiles(prefill_steps)["p99_ms"],
         "wall_s_timed": wall, "other_prefill": others,
-        "fused_selection": fsel,
+        "selection": "fused" if use_fused else "two-call", "other_selection": osel,
         "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "decode_token_level": dect,
         "training_step": trn, "stages": stages, "roofline": roof, "achievable_peaks": peaks, "cpu_baseline": cpu,
         "selection_structure": selection_structure(wp, pb.sel, pb.csr_offsets),

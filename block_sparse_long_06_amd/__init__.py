@@ -337,29 +337,41 @@ class PrefillBuffers:
     ws_invert: object
     ws_prefill: object
     out: object
+    ws_select: object = None  # fused selection's workspace (scores is then None)
 
 
-def alloc_prefill(prob: Problem, device="cuda") -> PrefillBuffers:
-    """Allocate (torch) every output and workspace of one prefill pass."""
+def alloc_prefill(prob: Problem, device="cuda", fused_selection: bool = False) -> PrefillBuffers:
+    """Allocate (torch) every output and workspace of one prefill pass.  With
+    fused_selection the pass selects blocks with msa_index_topk (no block-score matrix:
+    bf16 queries and top-k <= 16)."""
     import torch
     S, T, Hkv, nb, k = prob.batch, prob.num_q, prob.num_kv_heads, prob.nb, prob.topk
     odt = torch.bfloat16 if prob.dtype == MSA_BF16 else torch.float32
     wi = max(workspace_bytes(prob, MSA_CALL_INVERT), 1)
     wp = max(workspace_bytes(prob, MSA_CALL_PREFILL), 1)
+    ws_select = None
+    if fused_selection:
+        ws_select = torch.empty((max(workspace_bytes(prob, MSA_CALL_INDEX_TOPK), 1),), dtype=torch.uint8,
+                                device=device)
     return PrefillBuffers(
-        scores=torch.empty((S, Hkv, T, nb), dtype=torch.float32, device=device),
+        scores=None if fused_selection else torch.empty((S, Hkv, T, nb), dtype=torch.float32, device=device),
         sel=torch.empty((S, Hkv, T, k), dtype=torch.int32, device=device),
         csr_offsets=torch.empty((S, Hkv, nb + 1), dtype=torch.int32, device=device),
         csr_entries=torch.empty((S * Hkv * T * k,), dtype=torch.int32, device=device),
         ws_invert=torch.empty((wi,), dtype=torch.uint8, device=device),
         ws_prefill=torch.empty((wp,), dtype=torch.uint8, device=device),
-        out=torch.empty((S, T, prob.num_heads, prob.head_dim), dtype=odt, device=device))
+        out=torch.empty((S, T, prob.num_heads, prob.head_dim), dtype=odt, device=device),
+        ws_select=ws_select)
 
 
 def run_prefill(prob: Problem, q, k, v, q_idx, k_idx, bufs: PrefillBuffers, stream=None) -> None:
-    """The five-stage prefill pass: scores -> top-k -> inversion -> attention + merge."""
-    index_scores(prob, q_idx, k_idx, bufs.scores, stream)
-    block_topk(prob, bufs.scores, bufs.sel, stream)
+    """The prefill pass: scores -> top-k (or the fused selection when bufs were allocated
+    with fused_selection) -> inversion -> attention + merge."""
+    if bufs.scores is None:
+        index_topk(prob, q_idx, k_idx, bufs.sel, bufs.ws_select, bufs.ws_select.numel(), stream)
+    else:
+        index_scores(prob, q_idx, k_idx, bufs.scores, stream)
+        block_topk(prob, bufs.scores, bufs.sel, stream)
     invert_selection(prob, bufs.sel, bufs.csr_offsets, bufs.csr_entries, bufs.ws_invert,
                      bufs.ws_invert.numel(), stream)
     sparse_attn_prefill(prob, q, k, v, bufs.csr_offsets, bufs.csr_entries, bufs.sel, bufs.out,

@@ -3,15 +3,21 @@
 // MoBA / MSA 四方案深度对比", section 第一步：粗筛 (score every token, block max pooling,
 // 16 blocks with the current position's block always chosen, the rest by score).
 //
-// idx_topk_mfma: one workgroup = 256 query rows of one (sequence, group) x a span of up to
-// kSpan key blocks.  The block maxima are formed exactly as in the unfused matrix-core
-// indexer (same k-step order, same max chain), 16 blocks (a chunk) at a time into LDS; after
-// each chunk one thread per row merges the chunk's maxima into the row's running list of
-// its 15 best blocks (score descending, id ascending), kept in LDS.  Within a span the ids
-// arrive in ascending order, so a block enters a full list only with a score strictly
-// above the list's last one.  Only blocks b < b_t (strictly in the row's past) are ranked:
-// the own block is forced, later blocks are not eligible -- so no causal mask is needed.
-// Each (row, span) list is written out (score, id; id -1 for empty entries).
+// idx_topk_mfma: one workgroup = 512 query rows of one (sequence, group) x a span of up to
+// kSpan key blocks; each wave holds four 32-query tiles as resident MFMA operands, so a key
+// fragment read from LDS feeds four products.  The block maxima are formed exactly as in
+// the unfused matrix-core indexer (same k-step order; a maximum does not depend on the
+// order it is taken in).  Lane (h, n) of a wave ends each block with the maxima of rows
+// 2h * 32 + n and (2h + 1) * 32 + n of its query tiles and is also the thread that ranks
+// those two rows, so the maxima of 16 blocks (a chunk) go to lane-private LDS rows and
+// need no barrier.  After each chunk the lane merges them into each row's running list of
+// its 15 best blocks (score descending, id ascending), held in registers: only the chunk's
+// values above the list's last score are visited, each inserted by a branch-free shift.  Within a
+// span the ids arrive in ascending order, so a block enters only with a score strictly
+// above the list's last one (-inf while the list has room, so -inf and NaN never enter).
+// Only blocks b < b_t (strictly in the row's past) are ranked: the own block is forced,
+// later blocks are not eligible -- so no causal mask is needed.  Each (row, span) list is
+// written out (score, id; id -1 for empty entries).
 //
 // topk_merge: one thread per row merges its spans' lists into the k-1 best blocks (score
 // descending, id ascending), appends the own block and writes them in ascending order,
@@ -26,7 +32,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kQT = 2;
+constexpr int kQT = 4;           // 32-query tiles per wave
 constexpr int kQW = 32 * kQT;    // queries per wave
 constexpr int kQB = 4 * kQW;     // queries per workgroup
 constexpr int kChunk = 16;       // blocks merged per step
@@ -48,6 +54,52 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return (__builtin_bit_cast(uint32_t, f0) >> 16) | (__builtin_bit_cast(uint32_t, f1) & 0xFFFF0000u);
 }
 
+// The row's list of its kList best blocks so far (score descending, id ascending; empty
+// entries hold score -inf and id -1, so ls[kList - 1] is the entry bar), and the merge of
+// one chunk's maxima src[0..nv) -- block ids c0 + j, above every id in the list.
+struct RowList {
+  float ls[kList];
+  int li[kList];
+};
+
+__device__ __forceinline__ void list_init(RowList& L) {
+#pragma unroll
+  for (int i = 0; i < kList; ++i) {
+    L.ls[i] = -INFINITY;
+    L.li[i] = -1;
+  }
+}
+
+__device__ __forceinline__ void list_merge(RowList& L, const float* src, int nv, int c0) {
+  const float bar = L.ls[kList - 1];
+  uint32_t m = 0;
+#pragma unroll
+  for (int q4 = 0; q4 < kChunk / 4; ++q4) {
+    const float4 f = *reinterpret_cast<const float4*>(src + 4 * q4);
+    m |= (f.x > bar ? 1u : 0u) << (4 * q4);
+    m |= (f.y > bar ? 2u : 0u) << (4 * q4);
+    m |= (f.z > bar ? 4u : 0u) << (4 * q4);
+    m |= (f.w > bar ? 8u : 0u) << (4 * q4);
+  }
+  m &= nv >= kChunk ? 0xFFFFu : (nv > 0 ? (1u << nv) - 1u : 0u);
+  while (m) {  // ascending ids: a tie with an entry places the new block after it
+    const int j = __builtin_ctz(m);
+    m &= m - 1;
+    const float sc = src[j];
+    if (!(sc > L.ls[kList - 1])) continue;
+    bool gt[kList];
+#pragma unroll
+    for (int i = 0; i < kList; ++i) gt[i] = sc > L.ls[i];
+#pragma unroll
+    for (int i = kList - 1; i >= 1; --i) {
+      L.ls[i] = gt[i - 1] ? L.ls[i - 1] : (gt[i] ? sc : L.ls[i]);
+      L.li[i] = gt[i - 1] ? L.li[i - 1] : (gt[i] ? c0 + j : L.li[i]);
+    }
+    L.ls[0] = gt[0] ? sc : L.ls[0];
+    L.li[0] = gt[0] ? c0 + j : L.li[0];
+  }
+}
+
 template <int DI, typename TK>
 __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_topk_mfma(Dims D, const uint16_t* __restrict__ q_idx,
                                                         const TK* __restrict__ k_idx, float* __restrict__ cand_sc,
@@ -58,24 +110,28 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_topk_mfma(Dims D, 
   constexpr int PER_T = kBlk * CPR / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][kBlk * ROWB];
   __shared__ __attribute__((aligned(16))) float outb[4][kQW][kChunk + 4];  // 16-byte aligned rows
-  __shared__ float lsc[kQB][kList];
-  __shared__ uint16_t lid[kQB][kList];  // block ids < 8192
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int n = lane & 31;
-  const int64_t sg = blockIdx.z;
-  const int t_first = blockIdx.x * kQB;
+  // grid (sequence x group, span, row tile from the last): the longest (latest) row tiles
+  // are dispatched first, and consecutive workgroups -- spread over the XCDs in turn --
+  // take different (sequence, group)s, so each XCD's L2 holds fewer groups' index keys
+  const int64_t sg = blockIdx.x;
+  const int t_first = (int)(gridDim.z - 1 - blockIdx.z) * kQB;
   const int t_last = min(t_first + kQB - 1, D.T - 1);
   const int span = blockIdx.y;
   const int b_lo = span * kSpan;
   const int b_hi = min(b_lo + kSpan, (D.pos0 + t_last) / kBlk);  // exclusive: only past blocks are ranked
-  // this thread's row for the merges
-  const int tr = t_first + threadIdx.x;
-  const int bt_r = tr < D.T ? (D.pos0 + tr) / kBlk : 0;
-  int cnt = 0;
-  float theta = -INFINITY;  // the list's last score once it is full: the entry bar
+  // this lane ranks rows (2h) * 32 + n and (2h + 1) * 32 + n of its wave's query tiles
+  const int rw0 = (2 * h) * 32 + n, rw1 = rw0 + 32;
+  const int tr0 = t_first + wave * kQW + rw0, tr1 = tr0 + 32;
+  const int bt0 = tr0 < D.T ? (D.pos0 + tr0) / kBlk : 0;
+  const int bt1 = tr1 < D.T ? (D.pos0 + tr1) / kBlk : 0;
+  RowList L0, L1;
+  list_init(L0);
+  list_init(L1);
 
   if (b_lo < b_hi) {
     bf16x8 qf[kQT][KS];
@@ -124,7 +180,9 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_topk_mfma(Dims D, 
       float rmax[kQT];
 #pragma unroll
       for (int qt = 0; qt < kQT; ++qt) rmax[qt] = -INFINITY;
-      f32x16 acc[2][kQT];
+      // (key tile, query tile) steps in turn; each step's accumulator is reduced after the
+      // next step's products are issued, so two accumulators are live
+      f32x16 acc[2];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         bf16x8 af[KS];
@@ -133,63 +191,44 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_topk_mfma(Dims D, 
         for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(arow + ks * 32);
 #pragma unroll
         for (int qt = 0; qt < kQT; ++qt) {
-          acc[kt & 1][qt] = f32x16{};
+          const int step = kt * kQT + qt;
+          acc[step & 1] = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            acc[kt & 1][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[qt][ks], acc[kt & 1][qt], 0, 0, 0);
-        }
-        if (kt >= 1) {
-#pragma unroll
-          for (int qt = 0; qt < kQT; ++qt) rmax[qt] = __builtin_fmaxf(rmax[qt], max16(acc[(kt - 1) & 1][qt]));
+            acc[step & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[qt][ks], acc[step & 1], 0, 0, 0);
+          if (step >= 1) {
+            const int pq = (qt + kQT - 1) % kQT;
+            rmax[pq] = __builtin_fmaxf(rmax[pq], max16(acc[(step - 1) & 1]));
+          }
         }
       }
-#pragma unroll
-      for (int qt = 0; qt < kQT; ++qt) rmax[qt] = __builtin_fmaxf(rmax[qt], max16(acc[1][qt]));
+      rmax[kQT - 1] = __builtin_fmaxf(rmax[kQT - 1], max16(acc[(4 * kQT - 1) & 1]));
 #pragma unroll
       for (int qt = 0; qt < kQT; ++qt) rmax[qt] = __builtin_fmaxf(rmax[qt], __shfl_xor(rmax[qt], 32, 64));
-      // lane half h records query tile h
-      outb[wave][h * 32 + n][(b - b_lo) % kChunk] = h == 0 ? rmax[0] : rmax[1];
+      // lane half h records query tiles 2h and 2h + 1: its own two rows
+      const int col = (b - b_lo) % kChunk;
+      outb[wave][rw0][col] = h == 0 ? rmax[0] : rmax[2];
+      outb[wave][rw1][col] = h == 0 ? rmax[1] : rmax[3];
       if (b + 1 < b_hi) lstore(buf ^ 1);
       __syncthreads();
-      if ((b - b_lo) % kChunk == kChunk - 1 || b + 1 == b_hi) {
-        // merge the chunk's maxima into this thread's row list
-        const int c0 = b - (b - b_lo) % kChunk;
-        const float* src = outb[threadIdx.x >> 6][threadIdx.x & 63];
-        float v[kChunk];
-#pragma unroll
-        for (int q4 = 0; q4 < kChunk / 4; ++q4) {
-          const float4 f = *reinterpret_cast<const float4*>(src + 4 * q4);
-          v[4 * q4] = f.x; v[4 * q4 + 1] = f.y; v[4 * q4 + 2] = f.z; v[4 * q4 + 3] = f.w;
-        }
-        float* ls = lsc[threadIdx.x];
-        uint16_t* li = lid[threadIdx.x];
-        const int nv = min(b, bt_r - 1) - c0 + 1;  // this row's eligible blocks of the chunk
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          const float s = v[j];
-          if (j >= nv || !(s > theta)) continue;  // ids ascend: a tie with the bar stays out
-          int pos = cnt < kList ? cnt : kList - 1;
-          while (pos > 0 && ls[pos - 1] < s) {
-            ls[pos] = ls[pos - 1];
-            li[pos] = li[pos - 1];
-            --pos;
-          }
-          ls[pos] = s;
-          li[pos] = (uint16_t)(c0 + j);
-          cnt = cnt < kList ? cnt + 1 : kList;
-          if (cnt == kList) theta = ls[kList - 1];
-        }
-        __syncthreads();  // outb is rewritten by the next chunk
+      if (col == kChunk - 1 || b + 1 == b_hi) {
+        const int c0 = b - col;
+        list_merge(L0, outb[wave][rw0], min(b, bt0 - 1) - c0 + 1, c0);
+        list_merge(L1, outb[wave][rw1], min(b, bt1 - 1) - c0 + 1, c0);
       }
     }
   }
-  if (tr < D.T) {
+  auto put = [&](const RowList& L, int tr) {
+    if (tr >= D.T) return;
     const int64_t o = ((sg * D.T + tr) * nspan + span) * kList;
+#pragma unroll
     for (int i = 0; i < kList; ++i) {
-      cand_sc[o + i] = i < cnt ? lsc[threadIdx.x][i] : 0.0f;
-      cand_id[o + i] = i < cnt ? (int32_t)lid[threadIdx.x][i] : -1;
+      cand_sc[o + i] = L.li[i] >= 0 ? L.ls[i] : 0.0f;
+      cand_id[o + i] = L.li[i];
     }
-  }
+  };
+  put(L0, tr0);
+  put(L1, tr1);
 }
 
 // One thread per row: the k-1 best of the spans' candidates, plus the own block, ascending.
@@ -286,7 +325,7 @@ hipError_t launch_index_topk(const Dims& D, const void* q_idx, const void* k_idx
   float* cs = static_cast<float*>(ws);
   int32_t* ci = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + align_up(n * sizeof(float), 256));
   {
-    const dim3 grid((unsigned)((D.T + kQB - 1) / kQB), (unsigned)nspan, (unsigned)(D.S * D.Hkv));
+    const dim3 grid((unsigned)(D.S * D.Hkv), (unsigned)nspan, (unsigned)((D.T + kQB - 1) / kQB));
     LaunchScope scope("idx_topk_mfma", st);
     const uint16_t* q = static_cast<const uint16_t*>(q_idx);
     if (D.kdtype == MSA_FP8_E4M3) launch_fused(D, grid, q, static_cast<const uint8_t*>(k_idx), cs, ci, nspan, st);

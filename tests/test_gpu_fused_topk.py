@@ -57,3 +57,34 @@ def test_fused_selection_equals_the_two_calls(wl):
     # the candidate workspace is far smaller than the block-score matrix it replaces
     if wl.T >= 256:
         assert ws.numel() < scores.numel() * 4 or wl.nb < 64
+
+
+E2E = [CASES[0], CASES[1], CASES[3]]
+
+
+@pytest.mark.parametrize("wl", E2E, ids=[c.name for c in E2E])
+def test_fused_prefill_pass_equals_the_unfused_pass(wl):
+    """A whole prefill pass with the fused selection (alloc_prefill(fused_selection=True))
+    gives the same selection, inversion and attention output, bit for bit, as the pass
+    through the block-score matrix (which verify_prefill gates against the oracle)."""
+    require_gpu()
+    say("case", wl.name)
+    x = gen(wl)
+    prob = wl.problem()
+    ref = msa.alloc_prefill(prob)
+    fused = msa.alloc_prefill(prob, fused_selection=True)
+    assert fused.scores is None and fused.ws_select is not None
+    for bufs in (ref, fused):
+        msa.run_prefill(prob, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], bufs)
+    torch.cuda.synchronize()
+    for name in ("sel", "csr_offsets"):
+        assert torch.equal(getattr(ref, name), getattr(fused, name)), name
+    # csr_entries is sized for every pair; only the prefix the offsets cover is written
+    used = int(ref.csr_offsets[-1, -1, -1])
+    assert torch.equal(ref.csr_entries[:used], fused.csr_entries[:used])
+    assert torch.equal(ref.out.view(torch.uint8), fused.out.view(torch.uint8))
+    # a second fused pass over the same buffers repeats the first
+    first = fused.out.clone()
+    msa.run_prefill(prob, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], fused)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.uint8), fused.out.view(torch.uint8))
