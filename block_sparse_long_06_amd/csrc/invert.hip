@@ -81,6 +81,27 @@ __device__ __forceinline__ int row_block_at(const Dims& D, const int32_t* srow, 
   return ((skip >> i) & 1ull) ? -1 : b;
 }
 
+// LDS update for block b of every lane with ok set, where lanes that share the first
+// pending lane's block (up to two such groups of at least four) are served by one update
+// of their group's leader: in one slot of consecutive rows the sink, the own block and the
+// band blocks are usually one block for most lanes, whose individual atomics would
+// serialise on one address.  upd(b, m) applies the update for block b and lane mask m.
+template <typename Upd>
+__device__ __forceinline__ void peeled_update(int b, bool ok, Upd upd) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const uint64_t pend = __ballot(ok);
+    if (pend == 0ull) return;
+    const int v = __builtin_amdgcn_readlane(b, __builtin_ctzll(pend));
+    const uint64_t m = __ballot(ok && b == v);
+    if (__popcll(m) < 4) break;
+    if (lane == __builtin_ctzll(m)) upd(v, m);
+    ok = ok && b != v;
+  }
+  if (ok) upd(b, 1ull << lane);
+}
+
 // One thread per query row of the chunk.
 template <int KR>
 __global__ void __launch_bounds__(256) invert_count(Dims D, const int32_t* __restrict__ sel,
@@ -99,9 +120,16 @@ __global__ void __launch_bounds__(256) invert_count(Dims D, const int32_t* __res
     if constexpr (KR > 0) {
       int bl[KR];
       row_blocks<KR>(D, srow, skip, true, bl);
+      if (hotmask == nullptr) {  // the full selection: shared blocks are common in a slot
 #pragma unroll
-      for (int i = 0; i < KR; ++i)
-        if (bl[i] >= 0 && bl[i] < D.nb) atomicAdd(&hist[bl[i]], 1);
+        for (int i = 0; i < KR; ++i)
+          peeled_update(bl[i], bl[i] >= 0 && bl[i] < D.nb,
+                        [&](int b, uint64_t m) { atomicAdd(&hist[b], __popcll(m)); });
+      } else {  // the tile-shared entries are skipped: what remains rarely coincides
+#pragma unroll
+        for (int i = 0; i < KR; ++i)
+          if (bl[i] >= 0 && bl[i] < D.nb) atomicAdd(&hist[bl[i]], 1);
+      }
     } else {
       for (int i = 0; i < D.k; ++i) {
         const int b = row_block_at(D, srow, skip, i);

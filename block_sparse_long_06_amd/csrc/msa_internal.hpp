@@ -110,6 +110,7 @@ constexpr int kHotStride = kHotMax + 1;  // {count, ids...} per (sequence, group
 struct HotSplit {
   int ntiles;
   int32_t* hot;         // [S*Hkv, ntiles, kHotStride]
+  int32_t* nhot;        // [S*Hkv, ntiles]: the count of each tile's list, contiguous
   int32_t* tiles;       // (s*Hkv + g)*ntiles + tile of every tile with shared blocks, in order
   int* ntile;           // their number
   uint64_t* hotmask;    // [S, T, Hkv]
