@@ -39,12 +39,9 @@ __device__ __forceinline__ uint64_t row_skip(const Dims& D, const uint64_t* hotm
   return hotmask[(s * D.T + t) * D.Hkv + g];
 }
 
-// Rows hold distinct block ids (msa_block_topk's rows do).  A repeated id is outside
-// that contract; its later slots are dropped here, by the count and the scatter alike,
-// so that every list position the count reserves is written.
+// The k <= KR selections of a row, -1 beyond k or where ok is false.
 template <int KR>
-__device__ __forceinline__ void row_blocks(const Dims& D, const int32_t* srow, uint64_t skip, bool ok,
-                                           int (&bl)[KR]) {
+__device__ __forceinline__ void row_load(const Dims& D, const int32_t* srow, bool ok, int (&bl)[KR]) {
   if (KR % 4 == 0 && (D.k & 3) == 0 && (reinterpret_cast<uintptr_t>(srow) & 15) == 0) {
     // 16-byte loads: the row starts 16-byte aligned and holds whole groups of four
 #pragma unroll
@@ -59,12 +56,26 @@ __device__ __forceinline__ void row_blocks(const Dims& D, const int32_t* srow, u
 #pragma unroll
     for (int i = 0; i < KR; ++i) bl[i] = ok && i < D.k ? srow[i] : -1;
   }
+}
+
+// Rows hold distinct block ids (msa_block_topk's rows do).  A repeated id is outside
+// that contract; its later slots are dropped here, by the count and the scatter alike,
+// so that every list position the count reserves is written.  A row that is strictly
+// ascending up to its first negative entry, and negative after it (the form both top-k
+// paths emit), has no repeat, and skips the pairwise check.  Skipped slots become -1.
+template <int KR>
+__device__ __forceinline__ void row_clean(uint64_t skip, int (&bl)[KR]) {
+  bool asc = true;
 #pragma unroll
-  for (int i = 1; i < KR; ++i) {
-    bool rep = false;
+  for (int i = 1; i < KR; ++i) asc = asc && ((bl[i] > bl[i - 1] && bl[i - 1] >= 0) || bl[i] < 0);
+  if (!asc) {
 #pragma unroll
-    for (int j = 0; j < i; ++j) rep |= bl[j] == bl[i];
-    if (rep) bl[i] = -1;
+    for (int i = 1; i < KR; ++i) {
+      bool rep = false;
+#pragma unroll
+      for (int j = 0; j < i; ++j) rep |= bl[j] == bl[i];
+      if (rep) bl[i] = -1;
+    }
   }
 #pragma unroll
   for (int i = 0; i < KR; ++i)
@@ -114,23 +125,37 @@ __global__ void __launch_bounds__(256) invert_count(Dims D, const int32_t* __res
   __syncthreads();
   const int t0 = c * ct;
   const int t1 = min(t0 + ct, D.T);
-  for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
-    const int32_t* srow = sel + (sg * D.T + t) * D.k;
-    const uint64_t skip = row_skip(D, hotmask, sg, t);
-    if constexpr (KR > 0) {
-      int bl[KR];
-      row_blocks<KR>(D, srow, skip, true, bl);
+  if constexpr (KR > 0) {
+    // every row of this thread (ct <= 4 * 256) loaded before the first update
+    constexpr int kMaxR = 4;
+    int bl[kMaxR][KR];
+    uint64_t sk[kMaxR];
+#pragma unroll
+    for (int r = 0; r < kMaxR; ++r) {
+      const int t = t0 + (int)threadIdx.x + 256 * r;
+      const bool ok = 256 * r < ct && t < t1;
+      row_load<KR>(D, sel + (sg * D.T + (ok ? t : t0)) * D.k, ok, bl[r]);
+      sk[r] = ok ? row_skip(D, hotmask, sg, t) : 0ull;
+    }
+#pragma unroll
+    for (int r = 0; r < kMaxR; ++r) {
+      if (256 * r >= ct) break;
+      row_clean<KR>(sk[r], bl[r]);
       if (hotmask == nullptr) {  // the full selection: shared blocks are common in a slot
 #pragma unroll
         for (int i = 0; i < KR; ++i)
-          peeled_update(bl[i], bl[i] >= 0 && bl[i] < D.nb,
+          peeled_update(bl[r][i], bl[r][i] >= 0 && bl[r][i] < D.nb,
                         [&](int b, uint64_t m) { atomicAdd(&hist[b], __popcll(m)); });
       } else {  // the tile-shared entries are skipped: what remains rarely coincides
 #pragma unroll
         for (int i = 0; i < KR; ++i)
-          if (bl[i] >= 0 && bl[i] < D.nb) atomicAdd(&hist[bl[i]], 1);
+          if (bl[r][i] >= 0 && bl[r][i] < D.nb) atomicAdd(&hist[bl[r][i]], 1);
       }
-    } else {
+    }
+  } else {
+    for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
+      const int32_t* srow = sel + (sg * D.T + t) * D.k;
+      const uint64_t skip = row_skip(D, hotmask, sg, t);
       for (int i = 0; i < D.k; ++i) {
         const int b = row_block_at(D, srow, skip, i);
         if (b >= 0) atomicAdd(&hist[b], 1);
@@ -157,9 +182,11 @@ __global__ void __launch_bounds__(256) invert_offsets(Dims D, const int* __restr
   offsets[i] = v;
 }
 
-// KR > 0: the row's k <= KR selections are read once into registers; KR == 0: any k,
-// re-read from memory in each phase.  The chunk's per-block start positions are gathered
-// into LDS first, so ranking an entry needs no memory access.
+// KR > 0: the row's k <= KR selections are read once into registers (the next step's
+// while this one is ranked); KR == 0: any k, re-read from memory in each phase.  Per
+// block the LDS holds the lane mask of the current step and `at`, the list position of
+// the block's next entry (the chunk's start position, gathered first, plus the entries
+// already placed), so ranking an entry needs no memory access.
 template <int KR>
 __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __restrict__ sel,
                                                      const uint64_t* __restrict__ hotmask,
@@ -167,60 +194,94 @@ __global__ void __launch_bounds__(64) invert_scatter(Dims D, const int32_t* __re
                                                      int32_t* __restrict__ entries, int nchunks, int ct) {
   extern __shared__ unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
-  int* base = reinterpret_cast<int*>(smem + sizeof(unsigned long long) * D.nb);
-  uint16_t* run = reinterpret_cast<uint16_t*>(smem + (sizeof(unsigned long long) + sizeof(int)) * D.nb);
+  int* at = reinterpret_cast<int*>(smem + sizeof(unsigned long long) * D.nb);
   const int lane = threadIdx.x;
   const int c = blockIdx.x;
   const int64_t sg = blockIdx.y;
   const int* pos_c = pos + (sg * D.nb) * nchunks + c;  // pos of (sg, b, c) = pos_c[b * nchunks]
   for (int b = lane; b < D.nb; b += 64) {
     mask[b] = 0ull;
-    run[b] = 0;
-    base[b] = pos_c[(int64_t)b * nchunks];
+    at[b] = pos_c[(int64_t)b * nchunks];
   }
   __syncthreads();
   const int t0 = c * ct;
   const int t1 = min(t0 + ct, D.T);
   const unsigned long long lower = (1ull << lane) - 1ull;
+  int nx[KR > 0 ? KR : 1];
+  uint64_t nskip = 0ull;
+  auto fetch = [&](int tb) {
+    if constexpr (KR > 0) {
+      const int t = tb + lane;
+      const bool ok = t < t1;
+      row_load<KR>(D, sel + (sg * D.T + (ok ? t : t0)) * D.k, ok, nx);
+      nskip = ok ? row_skip(D, hotmask, sg, t) : 0ull;
+    }
+  };
+  fetch(t0);
   for (int tb = t0; tb < t1; tb += 64) {
     const int t = tb + lane;
-    const int32_t* srow = sel + (sg * D.T + t) * D.k;
-    const uint64_t skip = t < t1 ? row_skip(D, hotmask, sg, t) : 0ull;
-    int bl[KR > 0 ? KR : 1];
-    if constexpr (KR > 0) row_blocks<KR>(D, srow, skip, t < t1, bl);
-    // f(slot, block) over the row's slots (block -1 where nothing is listed)
-    auto for_slots = [&](auto f) {
-      if constexpr (KR > 0) {
+    if constexpr (KR > 0) {
+      int bl[KR];
 #pragma unroll
-        for (int i = 0; i < KR; ++i) f(i, bl[i]);
-      } else {
-        for (int i = 0; i < D.k; ++i) f(i, t < t1 ? row_block_at(D, srow, skip, i) : -1);
-      }
-    };
-    // phase 1: mark the lanes that chose each block
-    for_slots([&](int, int b) {
-      if (b >= 0 && b < D.nb) atomicOr(&mask[b], 1ull << lane);
-    });
-    __syncthreads();
-    // phase 2: rank among earlier lanes + running count -> global position
-    for_slots([&](int i, int b) {
-      if (b >= 0 && b < D.nb) {
-        const unsigned long long m = mask[b];
-        entries[base[b] + run[b] + __popcll(m & lower)] = t * D.k + i;
-      }
-    });
-    __syncthreads();
-    // phase 3: the lowest lane of each block advances its count and clears its mask
-    for_slots([&](int, int b) {
-      if (b >= 0 && b < D.nb) {
-        const unsigned long long m = mask[b];
-        if ((m & lower) == 0ull) {
-          run[b] = (uint16_t)(run[b] + __popcll(m));
-          mask[b] = 0ull;
+      for (int i = 0; i < KR; ++i) bl[i] = nx[i];
+      const uint64_t sk = nskip;
+      if (tb + 64 < t1) fetch(tb + 64);
+      row_clean<KR>(sk, bl);
+      // phase 1: mark the lanes that chose each block
+#pragma unroll
+      for (int i = 0; i < KR; ++i)
+        if (bl[i] >= 0 && bl[i] < D.nb) atomicOr(&mask[bl[i]], 1ull << lane);
+      __syncthreads();
+      // phase 2: rank among the earlier lanes -> list position; mask and position kept
+      unsigned long long m[KR];
+      int p[KR];
+#pragma unroll
+      for (int i = 0; i < KR; ++i) {
+        m[i] = 0ull;
+        p[i] = 0;
+        if (bl[i] >= 0 && bl[i] < D.nb) {
+          m[i] = mask[bl[i]];
+          p[i] = at[bl[i]];
+          entries[p[i] + __popcll(m[i] & lower)] = t * D.k + i;
         }
       }
-    });
-    __syncthreads();
+      __syncthreads();
+      // phase 3: the lowest lane of each block advances its position and clears its mask
+#pragma unroll
+      for (int i = 0; i < KR; ++i) {
+        if (bl[i] >= 0 && bl[i] < D.nb && (m[i] & lower) == 0ull) {
+          at[bl[i]] = p[i] + __popcll(m[i]);
+          mask[bl[i]] = 0ull;
+        }
+      }
+      __syncthreads();
+    } else {
+      const int32_t* srow = sel + (sg * D.T + t) * D.k;
+      const uint64_t skip = t < t1 ? row_skip(D, hotmask, sg, t) : 0ull;
+      auto blk = [&](int i) { return t < t1 ? row_block_at(D, srow, skip, i) : -1; };
+      for (int i = 0; i < D.k; ++i) {
+        const int b = blk(i);
+        if (b >= 0) atomicOr(&mask[b], 1ull << lane);
+      }
+      __syncthreads();
+      for (int i = 0; i < D.k; ++i) {
+        const int b = blk(i);
+        if (b >= 0) entries[at[b] + __popcll(mask[b] & lower)] = t * D.k + i;
+      }
+      __syncthreads();
+      // a lane that reads a mask its block's leader already cleared adds nothing
+      for (int i = 0; i < D.k; ++i) {
+        const int b = blk(i);
+        if (b >= 0) {
+          const unsigned long long mm = mask[b];
+          if ((mm & lower) == 0ull) {
+            atomicAdd(&at[b], __popcll(mm));
+            mask[b] = 0ull;
+          }
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -270,7 +331,7 @@ hipError_t launch_invert(const Dims& D, const int32_t* sel, int32_t* offsets, in
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    const size_t lds = (size_t)D.nb * (sizeof(unsigned long long) + sizeof(int) + sizeof(uint16_t));
+    const size_t lds = (size_t)D.nb * (sizeof(unsigned long long) + sizeof(int));
     const void* kern = D.k <= 16 ? reinterpret_cast<const void*>(invert_scatter<16>)
                                  : reinterpret_cast<const void*>(invert_scatter<0>);
     e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

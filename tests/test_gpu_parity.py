@@ -311,6 +311,18 @@ def test_invert_rows_with_repeated_ids(k):
     sel_np[:, 1] = sel_np[:, 0]                      # a repeat in every row
     sel_np[::7, -1] = sel_np[::7, 0]                  # and one at the far end
     sel_np[::5] = rng.integers(0, 3, size=(len(sel_np[::5]), k))  # heavy repeats
+    # ascending rows (the form the top-k emits, where the kernels skip the pairwise check)
+    # with a negative entry followed by a repeat, or a repeat right after its first slot
+    asc = np.arange(k, dtype=np.int32) % nb
+    for r in range(3, T, 11):
+        row = asc.copy()
+        if r % 2:
+            row[k // 2] = -1
+            row[k // 2 + 1] = row[0]
+        else:
+            row[-1] = row[-2]
+        sel_np[r] = row
+    sel_np[2::11] = asc                               # ascending, no repeat
     prob = msa.problem(1, T, N, 8, 1, 128, 64, k)
     sel = torch.from_numpy(sel_np).cuda().reshape(1, 1, T, k).contiguous()
     off = torch.empty((1, 1, nb + 1), dtype=torch.int32, device="cuda")
