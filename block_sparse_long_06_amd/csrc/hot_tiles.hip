@@ -60,7 +60,6 @@ __global__ void __launch_bounds__(256) hot_select(Dims D, const int32_t* __restr
   __shared__ int s_hot[4][kHotMax];
   __shared__ int s_cnt[4];
   __shared__ int s_list[kHotMax];
-  __shared__ int s_n;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int ti = blockIdx.x;
