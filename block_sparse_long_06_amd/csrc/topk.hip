@@ -503,6 +503,67 @@ constexpr int kLongCap = 1024;
 constexpr int kLongSlots = kLongCap / 64;
 constexpr int64_t kLongRows = 16384;  // up to 16K rows (workgroups of 16 waves)
 
+// 3. (one wave) the need-th largest of C > 64 candidates held in LDS in ascending id
+// order, NS per lane (candidate c in slot c / 64 of lane c % 64, so slot-major order is id
+// order, NS * 64 >= C): a radix search for its key, then every larger key and, among keys
+// equal to it, the lowest ids.  Empty slots hold key 0, which no candidate prefix reaches,
+// so no slot needs a guard.
+template <int NS>
+__device__ __forceinline__ void long_select(const uint32_t* s_ord, const int32_t* s_id, int C, int lane, int need,
+                                            int32_t* out) {
+  uint32_t ck[NS];
+  int32_t ci[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int cc = lane + 64 * u;
+    ck[u] = cc < C ? s_ord[cc] : 0u;
+    ci[u] = cc < C ? s_id[cc] : 0;
+  }
+  // prefix: the need-th largest candidate key, or a prefix of it that exactly `need`
+  // candidates reach (the search then stops: it separates them from the rest).  The
+  // search runs below the high bits every candidate shares.
+  uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int u = 0; u < NS; ++u)
+    if (lane + 64 * u < C) {
+      hi = max(hi, ck[u]);
+      lo = min(lo, ck[u]);
+    }
+  uint32_t whi, wlo;
+  wave_umax_umin(hi, lo, whi, wlo);
+  uint32_t prefix = whi;
+  if (whi != wlo) {
+    const int top = 31 - __builtin_clz(whi ^ wlo);
+    prefix = whi & ~((2u << top) - 1u);  // <= every candidate
+    for (int bit = top; bit >= 0; --bit) {
+      const uint32_t cand = prefix | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) cnt += __popcll(__ballot(ck[u] >= cand));
+      if (cnt >= need) {
+        prefix = cand;
+        if (cnt == need) break;
+      }
+    }
+  }
+  int c_gt = 0;
+#pragma unroll
+  for (int u = 0; u < NS; ++u) c_gt += __popcll(__ballot(ck[u] > prefix));
+  const int need_eq = need - c_gt;  // >= 0 (0 when the search stopped between keys)
+  int pos = 0, eq_seen = 0;
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const bool eq = ck[u] == prefix;
+    const uint64_t meq = __ballot(eq);
+    const bool f = ck[u] > prefix || (eq && eq_seen + lanes_below(meq) < need_eq);
+    const uint64_t m = __ballot(f);
+    const int at = pos + lanes_below(m);
+    if (f && at < need) out[at] = ci[u];
+    pos += __popcll(m);
+    eq_seen += __popcll(meq);
+  }
+}
+
 template <bool VEC>
 __global__ void __launch_bounds__(kLongThreads) block_topk_long(Dims D, const float* __restrict__ scores,
                                                                int32_t* __restrict__ sel) {
@@ -596,64 +657,10 @@ __global__ void __launch_bounds__(kLongThreads) block_topk_long(Dims D, const fl
   } else if (C <= 64) {
     const bool have = lane < C;
     pick_from_lanes(have ? s_ord[lane] : 0u, have ? s_id[lane] : 0, have, lane, need, C, out);
+  } else if (C <= 4 * 64) {
+    long_select<4>(s_ord, s_id, C, lane, need, out);
   } else {
-    // 3. at least `need` candidates (every selected block is one), in registers
-    const int nu = (C + 63) >> 6;
-    uint32_t ck[kLongSlots];
-    int32_t ci[kLongSlots];
-#pragma unroll
-    for (int u = 0; u < kLongSlots; ++u) {
-      const int cc = lane + 64 * u;
-      ck[u] = cc < C ? s_ord[cc] : 0u;  // 0 never reaches a candidate prefix below
-      ci[u] = cc < C ? s_id[cc] : 0;
-    }
-    // prefix: the need-th largest candidate key, or a prefix of it that exactly `need`
-    // candidates reach (the search then stops: it separates them from the rest).  The
-    // search runs below the high bits every candidate shares.
-    uint32_t hi = 0u, lo = 0xFFFFFFFFu;
-#pragma unroll
-    for (int u = 0; u < kLongSlots; ++u)
-      if (u < nu && lane + 64 * u < C) {
-        hi = max(hi, ck[u]);
-        lo = min(lo, ck[u]);
-      }
-    uint32_t whi, wlo;
-    wave_umax_umin(hi, lo, whi, wlo);
-    uint32_t prefix = whi;
-    if (whi != wlo) {
-      const int top = 31 - __builtin_clz(whi ^ wlo);
-      prefix = whi & ~((2u << top) - 1u);  // <= every candidate
-      for (int bit = top; bit >= 0; --bit) {
-        const uint32_t cand = prefix | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int u = 0; u < kLongSlots; ++u)
-          if (u < nu) cnt += __popcll(__ballot(ck[u] >= cand));
-        if (cnt >= need) {
-          prefix = cand;
-          if (cnt == need) break;
-        }
-      }
-    }
-    int c_gt = 0;
-#pragma unroll
-    for (int u = 0; u < kLongSlots; ++u)
-      if (u < nu) c_gt += __popcll(__ballot(ck[u] > prefix));
-    const int need_eq = need - c_gt;  // >= 0 (0 when the search stopped between keys)
-    int pos = 0, eq_seen = 0;
-#pragma unroll
-    for (int u = 0; u < kLongSlots; ++u) {
-      if (u < nu) {
-        const bool eq = ck[u] == prefix;
-        const uint64_t meq = __ballot(eq);
-        const bool f = ck[u] > prefix || (eq && eq_seen + lanes_below(meq) < need_eq);
-        const uint64_t m = __ballot(f);
-        const int at = pos + lanes_below(m);
-        if (f && at < need) out[at] = ci[u];
-        pos += __popcll(m);
-        eq_seen += __popcll(meq);
-      }
-    }
+    long_select<kLongSlots>(s_ord, s_id, C, lane, need, out);
   }
   if (lane == 0) out[need] = bt;  // the own block is the largest id of the row
 }

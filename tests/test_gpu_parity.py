@@ -224,7 +224,7 @@ def _topk_case(scores_np, T, N, k):
                                   "long_all_equal", "long_random", "long_ties_at_threshold",
                                   "few_values_odd_nb", "long_random_odd_nb", "ties_at_threshold_odd_nb",
                                   "mid_random", "mid_all_equal", "mid_ties_at_threshold", "mid_neg_inf_and_huge",
-                                  "mid_random_odd_nb", "int_ties", "mid_int_ties"])
+                                  "mid_random_odd_nb", "int_ties", "mid_int_ties", "long_int_ties"])
 @pytest.mark.parametrize("k", [1, 2, 16, 64])
 def test_topk_adversarial_rows(kind, k):
     """Rows of up to 300 blocks (held in registers), 130 rows of 8192 blocks (a workgroup
@@ -254,7 +254,7 @@ def test_topk_adversarial_rows(kind, k):
         sc = rng.choice([-np.inf, np.inf, -3e38, 3e38, 1e-45, -1e-45], size=(T, nb))
     elif kind in ("random", "long_random"):
         sc = rng.standard_normal((T, nb))
-    elif kind == "int_ties":  # few candidates, often tied at the k-th value
+    elif kind in ("int_ties", "long_int_ties"):  # few candidates, often tied at the k-th value
         sc = rng.integers(0, 3 * nb // 2, size=(T, nb)).astype(np.float64)
     else:  # many ties exactly at the k-th value
         sc = rng.standard_normal((T, nb)) - 10
