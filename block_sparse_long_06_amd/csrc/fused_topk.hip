@@ -232,55 +232,68 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_topk_mfma(Dims D, 
 }
 
 // One thread per row: the k-1 best of the spans' candidates, plus the own block, ascending.
+// With one span the row's list already is its best 15 in order; with several, each span's
+// list is merged into a register list (score descending, id ascending: a span's entries
+// arrive in its own order and every id is above the earlier spans', so a new entry goes
+// after the equal scores already held).  The chosen ids are placed by rank (they are
+// distinct), and the own block, above every ranked id, follows them.
 __global__ void __launch_bounds__(256) topk_merge(Dims D, int nspan, const float* __restrict__ cand_sc,
                                                   const int32_t* __restrict__ cand_id, int32_t* __restrict__ sel) {
-  __shared__ float bs[256][kList];
-  __shared__ int32_t bi[256][kList + 1];
   const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (s, g, t)
   if (row >= (int64_t)D.S * D.Hkv * D.T) return;
   const int t = (int)(row % D.T);
   const int bt = (D.pos0 + t) / kBlk;
   const int want = min(D.k - 1, bt);
-  float* ls = bs[threadIdx.x];
-  int32_t* li = bi[threadIdx.x];
-  int cnt = 0;
-  for (int sp = 0; sp < nspan; ++sp) {
-    const int64_t o = (row * nspan + sp) * kList;
+  int li[kList];
+  if (nspan == 1) {
+#pragma unroll
+    for (int i = 0; i < kList; ++i) li[i] = cand_id[row * kList + i];
+  } else {
+    float ls[kList];
+#pragma unroll
     for (int i = 0; i < kList; ++i) {
-      const int32_t id = cand_id[o + i];
-      if (id < 0) break;
-      const float s = cand_sc[o + i];
-      // better = higher score, then lower id
-      if (cnt == want && want > 0) {
-        const float ws = ls[want - 1];
-        const int32_t wi = li[want - 1];
-        if (!(s > ws || (s == ws && id < wi))) continue;
+      ls[i] = -INFINITY;
+      li[i] = -1;
+    }
+    for (int sp = 0; sp < nspan; ++sp) {
+      const int64_t o = (row * nspan + sp) * kList;
+      for (int j = 0; j < kList; ++j) {
+        const int32_t id = cand_id[o + j];
+        if (id < 0) break;  // the span's list ends
+        const float sc = cand_sc[o + j];
+        if (!(sc > ls[kList - 1])) break;  // the span's later entries score no higher
+        bool gt[kList];
+#pragma unroll
+        for (int i = 0; i < kList; ++i) gt[i] = sc > ls[i];
+#pragma unroll
+        for (int i = kList - 1; i >= 1; --i) {
+          ls[i] = gt[i - 1] ? ls[i - 1] : (gt[i] ? sc : ls[i]);
+          li[i] = gt[i - 1] ? li[i - 1] : (gt[i] ? id : li[i]);
+        }
+        ls[0] = gt[0] ? sc : ls[0];
+        li[0] = gt[0] ? id : li[0];
       }
-      if (want == 0) break;
-      int pos = cnt < want ? cnt : want - 1;
-      while (pos > 0 && (ls[pos - 1] < s || (ls[pos - 1] == s && li[pos - 1] > id))) {
-        ls[pos] = ls[pos - 1];
-        li[pos] = li[pos - 1];
-        --pos;
-      }
-      ls[pos] = s;
-      li[pos] = id;
-      cnt = cnt < want ? cnt + 1 : want;
     }
   }
-  li[cnt++] = bt;  // the own block
-  // ascending ids (insertion sort; at most 16 entries)
-  for (int i = 1; i < cnt; ++i) {
-    const int32_t x = li[i];
-    int j = i - 1;
-    while (j >= 0 && li[j] > x) {
-      li[j + 1] = li[j];
-      --j;
-    }
-    li[j + 1] = x;
+  // the first `want` entries, by rank among themselves (ids are distinct)
+  int v[kList];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kList; ++i) {
+    const bool ok = i < want && li[i] >= 0;
+    v[i] = ok ? li[i] : INT_MAX;
+    cnt += ok ? 1 : 0;
   }
   int32_t* out = sel + row * D.k;
-  for (int i = 0; i < D.k; ++i) out[i] = i < cnt ? li[i] : -1;
+#pragma unroll
+  for (int i = 0; i < kList; ++i) {
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < kList; ++j) r += v[j] < v[i] ? 1 : 0;
+    if (v[i] != INT_MAX) out[r] = v[i];
+  }
+  out[cnt] = bt;
+  for (int i = cnt + 1; i < D.k; ++i) out[i] = -1;
 }
 
 template <int DI, typename TK>
