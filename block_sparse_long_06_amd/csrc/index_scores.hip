@@ -97,6 +97,8 @@ __global__ void __launch_bounds__(kWaves * 64) idx_scores_rows(Dims D, const T* 
 // workgroup covers one contiguous 4 KB run of keys.  The lanes sharing a key add
 // their partial dots with xor shuffles; the block max is a wave reduction over key
 // slots plus an LDS step across the 4 waves.
+typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kStreamT = 8;
 constexpr int kStreamBlocks = 8;
 
@@ -112,7 +114,7 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
   constexpr int CPR = DI / DPL;              // lanes per key row
   constexpr int KPP = 256 / CPR;             // keys per pass of the workgroup
   constexpr int PASSES = 128 / KPP;          // passes per block
-  __shared__ float red[4][TQ];
+  __shared__ float red[kStreamBlocks][4][TQ];  // per (block, wave) maxima, combined at the end
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = threadIdx.x % CPR;
   const int kslot = threadIdx.x / CPR;
@@ -133,22 +135,23 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
   const int bend = min(b0 + kStreamBlocks, (ns + 127) / 128);
   // a block's rows are contiguous (dense cache or one page); an invalid page reads as 0.
   // Loads run one block ahead in registers (kn) so the next block's HBM reads overlap
-  // this block's dot products and reductions; block maxima are written at the end.
+  // this block's dot products and reductions; each key is read once (non-temporal loads).
+  // Each wave leaves its maximum of every block in LDS; the workgroup's four are combined
+  // once, after its last block, so the loop has no barrier.
   auto gload = [&](int b, uint4 (&kr)[PASSES]) {
     const int64_t kb0 = kv_row(D, s, g, b * 128, DI);
     const TK* kbase = k_idx + (kb0 < 0 ? 0 : kb0) + col * DPL;
 #pragma unroll
     for (int u = 0; u < PASSES; ++u) {
       const int jj = u * KPP + kslot;
-      kr[u] = kb0 >= 0 && b * 128 + jj < ns ? *reinterpret_cast<const uint4*>(kbase + (int64_t)jj * DI)
-                                            : make_uint4(0u, 0u, 0u, 0u);
+      kr[u] = kb0 >= 0 && b * 128 + jj < ns
+                  ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                        reinterpret_cast<const nt_u32x4*>(kbase + (int64_t)jj * DI)))
+                  : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   uint4 kr[PASSES], kn[PASSES];
   if (b0 < bend) gload(b0, kn);
-  float bm[kStreamBlocks];
-#pragma unroll
-  for (int i = 0; i < kStreamBlocks; ++i) bm[i] = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kStreamBlocks; ++i) {
     const int b = b0 + i;
@@ -194,22 +197,19 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
       float x = m[tq];
 #pragma unroll
       for (int o = CPR; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-      if (lane == 0) red[wave][tq] = x;
+      if (lane == 0) red[i][wave][tq] = x;
     }
-    __syncthreads();
-    if (threadIdx.x < TQ) {
-      const int tq = threadIdx.x;
-      bm[i] = fmaxf(fmaxf(red[0][tq], red[1][tq]), fmaxf(red[2][tq], red[3][tq]));
-    }
-    __syncthreads();
   }
   if constexpr (!TOKEN) {
+    __syncthreads();
     if (threadIdx.x < TQ && threadIdx.x < T) {
       const int tq = threadIdx.x;
 #pragma unroll
       for (int i = 0; i < kStreamBlocks; ++i) {
         const int b = b0 + i;
-        if (b < bend && b <= pq[tq] / 128) scores[(sg * T + tq) * (int64_t)D.nb + b] = bm[i];
+        if (b < bend && b <= pq[tq] / 128)
+          scores[(sg * T + tq) * (int64_t)D.nb + b] =
+              fmaxf(fmaxf(red[i][0][tq], red[i][1][tq]), fmaxf(red[i][2][tq], red[i][3][tq]));
       }
     }
   }
