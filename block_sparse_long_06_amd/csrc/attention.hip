@@ -306,6 +306,12 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(Dims D, const int32_t* _
   }
 }
 
+// 16 bytes read once (a partial): a non-temporal load.
+__device__ __forceinline__ uint4 load_once(const uint16_t* p) {
+  typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
+}
+
 // The same merge for the common shape (bf16 partials, k <= 16, G * d = 512 * CPL).
 // Without a hot mask every partial load of the lane (up to 16 slots x CPL 16-byte
 // chunks) is issued first, and the selection mask, lse values and weights are worked
@@ -342,15 +348,14 @@ __global__ void __launch_bounds__(256) lse_merge_bf16_k16(Dims D, const int32_t*
     for (int i = 0; i < 16; ++i)
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
-        raw[i][c] = (vmask >> i) & 1ull ? *reinterpret_cast<const uint4*>(prow + (int64_t)i * GD + (lane + 64 * c) * 8)
+        raw[i][c] = (vmask >> i) & 1ull ? load_once(prow + (int64_t)i * GD + (lane + 64 * c) * 8)
                                         : make_uint4(0u, 0u, 0u, 0u);
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
-        raw[i][c] = i < D.k ? *reinterpret_cast<const uint4*>(prow + (int64_t)i * GD + (lane + 64 * c) * 8)
-                            : make_uint4(0u, 0u, 0u, 0u);
+        raw[i][c] = i < D.k ? load_once(prow + (int64_t)i * GD + (lane + 64 * c) * 8) : make_uint4(0u, 0u, 0u, 0u);
     vmask = __ballot(lane < D.k && sl[lane < D.k ? lane : 0] >= 0);
   }
   const float* lrow = part_lse + row * KG;

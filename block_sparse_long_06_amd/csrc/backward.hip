@@ -398,8 +398,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
 
 // dq[s, t, h, :] = sum over the valid slots of row (s, t, g) of its bf16 partials; one
 // thread per 8 head dims.
+template <int KR>
 __global__ void __launch_bounds__(256) dq_merge(Dims D, const int32_t* __restrict__ sel,
                                                 const uint16_t* __restrict__ part_dq, float* __restrict__ dq) {
+  typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int gd8 = D.G * D.d / 8;
   const int64_t row = i / gd8;  // (s, t, g)
@@ -409,15 +411,35 @@ __global__ void __launch_bounds__(256) dq_merge(Dims D, const int32_t* __restric
   const int t = (int)((row / D.Hkv) % D.T);
   const int s = (int)(row / ((int64_t)D.Hkv * D.T));
   const int32_t* sl = sel + (((int64_t)s * D.Hkv + g) * D.T + t) * D.k;
+  const uint16_t* pr = part_dq + row * D.k * (int64_t)D.G * D.d + c8 * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int slot = 0; slot < D.k; ++slot) {
-    if (sl[slot] < 0) continue;
-    const uint4 u = *reinterpret_cast<const uint4*>(part_dq + (row * D.k + slot) * (int64_t)D.G * D.d + c8 * 8);
+  auto add = [&](const uint4& u) {
     const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       acc[2 * x] += bf16_to_f32((uint16_t)(wv[x] & 0xFFFFu));
       acc[2 * x + 1] += bf16_to_f32((uint16_t)(wv[x] >> 16));
+    }
+  };
+  if constexpr (KR > 0) {
+    // k <= KR: every partial of the thread is loaded (read once: non-temporal) before the
+    // first add; the adds keep the ascending slot order
+    uint4 u[KR];
+    bool ok[KR];
+#pragma unroll
+    for (int slot = 0; slot < KR; ++slot) {
+      ok[slot] = slot < D.k && sl[slot < D.k ? slot : 0] >= 0;
+      u[slot] = ok[slot] ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(
+                               pr + slot * (int64_t)D.G * D.d)))
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int slot = 0; slot < KR; ++slot)
+      if (ok[slot]) add(u[slot]);
+  } else {
+    for (int slot = 0; slot < D.k; ++slot) {
+      if (sl[slot] < 0) continue;
+      add(*reinterpret_cast<const uint4*>(pr + slot * (int64_t)D.G * D.d));
     }
   }
   float* o = dq + (((int64_t)s * D.T + t) * D.H + (int64_t)g * D.G) * D.d + c8 * 8;
@@ -823,7 +845,10 @@ hipError_t launch_attn_backward(const Dims& D, const void* q, const void* k, con
   if (e != hipSuccess) return e;
   const int64_t nthreads = (int64_t)D.S * D.T * D.Hkv * (D.G * D.d / 8);
   LaunchScope scope("dq_merge", st);
-  hipLaunchKernelGGL(dq_merge, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, D, sel, w.part_dq, dq);
+  if (D.k <= 16)
+    hipLaunchKernelGGL(dq_merge<16>, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, D, sel, w.part_dq, dq);
+  else
+    hipLaunchKernelGGL(dq_merge<0>, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, D, sel, w.part_dq, dq);
   return hipGetLastError();
 }
 
