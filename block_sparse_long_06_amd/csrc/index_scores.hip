@@ -134,8 +134,8 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
   }
   const int bend = min(b0 + kStreamBlocks, (ns + 127) / 128);
   // a block's rows are contiguous (dense cache or one page); an invalid page reads as 0.
-  // Loads run one block ahead in registers (kn) so the next block's HBM reads overlap
-  // this block's dot products and reductions; each key is read once (non-temporal loads).
+  // Loads run ahead in registers so the next blocks' HBM reads overlap this block's dot
+  // products and reductions; each key is read once (non-temporal loads).
   // Each wave leaves its maximum of every block in LDS; the workgroup's four are combined
   // once, after its last block, so the loop has no barrier.
   auto gload = [&](int b, uint4 (&kr)[PASSES]) {
@@ -150,15 +150,27 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
                   : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  uint4 kr[PASSES], kn[PASSES];
+  // (two ahead with one query row, the decode shape; one ahead with TQ rows, whose query
+  // registers leave no room for a third set)
+  constexpr bool AHEAD2 = TQ == 1;
+  uint4 kr[PASSES], kn[PASSES], kn2[AHEAD2 ? PASSES : 1];
   if (b0 < bend) gload(b0, kn);
+  if constexpr (AHEAD2) {
+    if (b0 + 1 < bend) gload(b0 + 1, kn2);
+  }
 #pragma unroll
   for (int i = 0; i < kStreamBlocks; ++i) {
     const int b = b0 + i;
     if (b >= bend) break;
 #pragma unroll
     for (int u = 0; u < PASSES; ++u) kr[u] = kn[u];
-    if (b + 1 < bend) gload(b + 1, kn);
+    if constexpr (AHEAD2) {
+#pragma unroll
+      for (int u = 0; u < PASSES; ++u) kn[u] = kn2[u];
+      if (b + 2 < bend) gload(b + 2, kn2);
+    } else {
+      if (b + 1 < bend) gload(b + 1, kn);
+    }
     float m[TQ];
 #pragma unroll
     for (int tq = 0; tq < TQ; ++tq) m[tq] = -INFINITY;
