@@ -70,8 +70,25 @@ def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
     _drain(procs, verbose)
     tmp = lib + ".tmp%d" % os.getpid()
     subprocess.run(["hipcc", "-shared", "--offload-arch=" + ARCH, *objs, "-o", tmp], check=True)
+    missing = undefined_kernel_stubs(tmp)
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("libmsa links kernels whose host launch stubs were not emitted (a kernel body the "
+                           "host pass rejected?): " + ", ".join(missing[:4]))
     os.replace(tmp, lib)
     return lib
+
+
+def undefined_kernel_stubs(lib: str) -> list:
+    """Kernel launch stubs the shared library references but does not define.  The host
+    pass of hipcc drops a template kernel's stub without an error when the instantiated
+    body uses device-only builtins inside host-device code (a lambda), and a shared library
+    links with the reference unresolved, so only loading it would fail."""
+    try:
+        out = subprocess.run(["nm", "-D", "--undefined-only", lib], check=True, capture_output=True, text=True).stdout
+    except (OSError, subprocess.CalledProcessError):
+        return []  # no nm: nothing to check with
+    return [line.split()[-1] for line in out.splitlines() if "__device_stub__" in line]
 
 
 def _drain(procs, verbose):

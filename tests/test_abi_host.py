@@ -26,6 +26,13 @@ def test_header_declares_the_five_hot_path_calls():
         assert f in names
 
 
+def test_library_defines_every_kernel_launch_stub():
+    """Every kernel the library launches has its host launch stub (a stub dropped by the
+    host compiler pass leaves an undefined symbol that only loading would report)."""
+    from block_sparse_long_06_amd import _build
+    assert _build.undefined_kernel_stubs(msa.LIB_PATH) == []
+
+
 def test_library_exports_every_declared_symbol():
     L = msa.lib()
     for name in _declared():
