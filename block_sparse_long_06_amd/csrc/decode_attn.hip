@@ -104,7 +104,9 @@ __global__ void __launch_bounds__(256) decode_attn(Dims D, const uint16_t* __res
   const int nvalid = kv0 < 0 ? 0 : min(kB, seq_len(D, s) - j0);
 
   // V -> LDS (direct loads; pad slots re-read a chunk of the same row, never read back;
-  // rows past the end repeat row 0: their keys are masked causally, so P = 0 there)
+  // rows past the end repeat row 0: their keys are masked causally, so P = 0 there).  K and
+  // V are read once per step, with non-temporal loads: after the index stream's
+  // non-temporal sweep of the index keys, ordinary loads here measured 50 against 35 us.
   if (kv0 >= 0) {
     typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
@@ -114,7 +116,7 @@ __global__ void __launch_bounds__(256) decode_attn(Dims D, const uint16_t* __res
       const int r = x / VROW, o = x % VROW;
       const int c = o < DH * 2 ? o / 16 : 0;
       const int rr = r < nvalid ? r : 0;
-      __builtin_amdgcn_global_load_lds(v + kv0 + (int64_t)rr * DH + c * 8, (lds_void*)(vt + off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(v + kv0 + (int64_t)rr * DH + c * 8, (lds_void*)(vt + off), 16, 0, 2);
     }
   } else {
     for (int i = threadIdx.x; i < VB / 16; i += 256) reinterpret_cast<u32x4*>(vt)[i] = u32x4{0u, 0u, 0u, 0u};
@@ -128,7 +130,8 @@ __global__ void __launch_bounds__(256) decode_attn(Dims D, const uint16_t* __res
     const int rr = key < nvalid ? key : 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      ka[tt][ks] = kv0 >= 0 ? *reinterpret_cast<const bf16x8*>(k + kv0 + (int64_t)rr * DH + 32 * ks + 8 * gl)
+      ka[tt][ks] = kv0 >= 0 ? __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                  k + kv0 + (int64_t)rr * DH + 32 * ks + 8 * gl)))
                             : bf16x8{};
   }
   const bool head_ok = n < G;
