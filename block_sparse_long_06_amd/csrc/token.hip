@@ -287,37 +287,56 @@ __global__ void __launch_bounds__(256) tk_filter(Dims D, int budget, int nch, co
     r.head[2] = b1;
     r.head[3] = (uint32_t)s_above;
   }
-  // ---- candidates of the chunk in position order: thread i takes 4 consecutive positions
-  // of each 1024-position tile
+  // ---- candidates of the chunk in position order: wave w takes the chunk's w-th quarter,
+  // 256 positions per step (4 consecutive per lane), ranks its candidates with a wave scan
+  // and keeps them in its quarter of the LDS buffer; the quarters follow in wave order
   const float* sc = tok + row * (int64_t)D.N;
-  int C = 0;
-  for (int base = j0; base < j1; base += 1024) {
-    const int j = base + 4 * (int)threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kQuarter = kTkLocal / 4;
+  uint32_t* wkey = lkey + wave * kQuarter;
+  int32_t* wpos = lpos + wave * kQuarter;
+  const int q0 = j0 + wave * (kTkChunk / 4), q1 = min(j1, q0 + kTkChunk / 4);
+  int cw = 0;
+  for (int base = q0; base < q1; base += 256) {
+    const int j = base + 4 * lane;
     uint32_t k4[4];
     int f = 0;
+    if (j + 3 < q1 && ((reinterpret_cast<uintptr_t>(sc + j) & 15) == 0)) {
+      const float4 v4 = *reinterpret_cast<const float4*>(sc + j);
+      k4[0] = ord_key(v4.x); k4[1] = ord_key(v4.y); k4[2] = ord_key(v4.z); k4[3] = ord_key(v4.w);
+    } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      k4[u] = j + u < j1 ? ord_key(sc[j + u]) : 0u;
-      f += (j + u < j1 && k4[u] >= t1) ? 1 : 0;
+      for (int u = 0; u < 4; ++u) k4[u] = j + u < q1 ? ord_key(sc[j + u]) : 0u;
     }
-    int ttot;
-    int at = C + block_scan256(f, wsum, &ttot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) f += (j + u < q1 && k4[u] >= t1) ? 1 : 0;
+    int x = f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    int at = cw + x - f;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (j + u < j1 && k4[u] >= t1) {
-        if (at < kTkLocal) {
-          lkey[at] = k4[u];
-          lpos[at] = j + u;
+      if (j + u < q1 && k4[u] >= t1) {
+        if (at < kQuarter) {
+          wkey[at] = k4[u];
+          wpos[at] = j + u;
         }
         ++at;
       }
-    C += ttot;
+    cw += __shfl(x, 63, 64);
   }
+  if (lane == 0) wsum[wave] = cw;
   __syncthreads();
+  const int c0 = wsum[0], c1 = wsum[1], c2 = wsum[2], c3 = wsum[3];
+  const int C = c0 + c1 + c2 + c3;
+  const bool wover = c0 > kQuarter || c1 > kQuarter || c2 > kQuarter || c3 > kQuarter;
   __shared__ uint32_t s_base;
   if (threadIdx.x == 0) {
-    const uint32_t b = C <= kTkLocal ? atomicAdd(&r.head[0], (uint32_t)C) : (uint32_t)kTkCap + 1u;
-    const bool over = C > kTkLocal || b + (uint32_t)C > (uint32_t)kTkCap;
+    const uint32_t b = wover ? (uint32_t)kTkCap + 1u : atomicAdd(&r.head[0], (uint32_t)C);
+    const bool over = wover || b + (uint32_t)C > (uint32_t)kTkCap;
     if (over) atomicOr(&r.head[1], 1u);
     s_base = over ? 0xFFFFFFFFu : b;
     r.coff[chunk] = over ? 0u : b;
@@ -326,9 +345,10 @@ __global__ void __launch_bounds__(256) tk_filter(Dims D, int budget, int nch, co
   __syncthreads();
   const uint32_t b = s_base;
   if (b == 0xFFFFFFFFu) return;
-  for (int i = threadIdx.x; i < C; i += 256) {
-    r.ckey[b + i] = lkey[i];
-    r.cpos[b + i] = lpos[i];
+  const uint32_t wb = b + (uint32_t)((wave > 0 ? c0 : 0) + (wave > 1 ? c1 : 0) + (wave > 2 ? c2 : 0));
+  for (int i = lane; i < cw; i += 64) {
+    r.ckey[wb + i] = wkey[i];
+    r.cpos[wb + i] = wpos[i];
   }
 }
 
