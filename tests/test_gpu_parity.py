@@ -36,6 +36,10 @@ CASES = [
     # k >= nb for most rows: every causal block is chosen by every row of a tile, so the
     # last tiles have more than 32 blocks that qualify as tile-shared (the cap applies)
     W.small("bf16_k64_all_blocks_shared", S=1, T=5120, N=5120, H=8, Hkv=1, d=128, dI=64, k=64),
+    # k > 16 (the generic selection, inversion and merge paths) with structured selections,
+    # queries from position 700: query tiles straddle the inversion's 64-row steps
+    W.small("bf16_k24_structured_offset", S=1, T=1900, N=2600, H=16, Hkv=2, d=128, dI=64, k=24,
+            structure="band_sink_needles"),
     W.small("fp32_g2_d128", S=2, T=500, N=777, H=4, Hkv=2, d=128, dI=64, k=5, dtype=synth.F32),
     W.small("fp32_g8_d64", S=1, T=1200, N=1300, H=8, Hkv=1, d=64, dI=32, k=6, dtype=synth.F32),
 ]
