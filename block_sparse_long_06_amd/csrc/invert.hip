@@ -13,8 +13,9 @@
 //  4. scatter: one wave per chunk walks its rows 64 at a time (lane = row).  For
 //              each block, a 64-bit LDS mask of the lanes that chose it gives each
 //              lane its rank among the earlier lanes (popcount of the lower bits),
-//              and a per-block running count carries ranks across steps, so every
-//              list comes out in ascending row order.
+//              and a per-block LDS word holding the list position of the block's next
+//              entry carries ranks across steps, so every list comes out in ascending
+//              row order.
 #include "msa_internal.hpp"
 #include "scan.hpp"
 
