@@ -442,11 +442,11 @@ __global__ void __launch_bounds__(kTkThreads) tk_finish(Dims D, int budget, int 
 
 template <int DH>
 struct TokLds {
-  float k[kChunk][DH + 1];  // padded: lane-per-key reads are conflict-free
+  uint16_t k[kChunk][DH + 2];  // bf16, rows of DH / 2 + 1 words: lane-per-key reads are conflict-free
   uint16_t v[kChunk][DH];
   int32_t pos[kChunk];
-  float p[16][kChunk];       // per head (wave): probabilities
-  float q[16][DH];
+  float p[16][kChunk];         // per head (wave): probabilities
+  uint16_t q[16][DH];          // bf16 (78 KB in all: two workgroups per CU)
 };
 
 // Work item (row (s, t, g), chunk c): tokens sel_tok[(s, g, t), c*128 ...]; wave h = head h.
@@ -484,16 +484,13 @@ __global__ void __launch_bounds__(1024) token_attn(Dims D, int budget, int nch, 
     }
     const uint32_t wk[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      L.k[j][cc + 2 * x] = bf16_to_f32((uint16_t)(wk[x] & 0xFFFFu));
-      L.k[j][cc + 2 * x + 1] = bf16_to_f32((uint16_t)(wk[x] >> 16));
-    }
+    for (int x = 0; x < 4; ++x) *reinterpret_cast<uint32_t*>(&L.k[j][cc + 2 * x]) = wk[x];
     *reinterpret_cast<uint4*>(&L.v[j][cc]) = vv;
   }
   const int h = wave;  // one wave per query head of the group
   const uint16_t* qv = q + (((int64_t)s * D.T + t) * D.H + (int64_t)g * D.G + h) * DH;
   if (h < D.G)
-    for (int cc = lane; cc < DH; cc += 64) L.q[h][cc] = bf16_to_f32(qv[cc]);
+    for (int cc = lane; cc < DH; cc += 64) L.q[h][cc] = qv[cc];
   __syncthreads();
   if (h >= D.G) return;
   float lg[2];
@@ -503,7 +500,12 @@ __global__ void __launch_bounds__(1024) token_attn(Dims D, int budget, int nch, 
     lg[u] = -INFINITY;
     if (L.pos[j] >= 0) {
       float acc = 0.0f;
-      for (int cc = 0; cc < DH; ++cc) acc = fmaf(L.q[h][cc], L.k[j][cc], acc);
+      for (int cc = 0; cc < DH; cc += 2) {
+        const uint32_t kw = *reinterpret_cast<const uint32_t*>(&L.k[j][cc]);
+        const uint32_t qw = *reinterpret_cast<const uint32_t*>(&L.q[h][cc]);
+        acc = fmaf(bf16_to_f32((uint16_t)(qw & 0xFFFFu)), bf16_to_f32((uint16_t)(kw & 0xFFFFu)), acc);
+        acc = fmaf(bf16_to_f32((uint16_t)(qw >> 16)), bf16_to_f32((uint16_t)(kw >> 16)), acc);
+      }
       lg[u] = acc * D.scale;
     }
   }
