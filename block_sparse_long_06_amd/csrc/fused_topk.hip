@@ -34,7 +34,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kQT = 4;           // 32-query tiles per wave
 constexpr int kQW = 32 * kQT;    // queries per wave
-constexpr int kQB = 4 * kQW;     // queries per workgroup
+// Waves per workgroup W: 4 (512 query rows), or 8 (1024 rows sharing each staged key block:
+// fewer staging loads per product) where each row tile has about the same work -- a chunk
+// far into its sequence -- and the registers allow two waves per SIMD (d_I <= 64); with
+// causal row tiles the longer tiles of eight waves made the launch's tail longer.
 constexpr int kChunk = 16;       // blocks merged per step
 constexpr int kSpan = 1024;      // blocks per span (workgroup)
 constexpr int kBlk = 128;
@@ -100,16 +103,19 @@ __device__ __forceinline__ void list_merge(RowList& L, const float* src, int nv,
   }
 }
 
-template <int DI, typename TK>
-__global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_topk_mfma(Dims D, const uint16_t* __restrict__ q_idx,
+template <int DI, typename TK, int W>
+__global__ void __launch_bounds__(64 * W, (DI == 128 || W == 8) ? 1 : 2) idx_topk_mfma(Dims D, const uint16_t* __restrict__ q_idx,
                                                         const TK* __restrict__ k_idx, float* __restrict__ cand_sc,
                                                         int32_t* __restrict__ cand_id, int nspan) {
   constexpr int KS = DI / 16;
   constexpr int ROWB = DI * 2 + 16;
   constexpr int CPR = DI / 8;
-  constexpr int PER_T = kBlk * CPR / 256;
+  constexpr int NT = 64 * W;
+  constexpr int kQB = W * kQW;  // queries per workgroup
+  constexpr int PER_T = kBlk * CPR / NT;
+  static_assert(PER_T >= 1 && PER_T * NT == kBlk * CPR, "whole 16-byte pieces per thread");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][kBlk * ROWB];
-  __shared__ __attribute__((aligned(16))) float outb[4][kQW][kChunk + 4];  // 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) float outb[W][kQW][kChunk + 4];  // 16-byte aligned rows
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -149,7 +155,7 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_topk_mfma(Dims D, 
     auto gload = [&](int b) {
 #pragma unroll
       for (int u = 0; u < PER_T; ++u) {
-        const int c = threadIdx.x + 256 * u;
+        const int c = threadIdx.x + NT * u;
         const int row = c / CPR, col = c % CPR;
         const int j = b * kBlk + row;
         stage[u] = j < D.N ? *reinterpret_cast<const Piece*>(kbase + (int64_t)j * DI + col * 8) : Piece{};
@@ -158,7 +164,7 @@ __global__ void __launch_bounds__(256, DI == 128 ? 1 : 2) idx_topk_mfma(Dims D, 
     auto lstore = [&](int buf) {
 #pragma unroll
       for (int u = 0; u < PER_T; ++u) {
-        const int c = threadIdx.x + 256 * u;
+        const int c = threadIdx.x + NT * u;
         const int row = c / CPR, col = c % CPR;
         uint4 w;
         if constexpr (sizeof(TK) == 2) {
@@ -296,10 +302,20 @@ __global__ void __launch_bounds__(256) topk_merge(Dims D, int nspan, const float
   for (int i = cnt + 1; i < D.k; ++i) out[i] = -1;
 }
 
+template <int DI, typename TK, int W>
+void launch_fused_w(const Dims& D, dim3 grid, const uint16_t* q, const TK* k, float* cs, int32_t* ci, int nspan,
+                    hipStream_t st) {
+  const dim3 g(grid.x, grid.y, (unsigned)((D.T + W * kQW - 1) / (W * kQW)));
+  hipLaunchKernelGGL((idx_topk_mfma<DI, TK, W>), g, dim3(64 * W), 0, st, D, q, k, cs, ci, nspan);
+}
+
 template <int DI, typename TK>
 void launch_fused_t(const Dims& D, dim3 grid, const uint16_t* q, const TK* k, float* cs, int32_t* ci, int nspan,
                     hipStream_t st) {
-  hipLaunchKernelGGL((idx_topk_mfma<DI, TK>), grid, dim3(256), 0, st, D, q, k, cs, ci, nspan);
+  if constexpr (DI <= 64) {
+    if ((int64_t)D.pos0 >= 4 * (int64_t)D.T) return launch_fused_w<DI, TK, 8>(D, grid, q, k, cs, ci, nspan, st);
+  }
+  launch_fused_w<DI, TK, 4>(D, grid, q, k, cs, ci, nspan, st);
 }
 
 template <typename TK>
@@ -338,7 +354,7 @@ hipError_t launch_index_topk(const Dims& D, const void* q_idx, const void* k_idx
   float* cs = static_cast<float*>(ws);
   int32_t* ci = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + align_up(n * sizeof(float), 256));
   {
-    const dim3 grid((unsigned)(D.S * D.Hkv), (unsigned)nspan, (unsigned)((D.T + kQB - 1) / kQB));
+    const dim3 grid((unsigned)(D.S * D.Hkv), (unsigned)nspan, 1u);  // row tiles: set per d_I at launch
     LaunchScope scope("idx_topk_mfma", st);
     const uint16_t* q = static_cast<const uint16_t*>(q_idx);
     if (D.kdtype == MSA_FP8_E4M3) launch_fused(D, grid, q, static_cast<const uint8_t*>(k_idx), cs, ci, nspan, st);

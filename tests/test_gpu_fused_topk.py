@@ -24,6 +24,10 @@ CASES = [
     W.small("fused_e4m3_dI32_k4", S=1, T=2048, N=2600, H=8, Hkv=2, d=64, dI=32, k=4, kidx_dtype=synth.FP8),
     W.small("fused_dI128_k1", S=1, T=700, N=900, H=8, Hkv=1, d=128, dI=128, k=1),
     W.small("fused_short_T", S=2, T=40, N=5000, H=8, Hkv=2, d=128, dI=64, k=16),
+    # chunks far into their sequences: eight-wave workgroups (1024 query rows), a ragged
+    # second row tile, and E4M3 keys at d_I = 32
+    W.small("fused_chunk_at_end", S=2, T=1500, N=40000, H=8, Hkv=2, d=128, dI=64, k=16),
+    W.small("fused_e4m3_chunk_at_end", S=1, T=700, N=30000, H=8, Hkv=2, d=64, dI=32, k=4, kidx_dtype=synth.FP8),
 ]
 
 
