@@ -197,7 +197,8 @@ __global__ void __launch_bounds__(256) idx_scores_stream(Dims D, const uint16_t*
 #pragma unroll
         for (int o = 1; o < CPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
         if constexpr (TOKEN) {
-          if (col == 0 && tq < T && j <= pq[tq]) scores[(sg * T + tq) * (int64_t)D.N + j] = acc;
+          if (col == 0 && tq < T && j <= pq[tq])
+            __builtin_nontemporal_store(acc, &scores[(sg * T + tq) * (int64_t)D.N + j]);
         } else {
           if (j <= pq[tq]) m[tq] = fmaxf(m[tq], acc);
         }
