@@ -211,7 +211,9 @@ __device__ __forceinline__ void store8(uint16_t* p, const float* v) {
   u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
   u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
   u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-  *reinterpret_cast<uint4*>(p) = u;
+  // the merged output is not read again by this library: a non-temporal store
+  typedef unsigned u32x4_st __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_st, u), reinterpret_cast<u32x4_st*>(p));
 }
 
 // One wave per row (s, t, g).  The row's slot lse values (k x G floats, contiguous)
