@@ -442,9 +442,11 @@ __global__ void __launch_bounds__(256) dq_merge(Dims D, const int32_t* __restric
       add(*reinterpret_cast<const uint4*>(pr + slot * (int64_t)D.G * D.d));
     }
   }
-  float* o = dq + (((int64_t)s * D.T + t) * D.H + (int64_t)g * D.G) * D.d + c8 * 8;
-  *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  // dq is not read again by this library: non-temporal stores
+  typedef float f32x4_st __attribute__((ext_vector_type(4)));
+  f32x4_st* o = reinterpret_cast<f32x4_st*>(dq + (((int64_t)s * D.T + t) * D.H + (int64_t)g * D.G) * D.d + c8 * 8);
+  __builtin_nontemporal_store(f32x4_st{acc[0], acc[1], acc[2], acc[3]}, o);
+  __builtin_nontemporal_store(f32x4_st{acc[4], acc[5], acc[6], acc[7]}, o + 1);
 }
 
 // Per row: KL(teacher || student) over the selected blocks and d loss / d block score.
