@@ -360,7 +360,8 @@ __global__ void __launch_bounds__(kThreads) ogq_mfma(Dims D, const uint16_t* __r
         __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(buf + mr * OgqLds<DH>::QROW + col * 16),
                                     reinterpret_cast<u32x4*>(part_o + (L.pidx[r0 + r] * G + hh) * DH + col * 8));
     }
-    if (lane < 32 && lane / G < nrows) part_lse[L.pidx[r0 + lane / G] * G + lane % G] = L.lse[wave][lane];
+    if (lane < 32 && lane / G < nrows)
+      __builtin_nontemporal_store(L.lse[wave][lane], &part_lse[L.pidx[r0 + lane / G] * G + lane % G]);
 
     j += kWaves;
     if (j >= nsub) break;
