@@ -17,9 +17,11 @@
 // above the list's last one (-inf while the list has room, so -inf and NaN never enter).
 // Only blocks b < b_t (strictly in the row's past) are ranked: the own block is forced,
 // later blocks are not eligible -- so no causal mask is needed.  Each (row, span) list is
-// written out (score, id; id -1 for empty entries).
+// written out (score, id; id -1 for empty entries) -- or, when the keys fit one span
+// (nb <= kSpan), the list already is the row's ranking and the lane writes the row's
+// selection itself.
 //
-// topk_merge: one thread per row merges its spans' lists into the k-1 best blocks (score
+// topk_merge (several spans): one thread per row merges its spans' lists into the k-1 best blocks (score
 // descending, id ascending), appends the own block and writes them in ascending order,
 // padded with -1: the output of msa_block_topk.
 #include "msa_internal.hpp"
@@ -103,10 +105,35 @@ __device__ __forceinline__ void list_merge(RowList& L, const float* src, int nv,
   }
 }
 
+// The row's selection from its list of best blocks (score descending, id ascending): the
+// first min(k - 1, b_t) entries ranked by id (ids are distinct), then the own block b_t,
+// then -1 padding -- the output of msa_block_topk.
+__device__ __forceinline__ void emit_row(const Dims& D, const int (&li)[kList], int bt, int32_t* out) {
+  const int want = min(D.k - 1, bt);
+  int v[kList];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kList; ++i) {
+    const bool ok = i < want && li[i] >= 0;
+    v[i] = ok ? li[i] : INT_MAX;
+    cnt += ok ? 1 : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kList; ++i) {
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < kList; ++j) r += v[j] < v[i] ? 1 : 0;
+    if (v[i] != INT_MAX) out[r] = v[i];
+  }
+  out[cnt] = bt;
+  for (int i = cnt + 1; i < D.k; ++i) out[i] = -1;
+}
+
 template <int DI, typename TK, int W>
 __global__ void __launch_bounds__(64 * W, (DI == 128 || W == 8) ? 1 : 2) idx_topk_mfma(Dims D, const uint16_t* __restrict__ q_idx,
                                                         const TK* __restrict__ k_idx, float* __restrict__ cand_sc,
-                                                        int32_t* __restrict__ cand_id, int nspan) {
+                                                        int32_t* __restrict__ cand_id, int nspan,
+                                                        int32_t* __restrict__ sel) {
   constexpr int KS = DI / 16;
   constexpr int ROWB = DI * 2 + 16;
   constexpr int CPR = DI / 8;
@@ -226,6 +253,10 @@ __global__ void __launch_bounds__(64 * W, (DI == 128 || W == 8) ? 1 : 2) idx_top
   }
   auto put = [&](const RowList& L, int tr) {
     if (tr >= D.T) return;
+    if (sel != nullptr) {  // one span: the list is the row's final ranking
+      emit_row(D, L.li, (D.pos0 + tr) / kBlk, sel + (sg * D.T + tr) * D.k);
+      return;
+    }
     const int64_t o = ((sg * D.T + tr) * nspan + span) * kList;
 #pragma unroll
     for (int i = 0; i < kList; ++i) {
@@ -249,7 +280,6 @@ __global__ void __launch_bounds__(256) topk_merge(Dims D, int nspan, const float
   if (row >= (int64_t)D.S * D.Hkv * D.T) return;
   const int t = (int)(row % D.T);
   const int bt = (D.pos0 + t) / kBlk;
-  const int want = min(D.k - 1, bt);
   int li[kList];
   if (nspan == 1) {
 #pragma unroll
@@ -281,49 +311,31 @@ __global__ void __launch_bounds__(256) topk_merge(Dims D, int nspan, const float
       }
     }
   }
-  // the first `want` entries, by rank among themselves (ids are distinct)
-  int v[kList];
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < kList; ++i) {
-    const bool ok = i < want && li[i] >= 0;
-    v[i] = ok ? li[i] : INT_MAX;
-    cnt += ok ? 1 : 0;
-  }
-  int32_t* out = sel + row * D.k;
-#pragma unroll
-  for (int i = 0; i < kList; ++i) {
-    int r = 0;
-#pragma unroll
-    for (int j = 0; j < kList; ++j) r += v[j] < v[i] ? 1 : 0;
-    if (v[i] != INT_MAX) out[r] = v[i];
-  }
-  out[cnt] = bt;
-  for (int i = cnt + 1; i < D.k; ++i) out[i] = -1;
+  emit_row(D, li, bt, sel + row * D.k);
 }
 
 template <int DI, typename TK, int W>
 void launch_fused_w(const Dims& D, dim3 grid, const uint16_t* q, const TK* k, float* cs, int32_t* ci, int nspan,
-                    hipStream_t st) {
+                    int32_t* sel, hipStream_t st) {
   const dim3 g(grid.x, grid.y, (unsigned)((D.T + W * kQW - 1) / (W * kQW)));
-  hipLaunchKernelGGL((idx_topk_mfma<DI, TK, W>), g, dim3(64 * W), 0, st, D, q, k, cs, ci, nspan);
+  hipLaunchKernelGGL((idx_topk_mfma<DI, TK, W>), g, dim3(64 * W), 0, st, D, q, k, cs, ci, nspan, sel);
 }
 
 template <int DI, typename TK>
 void launch_fused_t(const Dims& D, dim3 grid, const uint16_t* q, const TK* k, float* cs, int32_t* ci, int nspan,
-                    hipStream_t st) {
+                    int32_t* sel, hipStream_t st) {
   if constexpr (DI <= 64) {
-    if ((int64_t)D.pos0 >= 4 * (int64_t)D.T) return launch_fused_w<DI, TK, 8>(D, grid, q, k, cs, ci, nspan, st);
+    if ((int64_t)D.pos0 >= 4 * (int64_t)D.T) return launch_fused_w<DI, TK, 8>(D, grid, q, k, cs, ci, nspan, sel, st);
   }
-  launch_fused_w<DI, TK, 4>(D, grid, q, k, cs, ci, nspan, st);
+  launch_fused_w<DI, TK, 4>(D, grid, q, k, cs, ci, nspan, sel, st);
 }
 
 template <typename TK>
 void launch_fused(const Dims& D, dim3 grid, const uint16_t* q, const TK* k, float* cs, int32_t* ci, int nspan,
-                  hipStream_t st) {
-  if (D.dI == 32) launch_fused_t<32, TK>(D, grid, q, k, cs, ci, nspan, st);
-  else if (D.dI == 64) launch_fused_t<64, TK>(D, grid, q, k, cs, ci, nspan, st);
-  else launch_fused_t<128, TK>(D, grid, q, k, cs, ci, nspan, st);
+                  int32_t* sel, hipStream_t st) {
+  if (D.dI == 32) launch_fused_t<32, TK>(D, grid, q, k, cs, ci, nspan, sel, st);
+  else if (D.dI == 64) launch_fused_t<64, TK>(D, grid, q, k, cs, ci, nspan, sel, st);
+  else launch_fused_t<128, TK>(D, grid, q, k, cs, ci, nspan, sel, st);
 }
 
 int num_spans(const Dims& D) { return (D.nb + kSpan - 1) / kSpan; }
@@ -353,15 +365,20 @@ hipError_t launch_index_topk(const Dims& D, const void* q_idx, const void* k_idx
   const size_t n = (size_t)D.S * D.Hkv * D.T * nspan * kList;
   float* cs = static_cast<float*>(ws);
   int32_t* ci = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + align_up(n * sizeof(float), 256));
+  // with one span (nb <= kSpan) the kernel's lists are final: it writes sel itself and no
+  // merge pass runs
+  int32_t* direct = nspan == 1 ? sel : nullptr;
   {
     const dim3 grid((unsigned)(D.S * D.Hkv), (unsigned)nspan, 1u);  // row tiles: set per d_I at launch
     LaunchScope scope("idx_topk_mfma", st);
     const uint16_t* q = static_cast<const uint16_t*>(q_idx);
-    if (D.kdtype == MSA_FP8_E4M3) launch_fused(D, grid, q, static_cast<const uint8_t*>(k_idx), cs, ci, nspan, st);
-    else launch_fused(D, grid, q, static_cast<const uint16_t*>(k_idx), cs, ci, nspan, st);
+    if (D.kdtype == MSA_FP8_E4M3)
+      launch_fused(D, grid, q, static_cast<const uint8_t*>(k_idx), cs, ci, nspan, direct, st);
+    else
+      launch_fused(D, grid, q, static_cast<const uint16_t*>(k_idx), cs, ci, nspan, direct, st);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || direct != nullptr) return e;
   const int64_t rows = (int64_t)D.S * D.Hkv * D.T;
   LaunchScope scope("topk_merge", st);
   hipLaunchKernelGGL(topk_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, D, nspan, cs, ci, sel);
