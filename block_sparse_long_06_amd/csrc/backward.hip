@@ -8,16 +8,17 @@
 //  * attn_bwd: gradients of the block-sparse main branch (dQ, dK, dV) in the Outer-Gather-Q
 //    order of section Kernel 创新：Outer Gather Q: one work item = (sequence, group, KV
 //    block) and up to kRows rows of its inverted list; the block's K, V and K^T are staged
-//    once and every gathered row is processed against them.  Each of the 4 waves owns 32
-//    keys.  Per sub-chunk of 32 M-rows (M-row = (row, head)):
-//        S = Q K^T and dP = dO V^T          (v_mfma_f32_32x32x16_bf16; lane = key,
-//                                              registers = M-rows)
+//    once and every gathered row is processed against them.  Each of the 8 waves owns 16
+//    keys (two waves per SIMD).  Per sub-chunk of 32 M-rows (M-row = (row, head)):
+//        S = Q K^T and dP = dO V^T          (v_mfma_f32_16x16x32_bf16, two 16-M-row
+//                                              tiles; lane column = key)
 //        P = exp2(S scale log2e - lse log2e),  dS = P (dP - D)      (D = rowsum(dO o O))
-//        dV^T += dO^T P,  dK^T += Q^T dS    (the P / dS registers are the B operands: their
-//                                              M-row order is the accumulator's; dO^T and
-//                                              Q^T are stored in LDS in that order)
+//        dV^T += dO^T P,  dK^T += Q^T dS    (the P / dS registers are the B operands, in
+//                                              the accumulator's M-row order; dO^T and Q^T
+//                                              are read transposed out of the row-major
+//                                              tiles in that order)
 //        dQ = dS K                          (dS through LDS, wave w takes head dims
-//                                              [32w, 32w+32); K^T in LDS is the B operand)
+//                                              [16w, 16w+16); K^T in registers)
 //    dQ of each (row, slot, head) is stored as a bf16 partial (a row's k slots are
 //    different items) and a merge kernel sums a row's partials; dK, dV are accumulated in
 //    registers over the item's rows and added once per item with float atomics (a block's
@@ -103,51 +104,64 @@ __global__ void __launch_bounds__(256) zero_kernel(float* __restrict__ p, int64_
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
 }
 
-// dQ = scale * dS K for head dims [32 w, 32 w + 32) of one sub-chunk (dS M-row major in
-// LDS, the K^T operands in registers), written to the bf16 dQ tile; two accumulators (even
-// and odd key steps) so that consecutive matrix instructions do not wait on each other.
-template <int DH>
-__device__ __forceinline__ void dq_tile(const unsigned char* ds, const bf16x8 (&ktop)[kBlk / 16], unsigned char* dqt,
-                                        int w, int lane, float scale) {
-  constexpr int SROW = BwdLds<DH>::SROW, QROW = BwdLds<DH>::QROW;
-  const int h = lane >> 5, nl = lane & 31;
-  f32x16 qa = f32x16{}, qb = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < kBlk / 16; ++ks) {
-    // keys 16 ks + 8 h + {0..7}: the order of K^T operand ks
-    const bf16x8 as = *reinterpret_cast<const bf16x8*>(&ds[nl * SROW + (16 * ks + 8 * h) * 2]);
-    if (ks % 2 == 0)
-      qa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, ktop[ks], qa, 0, 0, 0);
-    else
-      qb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, ktop[ks], qb, 0, 0, 0);
-  }
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    const uint32_t wq = cvt_bf16x2((qa[r] + qb[r]) * scale, (qa[r + 1] + qb[r + 1]) * scale);
-    unsigned char* d0 = &dqt[acc_row(r, h) * QROW + (32 * w + nl) * 2];
-    *reinterpret_cast<uint16_t*>(d0) = (uint16_t)(wq & 0xFFFFu);
-    *reinterpret_cast<uint16_t*>(d0 + QROW) = (uint16_t)(wq >> 16);
-  }
+// ---- attention backward: 8 waves of 16 keys each (v_mfma_f32_16x16x32_bf16)
+// Sixteen keys per wave halve the per-wave accumulators (dK^T, dV^T: 16 keys x d), the
+// register-held K / V / K^T operands and the score tiles, so the kernel fits 256 registers
+// and runs two waves per SIMD: one wave's products overlap the other's softmax, LDS
+// traffic and barriers.  The price is twice the LDS operand reads per product (each wave
+// reads the whole Q / dO / dS tiles for its 16 keys).  16x16 layout: lane (c = lane % 16,
+// g = lane / 16); A operand = row c of the A tile, 8 k-values; B operand = column c, the
+// same 8 k-values; output register i of a 16x16 tile = row 4 g + i, column c.  A k-step's
+// 8 values of group g are k0 + 8 g + {0..7} for the row-major operands, or rows chosen to
+// match the accumulator (the P / dS operands below): any order works as long as A and B
+// agree.
+constexpr int kWaves16 = 8;
+constexpr int kThreads16 = kWaves16 * 64;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Transposed operand for the 16x16x32 layout: lane (c, g) gets column col0 + c of rows
+// r0 + {0..3} (elements 0..3) and r1 + {0..3} (elements 4..7), r0 and r1 chosen per group
+// (the transposing read works within each 16-lane group: destination lane i takes, as
+// element j, value i % 4 of the 8 bytes addressed by source lane 4 j + i / 4, so source
+// lane 4 j + q addresses row r + j at columns col0 + 4 q .. + 3).
+__device__ __forceinline__ bf16x8 tr_operand16(const unsigned char* tile, int row_bytes, int r0, int r1, int col0,
+                                               int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const int sl = lane & 15, j = sl >> 2, q = sl & 3;
+  const int col = col0 + 4 * q;
+  const lds_u8* t = (const lds_u8*)tile;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r0 + j) * row_bytes + col * 2));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r1 + j) * row_bytes + col * 2));
+  const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 template <int DH, int G>
-__global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* __restrict__ q,
-                                                        const uint16_t* __restrict__ k,
-                                                        const uint16_t* __restrict__ v,
-                                                        const uint16_t* __restrict__ dout,
-                                                        const float* __restrict__ lse,
-                                                        const float* __restrict__ drow,
-                                                        const int4* __restrict__ wl, const int* __restrict__ n_items,
-                                                        const int32_t* __restrict__ entries,
-                                                        uint16_t* __restrict__ part_dq, float* __restrict__ dk,
-                                                        float* __restrict__ dv) {
+__global__ void __launch_bounds__(kThreads16, 1) attn_bwd(Dims D, const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ v,
+                                                            const uint16_t* __restrict__ dout,
+                                                            const float* __restrict__ lse,
+                                                            const float* __restrict__ drow,
+                                                            const int4* __restrict__ wl, const int* __restrict__ n_items,
+                                                            const int32_t* __restrict__ entries,
+                                                            uint16_t* __restrict__ part_dq, float* __restrict__ dk,
+                                                            float* __restrict__ dv) {
   using L_ = BwdLds<DH>;
-  constexpr int KS = DH / 16;  // k-steps over the head dims
-  constexpr int DT = DH / 32;  // head-dim tiles
+  constexpr int KS = DH / 32;  // 32-dim k-steps of S and dP
+  constexpr int DT = DH / 16;  // 16-dim tiles of dK^T, dV^T (and the waves that form dQ)
   constexpr int CPR = DH / 8;  // 16-byte pieces per row
+  constexpr int NPC = 32 * CPR;  // 16-byte pieces of a sub-chunk's Q (or dO)
+  static_assert(NPC <= kThreads16 && kThreads16 % NPC == 0, "each thread one piece of Q and one of dO");
   __shared__ L_ L;
 
-  // XCD-aware order: consecutive items (same KV block) in one XCD's L2
   const int n = *n_items;
   const int per_xcd = (n + 7) / 8;
   const int slot_in_xcd = blockIdx.x >> 3;
@@ -161,15 +175,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
   const int j0 = b * kBlk;
   const int nvalid = min(kBlk, D.N - j0);
   const int rows = w.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, nl = lane & 31;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, c = lane & 15;
   const float sc = D.scale * kLog2e;
 
-  // ---- stage K, V (row-major)
   {
     const uint16_t* kb = k + (sg * D.N + j0) * DH;
     const uint16_t* vb = v + (sg * D.N + j0) * DH;
-    for (int c = threadIdx.x; c < kBlk * CPR; c += kThreads) {
-      const int row = c / CPR, col = c % CPR;
+    for (int x = threadIdx.x; x < kBlk * CPR; x += kThreads16) {
+      const int row = x / CPR, col = x % CPR;
       const bool ok = row < nvalid;
       const uint4 kk = ok ? *reinterpret_cast<const uint4*>(kb + row * DH + col * 8) : make_uint4(0u, 0u, 0u, 0u);
       const uint4 vv = ok ? *reinterpret_cast<const uint4*>(vb + row * DH + col * 8) : make_uint4(0u, 0u, 0u, 0u);
@@ -177,14 +190,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
       *reinterpret_cast<uint4*>(&L.vr[row * L_::KROW + col * 16]) = vv;
     }
   }
-
-  f32x16 dkt[DT], dvt[DT];
+  f32x4 dkt[DT], dvt[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    dkt[dt] = f32x16{};
-    dvt[dt] = f32x16{};
+    dkt[dt] = f32x4{};
+    dvt[dt] = f32x4{};
   }
-  for (int r = threadIdx.x; r < rows; r += kThreads) {
+  for (int r = threadIdx.x; r < rows; r += kThreads16) {
     const int e = entries[w.y + r];
     const int t = e / D.k;
     L.rowt[r] = t;
@@ -192,54 +204,42 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
   }
   __syncthreads();
   const int mrows = rows * G;
-  const int first_pos = D.pos0 + L.rowt[0];  // rows ascend: the smallest position
-  // M-rows past the list store their dQ here: one scratch row after the partials
+  const int first_pos = D.pos0 + L.rowt[0];
   const int64_t dq_trash = (int64_t)D.S * D.T * D.Hkv * D.k * G * DH;
   const bool need_mask = first_pos < j0 + kBlk - 1;
-  const int key = j0 + 32 * wave + nl;                // this lane's key
-  // The block's operands that do not change over the item stay in registers (read from
-  // LDS once): K and V rows of this wave's 32 keys (B operands of S and dP, k-step ks =
-  // head dims 16 ks + 8 h + {0..7}) and, for dQ, K^T for head dims [32 wave, +32) (k-step
-  // ks = keys 16 ks + 8 h + {0..7}).  Every sub-chunk then reads only its Q, dO and dS.
-  bf16x8 kop[KS], vop[KS], ktop[kBlk / 16];
+  const int key = j0 + 16 * wave + c;  // this lane's key (S, dP, dK, dV columns)
+  // K and V rows of this wave's 16 keys (B operands of S and dP: k-step ks = head dims
+  // 32 ks + 8 grp + {0..7}) and, for dQ, K^T for head dims [16 wave, +16) (k-step ks = keys
+  // 32 ks + 8 grp + {0..7}), read from LDS once per item
+  bf16x8 kop[KS], vop[KS], ktop[kBlk / 32];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    kop[ks] = *reinterpret_cast<const bf16x8*>(&L.kr[(32 * wave + nl) * L_::KROW + (16 * ks + 8 * h) * 2]);
-    vop[ks] = *reinterpret_cast<const bf16x8*>(&L.vr[(32 * wave + nl) * L_::KROW + (16 * ks + 8 * h) * 2]);
+    kop[ks] = *reinterpret_cast<const bf16x8*>(&L.kr[(16 * wave + c) * L_::KROW + (32 * ks + 8 * grp) * 2]);
+    vop[ks] = *reinterpret_cast<const bf16x8*>(&L.vr[(16 * wave + c) * L_::KROW + (32 * ks + 8 * grp) * 2]);
   }
 #pragma unroll
-  for (int ks = 0; ks < kBlk / 16; ++ks)
-    ktop[ks] = wave < DT ? tr_operand(L.kr, L_::KROW, 16 * ks + 8 * h, 16 * ks + 8 * h + 4, 32 * wave, lane)
+  for (int ks = 0; ks < kBlk / 32; ++ks)
+    ktop[ks] = wave < DT ? tr_operand16(L.kr, L_::KROW, 32 * ks + 8 * grp, 32 * ks + 8 * grp + 4, 16 * wave, lane)
                          : bf16x8{};
 
-  // Q and dO pieces of a sub-chunk: piece c -> M-row c % 32, 16-byte column c / 32 (lanes
-  // of a wave take consecutive M-rows, so the transposed 2-byte LDS writes of one
-  // instruction fall in distinct dwords).  The next sub-chunk's pieces are fetched into
-  // registers while the current one computes.
-  constexpr int NP = 32 * CPR / kThreads;
-  static_assert(NP >= 1 && 32 * CPR == NP * kThreads, "whole pieces per thread");
-  // Two sub-chunks ahead are in flight (two register sets, the loop unrolled by two): one
-  // sub-chunk's gathered Q and dO (16 KB per item at d = 128) per round trip was too little
-  // to cover the gathers' latency.  Every load is unconditional (a row past the list reads
-  // row 0 and is zeroed where it is stored to LDS), and so are the dQ stores below: with
-  // no memory operation under a branch the compiler counts them exactly.
+  // a sub-chunk's Q and dO: thread x takes piece x % NPC (M-row % 32, 16-byte column / 32)
   struct Pre {
-    uint4 q[NP], g[NP];
-    float lse, drow;  // per-M-row values (threads 0..31 store them); lse is scaled when stored
+    uint4 q, g;
+    float lse, drow;
     int t, slot;
   };
+  const int pc = threadIdx.x % NPC;
+  const int pm = pc % 32, pcol = pc / 32;
   auto fetch = [&](Pre& pr, int m0n) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int c = threadIdx.x + kThreads * u;
-      const int mr = m0n + c % 32, col = c / 32;
+    {
+      const int mr = m0n + pm;
       const int mc = mr < mrows ? mr : 0;
       const int t = L.rowt[mc / G];
-      const int64_t off = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mc % G) * DH + col * 8;
-      pr.q[u] = *reinterpret_cast<const uint4*>(q + off);
-      pr.g[u] = *reinterpret_cast<const uint4*>(dout + off);
+      const int64_t off = (((int64_t)s * D.T + t) * D.H + (int64_t)g * G + mc % G) * DH + pcol * 8;
+      pr.q = *reinterpret_cast<const uint4*>(q + off);
+      pr.g = *reinterpret_cast<const uint4*>(dout + off);
     }
-    const int mr = m0n + (int)(threadIdx.x & 31);  // every thread (no branch)
+    const int mr = m0n + (int)(threadIdx.x & 31);
     const int mc = mr < mrows ? mr : 0;
     pr.t = L.rowt[mc / G];
     pr.slot = L.rslot[mc / G];
@@ -249,149 +249,140 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd(Dims D, const uint16_t* 
   };
   Pre pa, pb;
   fetch(pa, 0);
-  fetch(pb, 32);  // past the last sub-chunk: row-0 loads, never used
+  fetch(pb, 32);
 
-  // dQ of a sub-chunk goes to an LDS tile and is stored at the start of the next
-  // iteration, before that iteration's prefetch: the loads waited for at a loop head are
-  // then never queued behind stores issued just before (this chip's counter does not
-  // order a store ahead of a later load); the first iteration stores to the scratch row
   if (threadIdx.x < 32) L.dqoff[1][threadIdx.x] = dq_trash;
-  constexpr int OP = 32 * CPR / kThreads;  // 16-byte dQ pieces per thread
   auto store_dq = [&](int par) {
-#pragma unroll
-    for (int u = 0; u < OP; ++u) {
-      const int c = threadIdx.x + kThreads * u;
-      const int m = c / CPR, col = c % CPR;  // a row's pieces in consecutive lanes
-      const uint4 x = *reinterpret_cast<const uint4*>(&L.dqt[m * L_::QROW + col * 16]);
-      *reinterpret_cast<uint4*>(part_dq + L.dqoff[par][m] + col * 8) = x;
+    for (int x = threadIdx.x; x < NPC; x += kThreads16) {
+      const int m = x / CPR, col = x % CPR;
+      const uint4 val = *reinterpret_cast<const uint4*>(&L.dqt[m * L_::QROW + col * 16]);
+      *reinterpret_cast<uint4*>(part_dq + L.dqoff[par][m] + col * 8) = val;
     }
   };
 
   auto step = [&](Pre& pr, int m0) __attribute__((always_inline)) {
     const int par = (m0 >> 5) & 1;
-    __syncthreads();  // previous sub-chunk's buffers are free (and the staging is complete)
-    store_dq(par ^ 1);  // the previous sub-chunk's dQ
-    // ---- this sub-chunk's Q and dO (rows past the list as zeros)
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int c = threadIdx.x + kThreads * u;
-      const int m = c % 32, col = c / 32;
-      const bool ok = m0 + m < mrows;
-      *reinterpret_cast<uint4*>(&L.qs[m * L_::QROW + col * 16]) = ok ? pr.q[u] : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(&L.dos[m * L_::QROW + col * 16]) = ok ? pr.g[u] : make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    store_dq(par ^ 1);
+    if (threadIdx.x < NPC) {
+      const bool ok = m0 + pm < mrows;
+      *reinterpret_cast<uint4*>(&L.qs[pm * L_::QROW + pcol * 16]) = ok ? pr.q : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&L.dos[pm * L_::QROW + pcol * 16]) = ok ? pr.g : make_uint4(0u, 0u, 0u, 0u);
     }
     if (threadIdx.x < 32) {
       const int m = threadIdx.x, mr = m0 + m;
       const bool ok = mr < mrows;
       const int64_t pidx = (((int64_t)s * D.T + pr.t) * D.Hkv + g) * D.k + pr.slot;
-      L.lse2[m] = ok ? pr.lse * kLog2e : INFINITY;  // P = 0 for an M-row past the list
+      L.lse2[m] = ok ? pr.lse * kLog2e : INFINITY;
       L.drow[m] = ok ? pr.drow : 0.0f;
       L.pos[m] = ok ? D.pos0 + pr.t : -1;
       L.dqoff[par][m] = ok ? (pidx * G + mr % G) * DH : dq_trash;
     }
-    fetch(pr, m0 + 64);  // past the last sub-chunk: row-0 loads, never used
+    fetch(pr, m0 + 64);
     __syncthreads();
 
-    // ---- S = Q K^T and dP = dO V^T for this wave's 32 keys
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    // S = Q K^T, dP = dO V^T for this wave's 16 keys: M-row tiles mt = 0, 1
+    f32x4 sacc[2], pacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sacc[mt] = f32x4{};
+      pacc[mt] = f32x4{};
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&L.qs[nl * L_::QROW + (16 * ks + 8 * h) * 2]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kop[ks], sacc, 0, 0, 0);
-      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&L.dos[nl * L_::QROW + (16 * ks + 8 * h) * 2]);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vop[ks], pacc, 0, 0, 0);
-    }
-    // ---- P, dS (registers r hold M-rows acc_row(r, h) of this lane's key)
-    // per-M-row values of registers 4a .. 4a+3: M-rows 8a + 4h + {0..3}, one 16-byte read each
-    float pv[16], dsv[16];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&L.lse2[8 * a + 4 * h]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&L.drow[8 * a + 4 * h]);
+      for (int mt = 0; mt < 2; ++mt) {
+        const int ro = (16 * mt + c) * L_::QROW + (32 * ks + 8 * grp) * 2;
+        sacc[mt] = mfma16(*reinterpret_cast<const bf16x8*>(&L.qs[ro]), kop[ks], sacc[mt]);
+        pacc[mt] = mfma16(*reinterpret_cast<const bf16x8*>(&L.dos[ro]), vop[ks], pacc[mt]);
+      }
+    }
+    // P, dS: register i of tile mt holds M-row 16 mt + 4 grp + i of this lane's key
+    float pv[2][4], dsv[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&L.lse2[16 * mt + 4 * grp]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&L.drow[16 * mt + 4 * grp]);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
       int pq[4] = {0, 0, 0, 0};
       if (need_mask) {
-        const int4 p4 = *reinterpret_cast<const int4*>(&L.pos[8 * a + 4 * h]);
+        const int4 p4 = *reinterpret_cast<const int4*>(&L.pos[16 * mt + 4 * grp]);
         pq[0] = p4.x; pq[1] = p4.y; pq[2] = p4.z; pq[3] = p4.w;
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = 4 * a + x;
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], sc, -lv[x]));
-        if (need_mask && key > pq[x]) p = 0.0f;
-        pv[r] = p;
-        dsv[r] = p * (pacc[r] - dv4[x]);
+      for (int i = 0; i < 4; ++i) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], sc, -lv[i]));
+        if (need_mask && key > pq[i]) p = 0.0f;
+        pv[mt][i] = p;
+        dsv[mt][i] = p * (pacc[mt][i] - dv4[i]);
       }
     }
-    bf16x8 pb[2], sb[2];
+    // B operands of dV^T and dK^T (k = M-rows): elements 0..3 = tile 0's registers (M-rows
+    // 4 grp + {0..3}), 4..7 = tile 1's (M-rows 16 + 4 grp + {0..3})
+    const uint32_t wp[4] = {cvt_bf16x2(pv[0][0], pv[0][1]), cvt_bf16x2(pv[0][2], pv[0][3]),
+                            cvt_bf16x2(pv[1][0], pv[1][1]), cvt_bf16x2(pv[1][2], pv[1][3])};
+    const uint32_t wsd[4] = {cvt_bf16x2(dsv[0][0], dsv[0][1]), cvt_bf16x2(dsv[0][2], dsv[0][3]),
+                             cvt_bf16x2(dsv[1][0], dsv[1][1]), cvt_bf16x2(dsv[1][2], dsv[1][3])};
+    const bf16x8 pbo = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
+    const bf16x8 sbo = __builtin_bit_cast(bf16x8, make_uint4(wsd[0], wsd[1], wsd[2], wsd[3]));
+    // dV^T += dO^T P, dK^T += Q^T dS: A = head dims 16 dt + c over the same M-rows (transposed reads)
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      uint32_t wp[4], wsd[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        wp[x] = cvt_bf16x2(pv[8 * pp + 2 * x], pv[8 * pp + 2 * x + 1]);
-        wsd[x] = cvt_bf16x2(dsv[8 * pp + 2 * x], dsv[8 * pp + 2 * x + 1]);
-      }
-      pb[pp] = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
-      sb[pp] = __builtin_bit_cast(bf16x8, make_uint4(wsd[0], wsd[1], wsd[2], wsd[3]));
+    for (int dt = 0; dt < DT; ++dt) {
+      dvt[dt] = mfma16(tr_operand16(L.dos, L_::QROW, 4 * grp, 16 + 4 * grp, 16 * dt, lane), pbo, dvt[dt]);
+      dkt[dt] = mfma16(tr_operand16(L.qs, L_::QROW, 4 * grp, 16 + 4 * grp, 16 * dt, lane), sbo, dkt[dt]);
     }
-    // ---- dV^T += dO^T P, dK^T += Q^T dS (k-step pp = M-rows of register group pp)
+    // dS to LDS (M-row major) for dQ
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        // rows (M-rows) 16 pp + 4 h + {0..3} and 16 pp + 8 + 4 h + {0..3}: register group pp
-        const bf16x8 ag = tr_operand(L.dos, L_::QROW, 16 * pp + 4 * h, 16 * pp + 8 + 4 * h, 32 * dt, lane);
-        dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pb[pp], dvt[dt], 0, 0, 0);
-        const bf16x8 aq = tr_operand(L.qs, L_::QROW, 16 * pp + 4 * h, 16 * pp + 8 + 4 * h, 32 * dt, lane);
-        dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[pp], dkt[dt], 0, 0, 0);
+      for (int x = 0; x < 2; ++x) {
+        const uint32_t wv = wsd[2 * mt + x];
+        unsigned char* d0 = &L.ds[(16 * mt + 4 * grp + 2 * x) * L_::SROW + (16 * wave + c) * 2];
+        *reinterpret_cast<uint16_t*>(d0) = (uint16_t)(wv & 0xFFFFu);
+        *reinterpret_cast<uint16_t*>(d0 + L_::SROW) = (uint16_t)(wv >> 16);
       }
-    }
-    // ---- dS to LDS (M-row major) for dQ: each packed pair holds M-rows acc_row(r, h) and
-    // acc_row(r, h) + 1 (r even)
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const uint4 wv = __builtin_bit_cast(uint4, sb[pp]);
-      const uint32_t wsd[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        unsigned char* d0 = &L.ds[acc_row(8 * pp + 2 * x, h) * L_::SROW + (32 * wave + nl) * 2];
-        *reinterpret_cast<uint16_t*>(d0) = (uint16_t)(wsd[x] & 0xFFFFu);
-        *reinterpret_cast<uint16_t*>(d0 + L_::SROW) = (uint16_t)(wsd[x] >> 16);
-      }
-    }
     __syncthreads();
-    // ---- dQ = scale * dS K for head dims [32 wave, 32 wave + 32)
+    // dQ = scale * dS K for head dims [16 wave, 16 wave + 16): two M-row tiles, k = keys
     if (wave < DT) {
-      dq_tile<DH>(L.ds, ktop, L.dqt, wave, lane, D.scale);
+      f32x4 qa[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+      for (int ks = 0; ks < kBlk / 32; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          qa[mt] = mfma16(*reinterpret_cast<const bf16x8*>(&L.ds[(16 * mt + c) * L_::SROW + (32 * ks + 8 * grp) * 2]),
+                          ktop[ks], qa[mt]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const uint32_t wq = cvt_bf16x2(qa[mt][2 * x] * D.scale, qa[mt][2 * x + 1] * D.scale);
+          unsigned char* d0 = &L.dqt[(16 * mt + 4 * grp + 2 * x) * L_::QROW + (16 * wave + c) * 2];
+          *reinterpret_cast<uint16_t*>(d0) = (uint16_t)(wq & 0xFFFFu);
+          *reinterpret_cast<uint16_t*>(d0 + L_::QROW) = (uint16_t)(wq >> 16);
+        }
     }
   };
-  // Sub-chunks in pairs, the second one unconditional (past the list it is all empty
-  // M-rows: P = 0, nothing accumulates, its dQ goes to the scratch row), so that the loop
-  // body is straight-line and each loop head waits for one set of loads only.
   for (int m0 = 0; m0 < mrows; m0 += 64) {
     step(pa, m0);
     step(pb, m0 + 32);
   }
   __syncthreads();
-  store_dq(1);  // the last (odd) sub-chunk's dQ
+  store_dq(1);
 
-  // ---- dK, dV of the block: through LDS (row-major fp32 over the K / V staging area) so
-  // that the atomic adds of a wave cover contiguous head dims
   __syncthreads();
-  float* red = reinterpret_cast<float*>(L.kr);  // kBlk x DH fp32 fits K + V staging
+  float* red = reinterpret_cast<float*>(L.kr);
   static_assert(sizeof(float) * kBlk * DH <= 2 * kBlk * BwdLds<DH>::KROW, "reduction buffer fits");
   for (int which = 0; which < 2; ++which) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float val = which == 0 ? dkt[dt][r] * D.scale : dvt[dt][r];
-        red[(32 * wave + nl) * DH + 32 * dt + acc_row(r, h)] = val;
+      for (int i = 0; i < 4; ++i) {
+        const float val = which == 0 ? dkt[dt][i] * D.scale : dvt[dt][i];
+        red[(16 * wave + c) * DH + 16 * dt + 4 * grp + i] = val;
       }
     __syncthreads();
     float* dst = (which == 0 ? dk : dv) + (sg * D.N + j0) * DH;
-    for (int i = threadIdx.x; i < nvalid * DH; i += kThreads) unsafeAtomicAdd(dst + i, red[i]);
+    for (int i = threadIdx.x; i < nvalid * DH; i += kThreads16) unsafeAtomicAdd(dst + i, red[i]);
     __syncthreads();
   }
 }
@@ -789,7 +780,7 @@ void launch_bwd_t(const Dims& D, const uint16_t* q, const uint16_t* k, const uin
                   const float* lse, const float* drow, const WorkList& wl, const int32_t* entries,
                   uint16_t* part_dq, float* dk, float* dv, hipStream_t st) {
   const int64_t grid = (wl.ub + 7) / 8 * 8 + 8;
-  hipLaunchKernelGGL((attn_bwd<DH, G>), dim3((unsigned)grid), dim3(kThreads), 0, st, D, q, k, v, dout, lse, drow,
+  hipLaunchKernelGGL((attn_bwd<DH, G>), dim3((unsigned)grid), dim3(kThreads16), 0, st, D, q, k, v, dout, lse, drow,
                      wl.wl, wl.n_items, entries, part_dq, dk, dv);
 }
 
