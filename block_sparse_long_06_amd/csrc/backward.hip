@@ -161,6 +161,19 @@ __global__ void __launch_bounds__(kThreads16, 1) attn_bwd(Dims D, const uint16_t
   constexpr int NPC = 32 * CPR;  // 16-byte pieces of a sub-chunk's Q (or dO)
   static_assert(NPC <= kThreads16 && kThreads16 % NPC == 0, "each thread one piece of Q and one of dO");
   __shared__ L_ L;
+  // Sub-chunk i uses tile set i % 2 (Q, dO, dS, per-M-row values) and dQ tile i % 3, so
+  // only two barriers per sub-chunk remain (see the step below).  Set 1 and dQ tiles 1, 2
+  // live in the K / V staging area, idle during the sub-chunk loop (K, V, K^T are in
+  // registers by then), when it is large enough (d = 128), else in an array of their own.
+  constexpr int QB = 32 * L_::QROW, SB = 32 * L_::SROW;
+  constexpr int SET1 = 4 * QB + SB;  // qs, dos, ds of set 1; dQ tiles 1 and 2
+  constexpr bool IN_KV = SET1 <= 2 * kBlk * L_::KROW;
+  __shared__ __attribute__((aligned(16))) unsigned char xbuf[IN_KV ? 16 : SET1];
+  __shared__ __attribute__((aligned(16))) float tl2[2][32];
+  __shared__ __attribute__((aligned(16))) float tdr[2][32];
+  __shared__ __attribute__((aligned(16))) int tpos[2][32];
+  __shared__ int64_t tdq[3][32];
+  unsigned char* const s1 = IN_KV ? L.kr : xbuf;
 
   const int n = *n_items;
   const int per_xcd = (n + 7) / 8;
@@ -251,32 +264,52 @@ __global__ void __launch_bounds__(kThreads16, 1) attn_bwd(Dims D, const uint16_t
   fetch(pa, 0);
   fetch(pb, 32);
 
-  if (threadIdx.x < 32) L.dqoff[1][threadIdx.x] = dq_trash;
-  auto store_dq = [&](int par) {
+  // dQ tiles of "sub-chunks" -2 and -1 go to the scratch row (every thread reads these
+  // offsets in the first two sub-chunks: a barrier before them)
+  if (threadIdx.x < 32) {
+    tdq[1][threadIdx.x] = dq_trash;
+    tdq[2][threadIdx.x] = dq_trash;
+  }
+  __syncthreads();
+  auto dqt_of = [&](int tri) __attribute__((always_inline)) {
+    return tri == 0 ? L.dqt : s1 + 2 * QB + SB + (tri - 1) * QB;
+  };
+  auto store_dq = [&](int tri) {
+    const unsigned char* src = dqt_of(tri);
     for (int x = threadIdx.x; x < NPC; x += kThreads16) {
       const int m = x / CPR, col = x % CPR;
-      const uint4 val = *reinterpret_cast<const uint4*>(&L.dqt[m * L_::QROW + col * 16]);
-      *reinterpret_cast<uint4*>(part_dq + L.dqoff[par][m] + col * 8) = val;
+      const uint4 val = *reinterpret_cast<const uint4*>(&src[m * L_::QROW + col * 16]);
+      *reinterpret_cast<uint4*>(part_dq + tdq[tri][m] + col * 8) = val;
     }
   };
 
+  // Sub-chunk i: (a) store the dQ tile of sub-chunk i - 2 and stage this one's Q, dO and
+  // per-M-row values into set i % 2; barrier; (b) S, dP, P, dS, dV, dK, dS into set i % 2;
+  // barrier; (c) dQ into tile i % 3.  No barrier ends (c): a wave still in (c) of i only
+  // reads dS of set i % 2 and writes dQ tile i % 3, while a wave already in (a) of i + 1
+  // writes set (i + 1) % 2 and stores dQ tile (i - 1) % 3 -- finished by every wave
+  // before the barrier in (a) of i.  Set i % 2 is next written in (a) of i + 2 and dQ
+  // tile i % 3 in (c) of i + 3, both after barriers that follow every use.
   auto step = [&](Pre& pr, int m0) __attribute__((always_inline)) {
-    const int par = (m0 >> 5) & 1;
-    __syncthreads();
-    store_dq(par ^ 1);
+    const int si = m0 >> 5;
+    const int par = si & 1, tri = si % 3;
+    unsigned char* const qsb = par ? s1 : L.qs;
+    unsigned char* const dosb = par ? s1 + QB : L.dos;
+    unsigned char* const dsb = par ? s1 + 2 * QB : L.ds;
+    store_dq((si + 1) % 3);  // sub-chunk si - 2
     if (threadIdx.x < NPC) {
       const bool ok = m0 + pm < mrows;
-      *reinterpret_cast<uint4*>(&L.qs[pm * L_::QROW + pcol * 16]) = ok ? pr.q : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(&L.dos[pm * L_::QROW + pcol * 16]) = ok ? pr.g : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&qsb[pm * L_::QROW + pcol * 16]) = ok ? pr.q : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&dosb[pm * L_::QROW + pcol * 16]) = ok ? pr.g : make_uint4(0u, 0u, 0u, 0u);
     }
     if (threadIdx.x < 32) {
       const int m = threadIdx.x, mr = m0 + m;
       const bool ok = mr < mrows;
       const int64_t pidx = (((int64_t)s * D.T + pr.t) * D.Hkv + g) * D.k + pr.slot;
-      L.lse2[m] = ok ? pr.lse * kLog2e : INFINITY;
-      L.drow[m] = ok ? pr.drow : 0.0f;
-      L.pos[m] = ok ? D.pos0 + pr.t : -1;
-      L.dqoff[par][m] = ok ? (pidx * G + mr % G) * DH : dq_trash;
+      tl2[par][m] = ok ? pr.lse * kLog2e : INFINITY;
+      tdr[par][m] = ok ? pr.drow : 0.0f;
+      tpos[par][m] = ok ? D.pos0 + pr.t : -1;
+      tdq[tri][m] = ok ? (pidx * G + mr % G) * DH : dq_trash;
     }
     fetch(pr, m0 + 64);
     __syncthreads();
@@ -293,20 +326,20 @@ __global__ void __launch_bounds__(kThreads16, 1) attn_bwd(Dims D, const uint16_t
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int ro = (16 * mt + c) * L_::QROW + (32 * ks + 8 * grp) * 2;
-        sacc[mt] = mfma16(*reinterpret_cast<const bf16x8*>(&L.qs[ro]), kop[ks], sacc[mt]);
-        pacc[mt] = mfma16(*reinterpret_cast<const bf16x8*>(&L.dos[ro]), vop[ks], pacc[mt]);
+        sacc[mt] = mfma16(*reinterpret_cast<const bf16x8*>(&qsb[ro]), kop[ks], sacc[mt]);
+        pacc[mt] = mfma16(*reinterpret_cast<const bf16x8*>(&dosb[ro]), vop[ks], pacc[mt]);
       }
     }
     // P, dS: register i of tile mt holds M-row 16 mt + 4 grp + i of this lane's key
     float pv[2][4], dsv[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&L.lse2[16 * mt + 4 * grp]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&L.drow[16 * mt + 4 * grp]);
+      const float4 l4 = *reinterpret_cast<const float4*>(&tl2[par][16 * mt + 4 * grp]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&tdr[par][16 * mt + 4 * grp]);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
       int pq[4] = {0, 0, 0, 0};
       if (need_mask) {
-        const int4 p4 = *reinterpret_cast<const int4*>(&L.pos[16 * mt + 4 * grp]);
+        const int4 p4 = *reinterpret_cast<const int4*>(&tpos[par][16 * mt + 4 * grp]);
         pq[0] = p4.x; pq[1] = p4.y; pq[2] = p4.z; pq[3] = p4.w;
       }
 #pragma unroll
@@ -328,8 +361,8 @@ __global__ void __launch_bounds__(kThreads16, 1) attn_bwd(Dims D, const uint16_t
     // dV^T += dO^T P, dK^T += Q^T dS: A = head dims 16 dt + c over the same M-rows (transposed reads)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      dvt[dt] = mfma16(tr_operand16(L.dos, L_::QROW, 4 * grp, 16 + 4 * grp, 16 * dt, lane), pbo, dvt[dt]);
-      dkt[dt] = mfma16(tr_operand16(L.qs, L_::QROW, 4 * grp, 16 + 4 * grp, 16 * dt, lane), sbo, dkt[dt]);
+      dvt[dt] = mfma16(tr_operand16(dosb, L_::QROW, 4 * grp, 16 + 4 * grp, 16 * dt, lane), pbo, dvt[dt]);
+      dkt[dt] = mfma16(tr_operand16(qsb, L_::QROW, 4 * grp, 16 + 4 * grp, 16 * dt, lane), sbo, dkt[dt]);
     }
     // dS to LDS (M-row major) for dQ
 #pragma unroll
@@ -337,37 +370,41 @@ __global__ void __launch_bounds__(kThreads16, 1) attn_bwd(Dims D, const uint16_t
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const uint32_t wv = wsd[2 * mt + x];
-        unsigned char* d0 = &L.ds[(16 * mt + 4 * grp + 2 * x) * L_::SROW + (16 * wave + c) * 2];
+        unsigned char* d0 = &dsb[(16 * mt + 4 * grp + 2 * x) * L_::SROW + (16 * wave + c) * 2];
         *reinterpret_cast<uint16_t*>(d0) = (uint16_t)(wv & 0xFFFFu);
         *reinterpret_cast<uint16_t*>(d0 + L_::SROW) = (uint16_t)(wv >> 16);
       }
     __syncthreads();
     // dQ = scale * dS K for head dims [16 wave, 16 wave + 16): two M-row tiles, k = keys
     if (wave < DT) {
+      unsigned char* const dqb = dqt_of(tri);
       f32x4 qa[2] = {f32x4{}, f32x4{}};
 #pragma unroll
       for (int ks = 0; ks < kBlk / 32; ++ks)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          qa[mt] = mfma16(*reinterpret_cast<const bf16x8*>(&L.ds[(16 * mt + c) * L_::SROW + (32 * ks + 8 * grp) * 2]),
+          qa[mt] = mfma16(*reinterpret_cast<const bf16x8*>(&dsb[(16 * mt + c) * L_::SROW + (32 * ks + 8 * grp) * 2]),
                           ktop[ks], qa[mt]);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const uint32_t wq = cvt_bf16x2(qa[mt][2 * x] * D.scale, qa[mt][2 * x + 1] * D.scale);
-          unsigned char* d0 = &L.dqt[(16 * mt + 4 * grp + 2 * x) * L_::QROW + (16 * wave + c) * 2];
+          unsigned char* d0 = &dqb[(16 * mt + 4 * grp + 2 * x) * L_::QROW + (16 * wave + c) * 2];
           *reinterpret_cast<uint16_t*>(d0) = (uint16_t)(wq & 0xFFFFu);
           *reinterpret_cast<uint16_t*>(d0 + L_::QROW) = (uint16_t)(wq >> 16);
         }
     }
   };
+  int nsub = 0;
   for (int m0 = 0; m0 < mrows; m0 += 64) {
     step(pa, m0);
     step(pb, m0 + 32);
+    nsub += 2;
   }
   __syncthreads();
-  store_dq(1);
+  store_dq((nsub - 2) % 3);  // the last two sub-chunks' dQ tiles
+  store_dq((nsub - 1) % 3);
 
   __syncthreads();
   float* red = reinterpret_cast<float*>(L.kr);
