@@ -40,6 +40,11 @@ CASES = [
     # queries from position 700: query tiles straddle the inversion's 64-row steps
     W.small("bf16_k24_structured_offset", S=1, T=1900, N=2600, H=16, Hkv=2, d=128, dI=64, k=24,
             structure="band_sink_needles"),
+    # degenerate sizes: a cache that is one partial block (only the own block exists, every
+    # row's selection is that block alone), and exactly one full block
+    W.small("bf16_one_partial_block", S=2, T=77, N=77, H=8, Hkv=1, d=128, dI=64, k=16),
+    W.small("bf16_exactly_one_block", S=1, T=128, N=128, H=16, Hkv=2, d=64, dI=64, k=4),
+    W.small("fp32_one_partial_block", S=1, T=50, N=50, H=4, Hkv=1, d=64, dI=32, k=4, dtype=synth.F32),
     W.small("fp32_g2_d128", S=2, T=500, N=777, H=4, Hkv=2, d=128, dI=64, k=5, dtype=synth.F32),
     W.small("fp32_g8_d64", S=1, T=1200, N=1300, H=8, Hkv=1, d=64, dI=32, k=6, dtype=synth.F32),
 ]
@@ -123,6 +128,10 @@ DEC_CASES = [
     W.small("dec_bf16_g16", S=2, T=1, N=3000, H=16, Hkv=1, d=128, dI=64, k=16),
     W.small("dec_bf16_g1_d64_multi_q", S=3, T=2, N=2500, H=2, Hkv=2, d=64, dI=64, k=8),
     W.small("dec_bf16_g2", S=2, T=1, N=1800, H=4, Hkv=2, d=128, dI=32, k=4),
+    # the first token (one key: attention returns its value) and one key past a block
+    # boundary (the own block holds a single key)
+    W.small("dec_first_token", S=2, T=1, N=1, H=16, Hkv=2, d=128, dI=64, k=16),
+    W.small("dec_one_past_a_block", S=2, T=1, N=129, H=8, Hkv=1, d=128, dI=64, k=16),
 ]
 
 
