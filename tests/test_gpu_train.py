@@ -33,6 +33,8 @@ GRAD_MAX_REL = 2e-2
 CASES = [
     (W.small("train_bf16_g8", S=1, T=700, N=1000, H=16, Hkv=2, d=128, dI=64, k=4), 0.125),
     (W.small("train_bf16_g4_d64_ragged", S=2, T=300, N=555, H=8, Hkv=2, d=64, dI=32, k=3), 0.0),
+    # a cache of one partial block: every row attends to its own block alone (77 valid keys)
+    (W.small("train_bf16_one_partial_block", S=2, T=77, N=77, H=8, Hkv=1, d=128, dI=64, k=16), 0.0),
     (W.small("train_bf16_structured", S=1, T=1024, N=1024, H=8, Hkv=1, d=128, dI=64, k=8,
              structure="band_sink_needles"), 0.05),
     (W.small("train_bf16_g16_dI128", S=1, T=300, N=900, H=16, Hkv=1, d=128, dI=128, k=4), 0.1),
