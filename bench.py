@@ -427,16 +427,7 @@ def paged_decode(args, msa, wd, xd):
         msa.run_decode_kv(prob, lay, xd["q"], pools["k"], pools["v"], xd["q_idx"], pools["k_idx"], bufs)
     step()
     torch.cuda.synchronize()
-    msa.profiler_read(None, reset=True)
-    msa.profiler_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    msa.profiler_enable(False)
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, ms_timer = timed_then_profiled(msa, step, args.steps)
     st = {}
     for kn in ("idx_scores_stream", "block_topk_t1", "decode_attn", "decode_merge"):
         tms, nl = msa.profiler_read(kn, reset=False)
@@ -473,16 +464,7 @@ def other_selection(args, msa, wp, xp, pb, fused):
             msa.block_topk(prob, scores, sel)
     call()
     torch.cuda.synchronize()
-    msa.profiler_read(None, reset=True)
-    msa.profiler_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    msa.profiler_enable(False)
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, ms_timer = timed_then_profiled(msa, call, args.steps)
     m = prefill_model(wp.S, wp.T, wp.N, wp.H, wp.Hkv, wp.d, wp.dI, wp.k)
     st = {}
     for kn in (("idx_topk_mfma", "topk_merge") if fused else ("idx_scores_mfma", "block_topk")):
@@ -513,16 +495,7 @@ def token_decode(args, msa, wd, xd, block_sel):
         msa.run_token_decode(prob, xd["q"], xd["k"], xd["v"], xd["q_idx"], xd["k_idx"], tb, budget)
     step()
     torch.cuda.synchronize()
-    msa.profiler_read(None, reset=True)
-    msa.profiler_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    msa.profiler_enable(False)
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, ms_timer = timed_then_profiled(msa, step, args.steps)
     st = {}
     for kn in ("token_scores", "token_topk", "token_attn", "token_merge"):
         tms, nl = msa.profiler_read(kn, reset=False)
@@ -567,16 +540,7 @@ def train_step(args, msa, wl):
         msa.run_train_step(prob, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], dout, tb)
     step()
     torch.cuda.synchronize()
-    msa.profiler_read(None, reset=True)
-    msa.profiler_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    msa.profiler_enable(False)
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, ms_timer = timed_then_profiled(msa, step, args.steps)
     st = {}
     for kn in ("idx_scores_mfma", "block_topk", "ogq_mfma", "lse_merge", "bwd_zero", "bwd_drow", "attn_bwd", "dq_merge",
                "index_kl", "index_bwd_zero", "index_bwd", "index_dq_gather"):
@@ -592,13 +556,35 @@ def train_step(args, msa, wl):
         st["ogq_mfma"].update(roofline(fwd_flops, m["ogq_attention"]["bytes"], st["ogq_mfma"]["ms"] / 1e3))
     del tb, x
     return dict(workload=wl.description + ", training step (forward + backward + index KL)",
-                ms_per_step=ms, tokens_per_s=wl.T / (ms / 1e3), stages=st)
+                ms_per_step=ms, ms_per_step_with_kernel_timer=ms_timer, tokens_per_s=wl.T / (ms / 1e3), stages=st)
 
 
 PREFILL_TIMER_NAMES = ("idx_scores_mfma", "idx_scores_rows", "block_topk", "invert_count", "invert_scatter",
                        "invert_offsets", "scan_tile_sums", "scan_top", "scan_apply", "wl_count", "wl_emit", "ogq_mfma",
                        "ogq_simple", "lse_merge", "hot_select", "hot_compact", "cold_count", "cold_scatter",
                        "cold_offsets", "hot_mfma", "idx_topk_mfma", "topk_merge")
+
+
+def timed_then_profiled(msa, step, steps):
+    """Mean time of `steps` calls of step() without the library's per-kernel timer (its
+    event records add a few microseconds per launch), then of as many with the timer on;
+    the timer's records of the second run are left for the caller to read."""
+    import torch
+
+    def run():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    ms = run()
+    msa.profiler_read(None, reset=True)
+    msa.profiler_enable(True)
+    ms_timer = run()
+    msa.profiler_enable(False)
+    return ms, ms_timer
 
 
 def read_timer(msa, names):
@@ -665,24 +651,30 @@ def other_prefill(args, msa, wl, fused):
     for _ in range(max(args.warmup, 1)):
         run()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    def timed():
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev[i][0].record()
+            run()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return [e[0].elapsed_time(e[1]) for e in ev]
+    # as for the headline workload: step times without the library's per-kernel timer,
+    # then the same steps with it for the stage times
+    steps_ms = timed()
     msa.profiler_read(None, reset=True)
     msa.profiler_enable(True)
-    for i in range(args.steps):
-        ev[i][0].record()
-        run()
-        ev[i][1].record()
-    torch.cuda.synchronize()
+    timer_ms = timed()
     msa.profiler_enable(False)
     kern = read_timer(msa, PREFILL_TIMER_NAMES)
     msa.profiler_read(None, reset=True)
-    steps_ms = [e[0].elapsed_time(e[1]) for e in ev]
     ms = sum(steps_ms) / len(steps_ms)
     stages, split = prefill_stage_report(wl, pb, kern, args.steps)
     del x, pb
     torch.cuda.empty_cache()
     desc = wl.description + (", fused index scores + top-k" if fused else ", index scores and top-k as two calls")
     return dict(workload=desc, tokens=wl.T, tokens_per_s=wl.T / (ms / 1e3), prefill_ms=ms,
+                prefill_ms_with_kernel_timer=sum(timer_ms) / len(timer_ms),
                 **{"prefill_" + k: v for k, v in percentiles(steps_ms).items()}, stages=stages,
                 attention_pairs=split["pairs"])
 
@@ -769,26 +761,35 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    def timed_steps():
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record()
+            prefill()
+            ev[i][1].record()
+            if db is not None:
+                decode()
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        pre = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+        dec = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)] if db else None
+        return pre, dec, wall_s
+
+    # The headline steps run without the library's per-kernel timer (its two event records
+    # per launch add ~0.1-0.2 ms to a prefill step and ~35 us to a decode step); the same
+    # number of steps then runs again with the timer on for the per-kernel times, the
+    # stage rooflines and the dominant kernel's roofline.
+    prefill_steps, decode_steps, wall = timed_steps()
     msa.profiler_read(None, reset=True)
     msa.profiler_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record()
-        prefill()
-        ev[i][1].record()
-        if db is not None:
-            decode()
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    prefill_steps_timer, decode_steps_timer, _ = timed_steps()
     msa.profiler_enable(False)
     kern = read_timer(msa, PREFILL_TIMER_NAMES + ("idx_scores_stream", "block_topk_t1", "decode_attn",
                                                   "decode_simple", "decode_merge"))
     msa.profiler_read(None, reset=True)
-    prefill_steps = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
-    decode_steps = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)] if db else None
     prefill_ms = sum(prefill_steps) / args.steps
     decode_ms = (sum(decode_steps) / args.steps) if db else None
     print("[bench] timed %d steps: prefill %.3f ms, decode %s ms" % (args.steps, prefill_ms,
@@ -824,6 +825,7 @@ def main():
                    us_per_step_p50=1e3 * percentiles(decode_steps)["p50_ms"],
                    us_per_step_p95=1e3 * percentiles(decode_steps)["p95_ms"],
                    us_per_step_p99=1e3 * percentiles(decode_steps)["p99_ms"],
+                   us_per_step_with_kernel_timer=1e3 * sum(decode_steps_timer) / args.steps,
                    sequences=wd.S, kv_len=wd.N, stages=dstages)
 
     dec8 = None
@@ -833,16 +835,7 @@ def main():
             msa.run_decode(dprob8, xd["q"], xd["k"], xd["v"], xd["q_idx"], kidx8, db8)
         decode8()
         torch.cuda.synchronize()
-        msa.profiler_read(None, reset=True)
-        msa.profiler_enable(True)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            decode8()
-        e1.record()
-        torch.cuda.synchronize()
-        msa.profiler_enable(False)
-        ms8 = e0.elapsed_time(e1) / args.steps
+        ms8, _ = timed_then_profiled(msa, decode8, args.steps)
         k8 = {}
         for kn in ("idx_scores_stream", "block_topk_t1", "decode_attn", "decode_merge"):
             tms, nl = msa.profiler_read(kn, reset=False)
@@ -916,6 +909,7 @@ def main():
                    "num_kv_heads": wp.Hkv, "head_dim": wp.d, "index_dim": wp.dI, "block": 128, "topk": wp.k},
         "prefill_ms": prefill_ms, "prefill_ms_p50": percentiles(prefill_steps)["p50_ms"],
         "prefill_ms_p95": percentiles(prefill_steps)["p95_ms"], "prefill_ms_p99": percentiles(prefill_steps)["p99_ms"],
+        "prefill_ms_with_kernel_timer": sum(prefill_steps_timer) / args.steps,
         "wall_s_timed": wall, "other_prefill": others,
         "selection": "fused" if use_fused else "two-call", "other_selection": osel,
         "decode": dec, "decode_e4m3_index_keys": dec8, "decode_ragged_paged": decp, "decode_token_level": dect,
